@@ -1,0 +1,193 @@
+"""Plain fp64 CPU oracle of the routed sparse attention layer (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``rt_oracle.c`` (plain C,
+float64, sequential loops; see that file's header for the steps and their
+page citations) with ctypes.  Inputs are float64 arrays holding the exact
+values the device receives; nothing here reads a device result.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against closed
+forms, library routines for the special cases the method reduces to, brute
+force on tiny inputs, and hand-derived golden values.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rt_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile rt_oracle.c with the host C compiler (no HIP anywhere)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC,
+                               "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = ctypes.CDLL(_LIB)
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def route(qk, mu, w: int, nthreads: int | None = None, want_scores: bool = False):
+    """O1-O3.  qk [B,H,n,d], mu [H,k,d] -> (inv_norm [B,H,n], idx [B,H,k,w],
+    margin [B,H,k], scores [B,H,k,n] or None)."""
+    lib = _load()
+    qk, mu = _f64(qk), _f64(mu)
+    B, H, n, d = qk.shape
+    k = mu.shape[1]
+    assert mu.shape == (H, k, d) and 1 <= w <= n
+    inv = np.empty((B, H, n))
+    idx = np.empty((B, H, k, w), dtype=np.int32)
+    margin = np.empty((B, H, k))
+    scores = np.empty((B, H, k, n)) if want_scores else None
+    lib.orc_route_all(_p(qk), _p(mu), ctypes.c_int(B), ctypes.c_int(H), ctypes.c_long(n),
+                      ctypes.c_int(d), ctypes.c_int(k), ctypes.c_long(w), _p(inv), _p(idx),
+                      _p(margin), _p(scores), ctypes.c_int(nthreads or default_threads()))
+    return inv, idx, margin, scores
+
+
+def routed_attn(q, kk, v, idx, scale: float, causal: bool = True, normalize: bool = True,
+                nthreads: int | None = None, want_clusters: bool = False):
+    """O1 (if normalize), O4, O5.  -> (out [B,H,n,d], lse [B,H,k,w],
+    o_clusters [B,H,k,w,d] or None)."""
+    lib = _load()
+    q, kk, v, idx = _f64(q), _f64(kk), _f64(v), _i32(idx)
+    B, H, n, d = q.shape
+    k, w = idx.shape[2], idx.shape[3]
+    assert kk.shape == q.shape and v.shape == q.shape and idx.shape[:2] == (B, H)
+    assert idx.min() >= 0 and idx.max() < n
+    out = np.empty((B, H, n, d))
+    lse = np.empty((B, H, k, w))
+    oc = np.empty((B, H, k, w, d)) if want_clusters else None
+    lib.orc_routed_attn_all(_p(q), _p(kk), _p(v), _p(idx), ctypes.c_int(B), ctypes.c_int(H),
+                            ctypes.c_long(n), ctypes.c_int(d), ctypes.c_int(k), ctypes.c_long(w),
+                            ctypes.c_double(scale), ctypes.c_int(int(causal)),
+                            ctypes.c_int(int(normalize)), _p(out), _p(lse), _p(oc),
+                            ctypes.c_int(nthreads or default_threads()))
+    return out, lse, oc
+
+
+def centroid_update(mu, q, kk, idx, lam: float):
+    """O1 + O6: returns the updated centroids (the input is not modified)."""
+    lib = _load()
+    mu2 = _f64(mu).copy()
+    q, kk, idx = _f64(q), _f64(kk), _i32(idx)
+    B, H, n, d = q.shape
+    k, w = idx.shape[2], idx.shape[3]
+    assert mu2.shape == (H, k, d)
+    lib.orc_centroid_update_all(_p(mu2), _p(q), _p(kk), _p(idx), ctypes.c_int(B), ctypes.c_int(H),
+                                ctypes.c_long(n), ctypes.c_int(d), ctypes.c_int(k),
+                                ctypes.c_long(w), ctypes.c_double(lam))
+    return mu2
+
+
+def local_attn(q, kk, v, window: int, scale: float, causal: bool = True,
+               nthreads: int | None = None):
+    """O7 for [B,H,n,d] tensors."""
+    lib = _load()
+    q, kk, v = _f64(q), _f64(kk), _f64(v)
+    B, H, n, d = q.shape
+    out = np.empty_like(q)
+    lib.orc_local_attn_all(_p(q), _p(kk), _p(v), ctypes.c_int(B), ctypes.c_int(H),
+                           ctypes.c_long(n), ctypes.c_int(d), ctypes.c_long(window),
+                           ctypes.c_double(scale), ctypes.c_int(int(causal)), _p(out),
+                           ctypes.c_int(nthreads or default_threads()))
+    return out
+
+
+def routed_attn_bwd(q, kk, v, idx, dout, scale: float, causal: bool = True,
+                    nthreads: int | None = None):
+    """O1 + O8: gradients w.r.t. the normalised q^, k^ and v."""
+    lib = _load()
+    q, kk, v, dout, idx = _f64(q), _f64(kk), _f64(v), _f64(dout), _i32(idx)
+    B, H, n, d = q.shape
+    k, w = idx.shape[2], idx.shape[3]
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    lib.orc_routed_attn_bwd_all(_p(q), _p(kk), _p(v), _p(idx), _p(dout), ctypes.c_int(B),
+                                ctypes.c_int(H), ctypes.c_long(n), ctypes.c_int(d),
+                                ctypes.c_int(k), ctypes.c_long(w), ctypes.c_double(scale),
+                                ctypes.c_int(int(causal)), _p(dq), _p(dk), _p(dv),
+                                ctypes.c_int(nthreads or default_threads()))
+    return dq, dk, dv
+
+
+def normalize(x):
+    """O1 on the last axis (returns x^ and 1/max(||x||, 1e-12))."""
+    lib = _load()
+    x = _f64(x)
+    d = x.shape[-1]
+    n = x.size // d
+    xhat = np.empty_like(x)
+    inv = np.empty(x.shape[:-1])
+    lib.orc_normalize(_p(x), ctypes.c_long(n), ctypes.c_int(d), _p(xhat), _p(inv))
+    return xhat, inv
+
+
+def select(scores, w: int):
+    """O3 for scores [k, n] -> (idx [k, w], margin [k])."""
+    lib = _load()
+    s = _f64(scores)
+    k, n = s.shape
+    idx = np.empty((k, w), dtype=np.int32)
+    margin = np.empty(k)
+    lib.orc_select(_p(s), ctypes.c_long(n), ctypes.c_int(k), ctypes.c_long(w), _p(idx), _p(margin))
+    return idx, margin
+
+
+def scores(xhat, mu):
+    """O2 for xhat [n, d], mu [k, d] -> s [k, n]."""
+    lib = _load()
+    xhat, mu = _f64(xhat), _f64(mu)
+    n, d = xhat.shape
+    k = mu.shape[0]
+    s = np.empty((k, n))
+    lib.orc_scores(_p(xhat), _p(mu), ctypes.c_long(n), ctypes.c_int(d), ctypes.c_int(k), _p(s))
+    return s
+
+
+def forward(inputs: dict, cfg, scale: float | None = None, nthreads: int | None = None):
+    """The whole routed forward of one workload: route, attend, scatter, EMA,
+    plus local attention for the local heads.  Returns a dict."""
+    qk = inputs["qk"].value
+    v = inputs["v"].value
+    mu = inputs["mu"]
+    sc = (1.0 / np.sqrt(cfg.d)) if scale is None else scale
+    inv, idx, margin, _ = route(qk, mu, cfg.w, nthreads)
+    out, lse, _ = routed_attn(qk, qk, v, idx, sc, cfg.causal, True, nthreads)
+    mu_new = centroid_update(mu, qk, qk, idx, cfg.lam)
+    res = {"inv_norm": inv, "idx": idx, "margin": margin, "out": out, "lse": lse,
+           "mu": mu_new}
+    if cfg.L > 0:
+        res["local_out"] = local_attn(inputs["q_local"].value, inputs["k_local"].value,
+                                      inputs["v_local"].value, cfg.window, sc, True, nthreads)
+    return res

@@ -1,0 +1,384 @@
+"""Pins of the fp64 CPU oracle against things other than itself.
+
+Each test checks the oracle against a closed form, a library routine for a
+special case the method reduces to (torch's scaled_dot_product_attention and
+autograd in float64, numpy sorting, scipy distances), brute force on tiny
+inputs, or hand-derived values (tests/golden/hand_example.json).  The pages
+describe the method in words (paperlayer.ai summary of "Efficient
+Content-Based Sparse Attention with Routing Transformers", §3 attention, §4
+routing attention with clustering and balanced clusters, §2/§4 online
+spherical k-means centroids shared across sequences).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.spatial.distance import cdist
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _unit(a):
+    return a / np.linalg.norm(a, axis=-1, keepdims=True)
+
+
+def _sdpa(q, k, v, scale, causal=True, mask=None):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)
+    return F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask,
+                                          is_causal=causal and mask is None,
+                                          scale=scale).numpy()
+
+
+def _ev(expr):
+    return eval(expr, {"ln2": math.log(2.0), "log": math.log})
+
+
+# ---------------------------------------------------------------- golden ----
+def test_golden_hand_example_routed(orc):
+    g = json.load(open(GOLDEN))["routed"]
+    qk = np.array(g["qk"], dtype=np.float64)[None, None]
+    v = np.array(g["v"], dtype=np.float64)[None, None]
+    mu = np.array(g["mu"], dtype=np.float64)[None]
+    inv, idx, margin, _ = orc.route(qk, mu, g["w"])
+    assert idx[0, 0].tolist() == g["idx"]
+    np.testing.assert_allclose(margin[0, 0], g["margin"], atol=TOL)
+    np.testing.assert_allclose(inv[0, 0], [0.2, 0.5, 1.0, 0.2], atol=TOL)
+    out, lse, _ = orc.routed_attn(qk, qk, v, idx, _ev(g["scale"]), True)
+    want = np.array([[_ev(x) for x in row] for row in g["out"]])
+    np.testing.assert_allclose(out[0, 0], want, atol=TOL)
+    want_lse = np.array([[_ev(x) for x in row] for row in g["lse"]])
+    np.testing.assert_allclose(lse[0, 0], want_lse, atol=TOL)
+    mu2 = orc.centroid_update(mu, qk, qk, idx, g["lam"])
+    np.testing.assert_allclose(mu2[0], g["mu_new"], atol=TOL)
+
+
+def test_golden_hand_example_local(orc):
+    g = json.load(open(GOLDEN))["local"]
+    a = lambda x: np.array(x, dtype=np.float64)[None, None]
+    out = orc.local_attn(a(g["q"]), a(g["k"]), a(g["v"]), g["window"], _ev(g["scale"]), True)
+    want = np.array([[_ev(x) for x in row] for row in g["out"]])
+    np.testing.assert_allclose(out[0, 0], want, atol=TOL)
+
+
+# ------------------------------------------------------------- O1 and O2 ----
+def test_normalize_matches_numpy_norm_and_clamp(orc):
+    x = _rng(1).standard_normal((5, 33, 16))
+    x[0, 3] = 0.0                                   # zero row: clamp 1e-12
+    xhat, inv = orc.normalize(x)
+    nrm = np.linalg.norm(x, axis=-1)
+    np.testing.assert_allclose(inv[nrm > 0], 1.0 / nrm[nrm > 0], rtol=1e-14)
+    assert inv[0, 3] == 1e12 and np.all(xhat[0, 3] == 0.0)
+    np.testing.assert_allclose(np.linalg.norm(xhat[nrm > 0], axis=-1), 1.0, atol=1e-14)
+
+
+def test_scores_match_matmul(orc):
+    r = _rng(2)
+    xhat = _unit(r.standard_normal((50, 8)))
+    mu = r.standard_normal((6, 8))
+    np.testing.assert_allclose(orc.scores(xhat, mu), mu @ xhat.T, atol=1e-14)
+
+
+def test_p6_dot_ranking_equals_euclidean_ranking(orc):
+    """Summary §2/§4: for unit vectors nearest centroid == largest inner
+    product (||x-mu||^2 = 1 - 2<x,mu> + ||mu||^2 with ||mu|| fixed per centroid)."""
+    r = _rng(3)
+    qk = r.standard_normal((1, 1, 200, 8))
+    mu = r.standard_normal((1, 5, 8))
+    _, idx, _, _ = orc.route(qk, mu, 20)
+    dist = cdist(mu[0], _unit(qk[0, 0]))            # [k, n] Euclidean
+    for c in range(5):
+        nearest = np.lexsort((np.arange(200), dist[c]))[:20]
+        assert sorted(nearest.tolist()) == idx[0, 0, c].tolist()
+
+
+# -------------------------------------------------------------------- O3 ----
+def test_p2_select_structure_and_library_topk(orc):
+    r = _rng(4)
+    for n, k, w in [(64, 4, 16), (100, 7, 9), (33, 3, 33), (50, 1, 1)]:
+        s = r.standard_normal((k, n))
+        s[:, ::5] = np.round(s[:, ::5], 1)          # plenty of exact ties
+        idx, margin = orc.select(s, w)
+        for c in range(k):
+            row = idx[c]
+            assert np.all(np.diff(row) > 0) and row.min() >= 0 and row.max() < n
+            order = np.lexsort((np.arange(n), -s[c]))   # score desc, position asc
+            assert row.tolist() == sorted(order[:w].tolist())
+            want = np.inf if w == n else s[c, order[w - 1]] - s[c, order[w]]
+            assert margin[c] == want
+        assert idx.size == k * w
+
+
+def test_p5_select_brute_force_rank_count(orc):
+    """t is chosen iff fewer than w tokens rank strictly above it, where u ranks
+    above t when (s_u, -u) > (s_t, -t) lexicographically."""
+    r = _rng(5)
+    for trial in range(20):
+        n, k = int(r.integers(2, 17)), int(r.integers(1, 5))
+        w = int(r.integers(1, n + 1))
+        s = np.round(r.standard_normal((k, n)), 1)
+        idx, _ = orc.select(s, w)
+        for c in range(k):
+            chosen = []
+            for t in range(n):
+                above = sum(1 for u in range(n)
+                            if s[c, u] > s[c, t] or (s[c, u] == s[c, t] and u < t))
+                if above < w:
+                    chosen.append(t)
+            assert chosen == idx[c].tolist()
+
+
+def test_p7_membership_invariant_to_centroid_scale(orc):
+    r = _rng(6)
+    qk = r.standard_normal((2, 2, 128, 16))
+    mu = r.standard_normal((2, 8, 16))
+    _, idx, _, _ = orc.route(qk, mu, 16)
+    for alpha in (0.25, 3.0, 1e3):
+        _, idx2, _, _ = orc.route(qk, alpha * mu, 16)
+        assert np.array_equal(idx, idx2)
+
+
+# ----------------------------------------------------------- O4 and O5 ----
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n,d,scale", [(37, 8, None), (256, 16, 4.0), (1024, 16, None)])
+def test_p1_one_cluster_equals_dense_attention(orc, causal, n, d, scale):
+    """k=1, w=n: one cluster holding every token is plain (causal) softmax
+    attention on the unit-normalised vectors (summary §3)."""
+    r = _rng(7)
+    q = r.standard_normal((2, 2, n, d))
+    kk = r.standard_normal((2, 2, n, d))
+    v = r.standard_normal((2, 2, n, d))
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    idx = np.broadcast_to(np.arange(n, dtype=np.int32), (2, 2, 1, n))
+    out, lse, _ = orc.routed_attn(q, kk, v, idx, sc, causal)
+    qn = F.normalize(torch.from_numpy(q), dim=-1).numpy()
+    kn = F.normalize(torch.from_numpy(kk), dim=-1).numpy()
+    np.testing.assert_allclose(out, _sdpa(qn, kn, v, sc, causal), atol=1e-12)
+    # lse is the log of the softmax denominator
+    logits = sc * np.einsum("bhid,bhjd->bhij", qn, kn)
+    if causal:
+        logits = np.where(np.tril(np.ones((n, n), bool)), logits, -np.inf)
+    m = logits.max(-1)
+    np.testing.assert_allclose(lse[:, :, 0], m + np.log(np.exp(logits - m[..., None]).sum(-1)),
+                               atol=1e-12)
+
+
+def test_p3_softmax_rows_sum_to_one(orc):
+    """With every value row equal to 1, each cluster row returns sum_s P_rs."""
+    r = _rng(8)
+    qk = r.standard_normal((1, 3, 96, 16))
+    mu = r.standard_normal((3, 6, 16))
+    _, idx, _, _ = orc.route(qk, mu, 16)
+    for scale in (0.25, 4.0, 30.0):
+        _, _, oc = orc.routed_attn(qk, qk, np.ones_like(qk), idx, scale, True, want_clusters=True)
+        np.testing.assert_allclose(oc, 1.0, atol=TOL)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_p5_attention_brute_force_dense_masks(orc, causal):
+    """n <= 16: per cluster, a dense n x n masked softmax over the whole
+    sequence (keys outside the cluster, or later than the query when causal,
+    get -inf) evaluated by torch SDPA, rows outside the cluster dropped, summed
+    over clusters."""
+    r = _rng(9)
+    for trial in range(10):
+        n, k, d = int(r.integers(4, 17)), int(r.integers(1, 5)), 4
+        w = int(r.integers(1, n + 1))
+        qk = r.standard_normal((1, 1, n, d))
+        v = r.standard_normal((1, 1, n, d))
+        mu = r.standard_normal((1, k, d))
+        _, idx, _, _ = orc.route(qk, mu, w)
+        out, _, _ = orc.routed_attn(qk, qk, v, idx, 2.5, causal)
+        qn = _unit(qk)
+        want = np.zeros((n, d))
+        for c in range(k):
+            member = np.zeros(n, bool)
+            member[idx[0, 0, c]] = True
+            allow = member[:, None] & member[None, :]
+            if causal:
+                allow &= np.tril(np.ones((n, n), bool))
+            res = _sdpa(qn, qn, v, 2.5, mask=torch.from_numpy(allow))[0, 0]
+            want[member] += res[member]
+        np.testing.assert_allclose(out[0, 0], want, atol=1e-12)
+
+
+def test_p9_outputs_are_convex_combinations(orc):
+    r = _rng(10)
+    qk = r.standard_normal((1, 2, 200, 16))
+    v = r.standard_normal((1, 2, 200, 16))
+    mu = r.standard_normal((2, 8, 16))
+    _, idx, _, _ = orc.route(qk, mu, 25)
+    _, _, oc = orc.routed_attn(qk, qk, v, idx, 3.0, True, want_clusters=True)
+    for h in range(2):
+        for c in range(8):
+            p = idx[0, h, c]
+            for rr in range(25):
+                seen = v[0, h, p[: rr + 1]]
+                assert np.all(oc[0, h, c, rr] <= seen.max(0) + 1e-12)
+                assert np.all(oc[0, h, c, rr] >= seen.min(0) - 1e-12)
+
+
+def test_p12_scatter_zero_and_double_membership(orc):
+    r = _rng(11)
+    n, d, k, w = 120, 8, 6, 12
+    qk = r.standard_normal((1, 1, n, d))
+    v = r.standard_normal((1, 1, n, d))
+    mu = r.standard_normal((1, k, d))
+    _, idx, _, _ = orc.route(qk, mu, w)
+    out, _, _ = orc.routed_attn(qk, qk, v, idx, 2.0, True)
+    cnt = np.bincount(idx.ravel(), minlength=n)
+    assert cnt.sum() == k * w and np.any(cnt == 0) and np.any(cnt == 2)
+    assert np.all(out[0, 0, cnt == 0] == 0.0)
+    singles = [orc.routed_attn(qk, qk, v, idx[:, :, c:c + 1], 2.0, True)[0] for c in range(k)]
+    for t in np.nonzero(cnt == 2)[0]:
+        cs = [c for c in range(k) if t in idx[0, 0, c]]
+        np.testing.assert_allclose(out[0, 0, t], singles[cs[0]][0, 0, t] + singles[cs[1]][0, 0, t],
+                                   atol=1e-12)
+
+
+def test_distinct_q_and_k_and_unnormalised_mode(orc):
+    """normalize=False attends with the vectors as given (used for the pins of
+    the backward); with q != k it is SDPA with the two tensors."""
+    r = _rng(12)
+    q = r.standard_normal((1, 1, 40, 8))
+    kk = r.standard_normal((1, 1, 40, 8))
+    v = r.standard_normal((1, 1, 40, 8))
+    idx = np.arange(40, dtype=np.int32).reshape(1, 1, 1, 40)
+    out, _, _ = orc.routed_attn(q, kk, v, idx, 0.7, True, normalize=False)
+    np.testing.assert_allclose(out, _sdpa(q, kk, v, 0.7, True), atol=1e-12)
+
+
+# -------------------------------------------------------------------- O6 ----
+def test_p4_ema_closed_forms(orc):
+    r = _rng(13)
+    B, H, n, d, k, w = 3, 2, 64, 8, 4, 16
+    qk = r.standard_normal((B, H, n, d))
+    mu = r.standard_normal((H, k, d))
+    _, idx, _, _ = orc.route(qk, mu, w)
+    assert np.array_equal(orc.centroid_update(mu, qk, qk, idx, 1.0), mu)
+    # lam = 0: (S_Q + S_K)/2 with S the batch-wide member sums of x^
+    xh = _unit(qk)
+    S = np.zeros((H, k, d))
+    for b in range(B):
+        for h in range(H):
+            for c in range(k):
+                S[h, c] += xh[b, h, idx[b, h, c]].sum(0)
+    np.testing.assert_allclose(orc.centroid_update(mu, qk, qk, idx, 0.0), S, atol=1e-12)
+    # all members equal u (shared q = k): lam*mu + (1-lam)*B*w*u
+    u = _unit(r.standard_normal(d))
+    same = np.broadcast_to(3.7 * u, (B, H, n, d)).copy()
+    got = orc.centroid_update(mu, same, same, idx, 0.9)
+    np.testing.assert_allclose(got, 0.9 * mu + 0.1 * B * w * u, atol=1e-12)
+    # T updates with a fixed membership: lam^T mu0 + (1 - lam^T) S
+    m = mu.copy()
+    for _ in range(7):
+        m = orc.centroid_update(m, qk, qk, idx, 0.8)
+    np.testing.assert_allclose(m, 0.8 ** 7 * mu + (1 - 0.8 ** 7) * S, atol=1e-12)
+    # distinct q and k: lam*mu + (1-lam)/2 (S_Q + S_K)
+    kk = r.standard_normal((B, H, n, d))
+    SK = np.zeros((H, k, d))
+    xk = _unit(kk)
+    for b in range(B):
+        for h in range(H):
+            for c in range(k):
+                SK[h, c] += xk[b, h, idx[b, h, c]].sum(0)
+    np.testing.assert_allclose(orc.centroid_update(mu, qk, kk, idx, 0.3),
+                               0.3 * mu + 0.35 * (S + SK), atol=1e-12)
+
+
+def test_p11_ema_sum_order_vs_exact_sum(orc):
+    r = _rng(14)
+    B, H, n, d, k, w = 8, 1, 256, 16, 4, 64
+    qk = r.standard_normal((B, H, n, d))
+    mu = r.standard_normal((H, k, d))
+    _, idx, _, _ = orc.route(qk, mu, w)
+    got = orc.centroid_update(mu, qk, qk, idx, 0.0)
+    xh = _unit(qk)
+    for c in range(k):
+        for i in range(d):
+            terms = [xh[b, 0, t, i] for b in range(B) for t in idx[b, 0, c]]
+            assert abs(got[0, c, i] - math.fsum(terms)) < 1e-12
+
+
+# -------------------------------------------------------------------- O7 ----
+@pytest.mark.parametrize("n,window", [(50, 1), (50, 7), (50, 50), (50, 80), (300, 64)])
+def test_p8_local_against_banded_sdpa(orc, n, window):
+    r = _rng(15)
+    q, kk, v = (r.standard_normal((2, 3, n, 8)) for _ in range(3))
+    out = orc.local_attn(q, kk, v, window, 0.9, True)
+    i = np.arange(n)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - window)
+    np.testing.assert_allclose(out, _sdpa(q, kk, v, 0.9, mask=torch.from_numpy(band)), atol=1e-12)
+    if window == 1:
+        np.testing.assert_allclose(out, v, atol=1e-14)
+    if window >= n:
+        np.testing.assert_allclose(out, _sdpa(q, kk, v, 0.9, True), atol=1e-12)
+
+
+def test_local_non_causal_band(orc):
+    r = _rng(16)
+    n, window = 40, 5
+    q, kk, v = (r.standard_normal((1, 1, n, 4)) for _ in range(3))
+    out = orc.local_attn(q, kk, v, window, 1.1, False)
+    i = np.arange(n)
+    band = np.abs(i[None, :] - i[:, None]) < window
+    np.testing.assert_allclose(out, _sdpa(q, kk, v, 1.1, mask=torch.from_numpy(band)), atol=1e-12)
+
+
+# -------------------------------------------------------------------- O8 ----
+def test_p10_backward_matches_autograd_dense(orc):
+    """k=1, w=n: gradients of causal SDPA on the normalised vectors, by torch
+    autograd in float64 (normalisation held fixed, as in O8)."""
+    r = _rng(17)
+    n, d = 48, 8
+    q, kk, v, g = (r.standard_normal((1, 2, n, d)) for _ in range(4))
+    idx = np.broadcast_to(np.arange(n, dtype=np.int32), (1, 2, 1, n))
+    dq, dk, dv = orc.routed_attn_bwd(q, kk, v, idx, g, 1.3, True)
+    tq = torch.from_numpy(_unit(q)).requires_grad_()
+    tk = torch.from_numpy(_unit(kk)).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=1.3)
+    o.backward(torch.from_numpy(g))
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-11)
+
+
+def test_p10_backward_finite_differences_routed(orc):
+    """Several overlapping clusters (fixed membership): central differences of
+    L = <dout, out> with respect to q^, k^ and v, evaluated with the oracle's
+    forward on unnormalised inputs (normalize=False, so the inputs are q^)."""
+    r = _rng(18)
+    n, d, k, w = 20, 4, 3, 8
+    q = _unit(r.standard_normal((1, 1, n, d)))
+    kk = _unit(r.standard_normal((1, 1, n, d)))
+    v = r.standard_normal((1, 1, n, d))
+    g = r.standard_normal((1, 1, n, d))
+    mu = r.standard_normal((1, k, d))
+    _, idx, _, _ = orc.route(q, mu, w)
+    dq, dk, dv = orc.routed_attn_bwd(q, kk, v, idx, g, 1.7, True)
+
+    def loss(qq, kq, vv):
+        o, _, _ = orc.routed_attn(qq, kq, vv, idx, 1.7, True, normalize=False)
+        return float((o * g).sum())
+
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        args = [q, kk, v]
+        num = np.zeros_like(q)
+        for t in range(n):
+            for i in range(d):
+                a = [x.copy() for x in args]
+                b = [x.copy() for x in args]
+                a[which][0, 0, t, i] += h
+                b[which][0, 0, t, i] -= h
+                num[0, 0, t, i] = (loss(*a) - loss(*b)) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
