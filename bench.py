@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-attention layer on one MI355X.
+
+One step = one forward pass of the layer's hot path over one batch of
+synthetic input already resident in HBM: rt_route (normalise + score + top-w)
+-> rt_routed_attn (in-cluster causal attention + scatter-add) ->
+rt_centroid_update (EMA) for the routed heads, plus rt_local_attn for the
+local heads.  The default workload is the long-sequence layer: batch 1, 8
+routed heads (k=64 centroids, w=128) and 4 local heads (window 512), n=8192,
+d=128, bfloat16.
+
+Prints one JSON line (see the design doc for the fields).  The CPU baseline is the
+fp64 oracle timed on the host on one full step of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic as S  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+WORKLOADS = {
+    "long": "long: B=1, 8 routed heads (k=64, w=128) + 4 local heads (window 512), "
+            "n=8192, d=128, bf16, causal, shared QK, EMA lambda=0.999",
+    "mixed": "mixed: B=2, 8 routed heads (k=64, w=64) + 8 local heads (window 256), "
+             "n=4096, d=64, bf16",
+    "routed": "routed: B=4, 8 routed heads (k=32, w=32), n=1024, d=64, bf16",
+    "stress": "stress: B=1, 8 routed heads (k=128, w=256) + 8 local (window 256), "
+              "n=32768, d=64, bf16, 10% skewed tokens",
+}
+
+
+def dev(t):
+    st = t.storage
+    if t.dtype == "bf16":
+        return torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(st).cuda()
+
+
+def algorithmic(cfg):
+    """Algorithmic HBM bytes and flops per step, per call (minimum traffic:
+    every input read once, every output written once)."""
+    B, R, L, n, d, k, w = cfg.B, cfg.R, cfg.L, cfg.n, cfg.d, cfg.k, cfg.w
+    e = 2 if cfg.dtype == "bf16" else 4
+    tok = B * R * n * d * e                      # one [B,R,n,d] token tensor
+    route_bytes = tok + R * k * d * 4 + B * R * n * 4 + B * R * k * w * 4
+    attn_bytes = 2 * tok + tok + B * R * k * w * 4 + B * R * n * 4   # qk, v gathered; out; idx; inv
+    ema_bytes = tok + B * R * k * w * 4 + 2 * R * k * d * 4 + B * R * n * 4
+    local_bytes = 4 * B * L * n * d * e
+    attn_flops_tile = 4.0 * B * R * k * w * w * d           # QK^T and PV over full w x w tiles
+    attn_flops_causal = 4.0 * B * R * k * (w * (w + 1) / 2) * d
+    route_flops = 2.0 * B * R * n * k * d
+    lw = min(cfg.window, n)
+    local_flops = 4.0 * B * L * d * (lw * (lw + 1) / 2 + max(0, n - lw) * lw)
+    return dict(route_bytes=route_bytes, attn_bytes=attn_bytes, ema_bytes=ema_bytes,
+                local_bytes=local_bytes, attn_flops_tile=attn_flops_tile,
+                attn_flops_causal=attn_flops_causal, route_flops=route_flops,
+                local_flops=local_flops)
+
+
+def cpu_baseline(cfg, inp, scale):
+    """The oracle on one full step of the workload on the host cores."""
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    qk = inp["qk"].value
+    _, idx, _, _ = oracle.route(qk, inp["mu"], cfg.w, nthreads=threads)
+    oracle.routed_attn(qk, qk, inp["v"].value, idx, scale, True, True, nthreads=threads)
+    oracle.centroid_update(inp["mu"], qk, qk, idx, cfg.lam)
+    if cfg.L > 0:
+        oracle.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
+                          cfg.window, scale, True, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": cfg.B * cfg.n / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"one full step ({cfg.name} workload: route, routed attention, EMA and "
+                      f"local attention), fp64, {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying "
+                    "a captured HIP graph of the step")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    import content_sparse_attention_unit_amd as rt
+    rt._load()
+
+    cfg = S.CONFIGS[args.workload]
+    inp = S.make_inputs(cfg)
+    scale = 1.0 / math.sqrt(cfg.d)
+    qk, v = dev(inp["qk"]), dev(inp["v"])
+    mu0 = torch.from_numpy(inp["mu"].astype(np.float32)).cuda()
+    mu = mu0.clone()
+    B, R, n, d, k, w = cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w
+    inv = torch.empty((B, R, n), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, R, k, w), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(qk)
+    ws_route = torch.empty(rt.workspace_bytes("route", B, R, n, d, k, w), dtype=torch.uint8,
+                           device="cuda")
+    ws_attn = torch.empty(rt.workspace_bytes("routed_attn", B, R, n, d, k, w), dtype=torch.uint8,
+                          device="cuda")
+    if cfg.L > 0:
+        ql, kl, vl = dev(inp["q_local"]), dev(inp["k_local"]), dev(inp["v_local"])
+        out_l = torch.empty_like(ql)
+
+    def do_route():
+        rt.route(qk, mu, w, out=(inv, idx), ws=ws_route)
+
+    def do_attn():
+        rt.routed_attn(qk, qk, v, idx, inv, inv, scale=scale, out=out, ws=ws_attn)
+
+    def do_ema():
+        rt.centroid_update_(mu, qk, inv, idx, cfg.lam)
+
+    def do_local():
+        if cfg.L > 0:
+            rt.local_attn(ql, kl, vl, cfg.window, scale=scale, out=out_l)
+
+    def step():
+        do_route()
+        do_attn()
+        do_ema()
+        do_local()
+
+    stream = torch.cuda.Stream()
+    use_graph = not args.no_graph
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
+        graph = None
+        if use_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                step()
+            torch.cuda.synchronize()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+
+        # Whole-step timing.
+        mu.copy_(mu0)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        ms_per_step = ev0.elapsed_time(ev1) / args.steps
+
+        # Per-call timing (events on the stream the kernels are launched on).
+        per_call = {}
+        for name, fn in (("rt_route", do_route), ("rt_routed_attn", do_attn),
+                         ("rt_centroid_update", do_ema), ("rt_local_attn", do_local)):
+            if name == "rt_local_attn" and cfg.L == 0:
+                continue
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = max(5, args.steps)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per_call[name] = a.elapsed_time(b) / reps
+
+    alg = algorithmic(cfg)
+    routed_ms = per_call["rt_route"] + per_call["rt_routed_attn"] + per_call["rt_centroid_update"]
+    attn_s = per_call["rt_routed_attn"] * 1e-3
+    achieved_gbs = alg["attn_bytes"] / attn_s / 1e9
+    tokens = B * n
+    res = {
+        "metric": "routed-attention tokens/sec/layer at n=8192 fwd; % bf16 MFMA peak",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shapes)",
+        "config": {"workload": WORKLOADS[args.workload], "batch": B, "seq_len": n,
+                   "routed_heads": R, "local_heads": cfg.L, "d_head": d, "k": k, "w": w,
+                   "window": cfg.window, "graph": use_graph},
+        "roofline": {"bound": "hbm", "kernel": "rt_routed_attn (in-cluster attention)",
+                     "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": None,
+                     "mfma_frac_tile": alg["attn_flops_tile"] / attn_s / 1e12 / PEAK_BF16_TFLOPS},
+        "per_call_ms": per_call,
+        "routed_tokens_per_s": tokens / (routed_ms * 1e-3),
+        "routed_over_local_time": (routed_ms / per_call["rt_local_attn"]
+                                   if "rt_local_attn" in per_call else None),
+        "wall_s_timed": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, scale)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

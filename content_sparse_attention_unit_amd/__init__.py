@@ -1,0 +1,227 @@
+"""Routed sparse attention (Routing Transformer) on MI355X: Python binding.
+
+A thin ctypes layer over ``lib/librouted_attn.so`` (the C ABI declared in
+``include/routed_attn.h``).  Every function here only checks tensor
+metadata, allocates outputs/workspace with torch on the tensors' device and
+passes raw device pointers plus the current HIP stream; all arithmetic runs in
+the library's gfx950 kernels.  There is no fallback: if the library is not
+built, or a tensor is not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "routed_attn_bwd",
+           "workspace_bytes", "library_path", "RTError", "RT_OP"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "librouted_attn.so")
+_lib = None
+
+RT_F32, RT_BF16 = 0, 1
+RT_OP = {"route": 0, "routed_attn": 1, "local_attn": 2, "centroid_update": 3,
+         "routed_attn_bwd": 4}
+_STATUS = {0: "RT_OK", 1: "RT_EINVAL", 2: "RT_EUNSUPPORTED", 3: "RT_EHIP"}
+
+
+class RTError(RuntimeError):
+    """A non-zero rt_status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(or python content_sparse_attention_unit_amd/build.py)")
+    lib = ctypes.CDLL(_LIB_PATH)  # torch (imported above) already holds the HIP runtime
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "rt_route": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, Z, P],
+        "rt_routed_attn": [P, P, P, I, P, P, P, I, I, I, I, I, I, F, I, P, P, P, Z, P],
+        "rt_local_attn": [P, P, P, I, I, I, I, I, I, F, I, P, P],
+        "rt_centroid_update": [P, P, P, P, P, I, P, I, I, I, I, I, I, F, P],
+        "rt_routed_attn_bwd": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z,
+                               P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.rt_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.rt_workspace_bytes.restype = ctypes.c_size_t
+    lib.rt_last_error.argtypes = []
+    lib.rt_last_error.restype = ctypes.c_char_p
+    lib.rt_status_string.argtypes = [I]
+    lib.rt_status_string.restype = ctypes.c_char_p
+    lib.rt_version.argtypes = []
+    lib.rt_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise RTError(status, _load().rt_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RT_F32
+    if t.dtype == torch.bfloat16:
+        return RT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on a GPU device")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def workspace_bytes(op: str, B: int, H: int, n: int, d: int, k: int, w: int) -> int:
+    return int(_load().rt_workspace_bytes(RT_OP[op], B, H, n, d, k, w))
+
+
+def _workspace(op, dev, B, H, n, d, k, w, ws=None):
+    need = workspace_bytes(op, B, H, n, d, k, w)
+    if ws is not None:
+        return ws, need
+    if need == 0:
+        return None, 0
+    return torch.empty(need, dtype=torch.uint8, device=dev), need
+
+
+def route(qk: torch.Tensor, mu: torch.Tensor, w: int, *, want_scores: bool = False,
+          want_qk_hat: bool = False, out=None, ws=None):
+    """Normalise, score and select: returns ``(inv_norm, idx)`` plus ``scores``
+    and/or ``qk_hat`` when asked.  qk [B,H,n,d] f32/bf16, mu [H,k,d] f32."""
+    lib = _load()
+    dev = _gpu(qk, mu)
+    B, H, n, d = qk.shape
+    k = mu.shape[1]
+    if mu.dtype != torch.float32 or tuple(mu.shape) != (H, k, d):
+        raise ValueError("mu must be float32 [H, k, d]")
+    if out is None:
+        inv = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, H, k, w), dtype=torch.int32, device=dev)
+    else:
+        inv, idx = out
+    scores = torch.empty((B, H, k, n), dtype=torch.float32, device=dev) if want_scores else None
+    qk_hat = torch.empty_like(qk) if want_qk_hat else None
+    if scores is None:
+        ws, need = _workspace("route", dev, B, H, n, d, k, w, ws)
+    else:
+        need = 0
+    _check(lib.rt_route(_ptr(qk), _dtype_code(qk), _ptr(mu), B, H, n, d, k, w, _ptr(inv),
+                        _ptr(idx), _ptr(qk_hat), _ptr(scores), _ptr(ws),
+                        0 if ws is None else ws.numel(), _stream(dev)))
+    res = [inv, idx]
+    if want_scores:
+        res.append(scores)
+    if want_qk_hat:
+        res.append(qk_hat)
+    return tuple(res)
+
+
+def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                q_inv: torch.Tensor | None = None, k_inv: torch.Tensor | None = None, *,
+                scale: float | None = None, causal: bool = True, want_lse: bool = False,
+                out=None, lse=None, ws=None):
+    """In-cluster attention scatter-added to token order; returns ``out`` (and
+    ``lse`` when asked).  Pass ``kk is q`` (and ``k_inv is q_inv``) for shared QK."""
+    lib = _load()
+    dev = _gpu(q, kk, v, idx, q_inv, k_inv)
+    B, H, n, d = q.shape
+    k, w = idx.shape[2], idx.shape[3]
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, k, w), dtype=torch.float32, device=dev)
+    ws, _ = _workspace("routed_attn", dev, B, H, n, d, k, w, ws)
+    _check(lib.rt_routed_attn(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
+                              _ptr(k_inv), _ptr(idx), B, H, n, d, k, w, sc, int(causal),
+                              _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(dev)))
+    return (out, lse) if want_lse else out
+
+
+def local_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, window: int, *,
+               scale: float | None = None, causal: bool = True, out=None):
+    """Sliding-window attention over [B,H,n,d] tensors."""
+    lib = _load()
+    dev = _gpu(q, kk, v)
+    B, H, n, d = q.shape
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.rt_local_attn(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), B, H, n, d, int(window),
+                             sc, int(causal), _ptr(out), _stream(dev)))
+    return out
+
+
+def centroid_update_(mu: torch.Tensor, q: torch.Tensor, q_inv: torch.Tensor, idx: torch.Tensor,
+                     lam: float, kk: torch.Tensor | None = None,
+                     k_inv: torch.Tensor | None = None):
+    """EMA step of the centroids, in place on ``mu`` [H,k,d] float32."""
+    lib = _load()
+    dev = _gpu(mu, q, q_inv, idx, kk, k_inv)
+    B, H, n, d = q.shape
+    k, w = idx.shape[2], idx.shape[3]
+    _check(lib.rt_centroid_update(_ptr(mu), _ptr(q), _ptr(q_inv), _ptr(kk), _ptr(k_inv),
+                                  _dtype_code(q), _ptr(idx), B, H, n, d, k, w, float(lam),
+                                  _stream(dev)))
+    return mu
+
+
+def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=None,
+                    causal=True, ws=None):
+    """Gradients (dq_hat, dk_hat, dv) of routed_attn for a fixed membership."""
+    lib = _load()
+    dev = _gpu(q, kk, v, idx, lse, dout, q_inv, k_inv)
+    B, H, n, d = q.shape
+    k, w = idx.shape[2], idx.shape[3]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws, _ = _workspace("routed_attn_bwd", dev, B, H, n, d, k, w, ws)
+    _check(lib.rt_routed_attn_bwd(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
+                                  _ptr(k_inv), _ptr(idx), _ptr(lse), _ptr(dout), B, H, n, d, k, w,
+                                  sc, int(causal), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(dev)))
+    return dq, dk, dv

@@ -1,0 +1,239 @@
+// capi.hip -- the C ABI (include/routed_attn.h): host-side argument checks,
+// workspace carving and kernel launches.  Every check runs before anything is
+// enqueued; no entry point allocates, synchronises or keeps state.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/routed_attn.h"
+#include "rt_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rt_status fail(rt_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+rt_status hip_fail(const char* where, hipError_t e) {
+    return fail(RT_EHIP, "%s: kernel launch failed: %s", where, hipGetErrorString(e));
+}
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Checks shared by the entry points that take [B][H][n][d] token tensors.
+rt_status check_tokens(const char* fn, int dtype, int B, int H, int n, int d) {
+    if (B <= 0 || H <= 0 || n <= 0 || d <= 0)
+        return fail(RT_EINVAL, "%s: sizes must be positive (B=%d H=%d n=%d d=%d)", fn, B, H, n, d);
+    if (dtype != RT_F32 && dtype != RT_BF16)
+        return fail(RT_EUNSUPPORTED, "%s: dtype %d is not RT_F32 or RT_BF16", fn, dtype);
+    if (!dim_ok(d)) return fail(RT_EUNSUPPORTED, "%s: d=%d not in {16,32,64,128}", fn, d);
+    if ((long long)B * H > 65535)
+        return fail(RT_EUNSUPPORTED, "%s: B*H=%lld exceeds 65535", fn, (long long)B * H);
+    if ((long long)n * d >= (1LL << 31))
+        return fail(RT_EUNSUPPORTED, "%s: n*d=%lld exceeds 2^31-1", fn, (long long)n * d);
+    return RT_OK;
+}
+
+rt_status check_clusters(const char* fn, int n, int k, int w) {
+    if (k <= 0 || w <= 0) return fail(RT_EINVAL, "%s: k=%d and w=%d must be positive", fn, k, w);
+    if (w > n) return fail(RT_EINVAL, "%s: w=%d exceeds n=%d", fn, w, n);
+    if (k > 256) return fail(RT_EUNSUPPORTED, "%s: k=%d exceeds 256", fn, k);
+    return RT_OK;
+}
+
+size_t route_ws(int B, int H, int n, int k) { return (size_t)B * H * k * n * sizeof(float); }
+
+size_t attn_ws_mask(int B, int H, int n, int k) {
+    return align256((size_t)B * H * n * rt::mask_words(k) * sizeof(uint32_t));
+}
+
+size_t attn_ws(int B, int H, int n, int d, int k, int w) {
+    return attn_ws_mask(B, H, n, k) + (size_t)B * H * k * w * d * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rt_version(void) { return 10000; }
+
+const char* rt_last_error(void) { return g_err; }
+
+const char* rt_status_string(int status) {
+    switch (status) {
+        case RT_OK: return "RT_OK";
+        case RT_EINVAL: return "RT_EINVAL: invalid argument";
+        case RT_EUNSUPPORTED: return "RT_EUNSUPPORTED: outside the supported shapes or types";
+        case RT_EHIP: return "RT_EHIP: HIP runtime error";
+        default: return "unknown rt_status";
+    }
+}
+
+size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
+    if (B <= 0 || H <= 0 || n <= 0 || d <= 0 || k <= 0 || w <= 0) return (size_t)-1;
+    switch (op) {
+        case RT_OP_ROUTE: return route_ws(B, H, n, k);
+        case RT_OP_ROUTED_ATTN: return attn_ws(B, H, n, d, k, w);
+        case RT_OP_LOCAL_ATTN: return 0;
+        case RT_OP_CENTROID_UPDATE: return 0;
+        case RT_OP_ROUTED_ATTN_BWD: return rt::bwd_workspace_bytes(B * H, n, d, k, w);
+        default: return (size_t)-1;
+    }
+}
+
+rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int n, int d, int k,
+                   int w, float* inv_norm, int32_t* idx, void* qk_hat, float* scores, void* ws,
+                   size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_route";
+    g_err[0] = 0;
+    if (!qk || !mu || !inv_norm || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    if (k <= 0 || w <= 0) return fail(RT_EINVAL, "%s: k=%d and w=%d must be positive", fn, k, w);
+    if (w > n) return fail(RT_EINVAL, "%s: w=%d exceeds n=%d", fn, w, n);
+    if (n > rt::kMaxSeqTopw)
+        return fail(RT_EUNSUPPORTED, "%s: n=%d exceeds %d", fn, n, rt::kMaxSeqTopw);
+    if ((long long)B * H * k > 0x7fffffffLL)
+        return fail(RT_EUNSUPPORTED, "%s: B*H*k too large", fn);
+    float* sc = scores;
+    if (sc == nullptr) {
+        const size_t need = route_ws(B, H, n, k);
+        if (ws == nullptr || ws_bytes < need)
+            return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        ws == nullptr ? (size_t)0 : ws_bytes);
+        sc = static_cast<float*>(ws);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = rt::launch_score(qk, dtype, mu, B, H, n, d, k, inv_norm, sc, qk_hat, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = rt::launch_topw(sc, B * H, n, k, w, idx, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype,
+                         const float* q_inv, const float* k_inv, const int32_t* idx, int B, int H,
+                         int n, int d, int k, int w, float scale, int causal, void* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_routed_attn";
+    g_err[0] = 0;
+    if (!q || !kk || !v || !idx || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if ((q_inv == nullptr) != (k_inv == nullptr))
+        return fail(RT_EINVAL, "%s: q_inv and k_inv must both be given or both be NULL", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    st = check_clusters(fn, n, k, w);
+    if (st != RT_OK) return st;
+    if (out == q || out == kk || out == v) return fail(RT_EINVAL, "%s: out aliases an input", fn);
+    if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
+    const bool shared = (q == kk) && (q_inv == k_inv);
+    const int wmax = rt::max_cluster_rows(dtype, d, shared);
+    if (w > wmax)
+        return fail(RT_EUNSUPPORTED, "%s: w=%d exceeds %d for this dtype, d and q/k sharing", fn,
+                    w, wmax);
+    const size_t need = attn_ws(B, H, n, d, k, w);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    uint32_t* mask = static_cast<uint32_t*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_mask(B, H, n, k));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = B * H;
+    hipError_t e = rt::launch_membership(idx, BH, n, k, w, mask, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, mask, BH, n, d, k, w, scale,
+                                causal, out, lse, part, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = rt::launch_combine(mask, idx, part, dtype, BH, n, d, k, w, out, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_local_attn(const void* q, const void* kk, const void* v, int dtype, int B, int H,
+                        int n, int d, int window, float scale, int causal, void* out,
+                        void* stream) {
+    static const char* fn = "rt_local_attn";
+    g_err[0] = 0;
+    if (!q || !kk || !v || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    if (window < 1) return fail(RT_EINVAL, "%s: window=%d must be >= 1", fn, window);
+    if (out == q || out == kk || out == v) return fail(RT_EINVAL, "%s: out aliases an input", fn);
+    if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
+    hipError_t e = rt::launch_local_attn(q, kk, v, dtype, B * H, n, d, window, scale, causal, out,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_centroid_update(float* mu, const void* q, const float* q_inv, const void* kk,
+                             const float* k_inv, int dtype, const int32_t* idx, int B, int H, int n,
+                             int d, int k, int w, float lambda, void* stream) {
+    static const char* fn = "rt_centroid_update";
+    g_err[0] = 0;
+    if (!mu || !q || !q_inv || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if ((kk == nullptr) != (k_inv == nullptr))
+        return fail(RT_EINVAL, "%s: kk and k_inv must both be given or both be NULL", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    if (k <= 0 || w <= 0) return fail(RT_EINVAL, "%s: k=%d and w=%d must be positive", fn, k, w);
+    if (w > n) return fail(RT_EINVAL, "%s: w=%d exceeds n=%d", fn, w, n);
+    if (k > 65535) return fail(RT_EUNSUPPORTED, "%s: k=%d exceeds 65535", fn, k);
+    if (!(lambda >= 0.f && lambda <= 1.f))
+        return fail(RT_EINVAL, "%s: lambda=%g outside [0, 1]", fn, (double)lambda);
+    if ((long long)B * w > 0x7fffffffLL) return fail(RT_EUNSUPPORTED, "%s: B*w too large", fn);
+    hipError_t e = rt::launch_ema(mu, q, q_inv, kk, k_inv, dtype, idx, B, H, n, d, k, w, lambda,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
+                             const float* q_inv, const float* k_inv, const int32_t* idx,
+                             const float* lse, const void* dout, int B, int H, int n, int d, int k,
+                             int w, float scale, int causal, float* dq_hat, float* dk_hat,
+                             float* dv, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_routed_attn_bwd";
+    g_err[0] = 0;
+    if (!q || !kk || !v || !idx || !lse || !dout || !dq_hat || !dk_hat || !dv)
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if ((q_inv == nullptr) != (k_inv == nullptr))
+        return fail(RT_EINVAL, "%s: q_inv and k_inv must both be given or both be NULL", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    st = check_clusters(fn, n, k, w);
+    if (st != RT_OK) return st;
+    if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
+    const bool shared = (q == kk) && (q_inv == k_inv);
+    const int wmax = rt::max_cluster_rows(dtype, d, shared);
+    if (w > wmax)
+        return fail(RT_EUNSUPPORTED, "%s: w=%d exceeds %d for this dtype, d and q/k sharing", fn,
+                    w, wmax);
+    const size_t need = rt::bwd_workspace_bytes(B * H, n, d, k, w);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    hipError_t e = rt::launch_cluster_attn_bwd(q, kk, v, dtype, q_inv, k_inv, idx, lse, dout,
+                                               B * H, n, d, k, w, scale, causal, dq_hat, dk_hat,
+                                               dv, static_cast<float*>(ws),
+                                               static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported)
+        return fail(RT_EUNSUPPORTED, "%s: this configuration has no backward kernel", fn);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// ema.hip -- online k-means update of the shared centroids (gfx950).
+//
+// The paperlayer.ai summary of "Efficient Content-Based Sparse Attention with
+// Routing Transformers" (§2 and §4) says the centroids are shared by queries
+// and keys and across sequences, and are learned online by mini-batch
+// spherical k-means alongside the model.  The update applied here is the
+// exponential moving average
+//     mu_c <- lambda * mu_c + (1 - lambda)/2 * (S_Q[c] + S_K[c]),
+// S_Q[c] the sum of the unit-normalised queries routed to c over the whole
+// batch, S_K[c] likewise for the keys; no renormalisation.
+//
+// One workgroup per (head, centroid) owns mu[h][c] and sums its B*w member
+// rows (raw bf16/f32 times the float32 inverse norm) in a fixed order, so the
+// update is deterministic and needs no cross-workgroup reduction.
+#include "rt_common.hpp"
+#include "rt_internal.hpp"
+
+namespace rt {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* p, long off);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p, long off) {
+    return *reinterpret_cast<const float4*>(p + off);
+}
+template <>
+__device__ __forceinline__ float4 load4<u16>(const u16* p, long off) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p + off);
+    return make_float4(bf2f((u16)(v.x & 0xffffu)), bf2f((u16)(v.x >> 16)),
+                       bf2f((u16)(v.y & 0xffffu)), bf2f((u16)(v.y >> 16)));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void ema_kernel(float* __restrict__ mu, const T* __restrict__ q,
+                                                  const float* __restrict__ q_inv,
+                                                  const T* __restrict__ kk,
+                                                  const float* __restrict__ k_inv,
+                                                  const int32_t* __restrict__ idx, int B, int H,
+                                                  int n, int D, int k, int w, float lam) {
+    __shared__ float4 red[256];
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int DG = D / 4;               // threads per row (4 dims each)
+    const int RPI = 256 / DG;           // rows in flight
+    const int dg = threadIdx.x % DG, rg = threadIdx.x / DG;
+    const bool shared = (kk == nullptr);
+    float4 sq = make_float4(0.f, 0.f, 0.f, 0.f), sk = sq;
+    const int members = B * w;
+    for (int mi = rg; mi < members; mi += RPI) {
+        const int b = mi / w, r = mi % w;
+        const long bh = (long)b * H + h;
+        const int t = clamp_pos(idx[(bh * k + c) * w + r], n);
+        const long tok = bh * n + t;
+        const float iq = q_inv[tok];
+        const float4 x = load4<T>(q, tok * D + 4 * dg);
+        sq.x = fmaf(x.x, iq, sq.x);
+        sq.y = fmaf(x.y, iq, sq.y);
+        sq.z = fmaf(x.z, iq, sq.z);
+        sq.w = fmaf(x.w, iq, sq.w);
+        if (!shared) {
+            const float ik = k_inv[tok];
+            const float4 y = load4<T>(kk, tok * D + 4 * dg);
+            sk.x = fmaf(y.x, ik, sk.x);
+            sk.y = fmaf(y.y, ik, sk.y);
+            sk.z = fmaf(y.z, ik, sk.z);
+            sk.w = fmaf(y.w, ik, sk.w);
+        }
+    }
+    // S_Q + S_K per thread, then a fixed-order sum over the row groups.
+    float4 s;
+    if (shared) {
+        s = make_float4(2.f * sq.x, 2.f * sq.y, 2.f * sq.z, 2.f * sq.w);
+    } else {
+        s = make_float4(sq.x + sk.x, sq.y + sk.y, sq.z + sk.z, sq.w + sk.w);
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    if (rg == 0) {
+        float4 tot = red[dg];
+        for (int g2 = 1; g2 < RPI; ++g2) {
+            const float4 o = red[g2 * DG + dg];
+            tot.x += o.x;
+            tot.y += o.y;
+            tot.z += o.z;
+            tot.w += o.w;
+        }
+        float* m = mu + ((long)h * k + c) * D + 4 * dg;
+        const float a = (1.0f - lam) * 0.5f;
+        m[0] = fmaf(lam, m[0], a * tot.x);
+        m[1] = fmaf(lam, m[1], a * tot.y);
+        m[2] = fmaf(lam, m[2], a * tot.z);
+        m[3] = fmaf(lam, m[3], a * tot.w);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ema(float* mu, const void* q, const float* q_inv, const void* kk,
+                      const float* k_inv, int dtype, const int32_t* idx, int B, int H, int n,
+                      int d, int k, int w, float lambda, hipStream_t s) {
+    if (dtype == 1)
+        hipLaunchKernelGGL(ema_kernel<u16>, dim3(k, H), dim3(256), 0, s, mu, (const u16*)q, q_inv,
+                           (const u16*)kk, k_inv, idx, B, H, n, d, k, w, lambda);
+    else
+        hipLaunchKernelGGL(ema_kernel<float>, dim3(k, H), dim3(256), 0, s, mu, (const float*)q,
+                           q_inv, (const float*)kk, k_inv, idx, B, H, n, d, k, w, lambda);
+    return hipGetLastError();
+}
+
+}  // namespace rt

@@ -1,0 +1,331 @@
+// route.hip -- routing: unit normalisation, centroid scores and balanced
+// top-w selection (gfx950).
+//
+// Routing attention (paperlayer.ai summary of "Efficient Content-Based Sparse
+// Attention with Routing Transformers", §4 "Routing attention with
+// clustering"): queries/keys are unit-normalised and compared with k shared
+// centroids (the O(nkd) routing comparisons); with balanced clusters every
+// centroid holds the same number w of tokens, the top-w assignment costing
+// far less than the attention itself.
+//
+// Kernels
+//   score_bf16_kernel  one workgroup = 128 tokens x all centroids of a head.
+//                      The raw bf16 token rows are the B operand of
+//                      v_mfma_f32_16x16x32_bf16 straight from HBM; the fp32
+//                      centroids are split into three bf16 terms in LDS
+//                      (mu = hi + mid + lo, exact), so three MFMA passes give
+//                      float32-accurate inner products.  Scores are scaled by
+//                      the token's inverse norm in fp32 afterwards.
+//   score_f32_kernel   the same on the vector ALUs for float32 inputs.
+//   topw_kernel        one workgroup per (batch, head, centroid) row of n
+//                      scores: an exact radix select of the w-th largest
+//                      order-preserving key (4 passes of 8 bits, histogram in
+//                      LDS), then a position-ordered compaction with wave
+//                      ballots, so the w members come out sorted by position
+//                      with ties taken at the lowest positions.
+#include "rt_common.hpp"
+#include "rt_internal.hpp"
+
+namespace rt {
+namespace {
+
+template <int D>
+struct ScoreCfg {
+    static constexpr int DP = D < 32 ? 32 : D;         // dims padded to the MFMA k-depth
+    static constexpr int KC = (D == 128) ? 64 : 128;   // centroids per LDS chunk
+    static constexpr int LD = DP + 8;                  // LDS row stride (bf16), 16 B aligned
+    static constexpr int NS = DP / 32;                 // MFMA k-steps per token row
+    static constexpr int TOK = 128;                    // tokens per workgroup (4 waves x 32)
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__ qk,
+                                                         const float* __restrict__ mu, int H,
+                                                         int n, int k,
+                                                         float* __restrict__ inv_norm,
+                                                         float* __restrict__ scores,
+                                                         u16* __restrict__ qk_hat) {
+    using C = ScoreCfg<D>;
+    __shared__ __attribute__((aligned(16))) u16 lmu[3][C::KC][C::LD];
+
+    const int bh = blockIdx.y;
+    const int h = bh % H;
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const long base = (long)bh * n;
+
+    uint4 breg[2][C::NS];
+    float inv[2];
+    int tok[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int t = blockIdx.x * C::TOK + wv * 32 + tb * 16 + r16;
+        tok[tb] = t;
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+            const int d0 = 32 * s + 8 * g;
+            uint4 v = zero_u4();
+            if (t < n && d0 < D) v = *reinterpret_cast<const uint4*>(qk + (base + t) * D + d0);
+            breg[tb][s] = v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = u4_elem(v, e);
+                ss = fmaf(x, x, ss);
+            }
+        }
+        ss = xor_sum_16_32(ss);
+        inv[tb] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+        if (g == 0 && t < n) inv_norm[base + t] = inv[tb];
+        if (qk_hat != nullptr && t < n) {
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) {
+                const int d0 = 32 * s + 8 * g;
+                if (d0 < D) {
+                    uint4 o;
+                    uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        ow[e] = pack2(f2bf(u4_elem(breg[tb][s], 2 * e) * inv[tb]),
+                                      f2bf(u4_elem(breg[tb][s], 2 * e + 1) * inv[tb]));
+                    *reinterpret_cast<uint4*>(qk_hat + (base + t) * D + d0) = o;
+                }
+            }
+        }
+    }
+
+    for (int c0 = 0; c0 < k; c0 += C::KC) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < C::KC * C::DP; e += 256) {
+            const int c = e / C::DP, dim = e % C::DP;
+            const float m = (c0 + c < k && dim < D) ? mu[((long)h * k + c0 + c) * D + dim] : 0.f;
+            const u16 hi = f2bf(m);
+            const float r1 = m - bf2f(hi);
+            const u16 mid = f2bf(r1);
+            const float r2 = r1 - bf2f(mid);
+            lmu[0][c][dim] = hi;
+            lmu[1][c][dim] = mid;
+            lmu[2][c][dim] = f2bf(r2);
+        }
+        __syncthreads();
+        const int cn = min(C::KC, k - c0);
+        for (int cb = 0; cb * 16 < cn; ++cb) {
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+#pragma unroll
+                for (int s = 0; s < C::NS; ++s) {
+                    const bf16x8 a = as_bf16x8(
+                        *reinterpret_cast<const uint4*>(&lmu[p][cb * 16 + r16][32 * s + 8 * g]));
+                    acc0 = mfma16(a, as_bf16x8(breg[0][s]), acc0);
+                    acc1 = mfma16(a, as_bf16x8(breg[1][s]), acc1);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = c0 + cb * 16 + 4 * g + i;
+                if (c < k) {
+                    float* row = scores + ((long)bh * k + c) * n;
+                    if (tok[0] < n) row[tok[0]] = acc0[i] * inv[0];
+                    if (tok[1] < n) row[tok[1]] = acc1[i] * inv[1];
+                }
+            }
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict__ qk,
+                                                        const float* __restrict__ mu, int H, int n,
+                                                        int k, float* __restrict__ inv_norm,
+                                                        float* __restrict__ scores,
+                                                        float* __restrict__ qk_hat) {
+    constexpr int KC = 8192 / D;  // 32 KB of centroids per chunk
+    __shared__ float lmu[KC * D];
+    const int bh = blockIdx.y, h = bh % H;
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    const long base = (long)bh * n;
+    float x[D];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        x[i] = (t < n) ? qk[(base + t) * D + i] : 0.f;
+        ss = fmaf(x[i], x[i], ss);
+    }
+    const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+    if (t < n) {
+        inv_norm[base + t] = inv;
+        if (qk_hat != nullptr)
+            for (int i = 0; i < D; ++i) qk_hat[(base + t) * D + i] = x[i] * inv;
+    }
+    for (int c0 = 0; c0 < k; c0 += KC) {
+        __syncthreads();
+        const int cn = min(KC, k - c0);
+        for (int e = threadIdx.x; e < cn * D; e += 256) lmu[e] = mu[((long)h * k + c0) * D + e];
+        __syncthreads();
+        if (t < n) {
+            for (int c = 0; c < cn; ++c) {
+                float acc = 0.f;
+#pragma unroll
+                for (int i = 0; i < D; ++i) acc = fmaf(x[i], lmu[c * D + i], acc);
+                scores[((long)bh * k + c0 + c) * n + t] = acc * inv;
+            }
+        }
+    }
+}
+
+// Order-preserving map float -> uint32 (larger float, larger key); -0 and +0
+// map to the same key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scores, int n, int w,
+                                                  int32_t* __restrict__ idx) {
+    constexpr int NWV = NT / kWave;
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sel_bin, sel_rem;
+    __shared__ uint32_t wgt[NWV], weq[NWV];
+
+    const long row = blockIdx.x;
+    const float* srow = scores + row * n;
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int seg0 = wv * kWave * KPT;
+
+    uint32_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int pos = seg0 + kWave * j + lane;
+        key[j] = (pos < n) ? order_key(srow[pos]) : 0u;
+    }
+
+    // Radix select: after the four passes `prefix` is the w-th largest key and
+    // `remaining` the number of keys equal to it that belong to the top w.
+    uint32_t prefix = 0u, himask = 0u, remaining = (uint32_t)w;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int pos = seg0 + kWave * j + lane;
+            if (pos < n && (key[j] & himask) == prefix)
+                atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wv == 0) {
+            uint32_t cnt[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) cnt[b] = hist[4 * lane + b];
+            const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+            uint32_t suf = tot;  // inclusive suffix sum over lanes
+#pragma unroll
+            for (int dl = 1; dl < kWave; dl <<= 1) {
+                const uint32_t o = __shfl_down(suf, dl);
+                if (lane + dl < kWave) suf += o;
+            }
+            uint32_t above = suf - tot;
+#pragma unroll
+            for (int b = 3; b >= 0; --b) {
+                if (above < remaining && remaining <= above + cnt[b]) {
+                    sel_bin = (uint32_t)(4 * lane + b);
+                    sel_rem = remaining - above;
+                }
+                above += cnt[b];
+            }
+        }
+        __syncthreads();
+        prefix |= sel_bin << shift;
+        himask |= 0xffu << shift;
+        remaining = sel_rem;
+    }
+    const uint32_t T = prefix, need_eq = remaining;
+
+    // Position-ordered compaction: wave wv owns positions [seg0, seg0 + 64*KPT),
+    // visited in (j, lane) order, which is ascending position.
+    uint32_t gtc = 0u, eqc = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int pos = seg0 + kWave * j + lane;
+        const bool valid = pos < n;
+        gtc += (uint32_t)__popcll(__ballot(valid && key[j] > T));
+        eqc += (uint32_t)__popcll(__ballot(valid && key[j] == T));
+    }
+    if (lane == 0) {
+        wgt[wv] = gtc;
+        weq[wv] = eqc;
+    }
+    __syncthreads();
+    uint32_t eq_before = 0u, sel_before = 0u;
+    for (int v = 0; v < wv; ++v) {
+        const uint32_t take = (need_eq > eq_before) ? min(need_eq - eq_before, weq[v]) : 0u;
+        sel_before += wgt[v] + take;
+        eq_before += weq[v];
+    }
+    int32_t* out = idx + row * w;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int pos = seg0 + kWave * j + lane;
+        const bool valid = pos < n;
+        const bool gt = valid && key[j] > T;
+        const bool eq = valid && key[j] == T;
+        const uint64_t em = __ballot(eq);
+        const bool sel = gt || (eq && eq_before + (uint32_t)lanes_below(em) < need_eq);
+        const uint64_t sm = __ballot(sel);
+        const uint32_t slot = sel_before + (uint32_t)lanes_below(sm);
+        if (sel && slot < (uint32_t)w) out[slot] = pos;
+        eq_before += (uint32_t)__popcll(em);
+        sel_before += (uint32_t)__popcll(sm);
+    }
+}
+
+template <int D>
+void launch_score_d(const void* qk, int dtype, const float* mu, int BH, int H, int n, int k,
+                    float* inv_norm, float* scores, void* qk_hat, hipStream_t s) {
+    if (dtype == 1) {
+        dim3 grid((n + ScoreCfg<D>::TOK - 1) / ScoreCfg<D>::TOK, BH);
+        hipLaunchKernelGGL(score_bf16_kernel<D>, grid, dim3(256), 0, s, (const u16*)qk, mu, H, n,
+                           k, inv_norm, scores, (u16*)qk_hat);
+    } else {
+        dim3 grid((n + 255) / 256, BH);
+        hipLaunchKernelGGL(score_f32_kernel<D>, grid, dim3(256), 0, s, (const float*)qk, mu, H, n,
+                           k, inv_norm, scores, (float*)qk_hat);
+    }
+}
+
+template <int NT, int KPT>
+void launch_topw_k(const float* scores, int rows, int n, int w, int32_t* idx, hipStream_t s) {
+    hipLaunchKernelGGL((topw_kernel<NT, KPT>), dim3(rows), dim3(NT), 0, s, scores, n, w, idx);
+}
+
+}  // namespace
+
+hipError_t launch_score(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
+                        int k, float* inv_norm, float* scores, void* qk_hat, hipStream_t s) {
+    const int BH = B * H;
+    switch (d) {
+        case 16: launch_score_d<16>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
+        case 32: launch_score_d<32>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
+        case 64: launch_score_d<64>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
+        default: launch_score_d<128>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t* idx,
+                       hipStream_t s) {
+    const int rows = BH * k;
+    const int per = (n + 511) / 512;
+    if (per <= 1) launch_topw_k<512, 1>(scores, rows, n, w, idx, s);
+    else if (per <= 2) launch_topw_k<512, 2>(scores, rows, n, w, idx, s);
+    else if (per <= 4) launch_topw_k<512, 4>(scores, rows, n, w, idx, s);
+    else if (per <= 8) launch_topw_k<512, 8>(scores, rows, n, w, idx, s);
+    else if (per <= 16) launch_topw_k<512, 16>(scores, rows, n, w, idx, s);
+    else if (per <= 32) launch_topw_k<512, 32>(scores, rows, n, w, idx, s);
+    else if (per <= 64) launch_topw_k<512, 64>(scores, rows, n, w, idx, s);
+    else launch_topw_k<1024, 64>(scores, rows, n, w, idx, s);
+    return hipGetLastError();
+}
+
+}  // namespace rt

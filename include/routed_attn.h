@@ -1,0 +1,197 @@
+/*
+ * routed_attn.h -- C ABI of the MI355X (gfx950) routed sparse attention
+ * library: the routing-attention layer of the Routing Transformer (Roy,
+ * Saffar, Vaswani, Grangier, "Efficient Content-Based Sparse Attention with
+ * Routing Transformers", TACL 9, 2021).
+ *
+ * Page citations are to the paperlayer.ai "Source-linked AI summary" of that
+ * paper ("summary §N") and to its arXiv abstract.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to contiguous row-major memory
+ *    owned by the caller.  Token tensors are [B][H][n][d] (d fastest);
+ *    centroids [H][k][d] float32; inverse norms [B][H][n] float32;
+ *    memberships idx [B][H][k][w] int32; lse [B][H][k][w] float32;
+ *    scores [B][H][k][n] float32.
+ *  - `dtype` is RT_F32 (float32) or RT_BF16 (bfloat16 bit patterns); it
+ *    applies to every token tensor of the call.  Arithmetic is float32
+ *    (bf16 matrix products accumulate in float32).
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *    call only enqueues work on it and returns; device faults surface at the
+ *    caller's next synchronisation.  The library never synchronises, never
+ *    allocates, keeps no state between calls and may be called from several
+ *    host threads at once.
+ *  - Scratch memory is caller-provided: `ws` must point to at least
+ *    rt_workspace_bytes(op, ...) bytes of device memory (any alignment of 256
+ *    bytes or more), or may be NULL when that size is 0.  The workspace's
+ *    contents need not be initialised and are garbage afterwards.  Two calls
+ *    in flight at once must not share a workspace.
+ *  - All argument checks happen on the host before anything is enqueued; a
+ *    failed check returns RT_EINVAL or RT_EUNSUPPORTED and enqueues nothing.
+ *    A failed kernel launch returns RT_EHIP.  The text of the last error of
+ *    the calling thread is available from rt_last_error().
+ *  - Supported shapes: d in {16, 32, 64, 128}; 1 <= w <= n; 1 <= k <= 256;
+ *    n < 2^31 / d; the in-cluster kernels keep a whole cluster in on-chip
+ *    memory, which bounds w (rt_routed_attn returns RT_EUNSUPPORTED beyond
+ *    w*d <= 32768 for bf16 and w <= 1024 for float32).
+ */
+#ifndef ROUTED_ATTN_H
+#define ROUTED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RT_OK = 0,
+    RT_EINVAL = 1,        /* a null pointer, a non-positive size, w > n, ... */
+    RT_EUNSUPPORTED = 2,  /* a legal request outside what the kernels cover  */
+    RT_EHIP = 3           /* the HIP runtime refused a launch                 */
+} rt_status;
+
+typedef enum { RT_F32 = 0, RT_BF16 = 1 } rt_dtype;
+
+/* Operation ids for rt_workspace_bytes. */
+typedef enum {
+    RT_OP_ROUTE = 0,
+    RT_OP_ROUTED_ATTN = 1,
+    RT_OP_LOCAL_ATTN = 2,
+    RT_OP_CENTROID_UPDATE = 3,
+    RT_OP_ROUTED_ATTN_BWD = 4
+} rt_op;
+
+/*
+ * rt_route -- normalise, score against the centroids, balanced top-w.
+ *   Summary §4 ("Routing attention with clustering"): queries/keys are
+ *   unit-normalised and compared with k shared centroids (the O(nkd) routing
+ *   comparisons); balanced clusters give each centroid the same number of
+ *   tokens.  Summary §1/§2: nearest centroid approximates maximum inner
+ *   product search.
+ *
+ *   qk        [B][H][n][d] dtype, the shared query/key vectors (raw).
+ *   mu        [H][k][d] float32 centroids (read only).
+ *   inv_norm  out [B][H][n] float32: 1 / max(||qk_t||_2, 1e-12).
+ *   idx       out [B][H][k][w] int32: for centroid c, the w positions whose
+ *             unit vector has the largest inner product with mu_c (equal
+ *             scores: lower position first), listed in ascending position.
+ *             Scores are float32-accurate (the bf16 path splits mu into three
+ *             bf16 terms so that no precision is lost in the products).
+ *   qk_hat    optional out (NULL to skip) [B][H][n][d] dtype: qk * inv_norm.
+ *   scores    optional out (NULL to skip) [B][H][k][n] float32: the inner
+ *             products <qk_t * inv_norm_t, mu_c>.  When NULL the scores live
+ *             in the workspace.
+ *   ws        rt_workspace_bytes(RT_OP_ROUTE, ...) bytes (0 when scores != NULL).
+ */
+rt_status rt_route(const void *qk, int dtype, const float *mu, int B, int H, int n, int d, int k,
+                   int w, float *inv_norm, int32_t *idx, void *qk_hat, float *scores, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * rt_routed_attn -- attention inside each cluster, scatter-added back.
+ *   Summary §3: softmax-normalised attention over the permitted keys, the
+ *   output is the weighted sum of values, and an autoregressive query sees no
+ *   later position.  Summary §4: only query-key pairs of the same cluster are
+ *   considered.  Queries and keys are used unit-normalised: the logit of
+ *   members (r, s) is scale * <q_r, k_s> * q_inv[r] * k_inv[s].
+ *
+ *   q, kk, v   [B][H][n][d] dtype.  kk may equal q (shared query/key).
+ *   q_inv, k_inv  [B][H][n] float32 inverse norms (e.g. from rt_route);
+ *              pass NULL for both to attend with q and kk as given.
+ *   idx        [B][H][k][w] int32 memberships: each row strictly increasing
+ *              positions in [0, n) (rows that are not give unspecified
+ *              results; out-of-range values are clamped, never dereferenced).
+ *   causal     1: member s is visible to member r iff pos(s) <= pos(r);
+ *              0: every member sees every member.
+ *   out        out [B][H][n][d] dtype: for each token, the sum of its output
+ *              rows over the clusters that hold it, in ascending centroid
+ *              order (float32 accumulation, one final rounding); 0 for a
+ *              token that no cluster holds.  Must not alias an input.
+ *   lse        optional out (NULL to skip) [B][H][k][w] float32: natural log
+ *              of each row's softmax denominator, max + log(sum exp).
+ *   ws         rt_workspace_bytes(RT_OP_ROUTED_ATTN, ...) bytes.
+ *   Deterministic: repeated calls give bit-identical results.
+ */
+rt_status rt_routed_attn(const void *q, const void *kk, const void *v, int dtype,
+                         const float *q_inv, const float *k_inv, const int32_t *idx, int B, int H,
+                         int n, int d, int k, int w, float scale, int causal, void *out,
+                         float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rt_local_attn -- sliding-window attention for the non-routed heads.
+ *   Abstract and summary §6: local attention over a window of recent
+ *   positions (windows 512 and 1024 are the ones the pages report).
+ *   out_i = sum_j softmax_j(scale * <q_i, k_j>) v_j over j in
+ *   [max(0, i-window+1), i] (causal = 1).  causal = 0 uses the symmetric band
+ *   |i - j| < window.
+ *
+ *   q, kk, v, out  [B][H][n][d] dtype (raw, not normalised); out must not
+ *   alias an input.  window >= 1.  No workspace.
+ */
+rt_status rt_local_attn(const void *q, const void *kk, const void *v, int dtype, int B, int H,
+                        int n, int d, int window, float scale, int causal, void *out,
+                        void *stream);
+
+/*
+ * rt_centroid_update -- one online k-means step of the shared centroids.
+ *   Summary §2/§4: centroids are shared by queries and keys and across
+ *   sequences and are learned online by mini-batch spherical k-means.  The
+ *   pages do not print the update; this library applies the exponential
+ *   moving average
+ *       mu_c <- lambda * mu_c + (1 - lambda)/2 * (S_Q[c] + S_K[c]),
+ *   S_Q[c] = sum over every batch row b and every member t of cluster c of
+ *   q_t * q_inv_t (likewise S_K with kk, k_inv), without renormalisation.
+ *
+ *   mu      in/out [H][k][d] float32, updated in place.
+ *   q, q_inv   [B][H][n][d] dtype and [B][H][n] float32.
+ *   kk, k_inv  the key side; pass kk = NULL (and k_inv = NULL) when keys are
+ *              the queries (shared QK): then S_K = S_Q.
+ *   idx     [B][H][k][w] int32 memberships (as for rt_routed_attn).
+ *   lambda  in [0, 1].  Deterministic (fixed summation order).  No workspace.
+ */
+rt_status rt_centroid_update(float *mu, const void *q, const float *q_inv, const void *kk,
+                             const float *k_inv, int dtype, const int32_t *idx, int B, int H, int n,
+                             int d, int k, int w, float lambda, void *stream);
+
+/*
+ * rt_routed_attn_bwd -- gradients of rt_routed_attn with respect to its
+ *   attention inputs, for a fixed membership (routing is a discrete choice
+ *   and the centroids move by the update above, not by gradient).
+ *
+ *   dout            [B][H][n][d] dtype, gradient of `out`.
+ *   lse             [B][H][k][w] float32 from the forward call.
+ *   dq_hat, dk_hat  out [B][H][n][d] float32: gradients w.r.t. the
+ *                   normalised vectors q*q_inv and kk*k_inv (token order,
+ *                   summed over clusters).  With shared QK the gradient of
+ *                   the shared normalised vector is dq_hat + dk_hat.
+ *   dv              out [B][H][n][d] float32.
+ *   Other arguments as for rt_routed_attn.  ws: rt_workspace_bytes(
+ *   RT_OP_ROUTED_ATTN_BWD, ...) bytes.  Deterministic.
+ */
+rt_status rt_routed_attn_bwd(const void *q, const void *kk, const void *v, int dtype,
+                             const float *q_inv, const float *k_inv, const int32_t *idx,
+                             const float *lse, const void *dout, int B, int H, int n, int d, int k,
+                             int w, float scale, int causal, float *dq_hat, float *dk_hat,
+                             float *dv, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace size in bytes for operation `op` at these sizes (0 if none,
+ * (size_t)-1 if the sizes are invalid). */
+size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w);
+
+/* Static text for a status code. */
+const char *rt_status_string(int status);
+
+/* Text of the calling thread's last error ("" if none). */
+const char *rt_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int rt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROUTED_ATTN_H */

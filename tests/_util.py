@@ -1,0 +1,75 @@
+"""Helpers shared by the tests: device transfer of synthetic inputs and the
+comparison rules between the HIP path and the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+# Tolerances (the arithmetic is float32 on the device, float64 in the oracle).
+MARGIN = 1e-5            # memberships must match wherever the top-w score gap exceeds this
+F32_MAX_ABS = 1e-4       # float32 outputs
+BF16_MAX_ABS = 2e-2      # bfloat16 outputs
+BF16_MEAN_REL = 5e-3     # bfloat16 outputs: sum|gpu - oracle| / sum|oracle|
+MU_MAX_ABS = 1e-5        # updated centroids (float32 state)
+
+
+def dev_tensor(t, device="cuda"):
+    """A synthetic.Tensor (or float32 numpy array) as a device tensor with the
+    same bytes."""
+    if hasattr(t, "storage") and hasattr(t, "dtype") and t.dtype in ("f32", "bf16"):
+        st = t.storage
+        if t.dtype == "bf16":
+            return torch.from_numpy(st.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(st).to(device)
+    return torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).to(device)
+
+
+def host(x: torch.Tensor) -> np.ndarray:
+    x = x.detach()
+    if x.dtype == torch.bfloat16:
+        x = x.float()
+    return x.cpu().numpy().astype(np.float64) if x.is_floating_point() else x.cpu().numpy()
+
+
+def assert_close_out(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "out"):
+    err = np.abs(got - want)
+    if dtype == "f32":
+        assert err.max() <= F32_MAX_ABS, f"{what}: max-abs {err.max():.3e} > {F32_MAX_ABS}"
+        return
+    denom = np.abs(want).sum()
+    mean_rel = err.sum() / denom if denom > 0 else err.sum()
+    assert err.max() <= BF16_MAX_ABS, f"{what}: max-abs {err.max():.3e} > {BF16_MAX_ABS}"
+    assert mean_rel <= BF16_MEAN_REL, f"{what}: mean-rel {mean_rel:.3e} > {BF16_MEAN_REL}"
+
+
+def check_membership(orc, gpu_idx, orc_idx, orc_margin, qk_value, mu, w):
+    """Equal rows wherever the oracle's margin exceeds MARGIN; elsewhere the GPU
+    row must be a valid top-w of the oracle's scores within MARGIN.  Returns
+    the boolean [B,H,k] array of clusters whose rows differ."""
+    B, H, k, _ = orc_idx.shape
+    same = (gpu_idx == orc_idx).all(-1)
+    robust = orc_margin > MARGIN
+    bad = np.argwhere(robust & ~same)
+    assert bad.size == 0, f"membership differs on {len(bad)} clusters with margin > {MARGIN}: {bad[:5]}"
+    for b, h, c in np.argwhere(~same):
+        row = gpu_idx[b, h, c]
+        assert np.all(np.diff(row) > 0) and row.min() >= 0 and row.max() < qk_value.shape[2]
+        xhat, _ = orc.normalize(qk_value[b, h])
+        s = orc.scores(xhat, mu[h, c:c + 1])[0]
+        order = np.sort(s)[::-1]
+        sw, sw1 = order[w - 1], (order[w] if w < len(s) else -np.inf)
+        chosen = np.zeros(len(s), bool)
+        chosen[row] = True
+        assert np.all(s[chosen] >= sw - MARGIN) and np.all(s[~chosen] <= sw1 + MARGIN)
+    return ~same
+
+
+def tokens_touched(idx_a, idx_b, differs, n):
+    """[B,H,n] mask of tokens that belong, under either membership, to a
+    cluster whose rows differ."""
+    B, H = idx_a.shape[:2]
+    touched = np.zeros((B, H, n), bool)
+    for b, h, c in np.argwhere(differs):
+        touched[b, h, idx_a[b, h, c]] = True
+        touched[b, h, idx_b[b, h, c]] = True
+    return touched

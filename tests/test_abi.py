@@ -1,0 +1,157 @@
+"""CPU tests of the C ABI: the library loads, exports every function declared
+in include/routed_attn.h, and rejects invalid arguments on the host before
+anything is enqueued (no GPU is touched: each call below fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "routed_attn.h")
+
+RT_OK, RT_EINVAL, RT_EUNSUPPORTED = 0, 1, 2
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import content_sparse_attention_unit_amd as rt
+    return rt._load()
+
+
+def _last(lib):
+    return lib.rt_last_error().decode()
+
+
+def test_exports_every_declared_function(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:rt_status|size_t|const char \*|int)\s*\*?\s*(rt_\w+)\s*\(",
+                              text, flags=re.M))
+    assert {"rt_route", "rt_routed_attn", "rt_local_attn", "rt_centroid_update",
+            "rt_routed_attn_bwd", "rt_workspace_bytes", "rt_status_string", "rt_last_error",
+            "rt_version"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in range(4):
+        assert lib.rt_status_string(code).startswith(b"RT_")
+    assert lib.rt_version() >= 10000
+
+
+def route(lib, qk=FAKE, dtype=1, mu=FAKE, B=1, H=1, n=64, d=16, k=4, w=16, inv=FAKE, idx=FAKE,
+          scores=None, ws=FAKE, ws_bytes=1 << 30):
+    return lib.rt_route(qk, dtype, mu, B, H, n, d, k, w, inv, idx, None, scores, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(qk=None), RT_EINVAL, "null"),
+    (dict(mu=None), RT_EINVAL, "null"),
+    (dict(inv=None), RT_EINVAL, "null"),
+    (dict(idx=None), RT_EINVAL, "null"),
+    (dict(B=0), RT_EINVAL, "positive"),
+    (dict(n=-1), RT_EINVAL, "positive"),
+    (dict(k=0), RT_EINVAL, "positive"),
+    (dict(w=0), RT_EINVAL, "positive"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(d=48), RT_EUNSUPPORTED, "d=48"),
+    (dict(dtype=7), RT_EUNSUPPORTED, "dtype"),
+    (dict(n=70000, w=16), RT_EUNSUPPORTED, "exceeds 65536"),
+    (dict(B=300, H=300), RT_EUNSUPPORTED, "B*H"),
+    (dict(ws=None), RT_EINVAL, "workspace"),
+    (dict(ws_bytes=100), RT_EINVAL, "workspace"),
+])
+def test_route_validation(lib, kw, code, msg):
+    assert route(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def attn(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE, B=1, H=1,
+         n=64, d=16, k=4, w=16, scale=0.25, causal=1, out=ctypes.c_void_p(0x2000), lse=None,
+         ws=FAKE, ws_bytes=0):
+    return lib.rt_routed_attn(q, kk, v, dtype, q_inv, k_inv, idx, B, H, n, d, k, w, scale, causal,
+                              out, lse, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), RT_EINVAL, "null"),
+    (dict(v=None), RT_EINVAL, "null"),
+    (dict(idx=None), RT_EINVAL, "null"),
+    (dict(out=None), RT_EINVAL, "null"),
+    (dict(k_inv=None), RT_EINVAL, "both"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(k=257), RT_EUNSUPPORTED, "k=257"),
+    (dict(d=8), RT_EUNSUPPORTED, "d=8"),
+    (dict(out=FAKE), RT_EINVAL, "alias"),
+    (dict(scale=float("inf")), RT_EINVAL, "scale"),
+    (dict(scale=float("nan")), RT_EINVAL, "scale"),
+    (dict(causal=2), RT_EINVAL, "causal"),
+    (dict(n=4096, d=128, w=300), RT_EUNSUPPORTED, "w=300"),
+    (dict(n=4096, d=64, w=600), RT_EUNSUPPORTED, "w=600"),
+    (dict(ws_bytes=10), RT_EINVAL, "workspace"),
+])
+def test_routed_attn_validation(lib, kw, code, msg):
+    assert attn(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_routed_attn_limits_depend_on_sharing(lib):
+    # distinct q/k at d=128 is limited to w=128, shared q/k to 256
+    assert attn(lib, q=ctypes.c_void_p(0x3000), n=4096, d=128, w=200, ws_bytes=0) == RT_EUNSUPPORTED
+    assert attn(lib, q=FAKE, kk=FAKE, n=4096, d=128, w=200, ws_bytes=0) == RT_EINVAL  # only ws missing
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), RT_EINVAL, "null"),
+    (dict(window=0), RT_EINVAL, "window"),
+    (dict(d=100), RT_EUNSUPPORTED, "d=100"),
+    (dict(out=FAKE), RT_EINVAL, "alias"),
+    (dict(causal=-1), RT_EINVAL, "causal"),
+])
+def test_local_validation(lib, kw, code, msg):
+    a = dict(q=FAKE, kk=FAKE, v=FAKE, dtype=1, B=1, H=1, n=64, d=16, window=8, scale=0.25,
+             causal=1, out=ctypes.c_void_p(0x2000))
+    a.update(kw)
+    assert lib.rt_local_attn(a["q"], a["kk"], a["v"], a["dtype"], a["B"], a["H"], a["n"], a["d"],
+                             a["window"], a["scale"], a["causal"], a["out"], None) == code
+    assert msg in _last(lib)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(mu=None), RT_EINVAL, "null"),
+    (dict(q_inv=None), RT_EINVAL, "null"),
+    (dict(kk=FAKE), RT_EINVAL, "both"),
+    (dict(lam=1.5), RT_EINVAL, "lambda"),
+    (dict(lam=-0.1), RT_EINVAL, "lambda"),
+    (dict(lam=float("nan")), RT_EINVAL, "lambda"),
+    (dict(w=100), RT_EINVAL, "exceeds n"),
+])
+def test_centroid_update_validation(lib, kw, code, msg):
+    a = dict(mu=FAKE, q=FAKE, q_inv=FAKE, kk=None, k_inv=None, dtype=1, idx=FAKE, B=1, H=1, n=64,
+             d=16, k=4, w=16, lam=0.999)
+    a.update(kw)
+    assert lib.rt_centroid_update(a["mu"], a["q"], a["q_inv"], a["kk"], a["k_inv"], a["dtype"],
+                                  a["idx"], a["B"], a["H"], a["n"], a["d"], a["k"], a["w"],
+                                  a["lam"], None) == code
+    assert msg in _last(lib)
+
+
+def test_workspace_sizes(lib):
+    B, H, n, d, k, w = 1, 8, 8192, 128, 64, 128
+    assert lib.rt_workspace_bytes(0, B, H, n, d, k, w) == B * H * k * n * 4
+    mask = ((B * H * n * 2 * 4 + 255) // 256) * 256
+    assert lib.rt_workspace_bytes(1, B, H, n, d, k, w) == mask + B * H * k * w * d * 4
+    assert lib.rt_workspace_bytes(2, B, H, n, d, k, w) == 0
+    assert lib.rt_workspace_bytes(3, B, H, n, d, k, w) == 0
+    assert lib.rt_workspace_bytes(9, B, H, n, d, k, w) == ctypes.c_size_t(-1).value
+    assert lib.rt_workspace_bytes(0, 0, H, n, d, k, w) == ctypes.c_size_t(-1).value
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import content_sparse_attention_unit_amd as rt
+    x = torch.zeros(1, 1, 64, 16)
+    with pytest.raises(ValueError):
+        rt.local_attn(x, x, x, 8)

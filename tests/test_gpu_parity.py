@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, on the
+same seeded inputs.
+
+Rules (see tests/_util.py): memberships equal wherever the oracle's top-w
+score margin exceeds 1e-5 and valid elsewhere; attention outputs within
+max-abs 1e-4 (float32) or max-abs 2e-2 and mean-rel 5e-3 (bfloat16);
+centroids within max-abs 1e-5.  Outputs that depend on the membership are
+compared twice: once with the oracle's membership fed to the GPU kernels,
+once end to end on the tokens whose clusters the two sides chose alike.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+from _util import (MU_MAX_ABS, assert_close_out, check_membership, dev_tensor, host,
+                   tokens_touched)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rt():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import content_sparse_attention_unit_amd as m
+    m._load()
+    return m
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def base(**kw):
+    return S.Config(cfg_id=kw.pop("cfg_id", 11), name=kw.pop("name", "case"), **kw)
+
+
+# Small cases: several tiles, ragged tails, every supported d, edge shapes.
+SMALL = {
+    "tiny_f32": S.CONFIGS["tiny"],
+    "tiny_bf16": S.CONFIGS["tiny"].scaled(dtype="bf16", cfg_id=12),
+    "ragged_d64": base(cfg_id=13, dtype="bf16", B=2, R=2, L=2, n=1000, d=64, k=32, w=31,
+                       window=100),
+    "ragged_d128": base(cfg_id=14, dtype="bf16", B=1, R=2, L=1, n=777, d=128, k=6, w=100,
+                        window=129),
+    "d32": base(cfg_id=15, dtype="bf16", B=1, R=3, L=1, n=300, d=32, k=10, w=30, window=33),
+    "d16": base(cfg_id=16, dtype="bf16", B=2, R=1, L=1, n=257, d=16, k=17, w=15, window=64),
+    "dense_k1": base(cfg_id=17, dtype="bf16", B=1, R=2, L=0, n=200, d=64, k=1, w=200, window=0),
+    "w1": base(cfg_id=18, dtype="bf16", B=1, R=1, L=0, n=130, d=64, k=40, w=1, window=0),
+    "w_eq_n": base(cfg_id=19, dtype="bf16", B=1, R=1, L=0, n=128, d=32, k=3, w=128, window=0),
+    "w256_d64": base(cfg_id=20, dtype="bf16", B=1, R=1, L=1, n=1500, d=64, k=5, w=256, window=256),
+    "w512_d32": base(cfg_id=21, dtype="bf16", B=1, R=1, L=0, n=2000, d=32, k=3, w=512, window=0),
+    "w256_d128": base(cfg_id=22, dtype="bf16", B=1, R=1, L=0, n=1100, d=128, k=4, w=256, window=0),
+    "f32_d64": base(cfg_id=23, dtype="f32", B=1, R=2, L=1, n=333, d=64, k=5, w=40, window=50),
+    "f32_d128": base(cfg_id=24, dtype="f32", B=1, R=1, L=1, n=200, d=128, k=3, w=64, window=70),
+    "k_many": base(cfg_id=25, dtype="bf16", B=1, R=1, L=0, n=4096, d=64, k=256, w=16, window=0),
+    "skewed": base(cfg_id=26, dtype="bf16", B=1, R=2, L=0, n=2048, d=64, k=16, w=128, window=0,
+                   skew=True),
+}
+
+
+def run_routed_case(rt, orc, cfg, scale=None, causal=True, check_scores=True):
+    say(f"[case] {cfg}")
+    inp = S.make_inputs(cfg)
+    sc = 1.0 / math.sqrt(cfg.d) if scale is None else scale
+    qk = dev_tensor(inp["qk"])
+    v = dev_tensor(inp["v"])
+    mu = dev_tensor(inp["mu"])
+    qk_val, v_val, mu_val = inp["qk"].value, inp["v"].value, inp["mu"]
+
+    # route
+    inv, idx, scores = rt.route(qk, mu, cfg.w, want_scores=True)
+    torch.cuda.synchronize()
+    inv_o, idx_o, margin_o, scores_o = orc.route(qk_val, mu_val, cfg.w, want_scores=check_scores)
+    np.testing.assert_allclose(host(inv), inv_o, rtol=2e-6)
+    if check_scores:
+        err = np.abs(host(scores) - scores_o).max()
+        assert err <= 2e-6, f"scores max-abs {err:.3e}"
+    gidx = host(idx)
+    differs = check_membership(orc, gidx, idx_o, margin_o, qk_val, mu_val, cfg.w)
+
+    # attention with the oracle's membership
+    idx_o_dev = torch.from_numpy(idx_o).cuda()
+    out, lse = rt.routed_attn(qk, qk, v, idx_o_dev, inv, inv, scale=sc, causal=causal,
+                              want_lse=True)
+    torch.cuda.synchronize()
+    out_o, lse_o, _ = orc.routed_attn(qk_val, qk_val, v_val, idx_o, sc, causal)
+    assert_close_out(host(out), out_o, cfg.dtype, "out")
+    lse_tol = 1e-4 if cfg.dtype == "f32" else 5e-3
+    assert np.abs(host(lse) - lse_o).max() <= lse_tol
+
+    # centroid update with the oracle's membership
+    mu2 = mu.clone()
+    rt.centroid_update_(mu2, qk, inv, idx_o_dev, cfg.lam)
+    torch.cuda.synchronize()
+    mu_o = orc.centroid_update(mu_val, qk_val, qk_val, idx_o, cfg.lam)
+    assert np.abs(host(mu2) - mu_o).max() <= MU_MAX_ABS
+
+    # end to end on the GPU's own membership
+    out_e = rt.routed_attn(qk, qk, v, idx, inv, inv, scale=sc, causal=causal)
+    mu_e = mu.clone()
+    rt.centroid_update_(mu_e, qk, inv, idx, cfg.lam)
+    torch.cuda.synchronize()
+    keep = ~tokens_touched(gidx, idx_o, differs, cfg.n)
+    assert_close_out(host(out_e)[keep], out_o[keep], cfg.dtype, "out end-to-end")
+    same_c = ~differs.any(axis=0)                      # [H, k]: identical for every batch row
+    assert np.abs(host(mu_e)[same_c] - mu_o[same_c]).max(initial=0.0) <= MU_MAX_ABS
+    return dict(inp=inp, qk=qk, v=v, mu=mu, inv=inv, idx=idx, out=out_e, mu_e=mu_e, sc=sc,
+                differs=differs)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_routed_small(rt, orc, name):
+    run_routed_case(rt, orc, SMALL[name])
+
+
+@pytest.mark.parametrize("name", ["ragged_d64", "d32", "tiny_f32"])
+def test_routed_noncausal(rt, orc, name):
+    run_routed_case(rt, orc, SMALL[name], causal=False, check_scores=False)
+
+
+@pytest.mark.parametrize("name", ["ragged_d128", "d16", "f32_d64", "w256_d64"])
+def test_routed_scale_sqrt_d(rt, orc, name):
+    cfg = SMALL[name]
+    run_routed_case(rt, orc, cfg, scale=math.sqrt(cfg.d), check_scores=False)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_distinct_q_and_k(rt, orc, dtype):
+    """Queries and keys from different tensors (each normalised by its own
+    norm) with one membership (the oracle's routing of the queries); the key
+    side of the EMA comes from the key tensor."""
+    cfg = base(cfg_id=30, dtype=dtype, B=2, R=2, L=0, n=600, d=64, k=8, w=70, window=0)
+    say(f"[case] distinct q/k {cfg}")
+    inp = S.make_inputs(cfg)
+    kin = S.normal_tensor(30_000 + 77, inp["qk"].value.shape, dtype)
+    q, kk, v, mu = (dev_tensor(inp["qk"]), dev_tensor(kin), dev_tensor(inp["v"]),
+                    dev_tensor(inp["mu"]))
+    q_inv, idx = rt.route(q, mu, cfg.w)
+    k_inv, _ = rt.route(kk, mu, cfg.w)
+    _, idx_o, margin_o, _ = orc.route(inp["qk"].value, inp["mu"], cfg.w)
+    check_membership(orc, host(idx), idx_o, margin_o, inp["qk"].value, inp["mu"], cfg.w)
+    idx_o_dev = torch.from_numpy(idx_o).cuda()
+    sc = 0.9
+    out = rt.routed_attn(q, kk, v, idx_o_dev, q_inv, k_inv, scale=sc)
+    mu2 = mu.clone()
+    rt.centroid_update_(mu2, q, q_inv, idx_o_dev, 0.7, kk=kk, k_inv=k_inv)
+    torch.cuda.synchronize()
+    out_o, _, _ = orc.routed_attn(inp["qk"].value, kin.value, inp["v"].value, idx_o, sc, True)
+    assert_close_out(host(out), out_o, dtype)
+    mu_o = orc.centroid_update(inp["mu"], inp["qk"].value, kin.value, idx_o, 0.7)
+    assert np.abs(host(mu2) - mu_o).max() <= MU_MAX_ABS
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.5, 1.0])
+def test_centroid_update_lambdas(rt, orc, lam):
+    cfg = SMALL["ragged_d64"]
+    inp = S.make_inputs(cfg)
+    qk, mu = dev_tensor(inp["qk"]), dev_tensor(inp["mu"])
+    inv, idx = rt.route(qk, mu, cfg.w)
+    _, idx_o, _, _ = orc.route(inp["qk"].value, inp["mu"], cfg.w)
+    mu2 = mu.clone()
+    rt.centroid_update_(mu2, qk, inv, torch.from_numpy(idx_o).cuda(), lam)
+    torch.cuda.synchronize()
+    mu_o = orc.centroid_update(inp["mu"], inp["qk"].value, inp["qk"].value, idx_o, lam)
+    assert np.abs(host(mu2) - mu_o).max() <= MU_MAX_ABS
+    if lam == 1.0:
+        assert torch.equal(mu2, mu)
+
+
+def test_unrouted_tokens_are_zero_and_deterministic(rt, orc):
+    cfg = SMALL["ragged_d64"]
+    res = run_routed_case(rt, orc, cfg, check_scores=False)
+    idx = host(res["idx"])
+    out = host(res["out"])
+    for b in range(cfg.B):
+        for h in range(cfg.R):
+            cnt = np.bincount(idx[b, h].ravel(), minlength=cfg.n)
+            assert np.all(out[b, h, cnt == 0] == 0.0)
+            assert np.any(cnt == 0) and np.any(cnt >= 2)
+    # bit-identical repeats
+    qk, v, mu = res["qk"], res["v"], res["mu"]
+    for _ in range(2):
+        inv2, idx2 = rt.route(qk, mu, cfg.w)
+        out2 = rt.routed_attn(qk, qk, v, idx2, inv2, inv2, scale=res["sc"])
+        mu3 = mu.clone()
+        rt.centroid_update_(mu3, qk, inv2, idx2, cfg.lam)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, res["idx"]) and torch.equal(inv2, res["inv"])
+        assert torch.equal(out2, res["out"]) and torch.equal(mu3, res["mu_e"])
+
+
+LOCAL = ["ragged_d64", "ragged_d128", "d32", "d16", "w256_d64", "f32_d64", "f32_d128"]
+
+
+@pytest.mark.parametrize("name", LOCAL)
+@pytest.mark.parametrize("causal", [True, False])
+def test_local_small(rt, orc, name, causal):
+    cfg = SMALL[name]
+    say(f"[case] local {name} causal={causal}")
+    inp = S.make_inputs(cfg)
+    q, kk, v = (dev_tensor(inp[x]) for x in ("q_local", "k_local", "v_local"))
+    sc = 1.0 / math.sqrt(cfg.d)
+    out = rt.local_attn(q, kk, v, cfg.window, scale=sc, causal=causal)
+    torch.cuda.synchronize()
+    out_o = orc.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
+                           cfg.window, sc, causal)
+    assert_close_out(host(out), out_o, cfg.dtype, "local out")
+
+
+@pytest.mark.parametrize("window", [1, 7, 64, 5000])
+def test_local_window_edges(rt, orc, window):
+    cfg = SMALL["ragged_d64"]
+    inp = S.make_inputs(cfg)
+    q, kk, v = (dev_tensor(inp[x]) for x in ("q_local", "k_local", "v_local"))
+    out = rt.local_attn(q, kk, v, window, scale=0.3)
+    torch.cuda.synchronize()
+    out_o = orc.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
+                           window, 0.3, True)
+    assert_close_out(host(out), out_o, cfg.dtype, "local out")
+    if window == 1:
+        assert torch.equal(out, v)
+
+
+# Full-size workloads, in the launch configuration the benchmark times.
+@pytest.mark.parametrize("name", ["routed", "mixed", "long", "stress"])
+def test_full_size_forward(rt, orc, name):
+    cfg = S.CONFIGS[name]
+    res = run_routed_case(rt, orc, cfg, check_scores=False)
+    say(f"[full] {name}: {int(res['differs'].sum())} near-tie clusters differ")
+    if cfg.L > 0:
+        inp = res["inp"]
+        q, kk, v = (dev_tensor(inp[x]) for x in ("q_local", "k_local", "v_local"))
+        out = rt.local_attn(q, kk, v, cfg.window, scale=res["sc"])
+        torch.cuda.synchronize()
+        out_o = orc.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
+                               cfg.window, res["sc"], True)
+        assert_close_out(host(out), out_o, cfg.dtype, "local out")
