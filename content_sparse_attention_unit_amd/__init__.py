@@ -51,8 +51,8 @@ def _load():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     sig = {
         "rt_route": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, Z, P],
-        "rt_routed_attn": [P, P, P, I, P, P, P, I, I, I, I, I, I, F, I, P, P, P, Z, P],
-        "rt_local_attn": [P, P, P, I, I, I, I, I, I, F, I, P, P],
+        "rt_routed_attn": [P, P, P, I, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P, Z, P],
+        "rt_local_attn": [P, P, P, I, I, I, I, I, I, F, I, P, I, P],
         "rt_centroid_update": [P, P, P, P, P, I, P, I, I, I, I, I, I, F, P],
         "rt_routed_attn_bwd": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z,
                                P],
@@ -158,9 +158,10 @@ def route(qk: torch.Tensor, mu: torch.Tensor, w: int, *, want_scores: bool = Fal
 def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                 q_inv: torch.Tensor | None = None, k_inv: torch.Tensor | None = None, *,
                 scale: float | None = None, causal: bool = True, want_lse: bool = False,
-                out=None, lse=None, ws=None):
+                out_dtype: torch.dtype | None = None, out=None, lse=None, ws=None):
     """In-cluster attention scatter-added to token order; returns ``out`` (and
-    ``lse`` when asked).  Pass ``kk is q`` (and ``k_inv is q_inv``) for shared QK."""
+    ``lse`` when asked).  Pass ``kk is q`` (and ``k_inv is q_inv``) for shared QK.
+    ``out_dtype`` (float32 or bfloat16) defaults to the input dtype."""
     lib = _load()
     dev = _gpu(q, kk, v, idx, q_inv, k_inv)
     B, H, n, d = q.shape
@@ -169,28 +170,30 @@ def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.T
         raise TypeError("idx must be int32")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     if want_lse and lse is None:
         lse = torch.empty((B, H, k, w), dtype=torch.float32, device=dev)
     ws, _ = _workspace("routed_attn", dev, B, H, n, d, k, w, ws)
     _check(lib.rt_routed_attn(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
                               _ptr(k_inv), _ptr(idx), B, H, n, d, k, w, sc, int(causal),
-                              _ptr(out), _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
-                              _stream(dev)))
+                              _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(dev)))
     return (out, lse) if want_lse else out
 
 
 def local_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, window: int, *,
-               scale: float | None = None, causal: bool = True, out=None):
-    """Sliding-window attention over [B,H,n,d] tensors."""
+               scale: float | None = None, causal: bool = True,
+               out_dtype: torch.dtype | None = None, out=None):
+    """Sliding-window attention over [B,H,n,d] tensors; ``out_dtype`` (float32 or
+    bfloat16) defaults to the input dtype."""
     lib = _load()
     dev = _gpu(q, kk, v)
     B, H, n, d = q.shape
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
     _check(lib.rt_local_attn(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), B, H, n, d, int(window),
-                             sc, int(causal), _ptr(out), _stream(dev)))
+                             sc, int(causal), _ptr(out), _dtype_code(out), _stream(dev)))
     return out
 
 

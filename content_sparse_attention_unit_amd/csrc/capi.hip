@@ -53,13 +53,18 @@ rt_status check_clusters(const char* fn, int n, int k, int w) {
 
 size_t route_ws(int B, int H, int n, int k) { return (size_t)B * H * k * n * sizeof(float); }
 
-size_t attn_ws_mask(int B, int H, int n, int k) {
-    return align256((size_t)B * H * n * rt::mask_words(k) * sizeof(uint32_t));
+// rt_routed_attn workspace: cnt [B*H*n] u32 | list [B*H*n][k] i32 | part [B*H*k*w][d] f32
+size_t attn_ws_cnt(int B, int H, int n) { return align256((size_t)B * H * n * sizeof(uint32_t)); }
+
+size_t attn_ws_list(int B, int H, int n, int k) {
+    return align256((size_t)B * H * n * k * sizeof(int32_t));
 }
 
 size_t attn_ws(int B, int H, int n, int d, int k, int w) {
-    return attn_ws_mask(B, H, n, k) + (size_t)B * H * k * w * d * sizeof(float);
+    return attn_ws_cnt(B, H, n) + attn_ws_list(B, H, n, k) + (size_t)B * H * k * w * d * sizeof(float);
 }
+
+bool out_dtype_ok(int t) { return t == RT_F32 || t == RT_BF16; }
 
 }  // namespace
 
@@ -124,7 +129,7 @@ rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int
 rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype,
                          const float* q_inv, const float* k_inv, const int32_t* idx, int B, int H,
                          int n, int d, int k, int w, float scale, int causal, void* out,
-                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+                         int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_routed_attn";
     g_err[0] = 0;
     if (!q || !kk || !v || !idx || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
@@ -137,6 +142,8 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
     if (out == q || out == kk || out == v) return fail(RT_EINVAL, "%s: out aliases an input", fn);
     if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
     if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
+    if (!out_dtype_ok(out_dtype))
+        return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
     const bool shared = (q == kk) && (q_inv == k_inv);
     const int wmax = rt::max_cluster_rows(dtype, d, shared);
     if (w > wmax)
@@ -146,23 +153,25 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
     if (ws == nullptr || ws_bytes < need)
         return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
-    uint32_t* mask = static_cast<uint32_t*>(ws);
-    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + attn_ws_mask(B, H, n, k));
+    char* base = static_cast<char*>(ws);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(base);
+    int32_t* list = reinterpret_cast<int32_t*>(base + attn_ws_cnt(B, H, n));
+    float* part = reinterpret_cast<float*>(base + attn_ws_cnt(B, H, n) + attn_ws_list(B, H, n, k));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = B * H;
-    hipError_t e = rt::launch_membership(idx, BH, n, k, w, mask, s);
+    hipError_t e = rt::launch_membership(idx, BH, n, k, w, cnt, list, s);
     if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, mask, BH, n, d, k, w, scale,
-                                causal, out, lse, part, s);
+    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, d, k, w, scale,
+                                causal, out, out_dtype, lse, part, s);
     if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_combine(mask, idx, part, dtype, BH, n, d, k, w, out, s);
+    e = rt::launch_combine(cnt, list, part, out_dtype, BH, n, d, k, w, out, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }
 
 rt_status rt_local_attn(const void* q, const void* kk, const void* v, int dtype, int B, int H,
                         int n, int d, int window, float scale, int causal, void* out,
-                        void* stream) {
+                        int out_dtype, void* stream) {
     static const char* fn = "rt_local_attn";
     g_err[0] = 0;
     if (!q || !kk || !v || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
@@ -172,8 +181,10 @@ rt_status rt_local_attn(const void* q, const void* kk, const void* v, int dtype,
     if (out == q || out == kk || out == v) return fail(RT_EINVAL, "%s: out aliases an input", fn);
     if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
     if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
+    if (!out_dtype_ok(out_dtype))
+        return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
     hipError_t e = rt::launch_local_attn(q, kk, v, dtype, B * H, n, d, window, scale, causal, out,
-                                         static_cast<hipStream_t>(stream));
+                                         out_dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

@@ -8,59 +8,66 @@
 // attention is the ordinary autoregressive softmax attention of §3: member s
 // is visible to member r when its original position is not later.
 //
-// Kernels
-//   membership_kernel   per (batch, head, token chunk): a k-bit membership
-//                       mask per token, built in LDS from the idx rows.
+// Kernels (in launch order)
+//   zero_u32_kernel     clears the per-token membership counters.
+//   membership_kernel   one thread per membership (c, r): bumps the token's
+//                       counter and appends c*w + r to the token's list.  The
+//                       list order is arbitrary; readers sort it.
 //   cluster_attn_bf16   one workgroup per cluster.  The w member rows of the
 //                       keys (raw bf16) and of the values (transposed) are
-//                       gathered into LDS once; each wave takes 16-row query
-//                       blocks in a zig-zag order that balances the causal
-//                       triangle, computes S^T = K Q^T with
-//                       v_mfma_f32_16x16x32_bf16 (so each lane owns one query
-//                       and the row statistics are per lane), applies the
-//                       inverse norms and the scale in fp32, runs an online
-//                       softmax over 64-key chunks, and accumulates
-//                       O^T = V^T P^T with the same MFMA.
+//                       gathered into LDS once, with every load of a thread
+//                       issued before the first LDS store; each wave takes
+//                       16-row query blocks in a zig-zag order that balances
+//                       the causal triangle, computes S^T = K Q^T with
+//                       v_mfma_f32_16x16x32_bf16 (each lane owns one query,
+//                       so row statistics are per lane), applies the inverse
+//                       norms and the scale in fp32, runs an online softmax
+//                       over 64-key chunks and accumulates O^T = V^T P^T with
+//                       the same MFMA.  A row whose token belongs to this
+//                       cluster only is written straight to `out`; otherwise
+//                       the fp32 row goes to the partial buffer.
 //   cluster_attn_f32    a plain vector-ALU variant for float32 inputs.
 //   combine_kernel      per token: 0 if no cluster holds it; the sum of its
-//                       float32 partial rows in ascending centroid order if
-//                       several do.  A token held by exactly one cluster is
-//                       written directly by the attention kernel.
+//                       fp32 partial rows in ascending centroid order if
+//                       several do (deterministic); nothing if one does.
 #include "rt_common.hpp"
 #include "rt_internal.hpp"
 
 namespace rt {
 namespace {
 
-constexpr int kMaskLdsWords = 8192;  // 32 KB of membership bits per workgroup
-
-__global__ __launch_bounds__(256) void membership_kernel(const int32_t* __restrict__ idx, int n,
-                                                         int k, int w, int KW, int chunk,
-                                                         uint32_t* __restrict__ mask) {
-    __shared__ uint32_t lm[kMaskLdsWords];
-    const int bh = blockIdx.y;
-    const int t0 = blockIdx.x * chunk;
-    const int tn = min(chunk, n - t0);
-    for (int e = threadIdx.x; e < tn * KW; e += 256) lm[e] = 0u;
-    __syncthreads();
-    const int32_t* ib = idx + (long)bh * k * w;
-    const int kw = k * w;
-    for (int e = threadIdx.x; e < kw; e += 256) {
-        const int t = ib[e];
-        if (t >= t0 && t < t0 + tn) {
-            const int c = e / w;
-            atomicOr(&lm[(t - t0) * KW + (c >> 5)], 1u << (c & 31));
-        }
-    }
-    __syncthreads();
-    uint32_t* mb = mask + ((long)bh * n + t0) * KW;
-    for (int e = threadIdx.x; e < tn * KW; e += 256) mb[e] = lm[e];
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, long count) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < count) p[i] = 0u;
 }
 
-__device__ __forceinline__ int popcount_mask(const uint32_t* m, int KW) {
-    int c = 0;
-    for (int i = 0; i < KW; ++i) c += __popc(m[i]);
-    return c;
+// grid (ceil(w / 256), k, BH)
+__global__ __launch_bounds__(256) void membership_kernel(const int32_t* __restrict__ idx, int n,
+                                                         int k, int w,
+                                                         uint32_t* __restrict__ cnt,
+                                                         int32_t* __restrict__ list) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    const int c = blockIdx.y, bh = blockIdx.z;
+    if (r >= w) return;
+    const int t = idx[((long)bh * k + c) * w + r];
+    if (t < 0 || t >= n) return;
+    const long tok = (long)bh * n + t;
+    const uint32_t slot = atomicAdd(&cnt[tok], 1u);
+    if (slot < (uint32_t)k) list[tok * k + slot] = c * w + r;
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<u16>(u16* dst, float a, float b, float c, float d) {
+    uint2 pk;
+    pk.x = pack2(f2bf(a), f2bf(b));
+    pk.y = pack2(f2bf(c), f2bf(d));
+    *reinterpret_cast<uint2*>(dst) = pk;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
 }
 
 template <int D, int WMAX, bool SHARED>
@@ -71,14 +78,20 @@ struct AttnCfg {
     static constexpr int NS = DP / 32;          // MFMA k-steps over d
     static constexpr int NJ = D / 16;           // 16-wide output column blocks
     static constexpr int QROWS = SHARED ? 1 : WMAX;
+    static constexpr int NW = WMAX <= 32 ? 1 : (WMAX <= 64 ? 2 : 4);  // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int CPR = DP / 8;          // 16-byte chunks per padded key row
+    static constexpr int XPT = (WMAX * CPR + NT - 1) / NT;         // key chunks per thread
+    static constexpr int DCH = D / 8;           // 16-byte chunks per value row
+    static constexpr int VPT = ((WMAX / 2) * DCH + NT - 1) / NT;   // value row-pair chunks per thread
 };
 
-template <int D, int WMAX, bool SHARED>
-__global__ __launch_bounds__(256) void cluster_attn_bf16_kernel(
+template <int D, int WMAX, bool SHARED, typename OutT>
+__global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kk, const u16* __restrict__ v,
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
-    int KW, float scale, int causal, u16* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ cnt, int n, int k, int w,
+    float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part) {
     using C = AttnCfg<D, WMAX, SHARED>;
     __shared__ __attribute__((aligned(16))) u16 lx[WMAX * C::LDX];
@@ -91,12 +104,11 @@ __global__ __launch_bounds__(256) void cluster_attn_bf16_kernel(
     __shared__ int lsingle[WMAX]; // 1 when exactly one cluster holds the token
 
     const int cl = blockIdx.x, bh = blockIdx.y;
-    const int nthr = blockDim.x;
     const long tokbase = (long)bh * n;
     const long rowbase = ((long)bh * k + cl) * w;
     const int32_t* irow = idx + rowbase;
 
-    for (int r = threadIdx.x; r < WMAX; r += nthr) {
+    for (int r = threadIdx.x; r < WMAX; r += C::NT) {
         int pos = -1, posc = 0, single = 0;
         float ik = 0.f, iq = 0.f;
         if (r < w) {
@@ -104,7 +116,7 @@ __global__ __launch_bounds__(256) void cluster_attn_bf16_kernel(
             posc = clamp_pos(raw, n);
             if (raw >= 0 && raw < n) {
                 pos = raw;
-                single = popcount_mask(mask + (tokbase + raw) * KW, KW) == 1;
+                single = cnt[tokbase + raw] == 1u;
             }
             ik = k_inv ? k_inv[tokbase + posc] : 1.f;
             iq = q_inv ? q_inv[tokbase + posc] : 1.f;
@@ -117,47 +129,71 @@ __global__ __launch_bounds__(256) void cluster_attn_bf16_kernel(
     }
     __syncthreads();
 
-    // Gather the member rows (padding rows are zero).
-    constexpr int CPR = C::DP / 8;
-    for (int e = threadIdx.x; e < WMAX * CPR; e += nthr) {
-        const int r = e / CPR, ch = e % CPR;
-        uint4 xk = zero_u4(), xq = zero_u4();
-        if (r < w && 8 * ch < D) {
-            const long off = (tokbase + lposc[r]) * D + 8 * ch;
-            xk = *reinterpret_cast<const uint4*>(kk + off);
-            if (!SHARED) xq = *reinterpret_cast<const uint4*>(q + off);
-        }
-        *reinterpret_cast<uint4*>(&lx[r * C::LDX + 8 * ch]) = xk;
-        if (!SHARED) *reinterpret_cast<uint4*>(&lq[r * C::LDX + 8 * ch]) = xq;
-    }
-    constexpr int DCH = D / 8;
-    for (int e = threadIdx.x; e < (WMAX / 2) * DCH; e += nthr) {
-        const int rp = e / DCH, ch = e % DCH;
-        const int r0 = 2 * rp, r1 = r0 + 1;
-        uint4 a = zero_u4(), b = zero_u4();
-        if (r0 < w) a = *reinterpret_cast<const uint4*>(v + (tokbase + lposc[r0]) * D + 8 * ch);
-        if (r1 < w) b = *reinterpret_cast<const uint4*>(v + (tokbase + lposc[r1]) * D + 8 * ch);
-        const uint32_t* aw = reinterpret_cast<const uint32_t*>(&a);
-        const uint32_t* bw = reinterpret_cast<const uint32_t*>(&b);
+    // Gather the member rows (padding rows are zero): all loads first.
+    {
+        uint4 xk[C::XPT], xq[SHARED ? 1 : C::XPT];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const int j = 8 * ch + 2 * e2;
-            *reinterpret_cast<uint32_t*>(&lvt[j * C::LDV + r0]) =
-                (aw[e2] & 0xffffu) | (bw[e2] << 16);
-            *reinterpret_cast<uint32_t*>(&lvt[(j + 1) * C::LDV + r0]) =
-                (aw[e2] >> 16) | (bw[e2] & 0xffff0000u);
+        for (int it = 0; it < C::XPT; ++it) {
+            const int e = threadIdx.x + it * C::NT;
+            const int r = e / C::CPR, ch = e % C::CPR;
+            xk[it] = zero_u4();
+            if (!SHARED) xq[it] = zero_u4();
+            if (r < w && 8 * ch < D) {
+                const long off = (tokbase + lposc[r]) * D + 8 * ch;
+                xk[it] = *reinterpret_cast<const uint4*>(kk + off);
+                if (!SHARED) xq[it] = *reinterpret_cast<const uint4*>(q + off);
+            }
+        }
+        uint4 va[C::VPT], vb[C::VPT];
+#pragma unroll
+        for (int it = 0; it < C::VPT; ++it) {
+            const int e = threadIdx.x + it * C::NT;
+            const int rp = e / C::DCH, ch = e % C::DCH;
+            const int r0 = 2 * rp;
+            va[it] = zero_u4();
+            vb[it] = zero_u4();
+            if (r0 < w) va[it] = *reinterpret_cast<const uint4*>(v + (tokbase + lposc[r0]) * D + 8 * ch);
+            if (r0 + 1 < w)
+                vb[it] = *reinterpret_cast<const uint4*>(v + (tokbase + lposc[r0 + 1]) * D + 8 * ch);
+        }
+#pragma unroll
+        for (int it = 0; it < C::XPT; ++it) {
+            const int e = threadIdx.x + it * C::NT;
+            if (e < WMAX * C::CPR) {
+                const int r = e / C::CPR, ch = e % C::CPR;
+                *reinterpret_cast<uint4*>(&lx[r * C::LDX + 8 * ch]) = xk[it];
+                if (!SHARED) *reinterpret_cast<uint4*>(&lq[r * C::LDX + 8 * ch]) = xq[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < C::VPT; ++it) {
+            const int e = threadIdx.x + it * C::NT;
+            if (e < (WMAX / 2) * C::DCH) {
+                const int rp = e / C::DCH, ch = e % C::DCH;
+                const int r0 = 2 * rp;
+                const uint32_t* aw = reinterpret_cast<const uint32_t*>(&va[it]);
+                const uint32_t* bw = reinterpret_cast<const uint32_t*>(&vb[it]);
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int j = 8 * ch + 2 * e2;
+                    *reinterpret_cast<uint32_t*>(&lvt[j * C::LDV + r0]) =
+                        (aw[e2] & 0xffffu) | (bw[e2] << 16);
+                    *reinterpret_cast<uint32_t*>(&lvt[(j + 1) * C::LDV + r0]) =
+                        (aw[e2] >> 16) | (bw[e2] & 0xffff0000u);
+                }
+            }
         }
     }
     __syncthreads();
 
-    const int lane = lane_id(), wv = threadIdx.x >> 6, NW = nthr >> 6;
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const int nqb = (w + 15) / 16;
     const float sl2 = scale * 1.4426950408889634f;  // logits in log2 units
     const u16* qsrc = SHARED ? lx : lq;
 
-    for (int round = 0; round * NW < nqb; ++round) {
-        const int qb = round * NW + ((round & 1) ? (NW - 1 - wv) : wv);
+    for (int round = 0; round * C::NW < nqb; ++round) {
+        const int qb = round * C::NW + ((round & 1) ? (C::NW - 1 - wv) : wv);
         if (qb >= nqb) continue;
         const int qrow = qb * 16 + r16;
         uint4 qreg[C::NS];
@@ -245,20 +281,17 @@ __global__ __launch_bounds__(256) void cluster_attn_bf16_kernel(
             const int t = lpos[qrow];
             if (t >= 0) {
                 if (lsingle[qrow]) {
-                    u16* dst = out + (tokbase + t) * D + 4 * g;
+                    OutT* dst = out + (tokbase + t) * D + 4 * g;
 #pragma unroll
-                    for (int jb = 0; jb < C::NJ; ++jb) {
-                        uint2 pk;
-                        pk.x = pack2(f2bf(o[jb][0] * rz), f2bf(o[jb][1] * rz));
-                        pk.y = pack2(f2bf(o[jb][2] * rz), f2bf(o[jb][3] * rz));
-                        *reinterpret_cast<uint2*>(dst + 16 * jb) = pk;
-                    }
+                    for (int jb = 0; jb < C::NJ; ++jb)
+                        store4<OutT>(dst + 16 * jb, o[jb][0] * rz, o[jb][1] * rz, o[jb][2] * rz,
+                                     o[jb][3] * rz);
                 } else {
                     float* dst = part + (rowbase + qrow) * D + 4 * g;
 #pragma unroll
                     for (int jb = 0; jb < C::NJ; ++jb)
-                        *reinterpret_cast<float4*>(dst + 16 * jb) =
-                            make_float4(o[jb][0] * rz, o[jb][1] * rz, o[jb][2] * rz, o[jb][3] * rz);
+                        store4<float>(dst + 16 * jb, o[jb][0] * rz, o[jb][1] * rz, o[jb][2] * rz,
+                                      o[jb][3] * rz);
                 }
             }
         }
@@ -266,12 +299,12 @@ __global__ __launch_bounds__(256) void cluster_attn_bf16_kernel(
 }
 
 // float32 inputs: one wave per cluster row, vector ALU only.
-template <int D>
+template <int D, typename OutT>
 __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kk, const float* __restrict__ v,
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
-    int KW, float scale, int causal, float* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ cnt, int n, int k, int w,
+    float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part) {
     __shared__ float lg[1024];
     __shared__ float lqrow[D];
@@ -308,7 +341,7 @@ __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
     __syncthreads();
     const bool valid = raw >= 0 && raw < n;
-    const bool single = valid && popcount_mask(mask + (tokbase + raw) * KW, KW) == 1;
+    const bool single = valid && cnt[tokbase + raw] == 1u;
     for (int i = lane; i < D; i += 64) {
         float acc = 0.f;
         if (z > 0.f) {
@@ -317,79 +350,70 @@ __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
             acc /= z;
         }
         if (valid) {
-            if (single) out[(tokbase + raw) * D + i] = acc;
+            if (single) Elem<OutT>::store(out, (tokbase + raw) * D + i, acc);
             else part[(rowbase + r) * D + i] = acc;
         }
     }
     if (lane == 0 && lse != nullptr) lse[rowbase + r] = (z > 0.f) ? m + logf(z) : -INFINITY;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ mask,
-                                                      const int32_t* __restrict__ idx,
+// One thread per (token, 4 output dims).  The token's list entries c*w + r
+// are visited in increasing order (selection over the short list), so the
+// sum runs in ascending centroid order whatever order the list was filled in.
+template <typename OutT>
+__global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ cnt,
+                                                      const int32_t* __restrict__ list,
                                                       const float* __restrict__ part, long BHn,
-                                                      int n, int D, int k, int w, int KW,
-                                                      T* __restrict__ out) {
+                                                      int n, int D, int k, int w,
+                                                      OutT* __restrict__ out) {
     const int DG = D / 4;
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
     const long tok = gid / DG;
     if (tok >= BHn) return;
     const int dg = (int)(gid % DG);
-    const uint32_t* mrow = mask + tok * KW;
-    int cnt = 0;
-    for (int i = 0; i < KW; ++i) cnt += __popc(mrow[i]);
-    if (cnt == 1) return;
-    const int bh = (int)(tok / n), t = (int)(tok % n);
+    const uint32_t c_tok = cnt[tok];
+    if (c_tok == 1u) return;
+    const int m = (int)min(c_tok, (uint32_t)k);
+    const long bh = tok / n;
+    const int32_t* lst = list + tok * k;
+    const float* pbase = part + bh * (long)k * w * D + 4 * dg;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int wi = 0; wi < KW && cnt > 1; ++wi) {
-        uint32_t bits = mrow[wi];
-        while (bits) {
-            const int c = 32 * wi + __ffs(bits) - 1;
-            bits &= bits - 1u;
-            const int32_t* ir = idx + ((long)bh * k + c) * w;
-            int lo = 0, hi = w;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (ir[mid] < t) lo = mid + 1;
-                else hi = mid;
-            }
-            if (lo < w && ir[lo] == t) {
-                const float4 p =
-                    *reinterpret_cast<const float4*>(part + (((long)bh * k + c) * w + lo) * D + 4 * dg);
-                acc.x += p.x;
-                acc.y += p.y;
-                acc.z += p.z;
-                acc.w += p.w;
-            }
+    int prev = -1;
+    for (int j = 0; j < m; ++j) {
+        int best = 0x7fffffff;
+        for (int i = 0; i < m; ++i) {
+            const int e = lst[i];
+            if (e > prev && e < best) best = e;
         }
+        prev = best;
+        const float4 p = *reinterpret_cast<const float4*>(pbase + (long)best * D);
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
     }
-    T* dst = out + tok * D + 4 * dg;
-    Elem<T>::store(dst, 0, acc.x);
-    Elem<T>::store(dst, 1, acc.y);
-    Elem<T>::store(dst, 2, acc.z);
-    Elem<T>::store(dst, 3, acc.w);
+    store4<OutT>(out + tok * D + 4 * dg, acc.x, acc.y, acc.z, acc.w);
 }
 
-template <int D, int WMAX, bool SHARED>
+template <int D, int WMAX, bool SHARED, typename OutT>
 void launch_bf16(const void* q, const void* kk, const void* v, const float* q_inv,
-                 const float* k_inv, const int32_t* idx, const uint32_t* mask, int BH, int n,
+                 const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n,
                  int k, int w, float scale, int causal, void* out, float* lse, float* part,
                  hipStream_t s) {
-    const int nqb = (w + 15) / 16;
-    int nw = nqb / 2;
-    nw = nw < 1 ? 1 : (nw > 4 ? 4 : nw);
-    hipLaunchKernelGGL((cluster_attn_bf16_kernel<D, WMAX, SHARED>), dim3(k, BH), dim3(64 * nw), 0,
-                       s, (const u16*)q, (const u16*)kk, (const u16*)v, q_inv, k_inv, idx, mask,
-                       n, k, w, mask_words(k), scale, causal, (u16*)out, lse, part);
+    using C = AttnCfg<D, WMAX, SHARED>;
+    hipLaunchKernelGGL((cluster_attn_bf16_kernel<D, WMAX, SHARED, OutT>), dim3(k, BH),
+                       dim3(C::NT), 0, s, (const u16*)q, (const u16*)kk, (const u16*)v, q_inv,
+                       k_inv, idx, cnt, n, k, w, scale, causal, (OutT*)out, lse, part);
 }
 
-template <int D, bool SHARED>
-hipError_t dispatch_w(const void* q, const void* kk, const void* v, const float* q_inv,
-                      const float* k_inv, const int32_t* idx, const uint32_t* mask, int BH, int n,
-                      int k, int w, float scale, int causal, void* out, float* lse, float* part,
-                      hipStream_t s) {
-#define RT_LAUNCH(WM) \
-    launch_bf16<D, WM, SHARED>(q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, scale, causal, out, lse, part, s)
+template <int D, bool SHARED, typename OutT>
+void dispatch_w(const void* q, const void* kk, const void* v, const float* q_inv,
+                const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n, int k,
+                int w, float scale, int causal, void* out, float* lse, float* part,
+                hipStream_t s) {
+#define RT_LAUNCH(WM)                                                                          \
+    launch_bf16<D, WM, SHARED, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale,     \
+                                     causal, out, lse, part, s)
     if (w <= 32) RT_LAUNCH(32);
     else if (w <= 64) RT_LAUNCH(64);
     else if (w <= 128) RT_LAUNCH(128);
@@ -402,17 +426,46 @@ hipError_t dispatch_w(const void* q, const void* kk, const void* v, const float*
         }
     }
 #undef RT_LAUNCH
-    return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename OutT>
 void launch_f32(const void* q, const void* kk, const void* v, const float* q_inv,
-                const float* k_inv, const int32_t* idx, const uint32_t* mask, int BH, int n, int k,
+                const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n, int k,
                 int w, float scale, int causal, void* out, float* lse, float* part,
                 hipStream_t s) {
-    hipLaunchKernelGGL(cluster_attn_f32_kernel<D>, dim3(w, k, BH), dim3(64), 0, s,
+    hipLaunchKernelGGL((cluster_attn_f32_kernel<D, OutT>), dim3(w, k, BH), dim3(64), 0, s,
                        (const float*)q, (const float*)kk, (const float*)v, q_inv, k_inv, idx,
-                       mask, n, k, w, mask_words(k), scale, causal, (float*)out, lse, part);
+                       cnt, n, k, w, scale, causal, (OutT*)out, lse, part);
+}
+
+template <int D, typename OutT>
+void launch_d(const void* q, const void* kk, const void* v, int dtype, const float* q_inv,
+              const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n, int k,
+              int w, float scale, int causal, void* out, float* lse, float* part,
+              hipStream_t s) {
+    if (dtype == 0) {
+        launch_f32<D, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out,
+                            lse, part, s);
+    } else if (q == kk && q_inv == k_inv) {
+        dispatch_w<D, true, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal,
+                                  out, lse, part, s);
+    } else {
+        dispatch_w<D, false, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal,
+                                   out, lse, part, s);
+    }
+}
+
+template <typename OutT>
+void launch_outt(const void* q, const void* kk, const void* v, int dtype, const float* q_inv,
+                 const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n,
+                 int d, int k, int w, float scale, int causal, void* out, float* lse,
+                 float* part, hipStream_t s) {
+    switch (d) {
+        case 16: launch_d<16, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
+        case 32: launch_d<32, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
+        case 64: launch_d<64, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
+        default: launch_d<128, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
+    }
 }
 
 }  // namespace
@@ -423,53 +476,42 @@ int max_cluster_rows(int dtype, int d, bool shared_qk) {
     return d == 128 ? 128 : 256;
 }
 
-hipError_t launch_membership(const int32_t* idx, int BH, int n, int k, int w, uint32_t* mask,
-                             hipStream_t s) {
-    const int KW = mask_words(k);
-    const int chunk = kMaskLdsWords / KW;
-    hipLaunchKernelGGL(membership_kernel, dim3((n + chunk - 1) / chunk, BH), dim3(256), 0, s, idx,
-                       n, k, w, KW, chunk, mask);
+hipError_t launch_membership(const int32_t* idx, int BH, int n, int k, int w, uint32_t* cnt,
+                             int32_t* list, hipStream_t s) {
+    const long count = (long)BH * n;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
+                       cnt, count);
+    hipLaunchKernelGGL(membership_kernel, dim3((w + 255) / 256, k, BH), dim3(256), 0, s, idx, n,
+                       k, w, cnt, list);
     return hipGetLastError();
 }
 
 hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int dtype,
                                const float* q_inv, const float* k_inv, const int32_t* idx,
-                               const uint32_t* mask, int BH, int n, int d, int k, int w,
-                               float scale, int causal, void* out, float* lse, float* part,
-                               hipStream_t s) {
-    if (dtype == 0) {
-        switch (d) {
-            case 16: launch_f32<16>(q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, scale, causal, out, lse, part, s); break;
-            case 32: launch_f32<32>(q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, scale, causal, out, lse, part, s); break;
-            case 64: launch_f32<64>(q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, scale, causal, out, lse, part, s); break;
-            default: launch_f32<128>(q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, scale, causal, out, lse, part, s); break;
-        }
-        return hipGetLastError();
-    }
-    const bool shared = (q == kk) && (q_inv == k_inv);
-#define RT_DISPATCH(DD)                                                                                 \
-    return shared ? dispatch_w<DD, true>(q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, scale, causal, out, lse, part, s) \
-                  : dispatch_w<DD, false>(q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, scale, causal, out, lse, part, s)
-    switch (d) {
-        case 16: RT_DISPATCH(16);
-        case 32: RT_DISPATCH(32);
-        case 64: RT_DISPATCH(64);
-        default: RT_DISPATCH(128);
-    }
-#undef RT_DISPATCH
+                               const uint32_t* cnt, int BH, int n, int d, int k, int w,
+                               float scale, int causal, void* out, int out_dtype, float* lse,
+                               float* part, hipStream_t s) {
+    if (out_dtype == 1)
+        launch_outt<u16>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, d, k, w, scale, causal,
+                         out, lse, part, s);
+    else
+        launch_outt<float>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, d, k, w, scale,
+                           causal, out, lse, part, s);
+    return hipGetLastError();
 }
 
-hipError_t launch_combine(const uint32_t* mask, const int32_t* idx, const float* part, int dtype,
-                          int BH, int n, int d, int k, int w, void* out, hipStream_t s) {
+hipError_t launch_combine(const uint32_t* cnt, const int32_t* list, const float* part,
+                          int out_dtype, int BH, int n, int d, int k, int w, void* out,
+                          hipStream_t s) {
     const long BHn = (long)BH * n;
     const long threads = BHn * (d / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
-    if (dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<u16>, grid, dim3(256), 0, s, mask, idx, part, BHn, n, d,
-                           k, w, mask_words(k), (u16*)out);
+    if (out_dtype == 1)
+        hipLaunchKernelGGL(combine_kernel<u16>, grid, dim3(256), 0, s, cnt, list, part, BHn, n, d,
+                           k, w, (u16*)out);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, mask, idx, part, BHn, n,
-                           d, k, w, mask_words(k), (float*)out);
+        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, cnt, list, part, BHn, n,
+                           d, k, w, (float*)out);
     return hipGetLastError();
 }
 

@@ -21,165 +21,242 @@ namespace {
 template <int D>
 struct LocalCfg {
     static constexpr int DP = D < 32 ? 32 : D;
-    static constexpr int LDX = DP + 8;
-    static constexpr int KT = 64;
-    static constexpr int LDV = KT + 8;
+    static constexpr int LDX = DP + 8;           // key row stride in LDS (bf16)
+    static constexpr int KT = 64;                // keys per tile
+    static constexpr int LDV = KT + 8;           // transposed value row stride (bf16)
     static constexpr int NS = DP / 32;
     static constexpr int NJ = D / 16;
+    static constexpr int QB = 2;                 // 16-query blocks per wave
+    static constexpr int QT = 4 * 16 * QB;       // queries per workgroup (4 waves)
+    static constexpr int CPR = DP / 8;
+    static constexpr int DCH = D / 8;
+    static constexpr int KPT = (KT * CPR) / 256;         // key chunks per thread per tile
+    static constexpr int VITEMS = (KT / 2) * DCH;         // value row-pair chunks per tile
+    static constexpr int VPT = (VITEMS + 255) / 256;       // ... per thread
+};
+
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<u16>(u16* dst, float a, float b, float c, float d) {
+    uint2 pk;
+    pk.x = pack2(f2bf(a), f2bf(b));
+    pk.y = pack2(f2bf(c), f2bf(d));
+    *reinterpret_cast<uint2*>(dst) = pk;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
+template <int D>
+struct TileRegs {
+    uint4 k[LocalCfg<D>::KPT > 0 ? LocalCfg<D>::KPT : 1];
+    uint4 va[LocalCfg<D>::VPT > 0 ? LocalCfg<D>::VPT : 1];
+    uint4 vb[LocalCfg<D>::VPT > 0 ? LocalCfg<D>::VPT : 1];
 };
 
 template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& tr, const u16* __restrict__ kk,
+                                          const u16* __restrict__ v, long base, int n, int kt) {
+    using C = LocalCfg<D>;
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+        const int e = threadIdx.x + 256 * it;
+        const int r = e / C::CPR, ch = e % C::CPR;
+        const int j = kt + r;
+        tr.k[it] = (j < n && 8 * ch < D) ? *reinterpret_cast<const uint4*>(kk + (base + j) * D + 8 * ch)
+                                         : zero_u4();
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+        const int e = threadIdx.x + 256 * it;
+        const int rp = e / C::DCH, ch = e % C::DCH;
+        const int j0 = (e < C::VITEMS) ? kt + 2 * rp : n;
+        tr.va[it] = (j0 < n) ? *reinterpret_cast<const uint4*>(v + (base + j0) * D + 8 * ch) : zero_u4();
+        tr.vb[it] = (j0 + 1 < n) ? *reinterpret_cast<const uint4*>(v + (base + j0 + 1) * D + 8 * ch)
+                                 : zero_u4();
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& tr, u16* lk, u16* lvt) {
+    using C = LocalCfg<D>;
+#pragma unroll
+    for (int it = 0; it < C::KPT; ++it) {
+        const int e = threadIdx.x + 256 * it;
+        const int r = e / C::CPR, ch = e % C::CPR;
+        *reinterpret_cast<uint4*>(&lk[r * C::LDX + 8 * ch]) = tr.k[it];
+    }
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+        const int e = threadIdx.x + 256 * it;
+        if (e >= C::VITEMS) continue;
+        const int rp = e / C::DCH, ch = e % C::DCH;
+        const uint32_t* aw = reinterpret_cast<const uint32_t*>(&tr.va[it]);
+        const uint32_t* bw = reinterpret_cast<const uint32_t*>(&tr.vb[it]);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const int jj = 8 * ch + 2 * e2;
+            *reinterpret_cast<uint32_t*>(&lvt[jj * C::LDV + 2 * rp]) = (aw[e2] & 0xffffu) | (bw[e2] << 16);
+            *reinterpret_cast<uint32_t*>(&lvt[(jj + 1) * C::LDV + 2 * rp]) =
+                (aw[e2] >> 16) | (bw[e2] & 0xffff0000u);
+        }
+    }
+}
+
+template <int D, typename OutT>
 __global__ __launch_bounds__(256) void local_attn_bf16_kernel(const u16* __restrict__ q,
                                                               const u16* __restrict__ kk,
                                                               const u16* __restrict__ v, int n,
                                                               int window, float scale, int causal,
-                                                              u16* __restrict__ out) {
+                                                              OutT* __restrict__ out) {
     using C = LocalCfg<D>;
-    __shared__ __attribute__((aligned(16))) u16 lk[C::KT * C::LDX];
-    __shared__ __attribute__((aligned(16))) u16 lvt[D * C::LDV];
+    static_assert(C::KPT * 256 == C::KT * C::CPR, "key tile must split evenly over 256 threads");
+    __shared__ __attribute__((aligned(16))) u16 lk[2][C::KT * C::LDX];
+    __shared__ __attribute__((aligned(16))) u16 lvt[2][D * C::LDV];
 
     const int bh = blockIdx.y;
-    const int q0 = blockIdx.x * 64;
+    const int q0 = blockIdx.x * C::QT;
     const long base = (long)bh * n;
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
-    const int qw0 = q0 + 16 * wv;      // first query of this wave
-    const int qi = qw0 + r16;          // this lane's query
-
-    uint4 qreg[C::NS];
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) {
-        const int d0 = 32 * s + 8 * g;
-        qreg[s] = (qi < n && d0 < D) ? *reinterpret_cast<const uint4*>(q + (base + qi) * D + d0)
-                                     : zero_u4();
-    }
     const float sl2 = scale * 1.4426950408889634f;
 
-    // Keys needed by the whole workgroup, and by this wave.
+    // This wave's query blocks: rows q0 + 16*(wv + 4*b) + r16, b < QB.
+    uint4 qreg[C::QB][C::NS];
+    int qi[C::QB];
+#pragma unroll
+    for (int b = 0; b < C::QB; ++b) {
+        qi[b] = q0 + 16 * (wv + 4 * b) + r16;
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s) {
+            const int d0 = 32 * s + 8 * g;
+            qreg[b][s] = (qi[b] < n && d0 < D)
+                             ? *reinterpret_cast<const uint4*>(q + (base + qi[b]) * D + d0)
+                             : zero_u4();
+        }
+    }
     const int lo = max(0, q0 - window + 1);
-    const int hi = causal ? min(n - 1, q0 + 63) : min(n - 1, q0 + 63 + window - 1);
-    const int wlo = qw0 - window + 1;
-    const int whi = causal ? qw0 + 15 : qw0 + 15 + window - 1;
+    const int hi = causal ? min(n - 1, q0 + C::QT - 1) : min(n - 1, q0 + C::QT - 1 + window - 1);
 
-    f32x4 o[C::NJ];
+    f32x4 o[C::QB][C::NJ];
+    float m[C::QB], z[C::QB];
 #pragma unroll
-    for (int jb = 0; jb < C::NJ; ++jb) o[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, z = 0.f;
+    for (int b = 0; b < C::QB; ++b) {
+        m[b] = -INFINITY;
+        z[b] = 0.f;
+#pragma unroll
+        for (int jb = 0; jb < C::NJ; ++jb) o[b][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    constexpr int CPR = C::DP / 8;
-    constexpr int DCH = D / 8;
-    for (int kt = lo & ~(C::KT - 1); kt <= hi; kt += C::KT) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < C::KT * CPR; e += 256) {
-            const int r = e / CPR, ch = e % CPR;
-            const int j = kt + r;
-            uint4 x = zero_u4();
-            if (j < n && 8 * ch < D) x = *reinterpret_cast<const uint4*>(kk + (base + j) * D + 8 * ch);
-            *reinterpret_cast<uint4*>(&lk[r * C::LDX + 8 * ch]) = x;
+    const int kt_first = lo & ~(C::KT - 1);
+    TileRegs<D> tr;
+    load_tile<D>(tr, kk, v, base, n, kt_first);
+    store_tile<D>(tr, lk[0], lvt[0]);
+    __syncthreads();
+
+    int buf = 0;
+    for (int kt = kt_first; kt <= hi; kt += C::KT) {
+        const bool more = kt + C::KT <= hi;
+        if (more) load_tile<D>(tr, kk, v, base, n, kt + C::KT);   // in flight during compute
+        const u16* LK = lk[buf];
+        const u16* LV = lvt[buf];
+#pragma unroll
+        for (int b = 0; b < C::QB; ++b) {
+            const int qb0 = q0 + 16 * (wv + 4 * b);        // first query of the block
+            const int blo = qb0 - window + 1;
+            const int bhi = causal ? qb0 + 15 : qb0 + 15 + window - 1;
+            if (kt + C::KT - 1 < blo || kt > bhi) continue;  // wave-uniform skip
+            f32x4 sv[4];
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int key0 = kt + 16 * kb;
+                if (key0 + 15 < blo || key0 > bhi || key0 >= n) {
+                    sv[kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                    continue;
+                }
+                sv[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < C::NS; ++s) {
+                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
+                        &LK[(16 * kb + r16) * C::LDX + 32 * s + 8 * g]));
+                    sv[kb] = mfma16(a, as_bf16x8(qreg[b][s]), sv[kb]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = key0 + 4 * g + i;
+                    const bool ok = j < n && j > qi[b] - window &&
+                                    (causal ? j <= qi[b] : j < qi[b] + window);
+                    sv[kb][i] = ok ? sv[kb][i] * sl2 : -INFINITY;
+                    cmax = fmaxf(cmax, sv[kb][i]);
+                }
+            }
+            cmax = xor_max_16_32(cmax);
+            const float mnew = fmaxf(m[b], cmax);
+            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(m[b] - msafe);
+            z[b] *= alpha;
+#pragma unroll
+            for (int jb = 0; jb < C::NJ; ++jb) o[b][jb] *= alpha;
+            m[b] = mnew;
+
+            u16 pb[4][4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u16 pv = f2bf(__builtin_amdgcn_exp2f(sv[kb][i] - msafe));
+                    pb[kb][i] = pv;
+                    z[b] += bf2f(pv);
+                }
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                uint4 pw;
+                pw.x = pack2(pb[2 * mm][0], pb[2 * mm][1]);
+                pw.y = pack2(pb[2 * mm][2], pb[2 * mm][3]);
+                pw.z = pack2(pb[2 * mm + 1][0], pb[2 * mm + 1][1]);
+                pw.w = pack2(pb[2 * mm + 1][2], pb[2 * mm + 1][3]);
+                if (__ballot((pw.x | pw.y | pw.z | pw.w) != 0u) == 0ull) continue;  // wave-uniform
+                const bf16x8 pbv = as_bf16x8(pw);
+#pragma unroll
+                for (int jb = 0; jb < C::NJ; ++jb) {
+                    const u16* vr = &LV[(16 * jb + r16) * C::LDV + 32 * mm + 4 * g];
+                    const uint2 l2 = *reinterpret_cast<const uint2*>(vr);
+                    const uint2 h2 = *reinterpret_cast<const uint2*>(vr + 16);
+                    o[b][jb] = mfma16(as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y)), pbv, o[b][jb]);
+                }
+            }
         }
-        for (int e = threadIdx.x; e < (C::KT / 2) * DCH; e += 256) {
-            const int rp = e / DCH, ch = e % DCH;
-            const int j0 = kt + 2 * rp;
-            uint4 a = zero_u4(), b = zero_u4();
-            if (j0 < n) a = *reinterpret_cast<const uint4*>(v + (base + j0) * D + 8 * ch);
-            if (j0 + 1 < n) b = *reinterpret_cast<const uint4*>(v + (base + j0 + 1) * D + 8 * ch);
-            const uint32_t* aw = reinterpret_cast<const uint32_t*>(&a);
-            const uint32_t* bw = reinterpret_cast<const uint32_t*>(&b);
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int jj = 8 * ch + 2 * e2;
-                *reinterpret_cast<uint32_t*>(&lvt[jj * C::LDV + 2 * rp]) =
-                    (aw[e2] & 0xffffu) | (bw[e2] << 16);
-                *reinterpret_cast<uint32_t*>(&lvt[(jj + 1) * C::LDV + 2 * rp]) =
-                    (aw[e2] >> 16) | (bw[e2] & 0xffff0000u);
-            }
-        }
-        __syncthreads();
-        if (kt + C::KT - 1 < wlo || kt > whi) continue;  // tile outside this wave's band
-
-        f32x4 sv[4];
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int key0 = kt + 16 * kb;
-            if (key0 + 15 < wlo || key0 > whi || key0 >= n) {
-                sv[kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                continue;
-            }
-            sv[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < C::NS; ++s) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    &lk[(16 * kb + r16) * C::LDX + 32 * s + 8 * g]));
-                sv[kb] = mfma16(a, as_bf16x8(qreg[s]), sv[kb]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = key0 + 4 * g + i;
-                const bool ok = j < n && j > qi - window &&
-                                (causal ? j <= qi : j < qi + window);
-                sv[kb][i] = ok ? sv[kb][i] * sl2 : -INFINITY;
-                cmax = fmaxf(cmax, sv[kb][i]);
-            }
-        }
-        cmax = xor_max_16_32(cmax);
-        const float mnew = fmaxf(m, cmax);
-        const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-        z *= alpha;
-#pragma unroll
-        for (int jb = 0; jb < C::NJ; ++jb) o[jb] *= alpha;
-        m = mnew;
-
-        u16 pb[4][4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u16 pv = f2bf(__builtin_amdgcn_exp2f(sv[kb][i] - msafe));
-                pb[kb][i] = pv;
-                z += bf2f(pv);
-            }
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            uint4 pw;
-            pw.x = pack2(pb[2 * mm][0], pb[2 * mm][1]);
-            pw.y = pack2(pb[2 * mm][2], pb[2 * mm][3]);
-            pw.z = pack2(pb[2 * mm + 1][0], pb[2 * mm + 1][1]);
-            pw.w = pack2(pb[2 * mm + 1][2], pb[2 * mm + 1][3]);
-            if (__ballot((pw.x | pw.y | pw.z | pw.w) != 0u) == 0ull) continue;  // wave-uniform
-            const bf16x8 pbv = as_bf16x8(pw);
-#pragma unroll
-            for (int jb = 0; jb < C::NJ; ++jb) {
-                const u16* vr = &lvt[(16 * jb + r16) * C::LDV + 32 * mm + 4 * g];
-                const uint2 l2 = *reinterpret_cast<const uint2*>(vr);
-                const uint2 h2 = *reinterpret_cast<const uint2*>(vr + 16);
-                o[jb] = mfma16(as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y)), pbv, o[jb]);
-            }
+        if (more) {
+            store_tile<D>(tr, lk[buf ^ 1], lvt[buf ^ 1]);
+            __syncthreads();
+            buf ^= 1;
         }
     }
 
-    const float zt = xor_sum_16_32(z);
-    const float rz = 1.0f / zt;
-    if (qi < n) {
-        u16* dst = out + (base + qi) * D + 4 * g;
 #pragma unroll
-        for (int jb = 0; jb < C::NJ; ++jb) {
-            uint2 pk;
-            pk.x = pack2(f2bf(o[jb][0] * rz), f2bf(o[jb][1] * rz));
-            pk.y = pack2(f2bf(o[jb][2] * rz), f2bf(o[jb][3] * rz));
-            *reinterpret_cast<uint2*>(dst + 16 * jb) = pk;
+    for (int b = 0; b < C::QB; ++b) {
+        const float zt = xor_sum_16_32(z[b]);
+        const float rz = 1.0f / zt;
+        if (qi[b] < n) {
+            OutT* dst = out + (base + qi[b]) * D + 4 * g;
+#pragma unroll
+            for (int jb = 0; jb < C::NJ; ++jb)
+                store4<OutT>(dst + 16 * jb, o[b][jb][0] * rz, o[b][jb][1] * rz, o[b][jb][2] * rz,
+                             o[b][jb][3] * rz);
         }
     }
 }
 
 // float32 inputs: one wave per query, 64-key chunks, online softmax.
-template <int D>
+template <int D, typename OutT>
 __global__ __launch_bounds__(64) void local_attn_f32_kernel(const float* __restrict__ q,
                                                             const float* __restrict__ kk,
                                                             const float* __restrict__ v, int n,
                                                             int window, float scale, int causal,
-                                                            float* __restrict__ out) {
+                                                            OutT* __restrict__ out) {
     __shared__ float lq[D];
     __shared__ float lp[64];
     const int i = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
@@ -224,34 +301,44 @@ __global__ __launch_bounds__(64) void local_attn_f32_kernel(const float* __restr
     }
     for (int u = 0; u < PER; ++u) {
         const int e = lane + 64 * u;
-        if (e < D) out[(base + i) * D + e] = acc[u] / z;
+        if (e < D) Elem<OutT>::store(out, (base + i) * D + e, acc[u] / z);
     }
 }
 
-template <int D>
+template <int D, typename OutT>
 void launch_local_d(const void* q, const void* kk, const void* v, int dtype, int BH, int n,
                     int window, float scale, int causal, void* out, hipStream_t s) {
     if (dtype == 1)
-        hipLaunchKernelGGL(local_attn_bf16_kernel<D>, dim3((n + 63) / 64, BH), dim3(256), 0, s,
+        hipLaunchKernelGGL((local_attn_bf16_kernel<D, OutT>),
+                           dim3((n + LocalCfg<D>::QT - 1) / LocalCfg<D>::QT, BH), dim3(256), 0, s,
                            (const u16*)q, (const u16*)kk, (const u16*)v, n, window, scale, causal,
-                           (u16*)out);
+                           (OutT*)out);
     else
-        hipLaunchKernelGGL(local_attn_f32_kernel<D>, dim3(n, BH), dim3(64), 0, s, (const float*)q,
-                           (const float*)kk, (const float*)v, n, window, scale, causal,
-                           (float*)out);
+        hipLaunchKernelGGL((local_attn_f32_kernel<D, OutT>), dim3(n, BH), dim3(64), 0, s,
+                           (const float*)q, (const float*)kk, (const float*)v, n, window, scale,
+                           causal, (OutT*)out);
+}
+
+template <typename OutT>
+void launch_local_outt(const void* q, const void* kk, const void* v, int dtype, int BH, int n,
+                       int d, int window, float scale, int causal, void* out, hipStream_t s) {
+    switch (d) {
+        case 16: launch_local_d<16, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
+        case 32: launch_local_d<32, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
+        case 64: launch_local_d<64, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
+        default: launch_local_d<128, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_local_attn(const void* q, const void* kk, const void* v, int dtype, int BH,
                              int n, int d, int window, float scale, int causal, void* out,
-                             hipStream_t s) {
-    switch (d) {
-        case 16: launch_local_d<16>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
-        case 32: launch_local_d<32>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
-        case 64: launch_local_d<64>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
-        default: launch_local_d<128>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
-    }
+                             int out_dtype, hipStream_t s) {
+    if (out_dtype == 1)
+        launch_local_outt<u16>(q, kk, v, dtype, BH, n, d, window, scale, causal, out, s);
+    else
+        launch_local_outt<float>(q, kk, v, dtype, BH, n, d, window, scale, causal, out, s);
     return hipGetLastError();
 }
 

@@ -10,9 +10,6 @@
 
 namespace rt {
 
-// Words of the per-token membership bitmask (one bit per centroid).
-inline int mask_words(int k) { return (k + 31) / 32; }
-
 // Largest cluster the in-cluster kernels keep on chip.
 int max_cluster_rows(int dtype, int d, bool shared_qk);
 
@@ -25,17 +22,20 @@ hipError_t launch_score(const void* qk, int dtype, const float* mu, int B, int H
 hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t* idx,
                        hipStream_t s);
 
-hipError_t launch_membership(const int32_t* idx, int BH, int n, int k, int w, uint32_t* mask,
-                             hipStream_t s);
+// Per-token membership counters cnt [BH*n] and lists list [BH*n][k] of
+// c*w + r entries (unordered).
+hipError_t launch_membership(const int32_t* idx, int BH, int n, int k, int w, uint32_t* cnt,
+                             int32_t* list, hipStream_t s);
 
 hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int dtype,
                                const float* q_inv, const float* k_inv, const int32_t* idx,
-                               const uint32_t* mask, int BH, int n, int d, int k, int w,
-                               float scale, int causal, void* out, float* lse, float* part,
-                               hipStream_t s);
+                               const uint32_t* cnt, int BH, int n, int d, int k, int w,
+                               float scale, int causal, void* out, int out_dtype, float* lse,
+                               float* part, hipStream_t s);
 
-hipError_t launch_combine(const uint32_t* mask, const int32_t* idx, const float* part, int dtype,
-                          int BH, int n, int d, int k, int w, void* out, hipStream_t s);
+hipError_t launch_combine(const uint32_t* cnt, const int32_t* list, const float* part,
+                          int out_dtype, int BH, int n, int d, int k, int w, void* out,
+                          hipStream_t s);
 
 hipError_t launch_ema(float* mu, const void* q, const float* q_inv, const void* kk,
                       const float* k_inv, int dtype, const int32_t* idx, int B, int H, int n,
@@ -43,7 +43,7 @@ hipError_t launch_ema(float* mu, const void* q, const float* q_inv, const void* 
 
 hipError_t launch_local_attn(const void* q, const void* kk, const void* v, int dtype, int BH,
                              int n, int d, int window, float scale, int causal, void* out,
-                             hipStream_t s);
+                             int out_dtype, hipStream_t s);
 
 hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
                                    const float* q_inv, const float* k_inv, const int32_t* idx,

@@ -106,19 +106,24 @@ rt_status rt_route(const void *qk, int dtype, const float *mu, int B, int H, int
  *              results; out-of-range values are clamped, never dereferenced).
  *   causal     1: member s is visible to member r iff pos(s) <= pos(r);
  *              0: every member sees every member.
- *   out        out [B][H][n][d] dtype: for each token, the sum of its output
+ *   out        out [B][H][n][d] of element type out_dtype (RT_F32 or RT_BF16,
+ *              independent of dtype): for each token, the sum of its output
  *              rows over the clusters that hold it, in ascending centroid
  *              order (float32 accumulation, one final rounding); 0 for a
- *              token that no cluster holds.  Must not alias an input.
+ *              token that no cluster holds.  Must not alias an input.  The
+ *              bf16 output is exactly the round-to-nearest-even of the
+ *              float32 output.
  *   lse        optional out (NULL to skip) [B][H][k][w] float32: natural log
  *              of each row's softmax denominator, max + log(sum exp).
- *   ws         rt_workspace_bytes(RT_OP_ROUTED_ATTN, ...) bytes.
+ *   ws         rt_workspace_bytes(RT_OP_ROUTED_ATTN, ...) bytes: per-token
+ *              membership counters and lists, and float32 partial rows of
+ *              tokens that several clusters hold.
  *   Deterministic: repeated calls give bit-identical results.
  */
 rt_status rt_routed_attn(const void *q, const void *kk, const void *v, int dtype,
                          const float *q_inv, const float *k_inv, const int32_t *idx, int B, int H,
                          int n, int d, int k, int w, float scale, int causal, void *out,
-                         float *lse, void *ws, size_t ws_bytes, void *stream);
+                         int out_dtype, float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * rt_local_attn -- sliding-window attention for the non-routed heads.
@@ -128,12 +133,13 @@ rt_status rt_routed_attn(const void *q, const void *kk, const void *v, int dtype
  *   [max(0, i-window+1), i] (causal = 1).  causal = 0 uses the symmetric band
  *   |i - j| < window.
  *
- *   q, kk, v, out  [B][H][n][d] dtype (raw, not normalised); out must not
- *   alias an input.  window >= 1.  No workspace.
+ *   q, kk, v  [B][H][n][d] dtype (raw, not normalised).
+ *   out       [B][H][n][d] of element type out_dtype (RT_F32 or RT_BF16); must
+ *             not alias an input.  window >= 1.  No workspace.
  */
 rt_status rt_local_attn(const void *q, const void *kk, const void *v, int dtype, int B, int H,
                         int n, int d, int window, float scale, int causal, void *out,
-                        void *stream);
+                        int out_dtype, void *stream);
 
 /*
  * rt_centroid_update -- one online k-means step of the shared centroids.

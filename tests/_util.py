@@ -32,14 +32,32 @@ def host(x: torch.Tensor) -> np.ndarray:
 
 
 def assert_close_out(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "out"):
+    """`dtype` is the input dtype of the computation; `got` is its float32 output."""
     err = np.abs(got - want)
+    if err.size == 0:
+        return
+    at = np.unravel_index(np.argmax(err), err.shape)
+    where = f"at {tuple(int(i) for i in at)}: got {got[at]:.6g} want {want[at]:.6g}"
     if dtype == "f32":
-        assert err.max() <= F32_MAX_ABS, f"{what}: max-abs {err.max():.3e} > {F32_MAX_ABS}"
+        assert err.max() <= F32_MAX_ABS, f"{what}: max-abs {err.max():.3e} > {F32_MAX_ABS} {where}"
         return
     denom = np.abs(want).sum()
     mean_rel = err.sum() / denom if denom > 0 else err.sum()
-    assert err.max() <= BF16_MAX_ABS, f"{what}: max-abs {err.max():.3e} > {BF16_MAX_ABS}"
+    assert err.max() <= BF16_MAX_ABS, f"{what}: max-abs {err.max():.3e} > {BF16_MAX_ABS} {where}"
     assert mean_rel <= BF16_MEAN_REL, f"{what}: mean-rel {mean_rel:.3e} > {BF16_MEAN_REL}"
+
+
+def assert_exact_rounding(out_storage: torch.Tensor, out_f32: torch.Tensor):
+    """A bf16 output must be exactly the round-to-nearest-even of the float32
+    output of the same computation (a float32 one must equal it)."""
+    assert out_f32.dtype == torch.float32
+    if out_storage.dtype == torch.bfloat16:
+        want = out_f32.to(torch.bfloat16)
+    else:
+        want = out_f32
+    eq = torch.eq(out_storage.view(torch.int16) if out_storage.dtype == torch.bfloat16 else out_storage,
+                  want.view(torch.int16) if want.dtype == torch.bfloat16 else want)
+    assert bool(eq.all()), f"{int((~eq).sum())} elements differ from the rounded float32 output"
 
 
 def check_membership(orc, gpu_idx, orc_idx, orc_margin, qk_value, mu, w):

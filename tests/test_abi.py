@@ -69,10 +69,10 @@ def test_route_validation(lib, kw, code, msg):
 
 
 def attn(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE, B=1, H=1,
-         n=64, d=16, k=4, w=16, scale=0.25, causal=1, out=ctypes.c_void_p(0x2000), lse=None,
-         ws=FAKE, ws_bytes=0):
+         n=64, d=16, k=4, w=16, scale=0.25, causal=1, out=ctypes.c_void_p(0x2000), out_dtype=1,
+         lse=None, ws=FAKE, ws_bytes=0):
     return lib.rt_routed_attn(q, kk, v, dtype, q_inv, k_inv, idx, B, H, n, d, k, w, scale, causal,
-                              out, lse, ws, ws_bytes, None)
+                              out, out_dtype, lse, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -91,6 +91,7 @@ def attn(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE
     (dict(n=4096, d=128, w=300), RT_EUNSUPPORTED, "w=300"),
     (dict(n=4096, d=64, w=600), RT_EUNSUPPORTED, "w=600"),
     (dict(ws_bytes=10), RT_EINVAL, "workspace"),
+    (dict(out_dtype=5), RT_EUNSUPPORTED, "out_dtype"),
 ])
 def test_routed_attn_validation(lib, kw, code, msg):
     assert attn(lib, **kw) == code
@@ -109,13 +110,15 @@ def test_routed_attn_limits_depend_on_sharing(lib):
     (dict(d=100), RT_EUNSUPPORTED, "d=100"),
     (dict(out=FAKE), RT_EINVAL, "alias"),
     (dict(causal=-1), RT_EINVAL, "causal"),
+    (dict(out_dtype=2), RT_EUNSUPPORTED, "out_dtype"),
 ])
 def test_local_validation(lib, kw, code, msg):
     a = dict(q=FAKE, kk=FAKE, v=FAKE, dtype=1, B=1, H=1, n=64, d=16, window=8, scale=0.25,
-             causal=1, out=ctypes.c_void_p(0x2000))
+             causal=1, out=ctypes.c_void_p(0x2000), out_dtype=1)
     a.update(kw)
     assert lib.rt_local_attn(a["q"], a["kk"], a["v"], a["dtype"], a["B"], a["H"], a["n"], a["d"],
-                             a["window"], a["scale"], a["causal"], a["out"], None) == code
+                             a["window"], a["scale"], a["causal"], a["out"], a["out_dtype"],
+                             None) == code
     assert msg in _last(lib)
 
 
@@ -141,8 +144,9 @@ def test_centroid_update_validation(lib, kw, code, msg):
 def test_workspace_sizes(lib):
     B, H, n, d, k, w = 1, 8, 8192, 128, 64, 128
     assert lib.rt_workspace_bytes(0, B, H, n, d, k, w) == B * H * k * n * 4
-    mask = ((B * H * n * 2 * 4 + 255) // 256) * 256
-    assert lib.rt_workspace_bytes(1, B, H, n, d, k, w) == mask + B * H * k * w * d * 4
+    cnt = ((B * H * n * 4 + 255) // 256) * 256
+    lst = ((B * H * n * k * 4 + 255) // 256) * 256
+    assert lib.rt_workspace_bytes(1, B, H, n, d, k, w) == cnt + lst + B * H * k * w * d * 4
     assert lib.rt_workspace_bytes(2, B, H, n, d, k, w) == 0
     assert lib.rt_workspace_bytes(3, B, H, n, d, k, w) == 0
     assert lib.rt_workspace_bytes(9, B, H, n, d, k, w) == ctypes.c_size_t(-1).value

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import synthetic as S
-from _util import (MU_MAX_ABS, assert_close_out, check_membership, dev_tensor, host,
-                   tokens_touched)
+from _util import (MU_MAX_ABS, assert_close_out, assert_exact_rounding, check_membership,
+                   dev_tensor, host, tokens_touched)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,11 +84,14 @@ def run_routed_case(rt, orc, cfg, scale=None, causal=True, check_scores=True):
     gidx = host(idx)
     differs = check_membership(orc, gidx, idx_o, margin_o, qk_val, mu_val, cfg.w)
 
-    # attention with the oracle's membership
+    # attention with the oracle's membership (float32 output checked against
+    # the tolerance; the storage-dtype output must be its exact rounding)
     idx_o_dev = torch.from_numpy(idx_o).cuda()
     out, lse = rt.routed_attn(qk, qk, v, idx_o_dev, inv, inv, scale=sc, causal=causal,
-                              want_lse=True)
+                              want_lse=True, out_dtype=torch.float32)
+    out_st = rt.routed_attn(qk, qk, v, idx_o_dev, inv, inv, scale=sc, causal=causal)
     torch.cuda.synchronize()
+    assert_exact_rounding(out_st, out)
     out_o, lse_o, _ = orc.routed_attn(qk_val, qk_val, v_val, idx_o, sc, causal)
     assert_close_out(host(out), out_o, cfg.dtype, "out")
     lse_tol = 1e-4 if cfg.dtype == "f32" else 5e-3
@@ -102,7 +105,8 @@ def run_routed_case(rt, orc, cfg, scale=None, causal=True, check_scores=True):
     assert np.abs(host(mu2) - mu_o).max() <= MU_MAX_ABS
 
     # end to end on the GPU's own membership
-    out_e = rt.routed_attn(qk, qk, v, idx, inv, inv, scale=sc, causal=causal)
+    out_e = rt.routed_attn(qk, qk, v, idx, inv, inv, scale=sc, causal=causal,
+                           out_dtype=torch.float32)
     mu_e = mu.clone()
     rt.centroid_update_(mu_e, qk, inv, idx, cfg.lam)
     torch.cuda.synchronize()
@@ -147,7 +151,9 @@ def test_distinct_q_and_k(rt, orc, dtype):
     check_membership(orc, host(idx), idx_o, margin_o, inp["qk"].value, inp["mu"], cfg.w)
     idx_o_dev = torch.from_numpy(idx_o).cuda()
     sc = 0.9
-    out = rt.routed_attn(q, kk, v, idx_o_dev, q_inv, k_inv, scale=sc)
+    out = rt.routed_attn(q, kk, v, idx_o_dev, q_inv, k_inv, scale=sc, out_dtype=torch.float32)
+    out_st = rt.routed_attn(q, kk, v, idx_o_dev, q_inv, k_inv, scale=sc)
+    assert_exact_rounding(out_st, out)
     mu2 = mu.clone()
     rt.centroid_update_(mu2, q, q_inv, idx_o_dev, 0.7, kk=kk, k_inv=k_inv)
     torch.cuda.synchronize()
@@ -187,7 +193,8 @@ def test_unrouted_tokens_are_zero_and_deterministic(rt, orc):
     qk, v, mu = res["qk"], res["v"], res["mu"]
     for _ in range(2):
         inv2, idx2 = rt.route(qk, mu, cfg.w)
-        out2 = rt.routed_attn(qk, qk, v, idx2, inv2, inv2, scale=res["sc"])
+        out2 = rt.routed_attn(qk, qk, v, idx2, inv2, inv2, scale=res["sc"],
+                              out_dtype=torch.float32)
         mu3 = mu.clone()
         rt.centroid_update_(mu3, qk, inv2, idx2, cfg.lam)
         torch.cuda.synchronize()
@@ -206,8 +213,10 @@ def test_local_small(rt, orc, name, causal):
     inp = S.make_inputs(cfg)
     q, kk, v = (dev_tensor(inp[x]) for x in ("q_local", "k_local", "v_local"))
     sc = 1.0 / math.sqrt(cfg.d)
-    out = rt.local_attn(q, kk, v, cfg.window, scale=sc, causal=causal)
+    out = rt.local_attn(q, kk, v, cfg.window, scale=sc, causal=causal, out_dtype=torch.float32)
+    out_st = rt.local_attn(q, kk, v, cfg.window, scale=sc, causal=causal)
     torch.cuda.synchronize()
+    assert_exact_rounding(out_st, out)
     out_o = orc.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
                            cfg.window, sc, causal)
     assert_close_out(host(out), out_o, cfg.dtype, "local out")
@@ -218,13 +227,13 @@ def test_local_window_edges(rt, orc, window):
     cfg = SMALL["ragged_d64"]
     inp = S.make_inputs(cfg)
     q, kk, v = (dev_tensor(inp[x]) for x in ("q_local", "k_local", "v_local"))
-    out = rt.local_attn(q, kk, v, window, scale=0.3)
+    out = rt.local_attn(q, kk, v, window, scale=0.3, out_dtype=torch.float32)
     torch.cuda.synchronize()
     out_o = orc.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
                            window, 0.3, True)
     assert_close_out(host(out), out_o, cfg.dtype, "local out")
     if window == 1:
-        assert torch.equal(out, v)
+        assert torch.equal(out, v.float())
 
 
 # Full-size workloads, in the launch configuration the benchmark times.
@@ -236,7 +245,7 @@ def test_full_size_forward(rt, orc, name):
     if cfg.L > 0:
         inp = res["inp"]
         q, kk, v = (dev_tensor(inp[x]) for x in ("q_local", "k_local", "v_local"))
-        out = rt.local_attn(q, kk, v, cfg.window, scale=res["sc"])
+        out = rt.local_attn(q, kk, v, cfg.window, scale=res["sc"], out_dtype=torch.float32)
         torch.cuda.synchronize()
         out_o = orc.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
                                cfg.window, res["sc"], True)

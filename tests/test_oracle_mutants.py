@@ -1,0 +1,80 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one error in a copy of oracle/rt_oracle.c (on the CPU, in a
+temporary directory), rebuilds it, and runs tests/test_oracle_pins.py against
+the copy: at least one pin has to fail.  The unmodified copy has to pass.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle")
+
+MUTANTS = {
+    "self_not_visible": ("ok[s] = (!causal) || (p[s] <= p[r]);",
+                         "ok[s] = (!causal) || (p[s] < p[r]);"),
+    "tie_break_flipped": ("return (x->t < y->t) ? -1 : (x->t > y->t);",
+                          "return (x->t > y->t) ? -1 : (x->t < y->t);"),
+    "smallest_scores": ("if (x->s > y->s) return -1;\n    if (x->s < y->s) return 1;",
+                        "if (x->s < y->s) return -1;\n    if (x->s > y->s) return 1;"),
+    "no_normalisation": ("xhat[t * d + i] = x[t * d + i] / r;", "xhat[t * d + i] = x[t * d + i];"),
+    "ema_missing_half": ("(1.0 - lam) * 0.5 * (sum_q[j] + sum_k[j])",
+                         "(1.0 - lam) * (sum_q[j] + sum_k[j])"),
+    "ema_wrong_weight": ("mu[j] = lam * mu[j]", "mu[j] = (1.0 - lam) * mu[j]"),
+    "scatter_overwrites": ("out[t * d + i] += o[((long)c * w + r) * d + i];",
+                           "out[t * d + i] = o[((long)c * w + r) * d + i];"),
+    "scale_dropped": ("logit[s] = scale * dot;", "logit[s] = dot;"),
+    "local_window_off_by_one": ("long lo = i - window + 1;", "long lo = i - window;"),
+    "softmax_bwd_sign": ("double dl = P[r * w + s] * (dP[r * w + s] - D);",
+                         "double dl = P[r * w + s] * (dP[r * w + s] + D);"),
+    "centroid_transposed": ("acc += xhat[t * d + i] * mu[c * d + i];",
+                            "acc += xhat[t * d + i] * mu[i * k + c];"),
+    "margin_wrong_rank": ("margin[c] = (w < n) ? buf[w - 1].s - buf[w].s : INFINITY;",
+                          "margin[c] = (w < n) ? buf[0].s - buf[w].s : INFINITY;"),
+    "ema_keys_from_queries": ("orc_normalize(kk + u * n * d, n, d, xhat, NULL);\n            "
+                              "orc_cluster_sums(xhat, idx + u * k * w, n, d, k, w, sk);",
+                              "orc_normalize(q + u * n * d, n, d, xhat, NULL);\n            "
+                              "orc_cluster_sums(xhat, idx + u * k * w, n, d, k, w, sk);"),
+    "lse_without_max": ("lse[(long)c * w + r] = m + log(z);", "lse[(long)c * w + r] = log(z);"),
+    "query_used_as_key": ("dot += qhat[(long)p[r] * d + i] * khat[(long)p[s] * d + i];\n"
+                          "                logit[s]",
+                          "dot += qhat[(long)p[r] * d + i] * khat[(long)p[r] * d + i];\n"
+                          "                logit[s]"),
+    "dv_from_wrong_row": ("dv[(long)p[s] * d + i] += pr * g[i];",
+                          "dv[(long)p[r] * d + i] += pr * g[i];"),
+}
+
+
+def _run_pins(oracle_dir):
+    env = dict(os.environ, RT_ORACLE_DIR=oracle_dir)
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests",
+                        "test_oracle_pins.py"), "-x", "-q", "-p", "no:cacheprovider"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return r.returncode, r.stdout[-2000:]
+
+
+def _copy(tmp_path, name, edit=None):
+    dst = tmp_path / name
+    shutil.copytree(SRC, dst, ignore=shutil.ignore_patterns("*.so*", "__pycache__"))
+    if edit is not None:
+        path = dst / "rt_oracle.c"
+        text = path.read_text()
+        old, new = edit
+        assert text.count(old) == 1, f"mutation site not found exactly once: {old!r}"
+        path.write_text(text.replace(old, new))
+    return str(dst)
+
+
+def test_unmodified_copy_passes(tmp_path):
+    rc, out = _run_pins(_copy(tmp_path, "clean"))
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_error_is_caught(tmp_path, name):
+    rc, out = _run_pins(_copy(tmp_path, name, MUTANTS[name]))
+    assert rc == 1, f"pins did not catch {name}:\n{out}"
