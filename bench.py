@@ -119,6 +119,8 @@ def main():
     B, R, n, d, k, w = cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w
     inv = torch.empty((B, R, n), dtype=torch.float32, device="cuda")
     idx = torch.empty((B, R, k, w), dtype=torch.int32, device="cuda")
+    mask = torch.empty((B, R, n, rt.mask_words(k)), dtype=torch.int32, device="cuda")
+    sum_q = torch.empty((B, R, k, d), dtype=torch.float32, device="cuda")
     out = torch.empty_like(qk)
     ws_route = torch.empty(rt.workspace_bytes("route", B, R, n, d, k, w), dtype=torch.uint8,
                            device="cuda")
@@ -129,13 +131,14 @@ def main():
         out_l = torch.empty_like(ql)
 
     def do_route():
-        rt.route(qk, mu, w, out=(inv, idx), ws=ws_route)
+        rt.route(qk, mu, w, out=(inv, idx, mask), ws=ws_route)
 
     def do_attn():
-        rt.routed_attn(qk, qk, v, idx, inv, inv, scale=scale, out=out, ws=ws_attn)
+        rt.routed_attn(qk, qk, v, idx, inv, inv, scale=scale, mask=mask, sums=(sum_q, None),
+                       out=out, ws=ws_attn)
 
     def do_ema():
-        rt.centroid_update_(mu, qk, inv, idx, cfg.lam)
+        rt.centroid_update_sums_(mu, sum_q, cfg.lam)
 
     def do_local():
         if cfg.L > 0:
@@ -182,7 +185,7 @@ def main():
         # Per-call timing (events on the stream the kernels are launched on).
         per_call = {}
         for name, fn in (("rt_route", do_route), ("rt_routed_attn", do_attn),
-                         ("rt_centroid_update", do_ema), ("rt_local_attn", do_local)):
+                         ("rt_centroid_update_sums", do_ema), ("rt_local_attn", do_local)):
             if name == "rt_local_attn" and cfg.L == 0:
                 continue
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -195,7 +198,8 @@ def main():
             per_call[name] = a.elapsed_time(b) / reps
 
     alg = algorithmic(cfg)
-    routed_ms = per_call["rt_route"] + per_call["rt_routed_attn"] + per_call["rt_centroid_update"]
+    routed_ms = (per_call["rt_route"] + per_call["rt_routed_attn"] +
+                 per_call["rt_centroid_update_sums"])
     attn_s = per_call["rt_routed_attn"] * 1e-3
     achieved_gbs = alg["attn_bytes"] / attn_s / 1e9
     tokens = B * n

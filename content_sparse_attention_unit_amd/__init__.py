@@ -15,8 +15,8 @@ import os
 
 import torch
 
-__all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "routed_attn_bwd",
-           "workspace_bytes", "library_path", "RTError", "RT_OP"]
+__all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
+           "routed_attn_bwd", "workspace_bytes", "library_path", "mask_words", "RTError", "RT_OP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "lib", "librouted_attn.so")
@@ -50,8 +50,10 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)  # torch (imported above) already holds the HIP runtime
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     sig = {
-        "rt_route": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, Z, P],
-        "rt_routed_attn": [P, P, P, I, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P, Z, P],
+        "rt_route": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, Z, P],
+        "rt_routed_attn": [P, P, P, I, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P, P, P, Z,
+                           P],
+        "rt_centroid_update_sums": [P, P, P, I, I, I, I, F, P],
         "rt_local_attn": [P, P, P, I, I, I, I, I, I, F, I, P, I, P],
         "rt_centroid_update": [P, P, P, P, P, I, P, I, I, I, I, I, I, F, P],
         "rt_routed_attn_bwd": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z,
@@ -123,21 +125,32 @@ def _workspace(op, dev, B, H, n, d, k, w, ws=None):
     return torch.empty(need, dtype=torch.uint8, device=dev), need
 
 
+def mask_words(k: int) -> int:
+    return (k + 31) // 32
+
+
 def route(qk: torch.Tensor, mu: torch.Tensor, w: int, *, want_scores: bool = False,
-          want_qk_hat: bool = False, out=None, ws=None):
-    """Normalise, score and select: returns ``(inv_norm, idx)`` plus ``scores``
-    and/or ``qk_hat`` when asked.  qk [B,H,n,d] f32/bf16, mu [H,k,d] f32."""
+          want_qk_hat: bool = False, want_mask: bool = False, out=None, ws=None):
+    """Normalise, score and select: returns ``(inv_norm, idx)`` plus the
+    membership bitmask, ``scores`` and ``qk_hat`` when asked (in that order).
+    qk [B,H,n,d] f32/bf16, mu [H,k,d] f32.  ``out`` may carry
+    ``(inv_norm, idx)`` or ``(inv_norm, idx, mask)`` preallocated."""
     lib = _load()
     dev = _gpu(qk, mu)
     B, H, n, d = qk.shape
     k = mu.shape[1]
     if mu.dtype != torch.float32 or tuple(mu.shape) != (H, k, d):
         raise ValueError("mu must be float32 [H, k, d]")
+    mask = None
     if out is None:
         inv = torch.empty((B, H, n), dtype=torch.float32, device=dev)
         idx = torch.empty((B, H, k, w), dtype=torch.int32, device=dev)
+    elif len(out) == 3:
+        inv, idx, mask = out
     else:
         inv, idx = out
+    if want_mask and mask is None:
+        mask = torch.empty((B, H, n, mask_words(k)), dtype=torch.int32, device=dev)
     scores = torch.empty((B, H, k, n), dtype=torch.float32, device=dev) if want_scores else None
     qk_hat = torch.empty_like(qk) if want_qk_hat else None
     if scores is None:
@@ -145,9 +158,11 @@ def route(qk: torch.Tensor, mu: torch.Tensor, w: int, *, want_scores: bool = Fal
     else:
         need = 0
     _check(lib.rt_route(_ptr(qk), _dtype_code(qk), _ptr(mu), B, H, n, d, k, w, _ptr(inv),
-                        _ptr(idx), _ptr(qk_hat), _ptr(scores), _ptr(ws),
+                        _ptr(idx), _ptr(mask), _ptr(qk_hat), _ptr(scores), _ptr(ws),
                         0 if ws is None else ws.numel(), _stream(dev)))
     res = [inv, idx]
+    if want_mask or (out is not None and len(out) == 3):
+        res.append(mask)
     if want_scores:
         res.append(scores)
     if want_qk_hat:
@@ -158,12 +173,16 @@ def route(qk: torch.Tensor, mu: torch.Tensor, w: int, *, want_scores: bool = Fal
 def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                 q_inv: torch.Tensor | None = None, k_inv: torch.Tensor | None = None, *,
                 scale: float | None = None, causal: bool = True, want_lse: bool = False,
-                out_dtype: torch.dtype | None = None, out=None, lse=None, ws=None):
+                out_dtype: torch.dtype | None = None, mask: torch.Tensor | None = None,
+                sums: tuple | None = None, out=None, lse=None, ws=None):
     """In-cluster attention scatter-added to token order; returns ``out`` (and
     ``lse`` when asked).  Pass ``kk is q`` (and ``k_inv is q_inv``) for shared QK.
-    ``out_dtype`` (float32 or bfloat16) defaults to the input dtype."""
+    ``out_dtype`` (float32 or bfloat16) defaults to the input dtype; ``mask``
+    is the membership bitmask from route(); ``sums`` = (sum_q, sum_k) float32
+    [B,H,k,d] tensors (either may be None) to receive per-cluster member sums."""
     lib = _load()
-    dev = _gpu(q, kk, v, idx, q_inv, k_inv)
+    sum_q, sum_k = sums if sums is not None else (None, None)
+    dev = _gpu(q, kk, v, idx, q_inv, k_inv, mask, sum_q, sum_k)
     B, H, n, d = q.shape
     k, w = idx.shape[2], idx.shape[3]
     if idx.dtype != torch.int32:
@@ -175,9 +194,10 @@ def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.T
         lse = torch.empty((B, H, k, w), dtype=torch.float32, device=dev)
     ws, _ = _workspace("routed_attn", dev, B, H, n, d, k, w, ws)
     _check(lib.rt_routed_attn(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
-                              _ptr(k_inv), _ptr(idx), B, H, n, d, k, w, sc, int(causal),
-                              _ptr(out), _dtype_code(out), _ptr(lse), _ptr(ws),
-                              0 if ws is None else ws.numel(), _stream(dev)))
+                              _ptr(k_inv), _ptr(idx), _ptr(mask), B, H, n, d, k, w, sc,
+                              int(causal), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(sum_q),
+                              _ptr(sum_k), _ptr(ws), 0 if ws is None else ws.numel(),
+                              _stream(dev)))
     return (out, lse) if want_lse else out
 
 
@@ -208,6 +228,17 @@ def centroid_update_(mu: torch.Tensor, q: torch.Tensor, q_inv: torch.Tensor, idx
     _check(lib.rt_centroid_update(_ptr(mu), _ptr(q), _ptr(q_inv), _ptr(kk), _ptr(k_inv),
                                   _dtype_code(q), _ptr(idx), B, H, n, d, k, w, float(lam),
                                   _stream(dev)))
+    return mu
+
+
+def centroid_update_sums_(mu: torch.Tensor, sum_q: torch.Tensor, lam: float,
+                          sum_k: torch.Tensor | None = None):
+    """EMA step of the centroids from per-cluster member sums [B,H,k,d]."""
+    lib = _load()
+    dev = _gpu(mu, sum_q, sum_k)
+    B, H, k, d = sum_q.shape
+    _check(lib.rt_centroid_update_sums(_ptr(mu), _ptr(sum_q), _ptr(sum_k), B, H, k, d, float(lam),
+                                       _stream(dev)))
     return mu
 
 

@@ -7,7 +7,7 @@
 
 #include <cmath>
 
-#include "../../include/routed_attn.h"
+#include "routed_attn.h"
 #include "rt_internal.hpp"
 
 namespace {
@@ -53,15 +53,19 @@ rt_status check_clusters(const char* fn, int n, int k, int w) {
 
 size_t route_ws(int B, int H, int n, int k) { return (size_t)B * H * k * n * sizeof(float); }
 
-// rt_routed_attn workspace: cnt [B*H*n] u32 | list [B*H*n][k] i32 | part [B*H*k*w][d] f32
-size_t attn_ws_cnt(int B, int H, int n) { return align256((size_t)B * H * n * sizeof(uint32_t)); }
+// rt_routed_attn workspace: mask [B*H*n][KW] u32 | slots [B*H*n][kSlots][d] f32 |
+// overflow [B*H*k*w][d] f32, each part 256-byte aligned.
+size_t attn_ws_mask(int B, int H, int n, int k) {
+    return align256((size_t)B * H * n * rt::mask_words(k) * sizeof(uint32_t));
+}
 
-size_t attn_ws_list(int B, int H, int n, int k) {
-    return align256((size_t)B * H * n * k * sizeof(int32_t));
+size_t attn_ws_slots(int B, int H, int n, int d) {
+    return align256((size_t)B * H * n * rt::kSlots * d * sizeof(float));
 }
 
 size_t attn_ws(int B, int H, int n, int d, int k, int w) {
-    return attn_ws_cnt(B, H, n) + attn_ws_list(B, H, n, k) + (size_t)B * H * k * w * d * sizeof(float);
+    return attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d) +
+           (size_t)B * H * k * w * d * sizeof(float);
 }
 
 bool out_dtype_ok(int t) { return t == RT_F32 || t == RT_BF16; }
@@ -97,8 +101,8 @@ size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
 }
 
 rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int n, int d, int k,
-                   int w, float* inv_norm, int32_t* idx, void* qk_hat, float* scores, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   int w, float* inv_norm, int32_t* idx, uint32_t* member_mask, void* qk_hat,
+                   float* scores, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_route";
     g_err[0] = 0;
     if (!qk || !mu || !inv_norm || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
@@ -119,17 +123,19 @@ rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int
         sc = static_cast<float*>(ws);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = rt::launch_score(qk, dtype, mu, B, H, n, d, k, inv_norm, sc, qk_hat, s);
+    hipError_t e =
+        rt::launch_score(qk, dtype, mu, B, H, n, d, k, inv_norm, sc, qk_hat, member_mask, s);
     if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_topw(sc, B * H, n, k, w, idx, s);
+    e = rt::launch_topw(sc, B * H, n, k, w, idx, member_mask, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }
 
 rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype,
-                         const float* q_inv, const float* k_inv, const int32_t* idx, int B, int H,
-                         int n, int d, int k, int w, float scale, int causal, void* out,
-                         int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                         const float* q_inv, const float* k_inv, const int32_t* idx,
+                         const uint32_t* member_mask, int B, int H, int n, int d, int k, int w,
+                         float scale, int causal, void* out, int out_dtype, float* lse,
+                         float* sum_q, float* sum_k, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_routed_attn";
     g_err[0] = 0;
     if (!q || !kk || !v || !idx || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
@@ -154,17 +160,22 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
         return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
     char* base = static_cast<char*>(ws);
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(base);
-    int32_t* list = reinterpret_cast<int32_t*>(base + attn_ws_cnt(B, H, n));
-    float* part = reinterpret_cast<float*>(base + attn_ws_cnt(B, H, n) + attn_ws_list(B, H, n, k));
+    uint32_t* mask_ws = reinterpret_cast<uint32_t*>(base);
+    float* slots = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k));
+    float* ovf = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = B * H;
-    hipError_t e = rt::launch_membership(idx, BH, n, k, w, cnt, list, s);
+    hipError_t e = hipSuccess;
+    const uint32_t* mask = member_mask;
+    if (mask == nullptr) {
+        e = rt::launch_mask(idx, BH, n, k, w, mask_ws, s);
+        if (e != hipSuccess) return hip_fail(fn, e);
+        mask = mask_ws;
+    }
+    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, mask, BH, n, d, k, w, scale,
+                                causal, out, out_dtype, lse, slots, ovf, sum_q, sum_k, s);
     if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, d, k, w, scale,
-                                causal, out, out_dtype, lse, part, s);
-    if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_combine(cnt, list, part, out_dtype, BH, n, d, k, w, out, s);
+    e = rt::launch_combine(mask, idx, slots, ovf, out_dtype, BH, n, d, k, w, out, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }
@@ -207,6 +218,23 @@ rt_status rt_centroid_update(float* mu, const void* q, const float* q_inv, const
     if ((long long)B * w > 0x7fffffffLL) return fail(RT_EUNSUPPORTED, "%s: B*w too large", fn);
     hipError_t e = rt::launch_ema(mu, q, q_inv, kk, k_inv, dtype, idx, B, H, n, d, k, w, lambda,
                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_centroid_update_sums(float* mu, const float* sum_q, const float* sum_k, int B,
+                                  int H, int k, int d, float lambda, void* stream) {
+    static const char* fn = "rt_centroid_update_sums";
+    g_err[0] = 0;
+    if (!mu || !sum_q) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (B <= 0 || H <= 0 || k <= 0 || d <= 0)
+        return fail(RT_EINVAL, "%s: sizes must be positive (B=%d H=%d k=%d d=%d)", fn, B, H, k, d);
+    if (!(lambda >= 0.f && lambda <= 1.f))
+        return fail(RT_EINVAL, "%s: lambda=%g outside [0, 1]", fn, (double)lambda);
+    if ((long long)B * H * k * d >= (1LL << 31))
+        return fail(RT_EUNSUPPORTED, "%s: B*H*k*d too large", fn);
+    hipError_t e = rt::launch_ema_sums(mu, sum_q, sum_k, B, H, k, d, lambda,
+                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

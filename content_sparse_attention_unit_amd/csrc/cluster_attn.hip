@@ -8,28 +8,35 @@
 // attention is the ordinary autoregressive softmax attention of §3: member s
 // is visible to member r when its original position is not later.
 //
-// Kernels (in launch order)
-//   zero_u32_kernel     clears the per-token membership counters.
-//   membership_kernel   one thread per membership (c, r): bumps the token's
-//                       counter and appends c*w + r to the token's list.  The
-//                       list order is arbitrary; readers sort it.
-//   cluster_attn_bf16   one workgroup per cluster.  The w member rows of the
-//                       keys (raw bf16) and of the values (transposed) are
-//                       gathered into LDS once, with every load of a thread
-//                       issued before the first LDS store; each wave takes
-//                       16-row query blocks in a zig-zag order that balances
-//                       the causal triangle, computes S^T = K Q^T with
-//                       v_mfma_f32_16x16x32_bf16 (each lane owns one query,
-//                       so row statistics are per lane), applies the inverse
-//                       norms and the scale in fp32, runs an online softmax
-//                       over 64-key chunks and accumulates O^T = V^T P^T with
-//                       the same MFMA.  A row whose token belongs to this
-//                       cluster only is written straight to `out`; otherwise
-//                       the fp32 row goes to the partial buffer.
+// Membership bitmask: mask[b][h][t] holds one bit per centroid (KW = ceil(k/32)
+// words per token).  For member row r of cluster c holding token t,
+// cnt = popcount(mask[t]) and rank = number of set bits below c.  A token held
+// by one cluster is written straight to `out`; otherwise its row goes to the
+// partial buffer at slot `rank` (token-major, kSlots slots per token; higher
+// ranks go to a cluster-major overflow buffer), and combine_kernel sums the
+// slots in rank order, i.e. ascending centroid order, so results are
+// deterministic.
+//
+// Kernels
+//   zero_u32_kernel / mask_kernel   build the bitmask from idx (skipped when
+//                       the caller passes the mask rt_route produced).
+//   cluster_attn_bf16   one workgroup per cluster.  Every member row of the
+//                       keys (raw bf16) and values is requested from memory at
+//                       once (the row index straight from idx); keys are
+//                       staged in LDS, values stay in flight while the first
+//                       query block's logits are computed, then are stored
+//                       transposed.  Each wave takes 16-row query blocks in a
+//                       zig-zag order that balances the causal triangle,
+//                       computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
+//                       (each lane owns one query, so the row statistics are
+//                       per lane), applies the inverse norms and the scale in
+//                       fp32, runs an online softmax over 64-key chunks and
+//                       accumulates O^T = V^T P^T with the same MFMA.  It can
+//                       also emit the per-cluster sums of the normalised rows
+//                       that the centroid update needs.
 //   cluster_attn_f32    a plain vector-ALU variant for float32 inputs.
-//   combine_kernel      per token: 0 if no cluster holds it; the sum of its
-//                       fp32 partial rows in ascending centroid order if
-//                       several do (deterministic); nothing if one does.
+//   combine_kernel      per token: zeros if no cluster holds it, the ordered
+//                       sum of its slots if several do, nothing if one does.
 #include "rt_common.hpp"
 #include "rt_internal.hpp"
 
@@ -41,40 +48,48 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p,
     if (i < count) p[i] = 0u;
 }
 
-// grid (ceil(w / 256), k, BH)
-__global__ __launch_bounds__(256) void membership_kernel(const int32_t* __restrict__ idx, int n,
-                                                         int k, int w,
-                                                         uint32_t* __restrict__ cnt,
-                                                         int32_t* __restrict__ list) {
+// grid (ceil(w / 256), k, BH): one thread per membership.
+__global__ __launch_bounds__(256) void mask_kernel(const int32_t* __restrict__ idx, int n, int k,
+                                                   int w, int KW, uint32_t* __restrict__ mask) {
     const int r = blockIdx.x * 256 + threadIdx.x;
     const int c = blockIdx.y, bh = blockIdx.z;
     if (r >= w) return;
     const int t = idx[((long)bh * k + c) * w + r];
     if (t < 0 || t >= n) return;
-    const long tok = (long)bh * n + t;
-    const uint32_t slot = atomicAdd(&cnt[tok], 1u);
-    if (slot < (uint32_t)k) list[tok * k + slot] = c * w + r;
+    atomicOr(&mask[((long)bh * n + t) * KW + (c >> 5)], 1u << (c & 31));
 }
 
 template <typename OutT>
 __device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
 template <>
 __device__ __forceinline__ void store4<u16>(u16* dst, float a, float b, float c, float d) {
-    uint2 pk;
-    pk.x = pack2(f2bf(a), f2bf(b));
-    pk.y = pack2(f2bf(c), f2bf(d));
-    *reinterpret_cast<uint2*>(dst) = pk;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(cvt_pk_bf16(a, b), cvt_pk_bf16(c, d));
 }
 template <>
 __device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
 }
 
+// Where member row r's output goes: -2 nowhere (padding or invalid position),
+// -1 straight to out, 0..kSlots-1 token slot, kSlots + rank overflow.
+__device__ __forceinline__ int row_dest(const uint32_t* __restrict__ m, int KW, int c) {
+    int cnt = 0, below = 0;
+    for (int i = 0; i < KW; ++i) {
+        const uint32_t word = m[i];
+        cnt += __popc(word);
+        if (i < (c >> 5)) below += __popc(word);
+        else if (i == (c >> 5)) below += __popc(word & ((1u << (c & 31)) - 1u));
+    }
+    return cnt == 1 ? -1 : below;
+}
+
 template <int D, int WMAX, bool SHARED>
 struct AttnCfg {
     static constexpr int DP = D < 32 ? 32 : D;  // dims padded to the MFMA k-depth
-    static constexpr int LDX = DP + 8;          // key/query row stride in LDS (bf16)
-    static constexpr int LDV = WMAX + 8;        // transposed value row stride (bf16)
+    // key/query/value row stride in LDS (bf16): an odd multiple of 16 elements,
+    // so 8 consecutive rows start in disjoint bank groups (DP + 8 for the
+    // largest tile, which would not fit otherwise)
+    static constexpr int LDX = (WMAX == 512) ? DP + 8 : DP + 16;
     static constexpr int NS = DP / 32;          // MFMA k-steps over d
     static constexpr int NJ = D / 16;           // 16-wide output column blocks
     static constexpr int QROWS = SHARED ? 1 : WMAX;
@@ -83,195 +98,193 @@ struct AttnCfg {
     static constexpr int CPR = DP / 8;          // 16-byte chunks per padded key row
     static constexpr int XPT = (WMAX * CPR + NT - 1) / NT;         // key chunks per thread
     static constexpr int DCH = D / 8;           // 16-byte chunks per value row
-    static constexpr int VPT = ((WMAX / 2) * DCH + NT - 1) / NT;   // value row-pair chunks per thread
+    static constexpr int VPT = (WMAX * DCH + NT - 1) / NT;         // value chunks per thread
 };
 
 template <int D, int WMAX, bool SHARED, typename OutT>
 __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kk, const u16* __restrict__ v,
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ cnt, int n, int k, int w,
-    float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part) {
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
+    int KW, float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ slots, float* __restrict__ ovf, float* __restrict__ sum_q,
+    float* __restrict__ sum_k) {
     using C = AttnCfg<D, WMAX, SHARED>;
     __shared__ __attribute__((aligned(16))) u16 lx[WMAX * C::LDX];
     __shared__ __attribute__((aligned(16))) u16 lq[C::QROWS * C::LDX];
-    __shared__ __attribute__((aligned(16))) u16 lvt[D * C::LDV];
+    __shared__ __attribute__((aligned(16))) u16 lv[WMAX * C::LDX];
     __shared__ __attribute__((aligned(16))) float linvk[WMAX];
     __shared__ __attribute__((aligned(16))) float linvq[C::QROWS];
-    __shared__ int lposc[WMAX];   // clamped position (safe to dereference)
-    __shared__ int lpos[WMAX];    // position, or -1 when the row is padding / invalid
-    __shared__ int lsingle[WMAX]; // 1 when exactly one cluster holds the token
+    __shared__ int lpos[WMAX];    // position, or -1 for padding / invalid rows
+    __shared__ int ldest[WMAX];   // see row_dest
+    __shared__ float lsum[C::NT];
 
     const int cl = blockIdx.x, bh = blockIdx.y;
     const long tokbase = (long)bh * n;
     const long rowbase = ((long)bh * k + cl) * w;
     const int32_t* irow = idx + rowbase;
 
+    // Request every member row at once: keys/queries, then values.
+    uint4 xk[C::XPT], xq[SHARED ? 1 : C::XPT];
+#pragma unroll
+    for (int it = 0; it < C::XPT; ++it) {
+        const int e = threadIdx.x + it * C::NT;
+        const int r = e / C::CPR, ch = e % C::CPR;
+        xk[it] = zero_u4();
+        if (!SHARED) xq[it] = zero_u4();
+        if (r < w && 8 * ch < D) {
+            const long off = (tokbase + clamp_pos(irow[r], n)) * D + 8 * ch;
+            xk[it] = *reinterpret_cast<const uint4*>(kk + off);
+            if (!SHARED) xq[it] = *reinterpret_cast<const uint4*>(q + off);
+        }
+    }
+    uint4 va[C::VPT];
+#pragma unroll
+    for (int it = 0; it < C::VPT; ++it) {
+        const int e = threadIdx.x + it * C::NT;
+        const int r = e / C::DCH, ch = e % C::DCH;
+        va[it] = zero_u4();
+        if (r < w) va[it] = *reinterpret_cast<const uint4*>(v + (tokbase + clamp_pos(irow[r], n)) * D + 8 * ch);
+    }
     for (int r = threadIdx.x; r < WMAX; r += C::NT) {
-        int pos = -1, posc = 0, single = 0;
+        int pos = -1, dest = -2;
         float ik = 0.f, iq = 0.f;
         if (r < w) {
             const int raw = irow[r];
-            posc = clamp_pos(raw, n);
+            const int posc = clamp_pos(raw, n);
             if (raw >= 0 && raw < n) {
                 pos = raw;
-                single = cnt[tokbase + raw] == 1u;
+                dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
             }
             ik = k_inv ? k_inv[tokbase + posc] : 1.f;
             iq = q_inv ? q_inv[tokbase + posc] : 1.f;
         }
         lpos[r] = pos;
-        lposc[r] = posc;
-        lsingle[r] = single;
+        ldest[r] = dest;
         linvk[r] = ik;
         if (!SHARED) linvq[r] = iq;
     }
+#pragma unroll
+    for (int it = 0; it < C::XPT; ++it) {
+        const int e = threadIdx.x + it * C::NT;
+        if (e < WMAX * C::CPR) {
+            const int r = e / C::CPR, ch = e % C::CPR;
+            *reinterpret_cast<uint4*>(&lx[r * C::LDX + 8 * ch]) = xk[it];
+            if (!SHARED) *reinterpret_cast<uint4*>(&lq[r * C::LDX + 8 * ch]) = xq[it];
+        }
+    }
     __syncthreads();
 
-    // Gather the member rows (padding rows are zero): all loads first.
-    {
-        uint4 xk[C::XPT], xq[SHARED ? 1 : C::XPT];
+    // Per-cluster sums of the normalised member rows (for the centroid update).
+    if (sum_q != nullptr || sum_k != nullptr) {
 #pragma unroll
-        for (int it = 0; it < C::XPT; ++it) {
-            const int e = threadIdx.x + it * C::NT;
-            const int r = e / C::CPR, ch = e % C::CPR;
-            xk[it] = zero_u4();
-            if (!SHARED) xq[it] = zero_u4();
-            if (r < w && 8 * ch < D) {
-                const long off = (tokbase + lposc[r]) * D + 8 * ch;
-                xk[it] = *reinterpret_cast<const uint4*>(kk + off);
-                if (!SHARED) xq[it] = *reinterpret_cast<const uint4*>(q + off);
-            }
-        }
-        uint4 va[C::VPT], vb[C::VPT];
-#pragma unroll
-        for (int it = 0; it < C::VPT; ++it) {
-            const int e = threadIdx.x + it * C::NT;
-            const int rp = e / C::DCH, ch = e % C::DCH;
-            const int r0 = 2 * rp;
-            va[it] = zero_u4();
-            vb[it] = zero_u4();
-            if (r0 < w) va[it] = *reinterpret_cast<const uint4*>(v + (tokbase + lposc[r0]) * D + 8 * ch);
-            if (r0 + 1 < w)
-                vb[it] = *reinterpret_cast<const uint4*>(v + (tokbase + lposc[r0 + 1]) * D + 8 * ch);
-        }
-#pragma unroll
-        for (int it = 0; it < C::XPT; ++it) {
-            const int e = threadIdx.x + it * C::NT;
-            if (e < WMAX * C::CPR) {
-                const int r = e / C::CPR, ch = e % C::CPR;
-                *reinterpret_cast<uint4*>(&lx[r * C::LDX + 8 * ch]) = xk[it];
-                if (!SHARED) *reinterpret_cast<uint4*>(&lq[r * C::LDX + 8 * ch]) = xq[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < C::VPT; ++it) {
-            const int e = threadIdx.x + it * C::NT;
-            if (e < (WMAX / 2) * C::DCH) {
-                const int rp = e / C::DCH, ch = e % C::DCH;
-                const int r0 = 2 * rp;
-                const uint32_t* aw = reinterpret_cast<const uint32_t*>(&va[it]);
-                const uint32_t* bw = reinterpret_cast<const uint32_t*>(&vb[it]);
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int j = 8 * ch + 2 * e2;
-                    *reinterpret_cast<uint32_t*>(&lvt[j * C::LDV + r0]) =
-                        (aw[e2] & 0xffffu) | (bw[e2] << 16);
-                    *reinterpret_cast<uint32_t*>(&lvt[(j + 1) * C::LDV + r0]) =
-                        (aw[e2] >> 16) | (bw[e2] & 0xffff0000u);
+        for (int side = 0; side < 2; ++side) {
+            float* dst = side == 0 ? sum_k : sum_q;
+            if (dst == nullptr) continue;
+            dst += ((long)bh * k + cl) * D;
+            const u16* src = (side == 0 || SHARED) ? lx : lq;
+            const float* inv = (side == 0 || SHARED) ? linvk : linvq;
+            if constexpr (C::NT >= D) {
+                constexpr int PARTS = C::NT / D;      // row groups summed in parallel
+                const int dcol = threadIdx.x % D, part = threadIdx.x / D;
+                float acc = 0.f;
+                for (int r = part; r < w; r += PARTS) acc = fmaf(bf2f(src[r * C::LDX + dcol]), inv[r], acc);
+                __syncthreads();
+                lsum[threadIdx.x] = acc;
+                __syncthreads();
+                if (threadIdx.x < D) {
+                    float tot = 0.f;
+                    for (int p2 = 0; p2 < PARTS; ++p2) tot += lsum[p2 * D + threadIdx.x];
+                    dst[threadIdx.x] = tot;
+                }
+            } else {
+                for (int dcol = threadIdx.x; dcol < D; dcol += C::NT) {
+                    float acc = 0.f;
+                    for (int r = 0; r < w; ++r) acc = fmaf(bf2f(src[r * C::LDX + dcol]), inv[r], acc);
+                    dst[dcol] = acc;
                 }
             }
         }
     }
-    __syncthreads();
 
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const int nqb = (w + 15) / 16;
     const float sl2 = scale * 1.4426950408889634f;  // logits in log2 units
     const u16* qsrc = SHARED ? lx : lq;
+    bool values_staged = false;
 
     for (int round = 0; round * C::NW < nqb; ++round) {
         const int qb = round * C::NW + ((round & 1) ? (C::NW - 1 - wv) : wv);
-        if (qb >= nqb) continue;
+        const bool active = qb < nqb;
         const int qrow = qb * 16 + r16;
         uint4 qreg[C::NS];
+        float qs = 0.f;
 #pragma unroll
-        for (int s = 0; s < C::NS; ++s)
-            qreg[s] = *reinterpret_cast<const uint4*>(&qsrc[qrow * C::LDX + 32 * s + 8 * g]);
-        const float qs = sl2 * (SHARED ? linvk[qrow] : linvq[qrow]);
-
+        for (int s = 0; s < C::NS; ++s) qreg[s] = zero_u4();
+        if (active) {
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s)
+                qreg[s] = *reinterpret_cast<const uint4*>(&qsrc[qrow * C::LDX + 32 * s + 8 * g]);
+            qs = sl2 * (SHARED ? linvk[qrow] : linvq[qrow]);
+        }
         f32x4 o[C::NJ];
 #pragma unroll
         for (int jb = 0; jb < C::NJ; ++jb) o[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = -INFINITY, z = 0.f;
-        const int kend = causal ? min(w, qb * 16 + 16) : w;
+        const int kend = !active ? 0 : (causal ? min(w, qb * 16 + 16) : w);
+        // keys below `clean` are visible to every query of the block
+        const int clean = causal ? qb * 16 : w;
 
-        for (int kc = 0; kc < kend; kc += 64) {
+        for (int kc = 0; kc < kend || !values_staged; kc += 64) {
             f32x4 sv[4];
-            float cmax = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int key0 = kc + 16 * kb;
-                sv[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (key0 < kend) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < C::NS; ++s) {
                         const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
                             &lx[(key0 + r16) * C::LDX + 32 * s + 8 * g]));
-                        sv[kb] = mfma16(a, as_bf16x8(qreg[s]), sv[kb]);
+                        acc = mfma16(a, as_bf16x8(qreg[s]), acc);
                     }
                     const float4 ik = *reinterpret_cast<const float4*>(&linvk[key0 + 4 * g]);
-                    const float ikv[4] = {ik.x, ik.y, ik.z, ik.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = key0 + 4 * g + i;
-                        const bool ok = key < w && (!causal || key <= qrow);
-                        sv[kb][i] = ok ? sv[kb][i] * qs * ikv[i] : -INFINITY;
-                        cmax = fmaxf(cmax, sv[kb][i]);
-                    }
+                    sv[kb][0] = acc[0] * qs * ik.x;
+                    sv[kb][1] = acc[1] * qs * ik.y;
+                    sv[kb][2] = acc[2] * qs * ik.z;
+                    sv[kb][3] = acc[3] * qs * ik.w;
                 } else {
                     sv[kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
                 }
             }
-            cmax = xor_max_16_32(cmax);
-            const float mnew = fmaxf(m, cmax);
-            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-            z *= alpha;
+            if (!values_staged) {  // first chunk of the first round: values arrive now
 #pragma unroll
-            for (int jb = 0; jb < C::NJ; ++jb) o[jb] *= alpha;
-            m = mnew;
-
-            u16 pb[4][4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u16 pv = f2bf(__builtin_amdgcn_exp2f(sv[kb][i] - msafe));
-                    pb[kb][i] = pv;
-                    z += bf2f(pv);
-                }
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-                if (kc + 32 * mm < kend) {
-                    uint4 pw;
-                    pw.x = pack2(pb[2 * mm][0], pb[2 * mm][1]);
-                    pw.y = pack2(pb[2 * mm][2], pb[2 * mm][3]);
-                    pw.z = pack2(pb[2 * mm + 1][0], pb[2 * mm + 1][1]);
-                    pw.w = pack2(pb[2 * mm + 1][2], pb[2 * mm + 1][3]);
-                    const bf16x8 pbv = as_bf16x8(pw);
-#pragma unroll
-                    for (int jb = 0; jb < C::NJ; ++jb) {
-                        const u16* vr = &lvt[(16 * jb + r16) * C::LDV + kc + 32 * mm + 4 * g];
-                        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
-                        o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pbv, o[jb]);
+                for (int it = 0; it < C::VPT; ++it) {
+                    const int e = threadIdx.x + it * C::NT;
+                    if (e < WMAX * C::DCH) {
+                        const int r = e / C::DCH, ch = e % C::DCH;
+                        *reinterpret_cast<uint4*>(&lv[r * C::LDX + 8 * ch]) = va[it];
                     }
                 }
+                __syncthreads();
+                values_staged = true;
+                if (kc >= kend) break;
             }
+            if (kc + 64 > clean) {  // chunk reaches the diagonal or the tail: mask
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = kc + 16 * kb + 4 * g + i;
+                        const bool ok = key < w && (!causal || key <= qrow);
+                        sv[kb][i] = ok ? sv[kb][i] : -INFINITY;
+                    }
+            }
+            const int halves = 1 | ((kc + 32 < kend) ? 2 : 0);
+            softmax_pv_chunk<C::NJ, C::LDX>(sv, m, z, o, &lv[kc * C::LDX], r16, g, halves);
         }
+        if (!active) continue;
 
         const float zt = xor_sum_16_32(z);
         const float rz = 1.0f / zt;
@@ -279,15 +292,17 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT)) void cluster_attn_b
             if (g == 0 && lse != nullptr)
                 lse[rowbase + qrow] = (m + __log2f(zt)) * 0.6931471805599453f;
             const int t = lpos[qrow];
+            const int dest = ldest[qrow];
             if (t >= 0) {
-                if (lsingle[qrow]) {
+                if (dest == -1) {
                     OutT* dst = out + (tokbase + t) * D + 4 * g;
 #pragma unroll
                     for (int jb = 0; jb < C::NJ; ++jb)
                         store4<OutT>(dst + 16 * jb, o[jb][0] * rz, o[jb][1] * rz, o[jb][2] * rz,
                                      o[jb][3] * rz);
                 } else {
-                    float* dst = part + (rowbase + qrow) * D + 4 * g;
+                    float* dst = (dest < kSlots ? slots + ((tokbase + t) * kSlots + dest) * D
+                                                : ovf + (rowbase + qrow) * D) + 4 * g;
 #pragma unroll
                     for (int jb = 0; jb < C::NJ; ++jb)
                         store4<float>(dst + 16 * jb, o[jb][0] * rz, o[jb][1] * rz, o[jb][2] * rz,
@@ -303,9 +318,9 @@ template <int D, typename OutT>
 __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kk, const float* __restrict__ v,
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ cnt, int n, int k, int w,
-    float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part) {
+    const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
+    int KW, float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ slots, float* __restrict__ ovf) {
     __shared__ float lg[1024];
     __shared__ float lqrow[D];
     const int r = blockIdx.x, cl = blockIdx.y, bh = blockIdx.z;
@@ -341,7 +356,7 @@ __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
     __syncthreads();
     const bool valid = raw >= 0 && raw < n;
-    const bool single = valid && cnt[tokbase + raw] == 1u;
+    const int dest = valid ? row_dest(mask + (tokbase + raw) * KW, KW, cl) : -2;
     for (int i = lane; i < D; i += 64) {
         float acc = 0.f;
         if (z > 0.f) {
@@ -349,122 +364,153 @@ __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
                 if (lg[s] != 0.f) acc = fmaf(lg[s], v[(tokbase + clamp_pos(irow[s], n)) * D + i], acc);
             acc /= z;
         }
-        if (valid) {
-            if (single) Elem<OutT>::store(out, (tokbase + raw) * D + i, acc);
-            else part[(rowbase + r) * D + i] = acc;
-        }
+        if (dest == -1) Elem<OutT>::store(out, (tokbase + raw) * D + i, acc);
+        else if (dest >= 0 && dest < kSlots) slots[((tokbase + raw) * kSlots + dest) * D + i] = acc;
+        else if (dest >= kSlots) ovf[(rowbase + r) * D + i] = acc;
     }
     if (lane == 0 && lse != nullptr) lse[rowbase + r] = (z > 0.f) ? m + logf(z) : -INFINITY;
 }
 
-// One thread per (token, 4 output dims).  The token's list entries c*w + r
-// are visited in increasing order (selection over the short list), so the
-// sum runs in ascending centroid order whatever order the list was filled in.
+// float32 inputs: per-cluster sums of the normalised member rows.
+__global__ __launch_bounds__(128) void cluster_sums_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ x_inv, const int32_t* __restrict__ idx,
+    int n, int D, int k, int w, float* __restrict__ sums) {
+    const int cl = blockIdx.x, bh = blockIdx.y;
+    const long tokbase = (long)bh * n;
+    const int32_t* irow = idx + ((long)bh * k + cl) * w;
+    for (int dcol = threadIdx.x; dcol < D; dcol += 128) {
+        float acc = 0.f;
+        for (int r = 0; r < w; ++r) {
+            const int t = clamp_pos(irow[r], n);
+            acc = fmaf(x[(tokbase + t) * D + dcol], x_inv ? x_inv[tokbase + t] : 1.f, acc);
+        }
+        sums[((long)bh * k + cl) * D + dcol] = acc;
+    }
+}
+
+// One thread per (token, 4 output dims): the slots hold the rows of ranks
+// 0..kSlots-1 contiguously; higher ranks are found in the overflow buffer by
+// walking the mask in ascending centroid order.
 template <typename OutT>
-__global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ cnt,
-                                                      const int32_t* __restrict__ list,
-                                                      const float* __restrict__ part, long BHn,
-                                                      int n, int D, int k, int w,
+__global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ mask,
+                                                      const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ slots,
+                                                      const float* __restrict__ ovf, long BHn,
+                                                      int n, int D, int k, int w, int KW,
                                                       OutT* __restrict__ out) {
     const int DG = D / 4;
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
     const long tok = gid / DG;
     if (tok >= BHn) return;
     const int dg = (int)(gid % DG);
-    const uint32_t c_tok = cnt[tok];
-    if (c_tok == 1u) return;
-    const int m = (int)min(c_tok, (uint32_t)k);
-    const long bh = tok / n;
-    const int32_t* lst = list + tok * k;
-    const float* pbase = part + bh * (long)k * w * D + 4 * dg;
+    const uint32_t* mrow = mask + tok * KW;
+    int cnt = 0;
+    for (int i = 0; i < KW; ++i) cnt += __popc(mrow[i]);
+    if (cnt == 1) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int prev = -1;
-    for (int j = 0; j < m; ++j) {
-        int best = 0x7fffffff;
-        for (int i = 0; i < m; ++i) {
-            const int e = lst[i];
-            if (e > prev && e < best) best = e;
-        }
-        prev = best;
-        const float4 p = *reinterpret_cast<const float4*>(pbase + (long)best * D);
+    const int direct = min(cnt, kSlots);
+    const float* sp = slots + tok * kSlots * D + 4 * dg;
+    for (int j = 0; j < direct; ++j) {
+        const float4 p = *reinterpret_cast<const float4*>(sp + (long)j * D);
         acc.x += p.x;
         acc.y += p.y;
         acc.z += p.z;
         acc.w += p.w;
     }
-    store4<OutT>(out + tok * D + 4 * dg, acc.x, acc.y, acc.z, acc.w);
-}
-
-template <int D, int WMAX, bool SHARED, typename OutT>
-void launch_bf16(const void* q, const void* kk, const void* v, const float* q_inv,
-                 const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n,
-                 int k, int w, float scale, int causal, void* out, float* lse, float* part,
-                 hipStream_t s) {
-    using C = AttnCfg<D, WMAX, SHARED>;
-    hipLaunchKernelGGL((cluster_attn_bf16_kernel<D, WMAX, SHARED, OutT>), dim3(k, BH),
-                       dim3(C::NT), 0, s, (const u16*)q, (const u16*)kk, (const u16*)v, q_inv,
-                       k_inv, idx, cnt, n, k, w, scale, causal, (OutT*)out, lse, part);
-}
-
-template <int D, bool SHARED, typename OutT>
-void dispatch_w(const void* q, const void* kk, const void* v, const float* q_inv,
-                const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n, int k,
-                int w, float scale, int causal, void* out, float* lse, float* part,
-                hipStream_t s) {
-#define RT_LAUNCH(WM)                                                                          \
-    launch_bf16<D, WM, SHARED, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale,     \
-                                     causal, out, lse, part, s)
-    if (w <= 32) RT_LAUNCH(32);
-    else if (w <= 64) RT_LAUNCH(64);
-    else if (w <= 128) RT_LAUNCH(128);
-    else {
-        if constexpr (SHARED || D <= 64) {
-            if (w <= 256) RT_LAUNCH(256);
-            else {
-                if constexpr (SHARED && D <= 64) RT_LAUNCH(512);
+    if (cnt > kSlots) {
+        const long bh = tok / n;
+        const int t = (int)(tok % n);
+        int seen = 0;
+        for (int wi = 0; wi < KW; ++wi) {
+            uint32_t bits = mrow[wi];
+            while (bits) {
+                const int c = 32 * wi + __ffs(bits) - 1;
+                bits &= bits - 1u;
+                if (seen++ < kSlots) continue;
+                const int32_t* ir = idx + (bh * k + c) * w;
+                int lo = 0, hi = w;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (ir[mid] < t) lo = mid + 1;
+                    else hi = mid;
+                }
+                if (lo < w && ir[lo] == t) {
+                    const float4 p = *reinterpret_cast<const float4*>(ovf + ((bh * k + c) * w + lo) * D + 4 * dg);
+                    acc.x += p.x;
+                    acc.y += p.y;
+                    acc.z += p.z;
+                    acc.w += p.w;
+                }
             }
         }
     }
-#undef RT_LAUNCH
+    store4<OutT>(out + tok * D + 4 * dg, acc.x, acc.y, acc.z, acc.w);
+}
+
+struct AttnArgs {
+    const void *q, *kk, *v;
+    const float *q_inv, *k_inv;
+    const int32_t* idx;
+    const uint32_t* mask;
+    int BH, n, k, w, KW;
+    float scale;
+    int causal;
+    void* out;
+    float *lse, *slots, *ovf, *sum_q, *sum_k;
+};
+
+template <int D, int WMAX, bool SHARED, typename OutT>
+void launch_bf16(const AttnArgs& a, hipStream_t s) {
+    using C = AttnCfg<D, WMAX, SHARED>;
+    hipLaunchKernelGGL((cluster_attn_bf16_kernel<D, WMAX, SHARED, OutT>), dim3(a.k, a.BH),
+                       dim3(C::NT), 0, s, (const u16*)a.q, (const u16*)a.kk, (const u16*)a.v,
+                       a.q_inv, a.k_inv, a.idx, a.mask, a.n, a.k, a.w, a.KW, a.scale, a.causal,
+                       (OutT*)a.out, a.lse, a.slots, a.ovf, a.sum_q, a.sum_k);
+}
+
+template <int D, bool SHARED, typename OutT>
+void dispatch_w(const AttnArgs& a, hipStream_t s) {
+    const int w = a.w;
+    if (w <= 32) launch_bf16<D, 32, SHARED, OutT>(a, s);
+    else if (w <= 64) launch_bf16<D, 64, SHARED, OutT>(a, s);
+    else if (w <= 128) launch_bf16<D, 128, SHARED, OutT>(a, s);
+    else {
+        if constexpr (SHARED || D <= 64) {
+            if (w <= 256) launch_bf16<D, 256, SHARED, OutT>(a, s);
+            else {
+                if constexpr (SHARED && D <= 64) launch_bf16<D, 512, SHARED, OutT>(a, s);
+            }
+        }
+    }
 }
 
 template <int D, typename OutT>
-void launch_f32(const void* q, const void* kk, const void* v, const float* q_inv,
-                const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n, int k,
-                int w, float scale, int causal, void* out, float* lse, float* part,
-                hipStream_t s) {
-    hipLaunchKernelGGL((cluster_attn_f32_kernel<D, OutT>), dim3(w, k, BH), dim3(64), 0, s,
-                       (const float*)q, (const float*)kk, (const float*)v, q_inv, k_inv, idx,
-                       cnt, n, k, w, scale, causal, (OutT*)out, lse, part);
-}
-
-template <int D, typename OutT>
-void launch_d(const void* q, const void* kk, const void* v, int dtype, const float* q_inv,
-              const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n, int k,
-              int w, float scale, int causal, void* out, float* lse, float* part,
-              hipStream_t s) {
+void launch_d(const AttnArgs& a, int dtype, hipStream_t s) {
     if (dtype == 0) {
-        launch_f32<D, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out,
-                            lse, part, s);
-    } else if (q == kk && q_inv == k_inv) {
-        dispatch_w<D, true, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal,
-                                  out, lse, part, s);
+        hipLaunchKernelGGL((cluster_attn_f32_kernel<D, OutT>), dim3(a.w, a.k, a.BH), dim3(64), 0,
+                           s, (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.q_inv,
+                           a.k_inv, a.idx, a.mask, a.n, a.k, a.w, a.KW, a.scale, a.causal,
+                           (OutT*)a.out, a.lse, a.slots, a.ovf);
+        if (a.sum_q)
+            hipLaunchKernelGGL(cluster_sums_f32_kernel, dim3(a.k, a.BH), dim3(128), 0, s,
+                               (const float*)a.q, a.q_inv, a.idx, a.n, D, a.k, a.w, a.sum_q);
+        if (a.sum_k)
+            hipLaunchKernelGGL(cluster_sums_f32_kernel, dim3(a.k, a.BH), dim3(128), 0, s,
+                               (const float*)a.kk, a.k_inv, a.idx, a.n, D, a.k, a.w, a.sum_k);
+    } else if (a.q == a.kk && a.q_inv == a.k_inv) {
+        dispatch_w<D, true, OutT>(a, s);
     } else {
-        dispatch_w<D, false, OutT>(q, kk, v, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal,
-                                   out, lse, part, s);
+        dispatch_w<D, false, OutT>(a, s);
     }
 }
 
 template <typename OutT>
-void launch_outt(const void* q, const void* kk, const void* v, int dtype, const float* q_inv,
-                 const float* k_inv, const int32_t* idx, const uint32_t* cnt, int BH, int n,
-                 int d, int k, int w, float scale, int causal, void* out, float* lse,
-                 float* part, hipStream_t s) {
+void launch_outt(const AttnArgs& a, int dtype, int d, hipStream_t s) {
     switch (d) {
-        case 16: launch_d<16, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
-        case 32: launch_d<32, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
-        case 64: launch_d<64, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
-        default: launch_d<128, OutT>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, k, w, scale, causal, out, lse, part, s); break;
+        case 16: launch_d<16, OutT>(a, dtype, s); break;
+        case 32: launch_d<32, OutT>(a, dtype, s); break;
+        case 64: launch_d<64, OutT>(a, dtype, s); break;
+        default: launch_d<128, OutT>(a, dtype, s); break;
     }
 }
 
@@ -476,42 +522,43 @@ int max_cluster_rows(int dtype, int d, bool shared_qk) {
     return d == 128 ? 128 : 256;
 }
 
-hipError_t launch_membership(const int32_t* idx, int BH, int n, int k, int w, uint32_t* cnt,
-                             int32_t* list, hipStream_t s) {
-    const long count = (long)BH * n;
+hipError_t launch_mask(const int32_t* idx, int BH, int n, int k, int w, uint32_t* mask,
+                       hipStream_t s) {
+    const int KW = mask_words(k);
+    const long count = (long)BH * n * KW;
     hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
-                       cnt, count);
-    hipLaunchKernelGGL(membership_kernel, dim3((w + 255) / 256, k, BH), dim3(256), 0, s, idx, n,
-                       k, w, cnt, list);
+                       mask, count);
+    hipLaunchKernelGGL(mask_kernel, dim3((w + 255) / 256, k, BH), dim3(256), 0, s, idx, n, k, w,
+                       KW, mask);
     return hipGetLastError();
 }
 
 hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int dtype,
                                const float* q_inv, const float* k_inv, const int32_t* idx,
-                               const uint32_t* cnt, int BH, int n, int d, int k, int w,
+                               const uint32_t* mask, int BH, int n, int d, int k, int w,
                                float scale, int causal, void* out, int out_dtype, float* lse,
-                               float* part, hipStream_t s) {
-    if (out_dtype == 1)
-        launch_outt<u16>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, d, k, w, scale, causal,
-                         out, lse, part, s);
-    else
-        launch_outt<float>(q, kk, v, dtype, q_inv, k_inv, idx, cnt, BH, n, d, k, w, scale,
-                           causal, out, lse, part, s);
+                               float* slots, float* ovf, float* sum_q, float* sum_k,
+                               hipStream_t s) {
+    const AttnArgs a{q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, mask_words(k), scale,
+                     causal, out, lse, slots, ovf, sum_q, sum_k};
+    if (out_dtype == 1) launch_outt<u16>(a, dtype, d, s);
+    else launch_outt<float>(a, dtype, d, s);
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const uint32_t* cnt, const int32_t* list, const float* part,
-                          int out_dtype, int BH, int n, int d, int k, int w, void* out,
-                          hipStream_t s) {
+hipError_t launch_combine(const uint32_t* mask, const int32_t* idx, const float* slots,
+                          const float* ovf, int out_dtype, int BH, int n, int d, int k, int w,
+                          void* out, hipStream_t s) {
     const long BHn = (long)BH * n;
     const long threads = BHn * (d / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
+    const int KW = mask_words(k);
     if (out_dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<u16>, grid, dim3(256), 0, s, cnt, list, part, BHn, n, d,
-                           k, w, (u16*)out);
+        hipLaunchKernelGGL(combine_kernel<u16>, grid, dim3(256), 0, s, mask, idx, slots, ovf, BHn,
+                           n, d, k, w, KW, (u16*)out);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, cnt, list, part, BHn, n,
-                           d, k, w, (float*)out);
+        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, mask, idx, slots, ovf,
+                           BHn, n, d, k, w, KW, (float*)out);
     return hipGetLastError();
 }
 

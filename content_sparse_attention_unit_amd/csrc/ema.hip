@@ -93,7 +93,32 @@ __global__ __launch_bounds__(256) void ema_kernel(float* __restrict__ mu, const 
     }
 }
 
+// mu <- lambda*mu + (1-lambda)/2 * (sum over b of sum_q + sum_k): one thread
+// per centroid element, batch rows summed in ascending order.
+__global__ __launch_bounds__(256) void ema_sums_kernel(float* __restrict__ mu,
+                                                       const float* __restrict__ sum_q,
+                                                       const float* __restrict__ sum_k, int B,
+                                                       long HKD, float lam) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= HKD) return;
+    float sq = 0.f, sk = 0.f;
+    for (int b = 0; b < B; ++b) {
+        sq += sum_q[b * HKD + i];
+        if (sum_k != nullptr) sk += sum_k[b * HKD + i];
+    }
+    const float tot = (sum_k != nullptr) ? sq + sk : 2.f * sq;
+    mu[i] = fmaf(lam, mu[i], (1.0f - lam) * 0.5f * tot);
+}
+
 }  // namespace
+
+hipError_t launch_ema_sums(float* mu, const float* sum_q, const float* sum_k, int B, int H,
+                           int k, int d, float lambda, hipStream_t s) {
+    const long HKD = (long)H * k * d;
+    hipLaunchKernelGGL(ema_sums_kernel, dim3((unsigned)((HKD + 255) / 256)), dim3(256), 0, s, mu,
+                       sum_q, sum_k, B, HKD, lambda);
+    return hipGetLastError();
+}
 
 hipError_t launch_ema(float* mu, const void* q, const float* q_inv, const void* kk,
                       const float* k_inv, int dtype, const int32_t* idx, int B, int H, int n,

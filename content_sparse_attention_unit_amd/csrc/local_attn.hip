@@ -21,28 +21,28 @@ namespace {
 template <int D>
 struct LocalCfg {
     static constexpr int DP = D < 32 ? 32 : D;
-    static constexpr int LDX = DP + 8;           // key row stride in LDS (bf16)
+    // key/value row stride in LDS (bf16): an odd multiple of 16 elements, so 8
+    // consecutive rows start in disjoint bank groups
+    static constexpr int LDX = DP + 16;
     static constexpr int KT = 64;                // keys per tile
-    static constexpr int LDV = KT + 8;           // transposed value row stride (bf16)
     static constexpr int NS = DP / 32;
     static constexpr int NJ = D / 16;
-    static constexpr int QB = 2;                 // 16-query blocks per wave
-    static constexpr int QT = 4 * 16 * QB;       // queries per workgroup (4 waves)
+    static constexpr int NWV = 8;                // waves per workgroup, 16 queries each
+    static constexpr int NT = 64 * NWV;
+    static constexpr int QT = 16 * NWV;          // queries per workgroup
     static constexpr int CPR = DP / 8;
     static constexpr int DCH = D / 8;
-    static constexpr int KPT = (KT * CPR) / 256;         // key chunks per thread per tile
-    static constexpr int VITEMS = (KT / 2) * DCH;         // value row-pair chunks per tile
-    static constexpr int VPT = (VITEMS + 255) / 256;       // ... per thread
+    static constexpr int KITEMS = KT * CPR;                // key row chunks per tile
+    static constexpr int KPT = (KITEMS + NT - 1) / NT;     // ... per thread
+    static constexpr int VITEMS = KT * DCH;                // value row chunks per tile
+    static constexpr int VPT = (VITEMS + NT - 1) / NT;     // ... per thread
 };
 
 template <typename OutT>
 __device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
 template <>
 __device__ __forceinline__ void store4<u16>(u16* dst, float a, float b, float c, float d) {
-    uint2 pk;
-    pk.x = pack2(f2bf(a), f2bf(b));
-    pk.y = pack2(f2bf(c), f2bf(d));
-    *reinterpret_cast<uint2*>(dst) = pk;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(cvt_pk_bf16(a, b), cvt_pk_bf16(c, d));
 }
 template <>
 __device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
@@ -51,9 +51,8 @@ __device__ __forceinline__ void store4<float>(float* dst, float a, float b, floa
 
 template <int D>
 struct TileRegs {
-    uint4 k[LocalCfg<D>::KPT > 0 ? LocalCfg<D>::KPT : 1];
-    uint4 va[LocalCfg<D>::VPT > 0 ? LocalCfg<D>::VPT : 1];
-    uint4 vb[LocalCfg<D>::VPT > 0 ? LocalCfg<D>::VPT : 1];
+    uint4 k[LocalCfg<D>::KPT];
+    uint4 va[LocalCfg<D>::VPT];
 };
 
 template <int D>
@@ -62,59 +61,49 @@ __device__ __forceinline__ void load_tile(TileRegs<D>& tr, const u16* __restrict
     using C = LocalCfg<D>;
 #pragma unroll
     for (int it = 0; it < C::KPT; ++it) {
-        const int e = threadIdx.x + 256 * it;
+        const int e = threadIdx.x + C::NT * it;
         const int r = e / C::CPR, ch = e % C::CPR;
-        const int j = kt + r;
+        const int j = (e < C::KITEMS) ? kt + r : n;
         tr.k[it] = (j < n && 8 * ch < D) ? *reinterpret_cast<const uint4*>(kk + (base + j) * D + 8 * ch)
                                          : zero_u4();
     }
 #pragma unroll
     for (int it = 0; it < C::VPT; ++it) {
-        const int e = threadIdx.x + 256 * it;
-        const int rp = e / C::DCH, ch = e % C::DCH;
-        const int j0 = (e < C::VITEMS) ? kt + 2 * rp : n;
-        tr.va[it] = (j0 < n) ? *reinterpret_cast<const uint4*>(v + (base + j0) * D + 8 * ch) : zero_u4();
-        tr.vb[it] = (j0 + 1 < n) ? *reinterpret_cast<const uint4*>(v + (base + j0 + 1) * D + 8 * ch)
-                                 : zero_u4();
+        const int e = threadIdx.x + C::NT * it;
+        const int r = e / C::DCH, ch = e % C::DCH;
+        const int j = (e < C::VITEMS) ? kt + r : n;
+        tr.va[it] = (j < n) ? *reinterpret_cast<const uint4*>(v + (base + j) * D + 8 * ch) : zero_u4();
     }
 }
 
 template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& tr, u16* lk, u16* lvt) {
+__device__ __forceinline__ void store_tile(const TileRegs<D>& tr, u16* lk, u16* lv) {
     using C = LocalCfg<D>;
 #pragma unroll
     for (int it = 0; it < C::KPT; ++it) {
-        const int e = threadIdx.x + 256 * it;
+        const int e = threadIdx.x + C::NT * it;
+        if (e >= C::KITEMS) continue;
         const int r = e / C::CPR, ch = e % C::CPR;
         *reinterpret_cast<uint4*>(&lk[r * C::LDX + 8 * ch]) = tr.k[it];
     }
 #pragma unroll
     for (int it = 0; it < C::VPT; ++it) {
-        const int e = threadIdx.x + 256 * it;
+        const int e = threadIdx.x + C::NT * it;
         if (e >= C::VITEMS) continue;
-        const int rp = e / C::DCH, ch = e % C::DCH;
-        const uint32_t* aw = reinterpret_cast<const uint32_t*>(&tr.va[it]);
-        const uint32_t* bw = reinterpret_cast<const uint32_t*>(&tr.vb[it]);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const int jj = 8 * ch + 2 * e2;
-            *reinterpret_cast<uint32_t*>(&lvt[jj * C::LDV + 2 * rp]) = (aw[e2] & 0xffffu) | (bw[e2] << 16);
-            *reinterpret_cast<uint32_t*>(&lvt[(jj + 1) * C::LDV + 2 * rp]) =
-                (aw[e2] >> 16) | (bw[e2] & 0xffff0000u);
-        }
+        const int r = e / C::DCH, ch = e % C::DCH;
+        *reinterpret_cast<uint4*>(&lv[r * C::LDX + 8 * ch]) = tr.va[it];
     }
 }
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(256) void local_attn_bf16_kernel(const u16* __restrict__ q,
+__global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restrict__ q,
                                                               const u16* __restrict__ kk,
                                                               const u16* __restrict__ v, int n,
                                                               int window, float scale, int causal,
                                                               OutT* __restrict__ out) {
     using C = LocalCfg<D>;
-    static_assert(C::KPT * 256 == C::KT * C::CPR, "key tile must split evenly over 256 threads");
     __shared__ __attribute__((aligned(16))) u16 lk[2][C::KT * C::LDX];
-    __shared__ __attribute__((aligned(16))) u16 lvt[2][D * C::LDV];
+    __shared__ __attribute__((aligned(16))) u16 lv[2][C::KT * C::LDX];
 
     const int bh = blockIdx.y;
     const int q0 = blockIdx.x * C::QT;
@@ -122,54 +111,43 @@ __global__ __launch_bounds__(256) void local_attn_bf16_kernel(const u16* __restr
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const float sl2 = scale * 1.4426950408889634f;
+    const int qb0 = q0 + 16 * wv;      // first query of this wave's block
+    const int qi = qb0 + r16;          // this lane's query
 
-    // This wave's query blocks: rows q0 + 16*(wv + 4*b) + r16, b < QB.
-    uint4 qreg[C::QB][C::NS];
-    int qi[C::QB];
+    uint4 qreg[C::NS];
 #pragma unroll
-    for (int b = 0; b < C::QB; ++b) {
-        qi[b] = q0 + 16 * (wv + 4 * b) + r16;
-#pragma unroll
-        for (int s = 0; s < C::NS; ++s) {
-            const int d0 = 32 * s + 8 * g;
-            qreg[b][s] = (qi[b] < n && d0 < D)
-                             ? *reinterpret_cast<const uint4*>(q + (base + qi[b]) * D + d0)
-                             : zero_u4();
-        }
+    for (int s = 0; s < C::NS; ++s) {
+        const int d0 = 32 * s + 8 * g;
+        qreg[s] = (qi < n && d0 < D) ? *reinterpret_cast<const uint4*>(q + (base + qi) * D + d0)
+                                     : zero_u4();
     }
+    // keys needed by the workgroup / by this wave's block; keys in [clo, chi]
+    // are visible to every query of the block
     const int lo = max(0, q0 - window + 1);
     const int hi = causal ? min(n - 1, q0 + C::QT - 1) : min(n - 1, q0 + C::QT - 1 + window - 1);
+    const int blo = qb0 - window + 1;
+    const int bhi = causal ? qb0 + 15 : qb0 + 15 + window - 1;
+    const int clo = qb0 + 15 - window + 1;
+    const int chi = min(n - 1, causal ? qb0 : qb0 + window - 1);
 
-    f32x4 o[C::QB][C::NJ];
-    float m[C::QB], z[C::QB];
+    f32x4 o[C::NJ];
 #pragma unroll
-    for (int b = 0; b < C::QB; ++b) {
-        m[b] = -INFINITY;
-        z[b] = 0.f;
-#pragma unroll
-        for (int jb = 0; jb < C::NJ; ++jb) o[b][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int jb = 0; jb < C::NJ; ++jb) o[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, z = 0.f;
 
     const int kt_first = lo & ~(C::KT - 1);
     TileRegs<D> tr;
     load_tile<D>(tr, kk, v, base, n, kt_first);
-    store_tile<D>(tr, lk[0], lvt[0]);
+    store_tile<D>(tr, lk[0], lv[0]);
     __syncthreads();
 
     int buf = 0;
     for (int kt = kt_first; kt <= hi; kt += C::KT) {
         const bool more = kt + C::KT <= hi;
         if (more) load_tile<D>(tr, kk, v, base, n, kt + C::KT);   // in flight during compute
-        const u16* LK = lk[buf];
-        const u16* LV = lvt[buf];
-#pragma unroll
-        for (int b = 0; b < C::QB; ++b) {
-            const int qb0 = q0 + 16 * (wv + 4 * b);        // first query of the block
-            const int blo = qb0 - window + 1;
-            const int bhi = causal ? qb0 + 15 : qb0 + 15 + window - 1;
-            if (kt + C::KT - 1 < blo || kt > bhi) continue;  // wave-uniform skip
+        if (kt + C::KT - 1 >= blo && kt <= bhi) {               // tile meets this wave's band
+            const u16* LK = lk[buf];
             f32x4 sv[4];
-            float cmax = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int key0 = kt + 16 * kb;
@@ -177,76 +155,44 @@ __global__ __launch_bounds__(256) void local_attn_bf16_kernel(const u16* __restr
                     sv[kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
                     continue;
                 }
-                sv[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < C::NS; ++s) {
                     const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
                         &LK[(16 * kb + r16) * C::LDX + 32 * s + 8 * g]));
-                    sv[kb] = mfma16(a, as_bf16x8(qreg[b][s]), sv[kb]);
+                    acc = mfma16(a, as_bf16x8(qreg[s]), acc);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = key0 + 4 * g + i;
-                    const bool ok = j < n && j > qi[b] - window &&
-                                    (causal ? j <= qi[b] : j < qi[b] + window);
-                    sv[kb][i] = ok ? sv[kb][i] * sl2 : -INFINITY;
-                    cmax = fmaxf(cmax, sv[kb][i]);
-                }
+                sv[kb] = acc * sl2;
             }
-            cmax = xor_max_16_32(cmax);
-            const float mnew = fmaxf(m[b], cmax);
-            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(m[b] - msafe);
-            z[b] *= alpha;
+            if (kt < clo || kt + C::KT - 1 > chi) {   // tile not entirely inside every band
 #pragma unroll
-            for (int jb = 0; jb < C::NJ; ++jb) o[b][jb] *= alpha;
-            m[b] = mnew;
-
-            u16 pb[4][4];
+                for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u16 pv = f2bf(__builtin_amdgcn_exp2f(sv[kb][i] - msafe));
-                    pb[kb][i] = pv;
-                    z[b] += bf2f(pv);
-                }
-#pragma unroll
-            for (int mm = 0; mm < 2; ++mm) {
-                uint4 pw;
-                pw.x = pack2(pb[2 * mm][0], pb[2 * mm][1]);
-                pw.y = pack2(pb[2 * mm][2], pb[2 * mm][3]);
-                pw.z = pack2(pb[2 * mm + 1][0], pb[2 * mm + 1][1]);
-                pw.w = pack2(pb[2 * mm + 1][2], pb[2 * mm + 1][3]);
-                if (__ballot((pw.x | pw.y | pw.z | pw.w) != 0u) == 0ull) continue;  // wave-uniform
-                const bf16x8 pbv = as_bf16x8(pw);
-#pragma unroll
-                for (int jb = 0; jb < C::NJ; ++jb) {
-                    const u16* vr = &LV[(16 * jb + r16) * C::LDV + 32 * mm + 4 * g];
-                    const uint2 l2 = *reinterpret_cast<const uint2*>(vr);
-                    const uint2 h2 = *reinterpret_cast<const uint2*>(vr + 16);
-                    o[b][jb] = mfma16(as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y)), pbv, o[b][jb]);
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = kt + 16 * kb + 4 * g + i;
+                        const bool ok = j < n && j > qi - window &&
+                                        (causal ? j <= qi : j < qi + window);
+                        sv[kb][i] = ok ? sv[kb][i] : -INFINITY;
+                    }
             }
+            const int halves = ((kt + 31 >= blo && kt <= bhi) ? 1 : 0) |
+                               ((kt + 63 >= blo && kt + 32 <= bhi) ? 2 : 0);
+            softmax_pv_chunk<C::NJ, C::LDX>(sv, m, z, o, lv[buf], r16, g, halves);
         }
         if (more) {
-            store_tile<D>(tr, lk[buf ^ 1], lvt[buf ^ 1]);
+            store_tile<D>(tr, lk[buf ^ 1], lv[buf ^ 1]);
             __syncthreads();
             buf ^= 1;
         }
     }
 
+    const float zt = xor_sum_16_32(z);
+    const float rz = 1.0f / zt;
+    if (qi < n) {
+        OutT* dst = out + (base + qi) * D + 4 * g;
 #pragma unroll
-    for (int b = 0; b < C::QB; ++b) {
-        const float zt = xor_sum_16_32(z[b]);
-        const float rz = 1.0f / zt;
-        if (qi[b] < n) {
-            OutT* dst = out + (base + qi[b]) * D + 4 * g;
-#pragma unroll
-            for (int jb = 0; jb < C::NJ; ++jb)
-                store4<OutT>(dst + 16 * jb, o[b][jb][0] * rz, o[b][jb][1] * rz, o[b][jb][2] * rz,
-                             o[b][jb][3] * rz);
-        }
+        for (int jb = 0; jb < C::NJ; ++jb)
+            store4<OutT>(dst + 16 * jb, o[jb][0] * rz, o[jb][1] * rz, o[jb][2] * rz, o[jb][3] * rz);
     }
 }
 
@@ -310,7 +256,8 @@ void launch_local_d(const void* q, const void* kk, const void* v, int dtype, int
                     int window, float scale, int causal, void* out, hipStream_t s) {
     if (dtype == 1)
         hipLaunchKernelGGL((local_attn_bf16_kernel<D, OutT>),
-                           dim3((n + LocalCfg<D>::QT - 1) / LocalCfg<D>::QT, BH), dim3(256), 0, s,
+                           dim3((n + LocalCfg<D>::QT - 1) / LocalCfg<D>::QT, BH),
+                           dim3(LocalCfg<D>::NT), 0, s,
                            (const u16*)q, (const u16*)kk, (const u16*)v, n, window, scale, causal,
                            (OutT*)out);
     else

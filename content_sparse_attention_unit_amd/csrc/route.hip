@@ -44,7 +44,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
                                                          int n, int k,
                                                          float* __restrict__ inv_norm,
                                                          float* __restrict__ scores,
-                                                         u16* __restrict__ qk_hat) {
+                                                         u16* __restrict__ qk_hat,
+                                                         uint32_t* __restrict__ mask, int KW) {
     using C = ScoreCfg<D>;
     __shared__ __attribute__((aligned(16))) u16 lmu[3][C::KC][C::LD];
 
@@ -76,7 +77,11 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
         }
         ss = xor_sum_16_32(ss);
         inv[tb] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
-        if (g == 0 && t < n) inv_norm[base + t] = inv[tb];
+        if (g == 0 && t < n) {
+            inv_norm[base + t] = inv[tb];
+            if (mask != nullptr)
+                for (int i = 0; i < KW; ++i) mask[(base + t) * KW + i] = 0u;
+        }
         if (qk_hat != nullptr && t < n) {
 #pragma unroll
             for (int s = 0; s < C::NS; ++s) {
@@ -139,7 +144,8 @@ __global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict_
                                                         const float* __restrict__ mu, int H, int n,
                                                         int k, float* __restrict__ inv_norm,
                                                         float* __restrict__ scores,
-                                                        float* __restrict__ qk_hat) {
+                                                        float* __restrict__ qk_hat,
+                                                        uint32_t* __restrict__ mask, int KW) {
     constexpr int KC = 8192 / D;  // 32 KB of centroids per chunk
     __shared__ float lmu[KC * D];
     const int bh = blockIdx.y, h = bh % H;
@@ -155,6 +161,8 @@ __global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict_
     const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
     if (t < n) {
         inv_norm[base + t] = inv;
+        if (mask != nullptr)
+            for (int i = 0; i < KW; ++i) mask[(base + t) * KW + i] = 0u;
         if (qk_hat != nullptr)
             for (int i = 0; i < D; ++i) qk_hat[(base + t) * D + i] = x[i] * inv;
     }
@@ -183,7 +191,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scores, int n, int w,
-                                                  int32_t* __restrict__ idx) {
+                                                  int32_t* __restrict__ idx, int k,
+                                                  uint32_t* __restrict__ mask, int KW) {
     constexpr int NWV = NT / kWave;
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sel_bin, sel_rem;
@@ -274,7 +283,14 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         const bool sel = gt || (eq && eq_before + (uint32_t)lanes_below(em) < need_eq);
         const uint64_t sm = __ballot(sel);
         const uint32_t slot = sel_before + (uint32_t)lanes_below(sm);
-        if (sel && slot < (uint32_t)w) out[slot] = pos;
+        if (sel && slot < (uint32_t)w) {
+            out[slot] = pos;
+            if (mask != nullptr) {
+                const long bh = row / k;
+                const int c = (int)(row % k);
+                atomicOr(&mask[(bh * n + pos) * KW + (c >> 5)], 1u << (c & 31));
+            }
+        }
         eq_before += (uint32_t)__popcll(em);
         sel_before += (uint32_t)__popcll(sm);
     }
@@ -282,49 +298,52 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
 
 template <int D>
 void launch_score_d(const void* qk, int dtype, const float* mu, int BH, int H, int n, int k,
-                    float* inv_norm, float* scores, void* qk_hat, hipStream_t s) {
+                    float* inv_norm, float* scores, void* qk_hat, uint32_t* mask, hipStream_t s) {
     if (dtype == 1) {
         dim3 grid((n + ScoreCfg<D>::TOK - 1) / ScoreCfg<D>::TOK, BH);
         hipLaunchKernelGGL(score_bf16_kernel<D>, grid, dim3(256), 0, s, (const u16*)qk, mu, H, n,
-                           k, inv_norm, scores, (u16*)qk_hat);
+                           k, inv_norm, scores, (u16*)qk_hat, mask, mask_words(k));
     } else {
         dim3 grid((n + 255) / 256, BH);
         hipLaunchKernelGGL(score_f32_kernel<D>, grid, dim3(256), 0, s, (const float*)qk, mu, H, n,
-                           k, inv_norm, scores, (float*)qk_hat);
+                           k, inv_norm, scores, (float*)qk_hat, mask, mask_words(k));
     }
 }
 
 template <int NT, int KPT>
-void launch_topw_k(const float* scores, int rows, int n, int w, int32_t* idx, hipStream_t s) {
-    hipLaunchKernelGGL((topw_kernel<NT, KPT>), dim3(rows), dim3(NT), 0, s, scores, n, w, idx);
+void launch_topw_k(const float* scores, int rows, int n, int w, int32_t* idx, int k,
+                   uint32_t* mask, hipStream_t s) {
+    hipLaunchKernelGGL((topw_kernel<NT, KPT>), dim3(rows), dim3(NT), 0, s, scores, n, w, idx, k,
+                       mask, mask_words(k));
 }
 
 }  // namespace
 
 hipError_t launch_score(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
-                        int k, float* inv_norm, float* scores, void* qk_hat, hipStream_t s) {
+                        int k, float* inv_norm, float* scores, void* qk_hat, uint32_t* mask,
+                        hipStream_t s) {
     const int BH = B * H;
     switch (d) {
-        case 16: launch_score_d<16>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
-        case 32: launch_score_d<32>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
-        case 64: launch_score_d<64>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
-        default: launch_score_d<128>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, s); break;
+        case 16: launch_score_d<16>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
+        case 32: launch_score_d<32>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
+        case 64: launch_score_d<64>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
+        default: launch_score_d<128>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t* idx,
-                       hipStream_t s) {
+                       uint32_t* mask, hipStream_t s) {
     const int rows = BH * k;
     const int per = (n + 511) / 512;
-    if (per <= 1) launch_topw_k<512, 1>(scores, rows, n, w, idx, s);
-    else if (per <= 2) launch_topw_k<512, 2>(scores, rows, n, w, idx, s);
-    else if (per <= 4) launch_topw_k<512, 4>(scores, rows, n, w, idx, s);
-    else if (per <= 8) launch_topw_k<512, 8>(scores, rows, n, w, idx, s);
-    else if (per <= 16) launch_topw_k<512, 16>(scores, rows, n, w, idx, s);
-    else if (per <= 32) launch_topw_k<512, 32>(scores, rows, n, w, idx, s);
-    else if (per <= 64) launch_topw_k<512, 64>(scores, rows, n, w, idx, s);
-    else launch_topw_k<1024, 64>(scores, rows, n, w, idx, s);
+    if (per <= 1) launch_topw_k<512, 1>(scores, rows, n, w, idx, k, mask, s);
+    else if (per <= 2) launch_topw_k<512, 2>(scores, rows, n, w, idx, k, mask, s);
+    else if (per <= 4) launch_topw_k<512, 4>(scores, rows, n, w, idx, k, mask, s);
+    else if (per <= 8) launch_topw_k<512, 8>(scores, rows, n, w, idx, k, mask, s);
+    else if (per <= 16) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
+    else if (per <= 32) launch_topw_k<512, 32>(scores, rows, n, w, idx, k, mask, s);
+    else if (per <= 64) launch_topw_k<512, 64>(scores, rows, n, w, idx, k, mask, s);
+    else launch_topw_k<1024, 64>(scores, rows, n, w, idx, k, mask, s);
     return hipGetLastError();
 }
 

@@ -16,13 +16,18 @@ constexpr int kWave = 64;
 // ---- bfloat16 <-> float32 ----------------------------------------------------
 __device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ u16 f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u16)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (u16)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two float32 -> packed bf16 (a in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+// Round to nearest even (NaN stays NaN).
+__device__ __forceinline__ u16 f2bf(float f) { return (u16)(cvt_pk_bf16(f, 0.f) & 0xffffu); }
 
 // 8 bf16 values packed in a uint4 (16 bytes) <-> MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -45,6 +50,76 @@ __device__ __forceinline__ uint32_t pack2(u16 lo, u16 hi) { return (uint32_t)lo 
 // operands alike gives the same product.
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i receives
+// element (i % 4) of the 4-element (8-byte) rows addressed by lanes
+// i/4, i/4 + 4, i/4 + 8 and i/4 + 12, in that order.  With a row-major
+// [key][dim] tile and source lane s pointing at key (k0 + s/4), dims
+// (d0 + 4*(s%4)) .. +3, lane i receives V[k0 + m][d0 + i] for m = 0..3: the
+// transposed operand an MFMA needs, without transposing the tile in memory.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const u16* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+#else
+    (void)p;
+    return make_uint2(0u, 0u);
+#endif
+}
+
+// Online-softmax step shared by the attention kernels.  `sv[kb][i]` holds the
+// logits, in log2 units, of keys kc + 16*kb + 4*g + i for this lane's query
+// (-inf where masked).  Updates the running max `m` and denominator `z`,
+// rescales the NJ accumulators O^T (16 x 16 tiles, rows = value dims), and
+// accumulates O^T += V^T P^T for the 64 keys of the chunk; `lv` points at the
+// chunk's first key row of the row-major value tile (row stride LDX), and
+// `halves` says which 32-key halves hold any visible key (wave-uniform).
+template <int NJ, int LDX>
+__device__ __forceinline__ void softmax_pv_chunk(f32x4 (&sv)[4], float& m, float& z,
+                                                 f32x4 (&o)[NJ], const u16* lv, int r16, int g,
+                                                 int halves) {
+    float cmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    cmax = fmaxf(cmax, fmaxf(fmaxf(fmaxf(sv[2][0], sv[2][1]), fmaxf(sv[2][2], sv[2][3])),
+                             fmaxf(fmaxf(sv[3][0], sv[3][1]), fmaxf(sv[3][2], sv[3][3]))));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float mnew = fmaxf(m, cmax);
+    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+    if (__ballot(mnew != m) != 0ull) {  // some lane's max moved: rescale (wave-uniform branch)
+        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+        z *= alpha;
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) o[jb] *= alpha;
+        m = mnew;
+    }
+    uint32_t pw[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[kb][0] - msafe);
+        const float p1 = __builtin_amdgcn_exp2f(sv[kb][1] - msafe);
+        const float p2 = __builtin_amdgcn_exp2f(sv[kb][2] - msafe);
+        const float p3 = __builtin_amdgcn_exp2f(sv[kb][3] - msafe);
+        z += (p0 + p1) + (p2 + p3);
+        pw[kb][0] = cvt_pk_bf16(p0, p1);
+        pw[kb][1] = cvt_pk_bf16(p2, p3);
+    }
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+        if (!(halves & (1 << mm))) continue;
+        // B operand: lane's keys 32mm + 4g + (0..3) and 32mm + 16 + 4g + (0..3)
+        const bf16x8 pbv = as_bf16x8(make_uint4(pw[2 * mm][0], pw[2 * mm][1], pw[2 * mm + 1][0],
+                                                pw[2 * mm + 1][1]));
+        const u16* vb = lv + (32 * mm + 4 * g + (r16 >> 2)) * LDX + 4 * (r16 & 3);
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+            const uint2 lo = lds_read_tr16(vb + 16 * jb);
+            const uint2 hi = lds_read_tr16(vb + 16 * LDX + 16 * jb);
+            o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pbv, o[jb]);
+        }
+    }
 }
 
 // ---- wave helpers --------------------------------------------------------------

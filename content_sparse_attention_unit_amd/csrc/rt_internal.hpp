@@ -16,26 +16,41 @@ int max_cluster_rows(int dtype, int d, bool shared_qk);
 // Largest sequence the top-w kernel holds in registers.
 constexpr int kMaxSeqTopw = 65536;
 
+// mask (nullable) [B*H*n][mask_words(k)]: zeroed by the score kernel, filled
+// by the top-w kernel.
 hipError_t launch_score(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
-                        int k, float* inv_norm, float* scores, void* qk_hat, hipStream_t s);
+                        int k, float* inv_norm, float* scores, void* qk_hat, uint32_t* mask,
+                        hipStream_t s);
 
 hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t* idx,
-                       hipStream_t s);
+                       uint32_t* mask, hipStream_t s);
 
-// Per-token membership counters cnt [BH*n] and lists list [BH*n][k] of
-// c*w + r entries (unordered).
-hipError_t launch_membership(const int32_t* idx, int BH, int n, int k, int w, uint32_t* cnt,
-                             int32_t* list, hipStream_t s);
+// Words of the per-token membership bitmask (one bit per centroid).
+inline int mask_words(int k) { return (k + 31) / 32; }
+
+// Token-major partial-row slots per token; higher membership ranks overflow
+// to a cluster-major buffer.
+constexpr int kSlots = 4;
+
+// Zero the bitmask mask [BH*n][mask_words(k)] and set one bit per membership.
+hipError_t launch_mask(const int32_t* idx, int BH, int n, int k, int w, uint32_t* mask,
+                       hipStream_t s);
 
 hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int dtype,
                                const float* q_inv, const float* k_inv, const int32_t* idx,
-                               const uint32_t* cnt, int BH, int n, int d, int k, int w,
+                               const uint32_t* mask, int BH, int n, int d, int k, int w,
                                float scale, int causal, void* out, int out_dtype, float* lse,
-                               float* part, hipStream_t s);
+                               float* slots, float* ovf, float* sum_q, float* sum_k,
+                               hipStream_t s);
 
-hipError_t launch_combine(const uint32_t* cnt, const int32_t* list, const float* part,
-                          int out_dtype, int BH, int n, int d, int k, int w, void* out,
-                          hipStream_t s);
+hipError_t launch_combine(const uint32_t* mask, const int32_t* idx, const float* slots,
+                          const float* ovf, int out_dtype, int BH, int n, int d, int k, int w,
+                          void* out, hipStream_t s);
+
+// mu <- lambda*mu + (1-lambda)/2 * (sum_b sum_q[b] + sum_b sum_k[b]); sum_k may
+// be NULL (keys are the queries: S_K = S_Q).  sums are [B][H][k][d].
+hipError_t launch_ema_sums(float* mu, const float* sum_q, const float* sum_k, int B, int H,
+                           int k, int d, float lambda, hipStream_t s);
 
 hipError_t launch_ema(float* mu, const void* q, const float* q_inv, const void* kk,
                       const float* k_inv, int dtype, const int32_t* idx, int B, int H, int n,

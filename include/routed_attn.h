@@ -80,6 +80,9 @@ typedef enum {
  *             scores: lower position first), listed in ascending position.
  *             Scores are float32-accurate (the bf16 path splits mu into three
  *             bf16 terms so that no precision is lost in the products).
+ *   member_mask  optional out (NULL to skip) [B][H][n][ceil(k/32)] uint32: bit
+ *             c of token t is set iff t is a member of cluster c (the input
+ *             rt_routed_attn would otherwise build from idx).
  *   qk_hat    optional out (NULL to skip) [B][H][n][d] dtype: qk * inv_norm.
  *   scores    optional out (NULL to skip) [B][H][k][n] float32: the inner
  *             products <qk_t * inv_norm_t, mu_c>.  When NULL the scores live
@@ -87,8 +90,8 @@ typedef enum {
  *   ws        rt_workspace_bytes(RT_OP_ROUTE, ...) bytes (0 when scores != NULL).
  */
 rt_status rt_route(const void *qk, int dtype, const float *mu, int B, int H, int n, int d, int k,
-                   int w, float *inv_norm, int32_t *idx, void *qk_hat, float *scores, void *ws,
-                   size_t ws_bytes, void *stream);
+                   int w, float *inv_norm, int32_t *idx, uint32_t *member_mask, void *qk_hat,
+                   float *scores, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * rt_routed_attn -- attention inside each cluster, scatter-added back.
@@ -104,6 +107,9 @@ rt_status rt_route(const void *qk, int dtype, const float *mu, int B, int H, int
  *   idx        [B][H][k][w] int32 memberships: each row strictly increasing
  *              positions in [0, n) (rows that are not give unspecified
  *              results; out-of-range values are clamped, never dereferenced).
+ *   member_mask   optional [B][H][n][ceil(k/32)] uint32 membership bits
+ *              consistent with idx (as rt_route emits them); NULL: built from
+ *              idx in the workspace.
  *   causal     1: member s is visible to member r iff pos(s) <= pos(r);
  *              0: every member sees every member.
  *   out        out [B][H][n][d] of element type out_dtype (RT_F32 or RT_BF16,
@@ -115,15 +121,19 @@ rt_status rt_route(const void *qk, int dtype, const float *mu, int B, int H, int
  *              float32 output.
  *   lse        optional out (NULL to skip) [B][H][k][w] float32: natural log
  *              of each row's softmax denominator, max + log(sum exp).
- *   ws         rt_workspace_bytes(RT_OP_ROUTED_ATTN, ...) bytes: per-token
- *              membership counters and lists, and float32 partial rows of
- *              tokens that several clusters hold.
+ *   sum_q, sum_k  optional outs (NULL to skip) [B][H][k][d] float32: per
+ *              cluster, the sum over its members of q*q_inv (resp. kk*k_inv),
+ *              the input of rt_centroid_update_sums.
+ *   ws         rt_workspace_bytes(RT_OP_ROUTED_ATTN, ...) bytes: membership
+ *              bits and float32 partial rows of tokens that several clusters
+ *              hold.
  *   Deterministic: repeated calls give bit-identical results.
  */
 rt_status rt_routed_attn(const void *q, const void *kk, const void *v, int dtype,
-                         const float *q_inv, const float *k_inv, const int32_t *idx, int B, int H,
-                         int n, int d, int k, int w, float scale, int causal, void *out,
-                         int out_dtype, float *lse, void *ws, size_t ws_bytes, void *stream);
+                         const float *q_inv, const float *k_inv, const int32_t *idx,
+                         const uint32_t *member_mask, int B, int H, int n, int d, int k, int w,
+                         float scale, int causal, void *out, int out_dtype, float *lse,
+                         float *sum_q, float *sum_k, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * rt_local_attn -- sliding-window attention for the non-routed heads.
@@ -161,6 +171,15 @@ rt_status rt_local_attn(const void *q, const void *kk, const void *v, int dtype,
 rt_status rt_centroid_update(float *mu, const void *q, const float *q_inv, const void *kk,
                              const float *k_inv, int dtype, const int32_t *idx, int B, int H, int n,
                              int d, int k, int w, float lambda, void *stream);
+
+/*
+ * rt_centroid_update_sums -- the same update as rt_centroid_update from the
+ *   per-cluster member sums rt_routed_attn emits (sum_q, sum_k [B][H][k][d]
+ *   float32, summed here over b in ascending order); sum_k = NULL when keys
+ *   are the queries (then S_K = S_Q).  mu [H][k][d] updated in place.
+ */
+rt_status rt_centroid_update_sums(float *mu, const float *sum_q, const float *sum_k, int B, int H,
+                                  int k, int d, float lambda, void *stream);
 
 /*
  * rt_routed_attn_bwd -- gradients of rt_routed_attn with respect to its

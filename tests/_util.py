@@ -60,6 +60,19 @@ def assert_exact_rounding(out_storage: torch.Tensor, out_f32: torch.Tensor):
     assert bool(eq.all()), f"{int((~eq).sum())} elements differ from the rounded float32 output"
 
 
+def assert_mask_matches(mask: np.ndarray, idx: np.ndarray, n: int):
+    """The membership bitmask [B,H,n,KW] must have bit c of token t set exactly
+    when t appears in idx[b,h,c]."""
+    B, H, k, _ = idx.shape
+    KW = (k + 31) // 32
+    want = np.zeros((B, H, n, KW), dtype=np.uint32)
+    for b in range(B):
+        for h in range(H):
+            for c in range(k):
+                want[b, h, idx[b, h, c], c // 32] |= np.uint32(1 << (c % 32))
+    assert np.array_equal(mask.astype(np.int64).astype(np.uint32), want)
+
+
 def check_membership(orc, gpu_idx, orc_idx, orc_margin, qk_value, mu, w):
     """Equal rows wherever the oracle's margin exceeds MARGIN; elsewhere the GPU
     row must be a valid top-w of the oracle's scores within MARGIN.  Returns

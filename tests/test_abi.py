@@ -29,7 +29,7 @@ def test_exports_every_declared_function(lib):
     declared = set(re.findall(r"^\s*(?:rt_status|size_t|const char \*|int)\s*\*?\s*(rt_\w+)\s*\(",
                               text, flags=re.M))
     assert {"rt_route", "rt_routed_attn", "rt_local_attn", "rt_centroid_update",
-            "rt_routed_attn_bwd", "rt_workspace_bytes", "rt_status_string", "rt_last_error",
+            "rt_centroid_update_sums", "rt_routed_attn_bwd", "rt_workspace_bytes", "rt_status_string", "rt_last_error",
             "rt_version"} <= declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -43,7 +43,8 @@ def test_status_strings_and_version(lib):
 
 def route(lib, qk=FAKE, dtype=1, mu=FAKE, B=1, H=1, n=64, d=16, k=4, w=16, inv=FAKE, idx=FAKE,
           scores=None, ws=FAKE, ws_bytes=1 << 30):
-    return lib.rt_route(qk, dtype, mu, B, H, n, d, k, w, inv, idx, None, scores, ws, ws_bytes, None)
+    return lib.rt_route(qk, dtype, mu, B, H, n, d, k, w, inv, idx, None, None, scores, ws, ws_bytes,
+                        None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -71,8 +72,8 @@ def test_route_validation(lib, kw, code, msg):
 def attn(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE, B=1, H=1,
          n=64, d=16, k=4, w=16, scale=0.25, causal=1, out=ctypes.c_void_p(0x2000), out_dtype=1,
          lse=None, ws=FAKE, ws_bytes=0):
-    return lib.rt_routed_attn(q, kk, v, dtype, q_inv, k_inv, idx, B, H, n, d, k, w, scale, causal,
-                              out, out_dtype, lse, ws, ws_bytes, None)
+    return lib.rt_routed_attn(q, kk, v, dtype, q_inv, k_inv, idx, None, B, H, n, d, k, w, scale,
+                              causal, out, out_dtype, lse, None, None, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -141,12 +142,26 @@ def test_centroid_update_validation(lib, kw, code, msg):
     assert msg in _last(lib)
 
 
+@pytest.mark.parametrize("args,code,msg", [
+    (dict(mu=None), RT_EINVAL, "null"),
+    (dict(sq=None), RT_EINVAL, "null"),
+    (dict(B=0), RT_EINVAL, "positive"),
+    (dict(lam=2.0), RT_EINVAL, "lambda"),
+])
+def test_centroid_update_sums_validation(lib, args, code, msg):
+    a = dict(mu=FAKE, sq=FAKE, sk=None, B=1, H=1, k=4, d=16, lam=0.5)
+    a.update(args)
+    assert lib.rt_centroid_update_sums(a["mu"], a["sq"], a["sk"], a["B"], a["H"], a["k"], a["d"],
+                                       a["lam"], None) == code
+    assert msg in _last(lib)
+
+
 def test_workspace_sizes(lib):
     B, H, n, d, k, w = 1, 8, 8192, 128, 64, 128
     assert lib.rt_workspace_bytes(0, B, H, n, d, k, w) == B * H * k * n * 4
-    cnt = ((B * H * n * 4 + 255) // 256) * 256
-    lst = ((B * H * n * k * 4 + 255) // 256) * 256
-    assert lib.rt_workspace_bytes(1, B, H, n, d, k, w) == cnt + lst + B * H * k * w * d * 4
+    mask = ((B * H * n * 2 * 4 + 255) // 256) * 256
+    slots = ((B * H * n * 4 * d * 4 + 255) // 256) * 256
+    assert lib.rt_workspace_bytes(1, B, H, n, d, k, w) == mask + slots + B * H * k * w * d * 4
     assert lib.rt_workspace_bytes(2, B, H, n, d, k, w) == 0
     assert lib.rt_workspace_bytes(3, B, H, n, d, k, w) == 0
     assert lib.rt_workspace_bytes(9, B, H, n, d, k, w) == ctypes.c_size_t(-1).value

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import synthetic as S
-from _util import (MU_MAX_ABS, assert_close_out, assert_exact_rounding, check_membership,
-                   dev_tensor, host, tokens_touched)
+from _util import (MU_MAX_ABS, assert_close_out, assert_exact_rounding, assert_mask_matches,
+                   check_membership, dev_tensor, host, tokens_touched)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +114,18 @@ def run_routed_case(rt, orc, cfg, scale=None, causal=True, check_scores=True):
     assert_close_out(host(out_e)[keep], out_o[keep], cfg.dtype, "out end-to-end")
     same_c = ~differs.any(axis=0)                      # [H, k]: identical for every batch row
     assert np.abs(host(mu_e)[same_c] - mu_o[same_c]).max(initial=0.0) <= MU_MAX_ABS
+
+    # fused path: membership bits from route, member sums from the attention
+    inv_f, idx_f, mask_f = rt.route(qk, mu, cfg.w, want_mask=True)
+    sum_q = torch.empty((cfg.B, cfg.R, cfg.k, cfg.d), dtype=torch.float32, device="cuda")
+    out_f = rt.routed_attn(qk, qk, v, idx_f, inv_f, inv_f, scale=sc, causal=causal,
+                           out_dtype=torch.float32, mask=mask_f, sums=(sum_q, None))
+    mu_f = mu.clone()
+    rt.centroid_update_sums_(mu_f, sum_q, cfg.lam)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx) and torch.equal(out_f, out_e)
+    assert_mask_matches(host(mask_f), gidx, cfg.n)
+    assert np.abs(host(mu_f)[same_c] - mu_o[same_c]).max(initial=0.0) <= MU_MAX_ABS
     return dict(inp=inp, qk=qk, v=v, mu=mu, inv=inv, idx=idx, out=out_e, mu_e=mu_e, sc=sc,
                 differs=differs)
 
@@ -151,16 +163,22 @@ def test_distinct_q_and_k(rt, orc, dtype):
     check_membership(orc, host(idx), idx_o, margin_o, inp["qk"].value, inp["mu"], cfg.w)
     idx_o_dev = torch.from_numpy(idx_o).cuda()
     sc = 0.9
-    out = rt.routed_attn(q, kk, v, idx_o_dev, q_inv, k_inv, scale=sc, out_dtype=torch.float32)
+    sq = torch.empty((cfg.B, cfg.R, cfg.k, cfg.d), dtype=torch.float32, device="cuda")
+    sk = torch.empty_like(sq)
+    out = rt.routed_attn(q, kk, v, idx_o_dev, q_inv, k_inv, scale=sc, out_dtype=torch.float32,
+                         sums=(sq, sk))
     out_st = rt.routed_attn(q, kk, v, idx_o_dev, q_inv, k_inv, scale=sc)
     assert_exact_rounding(out_st, out)
     mu2 = mu.clone()
     rt.centroid_update_(mu2, q, q_inv, idx_o_dev, 0.7, kk=kk, k_inv=k_inv)
+    mu3 = mu.clone()
+    rt.centroid_update_sums_(mu3, sq, 0.7, sum_k=sk)
     torch.cuda.synchronize()
     out_o, _, _ = orc.routed_attn(inp["qk"].value, kin.value, inp["v"].value, idx_o, sc, True)
     assert_close_out(host(out), out_o, dtype)
     mu_o = orc.centroid_update(inp["mu"], inp["qk"].value, kin.value, idx_o, 0.7)
     assert np.abs(host(mu2) - mu_o).max() <= MU_MAX_ABS
+    assert np.abs(host(mu3) - mu_o).max() <= MU_MAX_ABS
 
 
 @pytest.mark.parametrize("lam", [0.0, 0.5, 1.0])
