@@ -93,7 +93,8 @@ struct AttnCfg {
     static constexpr int NS = DP / 32;          // MFMA k-steps over d
     static constexpr int NJ = D / 16;           // 16-wide output column blocks
     static constexpr int QROWS = SHARED ? 1 : WMAX;
-    static constexpr int NW = WMAX <= 32 ? 1 : (WMAX <= 64 ? 2 : 4);  // waves per workgroup
+    // waves per workgroup: one or two 16-row query blocks each
+    static constexpr int NW = WMAX <= 32 ? 2 : (WMAX <= 64 ? 4 : 8);
     static constexpr int NT = 64 * NW;
     static constexpr int CPR = DP / 8;          // 16-byte chunks per padded key row
     static constexpr int XPT = (WMAX * CPR + NT - 1) / NT;         // key chunks per thread
@@ -102,7 +103,7 @@ struct AttnCfg {
 };
 
 template <int D, int WMAX, bool SHARED, typename OutT>
-__global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bf16_kernel(
+__global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kk, const u16* __restrict__ v,
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
     const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
@@ -388,34 +389,44 @@ __global__ __launch_bounds__(128) void cluster_sums_f32_kernel(
     }
 }
 
-// One thread per (token, 4 output dims): the slots hold the rows of ranks
+// One thread per (token, 16 output dims): the slots hold the rows of ranks
 // 0..kSlots-1 contiguously; higher ranks are found in the overflow buffer by
 // walking the mask in ascending centroid order.
-template <typename OutT>
+template <typename OutT, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ mask,
                                                       const int32_t* __restrict__ idx,
                                                       const float* __restrict__ slots,
                                                       const float* __restrict__ ovf, long BHn,
-                                                      int n, int D, int k, int w, int KW,
+                                                      int n, int k, int w, int KW,
                                                       OutT* __restrict__ out) {
-    const int DG = D / 4;
+    constexpr int DG = D / 16;
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
     const long tok = gid / DG;
     if (tok >= BHn) return;
-    const int dg = (int)(gid % DG);
+    const int d0 = 16 * (int)(gid % DG);
     const uint32_t* mrow = mask + tok * KW;
     int cnt = 0;
     for (int i = 0; i < KW; ++i) cnt += __popc(mrow[i]);
     if (cnt == 1) return;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int direct = min(cnt, kSlots);
-    const float* sp = slots + tok * kSlots * D + 4 * dg;
-    for (int j = 0; j < direct; ++j) {
-        const float4 p = *reinterpret_cast<const float4*>(sp + (long)j * D);
-        acc.x += p.x;
-        acc.y += p.y;
-        acc.z += p.z;
-        acc.w += p.w;
+    float4 p[kSlots][4];
+    const float* sp = slots + tok * kSlots * D + d0;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            p[j][q] = (j < cnt) ? *reinterpret_cast<const float4*>(sp + (long)j * D + 4 * q)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[q] = p[0][q];
+#pragma unroll
+        for (int j = 1; j < kSlots; ++j) {
+            acc[q].x += p[j][q].x;
+            acc[q].y += p[j][q].y;
+            acc[q].z += p[j][q].z;
+            acc[q].w += p[j][q].w;
+        }
     }
     if (cnt > kSlots) {
         const long bh = tok / n;
@@ -435,16 +446,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
                     else hi = mid;
                 }
                 if (lo < w && ir[lo] == t) {
-                    const float4 p = *reinterpret_cast<const float4*>(ovf + ((bh * k + c) * w + lo) * D + 4 * dg);
-                    acc.x += p.x;
-                    acc.y += p.y;
-                    acc.z += p.z;
-                    acc.w += p.w;
+                    const float* op = ovf + ((bh * k + c) * w + lo) * D + d0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 o = *reinterpret_cast<const float4*>(op + 4 * q);
+                        acc[q].x += o.x;
+                        acc[q].y += o.y;
+                        acc[q].z += o.z;
+                        acc[q].w += o.w;
+                    }
                 }
             }
         }
     }
-    store4<OutT>(out + tok * D + 4 * dg, acc.x, acc.y, acc.z, acc.w);
+    OutT* dst = out + tok * D + d0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store4<OutT>(dst + 4 * q, acc[q].x, acc[q].y, acc[q].z, acc[q].w);
 }
 
 struct AttnArgs {
@@ -546,19 +563,33 @@ hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int
     return hipGetLastError();
 }
 
+template <typename OutT, int D>
+void launch_combine_d(const uint32_t* mask, const int32_t* idx, const float* slots,
+                      const float* ovf, int BH, int n, int k, int w, void* out, hipStream_t s) {
+    const long BHn = (long)BH * n;
+    const long threads = BHn * (D / 16);
+    hipLaunchKernelGGL((combine_kernel<OutT, D>), dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, mask, idx, slots, ovf, BHn, n, k, w, mask_words(k),
+                       (OutT*)out);
+}
+
+template <typename OutT>
+void launch_combine_t(const uint32_t* mask, const int32_t* idx, const float* slots,
+                      const float* ovf, int BH, int n, int d, int k, int w, void* out,
+                      hipStream_t s) {
+    switch (d) {
+        case 16: launch_combine_d<OutT, 16>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
+        case 32: launch_combine_d<OutT, 32>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
+        case 64: launch_combine_d<OutT, 64>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
+        default: launch_combine_d<OutT, 128>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
+    }
+}
+
 hipError_t launch_combine(const uint32_t* mask, const int32_t* idx, const float* slots,
                           const float* ovf, int out_dtype, int BH, int n, int d, int k, int w,
                           void* out, hipStream_t s) {
-    const long BHn = (long)BH * n;
-    const long threads = BHn * (d / 4);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    const int KW = mask_words(k);
-    if (out_dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<u16>, grid, dim3(256), 0, s, mask, idx, slots, ovf, BHn,
-                           n, d, k, w, KW, (u16*)out);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, mask, idx, slots, ovf,
-                           BHn, n, d, k, w, KW, (float*)out);
+    if (out_dtype == 1) launch_combine_t<u16>(mask, idx, slots, ovf, BH, n, d, k, w, out, s);
+    else launch_combine_t<float>(mask, idx, slots, ovf, BH, n, d, k, w, out, s);
     return hipGetLastError();
 }
 

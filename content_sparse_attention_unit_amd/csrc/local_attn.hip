@@ -49,51 +49,40 @@ __device__ __forceinline__ void store4<float>(float* dst, float a, float b, floa
     *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
 }
 
-template <int D>
-struct TileRegs {
-    uint4 k[LocalCfg<D>::KPT];
-    uint4 va[LocalCfg<D>::VPT];
-};
+// The next key/value tile travels through registers (issued before the
+// current tile's compute, stored to LDS after it).
+#define RT_LOAD_TILE(KT0)                                                                   \
+    do {                                                                                    \
+        _Pragma("unroll") for (int it = 0; it < C::KPT; ++it) {                              \
+            const int e = threadIdx.x + C::NT * it;                                         \
+            const int r = e / C::CPR, ch = e % C::CPR;                                      \
+            const int j = (C::KITEMS % C::NT == 0 || e < C::KITEMS) ? (KT0) + r : n;        \
+            tk[it] = (j < n && 8 * ch < D)                                                  \
+                         ? *reinterpret_cast<const uint4*>(kk + (base + j) * D + 8 * ch)   \
+                         : zero_u4();                                                       \
+        }                                                                                   \
+        _Pragma("unroll") for (int it = 0; it < C::VPT; ++it) {                              \
+            const int e = threadIdx.x + C::NT * it;                                         \
+            const int r = e / C::DCH, ch = e % C::DCH;                                      \
+            const int j = (C::VITEMS % C::NT == 0 || e < C::VITEMS) ? (KT0) + r : n;        \
+            tv[it] = (j < n) ? *reinterpret_cast<const uint4*>(v + (base + j) * D + 8 * ch)\
+                             : zero_u4();                                                   \
+        }                                                                                   \
+    } while (0)
 
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& tr, const u16* __restrict__ kk,
-                                          const u16* __restrict__ v, long base, int n, int kt) {
-    using C = LocalCfg<D>;
-#pragma unroll
-    for (int it = 0; it < C::KPT; ++it) {
-        const int e = threadIdx.x + C::NT * it;
-        const int r = e / C::CPR, ch = e % C::CPR;
-        const int j = (e < C::KITEMS) ? kt + r : n;
-        tr.k[it] = (j < n && 8 * ch < D) ? *reinterpret_cast<const uint4*>(kk + (base + j) * D + 8 * ch)
-                                         : zero_u4();
-    }
-#pragma unroll
-    for (int it = 0; it < C::VPT; ++it) {
-        const int e = threadIdx.x + C::NT * it;
-        const int r = e / C::DCH, ch = e % C::DCH;
-        const int j = (e < C::VITEMS) ? kt + r : n;
-        tr.va[it] = (j < n) ? *reinterpret_cast<const uint4*>(v + (base + j) * D + 8 * ch) : zero_u4();
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& tr, u16* lk, u16* lv) {
-    using C = LocalCfg<D>;
-#pragma unroll
-    for (int it = 0; it < C::KPT; ++it) {
-        const int e = threadIdx.x + C::NT * it;
-        if (e >= C::KITEMS) continue;
-        const int r = e / C::CPR, ch = e % C::CPR;
-        *reinterpret_cast<uint4*>(&lk[r * C::LDX + 8 * ch]) = tr.k[it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::VPT; ++it) {
-        const int e = threadIdx.x + C::NT * it;
-        if (e >= C::VITEMS) continue;
-        const int r = e / C::DCH, ch = e % C::DCH;
-        *reinterpret_cast<uint4*>(&lv[r * C::LDX + 8 * ch]) = tr.va[it];
-    }
-}
+#define RT_STORE_TILE(LK, LV)                                                               \
+    do {                                                                                    \
+        _Pragma("unroll") for (int it = 0; it < C::KPT; ++it) {                              \
+            const int e = threadIdx.x + C::NT * it;                                         \
+            if (C::KITEMS % C::NT == 0 || e < C::KITEMS)                                    \
+                *reinterpret_cast<uint4*>(&(LK)[(e / C::CPR) * C::LDX + 8 * (e % C::CPR)]) = tk[it]; \
+        }                                                                                   \
+        _Pragma("unroll") for (int it = 0; it < C::VPT; ++it) {                              \
+            const int e = threadIdx.x + C::NT * it;                                         \
+            if (C::VITEMS % C::NT == 0 || e < C::VITEMS)                                    \
+                *reinterpret_cast<uint4*>(&(LV)[(e / C::DCH) * C::LDX + 8 * (e % C::DCH)]) = tv[it]; \
+        }                                                                                   \
+    } while (0)
 
 template <int D, typename OutT>
 __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restrict__ q,
@@ -136,15 +125,15 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
     float m = -INFINITY, z = 0.f;
 
     const int kt_first = lo & ~(C::KT - 1);
-    TileRegs<D> tr;
-    load_tile<D>(tr, kk, v, base, n, kt_first);
-    store_tile<D>(tr, lk[0], lv[0]);
+    uint4 tk[C::KPT], tv[C::VPT];
+    RT_LOAD_TILE(kt_first);
+    RT_STORE_TILE(lk[0], lv[0]);
     __syncthreads();
 
     int buf = 0;
     for (int kt = kt_first; kt <= hi; kt += C::KT) {
         const bool more = kt + C::KT <= hi;
-        if (more) load_tile<D>(tr, kk, v, base, n, kt + C::KT);   // in flight during compute
+        if (more) RT_LOAD_TILE(kt + C::KT);   // in flight during compute
         if (kt + C::KT - 1 >= blo && kt <= bhi) {               // tile meets this wave's band
             const u16* LK = lk[buf];
             f32x4 sv[4];
@@ -180,7 +169,7 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
             softmax_pv_chunk<C::NJ, C::LDX>(sv, m, z, o, lv[buf], r16, g, halves);
         }
         if (more) {
-            store_tile<D>(tr, lk[buf ^ 1], lv[buf ^ 1]);
+            RT_STORE_TILE(lk[buf ^ 1], lv[buf ^ 1]);
             __syncthreads();
             buf ^= 1;
         }

@@ -55,6 +55,35 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     const int g = lane >> 4, r16 = lane & 15;
     const long base = (long)bh * n;
 
+    // Centroids of the first chunk: request them before the token rows so the
+    // two latencies overlap (MPT fp32 values per thread).
+    constexpr int MPT = (C::KC * C::DP) / 256;
+    float mreg[MPT];
+    auto load_mu = [&](int c0) {
+#pragma unroll
+        for (int j = 0; j < MPT; ++j) {
+            const int e = threadIdx.x + 256 * j;
+            const int c = e / C::DP, dim = e % C::DP;
+            mreg[j] = (c0 + c < k && dim < D) ? mu[((long)h * k + c0 + c) * D + dim] : 0.f;
+        }
+    };
+    auto stage_mu = [&]() {
+#pragma unroll
+        for (int j = 0; j < MPT; ++j) {
+            const int e = threadIdx.x + 256 * j;
+            const int c = e / C::DP, dim = e % C::DP;
+            const float m = mreg[j];
+            const u16 hi = f2bf(m);
+            const float r1 = m - bf2f(hi);
+            const u16 mid = f2bf(r1);
+            const float r2 = r1 - bf2f(mid);
+            lmu[0][c][dim] = hi;
+            lmu[1][c][dim] = mid;
+            lmu[2][c][dim] = f2bf(r2);
+        }
+    };
+    load_mu(0);
+
     uint4 breg[2][C::NS];
     float inv[2];
     int tok[2];
@@ -62,19 +91,25 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     for (int tb = 0; tb < 2; ++tb) {
         const int t = blockIdx.x * C::TOK + wv * 32 + tb * 16 + r16;
         tok[tb] = t;
-        float ss = 0.f;
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
             const int d0 = 32 * s + 8 * g;
-            uint4 v = zero_u4();
-            if (t < n && d0 < D) v = *reinterpret_cast<const uint4*>(qk + (base + t) * D + d0);
-            breg[tb][s] = v;
+            breg[tb][s] = (t < n && d0 < D) ? *reinterpret_cast<const uint4*>(qk + (base + t) * D + d0)
+                                           : zero_u4();
+        }
+    }
+    stage_mu();
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int t = tok[tb];
+        float ss = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::NS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = u4_elem(v, e);
+                const float x = u4_elem(breg[tb][s], e);
                 ss = fmaf(x, x, ss);
             }
-        }
         ss = xor_sum_16_32(ss);
         inv[tb] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
         if (g == 0 && t < n) {
@@ -91,8 +126,8 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
                     uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        ow[e] = pack2(f2bf(u4_elem(breg[tb][s], 2 * e) * inv[tb]),
-                                      f2bf(u4_elem(breg[tb][s], 2 * e + 1) * inv[tb]));
+                        ow[e] = cvt_pk_bf16(u4_elem(breg[tb][s], 2 * e) * inv[tb],
+                                            u4_elem(breg[tb][s], 2 * e + 1) * inv[tb]);
                     *reinterpret_cast<uint4*>(qk_hat + (base + t) * D + d0) = o;
                 }
             }
@@ -100,17 +135,10 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     }
 
     for (int c0 = 0; c0 < k; c0 += C::KC) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < C::KC * C::DP; e += 256) {
-            const int c = e / C::DP, dim = e % C::DP;
-            const float m = (c0 + c < k && dim < D) ? mu[((long)h * k + c0 + c) * D + dim] : 0.f;
-            const u16 hi = f2bf(m);
-            const float r1 = m - bf2f(hi);
-            const u16 mid = f2bf(r1);
-            const float r2 = r1 - bf2f(mid);
-            lmu[0][c][dim] = hi;
-            lmu[1][c][dim] = mid;
-            lmu[2][c][dim] = f2bf(r2);
+        if (c0 > 0) {
+            __syncthreads();          // previous chunk's MFMAs are done with lmu
+            load_mu(c0);
+            stage_mu();
         }
         __syncthreads();
         const int cn = min(C::KC, k - c0);
@@ -189,12 +217,47 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave 0 finds, in a 256-bin histogram (bins summed over `parts` copies laid
+// out `stride` words apart), the bin holding the `remaining`-th largest key:
+// writes the bin and the rank left inside it.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, int parts, int stride,
+                                         uint32_t remaining, uint32_t* sel_bin,
+                                         uint32_t* sel_rem) {
+    const int lane = lane_id();
+    uint32_t cnt[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        uint32_t t = 0u;
+        for (int v = 0; v < parts; ++v) t += hist[v * stride + 4 * lane + b];
+        cnt[b] = t;
+    }
+    const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    uint32_t suf = tot;  // inclusive suffix sum over lanes
+#pragma unroll
+    for (int dl = 1; dl < kWave; dl <<= 1) {
+        const uint32_t o = __shfl_down(suf, dl);
+        if (lane + dl < kWave) suf += o;
+    }
+    uint32_t above = suf - tot;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+        if (above < remaining && remaining <= above + cnt[b]) {
+            *sel_bin = (uint32_t)(4 * lane + b);
+            *sel_rem = remaining - above;
+        }
+        above += cnt[b];
+    }
+}
+
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scores, int n, int w,
                                                   int32_t* __restrict__ idx, int k,
                                                   uint32_t* __restrict__ mask, int KW) {
     constexpr int NWV = NT / kWave;
+    constexpr int CAND = 4096;           // capacity of the candidate list
+    __shared__ uint32_t sub[NWV][256];   // per-wave histograms of the top byte
     __shared__ uint32_t hist[256];
+    __shared__ uint32_t cand[CAND];      // keys sharing the selected top byte
     __shared__ uint32_t sel_bin, sel_rem;
     __shared__ uint32_t wgt[NWV], weq[NWV];
 
@@ -204,50 +267,109 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     const int seg0 = wv * kWave * KPT;
 
     uint32_t key[KPT];
+    uint32_t tmin = 0xffu, tmax = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const int pos = seg0 + kWave * j + lane;
         key[j] = (pos < n) ? order_key(srow[pos]) : 0u;
+        if (pos < n) {
+            tmin = min(tmin, key[j] >> 24);
+            tmax = max(tmax, key[j] >> 24);
+        }
     }
-
-    // Radix select: after the four passes `prefix` is the w-th largest key and
-    // `remaining` the number of keys equal to it that belong to the top w.
-    uint32_t prefix = 0u, himask = 0u, remaining = (uint32_t)w;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
-        __syncthreads();
+    // Range of the top byte over the row.  Scores of one row usually share
+    // their sign and most of their exponent, so this first digit takes a few
+    // values only and is counted with wave ballots rather than (heavily
+    // contended) LDS atomics.
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, off));
+        tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, off));
+    }
+    if (lane == 0) {
+        wgt[wv] = tmin;
+        weq[wv] = tmax;
+    }
+    for (int e = threadIdx.x; e < NWV * 256; e += NT) (&sub[0][0])[e] = 0u;
+    __syncthreads();
+    tmin = 0xffu;
+    tmax = 0u;
+    for (int v = 0; v < NWV; ++v) {
+        tmin = min(tmin, wgt[v]);
+        tmax = max(tmax, weq[v]);
+    }
+    if (tmax - tmin < 16u) {
+        for (uint32_t dv = tmin; dv <= tmax; ++dv) {
+            uint32_t c = 0u;
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const int pos = seg0 + kWave * j + lane;
+                c += (uint32_t)__popcll(__ballot(pos < n && (key[j] >> 24) == dv));
+            }
+            if (lane == 0) sub[wv][dv] = c;
+        }
+    } else {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int pos = seg0 + kWave * j + lane;
-            if (pos < n && (key[j] & himask) == prefix)
-                atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+            if (pos < n) atomicAdd(&sub[wv][key[j] >> 24], 1u);
         }
-        __syncthreads();
-        if (wv == 0) {
-            uint32_t cnt[4];
+    }
+    __syncthreads();
+    if (wv == 0) find_bin(&sub[0][0], NWV, 256, (uint32_t)w, &sel_bin, &sel_rem);
+    __syncthreads();
+
+    // Radix select: after the four digits `prefix` is the w-th largest key and
+    // `remaining` the number of keys equal to it that belong to the top w.
+    const uint32_t bin0 = sel_bin;
+    uint32_t prefix = bin0 << 24, himask = 0xff000000u, remaining = sel_rem;
+    uint32_t ncand = 0u, cand_off = 0u;
+    for (int v = 0; v < NWV; ++v) {
+        if (v == wv) cand_off = ncand;
+        ncand += sub[v][bin0];
+    }
+    if (ncand <= (uint32_t)CAND) {
+        // The remaining digits only concern keys whose top byte is bin0: list
+        // them (in position order) and finish on the short list.
 #pragma unroll
-            for (int b = 0; b < 4; ++b) cnt[b] = hist[4 * lane + b];
-            const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-            uint32_t suf = tot;  // inclusive suffix sum over lanes
-#pragma unroll
-            for (int dl = 1; dl < kWave; dl <<= 1) {
-                const uint32_t o = __shfl_down(suf, dl);
-                if (lane + dl < kWave) suf += o;
-            }
-            uint32_t above = suf - tot;
-#pragma unroll
-            for (int b = 3; b >= 0; --b) {
-                if (above < remaining && remaining <= above + cnt[b]) {
-                    sel_bin = (uint32_t)(4 * lane + b);
-                    sel_rem = remaining - above;
-                }
-                above += cnt[b];
-            }
+        for (int j = 0; j < KPT; ++j) {
+            const int pos = seg0 + kWave * j + lane;
+            const bool is = pos < n && (key[j] >> 24) == bin0;
+            const uint64_t mb = __ballot(is);
+            if (is) cand[cand_off + (uint32_t)lanes_below(mb)] = key[j];
+            cand_off += (uint32_t)__popcll(mb);
         }
-        __syncthreads();
-        prefix |= sel_bin << shift;
-        himask |= 0xffu << shift;
-        remaining = sel_rem;
+        for (int shift = 16; shift >= 0; shift -= 8) {
+            if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
+            __syncthreads();
+            for (uint32_t i = threadIdx.x; i < ncand; i += NT) {
+                const uint32_t kc = cand[i];
+                if ((kc & himask) == prefix) atomicAdd(&hist[(kc >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (wv == 0) find_bin(hist, 1, 0, remaining, &sel_bin, &sel_rem);
+            __syncthreads();
+            prefix |= sel_bin << shift;
+            himask |= 0xffu << shift;
+            remaining = sel_rem;
+        }
+    } else {
+        for (int shift = 16; shift >= 0; shift -= 8) {
+            if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                const int pos = seg0 + kWave * j + lane;
+                if (pos < n && (key[j] & himask) == prefix)
+                    atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (wv == 0) find_bin(hist, 1, 0, remaining, &sel_bin, &sel_rem);
+            __syncthreads();
+            prefix |= sel_bin << shift;
+            himask |= 0xffu << shift;
+            remaining = sel_rem;
+        }
     }
     const uint32_t T = prefix, need_eq = remaining;
 
