@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying "
                     "a captured HIP graph of the step")
+    ap.add_argument("--one-stream", action="store_true", help="run the local heads after the "
+                    "routed heads on the same stream instead of concurrently on a second one")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
@@ -144,13 +146,23 @@ def main():
         if cfg.L > 0:
             rt.local_attn(ql, kl, vl, cfg.window, scale=scale, out=out_l)
 
+    stream = torch.cuda.Stream()
+    side = torch.cuda.Stream()          # local heads: independent of the routed heads
+
     def step():
+        if cfg.L > 0 and not args.one_stream:
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                do_local()
         do_route()
         do_attn()
         do_ema()
-        do_local()
+        if cfg.L > 0:
+            if args.one_stream:
+                do_local()
+            else:
+                stream.wait_stream(side)
 
-    stream = torch.cuda.Stream()
     use_graph = not args.no_graph
     with torch.cuda.stream(stream):
         for _ in range(max(1, args.warmup)):
@@ -218,7 +230,8 @@ def main():
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shapes)",
         "config": {"workload": WORKLOADS[args.workload], "batch": B, "seq_len": n,
                    "routed_heads": R, "local_heads": cfg.L, "d_head": d, "k": k, "w": w,
-                   "window": cfg.window, "graph": use_graph},
+                   "window": cfg.window, "graph": use_graph,
+                   "local_heads_stream": "same" if args.one_stream else "concurrent"},
         "roofline": {"bound": "hbm", "kernel": "rt_routed_attn (in-cluster attention)",
                      "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": None,

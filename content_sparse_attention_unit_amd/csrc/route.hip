@@ -217,6 +217,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += (uint32_t)__shfl_xor((int)x, off);
+    return x;
+}
+
 // Wave 0 finds, in a 256-bin histogram (bins summed over `parts` copies laid
 // out `stride` words apart), the bin holding the `remaining`-th largest key:
 // writes the bin and the rank left inside it.
@@ -277,10 +283,9 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
             tmax = max(tmax, key[j] >> 24);
         }
     }
-    // Range of the top byte over the row.  Scores of one row usually share
-    // their sign and most of their exponent, so this first digit takes a few
-    // values only and is counted with wave ballots rather than (heavily
-    // contended) LDS atomics.
+    // Range of the top byte (sign and high exponent bits) over the row.  A
+    // row's scores share it in large groups, so this first digit is counted
+    // with per-lane counts, not (heavily contended) LDS atomics.
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, off));
@@ -290,7 +295,6 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         wgt[wv] = tmin;
         weq[wv] = tmax;
     }
-    for (int e = threadIdx.x; e < NWV * 256; e += NT) (&sub[0][0])[e] = 0u;
     __syncthreads();
     tmin = 0xffu;
     tmax = 0u;
@@ -298,36 +302,61 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         tmin = min(tmin, wgt[v]);
         tmax = max(tmax, weq[v]);
     }
-    if (tmax - tmin < 16u) {
-        for (uint32_t dv = tmin; dv <= tmax; ++dv) {
-            uint32_t c = 0u;
+    // The w-th largest key nearly always has one of the row's highest top
+    // bytes: walk down from the maximum with per-lane counts (a few steps),
+    // falling back to a full histogram of the top byte otherwise.
+    uint32_t bin0 = tmax, remaining = (uint32_t)w, ncand = 0u, cand_off = 0u;
+    bool found = false;
+    __syncthreads();  // wgt/weq (top-byte range) have been read by every thread
+    for (int step = 0; step < 4 && !found; ++step) {
+        uint32_t c = 0u;
 #pragma unroll
-            for (int j = 0; j < KPT; ++j) {
-                const int pos = seg0 + kWave * j + lane;
-                c += (uint32_t)__popcll(__ballot(pos < n && (key[j] >> 24) == dv));
-            }
-            if (lane == 0) sub[wv][dv] = c;
+        for (int j = 0; j < KPT; ++j) {
+            const int pos = seg0 + kWave * j + lane;
+            c += (pos < n && (key[j] >> 24) == bin0) ? 1u : 0u;
         }
-    } else {
+        c = wave_sum_u32(c);
+        if (lane == 0) wgt[wv] = c;
+        __syncthreads();
+        uint32_t tot = 0u;
+        for (int v = 0; v < NWV; ++v) {
+            if (v == wv) cand_off = tot;
+            tot += wgt[v];
+        }
+        __syncthreads();  // before wgt is written again
+        if (tot >= remaining) {
+            found = true;
+            ncand = tot;
+        } else if (bin0 == tmin) {
+            break;  // unreachable: every key has a top byte >= tmin
+        } else {
+            remaining -= tot;
+            --bin0;
+        }
+    }
+    if (!found) {
+        for (int e = threadIdx.x; e < NWV * 256; e += NT) (&sub[0][0])[e] = 0u;
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             const int pos = seg0 + kWave * j + lane;
             if (pos < n) atomicAdd(&sub[wv][key[j] >> 24], 1u);
         }
+        __syncthreads();
+        if (wv == 0) find_bin(&sub[0][0], NWV, 256, (uint32_t)w, &sel_bin, &sel_rem);
+        __syncthreads();
+        bin0 = sel_bin;
+        remaining = sel_rem;
+        ncand = 0u;
+        for (int v = 0; v < NWV; ++v) {
+            if (v == wv) cand_off = ncand;
+            ncand += sub[v][bin0];
+        }
     }
-    __syncthreads();
-    if (wv == 0) find_bin(&sub[0][0], NWV, 256, (uint32_t)w, &sel_bin, &sel_rem);
-    __syncthreads();
 
     // Radix select: after the four digits `prefix` is the w-th largest key and
     // `remaining` the number of keys equal to it that belong to the top w.
-    const uint32_t bin0 = sel_bin;
-    uint32_t prefix = bin0 << 24, himask = 0xff000000u, remaining = sel_rem;
-    uint32_t ncand = 0u, cand_off = 0u;
-    for (int v = 0; v < NWV; ++v) {
-        if (v == wv) cand_off = ncand;
-        ncand += sub[v][bin0];
-    }
+    uint32_t prefix = bin0 << 24, himask = 0xff000000u;
     if (ncand <= (uint32_t)CAND) {
         // The remaining digits only concern keys whose top byte is bin0: list
         // them (in position order) and finish on the short list.
@@ -380,9 +409,11 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     for (int j = 0; j < KPT; ++j) {
         const int pos = seg0 + kWave * j + lane;
         const bool valid = pos < n;
-        gtc += (uint32_t)__popcll(__ballot(valid && key[j] > T));
-        eqc += (uint32_t)__popcll(__ballot(valid && key[j] == T));
+        gtc += (valid && key[j] > T) ? 1u : 0u;
+        eqc += (valid && key[j] == T) ? 1u : 0u;
     }
+    gtc = wave_sum_u32(gtc);
+    eqc = wave_sum_u32(eqc);
     if (lane == 0) {
         wgt[wv] = gtc;
         weq[wv] = eqc;
