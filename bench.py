@@ -99,8 +99,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying "
                     "a captured HIP graph of the step")
-    ap.add_argument("--one-stream", action="store_true", help="run the local heads after the "
-                    "routed heads on the same stream instead of concurrently on a second one")
+    ap.add_argument("--concurrent-local", action="store_true", help="run the local heads "
+                    "concurrently on a second stream instead of after the routed heads")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before timing, copy a MIB-mebibyte device buffer once (a plain copy "
+                    "of known size that scales the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
@@ -150,7 +153,7 @@ def main():
     side = torch.cuda.Stream()          # local heads: independent of the routed heads
 
     def step():
-        if cfg.L > 0 and not args.one_stream:
+        if cfg.L > 0 and args.concurrent_local:
             side.wait_stream(stream)
             with torch.cuda.stream(side):
                 do_local()
@@ -158,10 +161,19 @@ def main():
         do_attn()
         do_ema()
         if cfg.L > 0:
-            if args.one_stream:
+            if not args.concurrent_local:
                 do_local()
             else:
                 stream.wait_stream(side)
+
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     use_graph = not args.no_graph
     with torch.cuda.stream(stream):
@@ -212,9 +224,42 @@ def main():
     alg = algorithmic(cfg)
     routed_ms = (per_call["rt_route"] + per_call["rt_routed_attn"] +
                  per_call["rt_centroid_update_sums"])
-    attn_s = per_call["rt_routed_attn"] * 1e-3
-    achieved_gbs = alg["attn_bytes"] / attn_s / 1e9
     tokens = B * n
+
+    def rate(nbytes, flops, ms):
+        s_ = ms * 1e-3
+        r = {"ms": ms, "GB/s": nbytes / s_ / 1e9, "hbm_frac": nbytes / s_ / 1e9 / PEAK_HBM_GBS}
+        if flops:
+            r["TFLOP/s"] = flops / s_ / 1e12
+            r["mfma_frac"] = flops / s_ / 1e12 / PEAK_BF16_TFLOPS
+        return r
+
+    stages = {
+        "rt_route": rate(alg["route_bytes"], alg["route_flops"], per_call["rt_route"]),
+        "rt_routed_attn": rate(alg["attn_bytes"], alg["attn_flops_tile"], per_call["rt_routed_attn"]),
+        "rt_centroid_update_sums": rate(2 * R * k * d * 4 + B * R * k * d * 4, 0,
+                                        per_call["rt_centroid_update_sums"]),
+    }
+    if cfg.L > 0:
+        stages["rt_local_attn"] = rate(alg["local_bytes"], alg["local_flops"], per_call["rt_local_attn"])
+        # The longest kernel of the step is the local-window attention; rt_local_attn launches
+        # exactly it, once, so its per-call time is that kernel's launch duration.  Its
+        # arithmetic intensity (about window/2 flop per byte) sits below the ridge point
+        # (peak flops / peak bandwidth), so HBM bounds it.
+        t = per_call["rt_local_attn"] * 1e-3
+        achieved = alg["local_bytes"] / t / 1e9
+        roofline = {"bound": "hbm", "kernel": "local_attn_bf16_kernel (rt_local_attn)",
+                    "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                    "algorithmic_bytes": alg["local_bytes"],
+                    "mfma_frac": alg["local_flops"] / t / 1e12 / PEAK_BF16_TFLOPS}
+    else:
+        t = per_call["rt_routed_attn"] * 1e-3
+        achieved = alg["attn_bytes"] / t / 1e9
+        roofline = {"bound": "hbm", "kernel": "rt_routed_attn (in-cluster attention + combine)",
+                    "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                    "algorithmic_bytes": alg["attn_bytes"]}
     res = {
         "metric": "routed-attention tokens/sec/layer at n=8192 fwd; % bf16 MFMA peak",
         "value": tokens / (ms_per_step * 1e-3),
@@ -231,12 +276,10 @@ def main():
         "config": {"workload": WORKLOADS[args.workload], "batch": B, "seq_len": n,
                    "routed_heads": R, "local_heads": cfg.L, "d_head": d, "k": k, "w": w,
                    "window": cfg.window, "graph": use_graph,
-                   "local_heads_stream": "same" if args.one_stream else "concurrent"},
-        "roofline": {"bound": "hbm", "kernel": "rt_routed_attn (in-cluster attention)",
-                     "achieved": achieved_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": None,
-                     "mfma_frac_tile": alg["attn_flops_tile"] / attn_s / 1e12 / PEAK_BF16_TFLOPS},
+                   "local_heads_stream": "concurrent" if args.concurrent_local else "same"},
+        "roofline": roofline,
         "per_call_ms": per_call,
+        "stages": stages,
         "routed_tokens_per_s": tokens / (routed_ms * 1e-3),
         "routed_over_local_time": (routed_ms / per_call["rt_local_attn"]
                                    if "rt_local_attn" in per_call else None),

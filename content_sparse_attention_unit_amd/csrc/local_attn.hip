@@ -94,8 +94,11 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
     __shared__ __attribute__((aligned(16))) u16 lk[2][C::KT * C::LDX];
     __shared__ __attribute__((aligned(16))) u16 lv[2][C::KT * C::LDX];
 
-    const int bh = blockIdx.y;
-    const int q0 = blockIdx.x * C::QT;
+    // consecutive query tiles of a head read overlapping key windows: keep
+    // them on one XCD
+    const int item = xcd_contiguous(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    const int bh = item / gridDim.x;
+    const int q0 = (item % gridDim.x) * C::QT;
     const long base = (long)bh * n;
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;

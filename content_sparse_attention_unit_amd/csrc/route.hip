@@ -49,7 +49,9 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     using C = ScoreCfg<D>;
     __shared__ __attribute__((aligned(16))) u16 lmu[3][C::KC][C::LD];
 
-    const int bh = blockIdx.y;
+    // the token tiles of one head share its centroids: keep them on one XCD
+    const int item = xcd_contiguous(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    const int bh = item / gridDim.x, tile = item % gridDim.x;
     const int h = bh % H;
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     int tok[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-        const int t = blockIdx.x * C::TOK + wv * 32 + tb * 16 + r16;
+        const int t = tile * C::TOK + wv * 32 + tb * 16 + r16;
         tok[tb] = t;
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {

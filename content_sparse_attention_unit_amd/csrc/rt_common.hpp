@@ -146,6 +146,17 @@ __device__ __forceinline__ float xor_sum_16_32(float x) {
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
+// The dispatcher hands workgroups to the 8 XCDs round-robin (linear workgroup
+// id b goes to XCD b % 8), and each XCD has its own L2.  This renumbering
+// gives every XCD one contiguous run of the nb work items, so neighbouring
+// items that read overlapping rows share an L2.  It is a bijection on [0, nb).
+__device__ __forceinline__ int xcd_contiguous(int b, int nb) {
+    constexpr int kXcd = 8;
+    const int per = nb / kXcd, rem = nb % kXcd;
+    const int x = b % kXcd, s = b / kXcd;
+    return x * per + (x < rem ? x : rem) + s;
+}
+
 __device__ __forceinline__ int clamp_pos(int t, int n) { return t < 0 ? 0 : (t >= n ? n - 1 : t); }
 
 // Typed loads of one token element for the float32 and bf16 variants.
