@@ -250,6 +250,16 @@ rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int d
         return fail(RT_EINVAL, "%s: null tensor pointer", fn);
     if ((q_inv == nullptr) != (k_inv == nullptr))
         return fail(RT_EINVAL, "%s: q_inv and k_inv must both be given or both be NULL", fn);
+    {
+        const void* outs[3] = {dq_hat, dk_hat, dv};
+        const void* ins[5] = {q, kk, v, dout, lse};
+        for (int i = 0; i < 3; ++i) {
+            for (int j = 0; j < 5; ++j)
+                if (outs[i] == ins[j]) return fail(RT_EINVAL, "%s: a gradient aliases an input", fn);
+            for (int j = i + 1; j < 3; ++j)
+                if (outs[i] == outs[j]) return fail(RT_EINVAL, "%s: gradients alias each other", fn);
+        }
+    }
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
     if (st != RT_OK) return st;
     st = check_clusters(fn, n, k, w);
@@ -257,7 +267,7 @@ rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int d
     if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
     if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
     const bool shared = (q == kk) && (q_inv == k_inv);
-    const int wmax = rt::max_cluster_rows(dtype, d, shared);
+    const int wmax = rt::max_cluster_rows_bwd(dtype, d, shared);
     if (w > wmax)
         return fail(RT_EUNSUPPORTED, "%s: w=%d exceeds %d for this dtype, d and q/k sharing", fn,
                     w, wmax);
@@ -267,7 +277,7 @@ rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int d
                     ws == nullptr ? (size_t)0 : ws_bytes);
     hipError_t e = rt::launch_cluster_attn_bwd(q, kk, v, dtype, q_inv, k_inv, idx, lse, dout,
                                                B * H, n, d, k, w, scale, causal, dq_hat, dk_hat,
-                                               dv, static_cast<float*>(ws),
+                                               dv, ws,
                                                static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)
         return fail(RT_EUNSUPPORTED, "%s: this configuration has no backward kernel", fn);

@@ -59,30 +59,6 @@ __global__ __launch_bounds__(256) void mask_kernel(const int32_t* __restrict__ i
     atomicOr(&mask[((long)bh * n + t) * KW + (c >> 5)], 1u << (c & 31));
 }
 
-template <typename OutT>
-__device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store4<u16>(u16* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(cvt_pk_bf16(a, b), cvt_pk_bf16(c, d));
-}
-template <>
-__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
-}
-
-// Where member row r's output goes: -2 nowhere (padding or invalid position),
-// -1 straight to out, 0..kSlots-1 token slot, kSlots + rank overflow.
-__device__ __forceinline__ int row_dest(const uint32_t* __restrict__ m, int KW, int c) {
-    int cnt = 0, below = 0;
-    for (int i = 0; i < KW; ++i) {
-        const uint32_t word = m[i];
-        cnt += __popc(word);
-        if (i < (c >> 5)) below += __popc(word);
-        else if (i == (c >> 5)) below += __popc(word & ((1u << (c & 31)) - 1u));
-    }
-    return cnt == 1 ? -1 : below;
-}
-
 template <int D, int WMAX, bool SHARED>
 struct AttnCfg {
     static constexpr int DP = D < 32 ? 32 : D;  // dims padded to the MFMA k-depth

@@ -38,17 +38,6 @@ struct LocalCfg {
     static constexpr int VPT = (VITEMS + NT - 1) / NT;     // ... per thread
 };
 
-template <typename OutT>
-__device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
-template <>
-__device__ __forceinline__ void store4<u16>(u16* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(cvt_pk_bf16(a, b), cvt_pk_bf16(c, d));
-}
-template <>
-__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
-}
-
 // The next key/value tile travels through registers (issued before the
 // current tile's compute, stored to LDS after it).
 #define RT_LOAD_TILE(KT0)                                                                   \

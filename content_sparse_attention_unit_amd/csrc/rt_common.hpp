@@ -69,6 +69,32 @@ __device__ __forceinline__ uint2 lds_read_tr16(const u16* p) {
 #endif
 }
 
+// o^T += X^T W^T over the 64 rows of a row-major LDS tile: X is the tile
+// (rows = the contraction index, row stride LDX, `lx` at its first row), o^T
+// holds NJ 16 x 16 blocks of [column of X][this lane's column r16], and
+// pw[kb] packs, as bf16 pairs, this lane's W values for rows 16*kb + 4*g + 0..3.
+// X^T comes straight from the row-major tile through transposing LDS reads.
+// `halves` says which 32-row halves to include (wave-uniform); rows outside
+// them are never read.
+template <int NJ, int LDX>
+__device__ __forceinline__ void acc_xt_w(const uint32_t (&pw)[4][2], f32x4 (&o)[NJ],
+                                         const u16* lx, int r16, int g, int halves) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+        if (!(halves & (1 << mm))) continue;
+        // B operand: rows 32mm + 4g + (0..3) and 32mm + 16 + 4g + (0..3)
+        const bf16x8 wv = as_bf16x8(make_uint4(pw[2 * mm][0], pw[2 * mm][1], pw[2 * mm + 1][0],
+                                               pw[2 * mm + 1][1]));
+        const u16* xb = lx + (32 * mm + 4 * g + (r16 >> 2)) * LDX + 4 * (r16 & 3);
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+            const uint2 lo = lds_read_tr16(xb + 16 * jb);
+            const uint2 hi = lds_read_tr16(xb + 16 * LDX + 16 * jb);
+            o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), wv, o[jb]);
+        }
+    }
+}
+
 // Online-softmax step shared by the attention kernels.  `sv[kb][i]` holds the
 // logits, in log2 units, of keys kc + 16*kb + 4*g + i for this lane's query
 // (-inf where masked).  Updates the running max `m` and denominator `z`,
@@ -106,20 +132,34 @@ __device__ __forceinline__ void softmax_pv_chunk(f32x4 (&sv)[4], float& m, float
         pw[kb][0] = cvt_pk_bf16(p0, p1);
         pw[kb][1] = cvt_pk_bf16(p2, p3);
     }
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-        if (!(halves & (1 << mm))) continue;
-        // B operand: lane's keys 32mm + 4g + (0..3) and 32mm + 16 + 4g + (0..3)
-        const bf16x8 pbv = as_bf16x8(make_uint4(pw[2 * mm][0], pw[2 * mm][1], pw[2 * mm + 1][0],
-                                                pw[2 * mm + 1][1]));
-        const u16* vb = lv + (32 * mm + 4 * g + (r16 >> 2)) * LDX + 4 * (r16 & 3);
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) {
-            const uint2 lo = lds_read_tr16(vb + 16 * jb);
-            const uint2 hi = lds_read_tr16(vb + 16 * LDX + 16 * jb);
-            o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pbv, o[jb]);
-        }
+    acc_xt_w<NJ, LDX>(pw, o, lv, r16, g, halves);
+}
+
+// Four float32 values to 4 consecutive output elements (bf16: one 8-byte store).
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<u16>(u16* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(cvt_pk_bf16(a, b), cvt_pk_bf16(c, d));
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
+// Membership bitmask of one token (KW words, bit c = member of cluster c):
+// where that token's row of cluster c goes.  -1: straight to the output (the
+// token has no other cluster); otherwise its rank, the number of the token's
+// clusters below c (the combine step sums ranks in ascending order).
+__device__ __forceinline__ int row_dest(const uint32_t* __restrict__ m, int KW, int c) {
+    int cnt = 0, below = 0;
+    for (int i = 0; i < KW; ++i) {
+        const uint32_t word = m[i];
+        cnt += __popc(word);
+        if (i < (c >> 5)) below += __popc(word);
+        else if (i == (c >> 5)) below += __popc(word & ((1u << (c & 31)) - 1u));
     }
+    return cnt == 1 ? -1 : below;
 }
 
 // ---- wave helpers --------------------------------------------------------------

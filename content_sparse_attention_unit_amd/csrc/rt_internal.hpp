@@ -64,8 +64,11 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
                                    const float* q_inv, const float* k_inv, const int32_t* idx,
                                    const float* lse, const void* dout, int BH, int n, int d,
                                    int k, int w, float scale, int causal, float* dq, float* dk,
-                                   float* dv, float* ws, hipStream_t s);
+                                   float* dv, void* ws, hipStream_t s);
 
 size_t bwd_workspace_bytes(int BH, int n, int d, int k, int w);
+
+// Largest cluster the backward kernels keep on chip.
+int max_cluster_rows_bwd(int dtype, int d, bool shared_qk);
 
 }  // namespace rt

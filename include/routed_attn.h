@@ -32,9 +32,14 @@
  *    A failed kernel launch returns RT_EHIP.  The text of the last error of
  *    the calling thread is available from rt_last_error().
  *  - Supported shapes: d in {16, 32, 64, 128}; 1 <= w <= n; 1 <= k <= 256;
- *    n < 2^31 / d; the in-cluster kernels keep a whole cluster in on-chip
- *    memory, which bounds w (rt_routed_attn returns RT_EUNSUPPORTED beyond
- *    w*d <= 32768 for bf16 and w <= 1024 for float32).
+ *    n < 2^31 / d.  The in-cluster kernels keep a whole cluster in on-chip
+ *    memory, which bounds w (beyond it the call returns RT_EUNSUPPORTED):
+ *      rt_routed_attn, bf16, shared q/k:    w <= 512 (d <= 64), 256 (d = 128)
+ *      rt_routed_attn, bf16, distinct q/k:  w <= 256 (d <= 64), 128 (d = 128)
+ *      rt_routed_attn, float32:             w <= 1024
+ *      rt_routed_attn_bwd, bf16, shared:    w <= 256 (d <= 64), 128 (d = 128)
+ *      rt_routed_attn_bwd, bf16, distinct:  w <= 128 (d <= 64),  64 (d = 128)
+ *      rt_routed_attn_bwd, float32:         w <= 64
  */
 #ifndef ROUTED_ATTN_H
 #define ROUTED_ATTN_H
@@ -186,15 +191,19 @@ rt_status rt_centroid_update_sums(float *mu, const float *sum_q, const float *su
  *   attention inputs, for a fixed membership (routing is a discrete choice
  *   and the centroids move by the update above, not by gradient).
  *
- *   dout            [B][H][n][d] dtype, gradient of `out`.
- *   lse             [B][H][k][w] float32 from the forward call.
+ *   dout            [B][H][n][d] dtype (the dtype of q), gradient of `out`.
+ *   lse             [B][H][k][w] float32 from the forward call with the same
+ *                   inputs (the softmax is rebuilt from it, not renormalised).
  *   dq_hat, dk_hat  out [B][H][n][d] float32: gradients w.r.t. the
  *                   normalised vectors q*q_inv and kk*k_inv (token order,
  *                   summed over clusters).  With shared QK the gradient of
  *                   the shared normalised vector is dq_hat + dk_hat.
  *   dv              out [B][H][n][d] float32.
- *   Other arguments as for rt_routed_attn.  ws: rt_workspace_bytes(
- *   RT_OP_ROUTED_ATTN_BWD, ...) bytes.  Deterministic.
+ *   The three gradients are float32, distinct, and alias no input.  Tokens
+ *   held by no cluster get zero rows.  Other arguments as for rt_routed_attn.
+ *   ws: rt_workspace_bytes(RT_OP_ROUTED_ATTN_BWD, ...) bytes (membership bits
+ *   and the float32 partial rows of tokens that several clusters hold).
+ *   Deterministic: clusters are summed per token in ascending centroid order.
  */
 rt_status rt_routed_attn_bwd(const void *q, const void *kk, const void *v, int dtype,
                              const float *q_inv, const float *k_inv, const int32_t *idx,

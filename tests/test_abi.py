@@ -174,3 +174,41 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 1, 64, 16)
     with pytest.raises(ValueError):
         rt.local_attn(x, x, x, 8)
+
+
+def bwd(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE,
+        lse=ctypes.c_void_p(0x4000), dout=ctypes.c_void_p(0x5000), B=1, H=1, n=64, d=16, k=4,
+        w=16, scale=0.25, causal=1, dq=ctypes.c_void_p(0x6000), dk=ctypes.c_void_p(0x7000),
+        dv=ctypes.c_void_p(0x8000), ws=None, ws_bytes=0):
+    return lib.rt_routed_attn_bwd(q, kk, v, dtype, q_inv, k_inv, idx, lse, dout, B, H, n, d, k, w,
+                                  scale, causal, dq, dk, dv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(lse=None), RT_EINVAL, "null"),
+    (dict(dout=None), RT_EINVAL, "null"),
+    (dict(dv=None), RT_EINVAL, "null"),
+    (dict(q_inv=None), RT_EINVAL, "both"),
+    (dict(dq=FAKE), RT_EINVAL, "aliases an input"),
+    (dict(dk=ctypes.c_void_p(0x6000)), RT_EINVAL, "alias each other"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(d=24), RT_EUNSUPPORTED, "d=24"),
+    (dict(causal=3), RT_EINVAL, "causal"),
+    (dict(scale=float("nan")), RT_EINVAL, "scale"),
+    (dict(n=4096, d=128, w=129), RT_EUNSUPPORTED, "w=129"),
+    (dict(n=4096, d=64, w=257), RT_EUNSUPPORTED, "w=257"),
+    (dict(q=ctypes.c_void_p(0x3000), n=4096, d=64, w=129), RT_EUNSUPPORTED, "w=129"),
+    (dict(dtype=0, w=65, n=100), RT_EUNSUPPORTED, "w=65"),
+    (dict(), RT_EINVAL, "workspace"),
+])
+def test_routed_attn_bwd_validation(lib, kw, code, msg):
+    assert bwd(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_bwd_workspace_size(lib):
+    B, H, n, d, k, w = 1, 8, 32768, 64, 128, 256
+    mask = ((B * H * n * 4 * 4 + 255) // 256) * 256
+    slots = ((B * H * n * 4 * d * 4 + 255) // 256) * 256
+    ovf = B * H * k * w * d * 4
+    assert lib.rt_workspace_bytes(4, B, H, n, d, k, w) == mask + 3 * (slots + ovf)
