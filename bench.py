@@ -32,6 +32,34 @@ import synthetic as S  # noqa: E402
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 
+# HBM traffic of the local-window attention kernel at the long workload, from two rocprofv3
+# --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the same counter's
+# reading for a plain 256 MiB device copy in the same run (--copy-calibration 256).  Valid only
+# for the kernel sources with this digest: after any change the bench reports traffic null.
+LOCAL_TRAFFIC = {
+    "workload": "long",
+    "sources": ["content_sparse_attention_unit_amd/csrc/local_attn.hip",
+                "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
+    "sha256": "e626a8f759a780ea222364ac9819d9f3f632edc0eeab24faa696c10a162edb1e",
+    "fetch_kib": 12853.3, "write_kib": 8192.0,
+    "fetch_scale": 262144.0 / 131088.875, "write_scale": 262144.0 / 262144.0,
+}
+
+
+def measured_traffic(rec, workload):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch, or None when the kernel's
+    sources have changed since the counters were taken (or the workload differs)."""
+    import hashlib
+    if workload != rec["workload"]:
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["sha256"]:
+        return None
+    return 1024.0 * (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"])
+
 WORKLOADS = {
     "long": "long: B=1, 8 routed heads (k=64, w=128) + 4 local heads (window 512), "
             "n=8192, d=128, bf16, causal, shared QK, EMA lambda=0.999",
@@ -39,7 +67,7 @@ WORKLOADS = {
              "n=4096, d=64, bf16",
     "routed": "routed: B=4, 8 routed heads (k=32, w=32), n=1024, d=64, bf16",
     "stress": "stress: B=1, 8 routed heads (k=128, w=256) + 8 local (window 256), "
-              "n=32768, d=64, bf16, 10% skewed tokens",
+              "n=32768, d=64, bf16, 10% skewed tokens, forward + in-cluster backward",
 }
 
 
@@ -65,29 +93,43 @@ def algorithmic(cfg):
     route_flops = 2.0 * B * R * n * k * d
     lw = min(cfg.window, n)
     local_flops = 4.0 * B * L * d * (lw * (lw + 1) / 2 + max(0, n - lw) * lw)
-    return dict(route_bytes=route_bytes, attn_bytes=attn_bytes, ema_bytes=ema_bytes,
+    # backward: qk, v, dO gathered once, lse/idx; dq_hat, dk_hat, dv written once in fp32;
+    # five w x w x d products per cluster (S, dP, dV, dQ, dK)
+    bwd_bytes = 3 * tok + 2 * B * R * k * w * 4 + 3 * B * R * n * d * 4
+    bwd_flops_tile = 10.0 * B * R * k * w * w * d
+    return dict(bwd_bytes=bwd_bytes, bwd_flops_tile=bwd_flops_tile,
+                route_bytes=route_bytes, attn_bytes=attn_bytes, ema_bytes=ema_bytes,
                 local_bytes=local_bytes, attn_flops_tile=attn_flops_tile,
                 attn_flops_causal=attn_flops_causal, route_flops=route_flops,
                 local_flops=local_flops)
 
 
-def cpu_baseline(cfg, inp, scale):
-    """The oracle on one full step of the workload on the host cores."""
+def cpu_baseline(cfg, inp, scale, min_seconds=5.0):
+    """The oracle on full steps of the workload on the host cores, repeated
+    until about `min_seconds` have passed (at least once)."""
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    t0 = time.perf_counter()
     qk = inp["qk"].value
-    _, idx, _, _ = oracle.route(qk, inp["mu"], cfg.w, nthreads=threads)
-    oracle.routed_attn(qk, qk, inp["v"].value, idx, scale, True, True, nthreads=threads)
-    oracle.centroid_update(inp["mu"], qk, qk, idx, cfg.lam)
-    if cfg.L > 0:
-        oracle.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
-                          cfg.window, scale, True, nthreads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": cfg.B * cfg.n / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "seconds": dt,
-            "sample": f"one full step ({cfg.name} workload: route, routed attention, EMA and "
-                      f"local attention), fp64, {threads} threads"}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        _, idx, _, _ = oracle.route(qk, inp["mu"], cfg.w, nthreads=threads)
+        oracle.routed_attn(qk, qk, inp["v"].value, idx, scale, True, True, nthreads=threads)
+        oracle.centroid_update(inp["mu"], qk, qk, idx, cfg.lam)
+        if cfg.backward:
+            oracle.routed_attn_bwd(qk, qk, inp["v"].value, idx, inp["dout"].value, scale, True,
+                                   nthreads=threads)
+        if cfg.L > 0:
+            oracle.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
+                              cfg.window, scale, True, nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": reps * cfg.B * cfg.n / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": dt, "steps": reps,
+            "sample": f"{reps} full step(s) of the {cfg.name} workload (route, routed attention, "
+                      f"EMA{', in-cluster backward' if cfg.backward else ''} and local "
+                      f"attention), fp64, {threads} threads"}
 
 
 def main():
@@ -134,13 +176,26 @@ def main():
     if cfg.L > 0:
         ql, kl, vl = dev(inp["q_local"]), dev(inp["k_local"]), dev(inp["v_local"])
         out_l = torch.empty_like(ql)
+    lse = None
+    if cfg.backward:
+        # the forward keeps its softmax statistics; the backward takes a seeded dO
+        lse = torch.empty((B, R, k, w), dtype=torch.float32, device="cuda")
+        dout = dev(inp["dout"])
+        grads = tuple(torch.empty((B, R, n, d), dtype=torch.float32, device="cuda")
+                      for _ in range(3))
+        ws_bwd = torch.empty(rt.workspace_bytes("routed_attn_bwd", B, R, n, d, k, w),
+                             dtype=torch.uint8, device="cuda")
 
     def do_route():
         rt.route(qk, mu, w, out=(inv, idx, mask), ws=ws_route)
 
     def do_attn():
         rt.routed_attn(qk, qk, v, idx, inv, inv, scale=scale, mask=mask, sums=(sum_q, None),
-                       out=out, ws=ws_attn)
+                       out=out, lse=lse, ws=ws_attn)
+
+    def do_bwd():
+        rt.routed_attn_bwd(qk, qk, v, idx, lse, dout, inv, inv, scale=scale, out=grads,
+                           ws=ws_bwd)
 
     def do_ema():
         rt.centroid_update_sums_(mu, sum_q, cfg.lam)
@@ -160,6 +215,8 @@ def main():
         do_route()
         do_attn()
         do_ema()
+        if cfg.backward:
+            do_bwd()
         if cfg.L > 0:
             if not args.concurrent_local:
                 do_local()
@@ -209,8 +266,9 @@ def main():
         # Per-call timing (events on the stream the kernels are launched on).
         per_call = {}
         for name, fn in (("rt_route", do_route), ("rt_routed_attn", do_attn),
-                         ("rt_centroid_update_sums", do_ema), ("rt_local_attn", do_local)):
-            if name == "rt_local_attn" and cfg.L == 0:
+                         ("rt_centroid_update_sums", do_ema), ("rt_local_attn", do_local),
+                         ("rt_routed_attn_bwd", do_bwd if cfg.backward else None)):
+            if (name == "rt_local_attn" and cfg.L == 0) or fn is None:
                 continue
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = max(5, args.steps)
@@ -240,6 +298,9 @@ def main():
         "rt_centroid_update_sums": rate(2 * R * k * d * 4 + B * R * k * d * 4, 0,
                                         per_call["rt_centroid_update_sums"]),
     }
+    if cfg.backward:
+        stages["rt_routed_attn_bwd"] = rate(alg["bwd_bytes"], alg["bwd_flops_tile"],
+                                            per_call["rt_routed_attn_bwd"])
     if cfg.L > 0:
         stages["rt_local_attn"] = rate(alg["local_bytes"], alg["local_flops"], per_call["rt_local_attn"])
         # The longest kernel of the step is the local-window attention; rt_local_attn launches
@@ -250,7 +311,8 @@ def main():
         achieved = alg["local_bytes"] / t / 1e9
         roofline = {"bound": "hbm", "kernel": "local_attn_bf16_kernel (rt_local_attn)",
                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                    "frac": achieved / PEAK_HBM_GBS,
+                    "traffic": measured_traffic(LOCAL_TRAFFIC, args.workload),
                     "algorithmic_bytes": alg["local_bytes"],
                     "mfma_frac": alg["local_flops"] / t / 1e12 / PEAK_BF16_TFLOPS}
     else:
@@ -275,7 +337,7 @@ def main():
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shapes)",
         "config": {"workload": WORKLOADS[args.workload], "batch": B, "seq_len": n,
                    "routed_heads": R, "local_heads": cfg.L, "d_head": d, "k": k, "w": w,
-                   "window": cfg.window, "graph": use_graph,
+                   "window": cfg.window, "graph": use_graph, "backward": cfg.backward,
                    "local_heads_stream": "concurrent" if args.concurrent_local else "same"},
         "roofline": roofline,
         "per_call_ms": per_call,

@@ -243,16 +243,21 @@ def centroid_update_sums_(mu: torch.Tensor, sum_q: torch.Tensor, lam: float,
 
 
 def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=None,
-                    causal=True, ws=None):
-    """Gradients (dq_hat, dk_hat, dv) of routed_attn for a fixed membership."""
+                    causal=True, out=None, ws=None):
+    """Gradients (dq_hat, dk_hat, dv), float32, of routed_attn for a fixed
+    membership; ``lse`` comes from the forward call (want_lse=True) and
+    ``out`` may hold three preallocated float32 [B,H,n,d] tensors."""
     lib = _load()
     dev = _gpu(q, kk, v, idx, lse, dout, q_inv, k_inv)
     B, H, n, d = q.shape
     k, w = idx.shape[2], idx.shape[3]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    dk = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    dv = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    dq, dk, dv = out
+    _gpu(dq, dk, dv)
+    if any(t.dtype != torch.float32 for t in out):
+        raise TypeError("gradients are float32")
     ws, _ = _workspace("routed_attn_bwd", dev, B, H, n, d, k, w, ws)
     _check(lib.rt_routed_attn_bwd(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
                                   _ptr(k_inv), _ptr(idx), _ptr(lse), _ptr(dout), B, H, n, d, k, w,
