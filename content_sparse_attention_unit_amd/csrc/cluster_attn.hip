@@ -94,25 +94,36 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
     __shared__ __attribute__((aligned(16))) float linvq[C::QROWS];
     __shared__ int lpos[WMAX];    // position, or -1 for padding / invalid rows
     __shared__ int ldest[WMAX];   // see row_dest
-    __shared__ float lsum[C::NT];
+    // partial member sums per wave (one side for shared q/k, else keys then queries)
+    __shared__ float lsum[SHARED ? 1 : 2][C::NW][C::DP];
 
     const int cl = blockIdx.x, bh = blockIdx.y;
     const long tokbase = (long)bh * n;
     const long rowbase = ((long)bh * k + cl) * w;
     const int32_t* irow = idx + rowbase;
 
-    // Request every member row at once: keys/queries, then values.
+    // Request every member row at once: keys/queries, then values.  Thread t
+    // holds the 16-byte chunk t % CPR of rows t / CPR + (NT / CPR) * it.
+    const bool want_sums = sum_q != nullptr || sum_k != nullptr;
     uint4 xk[C::XPT], xq[SHARED ? 1 : C::XPT];
+    float ikr[C::XPT], iqr[SHARED ? 1 : C::XPT];   // their inverse norms (0 on padding)
 #pragma unroll
     for (int it = 0; it < C::XPT; ++it) {
         const int e = threadIdx.x + it * C::NT;
         const int r = e / C::CPR, ch = e % C::CPR;
         xk[it] = zero_u4();
         if (!SHARED) xq[it] = zero_u4();
+        ikr[it] = 0.f;
+        if (!SHARED) iqr[it] = 0.f;
         if (r < w && 8 * ch < D) {
-            const long off = (tokbase + clamp_pos(irow[r], n)) * D + 8 * ch;
+            const long tok = tokbase + clamp_pos(irow[r], n);
+            const long off = tok * D + 8 * ch;
             xk[it] = *reinterpret_cast<const uint4*>(kk + off);
             if (!SHARED) xq[it] = *reinterpret_cast<const uint4*>(q + off);
+            if (want_sums) {
+                ikr[it] = k_inv ? k_inv[tok] : 1.f;
+                if (!SHARED) iqr[it] = q_inv ? q_inv[tok] : 1.f;
+            }
         }
     }
     uint4 va[C::VPT];
@@ -150,37 +161,44 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
             if (!SHARED) *reinterpret_cast<uint4*>(&lq[r * C::LDX + 8 * ch]) = xq[it];
         }
     }
-    __syncthreads();
-
-    // Per-cluster sums of the normalised member rows (for the centroid update).
-    if (sum_q != nullptr || sum_k != nullptr) {
+    // Per-cluster sums of the normalised member rows (for the centroid update):
+    // each thread sums its own rows, then the lanes holding the same chunk, then
+    // the waves (after the barrier below).  Fixed order, so deterministic.
+    static_assert(C::NT % C::CPR == 0 && 64 % C::CPR == 0, "chunk per thread must be fixed");
+    if (want_sums) {
+        const int lane0 = lane_id(), wv0 = threadIdx.x >> 6;
 #pragma unroll
-        for (int side = 0; side < 2; ++side) {
-            float* dst = side == 0 ? sum_k : sum_q;
-            if (dst == nullptr) continue;
-            dst += ((long)bh * k + cl) * D;
-            const u16* src = (side == 0 || SHARED) ? lx : lq;
-            const float* inv = (side == 0 || SHARED) ? linvk : linvq;
-            if constexpr (C::NT >= D) {
-                constexpr int PARTS = C::NT / D;      // row groups summed in parallel
-                const int dcol = threadIdx.x % D, part = threadIdx.x / D;
-                float acc = 0.f;
-                for (int r = part; r < w; r += PARTS) acc = fmaf(bf2f(src[r * C::LDX + dcol]), inv[r], acc);
-                __syncthreads();
-                lsum[threadIdx.x] = acc;
-                __syncthreads();
-                if (threadIdx.x < D) {
-                    float tot = 0.f;
-                    for (int p2 = 0; p2 < PARTS; ++p2) tot += lsum[p2 * D + threadIdx.x];
-                    dst[threadIdx.x] = tot;
-                }
-            } else {
-                for (int dcol = threadIdx.x; dcol < D; dcol += C::NT) {
-                    float acc = 0.f;
-                    for (int r = 0; r < w; ++r) acc = fmaf(bf2f(src[r * C::LDX + dcol]), inv[r], acc);
-                    dst[dcol] = acc;
-                }
+        for (int side = 0; side < (SHARED ? 1 : 2); ++side) {
+            float a[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = 0.f;
+#pragma unroll
+            for (int it = 0; it < C::XPT; ++it) {
+                const uint4 x = (side == 0) ? xk[it] : xq[SHARED ? 0 : it];
+                const float iv = (side == 0) ? ikr[it] : iqr[SHARED ? 0 : it];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a[j] = fmaf(u4_elem(x, j), iv, a[j]);
             }
+#pragma unroll
+            for (int off = C::CPR; off < 64; off <<= 1)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a[j] += __shfl_xor(a[j], off);
+            if (lane0 < C::CPR) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) lsum[side][wv0][8 * lane0 + j] = a[j];
+            }
+        }
+    }
+    __syncthreads();
+    if (want_sums) {
+        const long sbase = ((long)bh * k + cl) * D;
+        for (int dcol = threadIdx.x; dcol < D; dcol += C::NT) {
+            float tot[2] = {0.f, 0.f};
+#pragma unroll
+            for (int side = 0; side < (SHARED ? 1 : 2); ++side)
+                for (int v2 = 0; v2 < C::NW; ++v2) tot[side] += lsum[side][v2][dcol];
+            if (sum_k != nullptr) sum_k[sbase + dcol] = tot[0];
+            if (sum_q != nullptr) sum_q[sbase + dcol] = tot[SHARED ? 0 : 1];
         }
     }
 

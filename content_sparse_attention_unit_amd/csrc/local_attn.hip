@@ -38,9 +38,10 @@ struct LocalCfg {
     static constexpr int VPT = (VITEMS + NT - 1) / NT;     // ... per thread
 };
 
-// The next key/value tile travels through registers (issued before the
-// current tile's compute, stored to LDS after it).
-#define RT_LOAD_TILE(KT0)                                                                   \
+// Key/value tiles travel through registers: a tile's loads are issued two
+// tiles ahead of its use and stored to LDS one tile ahead, so global-load
+// latency overlaps two tiles of compute.
+#define RT_LOAD_TILE(tk, tv, KT0)                                                           \
     do {                                                                                    \
         _Pragma("unroll") for (int it = 0; it < C::KPT; ++it) {                              \
             const int e = threadIdx.x + C::NT * it;                                         \
@@ -59,7 +60,7 @@ struct LocalCfg {
         }                                                                                   \
     } while (0)
 
-#define RT_STORE_TILE(LK, LV)                                                               \
+#define RT_STORE_TILE(LK, LV, tk, tv)                                                       \
     do {                                                                                    \
         _Pragma("unroll") for (int it = 0; it < C::KPT; ++it) {                              \
             const int e = threadIdx.x + C::NT * it;                                         \
@@ -116,56 +117,64 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
     for (int jb = 0; jb < C::NJ; ++jb) o[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, z = 0.f;
 
+    // One tile of keys [KT0, KT0 + 64) from LDS buffer BUF against this wave's queries.
+#define RT_COMPUTE_TILE(KT0, BUF)                                                            \
+    do {                                                                                     \
+        const int kt_ = (KT0);                                                               \
+        if (kt_ + C::KT - 1 >= blo && kt_ <= bhi) {        /* tile meets this wave's band */ \
+            const u16* LK = lk[BUF];                                                         \
+            f32x4 sv[4];                                                                     \
+            _Pragma("unroll") for (int kb = 0; kb < 4; ++kb) {                               \
+                const int key0 = kt_ + 16 * kb;                                              \
+                if (key0 + 15 < blo || key0 > bhi || key0 >= n) {                            \
+                    sv[kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};              \
+                    continue;                                                                \
+                }                                                                            \
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};                                            \
+                _Pragma("unroll") for (int s = 0; s < C::NS; ++s) {                          \
+                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(              \
+                        &LK[(16 * kb + r16) * C::LDX + 32 * s + 8 * g]));                    \
+                    acc = mfma16(a, as_bf16x8(qreg[s]), acc);                                \
+                }                                                                            \
+                sv[kb] = acc * sl2;                                                          \
+            }                                                                                \
+            if (kt_ < clo || kt_ + C::KT - 1 > chi) { /* not inside every band: mask */      \
+                _Pragma("unroll") for (int kb = 0; kb < 4; ++kb)                             \
+                    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                          \
+                        const int j = kt_ + 16 * kb + 4 * g + i;                             \
+                        const bool ok = j < n && j > qi - window &&                          \
+                                        (causal ? j <= qi : j < qi + window);                \
+                        sv[kb][i] = ok ? sv[kb][i] : -INFINITY;                              \
+                    }                                                                        \
+            }                                                                                \
+            const int halves = ((kt_ + 31 >= blo && kt_ <= bhi) ? 1 : 0) |                   \
+                               ((kt_ + 63 >= blo && kt_ + 32 <= bhi) ? 2 : 0);               \
+            softmax_pv_chunk<C::NJ, C::LDX>(sv, m, z, o, lv[BUF], r16, g, halves);           \
+        }                                                                                    \
+    } while (0)
+
     const int kt_first = lo & ~(C::KT - 1);
-    uint4 tk[C::KPT], tv[C::VPT];
-    RT_LOAD_TILE(kt_first);
-    RT_STORE_TILE(lk[0], lv[0]);
+    uint4 tka[C::KPT], tva[C::VPT], tkb[C::KPT], tvb[C::VPT];
+    RT_LOAD_TILE(tka, tva, kt_first);
+    if (kt_first + C::KT <= hi) RT_LOAD_TILE(tkb, tvb, kt_first + C::KT);
+    RT_STORE_TILE(lk[0], lv[0], tka, tva);
     __syncthreads();
 
-    int buf = 0;
-    for (int kt = kt_first; kt <= hi; kt += C::KT) {
-        const bool more = kt + C::KT <= hi;
-        if (more) RT_LOAD_TILE(kt + C::KT);   // in flight during compute
-        if (kt + C::KT - 1 >= blo && kt <= bhi) {               // tile meets this wave's band
-            const u16* LK = lk[buf];
-            f32x4 sv[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int key0 = kt + 16 * kb;
-                if (key0 + 15 < blo || key0 > bhi || key0 >= n) {
-                    sv[kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                    continue;
-                }
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < C::NS; ++s) {
-                    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(
-                        &LK[(16 * kb + r16) * C::LDX + 32 * s + 8 * g]));
-                    acc = mfma16(a, as_bf16x8(qreg[s]), acc);
-                }
-                sv[kb] = acc * sl2;
-            }
-            if (kt < clo || kt + C::KT - 1 > chi) {   // tile not entirely inside every band
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = kt + 16 * kb + 4 * g + i;
-                        const bool ok = j < n && j > qi - window &&
-                                        (causal ? j <= qi : j < qi + window);
-                        sv[kb][i] = ok ? sv[kb][i] : -INFINITY;
-                    }
-            }
-            const int halves = ((kt + 31 >= blo && kt <= bhi) ? 1 : 0) |
-                               ((kt + 63 >= blo && kt + 32 <= bhi) ? 2 : 0);
-            softmax_pv_chunk<C::NJ, C::LDX>(sv, m, z, o, lv[buf], r16, g, halves);
-        }
-        if (more) {
-            RT_STORE_TILE(lk[buf ^ 1], lv[buf ^ 1]);
-            __syncthreads();
-            buf ^= 1;
-        }
+    // Two tiles per trip so that the two register sets keep static names: on
+    // entry the tile at kt is in LDS buffer 0 and the next one in set b.
+    for (int kt = kt_first;; kt += 2 * C::KT) {
+        if (kt + 2 * C::KT <= hi) RT_LOAD_TILE(tka, tva, kt + 2 * C::KT);
+        RT_COMPUTE_TILE(kt, 0);
+        if (kt + C::KT > hi) break;
+        RT_STORE_TILE(lk[1], lv[1], tkb, tvb);
+        __syncthreads();
+        if (kt + 3 * C::KT <= hi) RT_LOAD_TILE(tkb, tvb, kt + 3 * C::KT);
+        RT_COMPUTE_TILE(kt + C::KT, 1);
+        if (kt + 2 * C::KT > hi) break;
+        RT_STORE_TILE(lk[0], lv[0], tka, tva);
+        __syncthreads();
     }
+#undef RT_COMPUTE_TILE
 
     const float zt = xor_sum_16_32(z);
     const float rz = 1.0f / zt;
