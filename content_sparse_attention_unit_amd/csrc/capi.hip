@@ -54,7 +54,8 @@ rt_status check_clusters(const char* fn, int n, int k, int w) {
 size_t route_ws(int B, int H, int n, int k) { return (size_t)B * H * k * n * sizeof(float); }
 
 // rt_routed_attn workspace: mask [B*H*n][KW] u32 | slots [B*H*n][kSlots][d] f32 |
-// overflow [B*H*k*w][d] f32, each part 256-byte aligned.
+// overflow [B*H*k*w][d] f32 | directory [B*H*n][k - kSlots] i32, each part
+// 256-byte aligned.
 size_t attn_ws_mask(int B, int H, int n, int k) {
     return align256((size_t)B * H * n * rt::mask_words(k) * sizeof(uint32_t));
 }
@@ -63,9 +64,13 @@ size_t attn_ws_slots(int B, int H, int n, int d) {
     return align256((size_t)B * H * n * rt::kSlots * d * sizeof(float));
 }
 
+size_t attn_ws_ovf(int B, int H, int d, int k, int w) {
+    return align256((size_t)B * H * k * w * d * sizeof(float));
+}
+
 size_t attn_ws(int B, int H, int n, int d, int k, int w) {
-    return attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d) +
-           (size_t)B * H * k * w * d * sizeof(float);
+    return attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d) + attn_ws_ovf(B, H, d, k, w) +
+           (size_t)B * H * n * rt::ovf_ranks(k) * sizeof(int32_t);
 }
 
 bool out_dtype_ok(int t) { return t == RT_F32 || t == RT_BF16; }
@@ -163,6 +168,8 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
     uint32_t* mask_ws = reinterpret_cast<uint32_t*>(base);
     float* slots = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k));
     float* ovf = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d));
+    int32_t* dir = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ovf) +
+                                              attn_ws_ovf(B, H, d, k, w));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = B * H;
     hipError_t e = hipSuccess;
@@ -173,9 +180,9 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
         mask = mask_ws;
     }
     e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, mask, BH, n, d, k, w, scale,
-                                causal, out, out_dtype, lse, slots, ovf, sum_q, sum_k, s);
+                                causal, out, out_dtype, lse, slots, ovf, dir, sum_q, sum_k, s);
     if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_combine(mask, idx, slots, ovf, out_dtype, BH, n, d, k, w, out, s);
+    e = rt::launch_combine(mask, slots, ovf, dir, out_dtype, BH, n, d, k, w, out, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

@@ -13,9 +13,9 @@
 // cnt = popcount(mask[t]) and rank = number of set bits below c.  A token held
 // by one cluster is written straight to `out`; otherwise its row goes to the
 // partial buffer at slot `rank` (token-major, kSlots slots per token; higher
-// ranks go to a cluster-major overflow buffer), and combine_kernel sums the
-// slots in rank order, i.e. ascending centroid order, so results are
-// deterministic.
+// ranks go to a cluster-major overflow buffer and are listed in a per-token
+// directory), and combine_kernel sums the slots in rank order, i.e. ascending
+// centroid order, so results are deterministic.
 //
 // Kernels
 //   zero_u32_kernel / mask_kernel   build the bitmask from idx (skipped when
@@ -84,8 +84,8 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
     const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
     int KW, float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ slots, float* __restrict__ ovf, float* __restrict__ sum_q,
-    float* __restrict__ sum_k) {
+    float* __restrict__ slots, float* __restrict__ ovf, int32_t* __restrict__ dir,
+    float* __restrict__ sum_q, float* __restrict__ sum_k) {
     using C = AttnCfg<D, WMAX, SHARED>;
     __shared__ __attribute__((aligned(16))) u16 lx[WMAX * C::LDX];
     __shared__ __attribute__((aligned(16))) u16 lq[C::QROWS * C::LDX];
@@ -143,6 +143,7 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
             if (raw >= 0 && raw < n) {
                 pos = raw;
                 dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
+                if (dest >= kSlots) dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
             }
             ik = k_inv ? k_inv[tokbase + posc] : 1.f;
             iq = q_inv ? q_inv[tokbase + posc] : 1.f;
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
     const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
     int KW, float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ slots, float* __restrict__ ovf) {
+    float* __restrict__ slots, float* __restrict__ ovf, int32_t* __restrict__ dir) {
     __shared__ float lg[1024];
     __shared__ float lqrow[D];
     const int r = blockIdx.x, cl = blockIdx.y, bh = blockIdx.z;
@@ -352,6 +353,7 @@ __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     __syncthreads();
     const bool valid = raw >= 0 && raw < n;
     const int dest = valid ? row_dest(mask + (tokbase + raw) * KW, KW, cl) : -2;
+    if (dest >= kSlots && lane == 0) dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
     for (int i = lane; i < D; i += 64) {
         float acc = 0.f;
         if (z > 0.f) {
@@ -384,13 +386,13 @@ __global__ __launch_bounds__(128) void cluster_sums_f32_kernel(
 }
 
 // One thread per (token, 16 output dims): the slots hold the rows of ranks
-// 0..kSlots-1 contiguously; higher ranks are found in the overflow buffer by
-// walking the mask in ascending centroid order.
+// 0..kSlots-1 contiguously; higher ranks are read from the overflow buffer at
+// the rows the directory lists.
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ mask,
-                                                      const int32_t* __restrict__ idx,
                                                       const float* __restrict__ slots,
-                                                      const float* __restrict__ ovf, long BHn,
+                                                      const float* __restrict__ ovf,
+                                                      const int32_t* __restrict__ dir, long BHn,
                                                       int n, int k, int w, int KW,
                                                       OutT* __restrict__ out) {
     constexpr int DG = D / 16;
@@ -423,33 +425,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
         }
     }
     if (cnt > kSlots) {
-        const long bh = tok / n;
-        const int t = (int)(tok % n);
-        int seen = 0;
-        for (int wi = 0; wi < KW; ++wi) {
-            uint32_t bits = mrow[wi];
-            while (bits) {
-                const int c = 32 * wi + __ffs(bits) - 1;
-                bits &= bits - 1u;
-                if (seen++ < kSlots) continue;
-                const int32_t* ir = idx + (bh * k + c) * w;
-                int lo = 0, hi = w;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (ir[mid] < t) lo = mid + 1;
-                    else hi = mid;
-                }
-                if (lo < w && ir[lo] == t) {
-                    const float* op = ovf + ((bh * k + c) * w + lo) * D + d0;
+        const long bhkw = (tok / n) * k * (long)w;
+        const int32_t* drow = dir + tok * (k - kSlots);
+        for (int j = kSlots; j < cnt; ++j) {
+            const float* op = ovf + (bhkw + drow[j - kSlots]) * D + d0;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 o = *reinterpret_cast<const float4*>(op + 4 * q);
-                        acc[q].x += o.x;
-                        acc[q].y += o.y;
-                        acc[q].z += o.z;
-                        acc[q].w += o.w;
-                    }
-                }
+            for (int q = 0; q < 4; ++q) {
+                const float4 o = *reinterpret_cast<const float4*>(op + 4 * q);
+                acc[q].x += o.x;
+                acc[q].y += o.y;
+                acc[q].z += o.z;
+                acc[q].w += o.w;
             }
         }
     }
@@ -467,7 +453,9 @@ struct AttnArgs {
     float scale;
     int causal;
     void* out;
-    float *lse, *slots, *ovf, *sum_q, *sum_k;
+    float *lse, *slots, *ovf;
+    int32_t* dir;
+    float *sum_q, *sum_k;
 };
 
 template <int D, int WMAX, bool SHARED, typename OutT>
@@ -476,7 +464,7 @@ void launch_bf16(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((cluster_attn_bf16_kernel<D, WMAX, SHARED, OutT>), dim3(a.k, a.BH),
                        dim3(C::NT), 0, s, (const u16*)a.q, (const u16*)a.kk, (const u16*)a.v,
                        a.q_inv, a.k_inv, a.idx, a.mask, a.n, a.k, a.w, a.KW, a.scale, a.causal,
-                       (OutT*)a.out, a.lse, a.slots, a.ovf, a.sum_q, a.sum_k);
+                       (OutT*)a.out, a.lse, a.slots, a.ovf, a.dir, a.sum_q, a.sum_k);
 }
 
 template <int D, bool SHARED, typename OutT>
@@ -501,7 +489,7 @@ void launch_d(const AttnArgs& a, int dtype, hipStream_t s) {
         hipLaunchKernelGGL((cluster_attn_f32_kernel<D, OutT>), dim3(a.w, a.k, a.BH), dim3(64), 0,
                            s, (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.q_inv,
                            a.k_inv, a.idx, a.mask, a.n, a.k, a.w, a.KW, a.scale, a.causal,
-                           (OutT*)a.out, a.lse, a.slots, a.ovf);
+                           (OutT*)a.out, a.lse, a.slots, a.ovf, a.dir);
         if (a.sum_q)
             hipLaunchKernelGGL(cluster_sums_f32_kernel, dim3(a.k, a.BH), dim3(128), 0, s,
                                (const float*)a.q, a.q_inv, a.idx, a.n, D, a.k, a.w, a.sum_q);
@@ -548,42 +536,42 @@ hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int
                                const float* q_inv, const float* k_inv, const int32_t* idx,
                                const uint32_t* mask, int BH, int n, int d, int k, int w,
                                float scale, int causal, void* out, int out_dtype, float* lse,
-                               float* slots, float* ovf, float* sum_q, float* sum_k,
-                               hipStream_t s) {
+                               float* slots, float* ovf, int32_t* dir, float* sum_q,
+                               float* sum_k, hipStream_t s) {
     const AttnArgs a{q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, mask_words(k), scale,
-                     causal, out, lse, slots, ovf, sum_q, sum_k};
+                     causal, out, lse, slots, ovf, dir, sum_q, sum_k};
     if (out_dtype == 1) launch_outt<u16>(a, dtype, d, s);
     else launch_outt<float>(a, dtype, d, s);
     return hipGetLastError();
 }
 
 template <typename OutT, int D>
-void launch_combine_d(const uint32_t* mask, const int32_t* idx, const float* slots,
-                      const float* ovf, int BH, int n, int k, int w, void* out, hipStream_t s) {
+void launch_combine_d(const uint32_t* mask, const float* slots, const float* ovf,
+                      const int32_t* dir, int BH, int n, int k, int w, void* out, hipStream_t s) {
     const long BHn = (long)BH * n;
     const long threads = BHn * (D / 16);
     hipLaunchKernelGGL((combine_kernel<OutT, D>), dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, s, mask, idx, slots, ovf, BHn, n, k, w, mask_words(k),
+                       dim3(256), 0, s, mask, slots, ovf, dir, BHn, n, k, w, mask_words(k),
                        (OutT*)out);
 }
 
 template <typename OutT>
-void launch_combine_t(const uint32_t* mask, const int32_t* idx, const float* slots,
-                      const float* ovf, int BH, int n, int d, int k, int w, void* out,
+void launch_combine_t(const uint32_t* mask, const float* slots, const float* ovf,
+                      const int32_t* dir, int BH, int n, int d, int k, int w, void* out,
                       hipStream_t s) {
     switch (d) {
-        case 16: launch_combine_d<OutT, 16>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
-        case 32: launch_combine_d<OutT, 32>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
-        case 64: launch_combine_d<OutT, 64>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
-        default: launch_combine_d<OutT, 128>(mask, idx, slots, ovf, BH, n, k, w, out, s); break;
+        case 16: launch_combine_d<OutT, 16>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
+        case 32: launch_combine_d<OutT, 32>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
+        case 64: launch_combine_d<OutT, 64>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
+        default: launch_combine_d<OutT, 128>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
     }
 }
 
-hipError_t launch_combine(const uint32_t* mask, const int32_t* idx, const float* slots,
-                          const float* ovf, int out_dtype, int BH, int n, int d, int k, int w,
+hipError_t launch_combine(const uint32_t* mask, const float* slots, const float* ovf,
+                          const int32_t* dir, int out_dtype, int BH, int n, int d, int k, int w,
                           void* out, hipStream_t s) {
-    if (out_dtype == 1) launch_combine_t<u16>(mask, idx, slots, ovf, BH, n, d, k, w, out, s);
-    else launch_combine_t<float>(mask, idx, slots, ovf, BH, n, d, k, w, out, s);
+    if (out_dtype == 1) launch_combine_t<u16>(mask, slots, ovf, dir, BH, n, d, k, w, out, s);
+    else launch_combine_t<float>(mask, slots, ovf, dir, BH, n, d, k, w, out, s);
     return hipGetLastError();
 }
 

@@ -107,6 +107,7 @@ struct BwdOut {
     float *dq, *dk, *dv;           // token order (rows of tokens held by one cluster)
     float *sq, *sk, *sv;           // rank slots
     float *oq, *ok, *ov;           // overflow ranks
+    int32_t* dir;                  // overflow directory (shared by the three)
 };
 
 template <int D, int WMAX, bool SHARED>
@@ -142,7 +143,11 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
         if (r < w) {
             const int raw = irow[r];
             const int posc = clamp_pos(raw, n);
-            if (raw >= 0 && raw < n) dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
+            if (raw >= 0 && raw < n) {
+                dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
+                if (dest >= kSlots)
+                    out.dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
+            }
             ik = k_inv ? k_inv[tokbase + posc] : 1.f;
             iq = q_inv ? q_inv[tokbase + posc] : 1.f;
             l2 = lse[rowbase + r] * 1.4426950408889634f;
@@ -369,6 +374,8 @@ __global__ __launch_bounds__(256) void cluster_attn_bwd_f32_kernel(
             av = fmaf(P[s][r], dout[(tokbase + tokr[s]) * D + i], av);
         }
         const int dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
+        if (dest >= kSlots && i == 0)
+            out.dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
         const float vals[3] = {aq * scale, ak * scale, av};
         float* direct[3] = {out.dq, out.dk, out.dv};
         float* slot[3] = {out.sq, out.sk, out.sv};
@@ -455,9 +462,14 @@ int max_cluster_rows_bwd(int dtype, int d, bool shared_qk) {
     return bwd_max_rows(d, shared_qk);
 }
 
-// workspace: mask | 3 x (slots | overflow)
+size_t bwd_dir_bytes(int BH, int n, int k) {
+    return align256((size_t)BH * n * ovf_ranks(k) * sizeof(int32_t));
+}
+
+// workspace: mask | directory | 3 x (slots | overflow)
 size_t bwd_workspace_bytes(int BH, int n, int d, int k, int w) {
-    return bwd_mask_bytes(BH, n, k) + 3 * (bwd_slot_bytes(BH, n, d) + bwd_ovf_bytes(BH, d, k, w));
+    return bwd_mask_bytes(BH, n, k) + bwd_dir_bytes(BH, n, k) +
+           3 * (bwd_slot_bytes(BH, n, d) + bwd_ovf_bytes(BH, d, k, w));
 }
 
 hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
@@ -468,6 +480,8 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
     char* base = static_cast<char*>(ws);
     uint32_t* mask = reinterpret_cast<uint32_t*>(base);
     base += bwd_mask_bytes(BH, n, k);
+    int32_t* dir = reinterpret_cast<int32_t*>(base);
+    base += bwd_dir_bytes(BH, n, k);
     float* part[3][2];
     for (int j = 0; j < 3; ++j) {
         part[j][0] = reinterpret_cast<float*>(base);
@@ -478,7 +492,7 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
     hipError_t e = launch_mask(idx, BH, n, k, w, mask, s);
     if (e != hipSuccess) return e;
     const BwdOut out{dq, dk, dv, part[0][0], part[1][0], part[2][0],
-                     part[0][1], part[1][1], part[2][1]};
+                     part[0][1], part[1][1], part[2][1], dir};
     const BwdArgs a{q, kk, v, q_inv, k_inv, idx, lse, dout, mask, BH, n, k, w, mask_words(k),
                     scale, causal, out};
     switch (d) {
@@ -491,7 +505,7 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
     if (e != hipSuccess) return e;
     float* grads[3] = {dq, dk, dv};
     for (int j = 0; j < 3; ++j) {
-        e = launch_combine(mask, idx, part[j][0], part[j][1], 0, BH, n, d, k, w, grads[j], s);
+        e = launch_combine(mask, part[j][0], part[j][1], dir, 0, BH, n, d, k, w, grads[j], s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -29,8 +29,10 @@ hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t
 inline int mask_words(int k) { return (k + 31) / 32; }
 
 // Token-major partial-row slots per token; higher membership ranks overflow
-// to a cluster-major buffer.
+// to a cluster-major buffer, found through a per-token directory
+// dir[token][rank - kSlots] = c * w + r (cluster c, member row r).
 constexpr int kSlots = 4;
+inline int ovf_ranks(int k) { return k > kSlots ? k - kSlots : 0; }
 
 // Zero the bitmask mask [BH*n][mask_words(k)] and set one bit per membership.
 hipError_t launch_mask(const int32_t* idx, int BH, int n, int k, int w, uint32_t* mask,
@@ -40,11 +42,11 @@ hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int
                                const float* q_inv, const float* k_inv, const int32_t* idx,
                                const uint32_t* mask, int BH, int n, int d, int k, int w,
                                float scale, int causal, void* out, int out_dtype, float* lse,
-                               float* slots, float* ovf, float* sum_q, float* sum_k,
-                               hipStream_t s);
+                               float* slots, float* ovf, int32_t* dir, float* sum_q,
+                               float* sum_k, hipStream_t s);
 
-hipError_t launch_combine(const uint32_t* mask, const int32_t* idx, const float* slots,
-                          const float* ovf, int out_dtype, int BH, int n, int d, int k, int w,
+hipError_t launch_combine(const uint32_t* mask, const float* slots, const float* ovf,
+                          const int32_t* dir, int out_dtype, int BH, int n, int d, int k, int w,
                           void* out, hipStream_t s);
 
 // mu <- lambda*mu + (1-lambda)/2 * (sum_b sum_q[b] + sum_b sum_k[b]); sum_k may

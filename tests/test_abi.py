@@ -161,7 +161,10 @@ def test_workspace_sizes(lib):
     assert lib.rt_workspace_bytes(0, B, H, n, d, k, w) == B * H * k * n * 4
     mask = ((B * H * n * 2 * 4 + 255) // 256) * 256
     slots = ((B * H * n * 4 * d * 4 + 255) // 256) * 256
-    assert lib.rt_workspace_bytes(1, B, H, n, d, k, w) == mask + slots + B * H * k * w * d * 4
+    dirs = B * H * n * (k - 4) * 4                       # overflow directory
+    assert lib.rt_workspace_bytes(1, B, H, n, d, k, w) == mask + slots + B * H * k * w * d * 4 + dirs
+    assert lib.rt_workspace_bytes(1, B, H, n, d, 4, w) == (
+        ((B * H * n * 4 + 255) // 256) * 256 + slots + B * H * 4 * w * d * 4)   # k <= 4: none
     assert lib.rt_workspace_bytes(2, B, H, n, d, k, w) == 0
     assert lib.rt_workspace_bytes(3, B, H, n, d, k, w) == 0
     assert lib.rt_workspace_bytes(9, B, H, n, d, k, w) == ctypes.c_size_t(-1).value
@@ -211,4 +214,5 @@ def test_bwd_workspace_size(lib):
     mask = ((B * H * n * 4 * 4 + 255) // 256) * 256
     slots = ((B * H * n * 4 * d * 4 + 255) // 256) * 256
     ovf = B * H * k * w * d * 4
-    assert lib.rt_workspace_bytes(4, B, H, n, d, k, w) == mask + 3 * (slots + ovf)
+    dirs = ((B * H * n * (k - 4) * 4 + 255) // 256) * 256
+    assert lib.rt_workspace_bytes(4, B, H, n, d, k, w) == mask + dirs + 3 * (slots + ovf)
