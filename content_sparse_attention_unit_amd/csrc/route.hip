@@ -268,80 +268,92 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     __shared__ uint32_t cand[CAND];      // keys sharing the selected top byte
     __shared__ uint32_t sel_bin, sel_rem;
     __shared__ uint32_t wgt[NWV], weq[NWV];
+    __shared__ uint32_t wtop[NWV][5];    // per wave: highest top byte, counts of it and 3 below
 
     const long row = blockIdx.x;
     const float* srow = scores + row * n;
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int seg0 = wv * kWave * KPT;
+    // Wave wv owns positions [seg0, seg0 + 64*KPT); its key j sits at
+    // seg0 + 64*VEC*(j / VEC) + VEC*lane + j % VEC: VEC consecutive positions
+    // per lane, loaded as one 16-byte vector when VEC = 4.
+    constexpr int VEC = (KPT % 4 == 0) ? 4 : 1;
+    auto key_pos = [&](int j) { return seg0 + kWave * VEC * (j / VEC) + VEC * lane + j % VEC; };
 
     uint32_t key[KPT];
-    uint32_t tmin = 0xffu, tmax = 0u;
+    uint32_t wtopb = 0u;   // highest top byte (sign and high exponent bits) in this lane
+    const bool vec_ok = VEC == 4 && (n & 3) == 0;   // rows start 16-byte aligned
+#pragma unroll
+    for (int jg = 0; jg < KPT / VEC; ++jg) {
+        const int p0 = key_pos(VEC * jg);
+        if (vec_ok && p0 + VEC <= n) {
+            const float4 f = *reinterpret_cast<const float4*>(srow + p0);
+            const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) key[VEC * jg + e] = order_key(fv[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) key[VEC * jg + e] = (p0 + e < n) ? order_key(srow[p0 + e]) : 0u;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if (key_pos(j) < n) wtopb = max(wtopb, key[j] >> 24);
+    // The w-th largest key nearly always has one of the row's four highest top
+    // bytes.  Each wave counts its keys in its own four highest top bytes with
+    // per-lane counters (a row's scores share top bytes in large groups, which
+    // makes an LDS histogram a hot spot of atomics); one exchange then gives
+    // the exact counts of the row's four highest top bytes.
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wtopb = max(wtopb, (uint32_t)__shfl_xor((int)wtopb, off));
+    uint32_t c01 = 0u, c23 = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        const int pos = seg0 + kWave * j + lane;
-        key[j] = (pos < n) ? order_key(srow[pos]) : 0u;
-        if (pos < n) {
-            tmin = min(tmin, key[j] >> 24);
-            tmax = max(tmax, key[j] >> 24);
+        const int pos = key_pos(j);
+        const uint32_t dlt = wtopb - (key[j] >> 24);   // >= 0 for every valid key
+        if (pos < n && dlt < 4u) {
+            if (dlt < 2u) c01 += 1u << (16 * dlt);
+            else c23 += 1u << (16 * (dlt - 2u));
         }
     }
-    // Range of the top byte (sign and high exponent bits) over the row.  A
-    // row's scores share it in large groups, so this first digit is counted
-    // with per-lane counts, not (heavily contended) LDS atomics.
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        tmin = min(tmin, (uint32_t)__shfl_xor((int)tmin, off));
-        tmax = max(tmax, (uint32_t)__shfl_xor((int)tmax, off));
-    }
+    c01 = wave_sum_u32(c01);
+    c23 = wave_sum_u32(c23);
     if (lane == 0) {
-        wgt[wv] = tmin;
-        weq[wv] = tmax;
+        wtop[wv][0] = wtopb;
+        wtop[wv][1] = c01 & 0xffffu;
+        wtop[wv][2] = c01 >> 16;
+        wtop[wv][3] = c23 & 0xffffu;
+        wtop[wv][4] = c23 >> 16;
     }
     __syncthreads();
-    tmin = 0xffu;
-    tmax = 0u;
-    for (int v = 0; v < NWV; ++v) {
-        tmin = min(tmin, wgt[v]);
-        tmax = max(tmax, weq[v]);
-    }
-    // The w-th largest key nearly always has one of the row's highest top
-    // bytes: walk down from the maximum with per-lane counts (a few steps),
-    // falling back to a full histogram of the top byte otherwise.
-    uint32_t bin0 = tmax, remaining = (uint32_t)w, ncand = 0u, cand_off = 0u;
+    uint32_t rtop = 0u;
+    for (int v = 0; v < NWV; ++v) rtop = max(rtop, wtop[v][0]);
+    uint32_t bin0 = rtop, remaining = (uint32_t)w, ncand = 0u, cand_off = 0u;
     bool found = false;
-    __syncthreads();  // wgt/weq (top-byte range) have been read by every thread
-    for (int step = 0; step < 4 && !found; ++step) {
-        uint32_t c = 0u;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const int pos = seg0 + kWave * j + lane;
-            c += (pos < n && (key[j] >> 24) == bin0) ? 1u : 0u;
-        }
-        c = wave_sum_u32(c);
-        if (lane == 0) wgt[wv] = c;
-        __syncthreads();
-        uint32_t tot = 0u;
+    for (uint32_t i = 0; i < 4u && i <= rtop; ++i) {
+        const uint32_t b = rtop - i;
+        uint32_t tot = 0u, before = 0u;
         for (int v = 0; v < NWV; ++v) {
-            if (v == wv) cand_off = tot;
-            tot += wgt[v];
+            const uint32_t dv = wtop[v][0] - b;   // wtop[v][0] <= rtop, so dv <= i
+            const uint32_t cv = (wtop[v][0] >= b) ? wtop[v][1 + dv] : 0u;
+            if (v < wv) before += cv;
+            tot += cv;
         }
-        __syncthreads();  // before wgt is written again
         if (tot >= remaining) {
-            found = true;
+            bin0 = b;
             ncand = tot;
-        } else if (bin0 == tmin) {
-            break;  // unreachable: every key has a top byte >= tmin
-        } else {
-            remaining -= tot;
-            --bin0;
+            cand_off = before;
+            found = true;
+            break;
         }
+        remaining -= tot;
     }
-    if (!found) {
+    if (!found) {   // the threshold lies lower: full histogram of the top byte
         for (int e = threadIdx.x; e < NWV * 256; e += NT) (&sub[0][0])[e] = 0u;
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const int pos = seg0 + kWave * j + lane;
+            const int pos = key_pos(j);
             if (pos < n) atomicAdd(&sub[wv][key[j] >> 24], 1u);
         }
         __syncthreads();
@@ -364,7 +376,7 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         // them (in position order) and finish on the short list.
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const int pos = seg0 + kWave * j + lane;
+            const int pos = key_pos(j);
             const bool is = pos < n && (key[j] >> 24) == bin0;
             const uint64_t mb = __ballot(is);
             if (is) cand[cand_off + (uint32_t)lanes_below(mb)] = key[j];
@@ -390,7 +402,7 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < KPT; ++j) {
-                const int pos = seg0 + kWave * j + lane;
+                const int pos = key_pos(j);
                 if (pos < n && (key[j] & himask) == prefix)
                     atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
             }
@@ -404,12 +416,12 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     }
     const uint32_t T = prefix, need_eq = remaining;
 
-    // Position-ordered compaction: wave wv owns positions [seg0, seg0 + 64*KPT),
-    // visited in (j, lane) order, which is ascending position.
+    // Position-ordered compaction: wave wv's positions are visited in
+    // ascending order (groups jg, then lanes, then the VEC keys of a lane).
     uint32_t gtc = 0u, eqc = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        const int pos = seg0 + kWave * j + lane;
+        const int pos = key_pos(j);
         const bool valid = pos < n;
         gtc += (valid && key[j] > T) ? 1u : 0u;
         eqc += (valid && key[j] == T) ? 1u : 0u;
@@ -428,26 +440,48 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         eq_before += weq[v];
     }
     int32_t* out = idx + row * w;
+    const long bh = row / k;
+    const int c = (int)(row % k);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int pos = seg0 + kWave * j + lane;
-        const bool valid = pos < n;
-        const bool gt = valid && key[j] > T;
-        const bool eq = valid && key[j] == T;
-        const uint64_t em = __ballot(eq);
-        const bool sel = gt || (eq && eq_before + (uint32_t)lanes_below(em) < need_eq);
-        const uint64_t sm = __ballot(sel);
-        const uint32_t slot = sel_before + (uint32_t)lanes_below(sm);
-        if (sel && slot < (uint32_t)w) {
-            out[slot] = pos;
-            if (mask != nullptr) {
-                const long bh = row / k;
-                const int c = (int)(row % k);
-                atomicOr(&mask[(bh * n + pos) * KW + (c >> 5)], 1u << (c & 31));
-            }
+    for (int jg = 0; jg < KPT / VEC; ++jg) {
+        // positions of group jg in ascending order: (lane, e) lexicographic
+        bool gt[VEC], eq[VEC], sel[VEC];
+        uint64_t eb[VEC], sb[VEC];
+        uint32_t eq_lanes = 0u, sel_lanes = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int j = VEC * jg + e;
+            const bool valid = key_pos(j) < n;
+            gt[e] = valid && key[j] > T;
+            eq[e] = valid && key[j] == T;
+            eb[e] = __ballot(eq[e]);
+            eq_lanes += (uint32_t)lanes_below(eb[e]);
         }
-        eq_before += (uint32_t)__popcll(em);
-        sel_before += (uint32_t)__popcll(sm);
+        uint32_t own = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            sel[e] = gt[e] || (eq[e] && eq_before + eq_lanes + own < need_eq);
+            own += eq[e] ? 1u : 0u;
+            sb[e] = __ballot(sel[e]);
+            sel_lanes += (uint32_t)lanes_below(sb[e]);
+        }
+        own = 0u;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const uint32_t slot = sel_before + sel_lanes + own;
+            if (sel[e] && slot < (uint32_t)w) {
+                const int pos = key_pos(VEC * jg + e);
+                out[slot] = pos;
+                if (mask != nullptr)
+                    atomicOr(&mask[(bh * n + pos) * KW + (c >> 5)], 1u << (c & 31));
+            }
+            own += sel[e] ? 1u : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            eq_before += (uint32_t)__popcll(eb[e]);
+            sel_before += (uint32_t)__popcll(sb[e]);
+        }
     }
 }
 
