@@ -257,6 +257,38 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int parts, int st
     }
 }
 
+// The same search done by each wave for itself on a shared histogram: every
+// lane gets the bin and the rank left inside it (no barrier needed after it).
+// `remaining` must be between 1 and the histogram total.
+__device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t remaining,
+                                              uint32_t& bin, uint32_t& rem) {
+    const int lane = lane_id();
+    const uint4 c4 = *reinterpret_cast<const uint4*>(hist + 4 * lane);
+    const uint32_t cnt[4] = {c4.x, c4.y, c4.z, c4.w};
+    const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    uint32_t suf = tot;   // inclusive suffix sum over lanes
+#pragma unroll
+    for (int dl = 1; dl < kWave; dl <<= 1) {
+        const uint32_t o = __shfl_down(suf, dl);
+        if (lane + dl < kWave) suf += o;
+    }
+    uint32_t above = suf - tot;
+    int fb = -1;
+    uint32_t fr = 0u;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+        if (above < remaining && remaining <= above + cnt[b]) {
+            fb = 4 * lane + b;
+            fr = remaining - above;
+        }
+        above += cnt[b];
+    }
+    const uint64_t m = __ballot(fb >= 0);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    bin = (uint32_t)__shfl(fb, src);
+    rem = (uint32_t)__shfl((int)fr, src);
+}
+
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scores, int n, int w,
                                                   int32_t* __restrict__ idx, int k,
@@ -268,7 +300,9 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     __shared__ uint32_t cand[CAND];      // keys sharing the selected top byte
     __shared__ uint32_t sel_bin, sel_rem;
     __shared__ uint32_t wgt[NWV], weq[NWV];
-    __shared__ uint32_t wtop[NWV][5];    // per wave: highest top byte, counts of it and 3 below
+    __shared__ __attribute__((aligned(16))) uint32_t wtop[NWV][8];   // per wave: highest top
+                                         // byte, counts of it and the 3 below (padded)
+    __shared__ __attribute__((aligned(16))) uint32_t hist3[3][256];
 
     const long row = blockIdx.x;
     const float* srow = scores + row * n;
@@ -325,17 +359,33 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         wtop[wv][3] = c23 & 0xffffu;
         wtop[wv][4] = c23 >> 16;
     }
+    // the first histogram of the candidate passes starts cleared
+    if (threadIdx.x < 256) hist3[0][threadIdx.x] = 0u;
     __syncthreads();
+    uint32_t wt[NWV][5];   // every wave's entry, read at once (independent LDS loads)
+#pragma unroll
+    for (int v = 0; v < NWV; ++v) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&wtop[v][0]);
+        wt[v][0] = a.x;
+        wt[v][1] = a.y;
+        wt[v][2] = a.z;
+        wt[v][3] = a.w;
+        wt[v][4] = wtop[v][4];
+    }
     uint32_t rtop = 0u;
-    for (int v = 0; v < NWV; ++v) rtop = max(rtop, wtop[v][0]);
+#pragma unroll
+    for (int v = 0; v < NWV; ++v) rtop = max(rtop, wt[v][0]);
     uint32_t bin0 = rtop, remaining = (uint32_t)w, ncand = 0u, cand_off = 0u;
     bool found = false;
     for (uint32_t i = 0; i < 4u && i <= rtop; ++i) {
         const uint32_t b = rtop - i;
         uint32_t tot = 0u, before = 0u;
+#pragma unroll
         for (int v = 0; v < NWV; ++v) {
-            const uint32_t dv = wtop[v][0] - b;   // wtop[v][0] <= rtop, so dv <= i
-            const uint32_t cv = (wtop[v][0] >= b) ? wtop[v][1 + dv] : 0u;
+            const uint32_t dv = wt[v][0] - b;   // wt[v][0] <= rtop, so dv <= i <= 3
+            uint32_t cv = 0u;
+            if (wt[v][0] >= b)
+                cv = dv == 0u ? wt[v][1] : dv == 1u ? wt[v][2] : dv == 2u ? wt[v][3] : wt[v][4];
             if (v < wv) before += cv;
             tot += cv;
         }
@@ -382,19 +432,23 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
             if (is) cand[cand_off + (uint32_t)lanes_below(mb)] = key[j];
             cand_off += (uint32_t)__popcll(mb);
         }
-        for (int shift = 16; shift >= 0; shift -= 8) {
-            if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
-            __syncthreads();
+        __syncthreads();
+        // One barrier per digit: every wave reads the histogram itself after
+        // it, and the histogram of the next digit (not read by anyone since
+        // the barrier before this one) is cleared while this one fills.
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = 16 - 8 * pass;
             for (uint32_t i = threadIdx.x; i < ncand; i += NT) {
                 const uint32_t kc = cand[i];
-                if ((kc & himask) == prefix) atomicAdd(&hist[(kc >> shift) & 255u], 1u);
+                if ((kc & himask) == prefix) atomicAdd(&hist3[pass][(kc >> shift) & 255u], 1u);
             }
+            if (threadIdx.x < 256) hist3[(pass + 1) % 3][threadIdx.x] = 0u;
             __syncthreads();
-            if (wv == 0) find_bin(hist, 1, 0, remaining, &sel_bin, &sel_rem);
-            __syncthreads();
-            prefix |= sel_bin << shift;
+            uint32_t b, r;
+            find_bin_wave(hist3[pass], remaining, b, r);
+            prefix |= b << shift;
             himask |= 0xffu << shift;
-            remaining = sel_rem;
+            remaining = r;
         }
     } else {
         for (int shift = 16; shift >= 0; shift -= 8) {
