@@ -7,11 +7,15 @@
 // softmax attention, to positions [i - window + 1, i] (causal) or to the band
 // |i - j| < window (non-causal).
 //
-// local_attn_bf16_kernel: one workgroup = 64 queries (4 waves x 16).  Key
-// tiles of 64 rows (and the matching value rows, transposed) are staged in
-// LDS and shared by the four waves; each wave computes S^T = K Q^T and
-// O^T = V^T P^T with v_mfma_f32_16x16x32_bf16 and an online softmax, skipping
-// key blocks that lie outside its own band.
+// local_attn_bf16_kernel: one workgroup = 128 queries in 8 blocks of 16, each
+// block served by two waves (16 waves): key/value tiles of 64 rows are staged
+// row-major in LDS, and of every tile one wave of a pair takes the first 32
+// keys, the other the last 32.  Each computes S^T = K Q^T and O^T = V^T P^T
+// with v_mfma_f32_16x16x32_bf16 (the transposed value operand read straight
+// from the row-major tile) and an online softmax over its keys; at the end the
+// two partial softmax states of a block are merged through LDS.  Splitting the
+// keys halves each wave's serial chain and doubles the waves per SIMD.  Key
+// blocks outside a block's band are skipped.
 #include "rt_common.hpp"
 #include "rt_internal.hpp"
 
@@ -27,9 +31,10 @@ struct LocalCfg {
     static constexpr int KT = 64;                // keys per tile
     static constexpr int NS = DP / 32;
     static constexpr int NJ = D / 16;
-    static constexpr int NWV = 8;                // waves per workgroup, 16 queries each
+    static constexpr int NQB = 8;                // 16-query blocks per workgroup
+    static constexpr int NWV = 2 * NQB;          // two waves per block (key halves)
     static constexpr int NT = 64 * NWV;
-    static constexpr int QT = 16 * NWV;          // queries per workgroup
+    static constexpr int QT = 16 * NQB;          // queries per workgroup
     static constexpr int CPR = DP / 8;
     static constexpr int DCH = D / 8;
     static constexpr int KITEMS = KT * CPR;                // key row chunks per tile
@@ -75,7 +80,7 @@ struct LocalCfg {
     } while (0)
 
 template <int D, typename OutT>
-__global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restrict__ q,
+__global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __restrict__ q,
                                                               const u16* __restrict__ kk,
                                                               const u16* __restrict__ v, int n,
                                                               int window, float scale, int causal,
@@ -93,8 +98,9 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const float sl2 = scale * 1.4426950408889634f;
-    const int qb0 = q0 + 16 * wv;      // first query of this wave's block
-    const int qi = qb0 + r16;          // this lane's query
+    const int hf = wv / C::NQB;                  // key half of every tile: [32 hf, 32 hf + 32)
+    const int qb0 = q0 + 16 * (wv % C::NQB);    // first query of this wave's block
+    const int qi = qb0 + r16;                    // this lane's query
 
     uint4 qreg[C::NS];
 #pragma unroll
@@ -117,15 +123,15 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
     for (int jb = 0; jb < C::NJ; ++jb) o[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, z = 0.f;
 
-    // One tile of keys [KT0, KT0 + 64) from LDS buffer BUF against this wave's queries.
+    // This wave's half of tile [KT0, KT0 + 64) from LDS buffer BUF.
 #define RT_COMPUTE_TILE(KT0, BUF)                                                            \
     do {                                                                                     \
-        const int kt_ = (KT0);                                                               \
-        if (kt_ + C::KT - 1 >= blo && kt_ <= bhi) {        /* tile meets this wave's band */ \
-            const u16* LK = lk[BUF];                                                         \
-            f32x4 sv[4];                                                                     \
-            _Pragma("unroll") for (int kb = 0; kb < 4; ++kb) {                               \
-                const int key0 = kt_ + 16 * kb;                                              \
+        const int kh_ = (KT0) + 32 * hf;                   /* first key of the half */       \
+        if (kh_ + 31 >= blo && kh_ <= bhi) {               /* half meets the band */         \
+            const u16* LK = lk[BUF] + 32 * hf * C::LDX;                                      \
+            f32x4 sv[2];                                                                     \
+            _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                               \
+                const int key0 = kh_ + 16 * kb;                                              \
                 if (key0 + 15 < blo || key0 > bhi || key0 >= n) {                            \
                     sv[kb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};              \
                     continue;                                                                \
@@ -138,18 +144,16 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
                 }                                                                            \
                 sv[kb] = acc * sl2;                                                          \
             }                                                                                \
-            if (kt_ < clo || kt_ + C::KT - 1 > chi) { /* not inside every band: mask */      \
-                _Pragma("unroll") for (int kb = 0; kb < 4; ++kb)                             \
+            if (kh_ < clo || kh_ + 31 > chi) {     /* not inside every band: mask */         \
+                _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
                     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                          \
-                        const int j = kt_ + 16 * kb + 4 * g + i;                             \
+                        const int j = kh_ + 16 * kb + 4 * g + i;                             \
                         const bool ok = j < n && j > qi - window &&                          \
                                         (causal ? j <= qi : j < qi + window);                \
                         sv[kb][i] = ok ? sv[kb][i] : -INFINITY;                              \
                     }                                                                        \
             }                                                                                \
-            const int halves = ((kt_ + 31 >= blo && kt_ <= bhi) ? 1 : 0) |                   \
-                               ((kt_ + 63 >= blo && kt_ + 32 <= bhi) ? 2 : 0);               \
-            softmax_pv_chunk<C::NJ, C::LDX>(sv, m, z, o, lv[BUF], r16, g, halves);           \
+            softmax_pv_half<C::NJ, C::LDX>(sv, m, z, o, lv[BUF] + 32 * hf * C::LDX, r16, g); \
         }                                                                                    \
     } while (0)
 
@@ -176,13 +180,40 @@ __global__ __launch_bounds__(512) void local_attn_bf16_kernel(const u16* __restr
     }
 #undef RT_COMPUTE_TILE
 
-    const float zt = xor_sum_16_32(z);
-    const float rz = 1.0f / zt;
-    if (qi < n) {
-        OutT* dst = out + (base + qi) * D + 4 * g;
+    // Merge the two key halves of each block: the second wave of a pair hands
+    // its softmax state (max, partial denominator, accumulators) to the first
+    // through LDS, reusing the tile buffers.
+    constexpr int MS = 2 + 4 * C::NJ;            // floats per lane
+    static_assert(C::NQB * 64 * MS * 4 <= (int)sizeof(lk) + (int)sizeof(lv), "merge area");
+    float* lmerge = reinterpret_cast<float*>(&lk[0][0]);
+    __syncthreads();                             // every wave is done with the tiles
+    float* mine = lmerge + ((wv % C::NQB) * 64 + lane) * MS;
+    if (hf == 1) {
+        mine[0] = m;
+        mine[1] = z;
 #pragma unroll
         for (int jb = 0; jb < C::NJ; ++jb)
-            store4<OutT>(dst + 16 * jb, o[jb][0] * rz, o[jb][1] * rz, o[jb][2] * rz, o[jb][3] * rz);
+            *reinterpret_cast<float4*>(mine + 2 + 4 * jb) =
+                make_float4(o[jb][0], o[jb][1], o[jb][2], o[jb][3]);
+    }
+    __syncthreads();
+    if (hf == 0) {
+        const float m2 = mine[0], z2 = mine[1];
+        const float mt = fmaxf(m, m2);
+        const float ms = (mt == -INFINITY) ? 0.f : mt;
+        const float a1 = __builtin_amdgcn_exp2f(m - ms), a2 = __builtin_amdgcn_exp2f(m2 - ms);
+        const float zt = xor_sum_16_32(z * a1 + z2 * a2);
+        const float rz = 1.0f / zt;
+        if (qi < n) {
+            OutT* dst = out + (base + qi) * D + 4 * g;
+#pragma unroll
+            for (int jb = 0; jb < C::NJ; ++jb) {
+                const float4 o2 = *reinterpret_cast<const float4*>(mine + 2 + 4 * jb);
+                store4<OutT>(dst + 16 * jb, (o[jb][0] * a1 + o2.x * a2) * rz,
+                             (o[jb][1] * a1 + o2.y * a2) * rz, (o[jb][2] * a1 + o2.z * a2) * rz,
+                             (o[jb][3] * a1 + o2.w * a2) * rz);
+            }
+        }
     }
 }
 

@@ -162,6 +162,46 @@ __device__ __forceinline__ int row_dest(const uint32_t* __restrict__ m, int KW, 
     return cnt == 1 ? -1 : below;
 }
 
+// The online-softmax step over 32 keys: `sv[kb][i]` holds the logits (log2
+// units, -inf where masked) of keys 16*kb + 4*g + i of the half tile whose
+// first value row `lv` points at (row stride LDX).
+template <int NJ, int LDX>
+__device__ __forceinline__ void softmax_pv_half(f32x4 (&sv)[2], float& m, float& z,
+                                                f32x4 (&o)[NJ], const u16* lv, int r16, int g) {
+    float cmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float mnew = fmaxf(m, cmax);
+    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+    if (__ballot(mnew != m) != 0ull) {
+        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+        z *= alpha;
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) o[jb] *= alpha;
+        m = mnew;
+    }
+    uint32_t pw[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[kb][0] - msafe);
+        const float p1 = __builtin_amdgcn_exp2f(sv[kb][1] - msafe);
+        const float p2 = __builtin_amdgcn_exp2f(sv[kb][2] - msafe);
+        const float p3 = __builtin_amdgcn_exp2f(sv[kb][3] - msafe);
+        z += (p0 + p1) + (p2 + p3);
+        pw[kb][0] = cvt_pk_bf16(p0, p1);
+        pw[kb][1] = cvt_pk_bf16(p2, p3);
+    }
+    const bf16x8 pbv = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+    const u16* vb = lv + (4 * g + (r16 >> 2)) * LDX + 4 * (r16 & 3);
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+        const uint2 lo = lds_read_tr16(vb + 16 * jb);
+        const uint2 hi = lds_read_tr16(vb + 16 * LDX + 16 * jb);
+        o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pbv, o[jb]);
+    }
+}
+
 // ---- wave helpers --------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
