@@ -45,23 +45,24 @@ struct LocalCfg {
 
 // Key/value tiles travel through registers: a tile's loads are issued two
 // tiles ahead of its use and stored to LDS one tile ahead, so global-load
-// latency overlaps two tiles of compute.
+// latency overlaps two tiles of compute.  The loads are range-checked buffer
+// loads (rows past the end read as zeros), issued unconditionally: the number
+// in flight is fixed, so a store waits only for its own tile.
 #define RT_LOAD_TILE(tk, tv, KT0)                                                           \
     do {                                                                                    \
         _Pragma("unroll") for (int it = 0; it < C::KPT; ++it) {                              \
             const int e = threadIdx.x + C::NT * it;                                         \
             const int r = e / C::CPR, ch = e % C::CPR;                                      \
-            const int j = (C::KITEMS % C::NT == 0 || e < C::KITEMS) ? (KT0) + r : n;        \
-            tk[it] = (j < n && 8 * ch < D)                                                  \
-                         ? *reinterpret_cast<const uint4*>(kk + (base + j) * D + 8 * ch)   \
-                         : zero_u4();                                                       \
+            const bool in = (C::KITEMS % C::NT == 0 || e < C::KITEMS) && 8 * ch < D;        \
+            tk[it] = buffer_load16(krs, in ? (uint32_t)(((KT0) + r) * D + 8 * ch) * 2u      \
+                                           : kOutOfRange);                                  \
         }                                                                                   \
         _Pragma("unroll") for (int it = 0; it < C::VPT; ++it) {                              \
             const int e = threadIdx.x + C::NT * it;                                         \
             const int r = e / C::DCH, ch = e % C::DCH;                                      \
-            const int j = (C::VITEMS % C::NT == 0 || e < C::VITEMS) ? (KT0) + r : n;        \
-            tv[it] = (j < n) ? *reinterpret_cast<const uint4*>(v + (base + j) * D + 8 * ch)\
-                             : zero_u4();                                                   \
+            const bool in = C::VITEMS % C::NT == 0 || e < C::VITEMS;                        \
+            tv[it] = buffer_load16(vrs, in ? (uint32_t)(((KT0) + r) * D + 8 * ch) * 2u      \
+                                           : kOutOfRange);                                  \
         }                                                                                   \
     } while (0)
 
@@ -159,20 +160,23 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
 
     const int kt_first = lo & ~(C::KT - 1);
     uint4 tka[C::KPT], tva[C::VPT], tkb[C::KPT], tvb[C::VPT];
+    // this head's keys and values as range-checked buffers
+    const buf_rsrc krs = make_rsrc(kk + base * D, (uint32_t)n * D * 2u);
+    const buf_rsrc vrs = make_rsrc(v + base * D, (uint32_t)n * D * 2u);
     RT_LOAD_TILE(tka, tva, kt_first);
-    if (kt_first + C::KT <= hi) RT_LOAD_TILE(tkb, tvb, kt_first + C::KT);
+    RT_LOAD_TILE(tkb, tvb, kt_first + C::KT);
     RT_STORE_TILE(lk[0], lv[0], tka, tva);
     __syncthreads();
 
     // Two tiles per trip so that the two register sets keep static names: on
     // entry the tile at kt is in LDS buffer 0 and the next one in set b.
     for (int kt = kt_first;; kt += 2 * C::KT) {
-        if (kt + 2 * C::KT <= hi) RT_LOAD_TILE(tka, tva, kt + 2 * C::KT);
+        RT_LOAD_TILE(tka, tva, kt + 2 * C::KT);
         RT_COMPUTE_TILE(kt, 0);
         if (kt + C::KT > hi) break;
         RT_STORE_TILE(lk[1], lv[1], tkb, tvb);
         __syncthreads();
-        if (kt + 3 * C::KT <= hi) RT_LOAD_TILE(tkb, tvb, kt + 3 * C::KT);
+        RT_LOAD_TILE(tkb, tvb, kt + 3 * C::KT);
         RT_COMPUTE_TILE(kt + C::KT, 1);
         if (kt + 2 * C::KT > hi) break;
         RT_STORE_TILE(lk[0], lv[0], tka, tva);

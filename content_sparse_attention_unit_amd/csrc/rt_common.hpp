@@ -95,6 +95,26 @@ __device__ __forceinline__ void acc_xt_w(const uint32_t (&pw)[4][2], f32x4 (&o)[
     }
 }
 
+// Raw buffer loads (gfx9 buffer resource: base, byte range, stride 0).  An
+// access past the range returns zeros without touching memory, so a load
+// needs no branch around it and every load is issued unconditionally.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ uint4 buffer_load16(buf_rsrc r, uint32_t byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+#else
+struct buf_rsrc {};
+__device__ __forceinline__ buf_rsrc make_rsrc(const void*, uint32_t) { return buf_rsrc{}; }
+__device__ __forceinline__ uint4 buffer_load16(buf_rsrc, uint32_t) { return make_uint4(0u, 0u, 0u, 0u); }
+#endif
+// a byte offset no range reaches (loads from it return zeros)
+constexpr uint32_t kOutOfRange = 0xfffffff0u;
+
 // Online-softmax step shared by the attention kernels.  `sv[kb][i]` holds the
 // logits, in log2 units, of keys kc + 16*kb + 4*g + i for this lane's query
 // (-inf where masked).  Updates the running max `m` and denominator `z`,
