@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
-           "routed_attn_bwd", "workspace_bytes", "library_path", "mask_words", "RTError", "RT_OP"]
+           "routed_attn_bwd", "in_proj", "out_proj", "workspace_bytes", "library_path",
+           "mask_words", "RTError", "RT_OP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "lib", "librouted_attn.so")
@@ -56,6 +57,8 @@ def _load():
         "rt_centroid_update_sums": [P, P, P, I, I, I, I, F, P],
         "rt_local_attn": [P, P, P, I, I, I, I, I, I, F, I, P, I, P],
         "rt_centroid_update": [P, P, P, P, P, I, P, I, I, I, I, I, I, F, P],
+        "rt_in_proj": [P, P, I, I, I, I, I, I, P, P, P, P, P, P],
+        "rt_out_proj": [P, P, P, P, I, I, I, I, I, I, P, P],
         "rt_routed_attn_bwd": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z,
                                P],
     }
@@ -264,3 +267,39 @@ def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=N
                                   sc, int(causal), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(dev)))
     return dq, dk, dv
+
+
+def in_proj(x: torch.Tensor, w_in: torch.Tensor, R: int, L: int, d: int, out=None):
+    """[qk | v | q_l | k_l | v_l] = x W_in^T for x [B,n,dm] and w_in
+    [(2R+3L)d, dm] (bfloat16); returns the five head-major [B,H,n,d] bfloat16
+    tensors (the local ones None when L = 0), or fills ``out``."""
+    lib = _load()
+    dev = _gpu(x, w_in)
+    if x.dtype != torch.bfloat16 or w_in.dtype != torch.bfloat16:
+        raise TypeError("in_proj takes bfloat16 tensors")
+    B, n, dm = x.shape
+    if out is None:
+        out = (torch.empty((B, R, n, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, R, n, d), dtype=torch.bfloat16, device=dev),
+               *((torch.empty((B, L, n, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+                 if L > 0 else (None, None, None)))
+    _gpu(*out)
+    _check(lib.rt_in_proj(_ptr(x), _ptr(w_in), B, n, dm, d, R, L, *(_ptr(t) for t in out),
+                          _stream(dev)))
+    return out
+
+
+def out_proj(o_r: torch.Tensor, o_l, w_o: torch.Tensor, x=None, out=None):
+    """y = x + [o_r | o_l] W_o^T (bfloat16) for o_r [B,R,n,d], o_l [B,L,n,d] or
+    None, w_o [dm, (R+L)d] and the residual x [B,n,dm] or None."""
+    lib = _load()
+    dev = _gpu(o_r, o_l, w_o, x)
+    B, R, n, d = o_r.shape
+    L = 0 if o_l is None else o_l.shape[1]
+    dm = w_o.shape[0]
+    if out is None:
+        out = torch.empty((B, n, dm), dtype=torch.bfloat16, device=dev)
+    _gpu(out)
+    _check(lib.rt_out_proj(_ptr(o_r), _ptr(o_l), _ptr(w_o), _ptr(x), B, n, dm, d, R, L, _ptr(out),
+                           _stream(dev)))
+    return out

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "routed_attn.h"
@@ -225,6 +226,85 @@ rt_status rt_centroid_update(float* mu, const void* q, const float* q_inv, const
     if ((long long)B * w > 0x7fffffffLL) return fail(RT_EUNSUPPORTED, "%s: B*w too large", fn);
     hipError_t e = rt::launch_ema(mu, q, q_inv, kk, k_inv, dtype, idx, B, H, n, d, k, w, lambda,
                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+namespace {
+
+rt_status check_proj(const char* fn, int B, int n, int dm, int d, int R, int L) {
+    if (B <= 0 || n <= 0 || dm <= 0 || d <= 0 || R <= 0 || L < 0)
+        return fail(RT_EINVAL, "%s: sizes must be positive (B=%d n=%d dm=%d d=%d R=%d L=%d)", fn,
+                    B, n, dm, d, R, L);
+    if (!dim_ok(d)) return fail(RT_EUNSUPPORTED, "%s: d=%d not in {16,32,64,128}", fn, d);
+    if (dm % 8 != 0) return fail(RT_EUNSUPPORTED, "%s: dm=%d is not a multiple of 8", fn, dm);
+    const long long wide = std::max<long long>(dm, (long long)(2 * R + 3 * L) * d);
+    if ((long long)B * n * wide >= (1LL << 31))
+        return fail(RT_EUNSUPPORTED, "%s: B*n*width too large", fn);
+    return RT_OK;
+}
+
+}  // namespace
+
+rt_status rt_in_proj(const void* x, const void* w_in, int B, int n, int dm, int d, int R, int L,
+                     void* qk, void* v, void* q_l, void* k_l, void* v_l, void* stream) {
+    static const char* fn = "rt_in_proj";
+    g_err[0] = 0;
+    if (!x || !w_in || !qk || !v) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (L > 0 && (!q_l || !k_l || !v_l))
+        return fail(RT_EINVAL, "%s: null local-head output with L=%d", fn, L);
+    rt_status st = check_proj(fn, B, n, dm, d, R, L);
+    if (st != RT_OK) return st;
+    const void* outs[5] = {qk, v, q_l, k_l, v_l};
+    for (int i = 0; i < (L > 0 ? 5 : 2); ++i) {
+        if (outs[i] == x || outs[i] == w_in) return fail(RT_EINVAL, "%s: an output aliases an input", fn);
+        for (int j = i + 1; j < (L > 0 ? 5 : 2); ++j)
+            if (outs[i] == outs[j]) return fail(RT_EINVAL, "%s: outputs alias each other", fn);
+    }
+    rt::ProjArgs p{};
+    p.a[0] = x;
+    p.w = w_in;
+    p.c[0] = qk;
+    p.c[1] = v;
+    p.c[2] = q_l;
+    p.c[3] = k_l;
+    p.c[4] = v_l;
+    p.hc[0] = R;
+    p.hc[1] = R;
+    p.hc[2] = p.hc[3] = p.hc[4] = L;
+    p.M = B * n;
+    p.N = (2 * R + 3 * L) * d;
+    p.K = dm;
+    p.n = n;
+    p.d = d;
+    hipError_t e = rt::launch_proj(p, 0, 1, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_out_proj(const void* o_r, const void* o_l, const void* w_o, const void* x, int B,
+                      int n, int dm, int d, int R, int L, void* y, void* stream) {
+    static const char* fn = "rt_out_proj";
+    g_err[0] = 0;
+    if (!o_r || !w_o || !y || (L > 0 && !o_l)) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_proj(fn, B, n, dm, d, R, L);
+    if (st != RT_OK) return st;
+    if (y == o_r || y == w_o || (L > 0 && y == o_l))
+        return fail(RT_EINVAL, "%s: y aliases a head output or the weights", fn);
+    rt::ProjArgs p{};
+    p.a[0] = o_r;
+    p.a[1] = o_l;
+    p.ha[0] = R;
+    p.ha[1] = L;
+    p.w = w_o;
+    p.c[0] = y;
+    p.res = x;
+    p.M = B * n;
+    p.N = dm;
+    p.K = (R + L) * d;
+    p.n = n;
+    p.d = d;
+    hipError_t e = rt::launch_proj(p, 1, 0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

@@ -70,6 +70,22 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
 
 size_t bwd_workspace_bytes(int BH, int n, int d, int k, int w);
 
+// C = A W^T (+ residual), bf16 in and out, float32 accumulation.  A is
+// row-major [M][K] (amode 0) or head-major segments a[s] [B][ha[s]][n][d]
+// (amode 1, k = head * d + i over the concatenated heads); W is [N][K]; C is
+// row-major [M][N] with an optional row-major residual (cmode 0) or head-major
+// segments c[s] [B][hc[s]][n][d] (cmode 1, unused segments have hc = 0).
+struct ProjArgs {
+    const void* a[2];
+    int ha[2];
+    const void* w;
+    void* c[5];
+    int hc[5];
+    const void* res;
+    int M, N, K, n, d;
+};
+hipError_t launch_proj(const ProjArgs& p, int amode, int cmode, hipStream_t s);
+
 // Largest cluster the backward kernels keep on chip.
 int max_cluster_rows_bwd(int dtype, int d, bool shared_qk);
 

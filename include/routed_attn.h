@@ -211,6 +211,41 @@ rt_status rt_routed_attn_bwd(const void *q, const void *kk, const void *v, int d
                              int w, float scale, int causal, float *dq_hat, float *dk_hat,
                              float *dv, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * rt_in_proj -- the heads' inputs of one layer from the layer input.
+ *   Summary §3: a self-attention layer maps n vectors of dimension d_model
+ *   to queries, keys and values with learned linear maps; here one product
+ *   gives the shared query/key and the values of the R routed heads and the
+ *   queries, keys and values of the L local heads:
+ *       [qk | v | q_l | k_l | v_l] = x W_in^T   (bf16, float32 accumulation,
+ *                                                one rounding per element).
+ *   x      [B][n][dm] bf16 (token-major layer input).
+ *   w_in   [(2R + 3L) d][dm] bf16: rows R*d of qk heads, R*d of v heads, then
+ *          L*d each of local q, k and v heads (head h, dim i = row h*d + i).
+ *   qk, v  out [B][R][n][d] bf16; q_l, k_l, v_l out [B][L][n][d] bf16 (NULL
+ *          when L = 0).  Outputs must not alias x or w_in.  No workspace.
+ *   Sizes: d in {16, 32, 64, 128}, dm a positive multiple of 8, R >= 1,
+ *   L >= 0, B*n*max(dm, (2R+3L)d) < 2^31.
+ */
+rt_status rt_in_proj(const void *x, const void *w_in, int B, int n, int dm, int d, int R, int L,
+                     void *qk, void *v, void *q_l, void *k_l, void *v_l, void *stream);
+
+/*
+ * rt_out_proj -- the layer output: y = x + [o_r | o_l] W_o^T.
+ *   The heads' outputs (routed heads, then local heads, concatenated per
+ *   token) mapped back to d_model and added to the residual stream
+ *   (summary §3, §5: a stack of such layers).
+ *   o_r    [B][R][n][d] bf16 (routed heads' outputs); o_l [B][L][n][d] bf16
+ *          (NULL when L = 0).
+ *   w_o    [dm][(R + L) d] bf16.
+ *   x      [B][n][dm] bf16 residual, or NULL for none.  y [B][n][dm] bf16
+ *          out; y may be x (each element's residual is read before it is
+ *          written), must not alias o_r, o_l or w_o.  Float32 accumulation
+ *          and residual add, one rounding per element.  No workspace.
+ */
+rt_status rt_out_proj(const void *o_r, const void *o_l, const void *w_o, const void *x, int B,
+                      int n, int dm, int d, int R, int L, void *y, void *stream);
+
 /* Workspace size in bytes for operation `op` at these sizes (0 if none,
  * (size_t)-1 if the sizes are invalid). */
 size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w);

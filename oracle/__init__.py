@@ -191,3 +191,66 @@ def forward(inputs: dict, cfg, scale: float | None = None, nthreads: int | None 
         res["local_out"] = local_attn(inputs["q_local"].value, inputs["k_local"].value,
                                       inputs["v_local"].value, cfg.window, sc, True, nthreads)
     return res
+
+
+# ---- the layer stack: projections and one layer --------------------------------------
+# The paperlayer.ai summary of the paper (§3) describes a self-attention layer as
+# three learned linear maps of the n input vectors; §5 reports a 22-layer stack at
+# n = 8192.  A stack layer here: [qk | v | q_l | k_l | v_l] = x W_in^T, routed and
+# local attention on those heads, y = x + [routed | local] W_o^T.  Activations are
+# stored in bfloat16 between the steps, so the oracle rounds at exactly those points
+# (the matrix products themselves are exact float64 library products).
+
+def round_bf16(x):
+    """Round float64 values to the nearest bfloat16 (8 significant bits), ties to
+    even, returned as float64.  Written from the format: x = m 2^e with
+    0.5 <= |m| < 1, keep m to 8 bits."""
+    f = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(f)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)   # np.round: half to even
+
+
+def in_proj(x, w_in, R: int, L: int, d: int):
+    """x [B,n,dm], w_in [(2R+3L)d, dm] -> (qk, v, q_l, k_l, v_l), each head-major
+    [B,H,n,d], rounded to bfloat16 (the local ones None when L = 0)."""
+    x, w_in = _f64(x), _f64(w_in)
+    B, n, dm = x.shape
+    y = round_bf16(x.reshape(B * n, dm) @ w_in.T)            # [B*n, (2R+3L)d]
+    heads = y.reshape(B, n, 2 * R + 3 * L, d).transpose(0, 2, 1, 3)
+    qk, v = heads[:, :R], heads[:, R:2 * R]
+    if L == 0:
+        return (np.ascontiguousarray(qk), np.ascontiguousarray(v), None, None, None)
+    ql, kl, vl = heads[:, 2 * R:2 * R + L], heads[:, 2 * R + L:2 * R + 2 * L], heads[:, 2 * R + 2 * L:]
+    return tuple(np.ascontiguousarray(t) for t in (qk, v, ql, kl, vl))
+
+
+def out_proj(o_r, o_l, w_o, x=None):
+    """y = x + [o_r | o_l] W_o^T, rounded to bfloat16.  o_r [B,R,n,d], o_l
+    [B,L,n,d] or None, w_o [dm, (R+L)d], x [B,n,dm] or None."""
+    o_r = _f64(o_r)
+    B, R, n, d = o_r.shape
+    parts = [o_r] if o_l is None else [o_r, _f64(o_l)]
+    cat = np.concatenate(parts, axis=1).transpose(0, 2, 1, 3).reshape(B * n, -1)   # [B*n, (R+L)d]
+    y = cat @ _f64(w_o).T
+    if x is not None:
+        y = y + _f64(x).reshape(B * n, -1)
+    return round_bf16(y).reshape(B, n, -1)
+
+
+def layer_forward(x, w_in, w_o, mu, R: int, L: int, d: int, w: int, window: int, lam: float,
+                  scale: float | None = None, nthreads: int | None = None):
+    """One stack layer (forward, causal, shared query/key in the routed heads).
+    Returns a dict with the intermediates: qk, v, q_l, k_l, v_l, idx, margin,
+    o_r (routed heads' output, bf16), o_l (local, bf16), mu (updated) and y."""
+    sc = (1.0 / np.sqrt(d)) if scale is None else scale
+    qk, v, ql, kl, vl = in_proj(x, w_in, R, L, d)
+    _, idx, margin, _ = route(qk, mu, w, nthreads)
+    o_r, _, _ = routed_attn(qk, qk, v, idx, sc, True, True, nthreads)
+    o_r = round_bf16(o_r)
+    mu_new = centroid_update(mu, qk, qk, idx, lam)
+    o_l = None
+    if L > 0:
+        o_l = round_bf16(local_attn(ql, kl, vl, window, sc, True, nthreads))
+    y = out_proj(o_r, o_l, w_o, x)
+    return {"qk": qk, "v": v, "q_l": ql, "k_l": kl, "v_l": vl, "idx": idx, "margin": margin,
+            "o_r": o_r, "o_l": o_l, "mu": mu_new, "y": y}

@@ -186,3 +186,51 @@ def make_inputs(cfg: Config) -> dict:
     if cfg.backward:
         out["dout"] = normal_tensor(s + TENSOR_IDS["dout"], shape_r, cfg.dtype)
     return out
+
+
+# ---- the layer stack of the long workload ---------------------------------------------
+# x ~ N(0, 1) [B, n, d_model]; per layer l: W_in [(2R+3L)d, d_model] and W_o
+# [d_model, (R+L)d] ~ N(0, 1/fan_in), centroids as in make_inputs.  Seeds:
+# 1000*cfg_id + 10 for x, 1000*cfg_id + 100 + 8l + j for layer l (j = 0 W_in,
+# 1 W_o, 2 centroids).
+
+@dataclasses.dataclass(frozen=True)
+class StackConfig:
+    cfg_id: int
+    name: str
+    B: int
+    n: int
+    dm: int             # model width
+    d: int              # head width
+    R: int              # routed heads per layer
+    L: int              # local heads per layer
+    k: int
+    w: int
+    window: int
+    layers: int
+    lam: float = 0.999
+
+    def scaled(self, **kw) -> "StackConfig":
+        return dataclasses.replace(self, **kw)
+
+
+def stack_x(sc: StackConfig) -> Tensor:
+    return normal_tensor(1000 * sc.cfg_id + 10, (sc.B, sc.n, sc.dm), "bf16")
+
+
+def stack_layer(sc: StackConfig, layer: int) -> dict:
+    s = 1000 * sc.cfg_id + 100 + 8 * layer
+    n_in = (2 * sc.R + 3 * sc.L) * sc.d
+    n_heads = (sc.R + sc.L) * sc.d
+    return {
+        "w_in": normal_tensor(s, (n_in, sc.dm), "bf16", sigma=1.0 / np.sqrt(sc.dm)),
+        "w_o": normal_tensor(s + 1, (sc.dm, n_heads), "bf16", sigma=1.0 / np.sqrt(n_heads)),
+        "mu": unit_rows_f32(s + 2, sc.R * sc.k, sc.d).reshape(sc.R, sc.k, sc.d),
+    }
+
+
+STACKS = {
+    # the long-sequence layer (8 routed + 4 local heads of width 128, k = 64,
+    # w = 128, window 512) at model width 1024, 22 layers
+    "long_stack": StackConfig(4, "long_stack", 1, 8192, 1024, 128, 8, 4, 64, 128, 512, 22),
+}

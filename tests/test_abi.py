@@ -216,3 +216,48 @@ def test_bwd_workspace_size(lib):
     ovf = B * H * k * w * d * 4
     dirs = ((B * H * n * (k - 4) * 4 + 255) // 256) * 256
     assert lib.rt_workspace_bytes(4, B, H, n, d, k, w) == mask + dirs + 3 * (slots + ovf)
+
+
+def in_proj(lib, x=FAKE, w=ctypes.c_void_p(0x9000), B=1, n=64, dm=64, d=16, R=2, L=1,
+            outs=(0xa000, 0xb000, 0xc000, 0xd000, 0xe000)):
+    o = [None if p is None else ctypes.c_void_p(p) for p in outs]
+    return lib.rt_in_proj(x, w, B, n, dm, d, R, L, *o, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(x=None), RT_EINVAL, "null"),
+    (dict(outs=(0xa000, 0xb000, None, 0xd000, 0xe000)), RT_EINVAL, "local-head output"),
+    (dict(outs=(0xa000, 0xa000, 0xc000, 0xd000, 0xe000)), RT_EINVAL, "alias each other"),
+    (dict(outs=(0x1000, 0xb000, 0xc000, 0xd000, 0xe000)), RT_EINVAL, "aliases an input"),
+    (dict(R=0), RT_EINVAL, "positive"),
+    (dict(L=-1), RT_EINVAL, "positive"),
+    (dict(d=24), RT_EUNSUPPORTED, "d=24"),
+    (dict(dm=60), RT_EUNSUPPORTED, "multiple of 8"),
+    (dict(B=4096, n=4096, dm=1024), RT_EUNSUPPORTED, "too large"),
+])
+def test_in_proj_validation(lib, kw, code, msg):
+    assert in_proj(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_in_proj_without_local_heads_needs_no_local_outputs(lib):
+    # L = 0: the local outputs may be NULL (fails later only on the fake sizes' check)
+    assert in_proj(lib, L=0, outs=(0xa000, 0xb000, None, None, None), d=24) == RT_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(o_r=None), RT_EINVAL, "null"),
+    (dict(o_l=None), RT_EINVAL, "null"),
+    (dict(y=0x3000), RT_EINVAL, "aliases"),
+    (dict(dm=12), RT_EUNSUPPORTED, "multiple of 8"),
+    (dict(d=8), RT_EUNSUPPORTED, "d=8"),
+])
+def test_out_proj_validation(lib, kw, code, msg):
+    a = dict(o_r=0x3000, o_l=0x4000, w_o=0x5000, x=0x6000, B=1, n=64, dm=64, d=16, R=2, L=1,
+             y=0x7000)
+    a.update(kw)
+    p = {k_: (None if a[k_] is None else ctypes.c_void_p(a[k_]))
+         for k_ in ("o_r", "o_l", "w_o", "x", "y")}
+    assert lib.rt_out_proj(p["o_r"], p["o_l"], p["w_o"], p["x"], a["B"], a["n"], a["dm"], a["d"],
+                           a["R"], a["L"], p["y"], None) == code
+    assert msg in _last(lib)

@@ -382,3 +382,80 @@ def test_p10_backward_finite_differences_routed(orc):
                 b[which][0, 0, t, i] -= h
                 num[0, 0, t, i] = (loss(*a) - loss(*b)) / (2 * h)
         np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+# ---- the layer stack (projections, rounding, one layer) --------------------------------
+
+def test_round_bf16_ties_and_values(orc):
+    """bfloat16 keeps 8 significant bits; halfway cases go to the even one."""
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -7, 1 + 2 ** -9, -(1 + 2 ** -8),
+                  3 * 2 ** -130, 255.0, 257.0, 0.0])
+    want = np.array([1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, 1.0, -1.0, 3 * 2 ** -130, 255.0, 256.0,
+                     0.0])
+    np.testing.assert_array_equal(orc.round_bf16(x), want)
+
+
+def test_round_bf16_matches_torch_on_float32_values(orc):
+    """On float32-representable inputs it equals torch's float32 -> bfloat16
+    conversion (round to nearest even), an independent implementation."""
+    rng = np.random.default_rng(3)
+    f = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    want = torch.from_numpy(f).to(torch.bfloat16).float().numpy().astype(np.float64)
+    np.testing.assert_array_equal(orc.round_bf16(f.astype(np.float64)), want)
+
+
+def test_in_proj_identity_splits_heads(orc):
+    """With W_in = I the projections are x's columns, split into head-major
+    tensors in the order qk, v, q_l, k_l, v_l (exact: x is bf16 already)."""
+    B, n, d, R, L = 2, 5, 4, 2, 1
+    dm = (2 * R + 3 * L) * d
+    x = orc.round_bf16(np.random.default_rng(4).standard_normal((B, n, dm)))
+    outs = orc.in_proj(x, np.eye(dm), R, L, d)
+    heads = [(0, R), (R, 2 * R), (2 * R, 2 * R + L), (2 * R + L, 2 * R + 2 * L),
+             (2 * R + 2 * L, 2 * R + 3 * L)]
+    for t, (h0, h1) in zip(outs, heads):
+        for b in range(B):
+            for h in range(h0, h1):
+                np.testing.assert_array_equal(t[b, h - h0], x[b, :, h * d:(h + 1) * d])
+    assert orc.in_proj(x[:, :, :2 * R * d], np.eye(2 * R * d), R, 0, d)[2] is None
+
+
+def test_in_proj_is_rounded_exact_product(orc):
+    rng = np.random.default_rng(5)
+    x = orc.round_bf16(rng.standard_normal((1, 7, 16)))
+    w = orc.round_bf16(rng.standard_normal((2 * 16, 16)))
+    qk, v, _, _, _ = orc.in_proj(x, w, 1, 0, 16)
+    exact = np.einsum("tk,nk->tn", x[0], w)   # independent of the oracle's product
+    np.testing.assert_array_equal(qk[0, 0], orc.round_bf16(exact[:, :16]))
+    np.testing.assert_array_equal(v[0, 0], orc.round_bf16(exact[:, 16:]))
+
+
+def test_out_proj_zero_weights_and_concat_order(orc):
+    rng = np.random.default_rng(6)
+    B, n, d, R, L = 2, 3, 4, 2, 1
+    o_r = orc.round_bf16(rng.standard_normal((B, R, n, d)))
+    o_l = orc.round_bf16(rng.standard_normal((B, L, n, d)))
+    dm = (R + L) * d
+    x = orc.round_bf16(rng.standard_normal((B, n, dm)))
+    np.testing.assert_array_equal(orc.out_proj(o_r, o_l, np.zeros((dm, dm)), x), x)
+    y = orc.out_proj(o_r, o_l, np.eye(dm))                  # identity: the concatenation
+    for b in range(B):
+        for h in range(R + L):
+            src = o_r[b, h] if h < R else o_l[b, h - R]
+            np.testing.assert_array_equal(y[b, :, h * d:(h + 1) * d], src)
+
+
+def test_layer_forward_composition_and_zero_output_map(orc):
+    """One layer with W_o = 0 leaves x unchanged, and its centroid update is
+    that of its own routed projections."""
+    rng = np.random.default_rng(8)
+    B, n, dm, d, R, L, k, w = 1, 40, 16, 16, 1, 1, 3, 10
+    x = orc.round_bf16(rng.standard_normal((B, n, dm)))
+    w_in = orc.round_bf16(rng.standard_normal(((2 * R + 3 * L) * d, dm)) / 4)
+    mu = rng.standard_normal((R, k, d))
+    res = orc.layer_forward(x, w_in, np.zeros((dm, (R + L) * d)), mu, R, L, d, w, 8, 0.9)
+    np.testing.assert_array_equal(res["y"], x)
+    qk = orc.in_proj(x, w_in, R, L, d)[0]
+    np.testing.assert_allclose(res["mu"], orc.centroid_update(mu, qk, qk, res["idx"], 0.9),
+                               rtol=0, atol=1e-12)
+    assert res["o_r"].shape == (B, R, n, d) and res["o_l"].shape == (B, L, n, d)
