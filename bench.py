@@ -132,6 +132,92 @@ def cpu_baseline(cfg, inp, scale, min_seconds=5.0):
                       f"attention), fp64, {threads} threads"}
 
 
+def time_stack(rt, sc, reps=5):
+    """The stack of sc.layers layers (x -> in_proj -> route -> routed attention
+    (+member sums) -> centroid update -> local attention -> out_proj, residual in
+    place), captured as one HIP graph; returns timings and rates."""
+    B, n, dm, d, R, L, k, w = sc.B, sc.n, sc.dm, sc.d, sc.R, sc.L, sc.k, sc.w
+    scale = 1.0 / math.sqrt(d)
+    x0 = dev(S.stack_x(sc))
+    layers = []
+    for l in range(sc.layers):
+        lw = S.stack_layer(sc, l)
+        layers.append((dev(lw["w_in"]), dev(lw["w_o"]),
+                       torch.from_numpy(lw["mu"].astype(np.float32)).cuda()))
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    qk, v = torch.empty((B, R, n, d), **bf), torch.empty((B, R, n, d), **bf)
+    ql, kl, vl = (torch.empty((B, L, n, d), **bf) for _ in range(3))
+    o_r, o_l = torch.empty((B, R, n, d), **bf), torch.empty((B, L, n, d), **bf)
+    inv = torch.empty((B, R, n), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, R, k, w), dtype=torch.int32, device="cuda")
+    mask = torch.empty((B, R, n, rt.mask_words(k)), dtype=torch.int32, device="cuda")
+    sum_q = torch.empty((B, R, k, d), dtype=torch.float32, device="cuda")
+    ws_r = torch.empty(rt.workspace_bytes("route", B, R, n, d, k, w), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(rt.workspace_bytes("routed_attn", B, R, n, d, k, w), dtype=torch.uint8,
+                       device="cuda")
+    xs = (torch.empty_like(x0), torch.empty_like(x0))   # layer outputs, alternating
+
+    def forward():
+        x = x0                                            # every forward starts from x0
+        for l, (w_in, w_o, mu) in enumerate(layers):
+            rt.in_proj(x, w_in, R, L, d, out=(qk, v, ql, kl, vl))
+            rt.route(qk, mu, w, out=(inv, idx, mask), ws=ws_r)
+            rt.routed_attn(qk, qk, v, idx, inv, inv, scale=scale, mask=mask, sums=(sum_q, None),
+                           out=o_r, ws=ws_a)
+            rt.centroid_update_sums_(mu, sum_q, sc.lam)
+            rt.local_attn(ql, kl, vl, sc.window, scale=scale, out=o_l)
+            rt.out_proj(o_r, o_l, w_o, x=x, out=xs[l % 2])
+            x = xs[l % 2]
+        return x
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        x = forward()
+        torch.cuda.synchronize()
+        finite = bool(torch.isfinite(x.float()).all())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            forward()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+    # the two projections alone (per call, back to back)
+    w_in, w_o, _ = layers[0]
+    per = {}
+    flops_in = 2.0 * B * n * dm * (2 * R + 3 * L) * d
+    flops_out = 2.0 * B * n * (R + L) * d * dm
+    y = torch.empty((B, n, dm), **bf)
+    with torch.cuda.stream(stream):
+        for name, fn in (("rt_in_proj", lambda: rt.in_proj(x, w_in, R, L, d, out=(qk, v, ql, kl, vl))),
+                         ("rt_out_proj", lambda: rt.out_proj(o_r, o_l, w_o, x=x, out=y))):
+            for _ in range(3):
+                fn()
+            a.record(stream)
+            for _ in range(20):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per[name] = a.elapsed_time(b) / 20
+    return {"layers": sc.layers, "d_model": dm, "ms_per_forward": ms,
+            "tokens_per_s": B * n / (ms * 1e-3), "us_per_layer": ms * 1e3 / sc.layers,
+            "finite": finite,
+            "proj_ms": per,
+            "proj_tflops": {"rt_in_proj": flops_in / (per["rt_in_proj"] * 1e-3) / 1e12,
+                            "rt_out_proj": flops_out / (per["rt_out_proj"] * 1e-3) / 1e12},
+            "proj_mfma_frac": {"rt_in_proj": flops_in / (per["rt_in_proj"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                               "rt_out_proj": flops_out / (per["rt_out_proj"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+            "workload": f"{sc.layers}-layer stack, d_model={dm}, {R} routed + {L} local heads of "
+                        f"{d}, n={n}, B={B}, random-init weights N(0, 1/fan_in)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +225,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip timing the 22-layer stack of "
+                    "the long workload (reported apart from the per-layer metric)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying "
                     "a captured HIP graph of the step")
     ap.add_argument("--concurrent-local", action="store_true", help="run the local heads "
@@ -347,6 +435,8 @@ def main():
                                    if "rt_local_attn" in per_call else None),
         "wall_s_timed": t_wall,
     }
+    if args.workload == "long" and not args.no_stack:
+        res["stack"] = time_stack(rt, S.STACKS["long_stack"])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, scale)
     print(json.dumps(res), flush=True)
