@@ -115,6 +115,25 @@ __device__ __forceinline__ uint4 buffer_load16(buf_rsrc, uint32_t) { return make
 // a byte offset no range reaches (loads from it return zeros)
 constexpr uint32_t kOutOfRange = 0xfffffff0u;
 
+// Lazy rescaling of an online softmax: the reference m (log2 units) moves, and
+// the denominator z and accumulators o are rescaled, only when some lane's new
+// chunk maximum exceeds its m by more than kLazyRescale; otherwise the chunk's
+// probabilities are taken against the old m and stay below 2^kLazyRescale
+// (harmless in float32 and bf16).  o / z, and m + log2 z, are the same either
+// way, and most chunks skip the NJ*4 multiplies.
+constexpr float kLazyRescale = 8.0f;
+template <int NJ>
+__device__ __forceinline__ void lazy_rescale(float cmax, float& m, float& z, f32x4 (&o)[NJ]) {
+    if (__ballot(cmax > m + kLazyRescale) != 0ull) {   // wave-uniform branch
+        const float mnew = fmaxf(m, cmax);
+        const float alpha = __builtin_amdgcn_exp2f(m - ((mnew == -INFINITY) ? 0.f : mnew));
+        z *= alpha;
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) o[jb] *= alpha;
+        m = mnew;
+    }
+}
+
 // Online-softmax step shared by the attention kernels.  `sv[kb][i]` holds the
 // logits, in log2 units, of keys kc + 16*kb + 4*g + i for this lane's query
 // (-inf where masked).  Updates the running max `m` and denominator `z`,
@@ -132,15 +151,8 @@ __device__ __forceinline__ void softmax_pv_chunk(f32x4 (&sv)[4], float& m, float
                              fmaxf(fmaxf(sv[3][0], sv[3][1]), fmaxf(sv[3][2], sv[3][3]))));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float mnew = fmaxf(m, cmax);
-    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-    if (__ballot(mnew != m) != 0ull) {  // some lane's max moved: rescale (wave-uniform branch)
-        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-        z *= alpha;
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) o[jb] *= alpha;
-        m = mnew;
-    }
+    lazy_rescale<NJ>(cmax, m, z, o);
+    const float msafe = (m == -INFINITY) ? 0.f : m;
     uint32_t pw[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -192,15 +204,8 @@ __device__ __forceinline__ void softmax_pv_half(f32x4 (&sv)[2], float& m, float&
                        fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float mnew = fmaxf(m, cmax);
-    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-    if (__ballot(mnew != m) != 0ull) {
-        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-        z *= alpha;
-#pragma unroll
-        for (int jb = 0; jb < NJ; ++jb) o[jb] *= alpha;
-        m = mnew;
-    }
+    lazy_rescale<NJ>(cmax, m, z, o);
+    const float msafe = (m == -INFINITY) ? 0.f : m;
     uint32_t pw[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
