@@ -203,7 +203,7 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
         }
     }
 
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int lane = lane_id(), wv = wave_id();
     const int g = lane >> 4, r16 = lane & 15;
     const int nqb = (w + 15) / 16;
     const float sl2 = scale * 1.4426950408889634f;  // logits in log2 units
@@ -227,7 +227,8 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
         f32x4 o[C::NJ];
 #pragma unroll
         for (int jb = 0; jb < C::NJ; ++jb) o[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m = -INFINITY, z = 0.f;
+        float m = -INFINITY;
+        f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
         const int kend = !active ? 0 : (causal ? min(w, qb * 16 + 16) : w);
         // keys below `clean` are visible to every query of the block
         const int clean = causal ? qb * 16 : w;
@@ -278,11 +279,11 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
                     }
             }
             const int halves = 1 | ((kc + 32 < kend) ? 2 : 0);
-            softmax_pv_chunk<C::NJ, C::LDX>(sv, m, z, o, &lv[kc * C::LDX], r16, g, halves);
+            softmax_pv_chunk<C::NJ, C::LDX>(sv, m, zacc, o, &lv[kc * C::LDX], r16, g, halves);
         }
         if (!active) continue;
 
-        const float zt = xor_sum_16_32(z);
+        const float zt = zacc[0];   // the query's denominator (every element holds it)
         const float rz = 1.0f / zt;
         if (qrow < w) {
             if (g == 0 && lse != nullptr)

@@ -161,7 +161,7 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
 
     const u16* lqs = SHARED ? lk : lq;
     const float* linvqs = SHARED ? linvk : linvq;
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int lane = lane_id(), wv = wave_id();
     const int g = lane >> 4, r16 = lane & 15;
     const int nb = (w + 15) / 16;
     const float sl2 = scale * 1.4426950408889634f;

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
     const int bh = item / gridDim.x;
     const int q0 = (item % gridDim.x) * C::QT;
     const long base = (long)bh * n;
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int lane = lane_id(), wv = wave_id();
     const int g = lane >> 4, r16 = lane & 15;
     const float sl2 = scale * 1.4426950408889634f;
     const int hf = wv / C::NQB;                  // key half of every tile: [32 hf, 32 hf + 32)
@@ -122,7 +122,8 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
     f32x4 o[C::NJ];
 #pragma unroll
     for (int jb = 0; jb < C::NJ; ++jb) o[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, z = 0.f;
+    float m = -INFINITY;
+    f32x4 zacc = {0.f, 0.f, 0.f, 0.f};   // the denominator (every element holds it)
 
     // This wave's half of tile [KT0, KT0 + 64) from LDS buffer BUF.
 #define RT_COMPUTE_TILE(KT0, BUF)                                                            \
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
                         sv[kb][i] = ok ? sv[kb][i] : -INFINITY;                              \
                     }                                                                        \
             }                                                                                \
-            softmax_pv_half<C::NJ, C::LDX>(sv, m, z, o, lv[BUF] + 32 * hf * C::LDX, r16, g); \
+            softmax_pv_half<C::NJ, C::LDX>(sv, m, zacc, o, lv[BUF] + 32 * hf * C::LDX, r16, g); \
         }                                                                                    \
     } while (0)
 
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
     float* mine = lmerge + ((wv % C::NQB) * 64 + lane) * MS;
     if (hf == 1) {
         mine[0] = m;
-        mine[1] = z;
+        mine[1] = zacc[0];
 #pragma unroll
         for (int jb = 0; jb < C::NJ; ++jb)
             *reinterpret_cast<float4*>(mine + 2 + 4 * jb) =
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
         const float mt = fmaxf(m, m2);
         const float ms = (mt == -INFINITY) ? 0.f : mt;
         const float a1 = __builtin_amdgcn_exp2f(m - ms), a2 = __builtin_amdgcn_exp2f(m2 - ms);
-        const float zt = xor_sum_16_32(z * a1 + z2 * a2);
+        const float zt = zacc[0] * a1 + z2 * a2;
         const float rz = 1.0f / zt;
         if (qi < n) {
             OutT* dst = out + (base + qi) * D + 4 * g;

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(PNT, 2) void proj_kernel(ProjArgs p) {
     __shared__ __attribute__((aligned(16))) u16 lw[2][PBN * PLD];
 
     const int m0 = blockIdx.x * PBM, n0 = blockIdx.y * PBN;
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int lane = lane_id(), wv = wave_id();
     const int g = lane >> 4, r16 = lane & 15;
     const int wm = wv >> 1, wn = wv & 1;
     const u16* w = static_cast<const u16*>(p.w);

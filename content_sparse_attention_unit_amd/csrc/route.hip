@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     const int item = xcd_contiguous(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
     const int bh = item / gridDim.x, tile = item % gridDim.x;
     const int h = bh % H;
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int lane = lane_id(), wv = wave_id();
     const int g = lane >> 4, r16 = lane & 15;
     const long base = (long)bh * n;
 
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
 
     const long row = blockIdx.x;
     const float* srow = scores + row * n;
-    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const int lane = lane_id(), wv = wave_id();
     const int seg0 = wv * kWave * KPT;
     // Wave wv owns positions [seg0, seg0 + 64*KPT); its key j sits at
     // seg0 + 64*VEC*(j / VEC) + VEC*lane + j % VEC: VEC consecutive positions

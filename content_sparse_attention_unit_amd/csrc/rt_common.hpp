@@ -115,56 +115,72 @@ __device__ __forceinline__ uint4 buffer_load16(buf_rsrc, uint32_t) { return make
 // a byte offset no range reaches (loads from it return zeros)
 constexpr uint32_t kOutOfRange = 0xfffffff0u;
 
-// Lazy rescaling of an online softmax: the reference m (log2 units) moves, and
-// the denominator z and accumulators o are rescaled, only when some lane's new
-// chunk maximum exceeds its m by more than kLazyRescale; otherwise the chunk's
-// probabilities are taken against the old m and stay below 2^kLazyRescale
-// (harmless in float32 and bf16).  o / z, and m + log2 z, are the same either
-// way, and most chunks skip the NJ*4 multiplies.
+// Online softmax with lazy rescaling.  The reference m (log2 units, shared by
+// the four lanes of a query) moves, and the accumulators are rescaled, only
+// when some lane's chunk maximum `lmax` exceeds m by more than kLazyRescale;
+// otherwise the chunk's probabilities are taken against the old m and stay
+// below 2^kLazyRescale (harmless in float32 and bf16).  o / z and m + log2 z
+// come out the same either way; the common case needs neither the cross-lane
+// maximum nor the NJ*4 multiplies.  The denominator is accumulated by the
+// matrix cores too (`zacc` = ones^T P^T, every element the query's sum of the
+// bf16 probabilities that weight the values), which also keeps it consistent
+// with those weights.
 constexpr float kLazyRescale = 8.0f;
 template <int NJ>
-__device__ __forceinline__ void lazy_rescale(float cmax, float& m, float& z, f32x4 (&o)[NJ]) {
-    if (__ballot(cmax > m + kLazyRescale) != 0ull) {   // wave-uniform branch
+__device__ __forceinline__ void lazy_rescale(float lmax, float& m, f32x4& zacc, f32x4 (&o)[NJ]) {
+    if (__ballot(lmax > m + kLazyRescale) != 0ull) {   // wave-uniform branch
+        float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
         const float mnew = fmaxf(m, cmax);
         const float alpha = __builtin_amdgcn_exp2f(m - ((mnew == -INFINITY) ? 0.f : mnew));
-        z *= alpha;
+        zacc *= alpha;
 #pragma unroll
         for (int jb = 0; jb < NJ; ++jb) o[jb] *= alpha;
         m = mnew;
     }
 }
 
+// bf16 ones, the A operand that turns P^T into its column sums.
+__device__ __forceinline__ bf16x8 bf16_ones() {
+    return as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+}
+
+__device__ __forceinline__ float max16(const f32x4 (&sv)[4]) {
+    return fmaxf(fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3]))),
+                 fmaxf(fmaxf(fmaxf(sv[2][0], sv[2][1]), fmaxf(sv[2][2], sv[2][3])),
+                       fmaxf(fmaxf(sv[3][0], sv[3][1]), fmaxf(sv[3][2], sv[3][3]))));
+}
+
 // Online-softmax step shared by the attention kernels.  `sv[kb][i]` holds the
 // logits, in log2 units, of keys kc + 16*kb + 4*g + i for this lane's query
-// (-inf where masked).  Updates the running max `m` and denominator `z`,
-// rescales the NJ accumulators O^T (16 x 16 tiles, rows = value dims), and
-// accumulates O^T += V^T P^T for the 64 keys of the chunk; `lv` points at the
-// chunk's first key row of the row-major value tile (row stride LDX), and
-// `halves` says which 32-key halves hold any visible key (wave-uniform).
+// (-inf where masked).  Updates the reference `m` and the denominator `zacc`,
+// and accumulates O^T += V^T P^T (NJ 16 x 16 tiles, rows = value dims) for the
+// 64 keys of the chunk; `lv` points at the chunk's first key row of the
+// row-major value tile (row stride LDX), and `halves` says which 32-key halves
+// hold any visible key (wave-uniform).
 template <int NJ, int LDX>
-__device__ __forceinline__ void softmax_pv_chunk(f32x4 (&sv)[4], float& m, float& z,
+__device__ __forceinline__ void softmax_pv_chunk(f32x4 (&sv)[4], float& m, f32x4& zacc,
                                                  f32x4 (&o)[NJ], const u16* lv, int r16, int g,
                                                  int halves) {
-    float cmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
-    cmax = fmaxf(cmax, fmaxf(fmaxf(fmaxf(sv[2][0], sv[2][1]), fmaxf(sv[2][2], sv[2][3])),
-                             fmaxf(fmaxf(sv[3][0], sv[3][1]), fmaxf(sv[3][2], sv[3][3]))));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    lazy_rescale<NJ>(cmax, m, z, o);
+    lazy_rescale<NJ>(max16(sv), m, zacc, o);
     const float msafe = (m == -INFINITY) ? 0.f : m;
     uint32_t pw[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const float p0 = __builtin_amdgcn_exp2f(sv[kb][0] - msafe);
-        const float p1 = __builtin_amdgcn_exp2f(sv[kb][1] - msafe);
-        const float p2 = __builtin_amdgcn_exp2f(sv[kb][2] - msafe);
-        const float p3 = __builtin_amdgcn_exp2f(sv[kb][3] - msafe);
-        z += (p0 + p1) + (p2 + p3);
-        pw[kb][0] = cvt_pk_bf16(p0, p1);
-        pw[kb][1] = cvt_pk_bf16(p2, p3);
+        pw[kb][0] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[kb][0] - msafe),
+                                __builtin_amdgcn_exp2f(sv[kb][1] - msafe));
+        pw[kb][1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[kb][2] - msafe),
+                                __builtin_amdgcn_exp2f(sv[kb][3] - msafe));
     }
     acc_xt_w<NJ, LDX>(pw, o, lv, r16, g, halves);
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+        if (!(halves & (1 << mm))) continue;
+        zacc = mfma16(bf16_ones(), as_bf16x8(make_uint4(pw[2 * mm][0], pw[2 * mm][1],
+                                                        pw[2 * mm + 1][0], pw[2 * mm + 1][1])),
+                      zacc);
+    }
 }
 
 // Four float32 values to 4 consecutive output elements (bf16: one 8-byte store).
@@ -198,24 +214,19 @@ __device__ __forceinline__ int row_dest(const uint32_t* __restrict__ m, int KW, 
 // units, -inf where masked) of keys 16*kb + 4*g + i of the half tile whose
 // first value row `lv` points at (row stride LDX).
 template <int NJ, int LDX>
-__device__ __forceinline__ void softmax_pv_half(f32x4 (&sv)[2], float& m, float& z,
+__device__ __forceinline__ void softmax_pv_half(f32x4 (&sv)[2], float& m, f32x4& zacc,
                                                 f32x4 (&o)[NJ], const u16* lv, int r16, int g) {
-    float cmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    lazy_rescale<NJ>(cmax, m, z, o);
+    const float lmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                             fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    lazy_rescale<NJ>(lmax, m, zacc, o);
     const float msafe = (m == -INFINITY) ? 0.f : m;
     uint32_t pw[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const float p0 = __builtin_amdgcn_exp2f(sv[kb][0] - msafe);
-        const float p1 = __builtin_amdgcn_exp2f(sv[kb][1] - msafe);
-        const float p2 = __builtin_amdgcn_exp2f(sv[kb][2] - msafe);
-        const float p3 = __builtin_amdgcn_exp2f(sv[kb][3] - msafe);
-        z += (p0 + p1) + (p2 + p3);
-        pw[kb][0] = cvt_pk_bf16(p0, p1);
-        pw[kb][1] = cvt_pk_bf16(p2, p3);
+        pw[kb][0] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[kb][0] - msafe),
+                                __builtin_amdgcn_exp2f(sv[kb][1] - msafe));
+        pw[kb][1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[kb][2] - msafe),
+                                __builtin_amdgcn_exp2f(sv[kb][3] - msafe));
     }
     const bf16x8 pbv = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
     const u16* vb = lv + (4 * g + (r16 >> 2)) * LDX + 4 * (r16 & 3);
@@ -225,10 +236,17 @@ __device__ __forceinline__ void softmax_pv_half(f32x4 (&sv)[2], float& m, float&
         const uint2 hi = lds_read_tr16(vb + 16 * LDX + 16 * jb);
         o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pbv, o[jb]);
     }
+    zacc = mfma16(bf16_ones(), pbv, zacc);
 }
 
 // ---- wave helpers --------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// This thread's wave within the workgroup, as a wave-uniform (scalar) value, so
+// that everything derived from it stays in scalar registers.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 
 // Number of set bits of `mask` in lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
