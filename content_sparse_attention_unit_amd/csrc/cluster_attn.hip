@@ -70,7 +70,7 @@ struct AttnCfg {
     static constexpr int NJ = D / 16;           // 16-wide output column blocks
     static constexpr int QROWS = SHARED ? 1 : WMAX;
     // waves per workgroup: one or two 16-row query blocks each
-    static constexpr int NW = WMAX <= 32 ? 2 : (WMAX <= 64 ? 4 : 8);
+    static constexpr int NW = WMAX <= 32 ? 2 : (WMAX <= 128 ? 4 : 8);
     static constexpr int NT = 64 * NW;
     static constexpr int CPR = DP / 8;          // 16-byte chunks per padded key row
     static constexpr int XPT = (WMAX * CPR + NT - 1) / NT;         // key chunks per thread
