@@ -58,30 +58,46 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     const long base = (long)bh * n;
 
     // Centroids of the first chunk: request them before the token rows so the
-    // two latencies overlap (MPT fp32 values per thread).
-    constexpr int MPT = (C::KC * C::DP) / 256;
-    float mreg[MPT];
+    // two latencies overlap.  Each thread takes MG groups of 8 consecutive
+    // dims (two 16-byte loads) and stores each of the three bf16 terms of a
+    // group with one 16-byte LDS write.
+    constexpr int GPR = C::DP / 8;                   // 8-dim groups per centroid row
+    constexpr int MG = (C::KC * GPR) / 256;          // groups per thread
+    float4 mreg[MG][2];
     auto load_mu = [&](int c0) {
 #pragma unroll
-        for (int j = 0; j < MPT; ++j) {
+        for (int j = 0; j < MG; ++j) {
             const int e = threadIdx.x + 256 * j;
-            const int c = e / C::DP, dim = e % C::DP;
-            mreg[j] = (c0 + c < k && dim < D) ? mu[((long)h * k + c0 + c) * D + dim] : 0.f;
+            const int c = e / GPR, dim0 = 8 * (e % GPR);
+            const bool ok = c0 + c < k && dim0 < D;
+            const float* src = mu + ((long)h * k + c0 + c) * D + dim0;
+            mreg[j][0] = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+            mreg[j][1] = ok ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto stage_mu = [&]() {
 #pragma unroll
-        for (int j = 0; j < MPT; ++j) {
+        for (int j = 0; j < MG; ++j) {
             const int e = threadIdx.x + 256 * j;
-            const int c = e / C::DP, dim = e % C::DP;
-            const float m = mreg[j];
-            const u16 hi = f2bf(m);
-            const float r1 = m - bf2f(hi);
-            const u16 mid = f2bf(r1);
-            const float r2 = r1 - bf2f(mid);
-            lmu[0][c][dim] = hi;
-            lmu[1][c][dim] = mid;
-            lmu[2][c][dim] = f2bf(r2);
+            const int c = e / GPR, dim0 = 8 * (e % GPR);
+            const float m8[8] = {mreg[j][0].x, mreg[j][0].y, mreg[j][0].z, mreg[j][0].w,
+                                 mreg[j][1].x, mreg[j][1].y, mreg[j][1].z, mreg[j][1].w};
+            uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // mu = hi + mid + lo exactly: each term is the bf16 rounding of
+                // what the previous ones leave
+                const float a = m8[2 * q], b = m8[2 * q + 1];
+                hw[q] = cvt_pk_bf16(a, b);
+                const float ra = a - __uint_as_float(hw[q] << 16);
+                const float rb = b - __uint_as_float(hw[q] & 0xffff0000u);
+                mw[q] = cvt_pk_bf16(ra, rb);
+                lw[q] = cvt_pk_bf16(ra - __uint_as_float(mw[q] << 16),
+                                    rb - __uint_as_float(mw[q] & 0xffff0000u));
+            }
+            *reinterpret_cast<uint4*>(&lmu[0][c][dim0]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            *reinterpret_cast<uint4*>(&lmu[1][c][dim0]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+            *reinterpret_cast<uint4*>(&lmu[2][c][dim0]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
     };
     load_mu(0);
