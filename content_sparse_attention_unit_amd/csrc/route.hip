@@ -305,15 +305,21 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t rem
     rem = (uint32_t)__shfl((int)fr, src);
 }
 
-template <int NT, int KPT>
+// LDSK: the row's keys live in LDS instead of registers (long rows: 64K keys
+// need 128 KiB, which LDS holds and registers do not).
+template <int NT, int KPT, bool LDSK>
 __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scores, int n, int w,
                                                   int32_t* __restrict__ idx, int k,
                                                   uint32_t* __restrict__ mask, int KW) {
     constexpr int NWV = NT / kWave;
     constexpr int CAND = 4096;           // capacity of the candidate list
-    __shared__ uint32_t sub[NWV][256];   // per-wave histograms of the top byte
+    // the candidate list, or before it (only when the first digit needs a full
+    // histogram) the per-wave histograms of the top byte
+    constexpr int CSZ = CAND > NWV * 256 ? CAND : NWV * 256;
+    __shared__ __attribute__((aligned(16))) uint32_t cand[CSZ];
+    uint32_t (*sub)[256] = reinterpret_cast<uint32_t (*)[256]>(cand);
+    __shared__ __attribute__((aligned(16))) uint32_t lkeys[LDSK ? NT * KPT : 4];
     __shared__ uint32_t hist[256];
-    __shared__ uint32_t cand[CAND];      // keys sharing the selected top byte
     __shared__ uint32_t sel_bin, sel_rem;
     __shared__ uint32_t wgt[NWV], weq[NWV];
     __shared__ __attribute__((aligned(16))) uint32_t wtop[NWV][8];   // per wave: highest top
@@ -330,25 +336,39 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     constexpr int VEC = (KPT % 4 == 0) ? 4 : 1;
     auto key_pos = [&](int j) { return seg0 + kWave * VEC * (j / VEC) + VEC * lane + j % VEC; };
 
-    uint32_t key[KPT];
+    uint32_t key[LDSK ? 1 : KPT];
+    // key j of this thread (in a register, or read back from LDS)
+#define RT_KEY(j) (LDSK ? lkeys[key_pos(j)] : key[LDSK ? 0 : (j)])
+    // loops over the keys: fully unrolled for registers, partly for LDS
+    constexpr int UNR = LDSK ? 4 : KPT;
+    constexpr int UNRG = LDSK ? 1 : KPT / VEC;
     uint32_t wtopb = 0u;   // highest top byte (sign and high exponent bits) in this lane
     const bool vec_ok = VEC == 4 && (n & 3) == 0;   // rows start 16-byte aligned
 #pragma unroll
     for (int jg = 0; jg < KPT / VEC; ++jg) {
         const int p0 = key_pos(VEC * jg);
+        uint32_t kv[VEC];
         if (vec_ok && p0 + VEC <= n) {
             const float4 f = *reinterpret_cast<const float4*>(srow + p0);
             const float fv[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) key[VEC * jg + e] = order_key(fv[e]);
+            for (int e = 0; e < VEC; ++e) kv[e] = order_key(fv[e]);
         } else {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) key[VEC * jg + e] = (p0 + e < n) ? order_key(srow[p0 + e]) : 0u;
+            for (int e = 0; e < VEC; ++e) kv[e] = (p0 + e < n) ? order_key(srow[p0 + e]) : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if (p0 + e < n) wtopb = max(wtopb, kv[e] >> 24);
+            if constexpr (!LDSK) key[VEC * jg + e] = kv[e];
+        }
+        if constexpr (LDSK) {
+            if constexpr (VEC == 4)
+                *reinterpret_cast<uint4*>(&lkeys[p0]) = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+            else
+                lkeys[p0] = kv[0];
         }
     }
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-        if (key_pos(j) < n) wtopb = max(wtopb, key[j] >> 24);
     // The w-th largest key nearly always has one of the row's four highest top
     // bytes.  Each wave counts its keys in its own four highest top bytes with
     // per-lane counters (a row's scores share top bytes in large groups, which
@@ -357,10 +377,10 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) wtopb = max(wtopb, (uint32_t)__shfl_xor((int)wtopb, off));
     uint32_t c01 = 0u, c23 = 0u;
-#pragma unroll
+#pragma unroll UNR
     for (int j = 0; j < KPT; ++j) {
         const int pos = key_pos(j);
-        const uint32_t dlt = wtopb - (key[j] >> 24);   // >= 0 for every valid key
+        const uint32_t dlt = wtopb - (RT_KEY(j) >> 24);   // >= 0 for every valid key
         if (pos < n && dlt < 4u) {
             if (dlt < 2u) c01 += 1u << (16 * dlt);
             else c23 += 1u << (16 * (dlt - 2u));
@@ -417,10 +437,10 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     if (!found) {   // the threshold lies lower: full histogram of the top byte
         for (int e = threadIdx.x; e < NWV * 256; e += NT) (&sub[0][0])[e] = 0u;
         __syncthreads();
-#pragma unroll
+#pragma unroll UNR
         for (int j = 0; j < KPT; ++j) {
             const int pos = key_pos(j);
-            if (pos < n) atomicAdd(&sub[wv][key[j] >> 24], 1u);
+            if (pos < n) atomicAdd(&sub[wv][RT_KEY(j) >> 24], 1u);
         }
         __syncthreads();
         if (wv == 0) find_bin(&sub[0][0], NWV, 256, (uint32_t)w, &sel_bin, &sel_rem);
@@ -432,6 +452,7 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
             if (v == wv) cand_off = ncand;
             ncand += sub[v][bin0];
         }
+        __syncthreads();   // the candidate list reuses the histograms' memory
     }
 
     // Radix select: after the four digits `prefix` is the w-th largest key and
@@ -440,12 +461,13 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     if (ncand <= (uint32_t)CAND) {
         // The remaining digits only concern keys whose top byte is bin0: list
         // them (in position order) and finish on the short list.
-#pragma unroll
+#pragma unroll UNR
         for (int j = 0; j < KPT; ++j) {
             const int pos = key_pos(j);
-            const bool is = pos < n && (key[j] >> 24) == bin0;
+            const uint32_t kj = RT_KEY(j);
+            const bool is = pos < n && (kj >> 24) == bin0;
             const uint64_t mb = __ballot(is);
-            if (is) cand[cand_off + (uint32_t)lanes_below(mb)] = key[j];
+            if (is) cand[cand_off + (uint32_t)lanes_below(mb)] = kj;
             cand_off += (uint32_t)__popcll(mb);
         }
         __syncthreads();
@@ -470,11 +492,12 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         for (int shift = 16; shift >= 0; shift -= 8) {
             if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
             __syncthreads();
-#pragma unroll
+#pragma unroll UNR
             for (int j = 0; j < KPT; ++j) {
                 const int pos = key_pos(j);
-                if (pos < n && (key[j] & himask) == prefix)
-                    atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+                const uint32_t kj = RT_KEY(j);
+                if (pos < n && (kj & himask) == prefix)
+                    atomicAdd(&hist[(kj >> shift) & 255u], 1u);
             }
             __syncthreads();
             if (wv == 0) find_bin(hist, 1, 0, remaining, &sel_bin, &sel_rem);
@@ -489,12 +512,13 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     // Position-ordered compaction: wave wv's positions are visited in
     // ascending order (groups jg, then lanes, then the VEC keys of a lane).
     uint32_t gtc = 0u, eqc = 0u;
-#pragma unroll
+#pragma unroll UNR
     for (int j = 0; j < KPT; ++j) {
         const int pos = key_pos(j);
         const bool valid = pos < n;
-        gtc += (valid && key[j] > T) ? 1u : 0u;
-        eqc += (valid && key[j] == T) ? 1u : 0u;
+        const uint32_t kj = RT_KEY(j);
+        gtc += (valid && kj > T) ? 1u : 0u;
+        eqc += (valid && kj == T) ? 1u : 0u;
     }
     gtc = wave_sum_u32(gtc);
     eqc = wave_sum_u32(eqc);
@@ -512,7 +536,7 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     int32_t* out = idx + row * w;
     const long bh = row / k;
     const int c = (int)(row % k);
-#pragma unroll
+#pragma unroll UNRG
     for (int jg = 0; jg < KPT / VEC; ++jg) {
         // positions of group jg in ascending order: (lane, e) lexicographic
         bool gt[VEC], eq[VEC], sel[VEC];
@@ -522,8 +546,9 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         for (int e = 0; e < VEC; ++e) {
             const int j = VEC * jg + e;
             const bool valid = key_pos(j) < n;
-            gt[e] = valid && key[j] > T;
-            eq[e] = valid && key[j] == T;
+            const uint32_t kj = RT_KEY(j);
+            gt[e] = valid && kj > T;
+            eq[e] = valid && kj == T;
             eb[e] = __ballot(eq[e]);
             eq_lanes += (uint32_t)lanes_below(eb[e]);
         }
@@ -569,11 +594,13 @@ void launch_score_d(const void* qk, int dtype, const float* mu, int BH, int H, i
     }
 }
 
-template <int NT, int KPT>
+#undef RT_KEY
+
+template <int NT, int KPT, bool LDSK = false>
 void launch_topw_k(const float* scores, int rows, int n, int w, int32_t* idx, int k,
                    uint32_t* mask, hipStream_t s) {
-    hipLaunchKernelGGL((topw_kernel<NT, KPT>), dim3(rows), dim3(NT), 0, s, scores, n, w, idx, k,
-                       mask, mask_words(k));
+    hipLaunchKernelGGL((topw_kernel<NT, KPT, LDSK>), dim3(rows), dim3(NT), 0, s, scores, n, w, idx,
+                       k, mask, mask_words(k));
 }
 
 }  // namespace
@@ -601,7 +628,7 @@ hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t
     else if (per <= 8) launch_topw_k<512, 8>(scores, rows, n, w, idx, k, mask, s);
     else if (per <= 16) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
     else if (per <= 32) launch_topw_k<512, 32>(scores, rows, n, w, idx, k, mask, s);
-    else if (per <= 64) launch_topw_k<512, 64>(scores, rows, n, w, idx, k, mask, s);
+    else if (per <= 64) launch_topw_k<1024, 32, true>(scores, rows, n, w, idx, k, mask, s);
     else launch_topw_k<1024, 64>(scores, rows, n, w, idx, k, mask, s);
     return hipGetLastError();
 }
