@@ -386,16 +386,22 @@ __global__ __launch_bounds__(128) void cluster_sums_f32_kernel(
     }
 }
 
-// One thread per (token, 16 output dims): the slots hold the rows of ranks
-// 0..kSlots-1 contiguously; higher ranks are read from the overflow buffer at
-// the rows the directory lists.
-template <typename OutT, int D>
+// One thread per (token, 16 output dims), for NO outputs sharing one
+// membership (the backward's three gradients): the slots hold the rows of
+// ranks 0..kSlots-1 contiguously; higher ranks are read from the overflow
+// buffer at the rows the directory lists.
+template <int NO>
+struct CombineSet {
+    const float* slots[NO];
+    const float* ovf[NO];
+    void* out[NO];
+};
+
+template <typename OutT, int D, int NO>
 __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ mask,
-                                                      const float* __restrict__ slots,
-                                                      const float* __restrict__ ovf,
-                                                      const int32_t* __restrict__ dir, long BHn,
-                                                      int n, int k, int w, int KW,
-                                                      OutT* __restrict__ out) {
+                                                      const int32_t* __restrict__ dir,
+                                                      CombineSet<NO> cs, long BHn, int n, int k,
+                                                      int w, int KW) {
     constexpr int DG = D / 16;
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
     const long tok = gid / DG;
@@ -405,44 +411,46 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
     int cnt = 0;
     for (int i = 0; i < KW; ++i) cnt += __popc(mrow[i]);
     if (cnt == 1) return;
-    float4 p[kSlots][4];
-    const float* sp = slots + tok * kSlots * D + d0;
+    const long bhkw = (tok / n) * k * (long)w;
+    const int32_t* drow = dir + tok * (k - kSlots);
 #pragma unroll
-    for (int j = 0; j < kSlots; ++j)
+    for (int o = 0; o < NO; ++o) {
+        float4 p[kSlots][4];
+        const float* sp = cs.slots[o] + tok * kSlots * D + d0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            p[j][q] = (j < cnt) ? *reinterpret_cast<const float4*>(sp + (long)j * D + 4 * q)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 acc[4];
+        for (int j = 0; j < kSlots; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        acc[q] = p[0][q];
+            for (int q = 0; q < 4; ++q)
+                p[j][q] = (j < cnt) ? *reinterpret_cast<const float4*>(sp + (long)j * D + 4 * q)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 acc[4];
 #pragma unroll
-        for (int j = 1; j < kSlots; ++j) {
-            acc[q].x += p[j][q].x;
-            acc[q].y += p[j][q].y;
-            acc[q].z += p[j][q].z;
-            acc[q].w += p[j][q].w;
-        }
-    }
-    if (cnt > kSlots) {
-        const long bhkw = (tok / n) * k * (long)w;
-        const int32_t* drow = dir + tok * (k - kSlots);
-        for (int j = kSlots; j < cnt; ++j) {
-            const float* op = ovf + (bhkw + drow[j - kSlots]) * D + d0;
+        for (int q = 0; q < 4; ++q) {
+            acc[q] = p[0][q];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 o = *reinterpret_cast<const float4*>(op + 4 * q);
-                acc[q].x += o.x;
-                acc[q].y += o.y;
-                acc[q].z += o.z;
-                acc[q].w += o.w;
+            for (int j = 1; j < kSlots; ++j) {
+                acc[q].x += p[j][q].x;
+                acc[q].y += p[j][q].y;
+                acc[q].z += p[j][q].z;
+                acc[q].w += p[j][q].w;
             }
         }
-    }
-    OutT* dst = out + tok * D + d0;
+        for (int j = kSlots; j < cnt; ++j) {
+            const float* op = cs.ovf[o] + (bhkw + drow[j - kSlots]) * D + d0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store4<OutT>(dst + 4 * q, acc[q].x, acc[q].y, acc[q].z, acc[q].w);
+            for (int q = 0; q < 4; ++q) {
+                const float4 v4 = *reinterpret_cast<const float4*>(op + 4 * q);
+                acc[q].x += v4.x;
+                acc[q].y += v4.y;
+                acc[q].z += v4.z;
+                acc[q].w += v4.w;
+            }
+        }
+        OutT* dst = static_cast<OutT*>(cs.out[o]) + tok * D + d0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            store4<OutT>(dst + 4 * q, acc[q].x, acc[q].y, acc[q].z, acc[q].w);
+    }
 }
 
 struct AttnArgs {
@@ -546,33 +554,41 @@ hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int
     return hipGetLastError();
 }
 
-template <typename OutT, int D>
-void launch_combine_d(const uint32_t* mask, const float* slots, const float* ovf,
-                      const int32_t* dir, int BH, int n, int k, int w, void* out, hipStream_t s) {
+template <typename OutT, int D, int NO>
+void launch_combine_d(const uint32_t* mask, const int32_t* dir, const CombineSet<NO>& cs, int BH,
+                      int n, int k, int w, hipStream_t s) {
     const long BHn = (long)BH * n;
     const long threads = BHn * (D / 16);
-    hipLaunchKernelGGL((combine_kernel<OutT, D>), dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, s, mask, slots, ovf, dir, BHn, n, k, w, mask_words(k),
-                       (OutT*)out);
+    hipLaunchKernelGGL((combine_kernel<OutT, D, NO>), dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, mask, dir, cs, BHn, n, k, w, mask_words(k));
 }
 
-template <typename OutT>
-void launch_combine_t(const uint32_t* mask, const float* slots, const float* ovf,
-                      const int32_t* dir, int BH, int n, int d, int k, int w, void* out,
-                      hipStream_t s) {
+template <typename OutT, int NO>
+void launch_combine_t(const uint32_t* mask, const int32_t* dir, const CombineSet<NO>& cs, int BH,
+                      int n, int d, int k, int w, hipStream_t s) {
     switch (d) {
-        case 16: launch_combine_d<OutT, 16>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
-        case 32: launch_combine_d<OutT, 32>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
-        case 64: launch_combine_d<OutT, 64>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
-        default: launch_combine_d<OutT, 128>(mask, slots, ovf, dir, BH, n, k, w, out, s); break;
+        case 16: launch_combine_d<OutT, 16, NO>(mask, dir, cs, BH, n, k, w, s); break;
+        case 32: launch_combine_d<OutT, 32, NO>(mask, dir, cs, BH, n, k, w, s); break;
+        case 64: launch_combine_d<OutT, 64, NO>(mask, dir, cs, BH, n, k, w, s); break;
+        default: launch_combine_d<OutT, 128, NO>(mask, dir, cs, BH, n, k, w, s); break;
     }
 }
 
 hipError_t launch_combine(const uint32_t* mask, const float* slots, const float* ovf,
                           const int32_t* dir, int out_dtype, int BH, int n, int d, int k, int w,
                           void* out, hipStream_t s) {
-    if (out_dtype == 1) launch_combine_t<u16>(mask, slots, ovf, dir, BH, n, d, k, w, out, s);
-    else launch_combine_t<float>(mask, slots, ovf, dir, BH, n, d, k, w, out, s);
+    const CombineSet<1> cs{{slots}, {ovf}, {out}};
+    if (out_dtype == 1) launch_combine_t<u16, 1>(mask, dir, cs, BH, n, d, k, w, s);
+    else launch_combine_t<float, 1>(mask, dir, cs, BH, n, d, k, w, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine3_f32(const uint32_t* mask, const float* const slots[3],
+                               const float* const ovf[3], const int32_t* dir, int BH, int n, int d,
+                               int k, int w, float* const out[3], hipStream_t s) {
+    const CombineSet<3> cs{{slots[0], slots[1], slots[2]}, {ovf[0], ovf[1], ovf[2]},
+                           {out[0], out[1], out[2]}};
+    launch_combine_t<float, 3>(mask, dir, cs, BH, n, d, k, w, s);
     return hipGetLastError();
 }
 

@@ -503,12 +503,10 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    float* grads[3] = {dq, dk, dv};
-    for (int j = 0; j < 3; ++j) {
-        e = launch_combine(mask, part[j][0], part[j][1], dir, 0, BH, n, d, k, w, grads[j], s);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    float* const grads[3] = {dq, dk, dv};
+    const float* const sl[3] = {part[0][0], part[1][0], part[2][0]};
+    const float* const ov[3] = {part[0][1], part[1][1], part[2][1]};
+    return launch_combine3_f32(mask, sl, ov, dir, BH, n, d, k, w, grads, s);
 }
 
 }  // namespace rt

@@ -49,6 +49,12 @@ hipError_t launch_combine(const uint32_t* mask, const float* slots, const float*
                           const int32_t* dir, int out_dtype, int BH, int n, int d, int k, int w,
                           void* out, hipStream_t s);
 
+// The same for three float32 outputs sharing one membership (one pass over the
+// bits).
+hipError_t launch_combine3_f32(const uint32_t* mask, const float* const slots[3],
+                               const float* const ovf[3], const int32_t* dir, int BH, int n, int d,
+                               int k, int w, float* const out[3], hipStream_t s);
+
 // mu <- lambda*mu + (1-lambda)/2 * (sum_b sum_q[b] + sum_b sum_k[b]); sum_k may
 // be NULL (keys are the queries: S_K = S_Q).  sums are [B][H][k][d].
 hipError_t launch_ema_sums(float* mu, const float* sum_q, const float* sum_k, int B, int H,
