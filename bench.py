@@ -218,6 +218,78 @@ def time_stack(rt, sc, reps=5):
                         f"{d}, n={n}, B={B}, random-init weights N(0, 1/fan_in)"}
 
 
+def sweep_configs():
+    """The long layer's shape (B=1, 8 routed + 4 local heads of width 128, window
+    512) at n = 1K .. 64K with k = sqrt(n) rounded down to a power of two and
+    w = n/k."""
+    out = []
+    for i, lg in enumerate(range(10, 17)):
+        n = 1 << lg
+        k = 1 << (lg // 2)
+        out.append(S.Config(80 + i, f"sweep_n{n}", "bf16", 1, 8, 4, n, 128, k, n // k, 512))
+    return out
+
+
+def run_sweep(rt, reps=20):
+    """Per-call times of the layer's entry points across sequence lengths, and
+    the fitted growth of the routed heads' time with n (the pages' O(n^1.5 d)
+    at k = sqrt(n)) and the routed/local ratio (the pages' ~1.7x on TPUv3)."""
+    pts = []
+    for cfg in sweep_configs():
+        inp = S.make_inputs(cfg)
+        B, R, n, d, k, w = cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w
+        scale = 1.0 / math.sqrt(d)
+        qk, v = dev(inp["qk"]), dev(inp["v"])
+        ql, kl, vl = dev(inp["q_local"]), dev(inp["k_local"]), dev(inp["v_local"])
+        mu = torch.from_numpy(inp["mu"].astype(np.float32)).cuda()
+        del inp
+        inv = torch.empty((B, R, n), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, R, k, w), dtype=torch.int32, device="cuda")
+        mask = torch.empty((B, R, n, rt.mask_words(k)), dtype=torch.int32, device="cuda")
+        sum_q = torch.empty((B, R, k, d), dtype=torch.float32, device="cuda")
+        out, out_l = torch.empty_like(qk), torch.empty_like(ql)
+        ws_r = torch.empty(rt.workspace_bytes("route", B, R, n, d, k, w), dtype=torch.uint8,
+                           device="cuda")
+        ws_a = torch.empty(rt.workspace_bytes("routed_attn", B, R, n, d, k, w), dtype=torch.uint8,
+                           device="cuda")
+        calls = {
+            "rt_route": lambda: rt.route(qk, mu, w, out=(inv, idx, mask), ws=ws_r),
+            "rt_routed_attn": lambda: rt.routed_attn(qk, qk, v, idx, inv, inv, scale=scale,
+                                                     mask=mask, sums=(sum_q, None), out=out,
+                                                     ws=ws_a),
+            "rt_centroid_update_sums": lambda: rt.centroid_update_sums_(mu, sum_q, cfg.lam),
+            "rt_local_attn": lambda: rt.local_attn(ql, kl, vl, cfg.window, scale=scale, out=out_l),
+        }
+        us = {}
+        for name, fn in calls.items():
+            for _ in range(3):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            us[name] = a.elapsed_time(b) / reps * 1e3
+        routed = us["rt_route"] + us["rt_routed_attn"] + us["rt_centroid_update_sums"]
+        pts.append({"n": n, "k": k, "w": w, "us": us, "routed_us": routed,
+                    "routed_over_local": routed / us["rt_local_attn"],
+                    "routed_tokens_per_s": B * n / (routed * 1e-6),
+                    "routed_gflop": (6.0 * n * k * d + 4.0 * k * w * w * d) * R * B / 1e9})
+        del qk, v, ql, kl, vl, ws_r, ws_a, out, out_l
+        torch.cuda.empty_cache()
+    ln = np.log([p["n"] for p in pts])
+    fit = lambda ys: float(np.polyfit(ln, np.log(ys), 1)[0])
+    big = [p for p in pts if p["n"] >= 8192]
+    lnb = np.log([p["n"] for p in big])
+    return {"metric": "routed-attention call times vs n at k = sqrt(n) (long layer shape)",
+            "points": pts,
+            "exponent_routed_time_all": fit([p["routed_us"] for p in pts]),
+            "exponent_routed_time_n_ge_8192": float(np.polyfit(lnb, np.log([p["routed_us"] for p in big]), 1)[0]),
+            "exponent_routed_flops": fit([p["routed_gflop"] for p in pts]),
+            "exponent_local_time": fit([p["us"]["rt_local_attn"] for p in pts])}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +303,9 @@ def main():
                     "a captured HIP graph of the step")
     ap.add_argument("--concurrent-local", action="store_true", help="run the local heads "
                     "concurrently on a second stream instead of after the routed heads")
+    ap.add_argument("--sweep", action="store_true", help="instead of the benchmark step, time "
+                    "the entry points at n = 1K..64K with k = sqrt(n) and print that as one JSON "
+                    "line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, copy a MIB-mebibyte device buffer once (a plain copy "
                     "of known size that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -244,6 +319,10 @@ def main():
 
     import content_sparse_attention_unit_amd as rt
     rt._load()
+
+    if args.sweep:
+        print(json.dumps(run_sweep(rt)), flush=True)
+        return
 
     cfg = S.CONFIGS[args.workload]
     inp = S.make_inputs(cfg)
