@@ -254,6 +254,16 @@ def test_local_window_edges(rt, orc, window):
         assert torch.equal(out, v.float())
 
 
+# The longest rows of the sequence-length sweep (k = sqrt(n)): the top-w variants
+# for n = 16K (registers) and 64K (the 1024-thread register variant), 2 heads.
+@pytest.mark.parametrize("n,k", [(16384, 128), (65536, 256)])
+def test_sweep_long_rows(rt, orc, n, k):
+    cfg = base(cfg_id=85 + (n == 65536), dtype="bf16", B=1, R=2, L=0, n=n, d=128, k=k, w=n // k,
+               window=0)
+    res = run_routed_case(rt, orc, cfg, check_scores=False)
+    say(f"[sweep] n={n}: {int(res['differs'].sum())} near-tie clusters differ")
+
+
 # Full-size workloads, in the launch configuration the benchmark times.
 @pytest.mark.parametrize("name", ["routed", "mixed", "long", "stress"])
 def test_full_size_forward(rt, orc, name):
