@@ -218,24 +218,26 @@ def time_stack(rt, sc, reps=5):
                         f"{d}, n={n}, B={B}, random-init weights N(0, 1/fan_in)"}
 
 
-def sweep_configs():
+def sweep_configs(only=None):
     """The long layer's shape (B=1, 8 routed + 4 local heads of width 128, window
     512) at n = 1K .. 64K with k = sqrt(n) rounded down to a power of two and
-    w = n/k."""
+    w = n/k (``only``: the subset of n to keep)."""
     out = []
     for i, lg in enumerate(range(10, 17)):
         n = 1 << lg
+        if only and n not in only:
+            continue
         k = 1 << (lg // 2)
         out.append(S.Config(80 + i, f"sweep_n{n}", "bf16", 1, 8, 4, n, 128, k, n // k, 512))
     return out
 
 
-def run_sweep(rt, reps=20):
+def run_sweep(rt, reps=20, only=None):
     """Per-call times of the layer's entry points across sequence lengths, and
     the fitted growth of the routed heads' time with n (the pages' O(n^1.5 d)
     at k = sqrt(n)) and the routed/local ratio (the pages' ~1.7x on TPUv3)."""
     pts = []
-    for cfg in sweep_configs():
+    for cfg in sweep_configs(only):
         inp = S.make_inputs(cfg)
         B, R, n, d, k, w = cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w
         scale = 1.0 / math.sqrt(d)
@@ -278,6 +280,9 @@ def run_sweep(rt, reps=20):
                     "routed_gflop": (6.0 * n * k * d + 4.0 * k * w * w * d) * R * B / 1e9})
         del qk, v, ql, kl, vl, ws_r, ws_a, out, out_l
         torch.cuda.empty_cache()
+    if len(pts) < 3:
+        return {"metric": "routed-attention call times vs n at k = sqrt(n) (long layer shape)",
+                "points": pts}
     ln = np.log([p["n"] for p in pts])
     fit = lambda ys: float(np.polyfit(ln, np.log(ys), 1)[0])
     big = [p for p in pts if p["n"] >= 8192]
@@ -306,6 +311,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="instead of the benchmark step, time "
                     "the entry points at n = 1K..64K with k = sqrt(n) and print that as one JSON "
                     "line")
+    ap.add_argument("--sweep-n", default="", help="with --sweep: comma-separated subset of the "
+                    "lengths (powers of two, 1024 .. 65536)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before timing, copy a MIB-mebibyte device buffer once (a plain copy "
                     "of known size that scales the FETCH_SIZE/WRITE_SIZE counters)")
@@ -321,7 +328,8 @@ def main():
     rt._load()
 
     if args.sweep:
-        print(json.dumps(run_sweep(rt)), flush=True)
+        only = {int(x) for x in args.sweep_n.split(",") if x}
+        print(json.dumps(run_sweep(rt, only=only)), flush=True)
         return
 
     cfg = S.CONFIGS[args.workload]

@@ -23,6 +23,8 @@
 //                      LDS), then a position-ordered compaction with wave
 //                      ballots, so the w members come out sorted by position
 //                      with ties taken at the lowest positions.
+#include <type_traits>
+
 #include "rt_common.hpp"
 #include "rt_internal.hpp"
 
@@ -235,46 +237,46 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += (uint32_t)__shfl_xor((int)x, off);
-    return x;
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ uint32_t buffer_load4(buf_rsrc r, uint32_t byte_off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
 }
+#else
+__device__ __forceinline__ uint32_t buffer_load4(buf_rsrc, uint32_t) { return 0u; }
+#endif
 
-// Wave 0 finds, in a 256-bin histogram (bins summed over `parts` copies laid
-// out `stride` words apart), the bin holding the `remaining`-th largest key:
-// writes the bin and the rank left inside it.
-__device__ __forceinline__ void find_bin(const uint32_t* hist, int parts, int stride,
-                                         uint32_t remaining, uint32_t* sel_bin,
-                                         uint32_t* sel_rem) {
-    const int lane = lane_id();
-    uint32_t cnt[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        uint32_t t = 0u;
-        for (int v = 0; v < parts; ++v) t += hist[v * stride + 4 * lane + b];
-        cnt[b] = t;
-    }
-    const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-    uint32_t suf = tot;  // inclusive suffix sum over lanes
-#pragma unroll
-    for (int dl = 1; dl < kWave; dl <<= 1) {
-        const uint32_t o = __shfl_down(suf, dl);
-        if (lane + dl < kWave) suf += o;
-    }
-    uint32_t above = suf - tot;
-#pragma unroll
-    for (int b = 3; b >= 0; --b) {
-        if (above < remaining && remaining <= above + cnt[b]) {
-            *sel_bin = (uint32_t)(4 * lane + b);
-            *sel_rem = remaining - above;
-        }
-        above += cnt[b];
-    }
+// Wave reductions on the DPP network (no LDS traffic): partial results move
+// along each row of 16 lanes, then across rows; the total lands in lane 63.
+template <bool MAX>
+__device__ __forceinline__ uint32_t dpp_step(uint32_t x, uint32_t y) {
+    return MAX ? max(x, y) : x + y;
 }
+#define RT_DPP(x, ctrl, rmask) \
+    (uint32_t) __builtin_amdgcn_update_dpp(0, (int)(x), ctrl, rmask, 0xf, true)
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x111, 0xf));   // row_shr:1
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x112, 0xf));   // row_shr:2
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x114, 0xf));   // row_shr:4
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x118, 0xf));   // row_shr:8
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x142, 0xa));   // row_bcast:15 into rows 1, 3
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x143, 0xc));   // row_bcast:31 into rows 2, 3
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+// The same over lanes 0..15 only.
+template <bool MAX>
+__device__ __forceinline__ uint32_t row16_reduce_u32(uint32_t x) {
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x111, 0xf));
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x112, 0xf));
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x114, 0xf));
+    x = dpp_step<MAX>(x, RT_DPP(x, 0x118, 0xf));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+}
+#undef RT_DPP
 
-// The same search done by each wave for itself on a shared histogram: every
-// lane gets the bin and the rank left inside it (no barrier needed after it).
+// Each wave finds for itself, in a shared 256-bin histogram, the bin holding
+// the `remaining`-th largest key: every lane gets the bin and the rank left
+// inside it (no barrier needed after it).
 // `remaining` must be between 1 and the histogram total.
 __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t remaining,
                                               uint32_t& bin, uint32_t& rem) {
@@ -305,223 +307,305 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t rem
     rem = (uint32_t)__shfl((int)fr, src);
 }
 
-// LDSK: the row's keys live in LDS instead of registers (long rows: 64K keys
-// need 128 KiB, which LDS holds and registers do not).
-template <int NT, int KPT, bool LDSK>
+// Balanced top-w of one row of n scores; one workgroup per row.  Key j of
+// lane l in wave v belongs to position v*64*KPT + 64*j + l, so that a wave's
+// ballot over its key j is the membership bitmap of 64 consecutive positions.
+//  1. Load the row as order-preserving keys (registers); each wave counts its
+//     keys in its own four highest top bytes (sign and high exponent bits).
+//  2. One exchange gives the row's counts of its four highest top bytes: the
+//     top byte bin0 of the w-th largest key and its rank inside that byte.
+//  3. Each wave lists its keys of top byte bin0 or above (fewer than w of
+//     them above) with their positions, in position order: a few per cent of
+//     the row.
+//  4. Three 8-bit digit passes over the lists give the w-th largest key T and
+//     how many keys equal to T belong to the top w.
+//  5. The lists, read in position order, give the members: the keys above T
+//     and, at the lowest positions, the keys equal to T.
+// A row whose bin0 is not among its four highest top bytes, or whose lists
+// overflow, finishes with the digit passes and the selection over all keys.
+// Positions past the row hold key 0, below every key of a number: they rank
+// last among equals and are never selected.
+constexpr int kCandPerWave = 512;
+
+// TOPB: only the keys' top bytes stay in registers (four to a register, for
+// 64 keys a lane); listed keys are re-read in full from the score row.
+template <int NT, int KPT, bool TOPB>
 __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scores, int n, int w,
                                                   int32_t* __restrict__ idx, int k,
                                                   uint32_t* __restrict__ mask, int KW) {
+    static_assert(NT >= 256 && NT % kWave == 0, "one thread per histogram bin");
     constexpr int NWV = NT / kWave;
-    constexpr int CAND = 4096;           // capacity of the candidate list
-    // the candidate list, or before it (only when the first digit needs a full
-    // histogram) the per-wave histograms of the top byte
-    constexpr int CSZ = CAND > NWV * 256 ? CAND : NWV * 256;
-    __shared__ __attribute__((aligned(16))) uint32_t cand[CSZ];
-    uint32_t (*sub)[256] = reinterpret_cast<uint32_t (*)[256]>(cand);
-    __shared__ __attribute__((aligned(16))) uint32_t lkeys[LDSK ? NT * KPT : 4];
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sel_bin, sel_rem;
-    __shared__ uint32_t wgt[NWV], weq[NWV];
-    __shared__ __attribute__((aligned(16))) uint32_t wtop[NWV][8];   // per wave: highest top
-                                         // byte, counts of it and the 3 below (padded)
+    constexpr int CW = kCandPerWave;
+    __shared__ __attribute__((aligned(16))) uint2 cand[NWV][CW];   // (key, position)
     __shared__ __attribute__((aligned(16))) uint32_t hist3[3][256];
+    __shared__ __attribute__((aligned(16))) uint32_t wtop[NWV][8];  // per wave: highest top
+                                         // byte, counts of it and the 3 below (padded)
+    __shared__ uint32_t wcnt[NWV], wgt[NWV], weq[NWV];
 
-    const long row = blockIdx.x;
-    const float* srow = scores + row * n;
+    const int row = blockIdx.x;
+    const float* srow = scores + (long)row * n;
     const int lane = lane_id(), wv = wave_id();
     const int seg0 = wv * kWave * KPT;
-    // Wave wv owns positions [seg0, seg0 + 64*KPT); its key j sits at
-    // seg0 + 64*VEC*(j / VEC) + VEC*lane + j % VEC: VEC consecutive positions
-    // per lane, loaded as one 16-byte vector when VEC = 4.
-    constexpr int VEC = (KPT % 4 == 0) ? 4 : 1;
-    auto key_pos = [&](int j) { return seg0 + kWave * VEC * (j / VEC) + VEC * lane + j % VEC; };
+    const int pl = seg0 + lane;   // position of key 0 of this lane; key j at pl + 64 j
+    int32_t* out = idx + (long)row * w;
+    const int bh = row / k, c = row - bh * k;
+    uint32_t* mrow = mask == nullptr ? nullptr : mask + (long)bh * n * KW + (c >> 5);
+    const uint32_t cbit = 1u << (c & 31);
 
-    uint32_t key[LDSK ? 1 : KPT];
-    // key j of this thread (in a register, or read back from LDS)
-#define RT_KEY(j) (LDSK ? lkeys[key_pos(j)] : key[LDSK ? 0 : (j)])
-    // loops over the keys: fully unrolled for registers, partly for LDS
-    constexpr int UNR = LDSK ? 4 : KPT;
-    constexpr int UNRG = LDSK ? 1 : KPT / VEC;
-    uint32_t wtopb = 0u;   // highest top byte (sign and high exponent bits) in this lane
-    const bool vec_ok = VEC == 4 && (n & 3) == 0;   // rows start 16-byte aligned
+    // 1. Keys.  Every load is issued unconditionally (a wave keeps them all in
+    // flight); only a wave whose segment runs past the row checks positions.
+    const buf_rsrc srs = make_rsrc(srow, 4u * (uint32_t)n);
+    constexpr int NKR = TOPB ? (KPT + 3) / 4 : KPT;
+    uint32_t key[NKR];   // the keys, or (TOPB) their top bytes
+    uint32_t mw = 0u;
+    auto load = [&](auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
-    for (int jg = 0; jg < KPT / VEC; ++jg) {
-        const int p0 = key_pos(VEC * jg);
-        uint32_t kv[VEC];
-        if (vec_ok && p0 + VEC <= n) {
-            const float4 f = *reinterpret_cast<const float4*>(srow + p0);
-            const float fv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) kv[e] = order_key(fv[e]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) kv[e] = (p0 + e < n) ? order_key(srow[p0 + e]) : 0u;
+        for (int j = 0; j < KPT; ++j) {
+            const int p = pl + kWave * j;
+            const bool in = !TAIL || p < n;
+            uint32_t kj =
+                order_key(__uint_as_float(buffer_load4(srs, in ? 4u * (uint32_t)p : kOutOfRange)));
+            kj = in ? kj : 0u;
+            mw = max(mw, kj);
+            if constexpr (TOPB) {
+                if (j % 4 == 0) key[j / 4] = kj >> 24;
+                else key[j / 4] |= (kj >> 24) << (8 * (j % 4));
+            } else {
+                key[j] = kj;
+            }
         }
+    };
+    if (seg0 + kWave * KPT <= n) load(std::false_type{});
+    else load(std::true_type{});
+    auto top8 = [&](int j) -> uint32_t {
+        if constexpr (TOPB) return (key[j / 4] >> (8 * (j % 4))) & 0xffu;
+        else return key[j] >> 24;
+    };
+    mw = wave_reduce_u32<true>(mw) >> 24;
+    // 7-bit counters of the top bytes mw, mw-1, mw-2, mw-3 (bits 28.. take the
+    // rest and may wrap); a lane holds at most 64 keys
+    uint32_t cf = 0u;
+    const uint32_t mw7 = 7u * mw;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            if (p0 + e < n) wtopb = max(wtopb, kv[e] >> 24);
-            if constexpr (!LDSK) key[VEC * jg + e] = kv[e];
-        }
-        if constexpr (LDSK) {
-            if constexpr (VEC == 4)
-                *reinterpret_cast<uint4*>(&lkeys[p0]) = make_uint4(kv[0], kv[1], kv[2], kv[3]);
-            else
-                lkeys[p0] = kv[0];
-        }
-    }
-    // The w-th largest key nearly always has one of the row's four highest top
-    // bytes.  Each wave counts its keys in its own four highest top bytes with
-    // per-lane counters (a row's scores share top bytes in large groups, which
-    // makes an LDS histogram a hot spot of atomics); one exchange then gives
-    // the exact counts of the row's four highest top bytes.
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) wtopb = max(wtopb, (uint32_t)__shfl_xor((int)wtopb, off));
-    uint32_t c01 = 0u, c23 = 0u;
-#pragma unroll UNR
-    for (int j = 0; j < KPT; ++j) {
-        const int pos = key_pos(j);
-        const uint32_t dlt = wtopb - (RT_KEY(j) >> 24);   // >= 0 for every valid key
-        if (pos < n && dlt < 4u) {
-            if (dlt < 2u) c01 += 1u << (16 * dlt);
-            else c23 += 1u << (16 * (dlt - 2u));
-        }
-    }
-    c01 = wave_sum_u32(c01);
-    c23 = wave_sum_u32(c23);
+    for (int j = 0; j < KPT; ++j) cf += 1u << min(mw7 - 7u * top8(j), 28u);
+    uint32_t c01 = (cf & 0x7fu) | (((cf >> 7) & 0x7fu) << 16);
+    uint32_t c23 = ((cf >> 14) & 0x7fu) | (((cf >> 21) & 0x7fu) << 16);
+    c01 = wave_reduce_u32<false>(c01);
+    c23 = wave_reduce_u32<false>(c23);
     if (lane == 0) {
-        wtop[wv][0] = wtopb;
+        wtop[wv][0] = mw;
         wtop[wv][1] = c01 & 0xffffu;
         wtop[wv][2] = c01 >> 16;
         wtop[wv][3] = c23 & 0xffffu;
         wtop[wv][4] = c23 >> 16;
     }
-    // the first histogram of the candidate passes starts cleared
     if (threadIdx.x < 256) hist3[0][threadIdx.x] = 0u;
     __syncthreads();
-    uint32_t wt[NWV][5];   // every wave's entry, read at once (independent LDS loads)
-#pragma unroll
-    for (int v = 0; v < NWV; ++v) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&wtop[v][0]);
-        wt[v][0] = a.x;
-        wt[v][1] = a.y;
-        wt[v][2] = a.z;
-        wt[v][3] = a.w;
-        wt[v][4] = wtop[v][4];
+
+    // 2. The row's four highest top bytes: lane v < NWV holds wave v's entry.
+    static_assert(NWV <= 16, "one DPP row holds every wave's entry");
+    uint4 we = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t we4 = 0u;
+    if (lane < NWV) {
+        we = *reinterpret_cast<const uint4*>(&wtop[lane][0]);
+        we4 = wtop[lane][4];
     }
-    uint32_t rtop = 0u;
+    const uint32_t rtop = row16_reduce_u32<true>(we.x);
+    uint32_t tot[4];
 #pragma unroll
-    for (int v = 0; v < NWV; ++v) rtop = max(rtop, wt[v][0]);
-    uint32_t bin0 = rtop, remaining = (uint32_t)w, ncand = 0u, cand_off = 0u;
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t b = rtop - (uint32_t)i, dv = we.x - b;
+        const uint32_t cv = (lane < NWV && rtop >= (uint32_t)i && we.x >= b)
+                                ? (dv == 0u ? we.y : dv == 1u ? we.z : dv == 2u ? we.w : we4)
+                                : 0u;
+        tot[i] = row16_reduce_u32<false>(cv);
+    }
+    uint32_t bin0 = rtop, remaining = (uint32_t)w;
     bool found = false;
-    for (uint32_t i = 0; i < 4u && i <= rtop; ++i) {
-        const uint32_t b = rtop - i;
-        uint32_t tot = 0u, before = 0u;
 #pragma unroll
-        for (int v = 0; v < NWV; ++v) {
-            const uint32_t dv = wt[v][0] - b;   // wt[v][0] <= rtop, so dv <= i <= 3
-            uint32_t cv = 0u;
-            if (wt[v][0] >= b)
-                cv = dv == 0u ? wt[v][1] : dv == 1u ? wt[v][2] : dv == 2u ? wt[v][3] : wt[v][4];
-            if (v < wv) before += cv;
-            tot += cv;
+    for (int i = 0; i < 4; ++i) {
+        if (!found && rtop >= (uint32_t)i) {
+            if (tot[i] >= remaining) {
+                bin0 = rtop - (uint32_t)i;
+                found = true;
+            } else {
+                remaining -= tot[i];
+            }
         }
-        if (tot >= remaining) {
-            bin0 = b;
-            ncand = tot;
-            cand_off = before;
-            found = true;
-            break;
-        }
-        remaining -= tot;
-    }
-    if (!found) {   // the threshold lies lower: full histogram of the top byte
-        for (int e = threadIdx.x; e < NWV * 256; e += NT) (&sub[0][0])[e] = 0u;
-        __syncthreads();
-#pragma unroll UNR
-        for (int j = 0; j < KPT; ++j) {
-            const int pos = key_pos(j);
-            if (pos < n) atomicAdd(&sub[wv][RT_KEY(j) >> 24], 1u);
-        }
-        __syncthreads();
-        if (wv == 0) find_bin(&sub[0][0], NWV, 256, (uint32_t)w, &sel_bin, &sel_rem);
-        __syncthreads();
-        bin0 = sel_bin;
-        remaining = sel_rem;
-        ncand = 0u;
-        for (int v = 0; v < NWV; ++v) {
-            if (v == wv) cand_off = ncand;
-            ncand += sub[v][bin0];
-        }
-        __syncthreads();   // the candidate list reuses the histograms' memory
     }
 
-    // Radix select: after the four digits `prefix` is the w-th largest key and
-    // `remaining` the number of keys equal to it that belong to the top w.
-    uint32_t prefix = bin0 << 24, himask = 0xff000000u;
-    if (ncand <= (uint32_t)CAND) {
-        // The remaining digits only concern keys whose top byte is bin0: list
-        // them (in position order) and finish on the short list.
-#pragma unroll UNR
+    // 3. This wave's keys of top byte bin0 or above, in position order, and
+    // the first digit's histogram of its keys of top byte bin0.
+    uint32_t nl = 0u;
+    if (found) {
+        const uint32_t lo = bin0 << 24;
+        uint32_t cnt = 0u;
+        bool ovf = false;
+#pragma unroll
         for (int j = 0; j < KPT; ++j) {
-            const int pos = key_pos(j);
-            const uint32_t kj = RT_KEY(j);
-            const bool is = pos < n && (kj >> 24) == bin0;
+            const bool is = TOPB ? top8(j) >= bin0 : key[TOPB ? 0 : j] >= lo;
             const uint64_t mb = __ballot(is);
-            if (is) cand[cand_off + (uint32_t)lanes_below(mb)] = kj;
-            cand_off += (uint32_t)__popcll(mb);
+            const uint32_t pc = (uint32_t)__popcll(mb);
+            if (cnt + pc <= (uint32_t)CW) {
+                if (is)
+                    cand[wv][cnt + (uint32_t)lanes_below(mb)] =
+                        make_uint2(TOPB ? 0u : key[TOPB ? 0 : j], (uint32_t)(pl + kWave * j));
+            } else {
+                ovf = true;
+            }
+            cnt += pc;
         }
-        __syncthreads();
-        // One barrier per digit: every wave reads the histogram itself after
-        // it, and the histogram of the next digit (not read by anyone since
-        // the barrier before this one) is cleared while this one fills.
+        nl = min(cnt, (uint32_t)CW);
+        if constexpr (TOPB) {
+            // the listed keys in full, from the score row (eight loads in flight)
+            for (uint32_t i0 = 0; i0 < nl; i0 += 8 * kWave) {
+                uint32_t pp[8], kv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + (uint32_t)(u * kWave + lane);
+                    pp[u] = i < nl ? cand[wv][i].y : 0xffffffffu;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    kv[u] = order_key(__uint_as_float(
+                        buffer_load4(srs, pp[u] < (uint32_t)n ? 4u * pp[u] : kOutOfRange)));
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t i = i0 + (uint32_t)(u * kWave + lane);
+                    if (i < nl) cand[wv][i].x = pp[u] < (uint32_t)n ? kv[u] : 0u;
+                }
+            }
+        }
+        for (uint32_t i = lane; i < nl; i += kWave) {
+            const uint32_t kc = cand[wv][i].x;
+            if ((kc >> 24) == bin0) atomicAdd(&hist3[0][(kc >> 16) & 255u], 1u);
+        }
+        if (lane == 0) wcnt[wv] = ovf ? 0xffffffffu : cnt;
+        if (threadIdx.x < 256) hist3[1][threadIdx.x] = 0u;
+    }
+    __syncthreads();
+    bool slow = !found;
+    if (found) {
+#pragma unroll
+        for (int v = 0; v < NWV; ++v) slow = slow || wcnt[v] == 0xffffffffu;
+    }
+
+    uint32_t prefix = bin0 << 24, himask = 0xff000000u;
+    if (!slow) {
+        // 4. Digit passes over the lists (one barrier each).
         for (int pass = 0; pass < 3; ++pass) {
             const int shift = 16 - 8 * pass;
-            for (uint32_t i = threadIdx.x; i < ncand; i += NT) {
-                const uint32_t kc = cand[i];
-                if ((kc & himask) == prefix) atomicAdd(&hist3[pass][(kc >> shift) & 255u], 1u);
+            if (pass > 0) {
+                for (uint32_t i = lane; i < nl; i += kWave) {
+                    const uint32_t kc = cand[wv][i].x;
+                    if ((kc & himask) == prefix) atomicAdd(&hist3[pass][(kc >> shift) & 255u], 1u);
+                }
+                if (threadIdx.x < 256) hist3[(pass + 1) % 3][threadIdx.x] = 0u;
+                __syncthreads();
             }
-            if (threadIdx.x < 256) hist3[(pass + 1) % 3][threadIdx.x] = 0u;
-            __syncthreads();
             uint32_t b, r;
             find_bin_wave(hist3[pass], remaining, b, r);
             prefix |= b << shift;
             himask |= 0xffu << shift;
             remaining = r;
         }
-    } else {
-        for (int shift = 16; shift >= 0; shift -= 8) {
-            if (threadIdx.x < 256) hist[threadIdx.x] = 0u;
-            __syncthreads();
-#pragma unroll UNR
-            for (int j = 0; j < KPT; ++j) {
-                const int pos = key_pos(j);
-                const uint32_t kj = RT_KEY(j);
-                if (pos < n && (kj & himask) == prefix)
-                    atomicAdd(&hist[(kj >> shift) & 255u], 1u);
-            }
-            __syncthreads();
-            if (wv == 0) find_bin(hist, 1, 0, remaining, &sel_bin, &sel_rem);
-            __syncthreads();
-            prefix |= sel_bin << shift;
-            himask |= 0xffu << shift;
-            remaining = sel_rem;
+        // 5. Members from the lists: counts per wave, then position-ordered writes.
+        const uint32_t T = prefix, need_eq = remaining;
+        uint32_t gtc = 0u, eqc = 0u;
+        for (uint32_t base = 0; base < nl; base += kWave) {
+            const uint32_t i = base + lane;
+            const uint32_t kc = i < nl ? cand[wv][i].x : 0u;
+            gtc += (uint32_t)__popcll(__ballot(i < nl && kc > T));
+            eqc += (uint32_t)__popcll(__ballot(i < nl && kc == T));
         }
+        if (lane == 0) {
+            wgt[wv] = gtc;
+            weq[wv] = eqc;
+        }
+        __syncthreads();
+        uint32_t eq_before = 0u, sel_before = 0u;
+        for (int v = 0; v < wv; ++v) {
+            const uint32_t take = (need_eq > eq_before) ? min(need_eq - eq_before, weq[v]) : 0u;
+            sel_before += wgt[v] + take;
+            eq_before += weq[v];
+        }
+        for (uint32_t base = 0; base < nl; base += kWave) {
+            const uint32_t i = base + lane;
+            const uint2 e = i < nl ? cand[wv][i] : make_uint2(0u, 0u);
+            const bool gt = i < nl && e.x > T, eq = i < nl && e.x == T;
+            const uint64_t eb = __ballot(eq);
+            const bool sel = gt || (eq && eq_before + (uint32_t)lanes_below(eb) < need_eq);
+            const uint64_t sb = __ballot(sel);
+            const uint32_t slot = sel_before + (uint32_t)lanes_below(sb);
+            if (sel && slot < (uint32_t)w && e.y < (uint32_t)n) {
+                out[slot] = (int32_t)e.y;
+                if (mrow != nullptr) atomicOr(mrow + (long)e.y * KW, cbit);
+            }
+            eq_before += (uint32_t)__popcll(eb);
+            sel_before += (uint32_t)__popcll(sb);
+        }
+        return;
     }
-    const uint32_t T = prefix, need_eq = remaining;
 
-    // Position-ordered compaction: wave wv's positions are visited in
-    // ascending order (groups jg, then lanes, then the VEC keys of a lane).
-    uint32_t gtc = 0u, eqc = 0u;
-#pragma unroll UNR
-    for (int j = 0; j < KPT; ++j) {
-        const int pos = key_pos(j);
-        const bool valid = pos < n;
-        const uint32_t kj = RT_KEY(j);
-        gtc += (valid && kj > T) ? 1u : 0u;
-        eqc += (valid && kj == T) ? 1u : 0u;
+    // Over all keys: the remaining digits (all four when bin0 is unknown) ...
+    // fn(j, key j) for every key of this lane, in order; (TOPB) re-read from
+    // the score row sixteen at a time
+    auto for_keys = [&](auto&& fn) {
+        if constexpr (!TOPB) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) {
+                fn(j, key[TOPB ? 0 : j]);
+                if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);   // few ballots live
+            }
+        } else {
+#pragma unroll 1
+            for (int j0 = 0; j0 < KPT; j0 += 16) {
+                uint32_t kk[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int p = pl + kWave * (j0 + u);
+                    const uint32_t kj = order_key(
+                        __uint_as_float(buffer_load4(srs, p < n ? 4u * (uint32_t)p : kOutOfRange)));
+                    kk[u] = p < n ? kj : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    fn(j0 + u, kk[u]);
+                    if (u % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    };
+    if (!found) {
+        prefix = 0u;
+        himask = 0u;
+        remaining = (uint32_t)w;
     }
-    gtc = wave_sum_u32(gtc);
-    eqc = wave_sum_u32(eqc);
+    if (threadIdx.x < 256) hist3[0][threadIdx.x] = 0u;
+    __syncthreads();
+    for (int shift = found ? 16 : 24, it = 0; shift >= 0; shift -= 8, ++it) {
+        uint32_t* h = hist3[it % 3];
+        for_keys([&](int, uint32_t kj) {
+            if ((kj & himask) == prefix) atomicAdd(&h[(kj >> shift) & 255u], 1u);
+        });
+        if (threadIdx.x < 256) hist3[(it + 1) % 3][threadIdx.x] = 0u;
+        __syncthreads();
+        uint32_t b, r;
+        find_bin_wave(h, remaining, b, r);
+        prefix |= b << shift;
+        himask |= 0xffu << shift;
+        remaining = r;
+    }
+    // ... and the members, in position order, from the keys.
+    const uint32_t T = prefix, need_eq = remaining;
+    uint32_t gtc = 0u, eqc = 0u;
+    for_keys([&](int, uint32_t kj) {
+        gtc += kj > T ? 1u : 0u;
+        eqc += kj == T ? 1u : 0u;
+    });
+    gtc = wave_reduce_u32<false>(gtc);
+    eqc = wave_reduce_u32<false>(eqc);
     if (lane == 0) {
         wgt[wv] = gtc;
         weq[wv] = eqc;
@@ -533,51 +617,23 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         sel_before += wgt[v] + take;
         eq_before += weq[v];
     }
-    int32_t* out = idx + row * w;
-    const long bh = row / k;
-    const int c = (int)(row % k);
-#pragma unroll UNRG
-    for (int jg = 0; jg < KPT / VEC; ++jg) {
-        // positions of group jg in ascending order: (lane, e) lexicographic
-        bool gt[VEC], eq[VEC], sel[VEC];
-        uint64_t eb[VEC], sb[VEC];
-        uint32_t eq_lanes = 0u, sel_lanes = 0u;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int j = VEC * jg + e;
-            const bool valid = key_pos(j) < n;
-            const uint32_t kj = RT_KEY(j);
-            gt[e] = valid && kj > T;
-            eq[e] = valid && kj == T;
-            eb[e] = __ballot(eq[e]);
-            eq_lanes += (uint32_t)lanes_below(eb[e]);
+    // (a copy of T the compiler cannot identify with it: the comparisons
+    // above are not kept alive, as scalar masks, until here)
+    const uint32_t T2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)T);
+    for_keys([&](int j, uint32_t kj) {
+        const int p = pl + kWave * j;
+        const bool eq = kj == T2;
+        const uint64_t eb = __ballot(eq);
+        const bool sel = kj > T2 || (eq && eq_before + (uint32_t)lanes_below(eb) < need_eq);
+        const uint64_t sb = __ballot(sel);
+        const uint32_t slot = sel_before + (uint32_t)lanes_below(sb);
+        if (sel && slot < (uint32_t)w && p < n) {
+            out[slot] = p;
+            if (mrow != nullptr) atomicOr(mrow + (long)p * KW, cbit);
         }
-        uint32_t own = 0u;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            sel[e] = gt[e] || (eq[e] && eq_before + eq_lanes + own < need_eq);
-            own += eq[e] ? 1u : 0u;
-            sb[e] = __ballot(sel[e]);
-            sel_lanes += (uint32_t)lanes_below(sb[e]);
-        }
-        own = 0u;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const uint32_t slot = sel_before + sel_lanes + own;
-            if (sel[e] && slot < (uint32_t)w) {
-                const int pos = key_pos(VEC * jg + e);
-                out[slot] = pos;
-                if (mask != nullptr)
-                    atomicOr(&mask[(bh * n + pos) * KW + (c >> 5)], 1u << (c & 31));
-            }
-            own += sel[e] ? 1u : 0u;
-        }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            eq_before += (uint32_t)__popcll(eb[e]);
-            sel_before += (uint32_t)__popcll(sb[e]);
-        }
-    }
+        eq_before += (uint32_t)__popcll(eb);
+        sel_before += (uint32_t)__popcll(sb);
+    });
 }
 
 template <int D>
@@ -594,12 +650,10 @@ void launch_score_d(const void* qk, int dtype, const float* mu, int BH, int H, i
     }
 }
 
-#undef RT_KEY
-
-template <int NT, int KPT, bool LDSK = false>
+template <int NT, int KPT, bool TOPB = false>
 void launch_topw_k(const float* scores, int rows, int n, int w, int32_t* idx, int k,
                    uint32_t* mask, hipStream_t s) {
-    hipLaunchKernelGGL((topw_kernel<NT, KPT, LDSK>), dim3(rows), dim3(NT), 0, s, scores, n, w, idx,
+    hipLaunchKernelGGL((topw_kernel<NT, KPT, TOPB>), dim3(rows), dim3(NT), 0, s, scores, n, w, idx,
                        k, mask, mask_words(k));
 }
 
@@ -621,15 +675,15 @@ hipError_t launch_score(const void* qk, int dtype, const float* mu, int B, int H
 hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t* idx,
                        uint32_t* mask, hipStream_t s) {
     const int rows = BH * k;
-    const int per = (n + 511) / 512;
-    if (per <= 1) launch_topw_k<512, 1>(scores, rows, n, w, idx, k, mask, s);
-    else if (per <= 2) launch_topw_k<512, 2>(scores, rows, n, w, idx, k, mask, s);
-    else if (per <= 4) launch_topw_k<512, 4>(scores, rows, n, w, idx, k, mask, s);
-    else if (per <= 8) launch_topw_k<512, 8>(scores, rows, n, w, idx, k, mask, s);
-    else if (per <= 16) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
-    else if (per <= 32) launch_topw_k<512, 32>(scores, rows, n, w, idx, k, mask, s);
-    else if (per <= 64) launch_topw_k<1024, 32, true>(scores, rows, n, w, idx, k, mask, s);
-    else launch_topw_k<1024, 64>(scores, rows, n, w, idx, k, mask, s);
+    if (n <= 256) launch_topw_k<256, 1>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 512) launch_topw_k<256, 2>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 1024) launch_topw_k<256, 4>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 2048) launch_topw_k<256, 8>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 4096) launch_topw_k<256, 16>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 8192) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 16384) launch_topw_k<512, 32>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 32768) launch_topw_k<1024, 32>(scores, rows, n, w, idx, k, mask, s);
+    else launch_topw_k<1024, 64, true>(scores, rows, n, w, idx, k, mask, s);
     return hipGetLastError();
 }
 

@@ -264,6 +264,53 @@ def test_sweep_long_rows(rt, orc, n, k):
     say(f"[sweep] n={n}: {int(res['differs'].sum())} near-tie clusters differ")
 
 
+# Selection paths of the top-w kernel, for each place its keys live (registers
+# up to n = 16K, LDS up to 32K, 16-bit prefixes in LDS beyond): exact ties
+# (tokens drawn from a pool of 97 vectors), a threshold deep in a crowded top
+# byte (tokens close to one direction: more candidates than the short list
+# holds), and a threshold below the four highest top bytes (w = n/2).
+TOPW_PATHS = {"ties": (97, None), "crowded": (None, 0.01), "median": (None, None)}
+
+
+@pytest.mark.parametrize("n", [3000, 20000, 40000, 65536])
+@pytest.mark.parametrize("kind", list(TOPW_PATHS))
+def test_topw_selection_paths(rt, orc, n, kind):
+    say(f"[topw] n={n} kind={kind}")
+    cid = 88 + list(TOPW_PATHS).index(kind)
+    d, k, H = 64, 2, 1
+    pool, spread = TOPW_PATHS[kind]
+    if pool is not None:
+        base_rows = S.normal(1000 * cid + 1, (pool, d))
+        val = base_rows[np.arange(n) % pool]
+    elif spread is not None:
+        centre = S.normal(1000 * cid + 1, (1, d))
+        val = centre + spread * S.normal(1000 * cid + 2, (n, d))
+    else:
+        val = S.normal(1000 * cid + 1, (n, d))
+    qk_t = S.rounded(val.reshape(1, H, n, d), "bf16")
+    mu_val = S.unit_rows_f32(1000 * cid + 3, H * k, d).reshape(H, k, d)
+    w = n // 2 if kind == "median" else min(n // k, 1024)
+    qk = dev_tensor(qk_t)
+    mu = dev_tensor(mu_val)
+    inv, idx, mask = rt.route(qk, mu, w, want_mask=True)
+    torch.cuda.synchronize()
+    _, idx_o, margin_o, _ = orc.route(qk_t.value, mu_val, w)
+    gidx = host(idx)
+    check_membership(orc, gidx, idx_o, margin_o, qk_t.value, mu_val, w)
+    assert_mask_matches(host(mask), gidx, n)
+    if kind == "ties":
+        # equal scores are taken in position order: the chosen set is the
+        # lowest positions among the tokens tied at the threshold
+        for c in range(k):
+            xhat, _ = orc.normalize(qk_t.value[0, 0])
+            s = orc.scores(xhat, mu_val[0, c:c + 1])[0]
+            row = gidx[0, 0, c]
+            thr = s[row].min()
+            tied = np.flatnonzero(s == thr)
+            taken = np.intersect1d(row, tied)
+            assert np.array_equal(taken, tied[:len(taken)])
+
+
 # Full-size workloads, in the launch configuration the benchmark times.
 @pytest.mark.parametrize("name", ["routed", "mixed", "long", "stress"])
 def test_full_size_forward(rt, orc, name):
