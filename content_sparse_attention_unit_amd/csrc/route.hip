@@ -681,8 +681,9 @@ hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t
     else if (n <= 2048) launch_topw_k<256, 8>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 4096) launch_topw_k<256, 16>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 8192) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
-    else if (n <= 16384) launch_topw_k<512, 32>(scores, rows, n, w, idx, k, mask, s);
-    else if (n <= 32768) launch_topw_k<1024, 32>(scores, rows, n, w, idx, k, mask, s);
+    // beyond 8K keys a row, top bytes only: fewer registers, two rows a CU
+    else if (n <= 16384) launch_topw_k<512, 32, true>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 32768) launch_topw_k<1024, 32, true>(scores, rows, n, w, idx, k, mask, s);
     else launch_topw_k<1024, 64, true>(scores, rows, n, w, idx, k, mask, s);
     return hipGetLastError();
 }
