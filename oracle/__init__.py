@@ -26,7 +26,8 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile rt_oracle.c with the host C compiler (no HIP anywhere)."""
-    if force or not os.path.exists(_LIB):
+    stale = (not os.path.exists(_LIB)) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC,
                                "-lm", "-lpthread"])
@@ -139,6 +140,34 @@ def routed_attn_bwd(q, kk, v, idx, dout, scale: float, causal: bool = True,
                                 ctypes.c_int(int(causal)), _p(dq), _p(dk), _p(dv),
                                 ctypes.c_int(nthreads or default_threads()))
     return dq, dk, dv
+
+
+def local_attn_bwd(q, kk, v, dout, window: int, scale: float, causal: bool = True,
+                   nthreads: int | None = None):
+    """O9: gradients of O7 w.r.t. q, k and v for [B,H,n,d] tensors."""
+    lib = _load()
+    q, kk, v, dout = _f64(q), _f64(kk), _f64(v), _f64(dout)
+    B, H, n, d = q.shape
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    lib.orc_local_attn_bwd_all(_p(q), _p(kk), _p(v), _p(dout), ctypes.c_int(B), ctypes.c_int(H),
+                               ctypes.c_long(n), ctypes.c_int(d), ctypes.c_long(window),
+                               ctypes.c_double(scale), ctypes.c_int(int(causal)), _p(dq), _p(dk),
+                               _p(dv), ctypes.c_int(nthreads or default_threads()))
+    return dq, dk, dv
+
+
+def normalize_bwd(x, g):
+    """Gradient of O1 along the last axis: for x^ = x / r with r = max(||x||,
+    1e-12) and the upstream gradient g of x^, dx = (g - x^ <x^, g>) / r while
+    ||x|| >= 1e-12 (the Jacobian of x / ||x|| is (I - x^ x^T) / ||x||), and
+    dx = g / 1e-12 where the clamp holds r constant."""
+    x, g = _f64(x), _f64(g)
+    nrm = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+    clamped = nrm < 1e-12
+    r = np.where(clamped, 1e-12, nrm)
+    xhat = x / r
+    along = (xhat * g).sum(axis=-1, keepdims=True)
+    return np.where(clamped, g / r, (g - xhat * along) / r)
 
 
 def normalize(x):
@@ -254,3 +283,88 @@ def layer_forward(x, w_in, w_o, mu, R: int, L: int, d: int, w: int, window: int,
     y = out_proj(o_r, o_l, w_o, x)
     return {"qk": qk, "v": v, "q_l": ql, "k_l": kl, "v_l": vl, "idx": idx, "margin": margin,
             "o_r": o_r, "o_l": o_l, "mu": mu_new, "y": y}
+
+
+# ---- the layer's backward -------------------------------------------------------------
+# Gradients of one stack layer for an upstream gradient dy of y, with the routing
+# (the membership) held fixed and the bfloat16 storage roundings of the forward
+# taken as the identity.  Where the library stores a value in bfloat16 (the
+# gradient of the attention outputs) or feeds a gradient to a bf16 matrix
+# product (the gradients of the projected heads), the oracle rounds at the same
+# point (rounding=True); rounding=False gives the exact gradient of the exact
+# (unrounded) layer, which the finite-difference pins check.
+
+def _heads_to_rows(parts):
+    """[B,H_s,n,d] tensors -> [B*n, sum(H_s)*d] (heads concatenated per token)."""
+    cat = np.concatenate([_f64(t) for t in parts], axis=1)
+    B, H, n, d = cat.shape
+    return cat.transpose(0, 2, 1, 3).reshape(B * n, H * d)
+
+
+def _rows_to_heads(y, B, n, hs, d):
+    """[B*n, sum(hs)*d] -> list of [B,h,n,d] tensors."""
+    heads = y.reshape(B, n, sum(hs), d).transpose(0, 2, 1, 3)
+    out, h0 = [], 0
+    for h in hs:
+        out.append(np.ascontiguousarray(heads[:, h0:h0 + h]))
+        h0 += h
+    return out
+
+
+def out_proj_bwd(dy, o_r, o_l, w_o, rounding: bool = True):
+    """Gradients of y = x + [o_r | o_l] W_o^T: returns (do_r, do_l, dw_o); the
+    gradient w.r.t. x is dy itself.  do = dy W_o (rounded to bfloat16 when the
+    library stores it so), dw_o = dy^T [o_r | o_l]."""
+    dy = _f64(dy)
+    B, n, dm = dy.shape
+    parts = [o_r] if o_l is None else [o_r, o_l]
+    hs = [p.shape[1] for p in parts]
+    d = o_r.shape[3]
+    rows = dy.reshape(B * n, dm)
+    do = rows @ _f64(w_o)
+    if rounding:
+        do = round_bf16(do)
+    dw_o = rows.T @ _heads_to_rows(parts)
+    outs = _rows_to_heads(do, B, n, hs, d)
+    return outs[0], (outs[1] if o_l is not None else None), dw_o
+
+
+def in_proj_bwd(x, w_in, dqk, dv, dq_l, dk_l, dv_l, dy=None, rounding: bool = True):
+    """Gradients of [qk | v | q_l | k_l | v_l] = x W_in^T for the heads'
+    gradients (each [B,H_s,n,d]; the local ones None when there are no local
+    heads): dx = dC W_in (+ dy, the residual's gradient), dw_in = dC^T x, with
+    dC the heads' gradients as token rows (rounded to bfloat16, the products'
+    operand precision, when rounding)."""
+    x = _f64(x)
+    B, n, dm = x.shape
+    parts = [dqk, dv] + ([dq_l, dk_l, dv_l] if dq_l is not None else [])
+    dc = _heads_to_rows(parts)
+    if rounding:
+        dc = round_bf16(dc)
+    dx = dc @ _f64(w_in)
+    if dy is not None:
+        dx = dx + _f64(dy).reshape(B * n, dm)
+    dw_in = dc.T @ x.reshape(B * n, dm)
+    return dx.reshape(B, n, dm), dw_in
+
+
+def layer_backward(x, w_in, w_o, fwd: dict, dy, R: int, L: int, d: int, window: int,
+                   scale: float | None = None, rounding: bool = True,
+                   nthreads: int | None = None):
+    """Backward of layer_forward (its result dict `fwd`) for the upstream
+    gradient dy: out_proj_bwd -> O8 on the routed heads and O9 on the local
+    heads -> the normalisation's gradient (q and k share qk, so their two
+    gradients add) -> in_proj_bwd.  Returns dx, dw_in, dw_o and the
+    intermediate gradients."""
+    sc = (1.0 / np.sqrt(d)) if scale is None else scale
+    do_r, do_l, dw_o = out_proj_bwd(dy, fwd["o_r"], fwd["o_l"], w_o, rounding)
+    qk = fwd["qk"]
+    dqh, dkh, dv = routed_attn_bwd(qk, qk, fwd["v"], fwd["idx"], do_r, sc, True, nthreads)
+    dqk = normalize_bwd(qk, dqh + dkh)
+    dq_l = dk_l = dv_l = None
+    if L > 0:
+        dq_l, dk_l, dv_l = local_attn_bwd(fwd["q_l"], fwd["k_l"], fwd["v_l"], do_l, window, sc,
+                                          True, nthreads)
+    dx, dw_in = in_proj_bwd(x, w_in, dqk, dv, dq_l, dk_l, dv_l, dy, rounding)
+    return {"do_r": do_r, "do_l": do_l, "dw_o": dw_o, "dq_hat": dqh, "dk_hat": dkh, "dv": dv,
+            "dqk": dqk, "dq_l": dq_l, "dk_l": dk_l, "dv_l": dv_l, "dx": dx, "dw_in": dw_in}

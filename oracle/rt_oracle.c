@@ -32,6 +32,7 @@
  *                  positions (self included)                 abstract; summary §6
  *   O8 backward    gradients of O4+O5 w.r.t. q^, k^, v (routing and the
  *                  normalisation are held fixed)
+ *   O9 local bwd   gradients of O7 w.r.t. q, k, v
  *
  * Every function is sequential over its unit; the *_all drivers only hand
  * independent (batch, head) units to worker threads.
@@ -321,6 +322,62 @@ void orc_attend_bwd(const double *qhat, const double *khat, const double *v, con
     free(dP);
 }
 
+/* ---------------------------------------------------------------- O9 ---- */
+/* Backward of O7 for the output gradients dout: with P the softmax row of
+ * query i over its window, dV[j] += P[i][j] dO[i], dP[i][j] = <dO[i], v[j]>,
+ * dl[i][j] = P[i][j] (dP[i][j] - sum_j' P[i][j'] dP[i][j']), and the logit
+ * gradient goes back through the scaled product: dQ[i] += scale dl k[j],
+ * dK[j] += scale dl q[i].  Outputs are zeroed here. */
+void orc_local_bwd(const double *q, const double *kk, const double *v, const double *dout, long n,
+                   int d, long window, double scale, int causal, double *dq, double *dk, double *dv)
+{
+    memset(dq, 0, sizeof(double) * (size_t)n * (size_t)d);
+    memset(dk, 0, sizeof(double) * (size_t)n * (size_t)d);
+    memset(dv, 0, sizeof(double) * (size_t)n * (size_t)d);
+    double *P = (double *)malloc(sizeof(double) * (size_t)(2 * window + 1));
+    double *dP = (double *)malloc(sizeof(double) * (size_t)(2 * window + 1));
+    for (long i = 0; i < n; ++i) {
+        long lo = i - window + 1;
+        if (lo < 0)
+            lo = 0;
+        long hi = causal ? i : i + window - 1;
+        if (hi > n - 1)
+            hi = n - 1;
+        double m = -INFINITY;
+        for (long j = lo; j <= hi; ++j) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += q[i * d + e] * kk[j * d + e];
+            P[j - lo] = scale * dot;
+            if (P[j - lo] > m)
+                m = P[j - lo];
+        }
+        double z = 0.0;
+        for (long j = lo; j <= hi; ++j)
+            z += exp(P[j - lo] - m);
+        double D = 0.0;
+        for (long j = lo; j <= hi; ++j) {
+            P[j - lo] = exp(P[j - lo] - m) / z;
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e) {
+                dot += dout[i * d + e] * v[j * d + e];
+                dv[j * d + e] += P[j - lo] * dout[i * d + e];
+            }
+            dP[j - lo] = dot;
+            D += P[j - lo] * dot;
+        }
+        for (long j = lo; j <= hi; ++j) {
+            double dl = P[j - lo] * (dP[j - lo] - D);
+            for (int e = 0; e < d; ++e) {
+                dq[i * d + e] += scale * dl * kk[j * d + e];
+                dk[j * d + e] += scale * dl * q[i * d + e];
+            }
+        }
+    }
+    free(P);
+    free(dP);
+}
+
 /* ------------------------------------------------ whole-tensor drivers ---- */
 /* Tensors are contiguous row-major [B][H][n][d] (qk, v, out), [H][k][d] (mu),
  * [B][H][n] (inv_norm), [B][H][k][w] (idx, lse), [B][H][k] (margin),
@@ -531,4 +588,29 @@ void orc_routed_attn_bwd_all(const double *q, const double *kk, const double *v,
 {
     bwd_args a = {q, kk, v, dout, idx, n, w, d, k, causal, scale, dq, dk, dv};
     parallel_units(bwd_unit, &a, (long)B * H, nthreads);
+}
+
+typedef struct {
+    const double *q, *kk, *v, *dout;
+    long n, window;
+    int d, causal;
+    double scale;
+    double *dq, *dk, *dv;
+} local_bwd_args;
+
+static void local_bwd_unit(void *p, long u)
+{
+    local_bwd_args *a = (local_bwd_args *)p;
+    long off = u * a->n * a->d;
+    orc_local_bwd(a->q + off, a->kk + off, a->v + off, a->dout + off, a->n, a->d, a->window,
+                  a->scale, a->causal, a->dq + off, a->dk + off, a->dv + off);
+}
+
+/* O9 for every (b, h). */
+void orc_local_attn_bwd_all(const double *q, const double *kk, const double *v, const double *dout,
+                            int B, int H, long n, int d, long window, double scale, int causal,
+                            double *dq, double *dk, double *dv, int nthreads)
+{
+    local_bwd_args a = {q, kk, v, dout, n, window, d, causal, scale, dq, dk, dv};
+    parallel_units(local_bwd_unit, &a, (long)B * H, nthreads);
 }

@@ -459,3 +459,147 @@ def test_layer_forward_composition_and_zero_output_map(orc):
     np.testing.assert_allclose(res["mu"], orc.centroid_update(mu, qk, qk, res["idx"], 0.9),
                                rtol=0, atol=1e-12)
     assert res["o_r"].shape == (B, R, n, d) and res["o_l"].shape == (B, L, n, d)
+
+
+# ---- the layer's backward (O9, the normalisation, the projections) ----------------------
+
+def _band(n, window, causal):
+    i = np.arange(n)
+    if causal:
+        return (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - window)
+    return np.abs(i[None, :] - i[:, None]) < window
+
+
+@pytest.mark.parametrize("n,window,causal", [(30, 7, True), (12, 12, True), (25, 1, True),
+                                             (20, 4, False)])
+def test_p13_local_bwd_matches_autograd_banded(orc, n, window, causal):
+    """O9 against torch autograd (float64) of SDPA with the same band."""
+    r = _rng(30)
+    q, kk, v, g = (r.standard_normal((2, 2, n, 6)) for _ in range(4))
+    dq, dk, dv = orc.local_attn_bwd(q, kk, v, g, window, 0.8, causal)
+    t = [torch.from_numpy(a.copy()).requires_grad_() for a in (q, kk, v)]
+    o = F.scaled_dot_product_attention(*t, attn_mask=torch.from_numpy(_band(n, window, causal)),
+                                       scale=0.8)
+    o.backward(torch.from_numpy(g))
+    for got, ref in zip((dq, dk, dv), t):
+        np.testing.assert_allclose(got, ref.grad.numpy(), atol=1e-11)
+
+
+def test_local_bwd_finite_differences(orc):
+    """Central differences of <g, local_attn(q, k, v)>, brute force."""
+    r = _rng(31)
+    n, d, window = 9, 3, 4
+    q, kk, v, g = (r.standard_normal((1, 1, n, d)) for _ in range(4))
+    grads = orc.local_attn_bwd(q, kk, v, g, window, 1.2, True)
+    h = 1e-6
+    for which in range(3):
+        num = np.zeros_like(q)
+        for t in range(n):
+            for i in range(d):
+                a = [q.copy(), kk.copy(), v.copy()]
+                b = [q.copy(), kk.copy(), v.copy()]
+                a[which][0, 0, t, i] += h
+                b[which][0, 0, t, i] -= h
+                num[0, 0, t, i] = ((orc.local_attn(*a, window, 1.2, True) * g).sum()
+                                   - (orc.local_attn(*b, window, 1.2, True) * g).sum()) / (2 * h)
+        np.testing.assert_allclose(grads[which], num, rtol=1e-6, atol=1e-8)
+
+
+def test_normalize_bwd_matches_autograd_and_clamp(orc):
+    r = _rng(32)
+    x = r.standard_normal((3, 5, 7))
+    x[1, 2] = 0.0                                      # clamped row: r = 1e-12 is constant
+    g = r.standard_normal(x.shape)
+    tx = torch.from_numpy(x.copy()).requires_grad_()
+    nrm = torch.clamp(torch.linalg.vector_norm(tx, dim=-1, keepdim=True), min=1e-12)
+    (tx / nrm).backward(torch.from_numpy(g))
+    got = orc.normalize_bwd(x, g)
+    np.testing.assert_allclose(got, tx.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(got[1, 2], g[1, 2] / 1e-12)
+    # the gradient is orthogonal to x (scaling x does not change x^)
+    keep = np.ones(x.shape[:-1], bool)
+    keep[1, 2] = False
+    assert np.abs((got * x).sum(-1)[keep]).max() < 1e-12
+
+
+def test_proj_bwd_matches_autograd(orc):
+    """Both projections' gradients (rounding=False) against torch autograd of
+    the exact linear maps, including the residual's gradient."""
+    r = _rng(33)
+    B, n, d, R, L = 2, 3, 4, 2, 1
+    dm = 10
+    x = r.standard_normal((B, n, dm))
+    w_in = r.standard_normal(((2 * R + 3 * L) * d, dm))
+    w_o = r.standard_normal((dm, (R + L) * d))
+    o_r, o_l = r.standard_normal((B, R, n, d)), r.standard_normal((B, L, n, d))
+    dy = r.standard_normal((B, n, dm))
+    tr, tl, tw = (torch.from_numpy(a.copy()).requires_grad_() for a in (o_r, o_l, w_o))
+    cat = torch.cat([tr, tl], 1).permute(0, 2, 1, 3).reshape(B, n, -1)
+    (cat @ tw.T).backward(torch.from_numpy(dy))
+    do_r, do_l, dw_o = orc.out_proj_bwd(dy, o_r, o_l, w_o, rounding=False)
+    np.testing.assert_allclose(do_r, tr.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(do_l, tl.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dw_o, tw.grad.numpy(), atol=1e-12)
+    gh = [r.standard_normal((B, h, n, d)) for h in (R, R, L, L, L)]
+    tx, twi = (torch.from_numpy(a.copy()).requires_grad_() for a in (x, w_in))
+    y = (tx @ twi.T).reshape(B, n, 2 * R + 3 * L, d).permute(0, 2, 1, 3)
+    g = torch.from_numpy(np.concatenate(gh, axis=1))
+    ((y * g).sum() + (tx * torch.from_numpy(dy)).sum()).backward()
+    dx, dw_in = orc.in_proj_bwd(x, w_in, *gh, dy=dy, rounding=False)
+    np.testing.assert_allclose(dx, tx.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dw_in, twi.grad.numpy(), atol=1e-12)
+    # rounding=True rounds the heads' gradients (the products' operands) only
+    dx_r, _ = orc.in_proj_bwd(x, w_in, *[orc.round_bf16(a) for a in gh], rounding=True)
+    dx_e, _ = orc.in_proj_bwd(x, w_in, *[orc.round_bf16(a) for a in gh], rounding=False)
+    np.testing.assert_array_equal(dx_r, dx_e)
+
+
+def test_layer_backward_matches_autograd(orc):
+    """The whole layer (fixed membership, no storage rounding) in torch float64:
+    projections, normalised shared q/k, per-cluster causal attention scattered
+    back, banded local attention; autograd of <dy, y> against layer_backward."""
+    r = _rng(34)
+    B, n, dm, d, R, L, k, w, window = 1, 24, 12, 4, 1, 1, 3, 9, 5
+    sc = 0.7
+    x = r.standard_normal((B, n, dm))
+    w_in = r.standard_normal(((2 * R + 3 * L) * d, dm)) / 3
+    w_o = r.standard_normal((dm, (R + L) * d)) / 3
+    mu = r.standard_normal((R, k, d))
+    dy = r.standard_normal((B, n, dm))
+    heads = (x.reshape(B * n, dm) @ w_in.T).reshape(B, n, 2 * R + 3 * L, d).transpose(0, 2, 1, 3)
+    qk, v = heads[:, :R].copy(), heads[:, R:2 * R].copy()
+    ql, kl, vl = heads[:, 2 * R:2 * R + L].copy(), heads[:, 2 * R + L:2 * R + 2 * L].copy(), \
+        heads[:, 2 * R + 2 * L:].copy()
+    _, idx, _, _ = orc.route(qk, mu, w)
+    o_r, _, _ = orc.routed_attn(qk, qk, v, idx, sc, True, True)
+    o_l = orc.local_attn(ql, kl, vl, window, sc, True)
+    fwd = {"qk": qk, "v": v, "q_l": ql, "k_l": kl, "v_l": vl, "idx": idx, "o_r": o_r, "o_l": o_l}
+    got = orc.layer_backward(x, w_in, w_o, fwd, dy, R, L, d, window, sc, rounding=False)
+
+    tx, twi, two = (torch.from_numpy(a.copy()).requires_grad_() for a in (x, w_in, w_o))
+    hh = (tx.reshape(B * n, dm) @ twi.T).reshape(B, n, 2 * R + 3 * L, d).permute(0, 2, 1, 3)
+    tqk, tv = hh[:, :R], hh[:, R:2 * R]
+    tq, tkl, tvl = hh[:, 2 * R:2 * R + L], hh[:, 2 * R + L:2 * R + 2 * L], hh[:, 2 * R + 2 * L:]
+    qn = tqk / torch.clamp(torch.linalg.vector_norm(tqk, dim=-1, keepdim=True), min=1e-12)
+    outs = []
+    for b in range(B):
+        for h in range(R):
+            acc = torch.zeros((n, d), dtype=torch.float64)
+            for c in range(k):
+                p = torch.from_numpy(idx[b, h, c].astype(np.int64))
+                qc, vc = qn[b, h][p], tv[b, h][p]
+                vis = p[None, :] <= p[:, None]
+                o = F.scaled_dot_product_attention(qc[None], qc[None], vc[None],
+                                                   attn_mask=vis[None], scale=sc)[0]
+                acc = acc.index_add(0, p, o)
+            outs.append(acc)
+    t_or = torch.stack(outs).reshape(B, R, n, d)
+    t_ol = F.scaled_dot_product_attention(tq, tkl, tvl,
+                                          attn_mask=torch.from_numpy(_band(n, window, True)),
+                                          scale=sc)
+    cat = torch.cat([t_or, t_ol], 1).permute(0, 2, 1, 3).reshape(B, n, -1)
+    y = tx + cat @ two.T
+    (y * torch.from_numpy(dy)).sum().backward()
+    np.testing.assert_allclose(got["dx"], tx.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(got["dw_in"], twi.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(got["dw_o"], two.grad.numpy(), atol=1e-10)
