@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
-           "routed_attn_bwd", "in_proj", "out_proj", "workspace_bytes", "library_path",
+           "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
+           "out_proj_bwd", "in_proj_bwd", "workspace_bytes", "library_path",
            "mask_words", "RTError", "RT_OP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -25,7 +26,7 @@ _lib = None
 
 RT_F32, RT_BF16 = 0, 1
 RT_OP = {"route": 0, "routed_attn": 1, "local_attn": 2, "centroid_update": 3,
-         "routed_attn_bwd": 4}
+         "routed_attn_bwd": 4, "local_attn_bwd": 5}
 _STATUS = {0: "RT_OK", 1: "RT_EINVAL", 2: "RT_EUNSUPPORTED", 3: "RT_EHIP"}
 
 
@@ -61,6 +62,10 @@ def _load():
         "rt_out_proj": [P, P, P, P, I, I, I, I, I, I, P, P],
         "rt_routed_attn_bwd": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z,
                                P],
+        "rt_local_attn_bwd": [P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z, P],
+        "rt_normalize_bwd": [P, I, P, P, P, ctypes.c_long, I, P, P],
+        "rt_out_proj_bwd": [P, P, P, P, I, I, I, I, I, I, P, P, P, P],
+        "rt_in_proj_bwd": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -302,4 +307,75 @@ def out_proj(o_r: torch.Tensor, o_l, w_o: torch.Tensor, x=None, out=None):
     _gpu(out)
     _check(lib.rt_out_proj(_ptr(o_r), _ptr(o_l), _ptr(w_o), _ptr(x), B, n, dm, d, R, L, _ptr(out),
                            _stream(dev)))
+    return out
+
+
+# ---- the layer's backward -------------------------------------------------------------
+
+def local_attn_bwd(q, kk, v, dout, window: int, *, scale=None, causal=True, out=None, ws=None):
+    """Gradients (dq, dk, dv), float32, of local_attn (bfloat16 inputs, d in
+    {64, 128}); ``out`` may hold three preallocated float32 [B,H,n,d] tensors."""
+    lib = _load()
+    dev = _gpu(q, kk, v, dout)
+    B, H, n, d = q.shape
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+    dq, dk, dv = out
+    _gpu(dq, dk, dv)
+    ws, _ = _workspace("local_attn_bwd", dev, B, H, n, d, 1, 1, ws)
+    _check(lib.rt_local_attn_bwd(_ptr(q), _ptr(kk), _ptr(v), _ptr(dout), _dtype_code(q), B, H, n,
+                                 d, int(window), sc, int(causal), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
+    return dq, dk, dv
+
+
+def normalize_bwd(x, inv_norm, g1, g2=None, out=None):
+    """dx (float32) through x^ = x / max(||x||, 1e-12) for the gradients g1 (+ g2)
+    of x^; x [..., d] as given to route, inv_norm from route."""
+    lib = _load()
+    dev = _gpu(x, inv_norm, g1, g2)
+    d = x.shape[-1]
+    rows = x.numel() // d
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    _gpu(out)
+    _check(lib.rt_normalize_bwd(_ptr(x), _dtype_code(x), _ptr(inv_norm), _ptr(g1), _ptr(g2), rows,
+                                d, _ptr(out), _stream(dev)))
+    return out
+
+
+def out_proj_bwd(dy, o_r, o_l, w_o, out=None):
+    """(do_r, do_l, dw_o) for y = x + [o_r | o_l] W_o^T: do_* bfloat16
+    head-major (do_l None when there are no local heads), dw_o float32."""
+    lib = _load()
+    dev = _gpu(dy, o_r, o_l, w_o)
+    B, R, n, d = o_r.shape
+    L = 0 if o_l is None else o_l.shape[1]
+    dm = w_o.shape[0]
+    if out is None:
+        out = (torch.empty((B, R, n, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((B, L, n, d), dtype=torch.bfloat16, device=dev) if L > 0 else None,
+               torch.empty((dm, (R + L) * d), dtype=torch.float32, device=dev))
+    _gpu(*out)
+    _check(lib.rt_out_proj_bwd(_ptr(dy), _ptr(o_r), _ptr(o_l), _ptr(w_o), B, n, dm, d, R, L,
+                               *(_ptr(t) for t in out), _stream(dev)))
+    return out
+
+
+def in_proj_bwd(x, w_in, dqk, dv, dq_l=None, dk_l=None, dv_l=None, dres=None, out=None):
+    """(dx, dw_in), float32, for [qk | v | q_l | k_l | v_l] = x W_in^T and the
+    heads' float32 gradients; dres (bfloat16 [B,n,dm] or None) is added to dx."""
+    lib = _load()
+    dev = _gpu(x, w_in, dqk, dv, dq_l, dk_l, dv_l, dres)
+    B, n, dm = x.shape
+    R, d = dqk.shape[1], dqk.shape[3]
+    L = 0 if dq_l is None else dq_l.shape[1]
+    if out is None:
+        out = (torch.empty((B, n, dm), dtype=torch.float32, device=dev),
+               torch.empty(((2 * R + 3 * L) * d, dm), dtype=torch.float32, device=dev))
+    _gpu(*out)
+    _check(lib.rt_in_proj_bwd(_ptr(x), _ptr(w_in), _ptr(dqk), _ptr(dv), _ptr(dq_l), _ptr(dk_l),
+                              _ptr(dv_l), _ptr(dres), B, n, dm, d, R, L, *(_ptr(t) for t in out),
+                              _stream(dev)))
     return out

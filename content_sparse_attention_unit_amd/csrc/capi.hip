@@ -102,6 +102,7 @@ size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
         case RT_OP_LOCAL_ATTN: return 0;
         case RT_OP_CENTROID_UPDATE: return 0;
         case RT_OP_ROUTED_ATTN_BWD: return rt::bwd_workspace_bytes(B * H, n, d, k, w);
+        case RT_OP_LOCAL_ATTN_BWD: return rt::local_bwd_workspace_bytes(B * H, n);
         default: return (size_t)-1;
     }
 }
@@ -368,6 +369,173 @@ rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int d
                                                static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)
         return fail(RT_EUNSUPPORTED, "%s: this configuration has no backward kernel", fn);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_local_attn_bwd(const void* q, const void* kk, const void* v, const void* dout,
+                            int dtype, int B, int H, int n, int d, int window, float scale,
+                            int causal, float* dq, float* dk, float* dv, void* ws,
+                            size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_local_attn_bwd";
+    g_err[0] = 0;
+    if (!q || !kk || !v || !dout || !dq || !dk || !dv)
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    {
+        const void* outs[3] = {dq, dk, dv};
+        const void* ins[4] = {q, kk, v, dout};
+        for (int i = 0; i < 3; ++i) {
+            for (int j = 0; j < 4; ++j)
+                if (outs[i] == ins[j]) return fail(RT_EINVAL, "%s: a gradient aliases an input", fn);
+            for (int j = i + 1; j < 3; ++j)
+                if (outs[i] == outs[j]) return fail(RT_EINVAL, "%s: gradients alias each other", fn);
+        }
+    }
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    if (window < 1) return fail(RT_EINVAL, "%s: window=%d must be >= 1", fn, window);
+    if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
+    if (dtype != RT_BF16 || (d != 64 && d != 128))
+        return fail(RT_EUNSUPPORTED, "%s: bf16 inputs with d in {64, 128} only", fn);
+    const size_t need = rt::local_bwd_workspace_bytes(B * H, n);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    hipError_t e = rt::launch_local_attn_bwd(q, kk, v, dout, B * H, n, d, window, scale, causal,
+                                             dq, dk, dv, ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_normalize_bwd(const void* x, int dtype, const float* inv_norm, const float* g1,
+                           const float* g2, long rows, int d, float* dx, void* stream) {
+    static const char* fn = "rt_normalize_bwd";
+    g_err[0] = 0;
+    if (!x || !inv_norm || !g1 || !dx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rows <= 0 || d <= 0) return fail(RT_EINVAL, "%s: rows=%ld and d=%d must be positive", fn,
+                                         rows, d);
+    if (dtype != RT_F32 && dtype != RT_BF16)
+        return fail(RT_EUNSUPPORTED, "%s: dtype %d is not RT_F32 or RT_BF16", fn, dtype);
+    if (!dim_ok(d)) return fail(RT_EUNSUPPORTED, "%s: d=%d not in {16,32,64,128}", fn, d);
+    if (dx == x || dx == static_cast<const void*>(inv_norm))
+        return fail(RT_EINVAL, "%s: dx aliases x or inv_norm", fn);
+    if (rows * (long)d >= (1L << 40)) return fail(RT_EUNSUPPORTED, "%s: rows*d too large", fn);
+    hipError_t e = rt::launch_norm_bwd(x, dtype, inv_norm, g1, g2, rows, d, dx,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_out_proj_bwd(const void* dy, const void* o_r, const void* o_l, const void* w_o,
+                          int B, int n, int dm, int d, int R, int L, void* do_r, void* do_l,
+                          float* dw_o, void* stream) {
+    static const char* fn = "rt_out_proj_bwd";
+    g_err[0] = 0;
+    if (!dy || !o_r || !w_o || !do_r || !dw_o || (L > 0 && (!o_l || !do_l)))
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_proj(fn, B, n, dm, d, R, L);
+    if (st != RT_OK) return st;
+    {
+        const void* outs[3] = {do_r, L > 0 ? do_l : nullptr, dw_o};
+        const void* ins[4] = {dy, o_r, o_l, w_o};
+        for (int i = 0; i < 3; ++i) {
+            if (outs[i] == nullptr) continue;
+            for (int j = 0; j < 4; ++j)
+                if (outs[i] == ins[j]) return fail(RT_EINVAL, "%s: an output aliases an input", fn);
+            for (int j = i + 1; j < 3; ++j)
+                if (outs[i] == outs[j]) return fail(RT_EINVAL, "%s: outputs alias each other", fn);
+        }
+    }
+    const int T = B * n, NO = (R + L) * d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rt::GemmArgs p{};
+    p.a.p[0] = dy;
+    p.a.ld = dm;
+    p.b.p[0] = w_o;
+    p.b.ld = NO;
+    p.c[0] = do_r;
+    p.c[1] = do_l;
+    p.hc[0] = R;
+    p.hc[1] = L;
+    p.M = T;
+    p.N = NO;
+    p.K = dm;
+    p.n = n;
+    p.d = d;
+    hipError_t e = rt::launch_gemm_bwd(rt::GEMM_DO, p, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    rt::GemmArgs q{};
+    q.a.p[0] = dy;
+    q.a.ld = dm;
+    q.b.p[0] = o_r;
+    q.b.p[1] = o_l;
+    q.b.hs[0] = R;
+    q.b.hs[1] = L;
+    q.c[0] = dw_o;
+    q.M = dm;
+    q.N = NO;
+    q.K = T;
+    q.n = n;
+    q.d = d;
+    e = rt::launch_gemm_bwd(rt::GEMM_DWO, q, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_in_proj_bwd(const void* x, const void* w_in, const float* dqk, const float* dv,
+                         const float* dq_l, const float* dk_l, const float* dv_l, const void* dres,
+                         int B, int n, int dm, int d, int R, int L, float* dx, float* dw_in,
+                         void* stream) {
+    static const char* fn = "rt_in_proj_bwd";
+    g_err[0] = 0;
+    if (!x || !w_in || !dqk || !dv || !dx || !dw_in || (L > 0 && (!dq_l || !dk_l || !dv_l)))
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_proj(fn, B, n, dm, d, R, L);
+    if (st != RT_OK) return st;
+    {
+        const void* outs[2] = {dx, dw_in};
+        const void* ins[8] = {x, w_in, dqk, dv, dq_l, dk_l, dv_l, dres};
+        if (dx == static_cast<const void*>(dw_in)) return fail(RT_EINVAL, "%s: outputs alias", fn);
+        for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 8; ++j)
+                if (ins[j] != nullptr && outs[i] == ins[j])
+                    return fail(RT_EINVAL, "%s: an output aliases an input", fn);
+    }
+    const int T = B * n, NC = (2 * R + 3 * L) * d;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rt::GemmOperand dc{};
+    dc.p[0] = dqk;
+    dc.p[1] = dv;
+    dc.p[2] = dq_l;
+    dc.p[3] = dk_l;
+    dc.p[4] = dv_l;
+    dc.hs[0] = dc.hs[1] = R;
+    dc.hs[2] = dc.hs[3] = dc.hs[4] = L;
+    rt::GemmArgs p{};
+    p.a = dc;
+    p.b.p[0] = w_in;
+    p.b.ld = dm;
+    p.c[0] = dx;
+    p.res = static_cast<const uint16_t*>(dres);
+    p.M = T;
+    p.N = dm;
+    p.K = NC;
+    p.n = n;
+    p.d = d;
+    hipError_t e = rt::launch_gemm_bwd(rt::GEMM_DX, p, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    rt::GemmArgs q{};
+    q.a = dc;
+    q.b.p[0] = x;
+    q.b.ld = dm;
+    q.c[0] = dw_in;
+    q.M = NC;
+    q.N = dm;
+    q.K = T;
+    q.n = n;
+    q.d = d;
+    e = rt::launch_gemm_bwd(rt::GEMM_DWIN, q, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

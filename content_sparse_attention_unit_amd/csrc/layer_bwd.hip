@@ -1,0 +1,286 @@
+// layer_bwd.hip -- gradients of the layer's projections and of the unit
+// normalisation of the routed heads (gfx950).
+//
+// The paperlayer.ai summary of "Efficient Content-Based Sparse Attention with
+// Routing Transformers" (§3) has a self-attention layer map its n input
+// vectors to queries, keys and values with learned linear maps, and (§4) use
+// queries and keys unit-normalised.  With [qk | v | q_l | k_l | v_l] = x W_in^T
+// and y = x + O W_o^T (O the heads' outputs, concatenated per token):
+//   dO = dy W_o,   dW_o = dy^T O,   dx = dy + dC W_in,   dW_in = dC^T x,
+// dC being the heads' input gradients; and for x^ = x / max(||x||, 1e-12),
+//   dx = (g - x^ <x^, g>) / ||x||   (g / 1e-12 where the clamp holds).
+//
+// gemm_kernel: C = A B^T over a contraction K for the four products above,
+// bf16 operands (float32 gradients are rounded to bf16 as they are staged),
+// float32 accumulation on v_mfma_f32_16x16x32_bf16.  Each operand X[idx][k]
+// lives in memory either k-contiguous (row-major rows of k) or
+// idx-contiguous (rows of idx for each k): the tile is copied to LDS in its
+// memory orientation, and the fragments come from plain 8-byte reads in the
+// first case and from transposing LDS reads (ds_read_b64_tr_b16) in the
+// second, both giving the same order of the contraction index, so no operand
+// is ever transposed in memory.  Operands can also be the head-major
+// [B][H][n][d] tensors of the attention heads (several segments, concatenated
+// over heads), so the layer needs no copies.  One workgroup = a 128 x 128
+// output tile (four waves of 64 x 64), K in steps of 64 through
+// double-buffered LDS tiles fed by register prefetch; each wave computes the
+// transposed product so a lane holds four consecutive output columns.
+//
+// norm_bwd_kernel: one wave per row, the row and its gradients in registers.
+#include "rt_common.hpp"
+#include "rt_internal.hpp"
+
+namespace rt {
+namespace {
+
+constexpr int GBM = 128, GBN = 128, GBK = 64;
+constexpr int GPLD = GBK + 8;      // k-contiguous tile: row stride (bf16)
+constexpr int GLDI = 128 + 16;     // idx-contiguous tile: row stride (bf16), an odd multiple of 16
+constexpr int GNT = 256;
+
+enum { OP_KC_RM = 0, OP_IC_RM = 1, OP_KC_HM = 2, OP_IC_HM = 3 };
+
+// Address of element (idx, k) of an operand; `col` is the head-concatenated
+// column and `tok` the token for the head-major modes.
+template <int MODE, bool F32>
+__device__ __forceinline__ const void* op_addr(const GemmOperand& o, int idx, int k, int n, int d) {
+    const int esz = F32 ? 4 : 2;
+    long off;
+    int s = 0;
+    if constexpr (MODE == OP_KC_RM) {
+        off = (long)idx * o.ld + k;
+    } else if constexpr (MODE == OP_IC_RM) {
+        off = (long)k * o.ld + idx;
+    } else {
+        const int tok = MODE == OP_KC_HM ? idx : k;
+        const int col = MODE == OP_KC_HM ? k : idx;
+        int hl = col / d;
+        const int i = col - hl * d;
+        while (s < 4 && hl >= o.hs[s]) hl -= o.hs[s++];
+        const int b = tok / n, t = tok - b * n;
+        off = (((long)b * o.hs[s] + hl) * n + t) * d + i;
+    }
+    return static_cast<const char*>(o.p[s]) + off * esz;
+}
+
+// Eight consecutive elements along the operand's contiguous direction, as bf16.
+template <bool F32>
+__device__ __forceinline__ uint4 load8(const void* p, bool ok) {
+    if (!ok) return zero_u4();
+    if constexpr (F32) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *(reinterpret_cast<const float4*>(p) + 1);
+        return make_uint4(cvt_pk_bf16(a.x, a.y), cvt_pk_bf16(a.z, a.w), cvt_pk_bf16(b.x, b.y),
+                          cvt_pk_bf16(b.z, b.w));
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
+
+constexpr bool k_contig(int mode) { return mode == OP_KC_RM || mode == OP_KC_HM; }
+
+// One 128 x 64 operand tile (rows idx0.., contraction k0..) into registers.
+template <int MODE, bool F32>
+__device__ __forceinline__ void tile_load(const GemmOperand& o, int idx0, int nidx, int k0, int K,
+                                          int n, int d, uint4 (&r)[4]) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = threadIdx.x + GNT * it;
+        int idx, k;
+        if constexpr (k_contig(MODE)) {
+            idx = idx0 + e / 8;
+            k = k0 + 8 * (e % 8);
+        } else {
+            idx = idx0 + 8 * (e % 16);
+            k = k0 + e / 16;
+        }
+        const bool ok = idx < nidx && k < K;
+        r[it] = load8<F32>(ok ? op_addr<MODE, F32>(o, idx, k, n, d) : nullptr, ok);
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ void tile_store(u16* t, const uint4 (&r)[4]) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int e = threadIdx.x + GNT * it;
+        if constexpr (k_contig(MODE))
+            *reinterpret_cast<uint4*>(&t[(e / 8) * GPLD + 8 * (e % 8)]) = r[it];
+        else
+            *reinterpret_cast<uint4*>(&t[(e / 16) * GLDI + 8 * (e % 16)]) = r[it];
+    }
+}
+
+// Fragment of 16 rows (block b of the tile's idx) for contraction step kk
+// (32 k): element e holds k = 32 kk + 4 g + e (e < 4) or 32 kk + 16 + 4 g + e - 4.
+template <int MODE>
+__device__ __forceinline__ bf16x8 frag(const u16* t, int b, int kk, int r16, int g) {
+    if constexpr (k_contig(MODE)) {
+        const u16* p = t + (16 * b + r16) * GPLD + 32 * kk + 4 * g;
+        const uint2 lo = *reinterpret_cast<const uint2*>(p);
+        const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
+        return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    } else {
+        const u16* p = t + (32 * kk + 4 * g + (r16 >> 2)) * GLDI + 4 * (r16 & 3) + 16 * b;
+        const uint2 lo = lds_read_tr16(p);
+        const uint2 hi = lds_read_tr16(p + 16 * GLDI);
+        return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+}
+
+template <int AM, bool AF, int BM, bool BF, int CM>
+__global__ __launch_bounds__(GNT, 2) void gemm_kernel(GemmArgs p) {
+    constexpr int ASZ = k_contig(AM) ? GBM * GPLD : GBK * GLDI;
+    constexpr int BSZ = k_contig(BM) ? GBN * GPLD : GBK * GLDI;
+    __shared__ __attribute__((aligned(16))) u16 la[2][ASZ];
+    __shared__ __attribute__((aligned(16))) u16 lb[2][BSZ];
+
+    const int m0 = blockIdx.x * GBM, n0 = blockIdx.y * GBN;
+    const int lane = lane_id(), wv = wave_id();
+    const int g = lane >> 4, r16 = lane & 15;
+    const int wm = wv >> 1, wn = wv & 1;
+
+    uint4 ra[4], rb[4];
+    f32x4 acc[4][4];   // [n block][m block]: C^T rows n0 + 64wn + 16ni + 4g + i, col m0 + 64wm + 16mi + r16
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (p.K + GBK - 1) / GBK;
+    tile_load<AM, AF>(p.a, m0, p.M, 0, p.K, p.n, p.d, ra);
+    tile_load<BM, BF>(p.b, n0, p.N, 0, p.K, p.n, p.d, rb);
+    tile_store<AM>(la[0], ra);
+    tile_store<BM>(lb[0], rb);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) {
+            tile_load<AM, AF>(p.a, m0, p.M, (kt + 1) * GBK, p.K, p.n, p.d, ra);
+            tile_load<BM, BF>(p.b, n0, p.N, (kt + 1) * GBK, p.K, p.n, p.d, rb);
+        }
+#pragma unroll
+        for (int kk = 0; kk < GBK / 32; ++kk) {
+            bf16x8 fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                fa[i] = frag<AM>(la[buf], 4 * wm + i, kk, r16, g);
+                fb[i] = frag<BM>(lb[buf], 4 * wn + i, kk, r16, g);
+            }
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = mfma16(fb[ni], fa[mi], acc[ni][mi]);
+        }
+        if (kt + 1 < nk) {
+            tile_store<AM>(la[buf ^ 1], ra);
+            tile_store<BM>(lb[buf ^ 1], rb);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: lane holds C[m][n .. n+3] for m = m0 + 64wm + 16mi + r16,
+    // n = n0 + 64wn + 16ni + 4g.
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int m = m0 + 64 * wm + 16 * mi + r16;
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int nn = n0 + 64 * wn + 16 * ni + 4 * g;
+            if (nn >= p.N) continue;
+            float c0 = acc[ni][mi][0], c1 = acc[ni][mi][1], c2 = acc[ni][mi][2], c3 = acc[ni][mi][3];
+            if constexpr (CM == 0) {
+                const long off = (long)m * p.N + nn;
+                if (p.res != nullptr) {
+                    const uint2 rr = *reinterpret_cast<const uint2*>(p.res + off);
+                    c0 += bf2f((u16)(rr.x & 0xffffu));
+                    c1 += bf2f((u16)(rr.x >> 16));
+                    c2 += bf2f((u16)(rr.y & 0xffffu));
+                    c3 += bf2f((u16)(rr.y >> 16));
+                }
+                store4<float>(static_cast<float*>(p.c[0]) + off, c0, c1, c2, c3);
+            } else {
+                int hl = nn / p.d;
+                const int i = nn - hl * p.d;
+                int s = 0;
+                while (s < 4 && hl >= p.hc[s]) hl -= p.hc[s++];
+                const int b = m / p.n, t = m - b * p.n;
+                u16* dst = static_cast<u16*>(p.c[s]) + (((long)b * p.hc[s] + hl) * p.n + t) * p.d + i;
+                store4<u16>(dst, c0, c1, c2, c3);
+            }
+        }
+    }
+}
+
+// One wave per row of d elements (d <= 128: two per lane).
+template <bool BF16>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(const void* __restrict__ x,
+                                                       const float* __restrict__ inv_norm,
+                                                       const float* __restrict__ g1,
+                                                       const float* __restrict__ g2, long rows,
+                                                       int d, float* __restrict__ dx) {
+    const long row = (long)blockIdx.x * 4 + wave_id();
+    if (row >= rows) return;
+    const int lane = lane_id();
+    float xv[2], gv[2];
+    float ss = 0.f, xg = 0.f;
+    const float inv = inv_norm[row];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = lane + 64 * u;
+        xv[u] = 0.f;
+        gv[u] = 0.f;
+        if (i < d) {
+            const long o = row * d + i;
+            xv[u] = BF16 ? bf2f(static_cast<const u16*>(x)[o]) : static_cast<const float*>(x)[o];
+            gv[u] = g1[o] + (g2 != nullptr ? g2[o] : 0.f);
+        }
+        ss = fmaf(xv[u], xv[u], ss);
+        xg = fmaf(xv[u] * inv, gv[u], xg);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        ss += __shfl_xor(ss, off);
+        xg += __shfl_xor(xg, off);
+    }
+    const bool clamped = sqrtf(ss) < 1e-12f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int i = lane + 64 * u;
+        if (i < d)
+            dx[row * d + i] = clamped ? gv[u] * inv : (gv[u] - xv[u] * inv * xg) * inv;
+    }
+}
+
+template <int AM, bool AF, int BM, bool BF, int CM>
+hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {
+    const dim3 grid((p.M + GBM - 1) / GBM, (p.N + GBN - 1) / GBN);
+    hipLaunchKernelGGL((gemm_kernel<AM, AF, BM, BF, CM>), grid, dim3(GNT), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bwd(int which, const GemmArgs& p, hipStream_t s) {
+    switch (which) {
+        case GEMM_DO: return launch_gemm<OP_KC_RM, false, OP_IC_RM, false, 1>(p, s);
+        case GEMM_DWO: return launch_gemm<OP_IC_RM, false, OP_IC_HM, false, 0>(p, s);
+        case GEMM_DX: return launch_gemm<OP_KC_HM, true, OP_IC_RM, false, 0>(p, s);
+        case GEMM_DWIN: return launch_gemm<OP_IC_HM, true, OP_IC_RM, false, 0>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_norm_bwd(const void* x, int dtype, const float* inv_norm, const float* g1,
+                           const float* g2, long rows, int d, float* dx, hipStream_t s) {
+    const unsigned blocks = (unsigned)((rows + 3) / 4);
+    if (dtype == 1)
+        hipLaunchKernelGGL(norm_bwd_kernel<true>, dim3(blocks), dim3(256), 0, s, x, inv_norm, g1,
+                           g2, rows, d, dx);
+    else
+        hipLaunchKernelGGL(norm_bwd_kernel<false>, dim3(blocks), dim3(256), 0, s, x, inv_norm, g1,
+                           g2, rows, d, dx);
+    return hipGetLastError();
+}
+
+}  // namespace rt

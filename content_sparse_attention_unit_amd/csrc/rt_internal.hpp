@@ -92,6 +92,42 @@ struct ProjArgs {
 };
 hipError_t launch_proj(const ProjArgs& p, int amode, int cmode, hipStream_t s);
 
+// Backward of the local-window attention: two kernels (dq with the per-query
+// log-sum-exp and D into ws, then dk and dv); bf16 inputs, d in {64, 128}.
+size_t local_bwd_workspace_bytes(int BH, int n);
+hipError_t launch_local_attn_bwd(const void* q, const void* kk, const void* v, const void* dout,
+                                 int BH, int n, int d, int window, float scale, int causal,
+                                 float* dq, float* dk, float* dv, void* ws, hipStream_t s);
+
+// Gradient through the unit normalisation, one row of d <= 128 per wave.
+hipError_t launch_norm_bwd(const void* x, int dtype, const float* inv_norm, const float* g1,
+                           const float* g2, long rows, int d, float* dx, hipStream_t s);
+
+// Operand X[idx][k] of the backward products: row-major with leading
+// dimension ld, or head-major segments p[s] [B][hs[s]][n][d] over the
+// concatenated heads (unused segments have hs = 0).
+struct GemmOperand {
+    const void* p[5];
+    int hs[5];
+    int ld;
+};
+// C[M][N] = sum_k A[m][k] B[n][k]: float32 row-major (+ bf16 residual res) or
+// bf16 head-major segments c[s] (m = token, n = head * d + i).
+struct GemmArgs {
+    GemmOperand a, b;
+    void* c[5];
+    int hc[5];
+    const uint16_t* res;
+    int M, N, K, n, d;
+};
+// The four products of the projections' backward:
+//   GEMM_DO    dO = dy W_o        A = dy [T][dm] row-major, B = W_o [dm][N] (idx-contiguous), C head-major bf16
+//   GEMM_DWO   dW_o = dy^T O      A = dy read idx-contiguous, B = O head-major (bf16), C fp32
+//   GEMM_DX    dx = dC W_in + dy  A = dC head-major fp32 (k-contiguous), B = W_in [K][dm], C fp32 + res
+//   GEMM_DWIN  dW_in = dC^T x     A = dC head-major fp32 (idx-contiguous), B = x [T][dm], C fp32
+enum { GEMM_DO = 0, GEMM_DWO = 1, GEMM_DX = 2, GEMM_DWIN = 3 };
+hipError_t launch_gemm_bwd(int which, const GemmArgs& p, hipStream_t s);
+
 // Largest cluster the backward kernels keep on chip.
 int max_cluster_rows_bwd(int dtype, int d, bool shared_qk);
 

@@ -66,7 +66,8 @@ typedef enum {
     RT_OP_ROUTED_ATTN = 1,
     RT_OP_LOCAL_ATTN = 2,
     RT_OP_CENTROID_UPDATE = 3,
-    RT_OP_ROUTED_ATTN_BWD = 4
+    RT_OP_ROUTED_ATTN_BWD = 4,
+    RT_OP_LOCAL_ATTN_BWD = 5
 } rt_op;
 
 /*
@@ -245,6 +246,82 @@ rt_status rt_in_proj(const void *x, const void *w_in, int B, int n, int dm, int 
  */
 rt_status rt_out_proj(const void *o_r, const void *o_l, const void *w_o, const void *x, int B,
                       int n, int dm, int d, int R, int L, void *y, void *stream);
+
+/*
+ * The layer's backward (gradients of one layer for the gradient dy of its
+ * output, membership held fixed): rt_out_proj_bwd -> rt_routed_attn_bwd on
+ * the routed heads and rt_local_attn_bwd on the local heads ->
+ * rt_normalize_bwd (the routed heads' shared q/k) -> rt_in_proj_bwd.
+ */
+
+/*
+ * rt_local_attn_bwd -- gradients of rt_local_attn with respect to q, k, v.
+ *   Summary §3 (softmax attention) over the local band of rt_local_attn.  For
+ *   the output gradient dout and P the softmax rows:
+ *     dv_j = sum_i P_ij dout_i,
+ *     dl_ij = P_ij (<dout_i, v_j> - sum_j' P_ij' <dout_i, v_j'>),
+ *     dq_i = scale sum_j dl_ij k_j,   dk_j = scale sum_i dl_ij q_i.
+ *   q, kk, v, dout  [B][H][n][d] bf16 (RT_BF16 only), d in {64, 128}.
+ *   dq, dk, dv      out [B][H][n][d] float32, distinct, aliasing no input.
+ *   The softmax is rebuilt from q, k (no state from the forward call); P and
+ *   dl are rounded to bf16 for the products, accumulation is float32.
+ *   ws: rt_workspace_bytes(RT_OP_LOCAL_ATTN_BWD, B, H, n, d, 1, 1) bytes
+ *   (each query's log-sum-exp and sum_j P dP).  Deterministic (no atomics).
+ */
+rt_status rt_local_attn_bwd(const void *q, const void *kk, const void *v, const void *dout,
+                            int dtype, int B, int H, int n, int d, int window, float scale,
+                            int causal, float *dq, float *dk, float *dv, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * rt_normalize_bwd -- gradient through the unit normalisation of rt_route.
+ *   Summary §4: queries and keys are used unit-normalised,
+ *   x^ = x / max(||x||, 1e-12).  For the gradients g1 and g2 (NULL for none)
+ *   of x^ (shared query/key: the query's and the key's gradients add),
+ *   with g = g1 + g2:  dx = (g - x^ <x^, g>) / ||x||, and dx = g / 1e-12 on
+ *   rows whose norm is below 1e-12 (the clamp is then constant).
+ *   x         [rows][d] dtype (the raw vectors given to rt_route).
+ *   inv_norm  [rows] float32 from rt_route.
+ *   g1, g2    [rows][d] float32.   dx out [rows][d] float32; dx may be g1 or
+ *             g2 (a row is read whole before it is written), not x.
+ */
+rt_status rt_normalize_bwd(const void *x, int dtype, const float *inv_norm, const float *g1,
+                           const float *g2, long rows, int d, float *dx, void *stream);
+
+/*
+ * rt_out_proj_bwd -- gradients of rt_out_proj.
+ *   For dy, the gradient of y = x + [o_r | o_l] W_o^T:
+ *     do = dy W_o (split into the routed and the local heads, head-major),
+ *     dw_o = dy^T [o_r | o_l];
+ *   the gradient of the residual x is dy itself (rt_in_proj_bwd adds it).
+ *   dy     [B][n][dm] bf16.  o_r, o_l, w_o as in rt_out_proj.
+ *   do_r   out [B][R][n][d] bf16; do_l out [B][L][n][d] bf16 (NULL when
+ *          L = 0): rounded once, as rt_routed_attn_bwd and rt_local_attn_bwd
+ *          take them.   dw_o out [dm][(R + L) d] float32.
+ *   bf16 products, float32 accumulation; outputs alias no input.
+ */
+rt_status rt_out_proj_bwd(const void *dy, const void *o_r, const void *o_l, const void *w_o,
+                          int B, int n, int dm, int d, int R, int L, void *do_r, void *do_l,
+                          float *dw_o, void *stream);
+
+/*
+ * rt_in_proj_bwd -- gradients of rt_in_proj.
+ *   For the heads' gradients dC = [dqk | dv | dq_l | dk_l | dv_l] (laid out
+ *   as rt_in_proj writes the heads):
+ *     dx = dC W_in + dres,   dw_in = dC^T x.
+ *   x, w_in  as in rt_in_proj.
+ *   dqk, dv  [B][R][n][d] float32; dq_l, dk_l, dv_l [B][L][n][d] float32
+ *            (NULL when L = 0).  dC is rounded to bf16 as the products'
+ *            operand; float32 accumulation.
+ *   dres     [B][n][dm] bf16 or NULL: a gradient added to dx (the residual's,
+ *            i.e. the dy given to rt_out_proj_bwd).
+ *   dx       out [B][n][dm] float32;  dw_in out [(2R + 3L) d][dm] float32.
+ *   Outputs alias no input.
+ */
+rt_status rt_in_proj_bwd(const void *x, const void *w_in, const float *dqk, const float *dv,
+                         const float *dq_l, const float *dk_l, const float *dv_l, const void *dres,
+                         int B, int n, int dm, int d, int R, int L, float *dx, float *dw_in,
+                         void *stream);
 
 /* Workspace size in bytes for operation `op` at these sizes (0 if none,
  * (size_t)-1 if the sizes are invalid). */

@@ -261,3 +261,93 @@ def test_out_proj_validation(lib, kw, code, msg):
     assert lib.rt_out_proj(p["o_r"], p["o_l"], p["w_o"], p["x"], a["B"], a["n"], a["dm"], a["d"],
                            a["R"], a["L"], p["y"], None) == code
     assert msg in _last(lib)
+
+
+# ---- the layer's backward ---------------------------------------------------------------
+
+def lbwd(lib, q=FAKE, kk=ctypes.c_void_p(0x2000), v=ctypes.c_void_p(0x3000),
+         dout=ctypes.c_void_p(0x4000), dtype=1, B=1, H=1, n=64, d=64, window=8, scale=0.25,
+         causal=1, dq=ctypes.c_void_p(0x6000), dk=ctypes.c_void_p(0x7000),
+         dv=ctypes.c_void_p(0x8000), ws=None, ws_bytes=0):
+    return lib.rt_local_attn_bwd(q, kk, v, dout, dtype, B, H, n, d, window, scale, causal, dq, dk,
+                                 dv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dout=None), RT_EINVAL, "null"),
+    (dict(dk=None), RT_EINVAL, "null"),
+    (dict(dq=FAKE), RT_EINVAL, "aliases an input"),
+    (dict(dv=ctypes.c_void_p(0x6000)), RT_EINVAL, "alias each other"),
+    (dict(window=0), RT_EINVAL, "window"),
+    (dict(causal=2), RT_EINVAL, "causal"),
+    (dict(scale=float("inf")), RT_EINVAL, "scale"),
+    (dict(d=32), RT_EUNSUPPORTED, "d in {64, 128}"),
+    (dict(dtype=0), RT_EUNSUPPORTED, "bf16"),
+    (dict(d=48), RT_EUNSUPPORTED, "d=48"),
+    (dict(), RT_EINVAL, "workspace"),
+    (dict(ws=FAKE, ws_bytes=64 * 8 - 1), RT_EINVAL, "workspace"),
+])
+def test_local_attn_bwd_validation(lib, kw, code, msg):
+    assert lbwd(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_local_bwd_workspace_size(lib):
+    assert lib.rt_workspace_bytes(5, 2, 4, 1000, 64, 1, 1) == 2 * 4 * 1000 * 8
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(x=None), RT_EINVAL, "null"),
+    (dict(g1=None), RT_EINVAL, "null"),
+    (dict(rows=0), RT_EINVAL, "positive"),
+    (dict(d=24), RT_EUNSUPPORTED, "d=24"),
+    (dict(dtype=7), RT_EUNSUPPORTED, "dtype"),
+    (dict(dx=FAKE), RT_EINVAL, "aliases"),
+])
+def test_normalize_bwd_validation(lib, kw, code, msg):
+    a = dict(x=FAKE, dtype=1, inv=ctypes.c_void_p(0x2000), g1=ctypes.c_void_p(0x3000), g2=None,
+             rows=10, d=64, dx=ctypes.c_void_p(0x4000))
+    a.update(kw)
+    assert lib.rt_normalize_bwd(a["x"], a["dtype"], a["inv"], a["g1"], a["g2"], a["rows"], a["d"],
+                                a["dx"], None) == code
+    assert msg in _last(lib)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dy=None), RT_EINVAL, "null"),
+    (dict(do_l=None), RT_EINVAL, "null"),
+    (dict(dw_o=None), RT_EINVAL, "null"),
+    (dict(R=0), RT_EINVAL, "positive"),
+    (dict(dm=12), RT_EUNSUPPORTED, "multiple of 8"),
+    (dict(do_r=FAKE), RT_EINVAL, "aliases an input"),
+    (dict(do_l=ctypes.c_void_p(0x5000)), RT_EINVAL, "alias each other"),
+])
+def test_out_proj_bwd_validation(lib, kw, code, msg):
+    a = dict(dy=FAKE, o_r=ctypes.c_void_p(0x2000), o_l=ctypes.c_void_p(0x3000),
+             w_o=ctypes.c_void_p(0x4000), B=1, n=16, dm=64, d=16, R=2, L=1,
+             do_r=ctypes.c_void_p(0x5000), do_l=ctypes.c_void_p(0x6000),
+             dw_o=ctypes.c_void_p(0x7000))
+    a.update(kw)
+    assert lib.rt_out_proj_bwd(a["dy"], a["o_r"], a["o_l"], a["w_o"], a["B"], a["n"], a["dm"],
+                               a["d"], a["R"], a["L"], a["do_r"], a["do_l"], a["dw_o"], None) == code
+    assert msg in _last(lib)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(x=None), RT_EINVAL, "null"),
+    (dict(dv=None), RT_EINVAL, "null"),
+    (dict(dk_l=None), RT_EINVAL, "null"),
+    (dict(d=40), RT_EUNSUPPORTED, "d=40"),
+    (dict(dx=FAKE), RT_EINVAL, "aliases an input"),
+    (dict(dw_in=ctypes.c_void_p(0x9000)), RT_EINVAL, "alias"),
+])
+def test_in_proj_bwd_validation(lib, kw, code, msg):
+    a = dict(x=FAKE, w_in=ctypes.c_void_p(0x2000), dqk=ctypes.c_void_p(0x3000),
+             dv=ctypes.c_void_p(0x4000), dq_l=ctypes.c_void_p(0x5000),
+             dk_l=ctypes.c_void_p(0x6000), dv_l=ctypes.c_void_p(0x7000), dres=None, B=1, n=16,
+             dm=64, d=16, R=2, L=1, dx=ctypes.c_void_p(0x9000), dw_in=ctypes.c_void_p(0xa000))
+    a.update(kw)
+    assert lib.rt_in_proj_bwd(a["x"], a["w_in"], a["dqk"], a["dv"], a["dq_l"], a["dk_l"],
+                              a["dv_l"], a["dres"], a["B"], a["n"], a["dm"], a["d"], a["R"],
+                              a["L"], a["dx"], a["dw_in"], None) == code
+    assert msg in _last(lib)
