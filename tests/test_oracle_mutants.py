@@ -28,7 +28,26 @@ MUTANTS = {
     "scatter_overwrites": ("out[t * d + i] += o[((long)c * w + r) * d + i];",
                            "out[t * d + i] = o[((long)c * w + r) * d + i];"),
     "scale_dropped": ("logit[s] = scale * dot;", "logit[s] = dot;"),
-    "local_window_off_by_one": ("long lo = i - window + 1;", "long lo = i - window;"),
+    "local_window_off_by_one": ("(size_t)(2 * window + 1));\n    for (long i = 0; i < n; ++i) {\n"
+                                "        long lo = i - window + 1;\n        if (lo < 0)\n"
+                                "            lo = 0;\n        long hi = causal ? i : i + window - 1;\n"
+                                "        if (hi > n - 1)\n            hi = n - 1;\n        double m = "
+                                "-INFINITY;\n        for (long j = lo; j <= hi; ++j) {\n            "
+                                "double dot = 0.0;\n            for (int e = 0; e < d; ++e)\n"
+                                "                dot += q[i * d + e] * kk[j * d + e];\n            logit",
+                                "(size_t)(2 * window + 1));\n    for (long i = 0; i < n; ++i) {\n"
+                                "        long lo = i - window;\n        if (lo < 0)\n"
+                                "            lo = 0;\n        long hi = causal ? i : i + window - 1;\n"
+                                "        if (hi > n - 1)\n            hi = n - 1;\n        double m = "
+                                "-INFINITY;\n        for (long j = lo; j <= hi; ++j) {\n            "
+                                "double dot = 0.0;\n            for (int e = 0; e < d; ++e)\n"
+                                "                dot += q[i * d + e] * kk[j * d + e];\n            logit"),
+    "local_bwd_softmax_sign": ("double dl = P[j - lo] * (dP[j - lo] - D);",
+                               "double dl = P[j - lo] * (dP[j - lo] + D);"),
+    "local_bwd_dk_from_keys": ("dk[j * d + e] += scale * dl * q[i * d + e];",
+                               "dk[j * d + e] += scale * dl * kk[i * d + e];"),
+    "local_bwd_dv_unweighted": ("dv[j * d + e] += P[j - lo] * dout[i * d + e];",
+                                "dv[j * d + e] += dout[i * d + e];"),
     "softmax_bwd_sign": ("double dl = P[r * w + s] * (dP[r * w + s] - D);",
                          "double dl = P[r * w + s] * (dP[r * w + s] + D);"),
     "centroid_transposed": ("acc += xhat[t * d + i] * mu[c * d + i];",
