@@ -206,7 +206,11 @@ def time_stack(rt, sc, reps=5):
             b.record(stream)
             torch.cuda.synchronize()
             per[name] = a.elapsed_time(b) / 20
+    bwd = time_layer_bwd(rt, sc, stream, layers[0], x0, dict(qk=qk, v=v, ql=ql, kl=kl, vl=vl,
+                                                          inv=inv, idx=idx, mask=mask, o_r=o_r,
+                                                          o_l=o_l, ws_r=ws_r, ws_a=ws_a))
     return {"layers": sc.layers, "d_model": dm, "ms_per_forward": ms,
+            "backward": bwd,
             "tokens_per_s": B * n / (ms * 1e-3), "us_per_layer": ms * 1e3 / sc.layers,
             "finite": finite,
             "proj_ms": per,
@@ -216,6 +220,76 @@ def time_stack(rt, sc, reps=5):
                                "rt_out_proj": flops_out / (per["rt_out_proj"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
             "workload": f"{sc.layers}-layer stack, d_model={dm}, {R} routed + {L} local heads of "
                         f"{d}, n={n}, B={B}, random-init weights N(0, 1/fan_in)"}
+
+
+def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
+    """The layer's backward at the stack's shapes (one layer, membership held
+    fixed): rt_out_proj_bwd -> rt_routed_attn_bwd + rt_normalize_bwd on the
+    routed heads, rt_local_attn_bwd on the local heads -> rt_in_proj_bwd.  Each
+    call timed back to back (HIP events); the sum is one layer's backward."""
+    B, n, dm, d, R, L, k, w = sc.B, sc.n, sc.dm, sc.d, sc.R, sc.L, sc.k, sc.w
+    scale = 1.0 / math.sqrt(d)
+    w_in, w_o, mu = layer
+    f32 = dict(dtype=torch.float32, device="cuda")
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    dy = dev(S.normal_tensor(1000 * sc.cfg_id + 60, (B, n, dm), "bf16"))
+    lse = torch.empty((B, R, k, w), **f32)
+    do_r, do_l = torch.empty((B, R, n, d), **bf), torch.empty((B, L, n, d), **bf)
+    dw_o = torch.empty((dm, (R + L) * d), **f32)
+    dqh, dkh, dv, dqk = (torch.empty((B, R, n, d), **f32) for _ in range(4))
+    dq_l, dk_l, dv_l = (torch.empty((B, L, n, d), **f32) for _ in range(3))
+    dx = torch.empty((B, n, dm), **f32)
+    dw_in = torch.empty(((2 * R + 3 * L) * d, dm), **f32)
+    ws_b = torch.empty(rt.workspace_bytes("routed_attn_bwd", B, R, n, d, k, w), dtype=torch.uint8,
+                       device="cuda")
+    ws_l = torch.empty(rt.workspace_bytes("local_attn_bwd", B, L, n, d, 1, 1), dtype=torch.uint8,
+                       device="cuda")
+    T, NO, NC = B * n, (R + L) * d, (2 * R + 3 * L) * d
+    band = L * B * (n * sc.window - sc.window * (sc.window - 1) / 2)   # (query, key) pairs
+    calls = {
+        "rt_out_proj_bwd": (lambda: rt.out_proj_bwd(dy, t["o_r"], t["o_l"], w_o,
+                                                    out=(do_r, do_l, dw_o)),
+                            2 * 2.0 * T * dm * NO),
+        "rt_routed_attn_bwd": (lambda: rt.routed_attn_bwd(t["qk"], t["qk"], t["v"], t["idx"], lse,
+                                                          do_r, t["inv"], t["inv"], scale=scale,
+                                                          out=(dqh, dkh, dv), ws=ws_b),
+                               10.0 * B * R * k * w * w * d),
+        "rt_normalize_bwd": (lambda: rt.normalize_bwd(t["qk"], t["inv"], dqh, dkh, out=dqk), 0.0),
+        "rt_local_attn_bwd": (lambda: rt.local_attn_bwd(t["ql"], t["kl"], t["vl"], do_l,
+                                                        sc.window, scale=scale,
+                                                        out=(dq_l, dk_l, dv_l), ws=ws_l),
+                              10.0 * band * d),
+        "rt_in_proj_bwd": (lambda: rt.in_proj_bwd(x0, w_in, dqk, dv, dq_l, dk_l, dv_l, dres=dy,
+                                                  out=(dx, dw_in)),
+                           2 * 2.0 * T * NC * dm),
+    }
+    per, tfl = {}, {}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        # forward state of one layer (with the softmax statistics the routed backward needs)
+        rt.in_proj(x0, w_in, R, L, d, out=(t["qk"], t["v"], t["ql"], t["kl"], t["vl"]))
+        rt.route(t["qk"], mu, w, out=(t["inv"], t["idx"], t["mask"]), ws=t["ws_r"])
+        rt.routed_attn(t["qk"], t["qk"], t["v"], t["idx"], t["inv"], t["inv"], scale=scale,
+                       mask=t["mask"], out=t["o_r"], lse=lse, ws=t["ws_a"])
+        rt.local_attn(t["ql"], t["kl"], t["vl"], sc.window, scale=scale, out=t["o_l"])
+        for name, (fn, flops) in calls.items():
+            for _ in range(3):
+                fn()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per[name] = a.elapsed_time(b) / reps
+            if flops:
+                tfl[name] = flops / (per[name] * 1e-3) / 1e12
+    finite = all(bool(torch.isfinite(g).all()) for g in (dx, dw_in, dw_o))
+    total = sum(per.values())
+    return {"ms_per_layer": total, "tokens_per_s": B * n / (total * 1e-3), "per_call_ms": per,
+            "tflops": tfl, "finite": finite,
+            "note": "one layer's backward (membership fixed), the sum of back-to-back call "
+                    "times; tflops on the algorithmic products (routed and local attention: "
+                    "5 products per visible pair)"}
 
 
 def sweep_configs(only=None):
