@@ -40,9 +40,9 @@ LOCAL_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/local_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "f4ea6e83e39c1f3238d59156272231c3cf0802c5c69356213dfa2fd3dd3b595e",
-    "fetch_kib": 12980.86, "write_kib": 8192.0,
-    "fetch_scale": 262144.0 / 131092.6875, "write_scale": 262144.0 / 262144.0,
+    "sha256": "461a63a5b6617aae7ebd8fde0e02d5cf475865bc19ae9dc5fb6c9d0a3407d940",
+    "fetch_kib": 12984.88, "write_kib": 8192.0,
+    "fetch_scale": 262144.0 / 131096.125, "write_scale": 262144.0 / 262144.0,
 }
 
 

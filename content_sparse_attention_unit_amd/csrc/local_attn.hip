@@ -22,6 +22,51 @@
 namespace rt {
 namespace {
 
+// softmax_pv_half on unscaled logits: the scale enters as one fma with the
+// reference, exp2(s * sl2 - m), and the chunk maximum is scaled once (sl2 > 0).
+// The fma does not round s * sl2 while m is the rounded product, so for the
+// maximum the argument is the rounding error of m: harmless while |m| is
+// moderate, but up to half an ulp of m (beyond the exponent range once |m|
+// passes ~2^24).  Waves whose reference is that large take the rounded
+// product first, as m was formed.
+template <int NJ, int LDX>
+__device__ __forceinline__ void softmax_pv_half_unscaled(f32x4 (&sv)[2], float sl2, float& m,
+                                                         f32x4& zacc, f32x4 (&o)[NJ],
+                                                         const u16* lv, int r16, int g) {
+    const float lmax = sl2 * fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                                   fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    lazy_rescale<NJ>(lmax, m, zacc, o);
+    const float nm = (m == -INFINITY) ? 0.f : -m;
+    uint32_t pw[2][2];
+    if (__ballot(fabsf(m) > 4096.f) == 0ull) {   // wave-uniform
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            pw[kb][0] = cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(sv[kb][0], sl2, nm)),
+                                    __builtin_amdgcn_exp2f(fmaf(sv[kb][1], sl2, nm)));
+            pw[kb][1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(fmaf(sv[kb][2], sl2, nm)),
+                                    __builtin_amdgcn_exp2f(fmaf(sv[kb][3], sl2, nm)));
+        }
+    } else {
+#pragma clang fp contract(off)   // round the product, as m was rounded
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            pw[kb][0] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[kb][0] * sl2 + nm),
+                                    __builtin_amdgcn_exp2f(sv[kb][1] * sl2 + nm));
+            pw[kb][1] = cvt_pk_bf16(__builtin_amdgcn_exp2f(sv[kb][2] * sl2 + nm),
+                                    __builtin_amdgcn_exp2f(sv[kb][3] * sl2 + nm));
+        }
+    }
+    const bf16x8 pbv = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+    const u16* vb = lv + (4 * g + (r16 >> 2)) * LDX + 4 * (r16 & 3);
+#pragma unroll
+    for (int jb = 0; jb < NJ; ++jb) {
+        const uint2 lo = lds_read_tr16(vb + 16 * jb);
+        const uint2 hi = lds_read_tr16(vb + 16 * LDX + 16 * jb);
+        o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pbv, o[jb]);
+    }
+    zacc = mfma16(bf16_ones(), pbv, zacc);
+}
+
 template <int D>
 struct LocalCfg {
     static constexpr int DP = D < 32 ? 32 : D;
@@ -98,7 +143,11 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
     const long base = (long)bh * n;
     const int lane = lane_id(), wv = wave_id();
     const int g = lane >> 4, r16 = lane & 15;
-    const float sl2 = scale * 1.4426950408889634f;
+    // log2-unit scale, kept positive: a negative scale negates the queries
+    // instead, and a zero scale becomes one too small to change any logit
+    const float sl2s = scale * 1.4426950408889634f;
+    const float sl2 = sl2s > 0.f ? sl2s : (sl2s < 0.f ? -sl2s : 1e-30f);
+    const uint32_t qflip = sl2s < 0.f ? 0x80008000u : 0u;
     const int hf = wv / C::NQB;                  // key half of every tile: [32 hf, 32 hf + 32)
     const int qb0 = q0 + 16 * (wv % C::NQB);    // first query of this wave's block
     const int qi = qb0 + r16;                    // this lane's query
@@ -109,6 +158,10 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
         const int d0 = 32 * s + 8 * g;
         qreg[s] = (qi < n && d0 < D) ? *reinterpret_cast<const uint4*>(q + (base + qi) * D + d0)
                                      : zero_u4();
+        qreg[s].x ^= qflip;
+        qreg[s].y ^= qflip;
+        qreg[s].z ^= qflip;
+        qreg[s].w ^= qflip;
     }
     // keys needed by the workgroup / by this wave's block; keys in [clo, chi]
     // are visible to every query of the block
@@ -144,7 +197,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
                         &LK[(16 * kb + r16) * C::LDX + 32 * s + 8 * g]));                    \
                     acc = mfma16(a, as_bf16x8(qreg[s]), acc);                                \
                 }                                                                            \
-                sv[kb] = acc * sl2;                                                          \
+                sv[kb] = acc;                          /* unscaled: sl2 enters in exp2 */  \
             }                                                                                \
             if (kh_ < clo || kh_ + 31 > chi) {     /* not inside every band: mask */         \
                 _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
@@ -155,7 +208,8 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
                         sv[kb][i] = ok ? sv[kb][i] : -INFINITY;                              \
                     }                                                                        \
             }                                                                                \
-            softmax_pv_half<C::NJ, C::LDX>(sv, m, zacc, o, lv[BUF] + 32 * hf * C::LDX, r16, g); \
+            softmax_pv_half_unscaled<C::NJ, C::LDX>(sv, sl2, m, zacc, o,                      \
+                                                   lv[BUF] + 32 * hf * C::LDX, r16, g);      \
         }                                                                                    \
     } while (0)
 

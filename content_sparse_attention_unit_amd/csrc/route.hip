@@ -37,11 +37,12 @@ struct ScoreCfg {
     static constexpr int KC = (D == 128) ? 64 : 128;   // centroids per LDS chunk
     static constexpr int LD = DP + 8;                  // LDS row stride (bf16), 16 B aligned
     static constexpr int NS = DP / 32;                 // MFMA k-steps per token row
-    static constexpr int TOK = 128;                    // tokens per workgroup (4 waves x 32)
+    static constexpr int NT = 512;                     // threads per workgroup (8 waves)
+    static constexpr int TOK = 32 * NT / 64;           // tokens per workgroup (32 per wave)
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__ qk,
+__global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* __restrict__ qk,
                                                          const float* __restrict__ mu, int H,
                                                          int n, int k,
                                                          float* __restrict__ inv_norm,
@@ -64,12 +65,12 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     // dims (two 16-byte loads) and stores each of the three bf16 terms of a
     // group with one 16-byte LDS write.
     constexpr int GPR = C::DP / 8;                   // 8-dim groups per centroid row
-    constexpr int MG = (C::KC * GPR) / 256;          // groups per thread
+    constexpr int MG = (C::KC * GPR) / C::NT;        // groups per thread
     float4 mreg[MG][2];
     auto load_mu = [&](int c0) {
 #pragma unroll
         for (int j = 0; j < MG; ++j) {
-            const int e = threadIdx.x + 256 * j;
+            const int e = threadIdx.x + C::NT * j;
             const int c = e / GPR, dim0 = 8 * (e % GPR);
             const bool ok = c0 + c < k && dim0 < D;
             const float* src = mu + ((long)h * k + c0 + c) * D + dim0;
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(256) void score_bf16_kernel(const u16* __restrict__
     auto stage_mu = [&]() {
 #pragma unroll
         for (int j = 0; j < MG; ++j) {
-            const int e = threadIdx.x + 256 * j;
+            const int e = threadIdx.x + C::NT * j;
             const int c = e / GPR, dim0 = 8 * (e % GPR);
             const float m8[8] = {mreg[j][0].x, mreg[j][0].y, mreg[j][0].z, mreg[j][0].w,
                                  mreg[j][1].x, mreg[j][1].y, mreg[j][1].z, mreg[j][1].w};
@@ -641,7 +642,7 @@ void launch_score_d(const void* qk, int dtype, const float* mu, int BH, int H, i
                     float* inv_norm, float* scores, void* qk_hat, uint32_t* mask, hipStream_t s) {
     if (dtype == 1) {
         dim3 grid((n + ScoreCfg<D>::TOK - 1) / ScoreCfg<D>::TOK, BH);
-        hipLaunchKernelGGL(score_bf16_kernel<D>, grid, dim3(256), 0, s, (const u16*)qk, mu, H, n,
+        hipLaunchKernelGGL(score_bf16_kernel<D>, grid, dim3(ScoreCfg<D>::NT), 0, s, (const u16*)qk, mu, H, n,
                            k, inv_norm, scores, (u16*)qk_hat, mask, mask_words(k));
     } else {
         dim3 grid((n + 255) / 256, BH);

@@ -254,6 +254,21 @@ def test_local_window_edges(rt, orc, window):
         assert torch.equal(out, v.float())
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.5])
+@pytest.mark.parametrize("causal", [True, False])
+def test_local_scale_signs(rt, orc, scale, causal):
+    """Negative, zero and large scales (the kernel keeps its log2 scale positive
+    by negating the queries, and treats zero as uniform weights)."""
+    cfg = SMALL["ragged_d128"]
+    inp = S.make_inputs(cfg)
+    q, kk, v = (dev_tensor(inp[x]) for x in ("q_local", "k_local", "v_local"))
+    out = rt.local_attn(q, kk, v, 50, scale=scale, causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    out_o = orc.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
+                           50, scale, causal)
+    assert_close_out(host(out), out_o, cfg.dtype, "local out")
+
+
 # The longest rows of the sequence-length sweep (k = sqrt(n)): the top-w variants
 # for n = 16K (registers) and 64K (the 1024-thread register variant), 2 heads.
 @pytest.mark.parametrize("n,k", [(16384, 128), (65536, 256)])
