@@ -156,6 +156,61 @@ def local_attn_bwd(q, kk, v, dout, window: int, scale: float, causal: bool = Tru
     return dq, dk, dv
 
 
+def local_attn_blocked(q, kk, v, block: int, lookback: int, scale: float,
+                       nthreads: int | None = None):
+    """O10 for [B,H,n,d] tensors (causal blocked local attention)."""
+    lib = _load()
+    q, kk, v = _f64(q), _f64(kk), _f64(v)
+    B, H, n, d = q.shape
+    out = np.empty_like(q)
+    lib.orc_local_blocked_all(_p(q), _p(kk), _p(v), ctypes.c_int(B), ctypes.c_int(H),
+                              ctypes.c_long(n), ctypes.c_int(d), ctypes.c_long(block),
+                              ctypes.c_long(lookback), ctypes.c_double(scale), _p(out),
+                              ctypes.c_int(nthreads or default_threads()))
+    return out
+
+
+def argmax_labels(x, mu):
+    """O1 + O2 + O11: x [B,H,n,d], mu [H,k,d] -> (label [B,H,n] int32, margin
+    [B,H,n]: the gap between the largest and the second largest score)."""
+    lib = _load()
+    x, mu = _f64(x), _f64(mu)
+    B, H, n, d = x.shape
+    k = mu.shape[1]
+    label = np.empty((B, H, n), dtype=np.int32)
+    margin = np.empty((B, H, n))
+    lib.orc_argmax_all(_p(x), _p(mu), ctypes.c_int(B), ctypes.c_int(H), ctypes.c_long(n),
+                       ctypes.c_int(d), ctypes.c_int(k), _p(label), _p(margin))
+    return label, margin
+
+
+def centroid_update_argmax(mu, q, kk, lam: float):
+    """O1 + O11: the EMA step with nearest-centroid assignments (the input is
+    not modified)."""
+    lib = _load()
+    mu2 = _f64(mu).copy()
+    q, kk = _f64(q), _f64(kk)
+    B, H, n, d = q.shape
+    k = mu2.shape[1]
+    lib.orc_centroid_update_argmax_all(_p(mu2), _p(q), _p(kk), ctypes.c_int(B), ctypes.c_int(H),
+                                       ctypes.c_long(n), ctypes.c_int(d), ctypes.c_int(k),
+                                       ctypes.c_double(lam))
+    return mu2
+
+
+def route_partition(x, mu):
+    """O1 + O2 + O12: partition-style balanced clusters, idx [B,H,k,n/k]."""
+    lib = _load()
+    x, mu = _f64(x), _f64(mu)
+    B, H, n, d = x.shape
+    k = mu.shape[1]
+    assert n % k == 0
+    idx = np.empty((B, H, k, n // k), dtype=np.int32)
+    lib.orc_route_partition_all(_p(x), _p(mu), ctypes.c_int(B), ctypes.c_int(H),
+                                ctypes.c_long(n), ctypes.c_int(d), ctypes.c_int(k), _p(idx))
+    return idx
+
+
 def normalize_bwd(x, g):
     """Gradient of O1 along the last axis: for x^ = x / r with r = max(||x||,
     1e-12) and the upstream gradient g of x^, dx = (g - x^ <x^, g>) / r while

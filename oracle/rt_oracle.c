@@ -33,6 +33,17 @@
  *   O8 backward    gradients of O4+O5 w.r.t. q^, k^, v (routing and the
  *                  normalisation are held fixed)
  *   O9 local bwd   gradients of O7 w.r.t. q, k, v
+ * Variants (readings the pages leave open, built beside the main path):
+ *   O10 blocked    blocked (chunked) local attention: blocks of `block`
+ *                  positions, position i sees the positions of its own block
+ *                  and of the `lookback` blocks before it, not later than i
+ *   O11 argmax     each token's nearest centroid (largest score, ties to the
+ *                  lower index), and the EMA of O6 over those assignments
+ *                  (every token counts once, for its own centroid)
+ *   O12 partition  one cluster per token, all clusters of n/k tokens: tokens
+ *                  ordered by (argmax centroid, descending score against it,
+ *                  position) and cut into k consecutive groups   summary §4
+ *                  (a token's assigned cluster; a sort)
  *
  * Every function is sequential over its unit; the *_all drivers only hand
  * independent (batch, head) units to worker threads.
@@ -378,6 +389,114 @@ void orc_local_bwd(const double *q, const double *kk, const double *v, const dou
     free(dP);
 }
 
+/* --------------------------------------------------------------- O10 ---- */
+/* Blocked local attention: position i, in block b = i / block, attends to the
+ * positions of blocks b - lookback .. b that are not later than i. */
+void orc_local_blocked(const double *q, const double *kk, const double *v, long n, int d,
+                       long block, long lookback, double scale, double *out)
+{
+    double *logit = (double *)malloc(sizeof(double) * (size_t)((lookback + 1) * block));
+    for (long i = 0; i < n; ++i) {
+        long lo = (i / block - lookback) * block;
+        if (lo < 0)
+            lo = 0;
+        double m = -INFINITY;
+        for (long j = lo; j <= i; ++j) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += q[i * d + e] * kk[j * d + e];
+            logit[j - lo] = scale * dot;
+            if (logit[j - lo] > m)
+                m = logit[j - lo];
+        }
+        double z = 0.0;
+        for (long j = lo; j <= i; ++j)
+            z += exp(logit[j - lo] - m);
+        for (int e = 0; e < d; ++e)
+            out[i * d + e] = 0.0;
+        for (long j = lo; j <= i; ++j) {
+            double pr = exp(logit[j - lo] - m) / z;
+            for (int e = 0; e < d; ++e)
+                out[i * d + e] += pr * v[j * d + e];
+        }
+    }
+    free(logit);
+}
+
+/* --------------------------------------------------------------- O11 ---- */
+/* Nearest centroid of each token from the scores s[c][t]: the largest score,
+ * ties to the lower centroid index.  margin[t] (nullable) is the gap to the
+ * second largest score (+inf when k == 1). */
+void orc_argmax(const double *s, long n, int k, int32_t *label, double *margin)
+{
+    for (long t = 0; t < n; ++t) {
+        int best = 0;
+        double b1 = s[t], b2 = -INFINITY;
+        for (int c = 1; c < k; ++c) {
+            double x = s[(long)c * n + t];
+            if (x > b1) {
+                b2 = b1;
+                b1 = x;
+                best = c;
+            } else if (x > b2) {
+                b2 = x;
+            }
+        }
+        label[t] = best;
+        if (margin)
+            margin[t] = b1 - b2;
+    }
+}
+
+/* acc[label[t]][*] += xhat[t][*] in ascending t. */
+void orc_label_sums(const double *xhat, const int32_t *label, long n, int d, double *acc)
+{
+    for (long t = 0; t < n; ++t)
+        for (int i = 0; i < d; ++i)
+            acc[(long)label[t] * d + i] += xhat[t * d + i];
+}
+
+/* --------------------------------------------------------------- O12 ---- */
+typedef struct {
+    int c;
+    double s;
+    long t;
+} labelled_t;
+
+/* lower centroid first; then larger score; then lower position */
+static int by_label_score_pos(const void *a, const void *b)
+{
+    const labelled_t *x = (const labelled_t *)a, *y = (const labelled_t *)b;
+    if (x->c != y->c) return (x->c < y->c) ? -1 : 1;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->t < y->t) ? -1 : (x->t > y->t);
+}
+
+/* Partition-style balanced clusters of w = n / k tokens (n a multiple of k):
+ * idx[c][*] are the tokens at ranks c*w .. c*w + w - 1 of the order above,
+ * listed by ascending position. */
+void orc_partition(const double *s, long n, int k, int32_t *idx)
+{
+    long w = n / k;
+    labelled_t *buf = (labelled_t *)malloc(sizeof(labelled_t) * (size_t)n);
+    int32_t *label = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    orc_argmax(s, n, k, label, NULL);
+    for (long t = 0; t < n; ++t) {
+        buf[t].c = label[t];
+        buf[t].s = s[(long)label[t] * n + t];
+        buf[t].t = t;
+    }
+    qsort(buf, (size_t)n, sizeof(labelled_t), by_label_score_pos);
+    for (int c = 0; c < k; ++c) {
+        for (long r = 0; r < w; ++r)
+            idx[(long)c * w + r] = (int32_t)buf[(long)c * w + r].t;
+        qsort(idx + (long)c * w, (size_t)w, sizeof(int32_t), by_int);
+    }
+    free(buf);
+    free(label);
+}
+
 /* ------------------------------------------------ whole-tensor drivers ---- */
 /* Tensors are contiguous row-major [B][H][n][d] (qk, v, out), [H][k][d] (mu),
  * [B][H][n] (inv_norm), [B][H][k][w] (idx, lse), [B][H][k] (margin),
@@ -613,4 +732,96 @@ void orc_local_attn_bwd_all(const double *q, const double *kk, const double *v, 
 {
     local_bwd_args a = {q, kk, v, dout, n, window, d, causal, scale, dq, dk, dv};
     parallel_units(local_bwd_unit, &a, (long)B * H, nthreads);
+}
+
+typedef struct {
+    const double *q, *kk, *v;
+    long n, block, lookback;
+    int d;
+    double scale;
+    double *out;
+} blocked_args;
+
+static void blocked_unit(void *p, long u)
+{
+    blocked_args *a = (blocked_args *)p;
+    long off = u * a->n * a->d;
+    orc_local_blocked(a->q + off, a->kk + off, a->v + off, a->n, a->d, a->block, a->lookback,
+                      a->scale, a->out + off);
+}
+
+/* O10 for every (b, h). */
+void orc_local_blocked_all(const double *q, const double *kk, const double *v, int B, int H,
+                           long n, int d, long block, long lookback, double scale, double *out,
+                           int nthreads)
+{
+    blocked_args a = {q, kk, v, n, block, lookback, d, scale, out};
+    parallel_units(blocked_unit, &a, (long)B * H, nthreads);
+}
+
+/* O1 + O2 + O11 for every (b, h): labels [B][H][n] and margins [B][H][n]. */
+void orc_argmax_all(const double *x, const double *mu, int B, int H, long n, int d, int k,
+                    int32_t *label, double *margin)
+{
+    double *xhat = (double *)malloc(sizeof(double) * (size_t)n * (size_t)d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)k * (size_t)n);
+    for (long u = 0; u < (long)B * H; ++u) {
+        int h = (int)(u % H);
+        orc_normalize(x + u * n * d, n, d, xhat, NULL);
+        orc_scores(xhat, mu + (long)h * k * d, n, d, k, s);
+        orc_argmax(s, n, k, label + u * n, margin ? margin + u * n : NULL);
+    }
+    free(xhat);
+    free(s);
+}
+
+/* O1 + O11: one EMA step of every head's centroids with each query and each
+ * key counted for its own nearest centroid (batch rows in ascending order).
+ * mu [H][k][d] is updated in place. */
+void orc_centroid_update_argmax_all(double *mu, const double *q, const double *kk, int B, int H,
+                                    long n, int d, int k, double lam)
+{
+    double *xhat = (double *)malloc(sizeof(double) * (size_t)n * (size_t)d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)k * (size_t)n);
+    int32_t *label = (int32_t *)malloc(sizeof(int32_t) * (size_t)n);
+    double *sq = (double *)malloc(sizeof(double) * (size_t)k * (size_t)d);
+    double *sk = (double *)malloc(sizeof(double) * (size_t)k * (size_t)d);
+    for (int h = 0; h < H; ++h) {
+        const double *muh = mu + (long)h * k * d;
+        memset(sq, 0, sizeof(double) * (size_t)k * (size_t)d);
+        memset(sk, 0, sizeof(double) * (size_t)k * (size_t)d);
+        for (int b = 0; b < B; ++b) {
+            long u = (long)b * H + h;
+            orc_normalize(q + u * n * d, n, d, xhat, NULL);
+            orc_scores(xhat, muh, n, d, k, s);
+            orc_argmax(s, n, k, label, NULL);
+            orc_label_sums(xhat, label, n, d, sq);
+            orc_normalize(kk + u * n * d, n, d, xhat, NULL);
+            orc_scores(xhat, muh, n, d, k, s);
+            orc_argmax(s, n, k, label, NULL);
+            orc_label_sums(xhat, label, n, d, sk);
+        }
+        orc_ema(mu + (long)h * k * d, sq, sk, k, d, lam);
+    }
+    free(xhat);
+    free(s);
+    free(label);
+    free(sq);
+    free(sk);
+}
+
+/* O1 + O2 + O12 for every (b, h): idx [B][H][k][n/k]. */
+void orc_route_partition_all(const double *x, const double *mu, int B, int H, long n, int d,
+                             int k, int32_t *idx)
+{
+    double *xhat = (double *)malloc(sizeof(double) * (size_t)n * (size_t)d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)k * (size_t)n);
+    for (long u = 0; u < (long)B * H; ++u) {
+        int h = (int)(u % H);
+        orc_normalize(x + u * n * d, n, d, xhat, NULL);
+        orc_scores(xhat, mu + (long)h * k * d, n, d, k, s);
+        orc_partition(s, n, k, idx + u * n);
+    }
+    free(xhat);
+    free(s);
 }

@@ -42,6 +42,14 @@ MUTANTS = {
                                 "-INFINITY;\n        for (long j = lo; j <= hi; ++j) {\n            "
                                 "double dot = 0.0;\n            for (int e = 0; e < d; ++e)\n"
                                 "                dot += q[i * d + e] * kk[j * d + e];\n            logit"),
+    "blocked_lookback_ignored": ("long lo = (i / block - lookback) * block;",
+                                 "long lo = (i / block) * block;"),
+    "argmax_ties_to_higher": ("            if (x > b1) {\n                b2 = b1;",
+                              "            if (x >= b1) {\n                b2 = b1;"),
+    "partition_smallest_first": ("    if (x->s > y->s) return -1;\n    if (x->s < y->s) return 1;\n"
+                                 "    return (x->t < y->t) ? -1 : (x->t > y->t);\n}\n\n/* Partition",
+                                 "    if (x->s < y->s) return -1;\n    if (x->s > y->s) return 1;\n"
+                                 "    return (x->t < y->t) ? -1 : (x->t > y->t);\n}\n\n/* Partition"),
     "local_bwd_softmax_sign": ("double dl = P[j - lo] * (dP[j - lo] - D);",
                                "double dl = P[j - lo] * (dP[j - lo] + D);"),
     "local_bwd_dk_from_keys": ("dk[j * d + e] += scale * dl * q[i * d + e];",

@@ -603,3 +603,105 @@ def test_layer_backward_matches_autograd(orc):
     np.testing.assert_allclose(got["dx"], tx.grad.numpy(), atol=1e-10)
     np.testing.assert_allclose(got["dw_in"], twi.grad.numpy(), atol=1e-10)
     np.testing.assert_allclose(got["dw_o"], two.grad.numpy(), atol=1e-10)
+
+
+# ---- variants: blocked local attention, nearest-centroid assignment, partition ---------
+
+def _block_mask(n, block, lookback):
+    i = np.arange(n)
+    lo = np.maximum(0, (i // block - lookback) * block)
+    return (i[None, :] <= i[:, None]) & (i[None, :] >= lo[:, None])
+
+
+@pytest.mark.parametrize("n,block,lookback", [(40, 8, 1), (37, 5, 0), (30, 7, 2), (20, 32, 0)])
+def test_o10_blocked_against_masked_sdpa(orc, n, block, lookback):
+    r = _rng(40)
+    q, kk, v = (r.standard_normal((2, 2, n, 6)) for _ in range(3))
+    out = orc.local_attn_blocked(q, kk, v, block, lookback, 0.8)
+    mask = torch.from_numpy(_block_mask(n, block, lookback))
+    np.testing.assert_allclose(out, _sdpa(q, kk, v, 0.8, mask=mask), atol=1e-12)
+    if block >= n and lookback == 0:                 # one block: plain causal attention
+        np.testing.assert_allclose(out, _sdpa(q, kk, v, 0.8, True), atol=1e-12)
+
+
+def test_o10_block_of_one_is_identity(orc):
+    r = _rng(41)
+    q, kk, v = (r.standard_normal((1, 1, 15, 4)) for _ in range(3))
+    np.testing.assert_allclose(orc.local_attn_blocked(q, kk, v, 1, 0, 1.0), v, atol=1e-14)
+
+
+def test_o11_argmax_is_nearest_centroid(orc):
+    """For unit tokens and unit centroids the largest inner product is the
+    smallest Euclidean distance (scipy cdist, an independent route)."""
+    r = _rng(42)
+    x = r.standard_normal((2, 3, 50, 8))
+    mu = _unit(r.standard_normal((3, 7, 8)))
+    label, margin = orc.argmax_labels(x, mu)
+    xh = _unit(x)
+    for b in range(2):
+        for h in range(3):
+            dist = cdist(xh[b, h], mu[h])
+            np.testing.assert_array_equal(label[b, h], np.argmin(dist, axis=1))
+            srt = np.sort(xh[b, h] @ mu[h].T, axis=1)
+            np.testing.assert_allclose(margin[b, h], srt[:, -1] - srt[:, -2], atol=1e-12)
+
+
+def test_o11_argmax_ties_to_lower_index(orc):
+    x = np.array([[[[1.0, 0.0], [0.0, 1.0]]]])
+    mu = np.array([[[1.0, 0.0], [1.0, 0.0], [0.0, 1.0]]])      # centroids 0 and 1 equal
+    label, margin = orc.argmax_labels(x, mu)
+    np.testing.assert_array_equal(label[0, 0], [0, 2])
+    assert margin[0, 0, 0] == 0.0
+
+
+def test_o11_ema_with_one_centroid_is_the_full_membership(orc):
+    """k = 1: every token is assigned to the only centroid, as O6 with w = n."""
+    r = _rng(43)
+    q, kk = r.standard_normal((2, 2, 30, 5)), r.standard_normal((2, 2, 30, 5))
+    mu = r.standard_normal((2, 1, 5))
+    idx = np.broadcast_to(np.arange(30, dtype=np.int32), (2, 2, 1, 30))
+    np.testing.assert_allclose(orc.centroid_update_argmax(mu, q, kk, 0.8),
+                               orc.centroid_update(mu, q, kk, idx, 0.8), atol=1e-12)
+
+
+def test_o11_ema_hand_example(orc):
+    """Two 2-d tokens, two centroids: token 0 is nearest to centroid 0, token 1
+    to centroid 1; with q = k, mu_c <- lam mu_c + (1 - lam) x^_c."""
+    x = np.array([[[[3.0, 0.0], [0.0, -2.0]]]])
+    mu = np.array([[[1.0, 0.0], [0.0, -1.0]]])
+    got = orc.centroid_update_argmax(mu, x, x, 0.75)
+    np.testing.assert_allclose(got, [[[1.0, 0.0], [0.0, -1.0]]], atol=1e-15)
+    mu2 = np.array([[[0.6, 0.8], [0.0, -1.0]]])
+    got2 = orc.centroid_update_argmax(mu2, x, x, 0.5)
+    np.testing.assert_allclose(got2, [[[0.8, 0.4], [0.0, -1.0]]], atol=1e-15)
+
+
+def test_o12_partition_invariants_and_balanced_case(orc):
+    r = _rng(44)
+    n, k, d = 48, 4, 6
+    x = r.standard_normal((2, 2, n, d))
+    mu = _unit(r.standard_normal((2, k, d)))
+    idx = orc.route_partition(x, mu)
+    assert idx.shape == (2, 2, k, n // k)
+    for b in range(2):
+        for h in range(2):
+            np.testing.assert_array_equal(np.sort(idx[b, h].ravel()), np.arange(n))
+            assert np.all(np.diff(idx[b, h], axis=1) > 0)
+    # tokens built so that each centroid is the nearest one of exactly n/k tokens
+    cent = _unit(r.standard_normal((k, d)))
+    toks = np.repeat(cent, n // k, axis=0) + 0.01 * r.standard_normal((n, d))
+    perm = r.permutation(n)
+    xb = toks[perm][None, None]
+    got = orc.route_partition(xb, cent[None])
+    lab = np.argmin(cdist(_unit(xb[0, 0]), cent), axis=1)
+    for c in range(k):
+        np.testing.assert_array_equal(got[0, 0, c], np.flatnonzero(lab == c))
+
+
+def test_o12_partition_hand_example(orc):
+    """All four tokens prefer centroid 0: its cluster takes the two with the
+    largest scores against it, centroid 1 the other two."""
+    x = np.array([[[[1.0, 0.1], [1.0, 0.5], [1.0, 0.0], [1.0, 0.3]]]])
+    mu = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    idx = orc.route_partition(x, mu)
+    np.testing.assert_array_equal(idx[0, 0], [[0, 2], [1, 3]])
