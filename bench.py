@@ -292,6 +292,46 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
                     "5 products per visible pair)"}
 
 
+def time_variants(rt, cfg, inp, reps=20):
+    """The variants at the workload's shapes: blocked local attention (blocks of
+    the window, one block of look-back) on the local heads, partition-style
+    routing and the nearest-centroid update on the routed heads."""
+    B, R, L, n, d, k = cfg.B, cfg.R, cfg.L, cfg.n, cfg.d, cfg.k
+    scale = 1.0 / math.sqrt(d)
+    qk = dev(inp["qk"])
+    ql, kl, vl = dev(inp["q_local"]), dev(inp["k_local"]), dev(inp["v_local"])
+    mu = torch.from_numpy(inp["mu"].astype(np.float32)).cuda()
+    out_l = torch.empty_like(ql)
+    inv = torch.empty((B, R, n), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, R, k, n // k), dtype=torch.int32, device="cuda")
+    ws_p = torch.empty(rt.workspace_bytes("route_partition", B, R, n, d, k, 1), dtype=torch.uint8,
+                       device="cuda")
+    ws_e = torch.empty(rt.workspace_bytes("centroid_update_argmax", B, R, n, d, k, 1),
+                       dtype=torch.uint8, device="cuda")
+    calls = {
+        "rt_local_attn_blocked": lambda: rt.local_attn_blocked(ql, kl, vl, cfg.window, 1,
+                                                               scale=scale, out=out_l),
+        "rt_route_partition": lambda: rt.route_partition(qk, mu, out=(inv, idx), ws=ws_p),
+        "rt_centroid_update_argmax": lambda: rt.centroid_update_argmax_(mu, qk, lam=cfg.lam,
+                                                                        ws=ws_e),
+    }
+    per = {}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        per[name] = a.elapsed_time(b) / reps
+    return {"per_call_ms": per,
+            "note": f"blocked local: blocks of {cfg.window}, one block of look-back, {L} heads; "
+                    f"partition: n/k = {n // k} tokens a cluster, {R} heads; nearest-centroid "
+                    f"update: shared q/k, {R} heads"}
+
+
 def sweep_configs(only=None):
     """The long layer's shape (B=1, 8 routed + 4 local heads of width 128, window
     512) at n = 1K .. 64K with k = sqrt(n) rounded down to a power of two and
@@ -598,6 +638,8 @@ def main():
     }
     if args.workload == "long" and not args.no_stack:
         res["stack"] = time_stack(rt, S.STACKS["long_stack"])
+    if args.workload == "long":
+        res["variants"] = time_variants(rt, cfg, inp)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, scale)
     print(json.dumps(res), flush=True)

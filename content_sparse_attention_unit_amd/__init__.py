@@ -17,7 +17,8 @@ import torch
 
 __all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
            "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
-           "out_proj_bwd", "in_proj_bwd", "workspace_bytes", "library_path",
+           "out_proj_bwd", "in_proj_bwd", "local_attn_blocked", "centroid_update_argmax_",
+           "route_partition", "workspace_bytes", "library_path",
            "mask_words", "RTError", "RT_OP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +27,8 @@ _lib = None
 
 RT_F32, RT_BF16 = 0, 1
 RT_OP = {"route": 0, "routed_attn": 1, "local_attn": 2, "centroid_update": 3,
-         "routed_attn_bwd": 4, "local_attn_bwd": 5}
+         "routed_attn_bwd": 4, "local_attn_bwd": 5, "centroid_update_argmax": 6,
+         "route_partition": 7}
 _STATUS = {0: "RT_OK", 1: "RT_EINVAL", 2: "RT_EUNSUPPORTED", 3: "RT_EHIP"}
 
 
@@ -66,6 +68,9 @@ def _load():
         "rt_normalize_bwd": [P, I, P, P, P, ctypes.c_long, I, P, P],
         "rt_out_proj_bwd": [P, P, P, P, I, I, I, I, I, I, P, P, P, P],
         "rt_in_proj_bwd": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P],
+        "rt_local_attn_blocked": [P, P, P, I, I, I, I, I, I, I, F, P, I, P],
+        "rt_centroid_update_argmax": [P, P, P, I, I, I, I, I, I, F, P, Z, P],
+        "rt_route_partition": [P, I, P, I, I, I, I, I, P, P, P, P, Z, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -379,3 +384,58 @@ def in_proj_bwd(x, w_in, dqk, dv, dq_l=None, dk_l=None, dv_l=None, dres=None, ou
                               _ptr(dv_l), _ptr(dres), B, n, dm, d, R, L, *(_ptr(t) for t in out),
                               _stream(dev)))
     return out
+
+
+# ---- variants ------------------------------------------------------------------------
+
+def local_attn_blocked(q, kk, v, block: int, lookback: int = 1, *, scale=None, out_dtype=None,
+                       out=None):
+    """Blocked local attention (causal): position i sees its own block of
+    `block` positions and the `lookback` blocks before it."""
+    lib = _load()
+    dev = _gpu(q, kk, v)
+    B, H, n, d = q.shape
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    odt = q.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(q.shape, dtype=odt, device=dev)
+    _gpu(out)
+    _check(lib.rt_local_attn_blocked(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), B, H, n, d,
+                                     int(block), int(lookback), sc, _ptr(out), _dtype_code(out),
+                                     _stream(dev)))
+    return out
+
+
+def centroid_update_argmax_(mu, q, kk=None, lam: float = 0.999, ws=None):
+    """In-place centroid update with nearest-centroid assignments (each query
+    and key counted once, for its own nearest centroid)."""
+    lib = _load()
+    dev = _gpu(mu, q, kk)
+    B, H, n, d = q.shape
+    k = mu.shape[1]
+    ws, _ = _workspace("centroid_update_argmax", dev, B, H, n, d, k, 1, ws)
+    _check(lib.rt_centroid_update_argmax(_ptr(mu), _ptr(q), _ptr(kk), _dtype_code(q), B, H, n, d,
+                                         k, float(lam), _ptr(ws),
+                                         0 if ws is None else ws.numel(), _stream(dev)))
+    return mu
+
+
+def route_partition(qk, mu, *, want_mask=False, out=None, ws=None):
+    """Partition-style balanced routing: returns (inv_norm, idx [B,H,k,n/k])
+    and the one-bit-per-token membership mask when asked."""
+    lib = _load()
+    dev = _gpu(qk, mu)
+    B, H, n, d = qk.shape
+    k = mu.shape[1]
+    if out is None:
+        inv = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+        idx = torch.empty((B, H, k, n // k), dtype=torch.int32, device=dev)
+        mask = (torch.empty((B, H, n, mask_words(k)), dtype=torch.int32, device=dev)
+                if want_mask else None)
+    else:
+        inv, idx, mask = (tuple(out) + (None,))[:3]
+    ws, _ = _workspace("route_partition", dev, B, H, n, d, k, 1, ws)
+    _check(lib.rt_route_partition(_ptr(qk), _dtype_code(qk), _ptr(mu), B, H, n, d, k, _ptr(inv),
+                                  _ptr(idx), _ptr(mask), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(dev)))
+    return (inv, idx, mask) if mask is not None else (inv, idx)

@@ -76,6 +76,15 @@ size_t attn_ws(int B, int H, int n, int d, int k, int w) {
 
 bool out_dtype_ok(int t) { return t == RT_F32 || t == RT_BF16; }
 
+// rt_centroid_update_argmax workspace, for either side (q, then kk when given):
+// inverse norms, labels, best scores [B*H*n] each, then the chunk partial sums
+// [chunks][H][k][d] float32; sized for distinct q and kk.
+size_t argmax_side_ws(int B, int H, int n, int d, int k) {
+    return align256((size_t)B * H * n * 3 * 4) +
+           align256((size_t)rt::label_chunks(B, n) * H * k * d * sizeof(float));
+}
+size_t argmax_ema_ws(int B, int H, int n, int d, int k) { return 2 * argmax_side_ws(B, H, n, d, k); }
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +112,8 @@ size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
         case RT_OP_CENTROID_UPDATE: return 0;
         case RT_OP_ROUTED_ATTN_BWD: return rt::bwd_workspace_bytes(B * H, n, d, k, w);
         case RT_OP_LOCAL_ATTN_BWD: return rt::local_bwd_workspace_bytes(B * H, n);
+        case RT_OP_CENTROID_UPDATE_ARGMAX: return argmax_ema_ws(B, H, n, d, k);
+        case RT_OP_ROUTE_PARTITION: return (size_t)B * H * n * 2 * 4;
         default: return (size_t)-1;
     }
 }
@@ -203,7 +214,7 @@ rt_status rt_local_attn(const void* q, const void* kk, const void* v, int dtype,
     if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
     if (!out_dtype_ok(out_dtype))
         return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
-    hipError_t e = rt::launch_local_attn(q, kk, v, dtype, B * H, n, d, window, scale, causal, out,
+    hipError_t e = rt::launch_local_attn(q, kk, v, dtype, B * H, n, d, window, -1, scale, causal, out,
                                          out_dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
@@ -536,6 +547,97 @@ rt_status rt_in_proj_bwd(const void* x, const void* w_in, const float* dqk, cons
     q.n = n;
     q.d = d;
     e = rt::launch_gemm_bwd(rt::GEMM_DWIN, q, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_local_attn_blocked(const void* q, const void* kk, const void* v, int dtype, int B,
+                                int H, int n, int d, int block, int lookback, float scale,
+                                void* out, int out_dtype, void* stream) {
+    static const char* fn = "rt_local_attn_blocked";
+    g_err[0] = 0;
+    if (!q || !kk || !v || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    if (block < 1) return fail(RT_EINVAL, "%s: block=%d must be >= 1", fn, block);
+    if (lookback < 0) return fail(RT_EINVAL, "%s: lookback=%d must be >= 0", fn, lookback);
+    if ((long long)block * (lookback + 1) > (1LL << 30))
+        return fail(RT_EUNSUPPORTED, "%s: block*(lookback+1) too large", fn);
+    if (out == q || out == kk || out == v) return fail(RT_EINVAL, "%s: out aliases an input", fn);
+    if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (!out_dtype_ok(out_dtype))
+        return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
+    hipError_t e = rt::launch_local_attn(q, kk, v, dtype, B * H, n, d, block, lookback, scale, 1,
+                                         out, out_dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_centroid_update_argmax(float* mu, const void* q, const void* kk, int dtype, int B,
+                                    int H, int n, int d, int k, float lambda, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_centroid_update_argmax";
+    g_err[0] = 0;
+    if (!mu || !q) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    if (k <= 0) return fail(RT_EINVAL, "%s: k=%d must be positive", fn, k);
+    if (k > 65535) return fail(RT_EUNSUPPORTED, "%s: k=%d exceeds 65535", fn, k);
+    if (!(lambda >= 0.f && lambda <= 1.f))
+        return fail(RT_EINVAL, "%s: lambda=%g outside [0, 1]", fn, (double)lambda);
+    const size_t need = argmax_ema_ws(B, H, n, d, k);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t BHn = (size_t)B * H * n, side = argmax_side_ws(B, H, n, d, k);
+    const size_t part_off = align256(BHn * 3 * 4);
+    float* inv[2];
+    int32_t* lab[2];
+    float* part[2];
+    for (int i = 0; i < 2; ++i) {
+        char* base = static_cast<char*>(ws) + i * side;
+        inv[i] = reinterpret_cast<float*>(base);
+        lab[i] = reinterpret_cast<int32_t*>(base + BHn * 4);
+        part[i] = reinterpret_cast<float*>(base + part_off);
+    }
+    float* best[2] = {reinterpret_cast<float*>(static_cast<char*>(ws) + BHn * 8),
+                      reinterpret_cast<float*>(static_cast<char*>(ws) + side + BHn * 8)};
+    const bool shared = (kk == nullptr || kk == q);
+    hipError_t e = rt::launch_nearest(q, dtype, mu, B, H, n, d, k, inv[0], lab[0], best[0],
+                                      nullptr, s);
+    if (e == hipSuccess && !shared)
+        e = rt::launch_nearest(kk, dtype, mu, B, H, n, d, k, inv[1], lab[1], best[1], nullptr, s);
+    if (e == hipSuccess)
+        e = rt::launch_label_ema(mu, q, inv[0], lab[0], shared ? nullptr : kk, inv[1], lab[1],
+                                 dtype, B, H, n, d, k, lambda, part[0], part[1], s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_route_partition(const void* qk, int dtype, const float* mu, int B, int H, int n,
+                             int d, int k, float* inv_norm, int32_t* idx, uint32_t* member_mask,
+                             void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_route_partition";
+    g_err[0] = 0;
+    if (!qk || !mu || !inv_norm || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, dtype, B, H, n, d);
+    if (st != RT_OK) return st;
+    if (k <= 0) return fail(RT_EINVAL, "%s: k=%d must be positive", fn, k);
+    if (k > 256) return fail(RT_EUNSUPPORTED, "%s: k=%d exceeds 256", fn, k);
+    if (n % k != 0) return fail(RT_EINVAL, "%s: n=%d is not a multiple of k=%d", fn, n, k);
+    if (n > rt::kPartitionMaxN)
+        return fail(RT_EUNSUPPORTED, "%s: n=%d exceeds %d", fn, n, rt::kPartitionMaxN);
+    const size_t need = (size_t)B * H * n * 2 * 4;
+    if (ws == nullptr || ws_bytes < need)
+        return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* label = static_cast<int32_t*>(ws);
+    float* best = reinterpret_cast<float*>(label + (size_t)B * H * n);
+    hipError_t e = rt::launch_nearest(qk, dtype, mu, B, H, n, d, k, inv_norm, label, best,
+                                      member_mask, s);
+    if (e == hipSuccess) e = rt::launch_partition(label, best, B * H, n, k, idx, member_mask, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

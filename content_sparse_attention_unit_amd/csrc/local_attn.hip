@@ -5,7 +5,10 @@
 // heads with local attention over a window of recent positions (windows of
 // 512 and 1024 are the ones reported).  Position i attends, with ordinary
 // softmax attention, to positions [i - window + 1, i] (causal) or to the band
-// |i - j| < window (non-causal).
+// |i - j| < window (non-causal).  The blocked variant (lookback >= 0, causal):
+// the sequence is cut into blocks of `window` positions and position i sees
+// the positions of its own block and of the `lookback` blocks before it, not
+// later than i; only the band's lower edge differs.
 //
 // local_attn_bf16_kernel: one workgroup = 128 queries in 8 blocks of 16, each
 // block served by two waves (16 waves): key/value tiles of 64 rows are staged
@@ -129,7 +132,8 @@ template <int D, typename OutT>
 __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __restrict__ q,
                                                               const u16* __restrict__ kk,
                                                               const u16* __restrict__ v, int n,
-                                                              int window, float scale, int causal,
+                                                              int window, int lookback,
+                                                              float scale, int causal,
                                                               OutT* __restrict__ out) {
     using C = LocalCfg<D>;
     __shared__ __attribute__((aligned(16))) u16 lk[2][C::KT * C::LDX];
@@ -165,11 +169,16 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
     }
     // keys needed by the workgroup / by this wave's block; keys in [clo, chi]
     // are visible to every query of the block
-    const int lo = max(0, q0 - window + 1);
+    // first key of position i's band (non-decreasing in i)
+    auto band_lo = [&](int i) {
+        return lookback < 0 ? i - window + 1 : max(0, (i / window - lookback) * window);
+    };
+    const int qlo = band_lo(qi);
+    const int lo = max(0, band_lo(q0));
     const int hi = causal ? min(n - 1, q0 + C::QT - 1) : min(n - 1, q0 + C::QT - 1 + window - 1);
-    const int blo = qb0 - window + 1;
+    const int blo = band_lo(qb0);
     const int bhi = causal ? qb0 + 15 : qb0 + 15 + window - 1;
-    const int clo = qb0 + 15 - window + 1;
+    const int clo = band_lo(qb0 + 15);
     const int chi = min(n - 1, causal ? qb0 : qb0 + window - 1);
 
     f32x4 o[C::NJ];
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
                 _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
                     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                          \
                         const int j = kh_ + 16 * kb + 4 * g + i;                             \
-                        const bool ok = j < n && j > qi - window &&                          \
+                        const bool ok = j < n && j >= qlo &&                                 \
                                         (causal ? j <= qi : j < qi + window);                \
                         sv[kb][i] = ok ? sv[kb][i] : -INFINITY;                              \
                     }                                                                        \
@@ -281,7 +290,8 @@ template <int D, typename OutT>
 __global__ __launch_bounds__(64) void local_attn_f32_kernel(const float* __restrict__ q,
                                                             const float* __restrict__ kk,
                                                             const float* __restrict__ v, int n,
-                                                            int window, float scale, int causal,
+                                                            int window, int lookback,
+                                                            float scale, int causal,
                                                             OutT* __restrict__ out) {
     __shared__ float lq[D];
     __shared__ float lp[64];
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(64) void local_attn_f32_kernel(const float* __restr
     const long base = (long)bh * n;
     for (int e = lane; e < D; e += 64) lq[e] = q[(base + i) * D + e];
     __syncthreads();
-    const int lo = max(0, i - window + 1);
+    const int lo = lookback < 0 ? max(0, i - window + 1) : max(0, (i / window - lookback) * window);
     const int hi = causal ? i : min(n - 1, i + window - 1);
     constexpr int PER = (D + 63) / 64;
     float acc[PER];
@@ -333,39 +343,44 @@ __global__ __launch_bounds__(64) void local_attn_f32_kernel(const float* __restr
 
 template <int D, typename OutT>
 void launch_local_d(const void* q, const void* kk, const void* v, int dtype, int BH, int n,
-                    int window, float scale, int causal, void* out, hipStream_t s) {
+                    int window, int lookback, float scale, int causal, void* out,
+                    hipStream_t s) {
     if (dtype == 1)
         hipLaunchKernelGGL((local_attn_bf16_kernel<D, OutT>),
                            dim3((n + LocalCfg<D>::QT - 1) / LocalCfg<D>::QT, BH),
                            dim3(LocalCfg<D>::NT), 0, s,
-                           (const u16*)q, (const u16*)kk, (const u16*)v, n, window, scale, causal,
+                           (const u16*)q, (const u16*)kk, (const u16*)v, n, window, lookback,
+                           scale, causal,
                            (OutT*)out);
     else
         hipLaunchKernelGGL((local_attn_f32_kernel<D, OutT>), dim3(n, BH), dim3(64), 0, s,
-                           (const float*)q, (const float*)kk, (const float*)v, n, window, scale,
+                           (const float*)q, (const float*)kk, (const float*)v, n, window, lookback,
+                           scale,
                            causal, (OutT*)out);
 }
 
 template <typename OutT>
 void launch_local_outt(const void* q, const void* kk, const void* v, int dtype, int BH, int n,
-                       int d, int window, float scale, int causal, void* out, hipStream_t s) {
+                       int d, int window, int lookback, float scale, int causal, void* out,
+                       hipStream_t s) {
     switch (d) {
-        case 16: launch_local_d<16, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
-        case 32: launch_local_d<32, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
-        case 64: launch_local_d<64, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
-        default: launch_local_d<128, OutT>(q, kk, v, dtype, BH, n, window, scale, causal, out, s); break;
+        case 16: launch_local_d<16, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
+        case 32: launch_local_d<32, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
+        case 64: launch_local_d<64, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
+        default: launch_local_d<128, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
     }
 }
 
 }  // namespace
 
 hipError_t launch_local_attn(const void* q, const void* kk, const void* v, int dtype, int BH,
-                             int n, int d, int window, float scale, int causal, void* out,
-                             int out_dtype, hipStream_t s) {
+                             int n, int d, int window, int lookback, float scale, int causal,
+                             void* out, int out_dtype, hipStream_t s) {
     if (out_dtype == 1)
-        launch_local_outt<u16>(q, kk, v, dtype, BH, n, d, window, scale, causal, out, s);
+        launch_local_outt<u16>(q, kk, v, dtype, BH, n, d, window, lookback, scale, causal, out, s);
     else
-        launch_local_outt<float>(q, kk, v, dtype, BH, n, d, window, scale, causal, out, s);
+        launch_local_outt<float>(q, kk, v, dtype, BH, n, d, window, lookback, scale, causal, out,
+                                 s);
     return hipGetLastError();
 }
 

@@ -41,14 +41,18 @@ struct ScoreCfg {
     static constexpr int TOK = 32 * NT / 64;           // tokens per workgroup (32 per wave)
 };
 
-template <int D>
+// ARGMAX: instead of the scores, each token's nearest centroid (largest score,
+// ties to the lower index) and that score go to label[] and best[].
+template <int D, bool ARGMAX>
 __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* __restrict__ qk,
                                                          const float* __restrict__ mu, int H,
                                                          int n, int k,
                                                          float* __restrict__ inv_norm,
                                                          float* __restrict__ scores,
                                                          u16* __restrict__ qk_hat,
-                                                         uint32_t* __restrict__ mask, int KW) {
+                                                         uint32_t* __restrict__ mask, int KW,
+                                                         int32_t* __restrict__ label,
+                                                         float* __restrict__ best) {
     using C = ScoreCfg<D>;
     __shared__ __attribute__((aligned(16))) u16 lmu[3][C::KC][C::LD];
 
@@ -155,6 +159,8 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
         }
     }
 
+    float bs[2] = {-INFINITY, -INFINITY};   // ARGMAX: this lane's best score and centroid
+    int bc[2] = {0, 0};
     for (int c0 = 0; c0 < k; c0 += C::KC) {
         if (c0 > 0) {
             __syncthreads();          // previous chunk's MFMAs are done with lmu
@@ -179,22 +185,50 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
             for (int i = 0; i < 4; ++i) {
                 const int c = c0 + cb * 16 + 4 * g + i;
                 if (c < k) {
-                    float* row = scores + ((long)bh * k + c) * n;
-                    if (tok[0] < n) row[tok[0]] = acc0[i] * inv[0];
-                    if (tok[1] < n) row[tok[1]] = acc1[i] * inv[1];
+                    const float s0 = acc0[i] * inv[0], s1 = acc1[i] * inv[1];
+                    if constexpr (ARGMAX) {
+                        // centroids arrive in ascending order for this lane
+                        if (s0 > bs[0]) { bs[0] = s0; bc[0] = c; }
+                        if (s1 > bs[1]) { bs[1] = s1; bc[1] = c; }
+                    } else {
+                        float* row = scores + ((long)bh * k + c) * n;
+                        if (tok[0] < n) row[tok[0]] = s0;
+                        if (tok[1] < n) row[tok[1]] = s1;
+                    }
                 }
+            }
+        }
+    }
+    if constexpr (ARGMAX) {
+        // the four lanes of a token (g = 0..3) hold disjoint centroids
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float os = __shfl_xor(bs[tb], off);
+                const int oc = __shfl_xor(bc[tb], off);
+                if (os > bs[tb] || (os == bs[tb] && oc < bc[tb])) {
+                    bs[tb] = os;
+                    bc[tb] = oc;
+                }
+            }
+            if (g == 0 && tok[tb] < n) {
+                label[base + tok[tb]] = bc[tb];
+                best[base + tok[tb]] = bs[tb];
             }
         }
     }
 }
 
-template <int D>
+template <int D, bool ARGMAX>
 __global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict__ qk,
                                                         const float* __restrict__ mu, int H, int n,
                                                         int k, float* __restrict__ inv_norm,
                                                         float* __restrict__ scores,
                                                         float* __restrict__ qk_hat,
-                                                        uint32_t* __restrict__ mask, int KW) {
+                                                        uint32_t* __restrict__ mask, int KW,
+                                                        int32_t* __restrict__ label,
+                                                        float* __restrict__ best) {
     constexpr int KC = 8192 / D;  // 32 KB of centroids per chunk
     __shared__ float lmu[KC * D];
     const int bh = blockIdx.y, h = bh % H;
@@ -215,6 +249,8 @@ __global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict_
         if (qk_hat != nullptr)
             for (int i = 0; i < D; ++i) qk_hat[(base + t) * D + i] = x[i] * inv;
     }
+    float bs = -INFINITY;
+    int bc = 0;
     for (int c0 = 0; c0 < k; c0 += KC) {
         __syncthreads();
         const int cn = min(KC, k - c0);
@@ -225,8 +261,21 @@ __global__ __launch_bounds__(256) void score_f32_kernel(const float* __restrict_
                 float acc = 0.f;
 #pragma unroll
                 for (int i = 0; i < D; ++i) acc = fmaf(x[i], lmu[c * D + i], acc);
-                scores[((long)bh * k + c0 + c) * n + t] = acc * inv;
+                if constexpr (ARGMAX) {
+                    if (acc * inv > bs) {
+                        bs = acc * inv;
+                        bc = c0 + c;
+                    }
+                } else {
+                    scores[((long)bh * k + c0 + c) * n + t] = acc * inv;
+                }
             }
+        }
+    }
+    if constexpr (ARGMAX) {
+        if (t < n) {
+            label[base + t] = bc;
+            best[base + t] = bs;
         }
     }
 }
@@ -637,17 +686,90 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     });
 }
 
-template <int D>
+// Partition-style balanced clusters, one workgroup per (batch, head): every
+// token sits in exactly one cluster of w = n / k.  A bitonic sort in LDS orders
+// the tokens by (nearest centroid, descending score against it, position);
+// rank r goes to cluster r / w; a second sort by (cluster, position) lists each
+// cluster by ascending position.  Keys are 64-bit: label | score key | token.
+
+__device__ __forceinline__ void bitonic_sort_lds(unsigned long long* keys, int n2) {
+    for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < (n2 >> 1); i += blockDim.x) {
+                const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
+                const unsigned long long a = keys[lo], b = keys[hi];
+                const bool up = (lo & size) == 0;
+                if ((a > b) == up) {
+                    keys[lo] = b;
+                    keys[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__global__ __launch_bounds__(1024) void partition_kernel(const int32_t* __restrict__ label,
+                                                         const float* __restrict__ best, int n,
+                                                         int k, int w, int32_t* __restrict__ idx,
+                                                         uint32_t* __restrict__ mask, int KW) {
+    __shared__ unsigned long long keys[kPartitionMaxN];
+    const long bh = blockIdx.x;
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (int t = threadIdx.x; t < n2; t += blockDim.x) {
+        unsigned long long key = ~0ull;   // padding sorts last
+        if (t < n) {
+            const uint32_t sk = ~order_key(best[bh * n + t]);   // larger score, smaller key
+            key = ((unsigned long long)(uint32_t)label[bh * n + t] << 56) |
+                  ((unsigned long long)sk << 24) | (unsigned long long)t;
+        }
+        keys[t] = key;
+    }
+    __syncthreads();
+    bitonic_sort_lds(keys, n2);
+    // rank r -> cluster r / w; re-key by (cluster, position)
+    for (int r = threadIdx.x; r < n2; r += blockDim.x) {
+        if (r < n) {
+            const unsigned long long t = keys[r] & 0xffffffull;
+            keys[r] = ((unsigned long long)(r / w) << 24) | t;
+        }
+    }
+    __syncthreads();
+    bitonic_sort_lds(keys, n2);
+    for (int r = threadIdx.x; r < n; r += blockDim.x) {
+        const int cl = (int)(keys[r] >> 24), t = (int)(keys[r] & 0xffffffull);
+        idx[(bh * k + cl) * w + (r - cl * w)] = t;
+        if (mask != nullptr) mask[(bh * n + t) * KW + (cl >> 5)] = 1u << (cl & 31);
+    }
+}
+
+template <int D, bool ARGMAX>
 void launch_score_d(const void* qk, int dtype, const float* mu, int BH, int H, int n, int k,
-                    float* inv_norm, float* scores, void* qk_hat, uint32_t* mask, hipStream_t s) {
+                    float* inv_norm, float* scores, void* qk_hat, uint32_t* mask, int32_t* label,
+                    float* best, hipStream_t s) {
     if (dtype == 1) {
         dim3 grid((n + ScoreCfg<D>::TOK - 1) / ScoreCfg<D>::TOK, BH);
-        hipLaunchKernelGGL(score_bf16_kernel<D>, grid, dim3(ScoreCfg<D>::NT), 0, s, (const u16*)qk, mu, H, n,
-                           k, inv_norm, scores, (u16*)qk_hat, mask, mask_words(k));
+        hipLaunchKernelGGL((score_bf16_kernel<D, ARGMAX>), grid, dim3(ScoreCfg<D>::NT), 0, s,
+                           (const u16*)qk, mu, H, n, k, inv_norm, scores, (u16*)qk_hat, mask,
+                           mask_words(k), label, best);
     } else {
         dim3 grid((n + 255) / 256, BH);
-        hipLaunchKernelGGL(score_f32_kernel<D>, grid, dim3(256), 0, s, (const float*)qk, mu, H, n,
-                           k, inv_norm, scores, (float*)qk_hat, mask, mask_words(k));
+        hipLaunchKernelGGL((score_f32_kernel<D, ARGMAX>), grid, dim3(256), 0, s, (const float*)qk,
+                           mu, H, n, k, inv_norm, scores, (float*)qk_hat, mask, mask_words(k),
+                           label, best);
+    }
+}
+
+template <bool ARGMAX>
+void launch_score_any(const void* qk, int dtype, const float* mu, int BH, int H, int n, int d,
+                      int k, float* inv_norm, float* scores, void* qk_hat, uint32_t* mask,
+                      int32_t* label, float* best, hipStream_t s) {
+    switch (d) {
+        case 16: launch_score_d<16, ARGMAX>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, label, best, s); break;
+        case 32: launch_score_d<32, ARGMAX>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, label, best, s); break;
+        case 64: launch_score_d<64, ARGMAX>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, label, best, s); break;
+        default: launch_score_d<128, ARGMAX>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, label, best, s); break;
     }
 }
 
@@ -663,13 +785,23 @@ void launch_topw_k(const float* scores, int rows, int n, int w, int32_t* idx, in
 hipError_t launch_score(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
                         int k, float* inv_norm, float* scores, void* qk_hat, uint32_t* mask,
                         hipStream_t s) {
-    const int BH = B * H;
-    switch (d) {
-        case 16: launch_score_d<16>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
-        case 32: launch_score_d<32>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
-        case 64: launch_score_d<64>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
-        default: launch_score_d<128>(qk, dtype, mu, BH, H, n, k, inv_norm, scores, qk_hat, mask, s); break;
-    }
+    launch_score_any<false>(qk, dtype, mu, B * H, H, n, d, k, inv_norm, scores, qk_hat, mask,
+                            nullptr, nullptr, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_nearest(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
+                          int k, float* inv_norm, int32_t* label, float* best, uint32_t* mask,
+                          hipStream_t s) {
+    launch_score_any<true>(qk, dtype, mu, B * H, H, n, d, k, inv_norm, nullptr, nullptr, mask,
+                           label, best, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_partition(const int32_t* label, const float* best, int BH, int n, int k,
+                            int32_t* idx, uint32_t* mask, hipStream_t s) {
+    hipLaunchKernelGGL(partition_kernel, dim3(BH), dim3(1024), 0, s, label, best, n, k, n / k, idx,
+                       mask, mask_words(k));
     return hipGetLastError();
 }
 

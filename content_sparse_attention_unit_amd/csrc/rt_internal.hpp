@@ -18,6 +18,28 @@ constexpr int kMaxSeqTopw = 65536;
 
 // mask (nullable) [B*H*n][mask_words(k)]: zeroed by the score kernel, filled
 // by the top-w kernel.
+// Each token's nearest centroid (largest score, ties to the lower index) and
+// that score, with the inverse norms (and the zeroed bitmask when mask != null).
+hipError_t launch_nearest(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
+                          int k, float* inv_norm, int32_t* label, float* best, uint32_t* mask,
+                          hipStream_t s);
+
+// Partition-style balanced clusters from the nearest-centroid labels and
+// scores (n a multiple of k, n <= kPartitionMaxN); mask (nullable) must be
+// zeroed.
+constexpr int kPartitionMaxN = 16384;
+hipError_t launch_partition(const int32_t* label, const float* best, int BH, int n, int k,
+                            int32_t* idx, uint32_t* mask, hipStream_t s);
+
+// The nearest-centroid EMA: per-chunk sums of each label's normalised rows
+// (part_q / part_k: label_chunks(B, n) * H * k * d floats each; kk == nullptr
+// for shared q/k), then the update.
+int label_chunks(int B, int n);
+hipError_t launch_label_ema(float* mu, const void* q, const float* q_inv, const int32_t* q_label,
+                            const void* kk, const float* k_inv, const int32_t* k_label, int dtype,
+                            int B, int H, int n, int d, int k, float lambda, float* part_q,
+                            float* part_k, hipStream_t s);
+
 hipError_t launch_score(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
                         int k, float* inv_norm, float* scores, void* qk_hat, uint32_t* mask,
                         hipStream_t s);
@@ -64,9 +86,12 @@ hipError_t launch_ema(float* mu, const void* q, const float* q_inv, const void* 
                       const float* k_inv, int dtype, const int32_t* idx, int B, int H, int n,
                       int d, int k, int w, float lambda, hipStream_t s);
 
+// lookback < 0: the sliding window [i - window + 1, i] (or the band when not
+// causal); lookback >= 0: blocks of `window` positions, own block and the
+// `lookback` before it (causal).
 hipError_t launch_local_attn(const void* q, const void* kk, const void* v, int dtype, int BH,
-                             int n, int d, int window, float scale, int causal, void* out,
-                             int out_dtype, hipStream_t s);
+                             int n, int d, int window, int lookback, float scale, int causal,
+                             void* out, int out_dtype, hipStream_t s);
 
 hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
                                    const float* q_inv, const float* k_inv, const int32_t* idx,

@@ -67,7 +67,9 @@ typedef enum {
     RT_OP_LOCAL_ATTN = 2,
     RT_OP_CENTROID_UPDATE = 3,
     RT_OP_ROUTED_ATTN_BWD = 4,
-    RT_OP_LOCAL_ATTN_BWD = 5
+    RT_OP_LOCAL_ATTN_BWD = 5,
+    RT_OP_CENTROID_UPDATE_ARGMAX = 6,
+    RT_OP_ROUTE_PARTITION = 7
 } rt_op;
 
 /*
@@ -322,6 +324,55 @@ rt_status rt_in_proj_bwd(const void *x, const void *w_in, const float *dqk, cons
                          const float *dq_l, const float *dk_l, const float *dv_l, const void *dres,
                          int B, int n, int dm, int d, int R, int L, float *dx, float *dw_in,
                          void *stream);
+
+/*
+ * Variants: readings the pages leave open, built beside the main path.
+ */
+
+/*
+ * rt_local_attn_blocked -- blocked (chunked) local attention.
+ *   The local heads' attention (arXiv abstract; summary §6) with the window
+ *   taken as blocks: the sequence is cut into blocks of `block` positions and
+ *   position i sees the positions of its own block and of the `lookback`
+ *   blocks before it that are not later than i (causal).  Softmax attention as
+ *   in rt_local_attn; arguments, layouts and limits as there.
+ */
+rt_status rt_local_attn_blocked(const void *q, const void *kk, const void *v, int dtype, int B,
+                                int H, int n, int d, int block, int lookback, float scale,
+                                void *out, int out_dtype, void *stream);
+
+/*
+ * rt_centroid_update_argmax -- the centroid update with nearest-centroid
+ *   assignments instead of the balanced memberships.
+ *   Summary §2, §4 (online spherical k-means): each unit-normalised query and
+ *   each key counts once, for the centroid with the largest inner product
+ *   (ties: the lower index); S_Q[c], S_K[c] are those sums over the whole
+ *   batch (ascending batch row and position) and
+ *       mu_c <- lambda * mu_c + (1 - lambda)/2 * (S_Q[c] + S_K[c]).
+ *   mu      [H][k][d] float32, updated in place.
+ *   q, kk   [B][H][n][d] dtype, raw; kk NULL (or == q) for shared q/k.
+ *   ws: rt_workspace_bytes(RT_OP_CENTROID_UPDATE_ARGMAX, B, H, n, d, k, 1)
+ *   bytes.  Deterministic (fixed summation order, no atomics).
+ */
+rt_status rt_centroid_update_argmax(float *mu, const void *q, const void *kk, int dtype, int B,
+                                    int H, int n, int d, int k, float lambda, void *ws,
+                                    size_t ws_bytes, void *stream);
+
+/*
+ * rt_route_partition -- partition-style balanced routing: every token in
+ *   exactly one cluster, every cluster w = n / k tokens.
+ *   Summary §4 (a token's assigned cluster; balanced clusters; the routing
+ *   cost of a sort): the tokens of a (batch, head) are ordered by (nearest
+ *   centroid, descending score against it, position) and cut into k
+ *   consecutive groups of w; group c is cluster c.
+ *   qk, mu, inv_norm as in rt_route.  idx out [B][H][k][n/k] int32, each row in
+ *   ascending position; member_mask optional out as in rt_route (one bit per
+ *   token).  n a multiple of k, n <= 16384, k <= 256.
+ *   ws: rt_workspace_bytes(RT_OP_ROUTE_PARTITION, ...) bytes.
+ */
+rt_status rt_route_partition(const void *qk, int dtype, const float *mu, int B, int H, int n,
+                             int d, int k, float *inv_norm, int32_t *idx, uint32_t *member_mask,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /* Workspace size in bytes for operation `op` at these sizes (0 if none,
  * (size_t)-1 if the sizes are invalid). */
