@@ -17,10 +17,12 @@ SRC = os.path.join(ROOT, "oracle")
 MUTANTS = {
     "self_not_visible": ("ok[s] = (!causal) || (p[s] <= p[r]);",
                          "ok[s] = (!causal) || (p[s] < p[r]);"),
-    "tie_break_flipped": ("return (x->t < y->t) ? -1 : (x->t > y->t);",
-                          "return (x->t > y->t) ? -1 : (x->t < y->t);"),
-    "smallest_scores": ("if (x->s > y->s) return -1;\n    if (x->s < y->s) return 1;",
-                        "if (x->s < y->s) return -1;\n    if (x->s > y->s) return 1;"),
+    "tie_break_flipped": ("return (x->t < y->t) ? -1 : (x->t > y->t);\n}\n\nstatic int by_int",
+                          "return (x->t > y->t) ? -1 : (x->t < y->t);\n}\n\nstatic int by_int"),
+    "smallest_scores": ("*y = (const scored_t *)b;\n    if (x->s > y->s) return -1;\n"
+                        "    if (x->s < y->s) return 1;",
+                        "*y = (const scored_t *)b;\n    if (x->s < y->s) return -1;\n"
+                        "    if (x->s > y->s) return 1;"),
     "no_normalisation": ("xhat[t * d + i] = x[t * d + i] / r;", "xhat[t * d + i] = x[t * d + i];"),
     "ema_missing_half": ("(1.0 - lam) * 0.5 * (sum_q[j] + sum_k[j])",
                          "(1.0 - lam) * (sum_q[j] + sum_k[j])"),
