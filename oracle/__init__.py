@@ -423,3 +423,85 @@ def layer_backward(x, w_in, w_o, fwd: dict, dy, R: int, L: int, d: int, window: 
     dx, dw_in = in_proj_bwd(x, w_in, dqk, dv, dq_l, dk_l, dv_l, dy, rounding)
     return {"do_r": do_r, "do_l": do_l, "dw_o": dw_o, "dq_hat": dqh, "dk_hat": dkh, "dv": dv,
             "dqk": dqk, "dq_l": dq_l, "dk_l": dk_l, "dv_l": dv_l, "dx": dx, "dw_in": dw_in}
+
+
+# ---- incremental decode ------------------------------------------------------------------
+# Decode-time routing (a reading: the pages' sampling needs one token at a time,
+# and the balanced top-w of a whole sequence is not defined for a single new
+# token): the new token joins the one cluster whose centroid is nearest (O11),
+# its key and value are appended to that cluster's cache, and its query attends
+# to every entry of that cache (all at earlier positions or itself, so the step
+# is causal).  Local heads keep the last `window` keys and values.  Plain
+# float64 numpy; a cache is a dict of arrays.
+
+def decode_cache_from_prefill(qk, v, idx, cap: int):
+    """Cluster caches from a prefill membership: for each (b, h, c) the member
+    rows of idx[b, h, c] (ascending positions): raw qk rows, their inverse
+    norms, values, positions; `cap` entries of room per cluster."""
+    qk, v, idx = _f64(qk), _f64(v), _i32(idx)
+    B, H, n, d = qk.shape
+    k, w = idx.shape[2], idx.shape[3]
+    assert cap >= w
+    _, inv = normalize(qk)
+    ck = np.zeros((B, H, k, cap, d))
+    cinv = np.zeros((B, H, k, cap))
+    cv = np.zeros((B, H, k, cap, d))
+    cpos = np.full((B, H, k, cap), -1, dtype=np.int32)
+    clen = np.full((B, H, k), w, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for c in range(k):
+                p = idx[b, h, c]
+                ck[b, h, c, :w] = qk[b, h, p]
+                cinv[b, h, c, :w] = inv[b, h, p]
+                cv[b, h, c, :w] = v[b, h, p]
+                cpos[b, h, c, :w] = p
+    return {"k": ck, "inv": cinv, "v": cv, "pos": cpos, "len": clen}
+
+
+def decode_step(cache: dict, qk_t, v_t, t: int, mu, scale: float):
+    """One routed decode step for the token at position t (qk_t, v_t [B, H, d]):
+    returns (out [B, H, d], label [B, H], the updated cache (a copy))."""
+    qk_t, v_t, mu = _f64(qk_t), _f64(v_t), _f64(mu)
+    B, H, d = qk_t.shape
+    cache = {name: arr.copy() for name, arr in cache.items()}
+    out = np.zeros((B, H, d))
+    label = np.zeros((B, H), dtype=np.int32)
+    cap = cache["k"].shape[3]
+    for b in range(B):
+        for h in range(H):
+            x = qk_t[b, h]
+            inv = 1.0 / max(np.sqrt((x * x).sum()), 1e-12)
+            s = mu[h] @ (x * inv)
+            c = int(np.argmax(s))                      # first maximum: ties to the lower index
+            label[b, h] = c
+            j = int(cache["len"][b, h, c])
+            assert j < cap, "cluster cache full"
+            cache["k"][b, h, c, j] = x
+            cache["inv"][b, h, c, j] = inv
+            cache["v"][b, h, c, j] = v_t[b, h]
+            cache["pos"][b, h, c, j] = t
+            cache["len"][b, h, c] = j + 1
+            keys = cache["k"][b, h, c, :j + 1] * cache["inv"][b, h, c, :j + 1, None]
+            logits = scale * (keys @ (x * inv))
+            p = np.exp(logits - logits.max())
+            p /= p.sum()
+            out[b, h] = p @ cache["v"][b, h, c, :j + 1]
+    return out, label, cache
+
+
+def local_decode_step(ring_k, ring_v, q_t, k_t, v_t, t: int, window: int, scale: float):
+    """One local decode step: ring_k, ring_v [B, H, window, d] hold position p
+    at slot p % window; the new key and value go to slot t % window, and the
+    query attends to positions max(0, t - window + 1) .. t.  Returns (out,
+    ring_k, ring_v) (copies)."""
+    ring_k, ring_v = _f64(ring_k).copy(), _f64(ring_v).copy()
+    q_t, k_t, v_t = _f64(q_t), _f64(k_t), _f64(v_t)
+    ring_k[:, :, t % window] = k_t
+    ring_v[:, :, t % window] = v_t
+    pos = np.arange(max(0, t - window + 1), t + 1)
+    keys, vals = ring_k[:, :, pos % window], ring_v[:, :, pos % window]   # [B, H, m, d]
+    logits = scale * np.einsum("bhmd,bhd->bhm", keys, q_t)
+    p = np.exp(logits - logits.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    return np.einsum("bhm,bhmd->bhd", p, vals), ring_k, ring_v

@@ -705,3 +705,54 @@ def test_o12_partition_hand_example(orc):
     mu = np.array([[[1.0, 0.0], [0.0, 1.0]]])
     idx = orc.route_partition(x, mu)
     np.testing.assert_array_equal(idx[0, 0], [[0, 2], [1, 3]])
+
+
+# ---- incremental decode --------------------------------------------------------------------
+
+def test_decode_one_cluster_is_dense_causal_attention(orc):
+    """k = 1: the only cluster holds every earlier token, so decoding position
+    t equals row t of causal SDPA over the normalised vectors."""
+    r = _rng(50)
+    B, H, n, d = 1, 2, 24, 8
+    x = r.standard_normal((B, H, n, d))
+    v = r.standard_normal((B, H, n, d))
+    mu = r.standard_normal((H, 1, d))
+    t = 17
+    idx = np.broadcast_to(np.arange(t, dtype=np.int32), (B, H, 1, t))
+    cache = orc.decode_cache_from_prefill(x[:, :, :t], v[:, :, :t], idx, 32)
+    out, label, cache2 = orc.decode_step(cache, x[:, :, t], v[:, :, t], t, mu, 0.6)
+    want = _sdpa(_unit(x[:, :, :t + 1]), _unit(x[:, :, :t + 1]), v[:, :, :t + 1], 0.6, True)[:, :, t]
+    np.testing.assert_allclose(out, want, atol=1e-12)
+    assert np.all(label == 0) and np.all(cache2["len"] == t + 1)
+    assert np.all(cache2["pos"][:, :, 0, t] == t)
+
+
+def test_decode_routes_to_nearest_centroid_and_attends_its_cache(orc):
+    r = _rng(51)
+    B, H, n, d, k, w = 2, 1, 40, 6, 4, 10
+    x = r.standard_normal((B, H, n, d))
+    v = r.standard_normal((B, H, n, d))
+    mu = _unit(r.standard_normal((H, k, d)))
+    _, idx, _, _ = orc.route(x[:, :, :n - 1], mu, w)
+    cache = orc.decode_cache_from_prefill(x[:, :, :n - 1], v[:, :, :n - 1], idx, w + 4)
+    out, label, cache2 = orc.decode_step(cache, x[:, :, n - 1], v[:, :, n - 1], n - 1, mu, 1.1)
+    for b in range(B):
+        c = int(np.argmin(cdist(_unit(x[b, 0, n - 1][None]), mu[0])))
+        assert label[b, 0] == c
+        members = list(idx[b, 0, c]) + [n - 1]
+        q = _unit(x[b, 0, members])
+        want = _sdpa(q[None, None], q[None, None], v[b, 0, members][None, None], 1.1, True)[0, 0, -1]
+        np.testing.assert_allclose(out[b, 0], want, atol=1e-12)
+
+
+def test_local_decode_matches_local_attention(orc):
+    """Feeding a sequence one token at a time through the ring buffer gives
+    the rows of O7 (the C sliding-window attention)."""
+    r = _rng(52)
+    B, H, n, d, W = 1, 2, 30, 5, 7
+    q, kk, v = (r.standard_normal((B, H, n, d)) for _ in range(3))
+    want = orc.local_attn(q, kk, v, W, 0.9, True)
+    rk, rv = np.zeros((B, H, W, d)), np.zeros((B, H, W, d))
+    for t in range(n):
+        out, rk, rv = orc.local_decode_step(rk, rv, q[:, :, t], kk[:, :, t], v[:, :, t], t, W, 0.9)
+        np.testing.assert_allclose(out, want[:, :, t], atol=1e-12)
