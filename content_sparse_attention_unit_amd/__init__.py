@@ -18,7 +18,8 @@ import torch
 __all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
            "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
            "out_proj_bwd", "in_proj_bwd", "local_attn_blocked", "centroid_update_argmax_",
-           "route_partition", "workspace_bytes", "library_path",
+           "route_partition", "decode_cache", "decode_fill", "decode_routed",
+           "decode_ring_fill", "decode_local", "workspace_bytes", "library_path",
            "mask_words", "RTError", "RT_OP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +72,10 @@ def _load():
         "rt_local_attn_blocked": [P, P, P, I, I, I, I, I, I, I, F, P, I, P],
         "rt_centroid_update_argmax": [P, P, P, I, I, I, I, I, I, F, P, Z, P],
         "rt_route_partition": [P, I, P, I, I, I, I, I, P, P, P, P, Z, P],
+        "rt_decode_fill": [P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P],
+        "rt_decode_ring_fill": [P, P, I, I, I, I, I, P, P, P],
+        "rt_decode_routed": [P, P, P, I, I, I, I, I, P, P, P, P, P, I, F, P, I, P, P],
+        "rt_decode_local": [P, P, P, I, I, I, I, P, P, I, F, P, I, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -439,3 +444,127 @@ def route_partition(qk, mu, *, want_mask=False, out=None, ws=None):
                                   _ptr(idx), _ptr(mask), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(dev)))
     return (inv, idx, mask) if mask is not None else (inv, idx)
+
+
+# ---- incremental decode ------------------------------------------------------------------
+
+def _bf16(*ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16:
+            raise TypeError("decode takes bfloat16 rows")
+
+
+def _shape(t, want, what):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _check_cache(cache, B, H, k, cap, d):
+    _shape(cache["k"], (B, H, k, cap, d), "cache k")
+    _shape(cache["v"], (B, H, k, cap, d), "cache v")
+    _shape(cache["inv"], (B, H, k, cap), "cache inv")
+    _shape(cache["pos"], (B, H, k, cap), "cache pos")
+    _shape(cache["len"], (B, H, k), "cache len")
+    for name, dt in (("k", torch.bfloat16), ("v", torch.bfloat16), ("inv", torch.float32),
+                     ("pos", torch.int32), ("len", torch.int32)):
+        if cache[name].dtype != dt:
+            raise TypeError(f"cache {name} must be {dt}")
+
+
+def decode_cache(B: int, H: int, k: int, cap: int, d: int, device) -> dict:
+    """Empty cluster caches (positions -1, no entries in use)."""
+    return {"k": torch.zeros((B, H, k, cap, d), dtype=torch.bfloat16, device=device),
+            "inv": torch.zeros((B, H, k, cap), dtype=torch.float32, device=device),
+            "v": torch.zeros((B, H, k, cap, d), dtype=torch.bfloat16, device=device),
+            "pos": torch.full((B, H, k, cap), -1, dtype=torch.int32, device=device),
+            "len": torch.zeros((B, H, k), dtype=torch.int32, device=device)}
+
+
+def decode_fill(qk, v, inv, idx, cap: int, cache=None) -> dict:
+    """Cluster caches from a prefill membership (idx [B,H,k,w], inv [B,H,n])."""
+    lib = _load()
+    dev = _gpu(qk, v, inv, idx)
+    _bf16(qk, v)
+    B, H, n, d = qk.shape
+    k, w = idx.shape[2], idx.shape[3]
+    _shape(v, qk.shape, "v")
+    _shape(inv, (B, H, n), "inv")
+    _shape(idx[:, :, 0, 0], (B, H), "idx")
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if cache is None:
+        cache = decode_cache(B, H, k, cap, d, dev)
+    _check_cache(cache, B, H, k, cap, d)
+    _check(lib.rt_decode_fill(_ptr(qk), _ptr(inv), _ptr(v), _ptr(idx), B, H, n, d, k, w, int(cap),
+                              _ptr(cache["k"]), _ptr(cache["inv"]), _ptr(cache["v"]),
+                              _ptr(cache["pos"]), _ptr(cache["len"]), _stream(dev)))
+    return cache
+
+
+def decode_routed(cache: dict, qk_t, v_t, t: int, mu, *, scale=None, out_dtype=None, out=None,
+                  label=None):
+    """One routed decode step (the caches are appended to in place); returns
+    (out [B,H,d], label [B,H])."""
+    lib = _load()
+    dev = _gpu(qk_t, v_t, mu, *cache.values())
+    _bf16(qk_t, v_t)
+    B, H, d = qk_t.shape
+    k, cap = cache["k"].shape[2], cache["k"].shape[3]
+    _shape(v_t, (B, H, d), "v_t")
+    _shape(mu, (H, k, d), "mu")
+    if mu.dtype != torch.float32:
+        raise TypeError("mu must be float32")
+    _check_cache(cache, B, H, k, cap, d)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype or qk_t.dtype, device=dev)
+    _shape(out, (B, H, d), "out")
+    if label is None:
+        label = torch.empty((B, H), dtype=torch.int32, device=dev)
+    _gpu(out, label)
+    _shape(label, (B, H), "label")
+    _check(lib.rt_decode_routed(_ptr(qk_t), _ptr(v_t), _ptr(mu), B, H, d, k, cap,
+                                _ptr(cache["k"]), _ptr(cache["inv"]), _ptr(cache["v"]),
+                                _ptr(cache["pos"]), _ptr(cache["len"]), int(t), sc, _ptr(out),
+                                _dtype_code(out), _ptr(label), _stream(dev)))
+    return out, label
+
+
+def decode_ring_fill(kk, v, window: int, ring=None):
+    """The local rings (ring_k, ring_v [B,H,window,d]) from a prefill's keys and values."""
+    lib = _load()
+    dev = _gpu(kk, v)
+    _bf16(kk, v)
+    B, H, n, d = kk.shape
+    _shape(v, kk.shape, "v")
+    if ring is None:
+        ring = (torch.zeros((B, H, window, d), dtype=torch.bfloat16, device=dev),
+                torch.zeros((B, H, window, d), dtype=torch.bfloat16, device=dev))
+    _bf16(*ring)
+    _shape(ring[0], (B, H, window, d), "ring_k")
+    _shape(ring[1], (B, H, window, d), "ring_v")
+    _check(lib.rt_decode_ring_fill(_ptr(kk), _ptr(v), B, H, n, d, int(window), _ptr(ring[0]),
+                                   _ptr(ring[1]), _stream(dev)))
+    return ring
+
+
+def decode_local(ring_k, ring_v, q_t, k_t, v_t, t: int, *, scale=None, out_dtype=None, out=None):
+    """One local decode step (the rings are written in place); returns out [B,H,d]."""
+    lib = _load()
+    dev = _gpu(ring_k, ring_v, q_t, k_t, v_t)
+    _bf16(ring_k, ring_v, q_t, k_t, v_t)
+    B, H, d = q_t.shape
+    window = ring_k.shape[2]
+    for t_, what in ((k_t, "k_t"), (v_t, "v_t")):
+        _shape(t_, (B, H, d), what)
+    _shape(ring_k, (B, H, window, d), "ring_k")
+    _shape(ring_v, (B, H, window, d), "ring_v")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype or q_t.dtype, device=dev)
+    _gpu(out)
+    _shape(out, (B, H, d), "out")
+    _check(lib.rt_decode_local(_ptr(q_t), _ptr(k_t), _ptr(v_t), B, H, d, window, _ptr(ring_k),
+                               _ptr(ring_v), int(t), sc, _ptr(out), _dtype_code(out),
+                               _stream(dev)))
+    return out

@@ -52,6 +52,23 @@ rt_status check_clusters(const char* fn, int n, int k, int w) {
     return RT_OK;
 }
 
+// Checks shared by the decode entry points.
+rt_status check_decode(const char* fn, int B, int H, int d) {
+    if (B <= 0 || H <= 0 || d <= 0)
+        return fail(RT_EINVAL, "%s: sizes must be positive (B=%d H=%d d=%d)", fn, B, H, d);
+    if (!dim_ok(d)) return fail(RT_EUNSUPPORTED, "%s: d=%d not in {16,32,64,128}", fn, d);
+    if ((long long)B * H > 65535)
+        return fail(RT_EUNSUPPORTED, "%s: B*H=%lld exceeds 65535", fn, (long long)B * H);
+    return RT_OK;
+}
+
+rt_status check_entries(const char* fn, const char* what, int m) {
+    if (m <= 0) return fail(RT_EINVAL, "%s: %s=%d must be positive", fn, what, m);
+    if (m > rt::kDecodeMaxEntries)
+        return fail(RT_EUNSUPPORTED, "%s: %s=%d exceeds %d", fn, what, m, rt::kDecodeMaxEntries);
+    return RT_OK;
+}
+
 size_t route_ws(int B, int H, int n, int k) { return (size_t)B * H * k * n * sizeof(float); }
 
 // rt_routed_attn workspace: mask [B*H*n][KW] u32 | slots [B*H*n][kSlots][d] f32 |
@@ -638,6 +655,90 @@ rt_status rt_route_partition(const void* qk, int dtype, const float* mu, int B, 
     hipError_t e = rt::launch_nearest(qk, dtype, mu, B, H, n, d, k, inv_norm, label, best,
                                       member_mask, s);
     if (e == hipSuccess) e = rt::launch_partition(label, best, B * H, n, k, idx, member_mask, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+// ---- decode -------------------------------------------------------------------------------
+
+rt_status rt_decode_fill(const void* qk, const float* inv_norm, const void* v, const int32_t* idx,
+                         int B, int H, int n, int d, int k, int w, int cap, void* cache_k,
+                         float* cache_inv, void* cache_v, int32_t* cache_pos, int32_t* cache_len,
+                         void* stream) {
+    static const char* fn = "rt_decode_fill";
+    g_err[0] = 0;
+    if (!qk || !inv_norm || !v || !idx || !cache_k || !cache_inv || !cache_v || !cache_pos ||
+        !cache_len)
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, RT_BF16, B, H, n, d);
+    if (st == RT_OK) st = check_clusters(fn, n, k, w);
+    if (st == RT_OK) st = check_entries(fn, "cap", cap);
+    if (st != RT_OK) return st;
+    if (cap < w) return fail(RT_EINVAL, "%s: cap=%d is below w=%d", fn, cap, w);
+    if ((long long)B * H * k * cap * d >= (1LL << 40))
+        return fail(RT_EUNSUPPORTED, "%s: cache too large", fn);
+    hipError_t e = rt::launch_decode_fill(qk, inv_norm, v, idx, B * H, n, d, k, w, cap, cache_k,
+                                          cache_inv, cache_v, cache_pos, cache_len,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_decode_ring_fill(const void* kk, const void* v, int B, int H, int n, int d,
+                              int window, void* ring_k, void* ring_v, void* stream) {
+    static const char* fn = "rt_decode_ring_fill";
+    g_err[0] = 0;
+    if (!kk || !v || !ring_k || !ring_v) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, RT_BF16, B, H, n, d);
+    if (st == RT_OK) st = check_entries(fn, "window", window);
+    if (st != RT_OK) return st;
+    hipError_t e = rt::launch_decode_ring_fill(kk, v, B * H, n, d, window, ring_k, ring_v,
+                                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_decode_routed(const void* qk_t, const void* v_t, const float* mu, int B, int H, int d,
+                           int k, int cap, void* cache_k, float* cache_inv, void* cache_v,
+                           int32_t* cache_pos, int32_t* cache_len, int t, float scale, void* out,
+                           int out_dtype, int32_t* label, void* stream) {
+    static const char* fn = "rt_decode_routed";
+    g_err[0] = 0;
+    if (!qk_t || !v_t || !mu || !cache_k || !cache_inv || !cache_v || !cache_pos || !cache_len ||
+        !out)
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_decode(fn, B, H, d);
+    if (st == RT_OK) st = check_entries(fn, "cap", cap);
+    if (st != RT_OK) return st;
+    if (k <= 0) return fail(RT_EINVAL, "%s: k=%d must be positive", fn, k);
+    if (k > 256) return fail(RT_EUNSUPPORTED, "%s: k=%d exceeds 256", fn, k);
+    if (t < 0) return fail(RT_EINVAL, "%s: position t=%d is negative", fn, t);
+    if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (out_dtype != RT_F32 && out_dtype != RT_BF16)
+        return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
+    hipError_t e = rt::launch_decode_routed(qk_t, v_t, mu, B * H, H, d, k, cap, cache_k, cache_inv,
+                                            cache_v, cache_pos, cache_len, t, scale, out,
+                                            out_dtype, label, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_decode_local(const void* q_t, const void* k_t, const void* v_t, int B, int H, int d,
+                          int window, void* ring_k, void* ring_v, int t, float scale, void* out,
+                          int out_dtype, void* stream) {
+    static const char* fn = "rt_decode_local";
+    g_err[0] = 0;
+    if (!q_t || !k_t || !v_t || !ring_k || !ring_v || !out)
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_decode(fn, B, H, d);
+    if (st == RT_OK) st = check_entries(fn, "window", window);
+    if (st != RT_OK) return st;
+    if (t < 0) return fail(RT_EINVAL, "%s: position t=%d is negative", fn, t);
+    if (!std::isfinite(scale)) return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (out_dtype != RT_F32 && out_dtype != RT_BF16)
+        return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
+    hipError_t e = rt::launch_decode_local(q_t, k_t, v_t, B * H, d, window, ring_k, ring_v, t,
+                                           scale, out, out_dtype, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

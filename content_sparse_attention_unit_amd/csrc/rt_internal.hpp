@@ -156,4 +156,19 @@ hipError_t launch_gemm_bwd(int which, const GemmArgs& p, hipStream_t s);
 // Largest cluster the backward kernels keep on chip.
 int max_cluster_rows_bwd(int dtype, int d, bool shared_qk);
 
+// One decode step (bfloat16 rows; caches as described with the entry points).
+constexpr int kDecodeMaxEntries = 16384;   // cap and window: their logits live in LDS
+hipError_t launch_decode_fill(const void* qk, const float* inv, const void* v, const int32_t* idx,
+                              int BH, int n, int d, int k, int w, int cap, void* ck, float* cinv,
+                              void* cv, int32_t* cpos, int32_t* clen, hipStream_t s);
+hipError_t launch_decode_ring_fill(const void* kk, const void* v, int BH, int n, int d,
+                                   int window, void* rk, void* rv, hipStream_t s);
+hipError_t launch_decode_routed(const void* qk_t, const void* v_t, const float* mu, int BH, int H,
+                                int d, int k, int cap, void* ck, float* cinv, void* cv,
+                                int32_t* cpos, int32_t* clen, int t, float scale, void* out,
+                                int out_dtype, int32_t* label, hipStream_t s);
+hipError_t launch_decode_local(const void* q_t, const void* k_t, const void* v_t, int BH, int d,
+                               int window, void* rk, void* rv, int t, float scale, void* out,
+                               int out_dtype, hipStream_t s);
+
 }  // namespace rt

@@ -374,6 +374,82 @@ rt_status rt_route_partition(const void *qk, int dtype, const float *mu, int B, 
                              int d, int k, float *inv_norm, int32_t *idx, uint32_t *member_mask,
                              void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * ---- Incremental decode ------------------------------------------------------------------
+ * Summary Appendix A generates one token at a time; Summary §3 (autoregressive
+ * factorisation: a query sees only earlier positions) and §4 (routing by the
+ * nearest shared centroid) say what one step computes.  The pages define no
+ * decode step, so this reading is used: the new token joins the one cluster
+ * whose centroid is nearest (largest inner product of the unit vectors, ties to
+ * the lower index); its raw key row, inverse norm, value and position are
+ * appended to that cluster's cache; its query attends, with the routed logit
+ * scale * <q_hat, k_hat>, to every entry of that cache (all earlier positions
+ * or itself).  The local heads keep the last `window` keys and values in a ring.
+ *
+ * Every decode entry point takes bfloat16 rows (no dtype argument) and keeps
+ * them in bfloat16 caches owned by the caller:
+ *   cache_k    [B][H][k][cap][d] bf16  raw key rows of each cluster
+ *   cache_inv  [B][H][k][cap]    float32 their inverse norms 1 / max(|x|, 1e-12)
+ *   cache_v    [B][H][k][cap][d] bf16  values
+ *   cache_pos  [B][H][k][cap]    int32 positions
+ *   cache_len  [B][H][k]         int32 entries in use (the first cache_len rows)
+ *   ring_k, ring_v [B][H][window][d] bf16: position p at slot p % window.
+ * cap and window are at most 16384 (the step keeps its logits on chip).  A
+ * step with B*H pieces of work is bound by launch latency; steps on one stream
+ * run in order, which is what the cache updates need.
+ */
+
+/*
+ * rt_decode_fill -- cluster caches from a prefill membership.
+ *   qk, v      [B][H][n][d] bf16, the prefill's shared query/key rows and values.
+ *   inv_norm   [B][H][n] float32 and idx [B][H][k][w] int32 as written by rt_route
+ *              (or rt_route_partition with w = n / k).
+ *   Writes rows 0..w-1 of every cluster's cache (row r: position idx[.., c, r])
+ *   and cache_len = w; rows w..cap-1 are left as they are.  cap >= w.
+ */
+rt_status rt_decode_fill(const void *qk, const float *inv_norm, const void *v, const int32_t *idx,
+                         int B, int H, int n, int d, int k, int w, int cap, void *cache_k,
+                         float *cache_inv, void *cache_v, int32_t *cache_pos, int32_t *cache_len,
+                         void *stream);
+
+/*
+ * rt_decode_ring_fill -- the local heads' rings from a prefill: slot s gets the
+ *   key and value of the last position p < n with p % window == s (slots with no
+ *   such position are left as they are).
+ *   kk, v  [B][H][n][d] bf16 (the local heads' keys and values).
+ */
+rt_status rt_decode_ring_fill(const void *kk, const void *v, int B, int H, int n, int d,
+                              int window, void *ring_k, void *ring_v, void *stream);
+
+/*
+ * rt_decode_routed -- one routed decode step for the token at position t.
+ *   qk_t, v_t  [B][H][d] bf16: the new token's shared query/key row and value.
+ *   mu         [H][k] unit rows of d float32 (the centroids; not changed).
+ *   The caches are read and appended to in place (see above).
+ *   out        out [B][H][d] of element type out_dtype (RT_F32 or RT_BF16).
+ *   label      optional out [B][H] int32: the chosen cluster.
+ *   A cluster whose cache is full (cache_len >= cap) is not written: that
+ *   (batch, head) gets label -1 and an all-NaN output row, and its caches are
+ *   unchanged; the other (batch, head) pairs are unaffected.  The caller keeps
+ *   room (cap >= fill + steps bounds every cluster).
+ */
+rt_status rt_decode_routed(const void *qk_t, const void *v_t, const float *mu, int B, int H, int d,
+                           int k, int cap, void *cache_k, float *cache_inv, void *cache_v,
+                           int32_t *cache_pos, int32_t *cache_len, int t, float scale, void *out,
+                           int out_dtype, int32_t *label, void *stream);
+
+/*
+ * rt_decode_local -- one local decode step for the token at position t >= 0:
+ *   writes k_t, v_t ([B][H][d] bf16) to slot t % window of the rings, then the
+ *   query q_t attends with logit scale * <q, k> (raw rows) to positions
+ *   max(0, t - window + 1) .. t, which the rings must hold (Summary §6, Abstract:
+ *   the local heads' sliding window).
+ *   out  out [B][H][d] of element type out_dtype.
+ */
+rt_status rt_decode_local(const void *q_t, const void *k_t, const void *v_t, int B, int H, int d,
+                          int window, void *ring_k, void *ring_v, int t, float scale, void *out,
+                          int out_dtype, void *stream);
+
 /* Workspace size in bytes for operation `op` at these sizes (0 if none,
  * (size_t)-1 if the sizes are invalid). */
 size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w);

@@ -351,3 +351,88 @@ def test_in_proj_bwd_validation(lib, kw, code, msg):
                               a["dv_l"], a["dres"], a["B"], a["n"], a["dm"], a["d"], a["R"],
                               a["L"], a["dx"], a["dw_in"], None) == code
     assert msg in _last(lib)
+
+
+def decode_routed(lib, qk_t=FAKE, v_t=FAKE, mu=FAKE, B=1, H=2, d=64, k=8, cap=64, ck=FAKE,
+                  cinv=FAKE, cv=FAKE, cpos=FAKE, clen=FAKE, t=10, scale=0.125, out=FAKE,
+                  out_dtype=0, label=None):
+    return lib.rt_decode_routed(qk_t, v_t, mu, B, H, d, k, cap, ck, cinv, cv, cpos, clen, t,
+                                ctypes.c_float(scale), out, out_dtype, label, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(qk_t=None), RT_EINVAL, "null"),
+    (dict(clen=None), RT_EINVAL, "null"),
+    (dict(out=None), RT_EINVAL, "null"),
+    (dict(B=0), RT_EINVAL, "positive"),
+    (dict(d=48), RT_EUNSUPPORTED, "d=48"),
+    (dict(k=0), RT_EINVAL, "k=0"),
+    (dict(k=257), RT_EUNSUPPORTED, "exceeds 256"),
+    (dict(cap=0), RT_EINVAL, "cap=0"),
+    (dict(cap=16385), RT_EUNSUPPORTED, "exceeds 16384"),
+    (dict(t=-1), RT_EINVAL, "negative"),
+    (dict(scale=float("inf")), RT_EINVAL, "scale"),
+    (dict(out_dtype=3), RT_EUNSUPPORTED, "out_dtype"),
+    (dict(B=300, H=300), RT_EUNSUPPORTED, "B*H"),
+])
+def test_decode_routed_validation(lib, kw, code, msg):
+    assert decode_routed(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def decode_local(lib, q_t=FAKE, k_t=FAKE, v_t=FAKE, B=1, H=2, d=64, window=32, rk=FAKE, rv=FAKE,
+                 t=0, scale=0.125, out=FAKE, out_dtype=1):
+    return lib.rt_decode_local(q_t, k_t, v_t, B, H, d, window, rk, rv, t, ctypes.c_float(scale),
+                               out, out_dtype, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(rk=None), RT_EINVAL, "null"),
+    (dict(H=0), RT_EINVAL, "positive"),
+    (dict(d=256), RT_EUNSUPPORTED, "d=256"),
+    (dict(window=0), RT_EINVAL, "window=0"),
+    (dict(window=20000), RT_EUNSUPPORTED, "exceeds 16384"),
+    (dict(t=-5), RT_EINVAL, "negative"),
+    (dict(scale=float("nan")), RT_EINVAL, "scale"),
+    (dict(out_dtype=2), RT_EUNSUPPORTED, "out_dtype"),
+])
+def test_decode_local_validation(lib, kw, code, msg):
+    assert decode_local(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(idx=None), RT_EINVAL, "null"),
+    (dict(w=0), RT_EINVAL, "positive"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(cap=15), RT_EINVAL, "below w"),
+    (dict(cap=20000), RT_EUNSUPPORTED, "exceeds 16384"),
+    (dict(d=24), RT_EUNSUPPORTED, "d=24"),
+])
+def test_decode_fill_validation(lib, kw, code, msg):
+    a = dict(qk=FAKE, inv=FAKE, v=FAKE, idx=FAKE, B=1, H=1, n=64, d=16, k=4, w=16, cap=32)
+    a.update(kw)
+    assert lib.rt_decode_fill(a["qk"], a["inv"], a["v"], a["idx"], a["B"], a["H"], a["n"], a["d"],
+                              a["k"], a["w"], a["cap"], FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert msg in _last(lib)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(kk=None), RT_EINVAL, "null"),
+    (dict(n=0), RT_EINVAL, "positive"),
+    (dict(window=0), RT_EINVAL, "window=0"),
+])
+def test_decode_ring_fill_validation(lib, kw, code, msg):
+    a = dict(kk=FAKE, B=1, H=1, n=64, d=16, window=8)
+    a.update(kw)
+    assert lib.rt_decode_ring_fill(a["kk"], FAKE, a["B"], a["H"], a["n"], a["d"], a["window"],
+                                   FAKE, FAKE, None) == code
+    assert msg in _last(lib)
+
+
+def test_decode_binding_rejects_float32_rows():
+    import torch
+    import content_sparse_attention_unit_amd as rt
+    with pytest.raises((TypeError, ValueError)):
+        rt.decode_local(*(torch.zeros(1, 1, 4, 16) for _ in range(2)),
+                        *(torch.zeros(1, 1, 16) for _ in range(3)), 0)
