@@ -332,6 +332,72 @@ def time_variants(rt, cfg, inp, reps=20):
                     f"update: shared q/k, {R} heads"}
 
 
+def time_decode(rt, cfg, inp, group=16, reps=20):
+    """Incremental decode after a prefill of the workload's n tokens: caches
+    filled from the prefill's routing, then steps of one new token per
+    sequence (the routed step on the routed heads and, concurrently on a second
+    stream, the local step on the local heads), captured as HIP graphs of
+    `group` consecutive steps."""
+    B, R, L, n, d, k, w = cfg.B, cfg.R, cfg.L, cfg.n, cfg.d, cfg.k, cfg.w
+    scale = 1.0 / math.sqrt(d)
+    qk, v = dev(inp["qk"]), dev(inp["v"])
+    kl, vl = dev(inp["k_local"]), dev(inp["v_local"])
+    mu = torch.from_numpy(inp["mu"].astype(np.float32)).cuda()
+    inv, idx = rt.route(qk, mu, w)
+    cap = w + group * (2 * reps + 8)
+    cache = rt.decode_fill(qk, v, inv, idx, cap)
+    rk, rv = rt.decode_ring_fill(kl, vl, cfg.window)
+    new = [dev(S.normal_tensor(4_000_000 + i, (group, B, H_, d), "bf16"))
+           for i, H_ in enumerate((R, R, L, L, L))]
+    out_r = torch.empty((group, B, R, d), dtype=torch.bfloat16, device="cuda")
+    lab = torch.empty((group, B, R), dtype=torch.int32, device="cuda")
+    out_l = torch.empty((group, B, L, d), dtype=torch.bfloat16, device="cuda")
+
+    def routed(g):
+        rt.decode_routed(cache, new[0][g], new[1][g], n + g, mu, scale=scale, out=out_r[g],
+                         label=lab[g])
+
+    def local(g):
+        rt.decode_local(rk, rv, new[2][g], new[3][g], new[4][g], n + g, scale=scale,
+                        out=out_l[g])
+
+    stream, side = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def step(g):
+        """Both kinds of heads of one token: the local heads on a second stream."""
+        side.wait_stream(stream)
+        routed(g)
+        with torch.cuda.stream(side):
+            local(g)
+        stream.wait_stream(side)
+
+    parts = {"routed": routed, "local": local, "step": step}
+    per = {}
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        for name, fn in parts.items():
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for g in range(group):
+                    fn(g)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps // 2):
+                graph.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            per[name] = a.elapsed_time(b) / (reps // 2) / group
+    assert int(cache["len"].max()) <= cap and bool((lab >= 0).all()), "decode cache overflow"
+    return {"ms_per_token_step": per["step"], "tokens_per_s": B / (per["step"] * 1e-3),
+            "per_call_ms": {"rt_decode_routed": per["routed"], "rt_decode_local": per["local"]},
+            "note": f"after a prefill of {n} tokens: {R} routed heads (k={k} caches of {w}+ "
+                    f"entries), {L} local heads (window {cfg.window}) on a second stream; graphs of "
+                    f"{group} steps"}
+
+
 def sweep_configs(only=None):
     """The long layer's shape (B=1, 8 routed + 4 local heads of width 128, window
     512) at n = 1K .. 64K with k = sqrt(n) rounded down to a power of two and
@@ -640,6 +706,7 @@ def main():
         res["stack"] = time_stack(rt, S.STACKS["long_stack"])
     if args.workload == "long":
         res["variants"] = time_variants(rt, cfg, inp)
+        res["decode"] = time_decode(rt, cfg, inp)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, scale)
     print(json.dumps(res), flush=True)
