@@ -1,8 +1,9 @@
 """The pins must catch plausible mistakes in the oracle.
 
-Each case plants one error in a copy of oracle/rt_oracle.c (on the CPU, in a
-temporary directory), rebuilds it, and runs tests/test_oracle_pins.py against
-the copy: at least one pin has to fail.  The unmodified copy has to pass.
+Each case plants one error in a copy of oracle/rt_oracle.c (or, where a third
+item names it, another file of the oracle) on the CPU, in a temporary
+directory, rebuilds it, and runs tests/test_oracle_pins.py against the copy: at
+least one pin has to fail.  The unmodified copy has to pass.
 """
 import os
 import shutil
@@ -75,6 +76,15 @@ MUTANTS = {
                           "                logit[s]"),
     "dv_from_wrong_row": ("dv[(long)p[s] * d + i] += pr * g[i];",
                           "dv[(long)p[r] * d + i] += pr * g[i];"),
+    # incremental decode (numpy, oracle/__init__.py)
+    "decode_ties_to_higher": ("c = int(np.argmax(s))  ", "c = int(len(s) - 1 - np.argmax(s[::-1]))  ",
+                              "__init__.py"),
+    "decode_keys_unnormalised": ('keys = cache["k"][b, h, c, :j + 1] * cache["inv"][b, h, c, :j + 1, None]',
+                                 'keys = cache["k"][b, h, c, :j + 1]', "__init__.py"),
+    "decode_fill_wrong_inv": ("cinv[b, h, c, :w] = inv[b, h, p]", "cinv[b, h, c, :w] = inv[b, h, p] * 0 + 1",
+                              "__init__.py"),
+    "local_decode_window_too_long": ("pos = np.arange(max(0, t - window + 1), t + 1)",
+                                     "pos = np.arange(max(0, t - window), t + 1)", "__init__.py"),
 }
 
 
@@ -90,9 +100,9 @@ def _copy(tmp_path, name, edit=None):
     dst = tmp_path / name
     shutil.copytree(SRC, dst, ignore=shutil.ignore_patterns("*.so*", "__pycache__"))
     if edit is not None:
-        path = dst / "rt_oracle.c"
+        old, new = edit[0], edit[1]
+        path = dst / (edit[2] if len(edit) > 2 else "rt_oracle.c")
         text = path.read_text()
-        old, new = edit
         assert text.count(old) == 1, f"mutation site not found exactly once: {old!r}"
         path.write_text(text.replace(old, new))
     return str(dst)

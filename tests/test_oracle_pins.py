@@ -756,3 +756,20 @@ def test_local_decode_matches_local_attention(orc):
     for t in range(n):
         out, rk, rv = orc.local_decode_step(rk, rv, q[:, :, t], kk[:, :, t], v[:, :, t], t, W, 0.9)
         np.testing.assert_allclose(out, want[:, :, t], atol=1e-12)
+
+
+def test_decode_ties_to_lower_centroid(orc):
+    """Two equal centroids: the new token joins the lower-indexed one (and its
+    cache), as the nearest-centroid rule breaks ties."""
+    B, H, d = 1, 1, 3
+    mu = np.array([[[0.0, 0.0, 1.0], [1.0, 0.0, 0.0], [1.0, 0.0, 0.0]]])
+    x = np.array([[[[0.0, 0.0, 2.0], [3.0, 0.5, 0.0], [0.1, 0.0, 4.0], [2.0, -0.5, 0.0]]]])
+    v = np.arange(12, dtype=float).reshape(B, H, 4, d)
+    idx = np.array([[[[0], [1], [1]]]], dtype=np.int32)      # clusters 1 and 2 both hold token 1
+    cache = orc.decode_cache_from_prefill(x[:, :, :3], v[:, :, :3], idx, 4)
+    out, label, cache2 = orc.decode_step(cache, x[:, :, 3], v[:, :, 3], 3, mu, 1.0)
+    assert label[0, 0] == 1
+    np.testing.assert_array_equal(cache2["len"][0, 0], [1, 2, 1])
+    q = _unit(x[0, 0, [1, 3]])
+    want = _sdpa(q[None, None], q[None, None], v[0, 0, [1, 3]][None, None], 1.0, True)[0, 0, -1]
+    np.testing.assert_allclose(out[0, 0], want, atol=1e-12)
