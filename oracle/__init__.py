@@ -425,6 +425,43 @@ def layer_backward(x, w_in, w_o, fwd: dict, dy, R: int, L: int, d: int, window: 
             "dqk": dqk, "dq_l": dq_l, "dk_l": dk_l, "dv_l": dv_l, "dx": dx, "dw_in": dw_in}
 
 
+# ---- separately routed queries and keys ----------------------------------------------------
+# Summary §4 routes queries and keys to the same shared centroids.  With distinct
+# query and key vectors each side is routed on its own (O1-O3 on q, and on k), and
+# cluster c's queries attend to cluster c's keys with no order between them (the
+# content-based sparsity of Summary §4 for data without an order; not causal).
+
+def routed_attn_split(q, kk, v, idx_q, idx_k, scale: float):
+    """Queries of cluster c (idx_q[b, h, c]) attend to its keys (idx_k[b, h, c]),
+    logit scale * <q^, k^>; each query token sums its rows over the clusters
+    that hold it.  -> (out [B,H,n,d], lse [B,H,k,w] (natural log of each query
+    row's denominator), sum_q, sum_k [B,H,k,d] (sums of the members' unit rows))."""
+    q, kk, v = _f64(q), _f64(kk), _f64(v)
+    idx_q, idx_k = _i32(idx_q), _i32(idx_k)
+    B, H, n, d = q.shape
+    k, w = idx_q.shape[2], idx_q.shape[3]
+    assert idx_k.shape == idx_q.shape and kk.shape == q.shape and v.shape == q.shape
+    qh, _ = normalize(q)
+    kh, _ = normalize(kk)
+    out = np.zeros((B, H, n, d))
+    lse = np.empty((B, H, k, w))
+    sum_q = np.empty((B, H, k, d))
+    sum_k = np.empty((B, H, k, d))
+    for b in range(B):
+        for h in range(H):
+            for c in range(k):
+                rq, rk = idx_q[b, h, c], idx_k[b, h, c]
+                logits = scale * (qh[b, h, rq] @ kh[b, h, rk].T)       # [w queries, w keys]
+                m = logits.max(axis=1, keepdims=True)
+                e = np.exp(logits - m)
+                z = e.sum(axis=1, keepdims=True)
+                lse[b, h, c] = (m + np.log(z))[:, 0]
+                np.add.at(out[b, h], rq, (e / z) @ v[b, h, rk])
+                sum_q[b, h, c] = qh[b, h, rq].sum(axis=0)
+                sum_k[b, h, c] = kh[b, h, rk].sum(axis=0)
+    return out, lse, sum_q, sum_k
+
+
 # ---- incremental decode ------------------------------------------------------------------
 # Decode-time routing (a reading: the pages' sampling needs one token at a time,
 # and the balanced top-w of a whole sequence is not defined for a single new

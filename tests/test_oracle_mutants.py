@@ -83,6 +83,13 @@ MUTANTS = {
                                  'keys = cache["k"][b, h, c, :j + 1]', "__init__.py"),
     "decode_fill_wrong_inv": ("cinv[b, h, c, :w] = inv[b, h, p]", "cinv[b, h, c, :w] = inv[b, h, p] * 0 + 1",
                               "__init__.py"),
+    # separately routed queries and keys (numpy)
+    "split_keys_from_query_rows": ("logits = scale * (qh[b, h, rq] @ kh[b, h, rk].T)",
+                                   "logits = scale * (qh[b, h, rq] @ kh[b, h, rq].T)", "__init__.py"),
+    "split_scatter_to_key_tokens": ("np.add.at(out[b, h], rq, (e / z) @ v[b, h, rk])",
+                                    "np.add.at(out[b, h], rk, (e / z) @ v[b, h, rk])", "__init__.py"),
+    "split_values_from_query_rows": ("np.add.at(out[b, h], rq, (e / z) @ v[b, h, rk])",
+                                     "np.add.at(out[b, h], rq, (e / z) @ v[b, h, rq])", "__init__.py"),
     "local_decode_window_too_long": ("pos = np.arange(max(0, t - window + 1), t + 1)",
                                      "pos = np.arange(max(0, t - window), t + 1)", "__init__.py"),
 }

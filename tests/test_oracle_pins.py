@@ -773,3 +773,50 @@ def test_decode_ties_to_lower_centroid(orc):
     q = _unit(x[0, 0, [1, 3]])
     want = _sdpa(q[None, None], q[None, None], v[0, 0, [1, 3]][None, None], 1.0, True)[0, 0, -1]
     np.testing.assert_allclose(out[0, 0], want, atol=1e-12)
+
+
+# ---- separately routed queries and keys ---------------------------------------------------
+
+def test_split_with_one_membership_is_noncausal_routed_attention(orc):
+    """The same membership on both sides: the C routed attention (non-causal)."""
+    r = _rng(60)
+    B, H, n, d, k, w = 2, 2, 40, 8, 4, 12
+    q, kk, v = (r.standard_normal((B, H, n, d)) for _ in range(3))
+    mu = _unit(r.standard_normal((H, k, d)))
+    _, idx, _, _ = orc.route(q, mu, w)
+    out, lse, _, _ = orc.routed_attn_split(q, kk, v, idx, idx, 0.7)
+    want, want_lse, _ = orc.routed_attn(q, kk, v, idx, 0.7, causal=False)
+    np.testing.assert_allclose(out, want, atol=1e-12)
+    np.testing.assert_allclose(lse, want_lse, atol=1e-12)
+
+
+def test_split_one_cluster_of_everything_is_dense_attention(orc):
+    """k = 1, w = n on both sides: non-causal SDPA of the unit queries on the unit keys."""
+    r = _rng(61)
+    B, H, n, d = 1, 2, 20, 6
+    q, kk, v = (r.standard_normal((B, H, n, d)) for _ in range(3))
+    idx = np.broadcast_to(np.arange(n, dtype=np.int32), (B, H, 1, n))
+    out, _, sum_q, sum_k = orc.routed_attn_split(q, kk, v, idx, idx[:, :, :, ::-1].copy()[:, :, :, ::-1], 1.3)
+    want = _sdpa(_unit(q), _unit(kk), v, 1.3, False)
+    np.testing.assert_allclose(out, want, atol=1e-12)
+    np.testing.assert_allclose(sum_q[:, :, 0], _unit(q).sum(axis=2), atol=1e-12)
+    np.testing.assert_allclose(sum_k[:, :, 0], _unit(kk).sum(axis=2), atol=1e-12)
+
+
+def test_split_hand_example(orc):
+    """Token 0's only cluster has the single key token 2: out[0] = v[2]; token 1
+    is in two query clusters: the sum of both rows; token 3 is in none: 0."""
+    d = 2
+    q = np.array([[[[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [0.5, -1.0]]]])
+    kk = np.array([[[[1.0, 0.0], [0.0, 2.0], [3.0, 0.0], [0.0, -1.0]]]])
+    v = np.array([[[[1.0, 2.0], [3.0, 4.0], [5.0, 6.0], [7.0, 8.0]]]])
+    idx_q = np.array([[[[0, 1], [1, 2]]]], dtype=np.int32)
+    idx_k = np.array([[[[2, 2], [1, 3]]]], dtype=np.int32)
+    out, lse, _, _ = orc.routed_attn_split(q, kk, v, idx_q, idx_k, 1.0)
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 0, 2], atol=1e-12)
+    # token 1: cluster 0 (keys 2, 2 -> v[2]) plus cluster 1 (keys 1 and 3, logits +1 and -1)
+    p = np.exp([1.0, -1.0]) / np.exp([1.0, -1.0]).sum()
+    np.testing.assert_allclose(out[0, 0, 1], v[0, 0, 2] + p[0] * v[0, 0, 1] + p[1] * v[0, 0, 3],
+                               atol=1e-12)
+    np.testing.assert_array_equal(out[0, 0, 3], np.zeros(d))
+    np.testing.assert_allclose(lse[0, 0, 0, 0], 1.0 + np.log(2.0), atol=1e-12)   # logit 1, twice
