@@ -308,9 +308,20 @@ def time_variants(rt, cfg, inp, reps=20):
                        device="cuda")
     ws_e = torch.empty(rt.workspace_bytes("centroid_update_argmax", B, R, n, d, k, 1),
                        dtype=torch.uint8, device="cuda")
+    # separately routed queries and keys: a distinct key tensor of the routed heads' shape
+    kd = dev(S.normal_tensor(5_000_000, (B, R, n, d), "bf16"))
+    vd = dev(inp["v"])
+    q_inv, idx_q, q_mask = rt.route(qk, mu, cfg.w, want_mask=True)
+    k_inv, idx_k = rt.route(kd, mu, cfg.w)
+    out_s = torch.empty_like(qk)
+    ws_s = torch.empty(rt.workspace_bytes("routed_attn", B, R, n, d, k, cfg.w), dtype=torch.uint8,
+                       device="cuda")
     calls = {
         "rt_local_attn_blocked": lambda: rt.local_attn_blocked(ql, kl, vl, cfg.window, 1,
                                                                scale=scale, out=out_l),
+        "rt_routed_attn_split": lambda: rt.routed_attn_split(qk, kd, vd, idx_q, idx_k, q_inv,
+                                                             k_inv, scale=scale, q_mask=q_mask,
+                                                             out=out_s, ws=ws_s),
         "rt_route_partition": lambda: rt.route_partition(qk, mu, out=(inv, idx), ws=ws_p),
         "rt_centroid_update_argmax": lambda: rt.centroid_update_argmax_(mu, qk, lam=cfg.lam,
                                                                         ws=ws_e),
@@ -329,7 +340,8 @@ def time_variants(rt, cfg, inp, reps=20):
     return {"per_call_ms": per,
             "note": f"blocked local: blocks of {cfg.window}, one block of look-back, {L} heads; "
                     f"partition: n/k = {n // k} tokens a cluster, {R} heads; nearest-centroid "
-                    f"update: shared q/k, {R} heads"}
+                    f"update: shared q/k, {R} heads; split routing: distinct q and k each "
+                    f"routed (k={k}, w={cfg.w}), {R} heads, non-causal"}
 
 
 def time_decode(rt, cfg, inp, group=16, reps=20):

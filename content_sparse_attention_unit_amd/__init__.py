@@ -18,7 +18,7 @@ import torch
 __all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
            "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
            "out_proj_bwd", "in_proj_bwd", "local_attn_blocked", "centroid_update_argmax_",
-           "route_partition", "decode_cache", "decode_fill", "decode_routed",
+           "route_partition", "routed_attn_split", "decode_cache", "decode_fill", "decode_routed",
            "decode_ring_fill", "decode_local", "workspace_bytes", "library_path",
            "mask_words", "RTError", "RT_OP"]
 
@@ -72,6 +72,8 @@ def _load():
         "rt_local_attn_blocked": [P, P, P, I, I, I, I, I, I, I, F, P, I, P],
         "rt_centroid_update_argmax": [P, P, P, I, I, I, I, I, I, F, P, Z, P],
         "rt_route_partition": [P, I, P, I, I, I, I, I, P, P, P, P, Z, P],
+        "rt_routed_attn_split": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P, P, P, P,
+                                 Z, P],
         "rt_decode_fill": [P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P],
         "rt_decode_ring_fill": [P, P, I, I, I, I, I, P, P, P],
         "rt_decode_routed": [P, P, P, I, I, I, I, I, P, P, P, P, P, I, F, P, I, P, P],
@@ -444,6 +446,40 @@ def route_partition(qk, mu, *, want_mask=False, out=None, ws=None):
                                   _ptr(idx), _ptr(mask), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(dev)))
     return (inv, idx, mask) if mask is not None else (inv, idx)
+
+
+def routed_attn_split(q, kk, v, idx_q, idx_k, q_inv=None, k_inv=None, *, scale=None,
+                      out_dtype=None, q_mask=None, want_lse=False, want_sums=False, out=None,
+                      ws=None):
+    """Queries and keys routed on their own: cluster c's queries (idx_q) attend
+    to its keys and values (idx_k), without a causal mask.  Returns out, plus
+    lse and (sum_q, sum_k) when asked."""
+    lib = _load()
+    dev = _gpu(q, kk, v, idx_q, idx_k, q_inv, k_inv, q_mask)
+    B, H, n, d = q.shape
+    k, w = idx_q.shape[2], idx_q.shape[3]
+    if tuple(idx_k.shape) != tuple(idx_q.shape):
+        raise ValueError("idx_q and idx_k must have the same shape")
+    if idx_q.dtype != torch.int32 or idx_k.dtype != torch.int32:
+        raise TypeError("idx_q and idx_k must be int32")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((B, H, k, w), dtype=torch.float32, device=dev) if want_lse else None
+    sums = (tuple(torch.empty((B, H, k, d), dtype=torch.float32, device=dev) for _ in range(2))
+            if want_sums else (None, None))
+    ws, _ = _workspace("routed_attn", dev, B, H, n, d, k, w, ws)
+    _check(lib.rt_routed_attn_split(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
+                                    _ptr(k_inv), _ptr(idx_q), _ptr(idx_k), _ptr(q_mask), B, H, n,
+                                    d, k, w, sc, _ptr(out), _dtype_code(out), _ptr(lse),
+                                    _ptr(sums[0]), _ptr(sums[1]), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(dev)))
+    res = (out,)
+    if want_lse:
+        res += (lse,)
+    if want_sums:
+        res += sums
+    return res[0] if len(res) == 1 else res
 
 
 # ---- incremental decode ------------------------------------------------------------------

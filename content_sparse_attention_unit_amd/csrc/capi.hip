@@ -166,12 +166,18 @@ rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int
     return RT_OK;
 }
 
-rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype,
-                         const float* q_inv, const float* k_inv, const int32_t* idx,
-                         const uint32_t* member_mask, int B, int H, int n, int d, int k, int w,
-                         float scale, int causal, void* out, int out_dtype, float* lse,
-                         float* sum_q, float* sum_k, void* ws, size_t ws_bytes, void* stream) {
-    static const char* fn = "rt_routed_attn";
+}  // extern "C"
+
+namespace {
+
+// rt_routed_attn and rt_routed_attn_split: idx holds the clusters' keys and
+// values, idx_q their queries (nullptr: idx).
+rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const void* v, int dtype,
+                           const float* q_inv, const float* k_inv, const int32_t* idx,
+                           const int32_t* idx_q, const uint32_t* member_mask, int B, int H, int n,
+                           int d, int k, int w, float scale, int causal, void* out, int out_dtype,
+                           float* lse, float* sum_q, float* sum_k, void* ws, size_t ws_bytes,
+                           void* stream) {
     g_err[0] = 0;
     if (!q || !kk || !v || !idx || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
     if ((q_inv == nullptr) != (k_inv == nullptr))
@@ -185,7 +191,7 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
     if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
     if (!out_dtype_ok(out_dtype))
         return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
-    const bool shared = (q == kk) && (q_inv == k_inv);
+    const bool shared = (q == kk) && (q_inv == k_inv) && (idx_q == nullptr || idx_q == idx);
     const int wmax = rt::max_cluster_rows(dtype, d, shared);
     if (w > wmax)
         return fail(RT_EUNSUPPORTED, "%s: w=%d exceeds %d for this dtype, d and q/k sharing", fn,
@@ -203,18 +209,49 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = B * H;
     hipError_t e = hipSuccess;
-    const uint32_t* mask = member_mask;
+    const uint32_t* mask = member_mask;             // the queries' memberships
     if (mask == nullptr) {
-        e = rt::launch_mask(idx, BH, n, k, w, mask_ws, s);
+        e = rt::launch_mask(idx_q ? idx_q : idx, BH, n, k, w, mask_ws, s);
         if (e != hipSuccess) return hip_fail(fn, e);
         mask = mask_ws;
     }
-    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, mask, BH, n, d, k, w, scale,
-                                causal, out, out_dtype, lse, slots, ovf, dir, sum_q, sum_k, s);
+    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, idx_q, mask, BH, n, d, k, w,
+                                scale, causal, out, out_dtype, lse, slots, ovf, dir, sum_q, sum_k,
+                                s);
     if (e != hipSuccess) return hip_fail(fn, e);
     e = rt::launch_combine(mask, slots, ovf, dir, out_dtype, BH, n, d, k, w, out, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype,
+                         const float* q_inv, const float* k_inv, const int32_t* idx,
+                         const uint32_t* member_mask, int B, int H, int n, int d, int k, int w,
+                         float scale, int causal, void* out, int out_dtype, float* lse,
+                         float* sum_q, float* sum_k, void* ws, size_t ws_bytes, void* stream) {
+    return routed_attn_impl("rt_routed_attn", q, kk, v, dtype, q_inv, k_inv, idx, nullptr,
+                            member_mask, B, H, n, d, k, w, scale, causal, out, out_dtype, lse,
+                            sum_q, sum_k, ws, ws_bytes, stream);
+}
+
+rt_status rt_routed_attn_split(const void* q, const void* kk, const void* v, int dtype,
+                               const float* q_inv, const float* k_inv, const int32_t* idx_q,
+                               const int32_t* idx_k, const uint32_t* q_mask, int B, int H, int n,
+                               int d, int k, int w, float scale, void* out, int out_dtype,
+                               float* lse, float* sum_q, float* sum_k, void* ws, size_t ws_bytes,
+                               void* stream) {
+    static const char* fn = "rt_routed_attn_split";
+    if (!idx_q) {
+        g_err[0] = 0;
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    }
+    return routed_attn_impl(fn, q, kk, v, dtype, q_inv, k_inv, idx_k, idx_q, q_mask, B, H, n, d,
+                            k, w, scale, 0, out, out_dtype, lse, sum_q, sum_k, ws, ws_bytes,
+                            stream);
 }
 
 rt_status rt_local_attn(const void* q, const void* kk, const void* v, int dtype, int B, int H,

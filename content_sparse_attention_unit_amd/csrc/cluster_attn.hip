@@ -82,7 +82,8 @@ template <int D, int WMAX, bool SHARED, typename OutT>
 __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_attn_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ kk, const u16* __restrict__ v,
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ idx_q,
+    const uint32_t* __restrict__ mask, int n, int k, int w,
     int KW, float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ slots, float* __restrict__ ovf, int32_t* __restrict__ dir,
     float* __restrict__ sum_q, float* __restrict__ sum_k) {
@@ -100,7 +101,10 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
     const int cl = blockIdx.x, bh = blockIdx.y;
     const long tokbase = (long)bh * n;
     const long rowbase = ((long)bh * k + cl) * w;
-    const int32_t* irow = idx + rowbase;
+    const int32_t* irow = idx + rowbase;              // the cluster's keys (and values)
+    // its queries: the same rows unless the queries were routed on their own
+    // (then only without causality: the mask below compares row indices)
+    const int32_t* irowq = SHARED ? irow : idx_q + rowbase;
 
     // Request every member row at once: keys/queries, then values.  Thread t
     // holds the 16-byte chunk t % CPR of rows t / CPR + (NT / CPR) * it.
@@ -117,12 +121,12 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
         if (!SHARED) iqr[it] = 0.f;
         if (r < w && 8 * ch < D) {
             const long tok = tokbase + clamp_pos(irow[r], n);
-            const long off = tok * D + 8 * ch;
-            xk[it] = *reinterpret_cast<const uint4*>(kk + off);
-            if (!SHARED) xq[it] = *reinterpret_cast<const uint4*>(q + off);
+            const long tokq = tokbase + clamp_pos(irowq[r], n);
+            xk[it] = *reinterpret_cast<const uint4*>(kk + tok * D + 8 * ch);
+            if (!SHARED) xq[it] = *reinterpret_cast<const uint4*>(q + tokq * D + 8 * ch);
             if (want_sums) {
                 ikr[it] = k_inv ? k_inv[tok] : 1.f;
-                if (!SHARED) iqr[it] = q_inv ? q_inv[tok] : 1.f;
+                if (!SHARED) iqr[it] = q_inv ? q_inv[tokq] : 1.f;
             }
         }
     }
@@ -138,15 +142,14 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
         int pos = -1, dest = -2;
         float ik = 0.f, iq = 0.f;
         if (r < w) {
-            const int raw = irow[r];
-            const int posc = clamp_pos(raw, n);
+            const int raw = irowq[r];                 // row r's query token: where its output goes
             if (raw >= 0 && raw < n) {
                 pos = raw;
                 dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
                 if (dest >= kSlots) dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
             }
-            ik = k_inv ? k_inv[tokbase + posc] : 1.f;
-            iq = q_inv ? q_inv[tokbase + posc] : 1.f;
+            ik = k_inv ? k_inv[tokbase + clamp_pos(irow[r], n)] : 1.f;
+            iq = q_inv ? q_inv[tokbase + clamp_pos(raw, n)] : 1.f;
         }
         lpos[r] = pos;
         ldest[r] = dest;
@@ -315,7 +318,8 @@ template <int D, typename OutT>
 __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ kk, const float* __restrict__ v,
     const float* __restrict__ q_inv, const float* __restrict__ k_inv,
-    const int32_t* __restrict__ idx, const uint32_t* __restrict__ mask, int n, int k, int w,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ idx_q,
+    const uint32_t* __restrict__ mask, int n, int k, int w,
     int KW, float scale, int causal, OutT* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ slots, float* __restrict__ ovf, int32_t* __restrict__ dir) {
     __shared__ float lg[1024];
@@ -324,8 +328,8 @@ __global__ __launch_bounds__(64) void cluster_attn_f32_kernel(
     const int lane = threadIdx.x;
     const long tokbase = (long)bh * n;
     const long rowbase = ((long)bh * k + cl) * w;
-    const int32_t* irow = idx + rowbase;
-    const int raw = irow[r];
+    const int32_t* irow = idx + rowbase;              // keys and values
+    const int raw = idx_q[rowbase + r];               // this row's query token
     const int tc = clamp_pos(raw, n);
     for (int i = lane; i < D; i += 64) lqrow[i] = q[(tokbase + tc) * D + i];
     const float qs = scale * (q_inv ? q_inv[tokbase + tc] : 1.f);
@@ -457,6 +461,7 @@ struct AttnArgs {
     const void *q, *kk, *v;
     const float *q_inv, *k_inv;
     const int32_t* idx;
+    const int32_t* idx_q;   // query rows (== idx unless the queries were routed on their own)
     const uint32_t* mask;
     int BH, n, k, w, KW;
     float scale;
@@ -472,8 +477,8 @@ void launch_bf16(const AttnArgs& a, hipStream_t s) {
     using C = AttnCfg<D, WMAX, SHARED>;
     hipLaunchKernelGGL((cluster_attn_bf16_kernel<D, WMAX, SHARED, OutT>), dim3(a.k, a.BH),
                        dim3(C::NT), 0, s, (const u16*)a.q, (const u16*)a.kk, (const u16*)a.v,
-                       a.q_inv, a.k_inv, a.idx, a.mask, a.n, a.k, a.w, a.KW, a.scale, a.causal,
-                       (OutT*)a.out, a.lse, a.slots, a.ovf, a.dir, a.sum_q, a.sum_k);
+                       a.q_inv, a.k_inv, a.idx, a.idx_q, a.mask, a.n, a.k, a.w, a.KW, a.scale,
+                       a.causal, (OutT*)a.out, a.lse, a.slots, a.ovf, a.dir, a.sum_q, a.sum_k);
 }
 
 template <int D, bool SHARED, typename OutT>
@@ -497,15 +502,15 @@ void launch_d(const AttnArgs& a, int dtype, hipStream_t s) {
     if (dtype == 0) {
         hipLaunchKernelGGL((cluster_attn_f32_kernel<D, OutT>), dim3(a.w, a.k, a.BH), dim3(64), 0,
                            s, (const float*)a.q, (const float*)a.kk, (const float*)a.v, a.q_inv,
-                           a.k_inv, a.idx, a.mask, a.n, a.k, a.w, a.KW, a.scale, a.causal,
+                           a.k_inv, a.idx, a.idx_q, a.mask, a.n, a.k, a.w, a.KW, a.scale, a.causal,
                            (OutT*)a.out, a.lse, a.slots, a.ovf, a.dir);
         if (a.sum_q)
             hipLaunchKernelGGL(cluster_sums_f32_kernel, dim3(a.k, a.BH), dim3(128), 0, s,
-                               (const float*)a.q, a.q_inv, a.idx, a.n, D, a.k, a.w, a.sum_q);
+                               (const float*)a.q, a.q_inv, a.idx_q, a.n, D, a.k, a.w, a.sum_q);
         if (a.sum_k)
             hipLaunchKernelGGL(cluster_sums_f32_kernel, dim3(a.k, a.BH), dim3(128), 0, s,
                                (const float*)a.kk, a.k_inv, a.idx, a.n, D, a.k, a.w, a.sum_k);
-    } else if (a.q == a.kk && a.q_inv == a.k_inv) {
+    } else if (a.q == a.kk && a.q_inv == a.k_inv && a.idx_q == a.idx) {
         dispatch_w<D, true, OutT>(a, s);
     } else {
         dispatch_w<D, false, OutT>(a, s);
@@ -543,12 +548,12 @@ hipError_t launch_mask(const int32_t* idx, int BH, int n, int k, int w, uint32_t
 
 hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int dtype,
                                const float* q_inv, const float* k_inv, const int32_t* idx,
-                               const uint32_t* mask, int BH, int n, int d, int k, int w,
-                               float scale, int causal, void* out, int out_dtype, float* lse,
-                               float* slots, float* ovf, int32_t* dir, float* sum_q,
+                               const int32_t* idx_q, const uint32_t* mask, int BH, int n, int d,
+                               int k, int w, float scale, int causal, void* out, int out_dtype,
+                               float* lse, float* slots, float* ovf, int32_t* dir, float* sum_q,
                                float* sum_k, hipStream_t s) {
-    const AttnArgs a{q, kk, v, q_inv, k_inv, idx, mask, BH, n, k, w, mask_words(k), scale,
-                     causal, out, lse, slots, ovf, dir, sum_q, sum_k};
+    const AttnArgs a{q, kk, v, q_inv, k_inv, idx, idx_q ? idx_q : idx, mask, BH, n, k, w,
+                     mask_words(k), scale, causal, out, lse, slots, ovf, dir, sum_q, sum_k};
     if (out_dtype == 1) launch_outt<u16>(a, dtype, d, s);
     else launch_outt<float>(a, dtype, d, s);
     return hipGetLastError();

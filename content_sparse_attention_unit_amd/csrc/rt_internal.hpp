@@ -60,11 +60,13 @@ inline int ovf_ranks(int k) { return k > kSlots ? k - kSlots : 0; }
 hipError_t launch_mask(const int32_t* idx, int BH, int n, int k, int w, uint32_t* mask,
                        hipStream_t s);
 
+// idx: the clusters' keys and values; idx_q: their queries (nullptr: idx; a
+// separate query membership only with causal == 0).
 hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int dtype,
                                const float* q_inv, const float* k_inv, const int32_t* idx,
-                               const uint32_t* mask, int BH, int n, int d, int k, int w,
-                               float scale, int causal, void* out, int out_dtype, float* lse,
-                               float* slots, float* ovf, int32_t* dir, float* sum_q,
+                               const int32_t* idx_q, const uint32_t* mask, int BH, int n, int d,
+                               int k, int w, float scale, int causal, void* out, int out_dtype,
+                               float* lse, float* slots, float* ovf, int32_t* dir, float* sum_q,
                                float* sum_k, hipStream_t s);
 
 hipError_t launch_combine(const uint32_t* mask, const float* slots, const float* ovf,

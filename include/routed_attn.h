@@ -144,6 +144,35 @@ rt_status rt_routed_attn(const void *q, const void *kk, const void *v, int dtype
                          float *sum_q, float *sum_k, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * rt_routed_attn_split -- rt_routed_attn for queries and keys routed on their
+ *   own (distinct query and key vectors, each given to rt_route with the same
+ *   centroids).
+ *   Summary §4: queries and keys are clustered by shared centroids and only
+ *   pairs in the same cluster are considered; content-based sparsity also
+ *   serves data with no order, so there is no causal mask here.  Cluster c's
+ *   queries (idx_q[c]) attend to cluster c's keys and values (idx_k[c]) with
+ *   logit scale * <q_r, k_s> * q_inv[r] * k_inv[s].
+ *   idx_q, idx_k  [B][H][k][w] int32 memberships as in rt_routed_attn (each row
+ *              strictly increasing; out-of-range values are clamped).
+ *   q_mask     optional membership bits of idx_q (the queries' rt_route);
+ *              NULL: built from idx_q in the workspace.
+ *   out        out [B][H][n][d] out_dtype: for each query token, the sum of its
+ *              rows over the clusters whose queries hold it (ascending centroid
+ *              order); 0 for a token that no query cluster holds.
+ *   lse        optional out [B][H][k][w]: per query row, as in rt_routed_attn.
+ *   sum_q, sum_k  optional outs [B][H][k][d]: sums of the unit query rows of
+ *              idx_q and of the unit key rows of idx_k (rt_centroid_update_sums).
+ *   Other arguments, the workspace (RT_OP_ROUTED_ATTN) and the limits on w are
+ *   those of rt_routed_attn with distinct q and kk.  Deterministic.
+ */
+rt_status rt_routed_attn_split(const void *q, const void *kk, const void *v, int dtype,
+                               const float *q_inv, const float *k_inv, const int32_t *idx_q,
+                               const int32_t *idx_k, const uint32_t *q_mask, int B, int H, int n,
+                               int d, int k, int w, float scale, void *out, int out_dtype,
+                               float *lse, float *sum_q, float *sum_k, void *ws, size_t ws_bytes,
+                               void *stream);
+
+/*
  * rt_local_attn -- sliding-window attention for the non-routed heads.
  *   Abstract and summary §6: local attention over a window of recent
  *   positions (windows 512 and 1024 are the ones the pages report).

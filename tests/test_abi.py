@@ -436,3 +436,22 @@ def test_decode_binding_rejects_float32_rows():
     with pytest.raises((TypeError, ValueError)):
         rt.decode_local(*(torch.zeros(1, 1, 4, 16) for _ in range(2)),
                         *(torch.zeros(1, 1, 16) for _ in range(3)), 0)
+
+
+def attn_split(lib, q=FAKE, kk=ctypes.c_void_p(0x3000), v=FAKE, dtype=1, idx_q=FAKE, idx_k=FAKE,
+               n=64, d=16, k=4, w=16, out=ctypes.c_void_p(0x2000), ws=FAKE, ws_bytes=0):
+    return lib.rt_routed_attn_split(q, kk, v, dtype, FAKE, FAKE, idx_q, idx_k, None, 1, 1, n, d,
+                                    k, w, 0.25, out, 1, None, None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(idx_q=None), RT_EINVAL, "null"),
+    (dict(idx_k=None), RT_EINVAL, "null"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(n=4096, d=128, w=200), RT_EUNSUPPORTED, "w=200"),
+    (dict(out=FAKE), RT_EINVAL, "alias"),
+    (dict(), RT_EINVAL, "workspace"),
+])
+def test_routed_attn_split_validation(lib, kw, code, msg):
+    assert attn_split(lib, **kw) == code
+    assert msg in _last(lib)

@@ -11,6 +11,9 @@ members such a token could change are left out of the comparison; the others
 within 1e-5.  Partition: exact clusters where no such near-tie exists (neither
 in a token's nearest centroid nor at a cut between two clusters); otherwise
 every token in exactly one cluster of n/k, rows in ascending position.
+Separately routed queries and keys: on the oracle's memberships, outputs as
+the routed attention, log-sum-exp within 1e-4 (float32) / 5e-3 (bfloat16),
+member sums within 1e-4 per 32 rows.
 """
 import math
 import sys
@@ -222,3 +225,66 @@ def test_partition_clusters_feed_routed_attention(rt, orc):
     torch.cuda.synchronize()
     want, _, _ = orc.routed_attn(x.value, x.value, v.value, want_idx, sc, True)
     assert_close_out(host(out), want, dtype, "routed out on partition clusters")
+
+
+# ---- separately routed queries and keys ----------------------------------------------------
+
+SPLIT = {
+    # name: (dtype, B, H, n, d, k, w)
+    "bf16_d64": ("bf16", 2, 2, 256, 64, 8, 32),
+    "bf16_d128_w128": ("bf16", 1, 2, 1000, 128, 16, 128),
+    "bf16_d32_ragged": ("bf16", 1, 1, 333, 32, 5, 70),
+    "f32_d32": ("f32", 1, 2, 200, 32, 6, 40),
+    "k1_w_eq_n": ("bf16", 1, 1, 96, 64, 1, 96),
+}
+
+
+def run_split(rt, orc, dtype, B, H, n, d, k, w, seed, want_sums=True):
+    q = S.normal_tensor(seed, (B, H, n, d), dtype)
+    kk = S.normal_tensor(seed + 1, (B, H, n, d), dtype)
+    v = S.normal_tensor(seed + 2, (B, H, n, d), dtype)
+    mu0 = S.unit_rows_f32(seed + 3, H * k, d).reshape(H, k, d)
+    _, idx_q, _, _ = orc.route(q.value, mu0, w)
+    _, idx_k, _, _ = orc.route(kk.value, mu0, w)
+    mu = torch.from_numpy(mu0.astype(np.float32)).cuda()
+    qd, kd, vd = dev_tensor(q), dev_tensor(kk), dev_tensor(v)
+    q_inv, _ = rt.route(qd, mu, w)
+    k_inv, _ = rt.route(kd, mu, w)
+    iq, ik = torch.from_numpy(idx_q).cuda(), torch.from_numpy(idx_k).cuda()
+    sc = 1.0 / math.sqrt(d)
+    out, lse, sum_q, sum_k = rt.routed_attn_split(qd, kd, vd, iq, ik, q_inv, k_inv, scale=sc,
+                                                  out_dtype=torch.float32, want_lse=True,
+                                                  want_sums=True)
+    torch.cuda.synchronize()
+    want, want_lse, want_sq, want_sk = orc.routed_attn_split(q.value, kk.value, v.value, idx_q,
+                                                             idx_k, sc)
+    assert_close_out(host(out), want, dtype, "split out")
+    # the bf16 kernels sum the bf16-rounded probabilities: the routed attention's rule
+    assert np.abs(host(lse) - want_lse).max() <= (1e-4 if dtype == "f32" else 5e-3)
+    np.testing.assert_allclose(host(sum_q), want_sq, atol=1e-4 * max(1, w / 32))
+    np.testing.assert_allclose(host(sum_k), want_sk, atol=1e-4 * max(1, w / 32))
+    return qd, kd, vd, iq, ik, q_inv, k_inv, out
+
+
+@pytest.mark.parametrize("name", list(SPLIT))
+def test_routed_attn_split(rt, orc, name):
+    say(f"[case] split {name}")
+    run_split(rt, orc, *SPLIT[name], 83_000 + 10 * list(SPLIT).index(name))
+
+
+def test_routed_attn_split_one_membership_matches_noncausal(rt, orc):
+    """With idx_q == idx_k the split entry point is rt_routed_attn without the
+    causal mask, bit for bit."""
+    dtype, B, H, n, d, k, w = SPLIT["bf16_d64"]
+    qd, kd, vd, iq, ik, q_inv, k_inv, _ = run_split(rt, orc, dtype, B, H, n, d, k, w, 83_900)
+    a = rt.routed_attn_split(qd, kd, vd, iq, iq, q_inv, k_inv, out_dtype=torch.float32)
+    b = rt.routed_attn(qd, kd, vd, iq, q_inv, k_inv, causal=False, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_routed_attn_split_full_size(rt, orc):
+    """The long workload's routed heads with distinct query and key vectors."""
+    cfg = S.CONFIGS["long"]
+    say("[case] split long")
+    run_split(rt, orc, "bf16", cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w, 83_950)
