@@ -462,6 +462,44 @@ def routed_attn_split(q, kk, v, idx_q, idx_k, scale: float):
     return out, lse, sum_q, sum_k
 
 
+# ---- Jensen-Shannon divergence between local and routed attention --------------------------
+# Summary §6 compares, per query, the attention distribution of a local head with that of a
+# routing head by the Jensen-Shannon divergence (natural log, so at most ln 2).  Here, for
+# every row of every cluster (a query i and one of the clusters holding it), P is the local
+# distribution of i (softmax over its window of scale_l * <q_l,i, k_l,j>) and Q the routed one
+# (softmax over the cluster's keys visible to i of scale_r * <q^_i, k^_s>); both are written
+# out as dense distributions over the n positions.
+
+def attn_js(qk, idx, q_l, k_l, window: int, scale_r: float, scale_l: float, causal: bool = True):
+    """-> js [B,H,k,w]: JS(P_local(i) || Q_routed(c, i)) for i = idx[b, h, c, r]."""
+    qk, q_l, k_l, idx = _f64(qk), _f64(q_l), _f64(k_l), _i32(idx)
+    B, H, n, d = qk.shape
+    k, w = idx.shape[2], idx.shape[3]
+    xh, _ = normalize(qk)
+    js = np.empty((B, H, k, w))
+    pos = np.arange(n)
+    for b in range(B):
+        for h in range(H):
+            for c in range(k):
+                members = idx[b, h, c]
+                for r in range(w):
+                    i = members[r]
+                    near = (pos <= i) & (pos > i - window) if causal else np.abs(pos - i) < window
+                    ll = np.where(near, scale_l * (k_l[b, h] @ q_l[b, h, i]), -np.inf)
+                    p = np.exp(ll - ll.max())
+                    p /= p.sum()
+                    keys = members[:r + 1] if causal else members
+                    lr = np.full(n, -np.inf)
+                    lr[keys] = scale_r * (xh[b, h, keys] @ xh[b, h, i])
+                    q = np.exp(lr - lr.max())
+                    q /= q.sum()
+                    m = 0.5 * (p + q)
+                    kl_p = np.sum(p[p > 0] * np.log(p[p > 0] / m[p > 0]))
+                    kl_q = np.sum(q[q > 0] * np.log(q[q > 0] / m[q > 0]))
+                    js[b, h, c, r] = 0.5 * (kl_p + kl_q)
+    return js
+
+
 # ---- incremental decode ------------------------------------------------------------------
 # Decode-time routing (a reading: the pages' sampling needs one token at a time,
 # and the balanced top-w of a whole sequence is not defined for a single new

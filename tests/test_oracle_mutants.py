@@ -90,6 +90,15 @@ MUTANTS = {
                                     "np.add.at(out[b, h], rk, (e / z) @ v[b, h, rk])", "__init__.py"),
     "split_values_from_query_rows": ("np.add.at(out[b, h], rq, (e / z) @ v[b, h, rk])",
                                      "np.add.at(out[b, h], rq, (e / z) @ v[b, h, rq])", "__init__.py"),
+    # Jensen-Shannon diagnostic (numpy)
+    "js_routed_sees_later_keys": ("keys = members[:r + 1] if causal else members",
+                                  "keys = members if causal else members", "__init__.py"),
+    "js_window_one_too_long": ("near = (pos <= i) & (pos > i - window) if causal",
+                               "near = (pos <= i) & (pos >= i - window) if causal", "__init__.py"),
+    "js_without_half": ("js[b, h, c, r] = 0.5 * (kl_p + kl_q)", "js[b, h, c, r] = kl_p + kl_q",
+                        "__init__.py"),
+    "js_local_unscaled": ("ll = np.where(near, scale_l * (k_l[b, h] @ q_l[b, h, i]), -np.inf)",
+                          "ll = np.where(near, (k_l[b, h] @ q_l[b, h, i]), -np.inf)", "__init__.py"),
     "local_decode_window_too_long": ("pos = np.arange(max(0, t - window + 1), t + 1)",
                                      "pos = np.arange(max(0, t - window), t + 1)", "__init__.py"),
 }

@@ -31,6 +31,11 @@ def _unit(a):
     return a / np.linalg.norm(a, axis=-1, keepdims=True)
 
 
+def _softmax(x):
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
 def _sdpa(q, k, v, scale, causal=True, mask=None):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64)
     return F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask,
@@ -820,3 +825,65 @@ def test_split_hand_example(orc):
                                atol=1e-12)
     np.testing.assert_array_equal(out[0, 0, 3], np.zeros(d))
     np.testing.assert_allclose(lse[0, 0, 0, 0], 1.0 + np.log(2.0), atol=1e-12)   # logit 1, twice
+
+
+# ---- Jensen-Shannon divergence between local and routed attention --------------------------
+
+def _dense_js(p, q):
+    from scipy.spatial.distance import jensenshannon
+    return jensenshannon(p, q) ** 2          # natural log by default; scipy returns the root
+
+
+def test_js_matches_scipy_on_dense_distributions(orc):
+    """Each row's divergence against scipy's Jensen-Shannon distance (squared) of
+    the two distributions built here by brute force (masked softmax rows)."""
+    r = _rng(70)
+    B, H, n, d, k, w, W = 1, 2, 30, 6, 3, 8, 5
+    qk = r.standard_normal((B, H, n, d))
+    ql, kl = r.standard_normal((B, H, n, d)), r.standard_normal((B, H, n, d))
+    mu = _unit(r.standard_normal((H, k, d)))
+    _, idx, _, _ = orc.route(qk, mu, w)
+    js = orc.attn_js(qk, idx, ql, kl, W, 1.7, 0.4)
+    u = _unit(qk)
+    for b in range(B):
+        for h in range(H):
+            for c in range(k):
+                for rr in range(w):
+                    i = idx[b, h, c, rr]
+                    lo = max(0, i - W + 1)
+                    p = np.zeros(n)
+                    p[lo:i + 1] = _softmax(0.4 * kl[b, h, lo:i + 1] @ ql[b, h, i])
+                    keys = idx[b, h, c, :rr + 1]
+                    q = np.zeros(n)
+                    q[keys] = _softmax(1.7 * u[b, h, keys] @ u[b, h, i])
+                    assert abs(js[b, h, c, rr] - _dense_js(p, q)) < 1e-12
+
+
+def test_js_zero_for_identical_and_bounded(orc):
+    """One cluster of every token, a window covering the sequence and the local
+    head given the routed head's unit vectors and scale: P = Q, JS = 0.  For
+    random inputs 0 <= JS <= ln 2."""
+    r = _rng(71)
+    B, H, n, d = 1, 1, 16, 4
+    qk = r.standard_normal((B, H, n, d))
+    idx = np.broadcast_to(np.arange(n, dtype=np.int32), (B, H, 1, n))
+    u = _unit(qk)
+    js = orc.attn_js(qk, idx, u, u, n, 0.9, 0.9)
+    np.testing.assert_allclose(js, 0.0, atol=1e-13)
+    ql, kl = 5 * r.standard_normal((B, H, n, d)), 5 * r.standard_normal((B, H, n, d))
+    js2 = orc.attn_js(qk, idx, ql, kl, 3, 4.0, 1.0)
+    assert np.all(js2 >= -1e-15) and np.all(js2 <= np.log(2) + 1e-15)
+
+
+def test_js_window_of_one_closed_form(orc):
+    """Window 1: P is the query itself.  With Q = (q_j, q_i) over an earlier key
+    j and the query: JS = 1/2 ln(2/(1+q_i)) + 1/2 (q_i ln(2 q_i/(1+q_i)) + q_j ln 2)."""
+    qk = np.array([[[[1.0, 0.0], [0.6, 0.8]]]])
+    idx = np.array([[[[0, 1]]]], dtype=np.int32)
+    ql = np.ones((1, 1, 2, 2))
+    js = orc.attn_js(qk, idx, ql, ql, 1, 2.0, 1.0)
+    s = 2.0 * np.array([0.6, 1.0])           # logits of key 0 and of the query itself
+    qj, qi = np.exp(s) / np.exp(s).sum()
+    want = 0.5 * np.log(2 / (1 + qi)) + 0.5 * (qi * np.log(2 * qi / (1 + qi)) + qj * np.log(2))
+    assert abs(js[0, 0, 0, 1] - want) < 1e-13
+    assert abs(js[0, 0, 0, 0]) < 1e-13       # the first token sees only itself on both sides
