@@ -316,7 +316,15 @@ def time_variants(rt, cfg, inp, reps=20):
     out_s = torch.empty_like(qk)
     ws_s = torch.empty(rt.workspace_bytes("routed_attn", B, R, n, d, k, cfg.w), dtype=torch.uint8,
                        device="cuda")
+    # the Jensen-Shannon diagnostic: routed head h against local head h (the first L heads)
+    qk_js = qk[:, :L].contiguous()
+    inv_js, idx_js = rt.route(qk_js, mu[:L].contiguous(), cfg.w)
+    js_out = torch.empty((B, L, k, cfg.w), dtype=torch.float32, device="cuda")
+    ws_js = torch.empty(rt.workspace_bytes("attn_js", B, L, n, d, k, cfg.w), dtype=torch.uint8,
+                        device="cuda")
     calls = {
+        "rt_attn_js": lambda: rt.attn_js(qk_js, inv_js, idx_js, ql, kl, cfg.window, scale_r=scale,
+                                         scale_l=scale, out=js_out, ws=ws_js),
         "rt_local_attn_blocked": lambda: rt.local_attn_blocked(ql, kl, vl, cfg.window, 1,
                                                                scale=scale, out=out_l),
         "rt_routed_attn_split": lambda: rt.routed_attn_split(qk, kd, vd, idx_q, idx_k, q_inv,
@@ -341,7 +349,10 @@ def time_variants(rt, cfg, inp, reps=20):
             "note": f"blocked local: blocks of {cfg.window}, one block of look-back, {L} heads; "
                     f"partition: n/k = {n // k} tokens a cluster, {R} heads; nearest-centroid "
                     f"update: shared q/k, {R} heads; split routing: distinct q and k each "
-                    f"routed (k={k}, w={cfg.w}), {R} heads, non-causal"}
+                    f"routed (k={k}, w={cfg.w}), {R} heads, non-causal; JS diagnostic: "
+                    f"{L} routed heads against the {L} local heads, incl. the local pass "
+                    f"for their denominators",
+            "js_mean": float(js_out.mean())}
 
 
 def time_decode(rt, cfg, inp, group=16, reps=20):

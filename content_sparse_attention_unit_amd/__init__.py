@@ -18,7 +18,7 @@ import torch
 __all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
            "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
            "out_proj_bwd", "in_proj_bwd", "local_attn_blocked", "centroid_update_argmax_",
-           "route_partition", "routed_attn_split", "decode_cache", "decode_fill", "decode_routed",
+           "route_partition", "routed_attn_split", "attn_js", "decode_cache", "decode_fill", "decode_routed",
            "decode_ring_fill", "decode_local", "workspace_bytes", "library_path",
            "mask_words", "RTError", "RT_OP"]
 
@@ -29,7 +29,7 @@ _lib = None
 RT_F32, RT_BF16 = 0, 1
 RT_OP = {"route": 0, "routed_attn": 1, "local_attn": 2, "centroid_update": 3,
          "routed_attn_bwd": 4, "local_attn_bwd": 5, "centroid_update_argmax": 6,
-         "route_partition": 7}
+         "route_partition": 7, "attn_js": 8}
 _STATUS = {0: "RT_OK", 1: "RT_EINVAL", 2: "RT_EUNSUPPORTED", 3: "RT_EHIP"}
 
 
@@ -74,6 +74,7 @@ def _load():
         "rt_route_partition": [P, I, P, I, I, I, I, I, P, P, P, P, Z, P],
         "rt_routed_attn_split": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P, P, P, P,
                                  Z, P],
+        "rt_attn_js": [P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, P, P, Z, P],
         "rt_decode_fill": [P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P],
         "rt_decode_ring_fill": [P, P, I, I, I, I, I, P, P, P],
         "rt_decode_routed": [P, P, P, I, I, I, I, I, P, P, P, P, P, I, F, P, I, P, P],
@@ -480,6 +481,34 @@ def routed_attn_split(q, kk, v, idx_q, idx_k, q_inv=None, k_inv=None, *, scale=N
     if want_sums:
         res += sums
     return res[0] if len(res) == 1 else res
+
+
+def attn_js(qk, q_inv, idx, q_l, k_l, window: int, *, scale_r=None, scale_l=None, causal=True,
+            out=None, ws=None):
+    """Jensen-Shannon divergence [B,H,k,w] between each cluster row's routed
+    distribution and its query's local one (a diagnostic; bf16 rows)."""
+    lib = _load()
+    dev = _gpu(qk, q_inv, idx, q_l, k_l)
+    for t_ in (qk, q_l, k_l):
+        if t_.dtype != torch.bfloat16:
+            raise TypeError("attn_js takes bfloat16 rows")
+    B, H, n, d = qk.shape
+    k, w = idx.shape[2], idx.shape[3]
+    _shape(q_l, qk.shape, "q_l")
+    _shape(k_l, qk.shape, "k_l")
+    _shape(q_inv, (B, H, n), "q_inv")
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    sr = 1.0 / math.sqrt(d) if scale_r is None else float(scale_r)
+    sl = 1.0 / math.sqrt(d) if scale_l is None else float(scale_l)
+    if out is None:
+        out = torch.empty((B, H, k, w), dtype=torch.float32, device=dev)
+    _shape(out, (B, H, k, w), "out")
+    ws, _ = _workspace("attn_js", dev, B, H, n, d, k, w, ws)
+    _check(lib.rt_attn_js(_ptr(qk), _ptr(q_inv), _ptr(idx), _ptr(q_l), _ptr(k_l), B, H, n, d, k,
+                          w, int(window), sr, sl, int(bool(causal)), _ptr(out), _ptr(ws),
+                          0 if ws is None else ws.numel(), _stream(dev)))
+    return out
 
 
 # ---- incremental decode ------------------------------------------------------------------

@@ -17,7 +17,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "librouted_attn.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["capi.hip", "route.hip", "cluster_attn.hip", "cluster_attn_bwd.hip", "ema.hip",
-           "local_attn.hip", "proj.hip", "local_attn_bwd.hip", "layer_bwd.hip", "decode.hip"]
+           "local_attn.hip", "proj.hip", "local_attn_bwd.hip", "layer_bwd.hip", "decode.hip", "js.hip"]
 ARCH = os.environ.get("RT_OFFLOAD_ARCH", "gfx950")
 
 

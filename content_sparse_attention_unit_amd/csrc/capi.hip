@@ -131,6 +131,7 @@ size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
         case RT_OP_LOCAL_ATTN_BWD: return rt::local_bwd_workspace_bytes(B * H, n);
         case RT_OP_CENTROID_UPDATE_ARGMAX: return argmax_ema_ws(B, H, n, d, k);
         case RT_OP_ROUTE_PARTITION: return (size_t)B * H * n * 2 * 4;
+        case RT_OP_ATTN_JS: return align256((size_t)B * H * n * d * 2) + align256((size_t)B * H * n * 4);
         default: return (size_t)-1;
     }
 }
@@ -269,7 +270,7 @@ rt_status rt_local_attn(const void* q, const void* kk, const void* v, int dtype,
     if (!out_dtype_ok(out_dtype))
         return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
     hipError_t e = rt::launch_local_attn(q, kk, v, dtype, B * H, n, d, window, -1, scale, causal, out,
-                                         out_dtype, static_cast<hipStream_t>(stream));
+                                         out_dtype, nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }
@@ -622,7 +623,7 @@ rt_status rt_local_attn_blocked(const void* q, const void* kk, const void* v, in
     if (!out_dtype_ok(out_dtype))
         return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
     hipError_t e = rt::launch_local_attn(q, kk, v, dtype, B * H, n, d, block, lookback, scale, 1,
-                                         out, out_dtype, static_cast<hipStream_t>(stream));
+                                         out, out_dtype, nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }
@@ -776,6 +777,40 @@ rt_status rt_decode_local(const void* q_t, const void* k_t, const void* v_t, int
         return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
     hipError_t e = rt::launch_decode_local(q_t, k_t, v_t, B * H, d, window, ring_k, ring_v, t,
                                            scale, out, out_dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_attn_js(const void* qk, const float* q_inv, const int32_t* idx, const void* q_l,
+                     const void* k_l, int B, int H, int n, int d, int k, int w, int window,
+                     float scale_r, float scale_l, int causal, float* js, void* ws,
+                     size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_attn_js";
+    g_err[0] = 0;
+    if (!qk || !q_inv || !idx || !q_l || !k_l || !js)
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    rt_status st = check_tokens(fn, RT_BF16, B, H, n, d);
+    if (st == RT_OK) st = check_clusters(fn, n, k, w);
+    if (st != RT_OK) return st;
+    if (w > rt::max_js_rows(d))
+        return fail(RT_EUNSUPPORTED, "%s: w=%d exceeds %d at d=%d", fn, w, rt::max_js_rows(d), d);
+    if (window < 1) return fail(RT_EINVAL, "%s: window=%d must be >= 1", fn, window);
+    if (!std::isfinite(scale_r) || !std::isfinite(scale_l))
+        return fail(RT_EINVAL, "%s: scale is not finite", fn);
+    if (causal != 0 && causal != 1) return fail(RT_EINVAL, "%s: causal must be 0 or 1", fn);
+    const size_t out_bytes = align256((size_t)B * H * n * d * 2);
+    const size_t need = out_bytes + align256((size_t)B * H * n * 4);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* lse_l = reinterpret_cast<float*>(static_cast<char*>(ws) + out_bytes);
+    // the local heads' log-denominators (their output, with the keys as values, is discarded)
+    hipError_t e = rt::launch_local_attn(q_l, k_l, k_l, RT_BF16, B * H, n, d, window, -1, scale_l,
+                                         causal, ws, RT_BF16, lse_l, s);
+    if (e == hipSuccess)
+        e = rt::launch_attn_js(qk, q_inv, idx, q_l, k_l, lse_l, B * H, n, d, k, w, window, scale_r,
+                               scale_l, causal, js, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

@@ -134,7 +134,8 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
                                                               const u16* __restrict__ v, int n,
                                                               int window, int lookback,
                                                               float scale, int causal,
-                                                              OutT* __restrict__ out) {
+                                                              OutT* __restrict__ out,
+                                                              float* __restrict__ lse) {
     using C = LocalCfg<D>;
     __shared__ __attribute__((aligned(16))) u16 lk[2][C::KT * C::LDX];
     __shared__ __attribute__((aligned(16))) u16 lv[2][C::KT * C::LDX];
@@ -273,6 +274,8 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
         const float zt = zacc[0] * a1 + z2 * a2;
         const float rz = 1.0f / zt;
         if (qi < n) {
+            if (lse != nullptr && g == 0)            // natural log of the denominator
+                lse[base + qi] = (ms + __log2f(zt)) * 0.6931471805599453f;
             OutT* dst = out + (base + qi) * D + 4 * g;
 #pragma unroll
             for (int jb = 0; jb < C::NJ; ++jb) {
@@ -292,7 +295,8 @@ __global__ __launch_bounds__(64) void local_attn_f32_kernel(const float* __restr
                                                             const float* __restrict__ v, int n,
                                                             int window, int lookback,
                                                             float scale, int causal,
-                                                            OutT* __restrict__ out) {
+                                                            OutT* __restrict__ out,
+                                                            float* __restrict__ lse) {
     __shared__ float lq[D];
     __shared__ float lp[64];
     const int i = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
@@ -339,35 +343,34 @@ __global__ __launch_bounds__(64) void local_attn_f32_kernel(const float* __restr
         const int e = lane + 64 * u;
         if (e < D) Elem<OutT>::store(out, (base + i) * D + e, acc[u] / z);
     }
+    if (lse != nullptr && lane == 0) lse[base + i] = m + logf(z);
 }
 
 template <int D, typename OutT>
 void launch_local_d(const void* q, const void* kk, const void* v, int dtype, int BH, int n,
-                    int window, int lookback, float scale, int causal, void* out,
+                    int window, int lookback, float scale, int causal, void* out, float* lse,
                     hipStream_t s) {
     if (dtype == 1)
         hipLaunchKernelGGL((local_attn_bf16_kernel<D, OutT>),
                            dim3((n + LocalCfg<D>::QT - 1) / LocalCfg<D>::QT, BH),
                            dim3(LocalCfg<D>::NT), 0, s,
                            (const u16*)q, (const u16*)kk, (const u16*)v, n, window, lookback,
-                           scale, causal,
-                           (OutT*)out);
+                           scale, causal, (OutT*)out, lse);
     else
         hipLaunchKernelGGL((local_attn_f32_kernel<D, OutT>), dim3(n, BH), dim3(64), 0, s,
                            (const float*)q, (const float*)kk, (const float*)v, n, window, lookback,
-                           scale,
-                           causal, (OutT*)out);
+                           scale, causal, (OutT*)out, lse);
 }
 
 template <typename OutT>
 void launch_local_outt(const void* q, const void* kk, const void* v, int dtype, int BH, int n,
                        int d, int window, int lookback, float scale, int causal, void* out,
-                       hipStream_t s) {
+                       float* lse, hipStream_t s) {
     switch (d) {
-        case 16: launch_local_d<16, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
-        case 32: launch_local_d<32, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
-        case 64: launch_local_d<64, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
-        default: launch_local_d<128, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, s); break;
+        case 16: launch_local_d<16, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, lse, s); break;
+        case 32: launch_local_d<32, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, lse, s); break;
+        case 64: launch_local_d<64, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, lse, s); break;
+        default: launch_local_d<128, OutT>(q, kk, v, dtype, BH, n, window, lookback, scale, causal, out, lse, s); break;
     }
 }
 
@@ -375,12 +378,13 @@ void launch_local_outt(const void* q, const void* kk, const void* v, int dtype, 
 
 hipError_t launch_local_attn(const void* q, const void* kk, const void* v, int dtype, int BH,
                              int n, int d, int window, int lookback, float scale, int causal,
-                             void* out, int out_dtype, hipStream_t s) {
+                             void* out, int out_dtype, float* lse, hipStream_t s) {
     if (out_dtype == 1)
-        launch_local_outt<u16>(q, kk, v, dtype, BH, n, d, window, lookback, scale, causal, out, s);
+        launch_local_outt<u16>(q, kk, v, dtype, BH, n, d, window, lookback, scale, causal, out,
+                               lse, s);
     else
         launch_local_outt<float>(q, kk, v, dtype, BH, n, d, window, lookback, scale, causal, out,
-                                 s);
+                                 lse, s);
     return hipGetLastError();
 }
 

@@ -91,9 +91,10 @@ hipError_t launch_ema(float* mu, const void* q, const float* q_inv, const void* 
 // lookback < 0: the sliding window [i - window + 1, i] (or the band when not
 // causal); lookback >= 0: blocks of `window` positions, own block and the
 // `lookback` before it (causal).
+// lse: optional [BH][n] float32, the natural log of each query's denominator.
 hipError_t launch_local_attn(const void* q, const void* kk, const void* v, int dtype, int BH,
                              int n, int d, int window, int lookback, float scale, int causal,
-                             void* out, int out_dtype, hipStream_t s);
+                             void* out, int out_dtype, float* lse, hipStream_t s);
 
 hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
                                    const float* q_inv, const float* k_inv, const int32_t* idx,
@@ -172,5 +173,13 @@ hipError_t launch_decode_routed(const void* qk_t, const void* v_t, const float* 
 hipError_t launch_decode_local(const void* q_t, const void* k_t, const void* v_t, int BH, int d,
                                int window, void* rk, void* rv, int t, float scale, void* out,
                                int out_dtype, hipStream_t s);
+
+// Jensen-Shannon divergence of each cluster row's routed distribution from its
+// query's local one (bf16 rows; lse_l: the local heads' natural log-denominators).
+int max_js_rows(int d);
+hipError_t launch_attn_js(const void* qk, const float* q_inv, const int32_t* idx, const void* q_l,
+                          const void* k_l, const float* lse_l, int BH, int n, int d, int k, int w,
+                          int window, float scale_r, float scale_l, int causal, float* js,
+                          hipStream_t s);
 
 }  // namespace rt

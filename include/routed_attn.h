@@ -69,7 +69,8 @@ typedef enum {
     RT_OP_ROUTED_ATTN_BWD = 4,
     RT_OP_LOCAL_ATTN_BWD = 5,
     RT_OP_CENTROID_UPDATE_ARGMAX = 6,
-    RT_OP_ROUTE_PARTITION = 7
+    RT_OP_ROUTE_PARTITION = 7,
+    RT_OP_ATTN_JS = 8
 } rt_op;
 
 /*
@@ -478,6 +479,33 @@ rt_status rt_decode_routed(const void *qk_t, const void *v_t, const float *mu, i
 rt_status rt_decode_local(const void *q_t, const void *k_t, const void *v_t, int B, int H, int d,
                           int window, void *ring_k, void *ring_v, int t, float scale, void *out,
                           int out_dtype, void *stream);
+
+/*
+ * rt_attn_js -- Jensen-Shannon divergence between local and routed attention,
+ *   a diagnostic (Summary §6 compares the two by this divergence, natural log,
+ *   at most ln 2).  For each row r of each cluster c, with i = idx[c][r]:
+ *     P = the local attention distribution of query i (softmax over i's window
+ *         of scale_l * <q_l[i], k_l[j]>, as rt_local_attn computes it),
+ *     Q = the routed distribution of that row (softmax over the cluster's keys
+ *         row r sees of scale_r * <qk[i], qk[s]> * q_inv[i] * q_inv[s]),
+ *     js[c][r] = 1/2 KL(P || M) + 1/2 KL(Q || M), M = (P + Q) / 2.
+ *   qk         [B][H][n][d] bf16, the routing heads' shared query/key rows;
+ *              q_inv [B][H][n] float32 and idx [B][H][k][w] as from rt_route.
+ *   q_l, k_l   [B][H][n][d] bf16, a local head's queries and keys (head h of
+ *              the local heads is compared with head h of the routing heads).
+ *   causal     1: row r sees the cluster's rows 0..r and i's window is
+ *              [i - window + 1, i]; 0: all rows and |i - j| < window.
+ *   js         out [B][H][k][w] float32, in [0, ln 2].
+ *   ws: rt_workspace_bytes(RT_OP_ATTN_JS, B, H, n, d, k, w) bytes (the local
+ *   heads' log-denominators and a discarded attention output).
+ *   Limits: w <= 128 at d = 128, 256 at d = 64, 512 below.  P's denominator
+ *   is the local kernel's (bf16 probabilities summed in float32), so values
+ *   agree with an exact evaluation to a few 1e-3.
+ */
+rt_status rt_attn_js(const void *qk, const float *q_inv, const int32_t *idx, const void *q_l,
+                     const void *k_l, int B, int H, int n, int d, int k, int w, int window,
+                     float scale_r, float scale_l, int causal, float *js, void *ws,
+                     size_t ws_bytes, void *stream);
 
 /* Workspace size in bytes for operation `op` at these sizes (0 if none,
  * (size_t)-1 if the sizes are invalid). */

@@ -455,3 +455,28 @@ def attn_split(lib, q=FAKE, kk=ctypes.c_void_p(0x3000), v=FAKE, dtype=1, idx_q=F
 def test_routed_attn_split_validation(lib, kw, code, msg):
     assert attn_split(lib, **kw) == code
     assert msg in _last(lib)
+
+
+def attn_js(lib, qk=FAKE, q_inv=FAKE, idx=FAKE, n=64, d=16, k=4, w=16, window=8, causal=1,
+            js=ctypes.c_void_p(0x2000), ws=FAKE, ws_bytes=0):
+    return lib.rt_attn_js(qk, q_inv, idx, FAKE, FAKE, 1, 1, n, d, k, w, window, 0.25, 0.25,
+                          causal, js, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(qk=None), RT_EINVAL, "null"),
+    (dict(js=None), RT_EINVAL, "null"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(n=4096, d=128, w=200), RT_EUNSUPPORTED, "w=200"),
+    (dict(d=48), RT_EUNSUPPORTED, "d=48"),
+    (dict(window=0), RT_EINVAL, "window"),
+    (dict(causal=3), RT_EINVAL, "causal"),
+    (dict(), RT_EINVAL, "workspace"),
+])
+def test_attn_js_validation(lib, kw, code, msg):
+    assert attn_js(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_attn_js_workspace_size(lib):
+    assert lib.rt_workspace_bytes(8, 1, 2, 100, 64, 4, 25) == 25600 + 1024

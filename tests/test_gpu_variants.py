@@ -288,3 +288,52 @@ def test_routed_attn_split_full_size(rt, orc):
     cfg = S.CONFIGS["long"]
     say("[case] split long")
     run_split(rt, orc, "bf16", cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w, 83_950)
+
+
+# ---- Jensen-Shannon divergence between local and routed attention --------------------------
+
+JS_TOL = 2e-3     # the local denominator is the local kernel's (bf16 probabilities, fp32 sum)
+
+JS = {
+    # name: (B, H, n, d, k, w, window, causal)
+    "d64_w32": (1, 2, 300, 64, 6, 40, 32, True),
+    "d128_w64": (1, 1, 1000, 128, 8, 128, 64, True),
+    "d32_noncausal": (1, 2, 200, 32, 5, 50, 16, False),
+    "d16_window1": (2, 1, 128, 16, 4, 32, 1, True),
+}
+
+
+def run_js(rt, orc, B, H, n, d, k, w, window, causal, seed, clusters=None):
+    qk, ql, kl = (S.normal_tensor(seed + i, (B, H, n, d), "bf16") for i in range(3))
+    mu0 = S.unit_rows_f32(seed + 3, H * k, d).reshape(H, k, d)
+    _, idx, _, _ = orc.route(qk.value, mu0, w)
+    qd = dev_tensor(qk)
+    q_inv, _ = rt.route(qd, torch.from_numpy(mu0.astype(np.float32)).cuda(), w)
+    sr, sl = 2.0, 1.0 / math.sqrt(d)
+    js = rt.attn_js(qd, q_inv, torch.from_numpy(idx).cuda(), dev_tensor(ql), dev_tensor(kl), window,
+                    scale_r=sr, scale_l=sl, causal=causal)
+    torch.cuda.synchronize()
+    got = host(js)
+    assert np.all(got >= 0) and np.all(got <= math.log(2) + 1e-7)
+    sel = list(range(k)) if clusters is None else clusters
+    want = orc.attn_js(qk.value, idx[:, :, sel], ql.value, kl.value, window, sr, sl, causal)
+    err = np.abs(got[:, :, sel] - want)
+    assert err.max() <= JS_TOL, f"max err {err.max():.3e}"
+    return got
+
+
+@pytest.mark.parametrize("name", list(JS))
+def test_attn_js(rt, orc, name):
+    say(f"[case] js {name}")
+    run_js(rt, orc, *JS[name], 84_000 + 10 * list(JS).index(name))
+
+
+def test_attn_js_full_size(rt, orc):
+    """The long workload's routed heads against a local head each (one batch
+    row, 8 heads, n = 8192, k = 64, w = 128, window 512); the oracle on three
+    clusters."""
+    cfg = S.CONFIGS["long"]
+    say("[case] js long")
+    got = run_js(rt, orc, cfg.B, 2, cfg.n, cfg.d, cfg.k, cfg.w, cfg.window, True, 84_900,
+                 clusters=[0, 31, 63])
+    say(f"[js long] mean {got.mean():.4f}")
