@@ -25,6 +25,15 @@
 namespace rt {
 namespace {
 
+// max of three floats in one instruction.  Written out because fmaxf on the
+// MFMA results makes the compiler quiet each operand first (they are not known
+// to be canonical), which costs an instruction per value.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // softmax_pv_half on unscaled logits: the scale enters as one fma with the
 // reference, exp2(s * sl2 - m), and the chunk maximum is scaled once (sl2 > 0).
 // The fma does not round s * sl2 while m is the rounded product, so for the
@@ -36,8 +45,9 @@ template <int NJ, int LDX>
 __device__ __forceinline__ void softmax_pv_half_unscaled(f32x4 (&sv)[2], float sl2, float& m,
                                                          f32x4& zacc, f32x4 (&o)[NJ],
                                                          const u16* lv, int r16, int g) {
-    const float lmax = sl2 * fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                                   fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    const float r1 = max3f(sv[0][0], sv[0][1], sv[0][2]);
+    const float r2 = max3f(sv[0][3], sv[1][0], sv[1][1]);
+    const float lmax = sl2 * max3f(max3f(sv[1][2], sv[1][3], r1), r2, r2);
     lazy_rescale<NJ>(lmax, m, zacc, o);
     const float nm = (m == -INFINITY) ? 0.f : -m;
     uint32_t pw[2][2];
@@ -175,6 +185,11 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
         return lookback < 0 ? i - window + 1 : max(0, (i / window - lookback) * window);
     };
     const int qlo = band_lo(qi);
+    // this lane's visible keys as one unsigned range: key j is visible iff
+    // (unsigned)(j - qlo_m) <= qspan (an empty band masks every key)
+    const int qhi = min(n - 1, causal ? qi : qi + window - 1);
+    const int qlo_m = qhi >= qlo ? qlo : -0x40000000;
+    const uint32_t qspan = qhi >= qlo ? (uint32_t)(qhi - qlo) : 0u;
     const int lo = max(0, band_lo(q0));
     const int hi = causal ? min(n - 1, q0 + C::QT - 1) : min(n - 1, q0 + C::QT - 1 + window - 1);
     const int blo = band_lo(qb0);
@@ -210,11 +225,10 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
                 sv[kb] = acc;                          /* unscaled: sl2 enters in exp2 */  \
             }                                                                                \
             if (kh_ < clo || kh_ + 31 > chi) {     /* not inside every band: mask */         \
+                const uint32_t rel0 = (uint32_t)(kh_ + 4 * g - qlo_m);                       \
                 _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
                     _Pragma("unroll") for (int i = 0; i < 4; ++i) {                          \
-                        const int j = kh_ + 16 * kb + 4 * g + i;                             \
-                        const bool ok = j < n && j >= qlo &&                                 \
-                                        (causal ? j <= qi : j < qi + window);                \
+                        const bool ok = rel0 + (uint32_t)(16 * kb + i) <= qspan;             \
                         sv[kb][i] = ok ? sv[kb][i] : -INFINITY;                              \
                     }                                                                        \
             }                                                                                \
