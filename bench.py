@@ -40,9 +40,9 @@ LOCAL_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/local_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "c4589438bb0525ca0521cd40c55ddfe15c2bc6ac9cf51e117a566e01bc3356cb",
-    "fetch_kib": 12989.4375, "write_kib": 8192.0,
-    "fetch_scale": 262144.0 / 131093.0, "write_scale": 262144.0 / 262144.0,
+    "sha256": "fa3ce382f9b13a47f7ef7647bc8c72832b5109eae163db1005f3138d11284aca",
+    "fetch_kib": 12983.395833333334, "write_kib": 8192.0,
+    "fetch_scale": 262144.0 / 131095.8, "write_scale": 262144.0 / 262144.0,
 }
 
 
