@@ -18,7 +18,7 @@ import torch
 __all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
            "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
            "out_proj_bwd", "in_proj_bwd", "local_attn_blocked", "centroid_update_argmax_",
-           "route_partition", "routed_attn_split", "attn_js", "decode_cache", "decode_fill", "decode_routed",
+           "route_partition", "routed_attn_split", "routed_attn_update_", "attn_js", "decode_cache", "decode_fill", "decode_routed",
            "decode_ring_fill", "decode_local", "workspace_bytes", "library_path",
            "mask_words", "RTError", "RT_OP"]
 
@@ -29,7 +29,7 @@ _lib = None
 RT_F32, RT_BF16 = 0, 1
 RT_OP = {"route": 0, "routed_attn": 1, "local_attn": 2, "centroid_update": 3,
          "routed_attn_bwd": 4, "local_attn_bwd": 5, "centroid_update_argmax": 6,
-         "route_partition": 7, "attn_js": 8}
+         "route_partition": 7, "attn_js": 8, "routed_attn_update": 9}
 _STATUS = {0: "RT_OK", 1: "RT_EINVAL", 2: "RT_EUNSUPPORTED", 3: "RT_EHIP"}
 
 
@@ -74,6 +74,8 @@ def _load():
         "rt_route_partition": [P, I, P, I, I, I, I, I, P, P, P, P, Z, P],
         "rt_routed_attn_split": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, P, I, P, P, P, P,
                                  Z, P],
+        "rt_routed_attn_update": [P, P, P, I, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P, F,
+                                  P, Z, P],
         "rt_attn_js": [P, P, P, P, P, I, I, I, I, I, I, I, F, F, I, P, P, Z, P],
         "rt_decode_fill": [P, P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, P],
         "rt_decode_ring_fill": [P, P, I, I, I, I, I, P, P, P],
@@ -447,6 +449,33 @@ def route_partition(qk, mu, *, want_mask=False, out=None, ws=None):
                                   _ptr(idx), _ptr(mask), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(dev)))
     return (inv, idx, mask) if mask is not None else (inv, idx)
+
+
+def routed_attn_update_(q, kk, v, idx, q_inv, k_inv, mu, lam: float, *, scale=None, causal=True,
+                        want_lse=False, out_dtype=None, mask=None, out=None, lse=None, ws=None):
+    """routed_attn followed by the centroid update from the same memberships
+    (mu updated in place, in the output's scatter launch).  Returns out (and
+    lse when asked)."""
+    lib = _load()
+    dev = _gpu(q, kk, v, idx, q_inv, k_inv, mask, mu)
+    B, H, n, d = q.shape
+    k, w = idx.shape[2], idx.shape[3]
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    if mu.dtype != torch.float32 or tuple(mu.shape) != (H, k, d):
+        raise ValueError("mu must be float32 [H, k, d]")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, k, w), dtype=torch.float32, device=dev)
+    ws, _ = _workspace("routed_attn_update", dev, B, H, n, d, k, w, ws)
+    _check(lib.rt_routed_attn_update(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
+                                     _ptr(k_inv), _ptr(idx), _ptr(mask), B, H, n, d, k, w, sc,
+                                     int(causal), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(mu),
+                                     float(lam), _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(dev)))
+    return (out, lse) if want_lse else out
 
 
 def routed_attn_split(q, kk, v, idx_q, idx_k, q_inv=None, k_inv=None, *, scale=None,

@@ -69,6 +69,11 @@ rt_status check_entries(const char* fn, const char* what, int m) {
     return RT_OK;
 }
 
+// rt_routed_attn_update's member sums (queries, then keys unless shared).
+size_t update_sums_ws(int B, int H, int k, int d) {
+    return align256((size_t)2 * B * H * k * d * sizeof(float));
+}
+
 size_t route_ws(int B, int H, int n, int k) { return (size_t)B * H * k * n * sizeof(float); }
 
 // rt_routed_attn workspace: mask [B*H*n][KW] u32 | slots [B*H*n][kSlots][d] f32 |
@@ -131,6 +136,7 @@ size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
         case RT_OP_LOCAL_ATTN_BWD: return rt::local_bwd_workspace_bytes(B * H, n);
         case RT_OP_CENTROID_UPDATE_ARGMAX: return argmax_ema_ws(B, H, n, d, k);
         case RT_OP_ROUTE_PARTITION: return (size_t)B * H * n * 2 * 4;
+        case RT_OP_ROUTED_ATTN_UPDATE: return attn_ws(B, H, n, d, k, w) + update_sums_ws(B, H, k, d);
         case RT_OP_ATTN_JS: return align256((size_t)B * H * n * d * 2) + align256((size_t)B * H * n * 4);
         default: return (size_t)-1;
     }
@@ -178,9 +184,11 @@ rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const 
                            const int32_t* idx_q, const uint32_t* member_mask, int B, int H, int n,
                            int d, int k, int w, float scale, int causal, void* out, int out_dtype,
                            float* lse, float* sum_q, float* sum_k, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           void* stream, float* mu = nullptr, float lambda = 0.f) {
     g_err[0] = 0;
     if (!q || !kk || !v || !idx || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (mu != nullptr && !(lambda >= 0.f && lambda <= 1.f))
+        return fail(RT_EINVAL, "%s: lambda=%g outside [0, 1]", fn, (double)lambda);
     if ((q_inv == nullptr) != (k_inv == nullptr))
         return fail(RT_EINVAL, "%s: q_inv and k_inv must both be given or both be NULL", fn);
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
@@ -197,11 +205,15 @@ rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const 
     if (w > wmax)
         return fail(RT_EUNSUPPORTED, "%s: w=%d exceeds %d for this dtype, d and q/k sharing", fn,
                     w, wmax);
-    const size_t need = attn_ws(B, H, n, d, k, w);
+    const size_t need = attn_ws(B, H, n, d, k, w) + (mu != nullptr ? update_sums_ws(B, H, k, d) : 0);
     if (ws == nullptr || ws_bytes < need)
         return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
     char* base = static_cast<char*>(ws);
+    if (mu != nullptr) {        // the member sums of the update, after the attention's parts
+        sum_q = reinterpret_cast<float*>(base + attn_ws(B, H, n, d, k, w));
+        sum_k = shared ? nullptr : sum_q + (size_t)B * H * k * d;
+    }
     uint32_t* mask_ws = reinterpret_cast<uint32_t*>(base);
     float* slots = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k));
     float* ovf = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d));
@@ -220,7 +232,8 @@ rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const 
                                 scale, causal, out, out_dtype, lse, slots, ovf, dir, sum_q, sum_k,
                                 s);
     if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_combine(mask, slots, ovf, dir, out_dtype, BH, n, d, k, w, out, s);
+    e = rt::launch_combine(mask, slots, ovf, dir, out_dtype, BH, n, d, k, w, out, s, mu, sum_q,
+                           sum_k, B, H, lambda);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }
@@ -237,6 +250,22 @@ rt_status rt_routed_attn(const void* q, const void* kk, const void* v, int dtype
     return routed_attn_impl("rt_routed_attn", q, kk, v, dtype, q_inv, k_inv, idx, nullptr,
                             member_mask, B, H, n, d, k, w, scale, causal, out, out_dtype, lse,
                             sum_q, sum_k, ws, ws_bytes, stream);
+}
+
+rt_status rt_routed_attn_update(const void* q, const void* kk, const void* v, int dtype,
+                                const float* q_inv, const float* k_inv, const int32_t* idx,
+                                const uint32_t* member_mask, int B, int H, int n, int d, int k,
+                                int w, float scale, int causal, void* out, int out_dtype,
+                                float* lse, float* mu, float lambda, void* ws, size_t ws_bytes,
+                                void* stream) {
+    static const char* fn = "rt_routed_attn_update";
+    if (!mu) {
+        g_err[0] = 0;
+        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    }
+    return routed_attn_impl(fn, q, kk, v, dtype, q_inv, k_inv, idx, nullptr, member_mask, B, H, n,
+                            d, k, w, scale, causal, out, out_dtype, lse, nullptr, nullptr, ws,
+                            ws_bytes, stream, mu, lambda);
 }
 
 rt_status rt_routed_attn_split(const void* q, const void* kk, const void* v, int dtype,

@@ -390,10 +390,12 @@ __global__ __launch_bounds__(128) void cluster_sums_f32_kernel(
     }
 }
 
-// One thread per (token, 16 output dims), for NO outputs sharing one
+// One thread per (token, 4 * kCombineQV output dims), for NO outputs sharing one
 // membership (the backward's three gradients): the slots hold the rows of
 // ranks 0..kSlots-1 contiguously; higher ranks are read from the overflow
 // buffer at the rows the directory lists.
+constexpr int kCombineQV = 2;
+
 template <int NO>
 struct CombineSet {
     const float* slots[NO];
@@ -401,16 +403,42 @@ struct CombineSet {
     void* out[NO];
 };
 
+// The centroid update folded into the same launch (the workgroups past the
+// combine's): mu <- lambda*mu + (1-lambda)/2 * (sum over b of sum_q + sum_k),
+// one thread per centroid element, as rt_centroid_update_sums computes it.
+struct FoldedEma {
+    float* mu;                 // nullptr: none
+    const float* sum_q;
+    const float* sum_k;        // nullptr: sum_q counts twice (shared q/k)
+    int B;
+    long HKD;
+    float lam;
+    unsigned first_block;      // first workgroup of the update
+};
+
 template <typename OutT, int D, int NO>
 __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict__ mask,
                                                       const int32_t* __restrict__ dir,
                                                       CombineSet<NO> cs, long BHn, int n, int k,
-                                                      int w, int KW) {
-    constexpr int DG = D / 16;
+                                                      int w, int KW, FoldedEma ema) {
+    constexpr int QV = kCombineQV;               // float4 per thread and row
+    constexpr int DG = D / (4 * QV);
+    if (ema.mu != nullptr && blockIdx.x >= ema.first_block) {
+        const long i = (long)(blockIdx.x - ema.first_block) * 256 + threadIdx.x;
+        if (i >= ema.HKD) return;
+        float sq = 0.f, sk = 0.f;
+        for (int b = 0; b < ema.B; ++b) {
+            sq += ema.sum_q[b * ema.HKD + i];
+            if (ema.sum_k != nullptr) sk += ema.sum_k[b * ema.HKD + i];
+        }
+        const float tot = (ema.sum_k != nullptr) ? sq + sk : 2.f * sq;
+        ema.mu[i] = fmaf(ema.lam, ema.mu[i], (1.0f - ema.lam) * 0.5f * tot);
+        return;
+    }
     const long gid = (long)blockIdx.x * 256 + threadIdx.x;
     const long tok = gid / DG;
     if (tok >= BHn) return;
-    const int d0 = 16 * (int)(gid % DG);
+    const int d0 = 4 * QV * (int)(gid % DG);
     const uint32_t* mrow = mask + tok * KW;
     int cnt = 0;
     for (int i = 0; i < KW; ++i) cnt += __popc(mrow[i]);
@@ -419,17 +447,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
     const int32_t* drow = dir + tok * (k - kSlots);
 #pragma unroll
     for (int o = 0; o < NO; ++o) {
-        float4 p[kSlots][4];
+        float4 p[kSlots][QV];
         const float* sp = cs.slots[o] + tok * kSlots * D + d0;
 #pragma unroll
         for (int j = 0; j < kSlots; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < QV; ++q)
                 p[j][q] = (j < cnt) ? *reinterpret_cast<const float4*>(sp + (long)j * D + 4 * q)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-        float4 acc[4];
+        float4 acc[QV];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < QV; ++q) {
             acc[q] = p[0][q];
 #pragma unroll
             for (int j = 1; j < kSlots; ++j) {
@@ -442,7 +470,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
         for (int j = kSlots; j < cnt; ++j) {
             const float* op = cs.ovf[o] + (bhkw + drow[j - kSlots]) * D + d0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < QV; ++q) {
                 const float4 v4 = *reinterpret_cast<const float4*>(op + 4 * q);
                 acc[q].x += v4.x;
                 acc[q].y += v4.y;
@@ -452,7 +480,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
         }
         OutT* dst = static_cast<OutT*>(cs.out[o]) + tok * D + d0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < QV; ++q)
             store4<OutT>(dst + 4 * q, acc[q].x, acc[q].y, acc[q].z, acc[q].w);
     }
 }
@@ -561,30 +589,35 @@ hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int
 
 template <typename OutT, int D, int NO>
 void launch_combine_d(const uint32_t* mask, const int32_t* dir, const CombineSet<NO>& cs, int BH,
-                      int n, int k, int w, hipStream_t s) {
+                      int n, int k, int w, FoldedEma ema, hipStream_t s) {
     const long BHn = (long)BH * n;
-    const long threads = BHn * (D / 16);
-    hipLaunchKernelGGL((combine_kernel<OutT, D, NO>), dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, s, mask, dir, cs, BHn, n, k, w, mask_words(k));
+    const long threads = BHn * (D / (4 * kCombineQV));
+    const unsigned comb_blocks = (unsigned)((threads + 255) / 256);
+    ema.first_block = comb_blocks;
+    const unsigned ema_blocks = ema.mu != nullptr ? (unsigned)((ema.HKD + 255) / 256) : 0u;
+    hipLaunchKernelGGL((combine_kernel<OutT, D, NO>), dim3(comb_blocks + ema_blocks), dim3(256), 0,
+                       s, mask, dir, cs, BHn, n, k, w, mask_words(k), ema);
 }
 
 template <typename OutT, int NO>
 void launch_combine_t(const uint32_t* mask, const int32_t* dir, const CombineSet<NO>& cs, int BH,
-                      int n, int d, int k, int w, hipStream_t s) {
+                      int n, int d, int k, int w, const FoldedEma& ema, hipStream_t s) {
     switch (d) {
-        case 16: launch_combine_d<OutT, 16, NO>(mask, dir, cs, BH, n, k, w, s); break;
-        case 32: launch_combine_d<OutT, 32, NO>(mask, dir, cs, BH, n, k, w, s); break;
-        case 64: launch_combine_d<OutT, 64, NO>(mask, dir, cs, BH, n, k, w, s); break;
-        default: launch_combine_d<OutT, 128, NO>(mask, dir, cs, BH, n, k, w, s); break;
+        case 16: launch_combine_d<OutT, 16, NO>(mask, dir, cs, BH, n, k, w, ema, s); break;
+        case 32: launch_combine_d<OutT, 32, NO>(mask, dir, cs, BH, n, k, w, ema, s); break;
+        case 64: launch_combine_d<OutT, 64, NO>(mask, dir, cs, BH, n, k, w, ema, s); break;
+        default: launch_combine_d<OutT, 128, NO>(mask, dir, cs, BH, n, k, w, ema, s); break;
     }
 }
 
 hipError_t launch_combine(const uint32_t* mask, const float* slots, const float* ovf,
                           const int32_t* dir, int out_dtype, int BH, int n, int d, int k, int w,
-                          void* out, hipStream_t s) {
+                          void* out, hipStream_t s, float* mu, const float* sum_q,
+                          const float* sum_k, int B, int H, float lambda) {
     const CombineSet<1> cs{{slots}, {ovf}, {out}};
-    if (out_dtype == 1) launch_combine_t<u16, 1>(mask, dir, cs, BH, n, d, k, w, s);
-    else launch_combine_t<float, 1>(mask, dir, cs, BH, n, d, k, w, s);
+    const FoldedEma ema{mu, sum_q, sum_k, B, (long)H * k * d, lambda, 0u};
+    if (out_dtype == 1) launch_combine_t<u16, 1>(mask, dir, cs, BH, n, d, k, w, ema, s);
+    else launch_combine_t<float, 1>(mask, dir, cs, BH, n, d, k, w, ema, s);
     return hipGetLastError();
 }
 
@@ -593,7 +626,7 @@ hipError_t launch_combine3_f32(const uint32_t* mask, const float* const slots[3]
                                int k, int w, float* const out[3], hipStream_t s) {
     const CombineSet<3> cs{{slots[0], slots[1], slots[2]}, {ovf[0], ovf[1], ovf[2]},
                            {out[0], out[1], out[2]}};
-    launch_combine_t<float, 3>(mask, dir, cs, BH, n, d, k, w, s);
+    launch_combine_t<float, 3>(mask, dir, cs, BH, n, d, k, w, FoldedEma{}, s);
     return hipGetLastError();
 }
 

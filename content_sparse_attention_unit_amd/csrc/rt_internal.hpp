@@ -69,9 +69,13 @@ hipError_t launch_cluster_attn(const void* q, const void* kk, const void* v, int
                                float* lse, float* slots, float* ovf, int32_t* dir, float* sum_q,
                                float* sum_k, hipStream_t s);
 
+// mu != nullptr: the centroid update from the member sums (sum_q, sum_k of B
+// batch rows; sum_k nullptr counts sum_q twice) runs in the same launch.
 hipError_t launch_combine(const uint32_t* mask, const float* slots, const float* ovf,
                           const int32_t* dir, int out_dtype, int BH, int n, int d, int k, int w,
-                          void* out, hipStream_t s);
+                          void* out, hipStream_t s, float* mu = nullptr,
+                          const float* sum_q = nullptr, const float* sum_k = nullptr, int B = 0,
+                          int H = 0, float lambda = 0.f);
 
 // The same for three float32 outputs sharing one membership (one pass over the
 // bits).

@@ -70,7 +70,8 @@ typedef enum {
     RT_OP_LOCAL_ATTN_BWD = 5,
     RT_OP_CENTROID_UPDATE_ARGMAX = 6,
     RT_OP_ROUTE_PARTITION = 7,
-    RT_OP_ATTN_JS = 8
+    RT_OP_ATTN_JS = 8,
+    RT_OP_ROUTED_ATTN_UPDATE = 9
 } rt_op;
 
 /*
@@ -143,6 +144,27 @@ rt_status rt_routed_attn(const void *q, const void *kk, const void *v, int dtype
                          const uint32_t *member_mask, int B, int H, int n, int d, int k, int w,
                          float scale, int causal, void *out, int out_dtype, float *lse,
                          float *sum_q, float *sum_k, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rt_routed_attn_update -- rt_routed_attn followed by the centroid update of
+ *   rt_centroid_update_sums from the same memberships, with the update run in
+ *   the launch that scatters the output (one launch fewer than the two calls).
+ *   Summary §4 (online k-means: the centroids move towards the mean of their
+ *   members as an exponential moving average): the member sums of the queries
+ *   and keys (q*q_inv, kk*k_inv over each cluster's rows, all batch rows) give
+ *       mu_c <- lambda * mu_c + (1 - lambda)/2 * (S_Q[c] + S_K[c]).
+ *   The attention uses idx, computed with mu before the update; results are
+ *   those of rt_routed_attn then rt_centroid_update_sums, bit for bit.
+ *   mu         [H][k][d] float32, updated in place; lambda in [0, 1].
+ *   Other arguments as rt_routed_attn (no sum outputs).
+ *   ws: rt_workspace_bytes(RT_OP_ROUTED_ATTN_UPDATE, ...) bytes.
+ */
+rt_status rt_routed_attn_update(const void *q, const void *kk, const void *v, int dtype,
+                                const float *q_inv, const float *k_inv, const int32_t *idx,
+                                const uint32_t *member_mask, int B, int H, int n, int d, int k,
+                                int w, float scale, int causal, void *out, int out_dtype,
+                                float *lse, float *mu, float lambda, void *ws, size_t ws_bytes,
+                                void *stream);
 
 /*
  * rt_routed_attn_split -- rt_routed_attn for queries and keys routed on their

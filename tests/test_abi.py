@@ -167,7 +167,7 @@ def test_workspace_sizes(lib):
         ((B * H * n * 4 + 255) // 256) * 256 + slots + B * H * 4 * w * d * 4)   # k <= 4: none
     assert lib.rt_workspace_bytes(2, B, H, n, d, k, w) == 0
     assert lib.rt_workspace_bytes(3, B, H, n, d, k, w) == 0
-    assert lib.rt_workspace_bytes(9, B, H, n, d, k, w) == ctypes.c_size_t(-1).value
+    assert lib.rt_workspace_bytes(10, B, H, n, d, k, w) == ctypes.c_size_t(-1).value
     assert lib.rt_workspace_bytes(0, 0, H, n, d, k, w) == ctypes.c_size_t(-1).value
 
 
@@ -480,3 +480,25 @@ def test_attn_js_validation(lib, kw, code, msg):
 
 def test_attn_js_workspace_size(lib):
     assert lib.rt_workspace_bytes(8, 1, 2, 100, 64, 4, 25) == 25600 + 1024
+
+
+def attn_update(lib, mu=FAKE, lam=0.9, ws=FAKE, ws_bytes=1 << 40):
+    return lib.rt_routed_attn_update(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 1, 1, 64, 16, 4,
+                                     16, 0.25, 1, ctypes.c_void_p(0x2000), 1, None, mu,
+                                     ctypes.c_float(lam), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(mu=None), RT_EINVAL, "null"),
+    (dict(lam=1.5), RT_EINVAL, "lambda"),
+    (dict(lam=float("nan")), RT_EINVAL, "lambda"),
+    (dict(ws_bytes=100), RT_EINVAL, "workspace"),
+])
+def test_routed_attn_update_validation(lib, kw, code, msg):
+    assert attn_update(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_routed_attn_update_workspace_size(lib):
+    plain = lib.rt_workspace_bytes(1, 2, 3, 100, 64, 8, 20)
+    assert lib.rt_workspace_bytes(9, 2, 3, 100, 64, 8, 20) == plain + 2 * 2 * 3 * 8 * 64 * 4

@@ -126,6 +126,13 @@ def run_routed_case(rt, orc, cfg, scale=None, causal=True, check_scores=True):
     assert torch.equal(idx_f, idx) and torch.equal(out_f, out_e)
     assert_mask_matches(host(mask_f), gidx, cfg.n)
     assert np.abs(host(mu_f)[same_c] - mu_o[same_c]).max(initial=0.0) <= MU_MAX_ABS
+
+    # attention and update in one call: the same output and centroids, bit for bit
+    mu_u = mu.clone()
+    out_u = rt.routed_attn_update_(qk, qk, v, idx_f, inv_f, inv_f, mu_u, cfg.lam, scale=sc,
+                                   causal=causal, out_dtype=torch.float32, mask=mask_f)
+    torch.cuda.synchronize()
+    assert torch.equal(out_u, out_f) and torch.equal(mu_u, mu_f)
     return dict(inp=inp, qk=qk, v=v, mu=mu, inv=inv, idx=idx, out=out_e, mu_e=mu_e, sc=sc,
                 differs=differs)
 
@@ -173,7 +180,11 @@ def test_distinct_q_and_k(rt, orc, dtype):
     rt.centroid_update_(mu2, q, q_inv, idx_o_dev, 0.7, kk=kk, k_inv=k_inv)
     mu3 = mu.clone()
     rt.centroid_update_sums_(mu3, sq, 0.7, sum_k=sk)
+    mu4 = mu.clone()
+    out4 = rt.routed_attn_update_(q, kk, v, idx_o_dev, q_inv, k_inv, mu4, 0.7, scale=sc,
+                                  out_dtype=torch.float32)
     torch.cuda.synchronize()
+    assert torch.equal(out4, out) and torch.equal(mu4, mu3)
     out_o, _, _ = orc.routed_attn(inp["qk"].value, kin.value, inp["v"].value, idx_o, sc, True)
     assert_close_out(host(out), out_o, dtype)
     mu_o = orc.centroid_update(inp["mu"], inp["qk"].value, kin.value, idx_o, 0.7)
