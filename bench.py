@@ -243,11 +243,12 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
                        device="cuda")
     ws_l = torch.empty(rt.workspace_bytes("local_attn_bwd", B, L, n, d, 1, 1), dtype=torch.uint8,
                        device="cuda")
+    ws_p = rt.proj_bwd_workspace(B, n, dm, d, R, L, "cuda")    # split weight gradients
     T, NO, NC = B * n, (R + L) * d, (2 * R + 3 * L) * d
     band = L * B * (n * sc.window - sc.window * (sc.window - 1) / 2)   # (query, key) pairs
     calls = {
         "rt_out_proj_bwd": (lambda: rt.out_proj_bwd(dy, t["o_r"], t["o_l"], w_o,
-                                                    out=(do_r, do_l, dw_o)),
+                                                    out=(do_r, do_l, dw_o), ws=ws_p),
                             2 * 2.0 * T * dm * NO),
         "rt_routed_attn_bwd": (lambda: rt.routed_attn_bwd(t["qk"], t["qk"], t["v"], t["idx"], lse,
                                                           do_r, t["inv"], t["inv"], scale=scale,
@@ -259,7 +260,7 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
                                                         out=(dq_l, dk_l, dv_l), ws=ws_l),
                               10.0 * band * d),
         "rt_in_proj_bwd": (lambda: rt.in_proj_bwd(x0, w_in, dqk, dv, dq_l, dk_l, dv_l, dres=dy,
-                                                  out=(dx, dw_in)),
+                                                  out=(dx, dw_in), ws=ws_p),
                            2 * 2.0 * T * NC * dm),
     }
     per, tfl = {}, {}

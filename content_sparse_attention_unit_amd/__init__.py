@@ -67,8 +67,8 @@ def _load():
                                P],
         "rt_local_attn_bwd": [P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z, P],
         "rt_normalize_bwd": [P, I, P, P, P, ctypes.c_long, I, P, P],
-        "rt_out_proj_bwd": [P, P, P, P, I, I, I, I, I, I, P, P, P, P],
-        "rt_in_proj_bwd": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P],
+        "rt_out_proj_bwd": [P, P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P],
+        "rt_in_proj_bwd": [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, Z, P],
         "rt_local_attn_blocked": [P, P, P, I, I, I, I, I, I, I, F, P, I, P],
         "rt_centroid_update_argmax": [P, P, P, I, I, I, I, I, I, F, P, Z, P],
         "rt_route_partition": [P, I, P, I, I, I, I, I, P, P, P, P, Z, P],
@@ -88,6 +88,8 @@ def _load():
         fn.restype = ctypes.c_int
     lib.rt_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.rt_workspace_bytes.restype = ctypes.c_size_t
+    lib.rt_proj_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.rt_proj_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.rt_last_error.argtypes = []
     lib.rt_last_error.restype = ctypes.c_char_p
     lib.rt_status_string.argtypes = [I]
@@ -360,9 +362,22 @@ def normalize_bwd(x, inv_norm, g1, g2=None, out=None):
     return out
 
 
-def out_proj_bwd(dy, o_r, o_l, w_o, out=None):
+def proj_bwd_workspace(B: int, n: int, dm: int, d: int, R: int, L: int, device):
+    """A workspace that lets the projections' weight gradients split their
+    contraction (None when they would not)."""
+    nb = int(_load().rt_proj_bwd_workspace_bytes(B, n, dm, d, R, L))
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb > 0 else None
+
+
+def _ws_args(ws):
+    return (_ptr(ws), 0 if ws is None else ws.numel())
+
+
+def out_proj_bwd(dy, o_r, o_l, w_o, out=None, ws="auto"):
     """(do_r, do_l, dw_o) for y = x + [o_r | o_l] W_o^T: do_* bfloat16
-    head-major (do_l None when there are no local heads), dw_o float32."""
+    head-major (do_l None when there are no local heads), dw_o float32.  ``ws``:
+    a workspace for the split weight gradient ("auto": allocated here; None:
+    no split)."""
     lib = _load()
     dev = _gpu(dy, o_r, o_l, w_o)
     B, R, n, d = o_r.shape
@@ -373,14 +388,18 @@ def out_proj_bwd(dy, o_r, o_l, w_o, out=None):
                torch.empty((B, L, n, d), dtype=torch.bfloat16, device=dev) if L > 0 else None,
                torch.empty((dm, (R + L) * d), dtype=torch.float32, device=dev))
     _gpu(*out)
+    if isinstance(ws, str):
+        ws = proj_bwd_workspace(B, n, dm, d, R, L, dev)
     _check(lib.rt_out_proj_bwd(_ptr(dy), _ptr(o_r), _ptr(o_l), _ptr(w_o), B, n, dm, d, R, L,
-                               *(_ptr(t) for t in out), _stream(dev)))
+                               *(_ptr(t) for t in out), *_ws_args(ws), _stream(dev)))
     return out
 
 
-def in_proj_bwd(x, w_in, dqk, dv, dq_l=None, dk_l=None, dv_l=None, dres=None, out=None):
+def in_proj_bwd(x, w_in, dqk, dv, dq_l=None, dk_l=None, dv_l=None, dres=None, out=None,
+                ws="auto"):
     """(dx, dw_in), float32, for [qk | v | q_l | k_l | v_l] = x W_in^T and the
-    heads' float32 gradients; dres (bfloat16 [B,n,dm] or None) is added to dx."""
+    heads' float32 gradients; dres (bfloat16 [B,n,dm] or None) is added to dx.
+    ``ws`` as in out_proj_bwd."""
     lib = _load()
     dev = _gpu(x, w_in, dqk, dv, dq_l, dk_l, dv_l, dres)
     B, n, dm = x.shape
@@ -390,9 +409,11 @@ def in_proj_bwd(x, w_in, dqk, dv, dq_l=None, dk_l=None, dv_l=None, dres=None, ou
         out = (torch.empty((B, n, dm), dtype=torch.float32, device=dev),
                torch.empty(((2 * R + 3 * L) * d, dm), dtype=torch.float32, device=dev))
     _gpu(*out)
+    if isinstance(ws, str):
+        ws = proj_bwd_workspace(B, n, dm, d, R, L, dev)
     _check(lib.rt_in_proj_bwd(_ptr(x), _ptr(w_in), _ptr(dqk), _ptr(dv), _ptr(dq_l), _ptr(dk_l),
                               _ptr(dv_l), _ptr(dres), B, n, dm, d, R, L, *(_ptr(t) for t in out),
-                              _stream(dev)))
+                              *_ws_args(ws), _stream(dev)))
     return out
 
 

@@ -74,6 +74,28 @@ size_t update_sums_ws(int B, int H, int k, int d) {
     return align256((size_t)2 * B * H * k * d * sizeof(float));
 }
 
+// Splits of a weight-gradient product (M x N outputs, contraction over T
+// tokens) that fill the chip (about two workgroups a compute unit) and fit in
+// ws_bytes of float32 partial products; 1 when no split applies.
+int weight_grad_splits(long M, long N, long T, size_t ws_bytes) {
+    const long tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    long want = 512 / tiles;
+    want = std::min(want, (T + 63) / 64 / 8);                   // at least 8 k-tiles a split
+    want = std::min(want, (long)(ws_bytes / ((size_t)M * N * sizeof(float))));
+    want = std::min(want, 8L);
+    return want >= 2 ? (int)want : 1;
+}
+
+// Workspace that lets both weight gradients of a layer split (0 if neither would).
+size_t proj_bwd_ws(int B, int n, int dm, int d, int R, int L) {
+    const long T = (long)B * n, NO = (long)(R + L) * d, NC = (long)(2 * R + 3 * L) * d;
+    const int so = weight_grad_splits(dm, NO, T, (size_t)-1);
+    const int si = weight_grad_splits(NC, dm, T, (size_t)-1);
+    const size_t bo = so > 1 ? (size_t)so * dm * NO * sizeof(float) : 0;
+    const size_t bi = si > 1 ? (size_t)si * NC * dm * sizeof(float) : 0;
+    return std::max(bo, bi);
+}
+
 size_t route_ws(int B, int H, int n, int k) { return (size_t)B * H * k * n * sizeof(float); }
 
 // rt_routed_attn workspace: mask [B*H*n][KW] u32 | slots [B*H*n][kSlots][d] f32 |
@@ -524,7 +546,7 @@ rt_status rt_normalize_bwd(const void* x, int dtype, const float* inv_norm, cons
 
 rt_status rt_out_proj_bwd(const void* dy, const void* o_r, const void* o_l, const void* w_o,
                           int B, int n, int dm, int d, int R, int L, void* do_r, void* do_l,
-                          float* dw_o, void* stream) {
+                          float* dw_o, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_out_proj_bwd";
     g_err[0] = 0;
     if (!dy || !o_r || !w_o || !do_r || !dw_o || (L > 0 && (!o_l || !do_l)))
@@ -573,6 +595,8 @@ rt_status rt_out_proj_bwd(const void* dy, const void* o_r, const void* o_l, cons
     q.K = T;
     q.n = n;
     q.d = d;
+    q.ksplit = ws != nullptr ? weight_grad_splits(dm, NO, T, ws_bytes) : 1;
+    q.part = static_cast<float*>(ws);
     e = rt::launch_gemm_bwd(rt::GEMM_DWO, q, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
@@ -581,7 +605,7 @@ rt_status rt_out_proj_bwd(const void* dy, const void* o_r, const void* o_l, cons
 rt_status rt_in_proj_bwd(const void* x, const void* w_in, const float* dqk, const float* dv,
                          const float* dq_l, const float* dk_l, const float* dv_l, const void* dres,
                          int B, int n, int dm, int d, int R, int L, float* dx, float* dw_in,
-                         void* stream) {
+                         void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_in_proj_bwd";
     g_err[0] = 0;
     if (!x || !w_in || !dqk || !dv || !dx || !dw_in || (L > 0 && (!dq_l || !dk_l || !dv_l)))
@@ -630,6 +654,8 @@ rt_status rt_in_proj_bwd(const void* x, const void* w_in, const float* dqk, cons
     q.K = T;
     q.n = n;
     q.d = d;
+    q.ksplit = ws != nullptr ? weight_grad_splits(NC, dm, T, ws_bytes) : 1;
+    q.part = static_cast<float*>(ws);
     e = rt::launch_gemm_bwd(rt::GEMM_DWIN, q, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
@@ -842,6 +868,11 @@ rt_status rt_attn_js(const void* qk, const float* q_inv, const int32_t* idx, con
                                scale_l, causal, js, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
+}
+
+size_t rt_proj_bwd_workspace_bytes(int B, int n, int dm, int d, int R, int L) {
+    if (B <= 0 || n <= 0 || dm <= 0 || d <= 0 || R <= 0 || L < 0) return (size_t)-1;
+    return proj_bwd_ws(B, n, dm, d, R, L);
 }
 
 }  // extern "C"

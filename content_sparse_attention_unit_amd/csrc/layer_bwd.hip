@@ -23,7 +23,11 @@
 // over heads), so the layer needs no copies.  One workgroup = a 128 x 128
 // output tile (four waves of 64 x 64), K in steps of 64 through
 // double-buffered LDS tiles fed by register prefetch; each wave computes the
-// transposed product so a lane holds four consecutive output columns.
+// transposed product so a lane holds four consecutive output columns.  The
+// weight gradients have few output tiles and a long contraction (all tokens):
+// they split the contraction over several workgroups per tile, write the
+// partial products to a workspace and add them up in a fixed order
+// (gemm_reduce_kernel), so results do not depend on scheduling.
 //
 // norm_bwd_kernel: one wave per row, the row and its gradients in registers.
 #include "rt_common.hpp"
@@ -146,14 +150,18 @@ __global__ __launch_bounds__(GNT, 2) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) acc[ni][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = (p.K + GBK - 1) / GBK;
-    tile_load<AM, AF>(p.a, m0, p.M, 0, p.K, p.n, p.d, ra);
-    tile_load<BM, BF>(p.b, n0, p.N, 0, p.K, p.n, p.d, rb);
+    // this workgroup's range of contraction tiles (all of them unless split)
+    const int nk_all = (p.K + GBK - 1) / GBK;
+    const int per = (nk_all + p.ksplit - 1) / p.ksplit;
+    const int kt0 = (int)blockIdx.z * per;
+    const int nk = min(nk_all, kt0 + per);
+    tile_load<AM, AF>(p.a, m0, p.M, kt0 * GBK, p.K, p.n, p.d, ra);
+    tile_load<BM, BF>(p.b, n0, p.N, kt0 * GBK, p.K, p.n, p.d, rb);
     tile_store<AM>(la[0], ra);
     tile_store<BM>(lb[0], rb);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
+    for (int kt = kt0; kt < nk; ++kt) {
+        const int buf = (kt - kt0) & 1;
         if (kt + 1 < nk) {
             tile_load<AM, AF>(p.a, m0, p.M, (kt + 1) * GBK, p.K, p.n, p.d, ra);
             tile_load<BM, BF>(p.b, n0, p.N, (kt + 1) * GBK, p.K, p.n, p.d, rb);
@@ -189,7 +197,9 @@ __global__ __launch_bounds__(GNT, 2) void gemm_kernel(GemmArgs p) {
             const int nn = n0 + 64 * wn + 16 * ni + 4 * g;
             if (nn >= p.N) continue;
             float c0 = acc[ni][mi][0], c1 = acc[ni][mi][1], c2 = acc[ni][mi][2], c3 = acc[ni][mi][3];
-            if constexpr (CM == 0) {
+            if (CM == 0 && p.ksplit > 1) {          // a partial product: added up later
+                store4<float>(p.part + ((long)blockIdx.z * p.M + m) * p.N + nn, c0, c1, c2, c3);
+            } else if constexpr (CM == 0) {
                 const long off = (long)m * p.N + nn;
                 if (p.res != nullptr) {
                     const uint2 rr = *reinterpret_cast<const uint2*>(p.res + off);
@@ -210,6 +220,31 @@ __global__ __launch_bounds__(GNT, 2) void gemm_kernel(GemmArgs p) {
             }
         }
     }
+}
+
+// C = sum over z of part[z] (in order of z) + the residual: four elements a
+// thread (M * N is a multiple of 4: N is).
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int S,
+                                                          long MN, const u16* __restrict__ res,
+                                                          float* __restrict__ c) {
+    const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= MN) return;
+    float4 t = *reinterpret_cast<const float4*>(part + i);
+    for (int z = 1; z < S; ++z) {
+        const float4 u = *reinterpret_cast<const float4*>(part + (long)z * MN + i);
+        t.x += u.x;
+        t.y += u.y;
+        t.z += u.z;
+        t.w += u.w;
+    }
+    if (res != nullptr) {
+        const uint2 rr = *reinterpret_cast<const uint2*>(res + i);
+        t.x += bf2f((u16)(rr.x & 0xffffu));
+        t.y += bf2f((u16)(rr.x >> 16));
+        t.z += bf2f((u16)(rr.y & 0xffffu));
+        t.w += bf2f((u16)(rr.y >> 16));
+    }
+    *reinterpret_cast<float4*>(c + i) = t;
 }
 
 // One wave per row of d elements (d <= 128: two per lane).
@@ -254,8 +289,17 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const void* __restrict__ 
 
 template <int AM, bool AF, int BM, bool BF, int CM>
 hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {
-    const dim3 grid((p.M + GBM - 1) / GBM, (p.N + GBN - 1) / GBN);
-    hipLaunchKernelGGL((gemm_kernel<AM, AF, BM, BF, CM>), grid, dim3(GNT), 0, s, p);
+    const int split = (CM == 0 && p.ksplit > 1 && p.part != nullptr) ? p.ksplit : 1;
+    GemmArgs q = p;
+    q.ksplit = split;
+    const dim3 grid((p.M + GBM - 1) / GBM, (p.N + GBN - 1) / GBN, split);
+    hipLaunchKernelGGL((gemm_kernel<AM, AF, BM, BF, CM>), grid, dim3(GNT), 0, s, q);
+    if (split > 1) {
+        const long MN = (long)p.M * p.N;
+        hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((MN / 4 + 255) / 256)), dim3(256),
+                           0, s, p.part, split, MN, reinterpret_cast<const u16*>(p.res),
+                           static_cast<float*>(p.c[0]));
+    }
     return hipGetLastError();
 }
 

@@ -151,6 +151,11 @@ struct GemmArgs {
     int hc[5];
     const uint16_t* res;
     int M, N, K, n, d;
+    // float32 row-major C only: ksplit > 1 splits the contraction into that
+    // many ranges, each product going to part[z][M][N], then added in order
+    // of z (deterministic) into C, with the residual.
+    int ksplit;
+    float* part;
 };
 // The four products of the projections' backward:
 //   GEMM_DO    dO = dy W_o        A = dy [T][dm] row-major, B = W_o [dm][N] (idx-contiguous), C head-major bf16

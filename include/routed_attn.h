@@ -353,10 +353,16 @@ rt_status rt_normalize_bwd(const void *x, int dtype, const float *inv_norm, cons
  *          L = 0): rounded once, as rt_routed_attn_bwd and rt_local_attn_bwd
  *          take them.   dw_o out [dm][(R + L) d] float32.
  *   bf16 products, float32 accumulation; outputs alias no input.
+ *   ws     optional float32 workspace (NULL: none) of ws_bytes: with room for
+ *          at least two dm x (R + L) d partial products, dw_o's contraction
+ *          over the B n tokens is split over more workgroups and the parts
+ *          are added in a fixed order (results independent of scheduling;
+ *          rt_proj_bwd_workspace_bytes gives the size that lets both layer
+ *          gradients split fully).
  */
 rt_status rt_out_proj_bwd(const void *dy, const void *o_r, const void *o_l, const void *w_o,
                           int B, int n, int dm, int d, int R, int L, void *do_r, void *do_l,
-                          float *dw_o, void *stream);
+                          float *dw_o, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * rt_in_proj_bwd -- gradients of rt_in_proj.
@@ -370,12 +376,18 @@ rt_status rt_out_proj_bwd(const void *dy, const void *o_r, const void *o_l, cons
  *   dres     [B][n][dm] bf16 or NULL: a gradient added to dx (the residual's,
  *            i.e. the dy given to rt_out_proj_bwd).
  *   dx       out [B][n][dm] float32;  dw_in out [(2R + 3L) d][dm] float32.
+ *   ws       optional workspace as in rt_out_proj_bwd, for dw_in.
  *   Outputs alias no input.
  */
 rt_status rt_in_proj_bwd(const void *x, const void *w_in, const float *dqk, const float *dv,
                          const float *dq_l, const float *dk_l, const float *dv_l, const void *dres,
                          int B, int n, int dm, int d, int R, int L, float *dx, float *dw_in,
-                         void *stream);
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace in bytes that lets the weight gradients of rt_out_proj_bwd and
+ * rt_in_proj_bwd split their contraction fully at these sizes (0: they would
+ * not split; (size_t)-1: invalid sizes). */
+size_t rt_proj_bwd_workspace_bytes(int B, int n, int dm, int d, int R, int L);
 
 /*
  * Variants: readings the pages leave open, built beside the main path.

@@ -329,7 +329,8 @@ def test_out_proj_bwd_validation(lib, kw, code, msg):
              dw_o=ctypes.c_void_p(0x7000))
     a.update(kw)
     assert lib.rt_out_proj_bwd(a["dy"], a["o_r"], a["o_l"], a["w_o"], a["B"], a["n"], a["dm"],
-                               a["d"], a["R"], a["L"], a["do_r"], a["do_l"], a["dw_o"], None) == code
+                               a["d"], a["R"], a["L"], a["do_r"], a["do_l"], a["dw_o"], None, 0,
+                               None) == code
     assert msg in _last(lib)
 
 
@@ -349,7 +350,7 @@ def test_in_proj_bwd_validation(lib, kw, code, msg):
     a.update(kw)
     assert lib.rt_in_proj_bwd(a["x"], a["w_in"], a["dqk"], a["dv"], a["dq_l"], a["dk_l"],
                               a["dv_l"], a["dres"], a["B"], a["n"], a["dm"], a["d"], a["R"],
-                              a["L"], a["dx"], a["dw_in"], None) == code
+                              a["L"], a["dx"], a["dw_in"], None, 0, None) == code
     assert msg in _last(lib)
 
 
@@ -502,3 +503,13 @@ def test_routed_attn_update_validation(lib, kw, code, msg):
 def test_routed_attn_update_workspace_size(lib):
     plain = lib.rt_workspace_bytes(1, 2, 3, 100, 64, 8, 20)
     assert lib.rt_workspace_bytes(9, 2, 3, 100, 64, 8, 20) == plain + 2 * 2 * 3 * 8 * 64 * 4
+
+
+def test_proj_bwd_workspace_size(lib):
+    # the long stack layer: dW_o (1024 x 1536, 96 output tiles) splits 5 ways over 8192
+    # tokens, dW_in (3584 x 1024, 224 tiles) 2 ways: the larger of the two partial sets
+    B, n, dm, d, R, L = 1, 8192, 1024, 128, 8, 4
+    want = max(5 * dm * (R + L) * d * 4, 2 * (2 * R + 3 * L) * d * dm * 4)
+    assert lib.rt_proj_bwd_workspace_bytes(B, n, dm, d, R, L) == want
+    assert lib.rt_proj_bwd_workspace_bytes(1, 64, 64, 16, 2, 1) == 0     # too few k-tiles
+    assert lib.rt_proj_bwd_workspace_bytes(0, 64, 64, 16, 2, 1) == ctypes.c_size_t(-1).value

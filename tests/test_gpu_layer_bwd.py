@@ -154,6 +154,9 @@ PROJ = {
     "d16": (1, 200, 64, 16, 3, 2),
     "no_local": (1, 130, 96, 32, 2, 0),
     "d128": (1, 256, 512, 128, 2, 1),
+    # enough tokens for the weight gradients to split their contraction (ragged last split)
+    "split_ragged": (1, 2500, 192, 64, 2, 1),
+    "split_b2": (2, 1024, 256, 64, 2, 1),
 }
 
 
@@ -247,6 +250,34 @@ def test_proj_bwd_full_size(rt, orc):
     assert_within(host(got[2]), dw_o, 1.01 * sc.n * 2.0 ** -24 * m_w, "dw_o")
     rows = np.sort(np.random.default_rng(9).choice(sc.n, 256, replace=False))
     check_out_proj_bwd(rt, orc, x, w_in, w_o, o_r, o_l, dy, rows=rows)
+
+
+def test_weight_grad_split_is_deterministic_and_matches_unsplit(rt, orc):
+    """The split weight gradients: bit-identical on repeats, and the unsplit
+    products (no workspace) within the same float32 summation bound."""
+    B, n, dm, d, R, L = PROJ["split_ragged"]
+    x, w_in, w_o, o_r, o_l, dy, dc = proj_bwd_case(B, n, dm, d, R, L, 77_000)
+    ws = rt.proj_bwd_workspace(B, n, dm, d, R, L, "cuda")
+    assert ws is not None
+    args = (dev_tensor(dy), dev_tensor(o_r), dev_tensor(o_l), dev_tensor(w_o))
+    a = rt.out_proj_bwd(*args, ws=ws)[2].clone()
+    b = rt.out_proj_bwd(*args, ws=ws)[2].clone()
+    c = rt.out_proj_bwd(*args, ws=None)[2]
+    dcd = [torch.from_numpy(t.astype(np.float32)).cuda() for t in dc]
+    xin = (dev_tensor(x), dev_tensor(w_in), *dcd)
+    e = rt.in_proj_bwd(*xin, ws=ws)[1].clone()
+    f = rt.in_proj_bwd(*xin, ws=ws)[1].clone()
+    g = rt.in_proj_bwd(*xin, ws=None)[1]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(e, f)
+    _, _, dw_o = orc.out_proj_bwd(dy.value, o_r.value, o_l.value, w_o.value)
+    _, _, m_w = orc.out_proj_bwd(np.abs(dy.value), np.abs(o_r.value), np.abs(o_l.value),
+                                 np.abs(w_o.value), rounding=False)
+    assert_within(host(c), dw_o, 1.01 * n * 2.0 ** -24 * m_w, "dw_o unsplit")
+    _, want_dw = orc.in_proj_bwd(x.value, w_in.value, *dc)
+    rnd = [np.abs(orc.round_bf16(t)) for t in dc]
+    _, m_dw = orc.in_proj_bwd(np.abs(x.value), np.abs(w_in.value), *rnd, rounding=False)
+    assert_within(host(g), want_dw, 1.01 * n * 2.0 ** -24 * m_dw, "dw_in unsplit")
 
 
 # ---- the whole layer ---------------------------------------------------------------------
