@@ -9,8 +9,10 @@ local heads.  The default workload is the long-sequence layer: batch 1, 8
 routed heads (k=64 centroids, w=128) and 4 local heads (window 512), n=8192,
 d=128, bfloat16.
 
-Prints one JSON line (see the design doc for the fields).  The CPU baseline is the
-fp64 oracle timed on the host on one full step of the same workload.
+The steps are launched eagerly on one stream (--graph replays a captured HIP
+graph of the step instead).  Prints one JSON line: the metric and its value,
+the per-call timings, the roofline of the dominant kernel and, beside them, the
+fp64 oracle timed on the host cores on full steps of the same workload.
 """
 from __future__ import annotations
 
@@ -132,10 +134,11 @@ def cpu_baseline(cfg, inp, scale, min_seconds=5.0):
                       f"attention), fp64, {threads} threads"}
 
 
-def time_stack(rt, sc, reps=5):
+def time_stack(rt, sc, reps=5, use_graph=False):
     """The stack of sc.layers layers (x -> in_proj -> route -> routed attention
     (+member sums) -> centroid update -> local attention -> out_proj, residual in
-    place), captured as one HIP graph; returns timings and rates."""
+    place), launched eagerly on one stream or captured as one HIP graph;
+    returns timings and rates."""
     B, n, dm, d, R, L, k, w = sc.B, sc.n, sc.dm, sc.d, sc.R, sc.L, sc.k, sc.w
     scale = 1.0 / math.sqrt(d)
     x0 = dev(S.stack_x(sc))
@@ -174,17 +177,20 @@ def time_stack(rt, sc, reps=5):
         x = forward()
         torch.cuda.synchronize()
         finite = bool(torch.isfinite(x.float()).all())
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            forward()
+        run = forward
+        if use_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                forward()
+            run = graph.replay
         torch.cuda.synchronize()
         for _ in range(2):
-            graph.replay()
+            run()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(reps):
-            graph.replay()
+            run()
         b.record(stream)
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / reps
@@ -208,7 +214,7 @@ def time_stack(rt, sc, reps=5):
     bwd = time_layer_bwd(rt, sc, stream, layers[0], x0, dict(qk=qk, v=v, ql=ql, kl=kl, vl=vl,
                                                           inv=inv, idx=idx, mask=mask, o_r=o_r,
                                                           o_l=o_l, ws_r=ws_r, ws_a=ws_a))
-    return {"layers": sc.layers, "d_model": dm, "ms_per_forward": ms,
+    return {"layers": sc.layers, "d_model": dm, "ms_per_forward": ms, "graph": use_graph,
             "backward": bwd,
             "tokens_per_s": B * n / (ms * 1e-3), "us_per_layer": ms * 1e3 / sc.layers,
             "finite": finite,
@@ -509,8 +515,10 @@ def main():
                     "the long workload (reported apart from the per-layer metric)")
     ap.add_argument("--no-extras", action="store_true", help="skip timing the variants and the "
                     "decode steps of the long workload (reported apart from the metric)")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying "
-                    "a captured HIP graph of the step")
+    ap.add_argument("--graph", action="store_true", help="replay a captured HIP graph of the "
+                    "step (and of the stack) instead of launching eagerly on one stream; graph "
+                    "replay measured slower here")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly (the default)")
     ap.add_argument("--concurrent-local", action="store_true", help="run the local heads "
                     "concurrently on a second stream instead of after the routed heads")
     ap.add_argument("--sweep", action="store_true", help="instead of the benchmark step, time "
@@ -618,7 +626,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    use_graph = not args.no_graph
+    use_graph = args.graph and not args.no_graph
     with torch.cuda.stream(stream):
         for _ in range(max(1, args.warmup)):
             step()
@@ -736,7 +744,7 @@ def main():
         "wall_s_timed": t_wall,
     }
     if args.workload == "long" and not args.no_stack:
-        res["stack"] = time_stack(rt, S.STACKS["long_stack"])
+        res["stack"] = time_stack(rt, S.STACKS["long_stack"], use_graph=use_graph)
     if args.workload == "long" and not args.no_extras:
         res["variants"] = time_variants(rt, cfg, inp)
         res["decode"] = time_decode(rt, cfg, inp)
