@@ -21,7 +21,8 @@
 // is ever transposed in memory.  Operands can also be the head-major
 // [B][H][n][d] tensors of the attention heads (several segments, concatenated
 // over heads), so the layer needs no copies.  One workgroup = a 128 x 128
-// output tile (four waves of 64 x 64) or a 128 x 256 one (eight), K in steps of 64 through
+// output tile (eight waves of 64 x 32) or a 128 x 256 one (sixteen waves of
+// 32 x 64), K in steps of 64 through
 // double-buffered LDS tiles fed by register prefetch; each wave computes the
 // transposed product so a lane holds four consecutive output columns.  The
 // weight gradients have few output tiles and a long contraction (all tokens):
@@ -325,13 +326,15 @@ hipError_t launch_gemm(const GemmArgs& p, hipStream_t s) {
 
 hipError_t launch_gemm_bwd(int which, const GemmArgs& p, hipStream_t s) {
     switch (which) {
-        case GEMM_DO: return launch_gemm<OP_KC_RM, false, OP_IC_RM, false, 1, 128, 128, 2, 2, 2>(p, s);
-        case GEMM_DWO: return launch_gemm<OP_IC_RM, false, OP_IC_HM, false, 0, 128, 128, 2, 2, 2>(p, s);
-        // The two products of the input projection's backward (float32 operands
-        // A) measured 19% faster on 128 x 256 tiles of eight waves at d_model =
-        // 1024, n = 8192; those of the output projection stay on 128 x 128.
-        case GEMM_DX: return launch_gemm<OP_KC_HM, true, OP_IC_RM, false, 0, 128, 256, 2, 4, 1>(p, s);
-        case GEMM_DWIN: return launch_gemm<OP_IC_HM, true, OP_IC_RM, false, 0, 128, 256, 2, 4, 1>(p, s);
+        // Tile shapes measured at d_model = 1024, n = 8192 (8 + 4 heads of 128):
+        // more waves per SIMD pay as long as each still holds a 64 x 64 or
+        // 32 x 64 block.  dO and dW_o: 128 x 128 with eight waves (115 vs 130 µs
+        // for both with four); dx and dW_in (float32 operand A): 128 x 256 with
+        // sixteen (242 vs 350 µs with 128 x 128 and four).
+        case GEMM_DO: return launch_gemm<OP_KC_RM, false, OP_IC_RM, false, 1, 128, 128, 2, 4, 2>(p, s);
+        case GEMM_DWO: return launch_gemm<OP_IC_RM, false, OP_IC_HM, false, 0, 128, 128, 2, 4, 2>(p, s);
+        case GEMM_DX: return launch_gemm<OP_KC_HM, true, OP_IC_RM, false, 0, 128, 256, 4, 4, 1>(p, s);
+        case GEMM_DWIN: return launch_gemm<OP_IC_HM, true, OP_IC_RM, false, 0, 128, 256, 4, 4, 1>(p, s);
         default: return hipErrorInvalidValue;
     }
 }
