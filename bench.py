@@ -43,8 +43,8 @@ LOCAL_TRAFFIC = {
     "sources": ["content_sparse_attention_unit_amd/csrc/local_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
     "sha256": "fa3ce382f9b13a47f7ef7647bc8c72832b5109eae163db1005f3138d11284aca",
-    "fetch_kib": 12983.39375, "write_kib": 8192.0,
-    "fetch_scale": 262144.0 / 131095.4, "write_scale": 262144.0 / 262144.0,
+    "fetch_kib": 12983.4, "write_kib": 8192.0,
+    "fetch_scale": 262144.0 / 131088.7, "write_scale": 262144.0 / 262144.0,
 }
 
 
