@@ -63,9 +63,11 @@ template <int D, int WMAX, bool SHARED>
 struct AttnCfg {
     static constexpr int DP = D < 32 ? 32 : D;  // dims padded to the MFMA k-depth
     // key/query/value row stride in LDS (bf16): an odd multiple of 16 elements,
-    // so 8 consecutive rows start in disjoint bank groups (DP + 8 for the
-    // largest tile, which would not fit otherwise)
-    static constexpr int LDX = (WMAX == 512) ? DP + 8 : DP + 16;
+    // so 8 consecutive rows start in disjoint bank groups; DP + 8 from 256
+    // rows on, which lets two workgroups share a CU at d = 64, w = 256 (twice
+    // the waves in flight: 72 -> 57 us for the 32K-token stress call) and the
+    // 512-row tile fit at all
+    static constexpr int LDX = (WMAX >= 256) ? DP + 8 : DP + 16;
     static constexpr int NS = DP / 32;          // MFMA k-steps over d
     static constexpr int NJ = D / 16;           // 16-wide output column blocks
     static constexpr int QROWS = SHARED ? 1 : WMAX;
