@@ -42,9 +42,9 @@ LOCAL_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/local_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "fa3ce382f9b13a47f7ef7647bc8c72832b5109eae163db1005f3138d11284aca",
-    "fetch_kib": 12983.4, "write_kib": 8192.0,
-    "fetch_scale": 262144.0 / 131088.7, "write_scale": 262144.0 / 262144.0,
+    "sha256": "a71429ee94422d92ae8c6bcfa6bb4801c987df680c126936fc6521e22ce8c6e8",
+    "fetch_kib": 12983.80625, "write_kib": 8192.0,
+    "fetch_scale": 262144.0 / 131088.9, "write_scale": 262144.0 / 262144.0,
 }
 
 

@@ -10,8 +10,8 @@
 // the positions of its own block and of the `lookback` blocks before it, not
 // later than i; only the band's lower edge differs.
 //
-// local_attn_bf16_kernel: one workgroup = 128 queries in 8 blocks of 16, each
-// block served by two waves (16 waves): key/value tiles of 64 rows are staged
+// local_attn_bf16_kernel: one workgroup = 128 queries in 8 blocks of 16 (64
+// queries in 4 blocks at d <= 64), each block served by two waves: key/value tiles of 64 rows are staged
 // row-major in LDS, and of every tile one wave of a pair takes the first 32
 // keys, the other the last 32.  Each computes S^T = K Q^T and O^T = V^T P^T
 // with v_mfma_f32_16x16x32_bf16 (the transposed value operand read straight
@@ -89,7 +89,11 @@ struct LocalCfg {
     static constexpr int KT = 64;                // keys per tile
     static constexpr int NS = DP / 32;
     static constexpr int NJ = D / 16;
-    static constexpr int NQB = 8;                // 16-query blocks per workgroup
+    // 16-query blocks per workgroup: eight (1024 threads) at d = 128, four at
+    // d <= 64, where a workgroup's 79 VGPRs a lane let 24 waves share a CU in
+    // 512-thread workgroups but only 16 in 1024-thread ones (window 256, 32K
+    // tokens: 72 -> 53 us; at d = 128 four blocks spill and run slower)
+    static constexpr int NQB = D <= 64 ? 4 : 8;
     static constexpr int NWV = 2 * NQB;          // two waves per block (key halves)
     static constexpr int NT = 64 * NWV;
     static constexpr int QT = 16 * NQB;          // queries per workgroup
