@@ -40,7 +40,9 @@ struct BwdCfg {
     static constexpr int NS = DP / 32;
     static constexpr int NJ = D / 16;
     static constexpr int QROWS = SHARED ? 1 : WMAX;
-    static constexpr int NW = WMAX <= 32 ? 2 : (WMAX <= 64 ? 4 : 8);
+    // waves per workgroup; sixteen from 256 rows on, where the LDS tiles allow
+    // one workgroup a CU (d = 64, w = 256: 236 -> 211 us for the 32K-token call)
+    static constexpr int NW = WMAX <= 32 ? 2 : (WMAX <= 64 ? 4 : (WMAX <= 128 ? 8 : 16));
     static constexpr int NT = 64 * NW;
     static constexpr int CPR = DP / 8;           // 16-byte chunks per padded row
     static constexpr int XPT = (WMAX * CPR + NT - 1) / NT;
