@@ -531,7 +531,8 @@ def main():
                     "of known size that scales the FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the layer runs and is measured on one GPU; --gpus must be 1 "
+                                   "(no sharding or collectives are implemented)"}))
         sys.exit(2)
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
