@@ -380,7 +380,7 @@ constexpr int kCandPerWave = 512;
 // TOPB: only the keys' top bytes stay in registers (four to a register, for
 // 64 keys a lane); listed keys are re-read in full from the score row.
 template <int NT, int KPT, bool TOPB>
-__global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scores, int n, int w,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void topw_kernel(const float* __restrict__ scores, int n, int w,
                                                   int32_t* __restrict__ idx, int k,
                                                   uint32_t* __restrict__ mask, int KW) {
     static_assert(NT >= 256 && NT % kWave == 0, "one thread per histogram bin");
@@ -542,9 +542,10 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
     }
 
     uint32_t prefix = bin0 << 24, himask = 0xff000000u;
-    if (!slow) {
-        // 4. Digit passes over the lists (one barrier each).
-        for (int pass = 0; pass < 3; ++pass) {
+    // 4. Digit passes over the lists (one barrier each), from digit pass0 on
+    // (prefix, himask and remaining hold the digits before it), then 5.
+    auto list_path = [&](int pass0) {
+        for (int pass = pass0; pass < 3; ++pass) {
             const int shift = 16 - 8 * pass;
             if (pass > 0) {
                 for (uint32_t i = lane; i < nl; i += kWave) {
@@ -595,6 +596,9 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
             eq_before += (uint32_t)__popcll(eb);
             sel_before += (uint32_t)__popcll(sb);
         }
+    };
+    if (!slow) {
+        list_path(0);
         return;
     }
 
@@ -646,6 +650,36 @@ __global__ __launch_bounds__(NT) void topw_kernel(const float* __restrict__ scor
         prefix |= b << shift;
         himask |= 0xffu << shift;
         remaining = r;
+        if (found && shift == 16) {
+            // The top-byte lists overflowed (a top byte spans a factor of 4 in
+            // score): list the keys at or above the 16-bit prefix instead, one
+            // more pass over the keys, and finish on the lists if they fit.
+            uint32_t cnt = 0u;
+            bool ovf = false;
+            for_keys([&](int j, uint32_t kj) {
+                const bool is = kj >= prefix;
+                const uint64_t mb = __ballot(is);
+                const uint32_t pc = (uint32_t)__popcll(mb);
+                if (cnt + pc <= (uint32_t)CW) {
+                    if (is)
+                        cand[wv][cnt + (uint32_t)lanes_below(mb)] =
+                            make_uint2(kj, (uint32_t)(pl + kWave * j));
+                } else {
+                    ovf = true;
+                }
+                cnt += pc;
+            });
+            if (lane == 0) wcnt[wv] = ovf ? 0xffffffffu : cnt;   // read before the last barrier
+            __syncthreads();
+            bool again = false;
+#pragma unroll
+            for (int v = 0; v < NWV; ++v) again = again || wcnt[v] == 0xffffffffu;
+            if (!again) {
+                nl = cnt;
+                list_path(1);
+                return;
+            }
+        }
     }
     // ... and the members, in position order, from the keys.
     const uint32_t T = prefix, need_eq = remaining;

@@ -294,8 +294,12 @@ def test_sweep_long_rows(rt, orc, n, k):
 # up to n = 16K, LDS up to 32K, 16-bit prefixes in LDS beyond): exact ties
 # (tokens drawn from a pool of 97 vectors), a threshold deep in a crowded top
 # byte (tokens close to one direction: more candidates than the short list
-# holds), and a threshold below the four highest top bytes (w = n/2).
-TOPW_PATHS = {"ties": (97, None), "crowded": (None, 0.01), "median": (None, None)}
+# holds, even at 16-bit prefixes), a top byte too crowded for the short lists
+# whose 16-bit prefixes are not (tokens spread about one direction, a centroid
+# of norm 1.9 along it: scores 1.2 .. 1.5, all in the top byte [0.5, 2)), and a
+# threshold below the four highest top bytes (w = n/2).
+TOPW_PATHS = {"ties": (97, None), "crowded": (None, 0.01), "refine": (None, 1.0),
+              "median": (None, None)}
 
 
 @pytest.mark.parametrize("n", [3000, 20000, 40000, 65536])
@@ -315,6 +319,10 @@ def test_topw_selection_paths(rt, orc, n, kind):
         val = S.normal(1000 * cid + 1, (n, d))
     qk_t = S.rounded(val.reshape(1, H, n, d), "bf16")
     mu_val = S.unit_rows_f32(1000 * cid + 3, H * k, d).reshape(H, k, d)
+    if kind == "refine":
+        unit = centre[0] / np.sqrt((centre[0] ** 2).sum())
+        mu_val = mu_val.copy()
+        mu_val[0, 0] = (1.9 * unit).astype(np.float32).astype(np.float64)
     w = n // 2 if kind == "median" else min(n // k, 1024)
     qk = dev_tensor(qk_t)
     mu = dev_tensor(mu_val)
