@@ -258,7 +258,8 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
                             2 * 2.0 * T * dm * NO),
         "rt_routed_attn_bwd": (lambda: rt.routed_attn_bwd(t["qk"], t["qk"], t["v"], t["idx"], lse,
                                                           do_r, t["inv"], t["inv"], scale=scale,
-                                                          out=(dqh, dkh, dv), ws=ws_b),
+                                                          mask=t["mask"], out=(dqh, dkh, dv),
+                                                          ws=ws_b),
                                10.0 * B * R * k * w * w * d),
         "rt_normalize_bwd": (lambda: rt.normalize_bwd(t["qk"], t["inv"], dqh, dkh, out=dqk), 0.0),
         "rt_local_attn_bwd": (lambda: rt.local_attn_bwd(t["ql"], t["kl"], t["vl"], do_l,
@@ -585,8 +586,8 @@ def main():
                        out=out, lse=lse, ws=ws_attn)
 
     def do_bwd():
-        rt.routed_attn_bwd(qk, qk, v, idx, lse, dout, inv, inv, scale=scale, out=grads,
-                           ws=ws_bwd)
+        rt.routed_attn_bwd(qk, qk, v, idx, lse, dout, inv, inv, scale=scale, mask=mask,
+                           out=grads, ws=ws_bwd)
 
     def do_ema():
         rt.centroid_update_sums_(mu, sum_q, cfg.lam)

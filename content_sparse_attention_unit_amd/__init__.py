@@ -63,8 +63,8 @@ def _load():
         "rt_centroid_update": [P, P, P, P, P, I, P, I, I, I, I, I, I, F, P],
         "rt_in_proj": [P, P, I, I, I, I, I, I, P, P, P, P, P, P],
         "rt_out_proj": [P, P, P, P, I, I, I, I, I, I, P, P],
-        "rt_routed_attn_bwd": [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z,
-                               P],
+        "rt_routed_attn_bwd": [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P,
+                               Z, P],
         "rt_local_attn_bwd": [P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z, P],
         "rt_normalize_bwd": [P, I, P, P, P, ctypes.c_long, I, P, P],
         "rt_out_proj_bwd": [P, P, P, P, I, I, I, I, I, I, P, P, P, P, Z, P],
@@ -268,12 +268,13 @@ def centroid_update_sums_(mu: torch.Tensor, sum_q: torch.Tensor, lam: float,
 
 
 def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=None,
-                    causal=True, out=None, ws=None):
+                    causal=True, mask=None, out=None, ws=None):
     """Gradients (dq_hat, dk_hat, dv), float32, of routed_attn for a fixed
-    membership; ``lse`` comes from the forward call (want_lse=True) and
-    ``out`` may hold three preallocated float32 [B,H,n,d] tensors."""
+    membership; ``lse`` comes from the forward call (want_lse=True), ``mask``
+    may be the membership bitmask route() wrote for ``idx`` and ``out`` may
+    hold three preallocated float32 [B,H,n,d] tensors."""
     lib = _load()
-    dev = _gpu(q, kk, v, idx, lse, dout, q_inv, k_inv)
+    dev = _gpu(q, kk, v, idx, lse, dout, q_inv, k_inv, mask)
     B, H, n, d = q.shape
     k, w = idx.shape[2], idx.shape[3]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -285,7 +286,8 @@ def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=N
         raise TypeError("gradients are float32")
     ws, _ = _workspace("routed_attn_bwd", dev, B, H, n, d, k, w, ws)
     _check(lib.rt_routed_attn_bwd(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
-                                  _ptr(k_inv), _ptr(idx), _ptr(lse), _ptr(dout), B, H, n, d, k, w,
+                                  _ptr(k_inv), _ptr(idx), _ptr(mask), _ptr(lse), _ptr(dout), B, H,
+                                  n, d, k, w,
                                   sc, int(causal), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(dev)))
     return dq, dk, dv

@@ -446,7 +446,7 @@ rt_status rt_centroid_update_sums(float* mu, const float* sum_q, const float* su
 
 rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
                              const float* q_inv, const float* k_inv, const int32_t* idx,
-                             const float* lse, const void* dout, int B, int H, int n, int d, int k,
+                             const uint32_t* member_mask, const float* lse, const void* dout, int B, int H, int n, int d, int k,
                              int w, float scale, int causal, float* dq_hat, float* dk_hat,
                              float* dv, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_routed_attn_bwd";
@@ -480,7 +480,8 @@ rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int d
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
-    hipError_t e = rt::launch_cluster_attn_bwd(q, kk, v, dtype, q_inv, k_inv, idx, lse, dout,
+    hipError_t e = rt::launch_cluster_attn_bwd(q, kk, v, dtype, q_inv, k_inv, idx, member_mask,
+                                               lse, dout,
                                                B * H, n, d, k, w, scale, causal, dq_hat, dk_hat,
                                                dv, ws,
                                                static_cast<hipStream_t>(stream));

@@ -476,11 +476,12 @@ size_t bwd_workspace_bytes(int BH, int n, int d, int k, int w) {
 
 hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
                                    const float* q_inv, const float* k_inv, const int32_t* idx,
-                                   const float* lse, const void* dout, int BH, int n, int d,
+                                   const uint32_t* member_mask, const float* lse,
+                                   const void* dout, int BH, int n, int d,
                                    int k, int w, float scale, int causal, float* dq, float* dk,
                                    float* dv, void* ws, hipStream_t s) {
     char* base = static_cast<char*>(ws);
-    uint32_t* mask = reinterpret_cast<uint32_t*>(base);
+    uint32_t* mask_ws = reinterpret_cast<uint32_t*>(base);
     base += bwd_mask_bytes(BH, n, k);
     int32_t* dir = reinterpret_cast<int32_t*>(base);
     base += bwd_dir_bytes(BH, n, k);
@@ -491,8 +492,12 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
         part[j][1] = reinterpret_cast<float*>(base);
         base += bwd_ovf_bytes(BH, d, k, w);
     }
-    hipError_t e = launch_mask(idx, BH, n, k, w, mask, s);
-    if (e != hipSuccess) return e;
+    const uint32_t* mask = member_mask;   // the memberships rt_route produced, or built here
+    if (mask == nullptr) {
+        hipError_t e = launch_mask(idx, BH, n, k, w, mask_ws, s);
+        if (e != hipSuccess) return e;
+        mask = mask_ws;
+    }
     const BwdOut out{dq, dk, dv, part[0][0], part[1][0], part[2][0],
                      part[0][1], part[1][1], part[2][1], dir};
     const BwdArgs a{q, kk, v, q_inv, k_inv, idx, lse, dout, mask, BH, n, k, w, mask_words(k),
@@ -503,7 +508,7 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
         case 64: bwd_launch_d<64>(a, dtype, s); break;
         default: bwd_launch_d<128>(a, dtype, s); break;
     }
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     float* const grads[3] = {dq, dk, dv};
     const float* const sl[3] = {part[0][0], part[1][0], part[2][0]};

@@ -102,7 +102,8 @@ hipError_t launch_local_attn(const void* q, const void* kk, const void* v, int d
 
 hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v, int dtype,
                                    const float* q_inv, const float* k_inv, const int32_t* idx,
-                                   const float* lse, const void* dout, int BH, int n, int d,
+                                   const uint32_t* member_mask, const float* lse,
+                                   const void* dout, int BH, int n, int d,
                                    int k, int w, float scale, int causal, float* dq, float* dk,
                                    float* dv, void* ws, hipStream_t s);
 

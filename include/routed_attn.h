@@ -254,6 +254,9 @@ rt_status rt_centroid_update_sums(float *mu, const float *sum_q, const float *su
  *                   summed over clusters).  With shared QK the gradient of
  *                   the shared normalised vector is dq_hat + dk_hat.
  *   dv              out [B][H][n][d] float32.
+ *   member_mask     [B][H][n][ceil(k/32)] uint32 or NULL, as for rt_routed_attn:
+ *                   the membership bits rt_route wrote for this idx (saves
+ *                   building them again); NULL builds them from idx in ws.
  *   The three gradients are float32, distinct, and alias no input.  Tokens
  *   held by no cluster get zero rows.  Other arguments as for rt_routed_attn.
  *   ws: rt_workspace_bytes(RT_OP_ROUTED_ATTN_BWD, ...) bytes (membership bits
@@ -262,7 +265,7 @@ rt_status rt_centroid_update_sums(float *mu, const float *sum_q, const float *su
  */
 rt_status rt_routed_attn_bwd(const void *q, const void *kk, const void *v, int dtype,
                              const float *q_inv, const float *k_inv, const int32_t *idx,
-                             const float *lse, const void *dout, int B, int H, int n, int d, int k,
+                             const uint32_t *member_mask, const float *lse, const void *dout, int B, int H, int n, int d, int k,
                              int w, float scale, int causal, float *dq_hat, float *dk_hat,
                              float *dv, void *ws, size_t ws_bytes, void *stream);
 

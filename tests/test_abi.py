@@ -179,12 +179,12 @@ def test_binding_rejects_cpu_tensors():
         rt.local_attn(x, x, x, 8)
 
 
-def bwd(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE,
+def bwd(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE, mask=None,
         lse=ctypes.c_void_p(0x4000), dout=ctypes.c_void_p(0x5000), B=1, H=1, n=64, d=16, k=4,
         w=16, scale=0.25, causal=1, dq=ctypes.c_void_p(0x6000), dk=ctypes.c_void_p(0x7000),
         dv=ctypes.c_void_p(0x8000), ws=None, ws_bytes=0):
-    return lib.rt_routed_attn_bwd(q, kk, v, dtype, q_inv, k_inv, idx, lse, dout, B, H, n, d, k, w,
-                                  scale, causal, dq, dk, dv, ws, ws_bytes, None)
+    return lib.rt_routed_attn_bwd(q, kk, v, dtype, q_inv, k_inv, idx, mask, lse, dout, B, H, n,
+                                  d, k, w, scale, causal, dq, dk, dv, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [

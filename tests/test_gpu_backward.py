@@ -102,11 +102,18 @@ def run_bwd_case(rt, orc, cfg, causal=True, scale=None, distinct=False, heads=No
     _, lse = rt.routed_attn(q, kk, v, idx, q_inv, k_inv, scale=sc, causal=causal, want_lse=True,
                             out_dtype=torch.float32)
     dq, dk, dv = rt.routed_attn_bwd(q, kk, v, idx, lse, g, q_inv, k_inv, scale=sc, causal=causal)
+    # again, with the membership bits given (built here from idx, as rt_route
+    # writes them) instead of built by the call: the same gradients, bit for bit
+    B_, H_, k_, w_ = idx_o.shape
+    bits = np.zeros((B_, H_, cfg.n, (k_ + 31) // 32), dtype=np.uint32)
+    bb, hh, cc, _ = np.indices(idx_o.shape)
+    np.bitwise_or.at(bits, (bb, hh, idx_o, cc // 32), (np.uint32(1) << (cc % 32).astype(np.uint32)))
+    mask = torch.from_numpy(bits.view(np.int32)).cuda()
     dq2, dk2, dv2 = rt.routed_attn_bwd(q, kk, v, idx, lse, g, q_inv, k_inv, scale=sc,
-                                       causal=causal)
+                                       causal=causal, mask=mask)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), \
-        "backward is not deterministic"
+        "backward is not deterministic, or differs with the membership bits given"
     hs = range(cfg.R) if heads is None else heads
     for h in hs:
         sl = (slice(None), slice(h, h + 1))
