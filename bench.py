@@ -43,8 +43,8 @@ LOCAL_TRAFFIC = {
     "sources": ["content_sparse_attention_unit_amd/csrc/local_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
     "sha256": "a71429ee94422d92ae8c6bcfa6bb4801c987df680c126936fc6521e22ce8c6e8",
-    "fetch_kib": 12983.4, "write_kib": 8192.0,
-    "fetch_scale": 262144.0 / 131088.5, "write_scale": 262144.0 / 262144.0,
+    "fetch_kib": 12983.375, "write_kib": 8192.0,
+    "fetch_scale": 262144.0 / 131088.8, "write_scale": 262144.0 / 262144.0,
 }
 
 
