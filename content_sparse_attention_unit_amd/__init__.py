@@ -137,6 +137,45 @@ def _gpu(*ts):
     return dev
 
 
+def _expect(t, shape, dtype, what):
+    """Raise ValueError unless ``t`` (if given) has this shape and dtype: the
+    kernels index these buffers by the shape arguments alone."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{what} has dtype {t.dtype}, expected {dtype}")
+
+
+def _check_routed(q, kk, v, idx, q_inv, k_inv, mask=None, lse=None, dout=None, sums=(None, None),
+                  mu=None):
+    """Metadata checks shared by the routed-attention calls: q, kk, v [B,H,n,d]
+    of one dtype, idx int32 [B,H,k,w], inverse norms float32 [B,H,n], the
+    membership bitmask int32 [B,H,n,ceil(k/32)] (it must be the one route()
+    wrote for this idx), lse float32 [B,H,k,w], dout like q, member sums
+    float32 [B,H,k,d], mu float32 [H,k,d]."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, n, d]")
+    B, H, n, d = q.shape
+    if idx.dim() != 4 or tuple(idx.shape[:2]) != (B, H):
+        raise ValueError(f"idx has shape {tuple(idx.shape)}, expected ({B}, {H}, k, w)")
+    if idx.dtype != torch.int32:
+        raise TypeError("idx must be int32")
+    k, w = idx.shape[2], idx.shape[3]
+    _expect(kk, q.shape, q.dtype, "kk")
+    _expect(v, q.shape, q.dtype, "v")
+    _expect(q_inv, (B, H, n), torch.float32, "q_inv")
+    _expect(k_inv, (B, H, n), torch.float32, "k_inv")
+    _expect(mask, (B, H, n, mask_words(k)), torch.int32, "mask")
+    _expect(lse, (B, H, k, w), torch.float32, "lse")
+    _expect(dout, q.shape, q.dtype, "dout")
+    for i, t in enumerate(sums):
+        _expect(t, (B, H, k, d), torch.float32, f"sums[{i}]")
+    _expect(mu, (H, k, d), torch.float32, "mu")
+    return B, H, n, d, k, w
+
+
 def workspace_bytes(op: str, B: int, H: int, n: int, d: int, k: int, w: int) -> int:
     return int(_load().rt_workspace_bytes(RT_OP[op], B, H, n, d, k, w))
 
@@ -207,14 +246,13 @@ def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.T
     [B,H,k,d] tensors (either may be None) to receive per-cluster member sums."""
     lib = _load()
     sum_q, sum_k = sums if sums is not None else (None, None)
-    dev = _gpu(q, kk, v, idx, q_inv, k_inv, mask, sum_q, sum_k)
-    B, H, n, d = q.shape
-    k, w = idx.shape[2], idx.shape[3]
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
+    dev = _gpu(q, kk, v, idx, q_inv, k_inv, mask, sum_q, sum_k, out, lse)
+    B, H, n, d, k, w = _check_routed(q, kk, v, idx, q_inv, k_inv, mask=mask, lse=lse,
+                                     sums=(sum_q, sum_k))
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    _shape(out, q.shape, "out")
     if want_lse and lse is None:
         lse = torch.empty((B, H, k, w), dtype=torch.float32, device=dev)
     ws, _ = _workspace("routed_attn", dev, B, H, n, d, k, w, ws)
@@ -275,8 +313,9 @@ def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=N
     hold three preallocated float32 [B,H,n,d] tensors."""
     lib = _load()
     dev = _gpu(q, kk, v, idx, lse, dout, q_inv, k_inv, mask)
-    B, H, n, d = q.shape
-    k, w = idx.shape[2], idx.shape[3]
+    if lse is None or dout is None:
+        raise ValueError("routed_attn_bwd needs the forward's lse and dout")
+    B, H, n, d, k, w = _check_routed(q, kk, v, idx, q_inv, k_inv, mask=mask, lse=lse, dout=dout)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
@@ -284,6 +323,8 @@ def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=N
     _gpu(dq, dk, dv)
     if any(t.dtype != torch.float32 for t in out):
         raise TypeError("gradients are float32")
+    for name, t in zip(("dq", "dk", "dv"), out):
+        _shape(t, q.shape, name)
     ws, _ = _workspace("routed_attn_bwd", dev, B, H, n, d, k, w, ws)
     _check(lib.rt_routed_attn_bwd(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
                                   _ptr(k_inv), _ptr(idx), _ptr(mask), _ptr(lse), _ptr(dout), B, H,
@@ -480,16 +521,14 @@ def routed_attn_update_(q, kk, v, idx, q_inv, k_inv, mu, lam: float, *, scale=No
     (mu updated in place, in the output's scatter launch).  Returns out (and
     lse when asked)."""
     lib = _load()
-    dev = _gpu(q, kk, v, idx, q_inv, k_inv, mask, mu)
-    B, H, n, d = q.shape
-    k, w = idx.shape[2], idx.shape[3]
-    if idx.dtype != torch.int32:
-        raise TypeError("idx must be int32")
-    if mu.dtype != torch.float32 or tuple(mu.shape) != (H, k, d):
+    dev = _gpu(q, kk, v, idx, q_inv, k_inv, mask, mu, out, lse)
+    if mu is None:
         raise ValueError("mu must be float32 [H, k, d]")
+    B, H, n, d, k, w = _check_routed(q, kk, v, idx, q_inv, k_inv, mask=mask, lse=lse, mu=mu)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    _shape(out, q.shape, "out")
     if want_lse and lse is None:
         lse = torch.empty((B, H, k, w), dtype=torch.float32, device=dev)
     ws, _ = _workspace("routed_attn_update", dev, B, H, n, d, k, w, ws)
@@ -509,11 +548,10 @@ def routed_attn_split(q, kk, v, idx_q, idx_k, q_inv=None, k_inv=None, *, scale=N
     lse and (sum_q, sum_k) when asked."""
     lib = _load()
     dev = _gpu(q, kk, v, idx_q, idx_k, q_inv, k_inv, q_mask)
-    B, H, n, d = q.shape
-    k, w = idx_q.shape[2], idx_q.shape[3]
+    B, H, n, d, k, w = _check_routed(q, kk, v, idx_q, q_inv, k_inv, mask=q_mask)
     if tuple(idx_k.shape) != tuple(idx_q.shape):
         raise ValueError("idx_q and idx_k must have the same shape")
-    if idx_q.dtype != torch.int32 or idx_k.dtype != torch.int32:
+    if idx_k.dtype != torch.int32:
         raise TypeError("idx_q and idx_k must be int32")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:

@@ -119,7 +119,10 @@ rt_status rt_route(const void *qk, int dtype, const float *mu, int B, int H, int
  *              results; out-of-range values are clamped, never dereferenced).
  *   member_mask   optional [B][H][n][ceil(k/32)] uint32 membership bits
  *              consistent with idx (as rt_route emits them); NULL: built from
- *              idx in the workspace.
+ *              idx in the workspace.  The bits decide how many rows each
+ *              token gets: bits that are not those of this idx give wrong
+ *              outputs, and a smaller buffer is read out of bounds (the
+ *              library sees only the pointer).
  *   causal     1: member s is visible to member r iff pos(s) <= pos(r);
  *              0: every member sees every member.
  *   out        out [B][H][n][d] of element type out_dtype (RT_F32 or RT_BF16,

@@ -534,9 +534,14 @@ def decode_cache_from_prefill(qk, v, idx, cap: int):
     return {"k": ck, "inv": cinv, "v": cv, "pos": cpos, "len": clen}
 
 
-def decode_step(cache: dict, qk_t, v_t, t: int, mu, scale: float):
+def decode_step(cache: dict, qk_t, v_t, t: int, mu, scale: float, label_given=None):
     """One routed decode step for the token at position t (qk_t, v_t [B, H, d]):
-    returns (out [B, H, d], label [B, H], the updated cache (a copy))."""
+    returns (out [B, H, d], label [B, H], the updated cache (a copy)).
+
+    ``label_given`` [B, H] (optional): the cluster each (batch, head) joins,
+    in place of its own nearest centroid.  Where two centroids are equally
+    near within rounding either is a valid choice; a caller that saw the
+    other choice taken passes it here so that the caches stay comparable."""
     qk_t, v_t, mu = _f64(qk_t), _f64(v_t), _f64(mu)
     B, H, d = qk_t.shape
     cache = {name: arr.copy() for name, arr in cache.items()}
@@ -549,6 +554,8 @@ def decode_step(cache: dict, qk_t, v_t, t: int, mu, scale: float):
             inv = 1.0 / max(np.sqrt((x * x).sum()), 1e-12)
             s = mu[h] @ (x * inv)
             c = int(np.argmax(s))                      # first maximum: ties to the lower index
+            if label_given is not None:
+                c = int(label_given[b, h])
             label[b, h] = c
             j = int(cache["len"][b, h, c])
             assert j < cap, "cluster cache full"

@@ -234,3 +234,37 @@ STACKS = {
     # w = 128, window 512) at model width 1024, 22 layers
     "long_stack": StackConfig(4, "long_stack", 1, 8192, 1024, 128, 8, 4, 64, 128, 512, 22),
 }
+
+
+def separated_tokens(seed: int, B: int, H: int, n: int, d: int, k: int, dtype: str = "bf16",
+                     spacing: float = 1.5e-3):
+    """Tokens gathered around k random unit centres, for inputs whose
+    nearest-centre assignment and within-group order hold no near-equal
+    values.  Returns (tokens [B,H,n,d] as a Tensor, centres [H,k,d] float32
+    values).
+
+    Each token draws its group c with probability proportional to a weight in
+    [0.7, 1.3] per (head, group), so groups are unequal in size.  The j-th
+    token of a group (in a seeded random order) is 2 * (cos(a) m_c + sin(a) u),
+    with cos(a) = 0.995 - spacing * j and u a random unit vector orthogonal to
+    the centre m_c, so the cosines inside a group are `spacing` apart."""
+    mu = unit_rows_f32(seed, H * k, d).reshape(H, k, d)
+    weight = 0.7 + 0.6 * uniform01(seed + 1, H * k).reshape(H, k)
+    u_lab = uniform01(seed + 2, B * H * n).reshape(B, H, n)
+    order_keys = splitmix64(seed + 3, B * H * n).reshape(B, H, n)
+    g = normal(seed + 4, (B, H, n, d))
+    x = np.empty((B, H, n, d))
+    for b in range(B):
+        for h in range(H):
+            cdf = np.cumsum(weight[h]) / weight[h].sum()
+            lab = np.minimum(np.searchsorted(cdf, u_lab[b, h], side="left"), k - 1)
+            cos_a = np.empty(n)
+            for c in range(k):
+                sel = np.flatnonzero(lab == c)
+                rank = np.argsort(np.argsort(order_keys[b, h, sel], kind="stable"), kind="stable")
+                cos_a[sel] = 0.995 - spacing * rank
+            m = mu[h, lab]                                        # [n, d]
+            u = g[b, h] - (g[b, h] * m).sum(axis=1, keepdims=True) * m
+            u /= np.sqrt((u * u).sum(axis=1, keepdims=True))
+            x[b, h] = 2.0 * (cos_a[:, None] * m + np.sqrt(1.0 - cos_a[:, None] ** 2) * u)
+    return rounded(x, dtype), mu

@@ -104,3 +104,63 @@ def tokens_touched(idx_a, idx_b, differs, n):
         touched[b, h, idx_a[b, h, c]] = True
         touched[b, h, idx_b[b, h, c]] = True
     return touched
+
+
+def partition_cluster_range(orc, x_bh, mu_h, tie=MARGIN):
+    """Per token of one (batch, head), the range [lo, hi] of partition clusters
+    its place in the order (nearest centroid, descending score, position)
+    allows, given the oracle's float64 scores and that any two keys within
+    ``tie`` of each other may be ordered either way by float32 scores.
+
+    A token's label may be any centroid within ``tie`` of its best one.  Token
+    u certainly precedes t when every label u may take is below every label t
+    may take, or when both have one possible label, the same, and u's score
+    exceeds t's by more than ``tie``; certainly follows likewise.  Then t's
+    rank lies in [#before, n - 1 - #after] and its cluster in that range
+    divided by n/k.  Returns (lo, hi) int arrays [n]."""
+    xh, _ = orc.normalize(x_bh)
+    s = xh @ mu_h.T                                        # [n, k]
+    n, k = s.shape
+    w = n // k
+    top = s.max(axis=1)
+    allowed = s >= top[:, None] - tie
+    lab_lo = np.argmax(allowed, axis=1)
+    lab_hi = k - 1 - np.argmax(allowed[:, ::-1], axis=1)
+    unique = lab_lo == lab_hi
+    best = s[np.arange(n), lab_lo]
+    before = np.searchsorted(np.sort(lab_hi), lab_lo, side="left")
+    after = n - np.searchsorted(np.sort(lab_lo), lab_hi, side="right")
+    for c in range(k):
+        sel = np.flatnonzero(unique & (lab_lo == c))
+        if sel.size == 0:
+            continue
+        bs = np.sort(best[sel])
+        bt = best[sel]
+        before[sel] += bs.size - np.searchsorted(bs, bt + tie, side="right")
+        after[sel] += np.searchsorted(bs, bt - tie, side="left")
+    return before // w, (n - 1 - after) // w
+
+
+def check_partition(orc, got_idx, x_value, mu, tie=MARGIN):
+    """A partition membership [B,H,k,n/k] from the device must hold every token
+    once, list rows by ascending position, and put each token in a cluster its
+    oracle rank allows (partition_cluster_range).  Returns (tokens whose cluster
+    is fixed, tokens with a choice)."""
+    B, H, k, w = got_idx.shape
+    n = k * w
+    pinned = free = 0
+    for b in range(B):
+        for h in range(H):
+            g = got_idx[b, h]
+            np.testing.assert_array_equal(np.sort(g.ravel()), np.arange(n))
+            assert np.all(np.diff(g, axis=1) > 0), "rows not in ascending position"
+            cl = np.empty(n, np.int64)
+            cl[g.ravel()] = np.repeat(np.arange(k), w)
+            lo, hi = partition_cluster_range(orc, x_value[b, h], mu[h], tie)
+            bad = np.flatnonzero((cl < lo) | (cl > hi))
+            assert bad.size == 0, (f"(b={b}, h={h}): {bad.size} tokens in a cluster their rank "
+                                   f"excludes, e.g. token {bad[0]} in {cl[bad[0]]}, allowed "
+                                   f"[{lo[bad[0]]}, {hi[bad[0]]}]")
+            pinned += int((lo == hi).sum())
+            free += int((lo != hi).sum())
+    return pinned, free

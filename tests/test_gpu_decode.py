@@ -6,10 +6,12 @@ prefill, then several local steps.
 Rules.  Cache rows are bf16 copies: bit-exact; inverse norms within 2e-6
 relative.  A step's cluster is a nearest-centroid decision taken from float32
 scores on the device and float64 ones in the oracle: where the oracle's gap
-between the two best centroids is below 1e-5 either choice is valid, and a
-(batch, head) whose choice differs there has diverged caches, so it is not
-compared after that step; elsewhere the labels must be equal.  Outputs:
-float32 within 1e-4, bfloat16 within the bf16 rule.
+between the two best centroids is below 1e-5 either choice is valid, so a
+(batch, head) whose choice differs there must have taken one of the centroids
+within 1e-5 of the best, and the oracle's step is re-run with the device's
+choice, so that its later steps and caches are still compared; elsewhere the
+labels must be equal.  Outputs: float32 within 1e-4, bfloat16 within the
+bf16 rule.
 """
 import math
 import sys
@@ -39,14 +41,13 @@ def say(msg):
     sys.stdout.flush()
 
 
-def label_gap(orc, x, mu):
-    """[B, H] gap between the oracle's two best centroid scores for rows x [B,H,d]."""
+def label_slack(orc, x, mu, label):
+    """[B, H] how far below the best centroid score the centroid `label` scores,
+    for rows x [B,H,d] (the oracle's float64 scores)."""
     xh, _ = orc.normalize(x[:, :, None, :])
     s = np.einsum("bhd,hkd->bhk", xh[:, :, 0], mu)
-    if s.shape[2] == 1:
-        return np.full(s.shape[:2], np.inf)
-    srt = np.sort(s, axis=2)
-    return srt[:, :, -1] - srt[:, :, -2]
+    got = np.take_along_axis(s, label[:, :, None].astype(np.int64), axis=2)[:, :, 0]
+    return s.max(axis=2) - got
 
 
 def compare_cache(got, want, live, what):
@@ -94,31 +95,34 @@ def run_routed(rt, orc, B, H, n, d, k, w, slack, steps, odt, seed):
     torch.cuda.synchronize()
     live = np.ones((B, H), bool)
     compare_cache(cache, want, live, "fill")
-    diverged = 0
+    resynced = 0
     for t in range(n, tot):
         qk_t, v_t = qk_d[:, :, t].contiguous(), v_d[:, :, t].contiguous()
         out, label = rt.decode_routed(cache, qk_t, v_t, t, mu_d, scale=sc, out_dtype=odt)
         torch.cuda.synchronize()
-        wout, wlab, want = orc.decode_step(want, qk.value[:, :, t], v.value[:, :, t], t, mu, sc)
-        gap = label_gap(orc, qk.value[:, :, t], mu)
         glab = host(label)
-        differ = (glab != wlab) & live
-        assert np.all(gap[differ] < TIE), f"step {t}: labels differ away from a near-tie"
-        live &= ~differ
-        diverged += int(differ.sum())
+        prev = want
+        wout, wlab, want = orc.decode_step(prev, qk.value[:, :, t], v.value[:, :, t], t, mu, sc)
+        differ = glab != wlab
+        if differ.any():
+            slack = label_slack(orc, qk.value[:, :, t], mu, glab)
+            assert np.all(slack[differ] < TIE), f"step {t}: labels differ away from a near-tie"
+            # the device's choice is valid: the oracle takes it too and goes on
+            wout, wlab, want = orc.decode_step(prev, qk.value[:, :, t], v.value[:, :, t], t, mu,
+                                               sc, label_given=glab)
+            resynced += int(differ.sum())
         got = host(out)
-        assert_close_out(got[live], wout[live], "f32" if odt == torch.float32 else "bf16",
-                         f"step {t} out")
+        assert_close_out(got, wout, "f32" if odt == torch.float32 else "bf16", f"step {t} out")
     compare_cache(cache, want, live, "after steps")
-    return diverged
+    return resynced
 
 
 @pytest.mark.parametrize("name", list(ROUTED))
 def test_decode_routed(rt, orc, name):
     say(f"[case] decode routed {name}")
     seed = 90_000 + 10 * list(ROUTED).index(name)
-    diverged = run_routed(rt, orc, *ROUTED[name], seed)
-    say(f"[decode routed] {diverged} (batch, head) pairs diverged at a near-tie")
+    resynced = run_routed(rt, orc, *ROUTED[name], seed)
+    say(f"[decode routed] {resynced} steps took the other side of a near-tie (oracle re-synced)")
 
 
 def test_decode_routed_full_size(rt, orc):
@@ -126,9 +130,9 @@ def test_decode_routed_full_size(rt, orc):
     w = 128): prefill caches, then 6 steps."""
     cfg = S.CONFIGS["long"]
     say("[case] decode routed long")
-    diverged = run_routed(rt, orc, cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w, 32, 6,
+    resynced = run_routed(rt, orc, cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w, 32, 6,
                           torch.float32, 90_900)
-    say(f"[decode routed long] {diverged} diverged")
+    say(f"[decode routed long] {resynced} re-synced at a near-tie")
 
 
 def test_decode_routed_full_cluster(rt, orc):

@@ -231,6 +231,36 @@ def test_unrouted_tokens_are_zero_and_deterministic(rt, orc):
         assert torch.equal(out2, res["out"]) and torch.equal(mu3, res["mu_e"])
 
 
+def test_binding_rejects_bad_shapes(rt):
+    """The binding checks every buffer the kernels index by the shape
+    arguments alone before anything is launched."""
+    B, H, n, d, k, w = 1, 2, 128, 64, 8, 16
+    qk = torch.randn((B, H, n, d), device="cuda").to(torch.bfloat16)
+    v = torch.randn_like(qk)
+    mu = torch.nn.functional.normalize(torch.randn((H, k, d), device="cuda"), dim=-1)
+    inv, idx, mask = rt.route(qk, mu, w, want_mask=True)
+    out, lse = rt.routed_attn(qk, qk, v, idx, inv, inv, mask=mask, want_lse=True)
+    bad = {
+        "mask": dict(mask=mask[:, :, : n - 1].contiguous()),
+        "mask dtype": dict(mask=mask.to(torch.int64)),
+        "lse": dict(lse=torch.empty((B, H, k, w - 1), device="cuda")),
+        "q_inv": dict(q_inv=inv[:, :1].contiguous()),
+    }
+    for what, kw in bad.items():
+        args = dict(q_inv=inv, k_inv=inv, mask=mask)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            rt.routed_attn(qk, qk, v, idx, args.pop("q_inv"), args.pop("k_inv"), **args)
+    dout = torch.randn_like(qk)
+    with pytest.raises(ValueError):
+        rt.routed_attn_bwd(qk, qk, v, idx, lse[..., :-1].contiguous(), dout, inv, inv, mask=mask)
+    with pytest.raises(ValueError):
+        rt.routed_attn_bwd(qk, qk, v, idx, lse, dout[:, :1].contiguous(), inv, inv, mask=mask)
+    with pytest.raises(ValueError):
+        rt.routed_attn_update_(qk, qk, v, idx, inv, inv, mu[:, :-1].contiguous(), 0.9, mask=mask)
+    torch.cuda.synchronize()
+
+
 LOCAL = ["ragged_d64", "ragged_d128", "d32", "d16", "w256_d64", "f32_d64", "f32_d128"]
 
 

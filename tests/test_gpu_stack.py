@@ -19,7 +19,8 @@ import pytest
 import torch
 
 import synthetic as S
-from _util import BF16_MEAN_REL, MU_MAX_ABS, dev_tensor, host, tokens_touched
+from _util import (BF16_MEAN_REL, MU_MAX_ABS, check_membership, dev_tensor, host,
+                   tokens_touched)
 
 pytestmark = pytest.mark.gpu
 
@@ -155,7 +156,7 @@ def gpu_layer(rt, x, lw, sc, scale):
     rt.centroid_update_(mu, qk, inv, idx, sc.lam)
     o_l = rt.local_attn(ql, kl, vl, sc.window, scale=scale) if sc.L > 0 else None
     y = rt.out_proj(o_r, o_l, lw["w_o"], x=x)
-    return dict(qk=qk, v=v, q_l=ql, k_l=kl, v_l=vl, idx=idx, mu=mu, y=y)
+    return dict(qk=qk, v=v, q_l=ql, k_l=kl, v_l=vl, idx=idx, mu=mu, o_r=o_r, o_l=o_l, y=y)
 
 
 def check_layer(orc, got, want, sc, x, w_in, tau=1e-3):
@@ -177,6 +178,51 @@ def check_layer(orc, got, want, sc, x, w_in, tau=1e-3):
     same_c = ~(~same).any(axis=0)
     assert np.abs(host(got["mu"])[same_c] - want["mu"][same_c]).max(initial=0.0) <= MU_MAX_ABS
     return int((~same).sum()), float(keep_tok.mean())
+
+
+def assert_rows_close(got, want, what):
+    """Attention outputs: each element within 2e-2 of the largest magnitude in
+    its output row (a row may cancel to near zero where the values it averages
+    are large), and mean-rel 5e-3 over the whole tensor."""
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    scale = np.maximum(1.0, np.abs(want).max(axis=-1, keepdims=True))
+    err = np.abs(got - want)
+    assert np.all(err <= 2e-2 * scale), f"{what}: max scaled err {(err / scale).max():.3e}"
+    assert err.sum() / max(np.abs(want).sum(), 1e-300) <= BF16_MEAN_REL, f"{what}: mean-rel"
+
+
+def check_layer_staged(orc, got, x_in, lw, sc, scale):
+    """One layer at any depth, each stage against the oracle run on the device's
+    own input to that stage (so that no difference carries over from an earlier
+    stage): the five projections within one ulp plus the float32 summation
+    bound; memberships by the margin rule on the device's qk; the routed heads
+    on the device's membership and the local heads, by the row-scaled rule;
+    the centroid update within 1e-5; the layer output, from the device's head
+    outputs and the residual, within one ulp plus the summation bound.  Returns
+    the number of clusters a near-tie let differ."""
+    w_in, w_o, mu0 = lw["w_in"].value, lw["w_o"].value, lw["mu"]
+    want5 = orc.in_proj(x_in, w_in, sc.R, sc.L, sc.d)
+    bounds = in_bounds(orc, x_in, w_in, sc.R, sc.L, sc.d)
+    for nm, w_, b_ in zip(("qk", "v", "q_l", "k_l", "v_l"), want5, bounds):
+        if w_ is not None:
+            assert_bf16_rounding_close(host(got[nm]), w_, f"layer {nm}", b_)
+    qk, v = host(got["qk"]), host(got["v"])
+    _, idx_o, margin_o, _ = orc.route(qk, mu0, sc.w)
+    gidx = host(got["idx"])
+    differs = check_membership(orc, gidx, idx_o, margin_o, qk, mu0, sc.w)
+    o_r, _, _ = orc.routed_attn(qk, qk, v, gidx, scale, True)
+    assert_rows_close(host(got["o_r"]), o_r, "routed heads")
+    mu_o = orc.centroid_update(mu0, qk, qk, gidx, sc.lam)
+    assert np.abs(host(got["mu"]) - mu_o).max() <= MU_MAX_ABS
+    o_l = None
+    if sc.L > 0:
+        o_l = orc.local_attn(host(got["q_l"]), host(got["k_l"]), host(got["v_l"]), sc.window,
+                             scale, True)
+        assert_rows_close(host(got["o_l"]), o_l, "local heads")
+    args_o = (host(got["o_r"]), None if sc.L == 0 else host(got["o_l"]), w_o, x_in)
+    assert_bf16_rounding_close(host(got["y"]), orc.out_proj(*args_o), "layer output",
+                               out_bound(orc, *args_o))
+    return int(differs.sum())
 
 
 SMALL_STACK = S.StackConfig(62, "small_stack", 1, 512, 256, 64, 2, 2, 8, 64, 64, 2)
@@ -213,19 +259,37 @@ def test_layer_full_size(rt, orc):
     assert kept > 0.5
 
 
-def test_stack_22_layers_deterministic(rt):
-    """The 22-layer long stack runs end to end, stays finite, and repeats
-    bit-identically."""
+SAMPLED_LAYERS = (1, 11, 21)
+
+
+def test_stack_22_layers(rt, orc):
+    """The 22-layer long stack runs end to end, stays finite and repeats
+    bit-identically; layers 1, 11 and 21 are each checked stage by stage
+    against the oracle on the device's own inputs (the residual stream grows
+    with depth, so the layer output can cancel to far below its terms: it is
+    held to the rounding rule of its own product instead of a relative
+    tolerance)."""
     sc = S.STACKS["long_stack"]
     scale = 1.0 / math.sqrt(sc.d)
-    layers = [{k_: dev_tensor(v_) for k_, v_ in S.stack_layer(sc, l).items()}
-              for l in range(sc.layers)]
+    host_layers = [S.stack_layer(sc, l) for l in range(sc.layers)]
+    layers = [{k_: dev_tensor(v_) for k_, v_ in hl.items()} for hl in host_layers]
     outs = []
-    for _ in range(2):
+    sampled = {}
+    for rep in range(2):
         x = dev_tensor(S.stack_x(sc))
         for l in range(sc.layers):
-            x = gpu_layer(rt, x, layers[l], sc, scale)["y"]
+            if rep == 0 and l in SAMPLED_LAYERS:
+                x_in = host(x)
+            res = gpu_layer(rt, x, layers[l], sc, scale)
+            if rep == 0 and l in SAMPLED_LAYERS:
+                torch.cuda.synchronize()
+                sampled[l] = (x_in, {k_: v_.clone() for k_, v_ in res.items()})
+            x = res["y"]
         torch.cuda.synchronize()
         outs.append(x)
     assert torch.isfinite(outs[0].float()).all()
     assert torch.equal(outs[0], outs[1])
+    for l, (x_in, got) in sampled.items():
+        ndiff = check_layer_staged(orc, got, x_in, host_layers[l], sc, scale)
+        say(f"[stack layer {l}] every stage matches the oracle on its own input; "
+            f"{ndiff} clusters differ at a near-tie; max |x| {np.abs(x_in).max():.3g}")

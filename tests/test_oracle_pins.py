@@ -780,6 +780,33 @@ def test_decode_ties_to_lower_centroid(orc):
     np.testing.assert_allclose(out[0, 0], want, atol=1e-12)
 
 
+def test_decode_given_label_joins_that_cluster(orc):
+    """With the two equal centroids above, the step told to take the upper one
+    appends to that cluster's cache and attends to its members instead; told
+    its own choice, it changes nothing."""
+    B, H, d = 1, 1, 3
+    mu = np.array([[[0.0, 0.0, 1.0], [1.0, 0.0, 0.0], [1.0, 0.0, 0.0]]])
+    x = np.array([[[[0.0, 0.0, 2.0], [3.0, 0.5, 0.0], [0.1, 0.0, 4.0], [2.0, -0.5, 0.0]]]])
+    v = np.arange(12, dtype=float).reshape(B, H, 4, d)
+    idx = np.array([[[[0], [1], [2]]]], dtype=np.int32)
+    cache = orc.decode_cache_from_prefill(x[:, :, :3], v[:, :, :3], idx, 4)
+    out1, lab1, c1 = orc.decode_step(cache, x[:, :, 3], v[:, :, 3], 3, mu, 1.0)
+    out2, lab2, c2 = orc.decode_step(cache, x[:, :, 3], v[:, :, 3], 3, mu, 1.0,
+                                     label_given=np.array([[1]]))
+    assert lab1[0, 0] == 1 and lab2[0, 0] == 1
+    np.testing.assert_array_equal(out1, out2)
+    for name in c1:
+        np.testing.assert_array_equal(c1[name], c2[name])
+    out3, lab3, c3 = orc.decode_step(cache, x[:, :, 3], v[:, :, 3], 3, mu, 1.0,
+                                     label_given=np.array([[2]]))
+    assert lab3[0, 0] == 2
+    np.testing.assert_array_equal(c3["len"][0, 0], [1, 1, 2])
+    assert c3["pos"][0, 0, 2, 1] == 3
+    q = _unit(x[0, 0, [2, 3]])
+    want = _sdpa(q[None, None], q[None, None], v[0, 0, [2, 3]][None, None], 1.0, True)[0, 0, -1]
+    np.testing.assert_allclose(out3[0, 0], want, atol=1e-12)
+
+
 # ---- separately routed queries and keys ---------------------------------------------------
 
 def test_split_with_one_membership_is_noncausal_routed_attention(orc):
