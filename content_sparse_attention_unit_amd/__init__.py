@@ -15,7 +15,7 @@ import os
 
 import torch
 
-__all__ = ["route", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
+__all__ = ["route", "route_noalloc", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
            "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
            "out_proj_bwd", "in_proj_bwd", "local_attn_blocked", "centroid_update_argmax_",
            "route_partition", "routed_attn_split", "routed_attn_update_", "attn_js", "decode_cache", "decode_fill", "decode_routed",
@@ -56,6 +56,7 @@ def _load():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     sig = {
         "rt_route": [P, I, P, I, I, I, I, I, I, P, P, P, P, P, P, Z, P],
+        "rt_route_noalloc": [P, I, P, I, I, I, I, I, I, P, P, P, P, P],
         "rt_routed_attn": [P, P, P, I, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P, P, P, Z,
                            P],
         "rt_centroid_update_sums": [P, P, P, I, I, I, I, F, P],
@@ -232,6 +233,30 @@ def route(qk: torch.Tensor, mu: torch.Tensor, w: int, *, want_scores: bool = Fal
     if want_qk_hat:
         res.append(qk_hat)
     return tuple(res)
+
+
+ROUTE_NOALLOC_MAX_SCORES = 16 * 1024 * 1024
+
+
+def route_noalloc(qk: torch.Tensor, mu: torch.Tensor, w: int, out, *, qk_hat=None):
+    """route() through rt_route_noalloc: no workspace, the scores live in the
+    library's static per-GPU array (B*H*k*n <= ROUTE_NOALLOC_MAX_SCORES).
+    ``out`` = (inv_norm, idx) or (inv_norm, idx, mask), preallocated by the
+    caller (this function allocates nothing); returns ``out``."""
+    lib = _load()
+    inv, idx = out[0], out[1]
+    mask = out[2] if len(out) > 2 else None
+    dev = _gpu(qk, mu, inv, idx, mask, qk_hat)
+    B, H, n, d = qk.shape
+    k = mu.shape[1]
+    _expect(mu, (H, k, d), torch.float32, "mu")
+    _expect(inv, (B, H, n), torch.float32, "inv_norm")
+    _expect(idx, (B, H, k, w), torch.int32, "idx")
+    _expect(mask, (B, H, n, mask_words(k)), torch.int32, "mask")
+    _expect(qk_hat, qk.shape, qk.dtype, "qk_hat")
+    _check(lib.rt_route_noalloc(_ptr(qk), _dtype_code(qk), _ptr(mu), B, H, n, d, k, w, _ptr(inv),
+                                _ptr(idx), _ptr(mask), _ptr(qk_hat), _stream(dev)))
+    return out
 
 
 def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "routed_attn.h"
 #include "rt_internal.hpp"
@@ -164,10 +165,12 @@ size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
     }
 }
 
-rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int n, int d, int k,
-                   int w, float* inv_norm, int32_t* idx, uint32_t* member_mask, void* qk_hat,
-                   float* scores, void* ws, size_t ws_bytes, void* stream) {
-    static const char* fn = "rt_route";
+}  // extern "C"
+
+namespace {
+
+rt_status check_route(const char* fn, const void* qk, int dtype, const float* mu, int B, int H,
+                      int n, int d, int k, int w, const float* inv_norm, const int32_t* idx) {
     g_err[0] = 0;
     if (!qk || !mu || !inv_norm || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
@@ -178,6 +181,58 @@ rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int
         return fail(RT_EUNSUPPORTED, "%s: n=%d exceeds %d", fn, n, rt::kMaxSeqTopw);
     if ((long long)B * H * k > 0x7fffffffLL)
         return fail(RT_EUNSUPPORTED, "%s: B*H*k too large", fn);
+    return RT_OK;
+}
+
+// The score matrix of rt_route_noalloc: one copy per GPU the library runs on,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the address from
+// hipGetSymbolAddress (scratch_on_current_device) and never this name.
+constexpr size_t kNoallocScores = (size_t)RT_ROUTE_NOALLOC_MAX_SCORES;
+static __device__ __align__(256) float scratch[kNoallocScores];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr with g_err set on failure.
+float* scratch_on_current_device(const char* fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        fail(RT_EHIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        fail(RT_EUNSUPPORTED, "%s: device %d beyond the %d this library tracks", fn, dev,
+             kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            fail(RT_EHIP, "%s: hipGetSymbolAddress(scratch) failed: %s", fn,
+                 hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<float*>(ptr);
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int n, int d, int k,
+                   int w, float* inv_norm, int32_t* idx, uint32_t* member_mask, void* qk_hat,
+                   float* scores, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_route";
+    rt_status st = check_route(fn, qk, dtype, mu, B, H, n, d, k, w, inv_norm, idx);
+    if (st != RT_OK) return st;
     float* sc = scores;
     if (sc == nullptr) {
         const size_t need = route_ws(B, H, n, k);
@@ -187,6 +242,29 @@ rt_status rt_route(const void* qk, int dtype, const float* mu, int B, int H, int
         sc = static_cast<float*>(ws);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e =
+        rt::launch_score(qk, dtype, mu, B, H, n, d, k, inv_norm, sc, qk_hat, member_mask, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    e = rt::launch_topw(sc, B * H, n, k, w, idx, member_mask, s);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
+}
+
+rt_status rt_route_noalloc(const void* qk, int dtype, const float* mu, int B, int H, int n, int d,
+                           int k, int w, float* inv_norm, int32_t* idx, uint32_t* member_mask,
+                           void* qk_hat, void* stream) {
+    static const char* fn = "rt_route_noalloc";
+    rt_status st = check_route(fn, qk, dtype, mu, B, H, n, d, k, w, inv_norm, idx);
+    if (st != RT_OK) return st;
+    const size_t nscores = (size_t)B * H * k * n;
+    if (nscores > kNoallocScores)
+        return fail(RT_EUNSUPPORTED, "%s: B*H*k*n=%zu scores exceed the static scratch of %zu",
+                    fn, nscores, kNoallocScores);
+    float* sc = scratch_on_current_device(fn);
+    if (sc == nullptr) return RT_EHIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // every score the selection reads is written first by the scoring kernel,
+    // so the array needs no clearing between calls
     hipError_t e =
         rt::launch_score(qk, dtype, mu, B, H, n, d, k, inv_norm, sc, qk_hat, member_mask, s);
     if (e != hipSuccess) return hip_fail(fn, e);

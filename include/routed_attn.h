@@ -104,6 +104,25 @@ rt_status rt_route(const void *qk, int dtype, const float *mu, int B, int H, int
                    float *scores, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * rt_route_noalloc -- rt_route without a workspace, for callers that cannot
+ *   allocate device memory: code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid allocation.  Same kernels and results as rt_route
+ *   (bit for bit); the scores live in a static device array of
+ *   RT_ROUTE_NOALLOC_MAX_SCORES float32 (64 MiB) that the library holds on
+ *   every GPU it runs on until the process ends.  The array's address is looked
+ *   up on the first call on each device; the stream must belong to the current
+ *   device.
+ *   Arguments as rt_route (no scores output, no workspace).
+ *   B*H*k*n above RT_ROUTE_NOALLOC_MAX_SCORES: RT_EUNSUPPORTED, nothing
+ *   launched.  Calls that overlap on one GPU (other streams, other threads)
+ *   share the array and race: serialise them.  No allocation of any kind.
+ */
+#define RT_ROUTE_NOALLOC_MAX_SCORES (16 * 1024 * 1024)
+rt_status rt_route_noalloc(const void *qk, int dtype, const float *mu, int B, int H, int n, int d,
+                           int k, int w, float *inv_norm, int32_t *idx, uint32_t *member_mask,
+                           void *qk_hat, void *stream);
+
+/*
  * rt_routed_attn -- attention inside each cluster, scatter-added back.
  *   Summary §3: softmax-normalised attention over the permitted keys, the
  *   output is the weighted sum of values, and an autoregressive query sees no

@@ -69,6 +69,33 @@ def test_route_validation(lib, kw, code, msg):
     assert msg in _last(lib)
 
 
+def route_noalloc(lib, qk=FAKE, dtype=1, mu=FAKE, B=1, H=1, n=64, d=16, k=4, w=16, inv=FAKE,
+                  idx=FAKE):
+    return lib.rt_route_noalloc(qk, dtype, mu, B, H, n, d, k, w, inv, idx, None, None, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(qk=None), RT_EINVAL, "null"),
+    (dict(idx=None), RT_EINVAL, "null"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(d=48), RT_EUNSUPPORTED, "d=48"),
+    (dict(B=1, H=8, n=32768, k=128, w=256), RT_EUNSUPPORTED, "static scratch"),
+    (dict(B=2, H=1, n=65536, k=129, w=16), RT_EUNSUPPORTED, "static scratch"),
+])
+def test_route_noalloc_validation(lib, kw, code, msg):
+    """Checked on the host before the scratch array is looked up or anything
+    is launched; the limit is RT_ROUTE_NOALLOC_MAX_SCORES scores."""
+    assert route_noalloc(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_route_noalloc_limit_matches_header():
+    import content_sparse_attention_unit_amd as rt
+    text = open(HEADER).read()
+    m = re.search(r"#define RT_ROUTE_NOALLOC_MAX_SCORES \((\d+) \* (\d+) \* (\d+)\)", text)
+    assert m and int(m[1]) * int(m[2]) * int(m[3]) == rt.ROUTE_NOALLOC_MAX_SCORES
+
+
 def attn(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE, B=1, H=1,
          n=64, d=16, k=4, w=16, scale=0.25, causal=1, out=ctypes.c_void_p(0x2000), out_dtype=1,
          lse=None, ws=FAKE, ws_bytes=0):
