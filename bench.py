@@ -34,17 +34,17 @@ import synthetic as S  # noqa: E402
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 
-# HBM traffic of the local-window attention kernel at the long workload, from two rocprofv3
+# HBM traffic of the in-cluster attention kernel at the long workload, from two rocprofv3
 # --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the same counter's
 # reading for a plain 256 MiB device copy in the same run (--copy-calibration 256).  Valid only
 # for the kernel sources with this digest: after any change the bench reports traffic null.
-LOCAL_TRAFFIC = {
+CLUSTER_TRAFFIC = {
     "workload": "long",
-    "sources": ["content_sparse_attention_unit_amd/csrc/local_attn.hip",
+    "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "a71429ee94422d92ae8c6bcfa6bb4801c987df680c126936fc6521e22ce8c6e8",
-    "fetch_kib": 12983.375, "write_kib": 8192.0,
-    "fetch_scale": 262144.0 / 131088.8, "write_scale": 262144.0 / 262144.0,
+    "sha256": "",
+    "fetch_kib": 0.0, "write_kib": 0.0,
+    "fetch_scale": 1.0, "write_scale": 1.0,
 }
 
 
@@ -52,7 +52,7 @@ def measured_traffic(rec, workload):
     """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch, or None when the kernel's
     sources have changed since the counters were taken (or the workload differs)."""
     import hashlib
-    if workload != rec["workload"]:
+    if workload != rec["workload"] or not rec["sha256"]:
         return None
     h = hashlib.sha256()
     for f in rec["sources"]:
@@ -99,39 +99,68 @@ def algorithmic(cfg):
     # five w x w x d products per cluster (S, dP, dV, dQ, dK)
     bwd_bytes = 3 * tok + 2 * B * R * k * w * 4 + 3 * B * R * n * d * 4
     bwd_flops_tile = 10.0 * B * R * k * w * w * d
+    bwd_flops_causal = 10.0 * B * R * k * (w * (w + 1) / 2) * d
+    # the scatter's own reads (membership bits); the rows it completes are
+    # counted with the attention's output
+    scatter_bytes = B * R * n * ((k + 31) // 32) * 4
     return dict(bwd_bytes=bwd_bytes, bwd_flops_tile=bwd_flops_tile,
+                bwd_flops_causal=bwd_flops_causal, scatter_bytes=scatter_bytes,
                 route_bytes=route_bytes, attn_bytes=attn_bytes, ema_bytes=ema_bytes,
                 local_bytes=local_bytes, attn_flops_tile=attn_flops_tile,
                 attn_flops_causal=attn_flops_causal, route_flops=route_flops,
                 local_flops=local_flops)
 
 
-def cpu_baseline(cfg, inp, scale, min_seconds=5.0):
-    """The oracle on full steps of the workload on the host cores, repeated
-    until about `min_seconds` have passed (at least once)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_routed_step(oracle, cfg, inp, scale, threads):
+    """The routed heads' step on the oracle: route, routed attention and the
+    centroid update (and the in-cluster backward for the stress workload)."""
+    qk = inp["qk"].value
+    _, idx, _, _ = oracle.route(qk, inp["mu"], cfg.w, nthreads=threads)
+    oracle.routed_attn(qk, qk, inp["v"].value, idx, scale, True, True, nthreads=threads)
+    oracle.centroid_update(inp["mu"], qk, qk, idx, cfg.lam)
+    if cfg.backward:
+        oracle.routed_attn_bwd(qk, qk, inp["v"].value, idx, inp["dout"].value, scale, True,
+                               nthreads=threads)
+
+
+def cpu_baseline(cfg, inp, scale, min_seconds=10.0):
+    """The oracle (fp64, as written: never tuned) on the routed step of the
+    workload, on the host cores, repeated until about `min_seconds` have passed;
+    plus single-thread times of one step of the tiny and routed workloads."""
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    qk = inp["qk"].value
     reps, t0 = 0, time.perf_counter()
     while True:
-        _, idx, _, _ = oracle.route(qk, inp["mu"], cfg.w, nthreads=threads)
-        oracle.routed_attn(qk, qk, inp["v"].value, idx, scale, True, True, nthreads=threads)
-        oracle.centroid_update(inp["mu"], qk, qk, idx, cfg.lam)
-        if cfg.backward:
-            oracle.routed_attn_bwd(qk, qk, inp["v"].value, idx, inp["dout"].value, scale, True,
-                                   nthreads=threads)
-        if cfg.L > 0:
-            oracle.local_attn(inp["q_local"].value, inp["k_local"].value, inp["v_local"].value,
-                              cfg.window, scale, True, nthreads=threads)
+        oracle_routed_step(oracle, cfg, inp, scale, threads)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    single = {}
+    for name in ("tiny", "routed"):
+        c = S.CONFIGS[name]
+        ci = S.make_inputs(c)
+        t1 = time.perf_counter()
+        oracle_routed_step(oracle, c, ci, 1.0 / math.sqrt(c.d), 1)
+        single[name] = time.perf_counter() - t1
     return {"value": reps * cfg.B * cfg.n / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "seconds": dt, "steps": reps,
-            "sample": f"{reps} full step(s) of the {cfg.name} workload (route, routed attention, "
-                      f"EMA{', in-cluster backward' if cfg.backward else ''} and local "
-                      f"attention), fp64, {threads} threads"}
+            "kind": "oracle", "seconds": dt, "steps": reps, "cpu_model": cpu_model(),
+            "single_thread_s_per_step": single,
+            "sample": f"{reps} routed step(s) of the {cfg.name} workload (route, routed "
+                      f"attention, centroid update{', in-cluster backward' if cfg.backward else ''}"
+                      f"; the metric's step), fp64, {threads} threads; single-thread: one step "
+                      f"of the tiny and routed workloads"}
 
 
 def time_stack(rt, sc, reps=5, use_graph=False):
@@ -505,12 +534,33 @@ def run_sweep(rt, reps=20, only=None):
             "exponent_local_time": fit([p["us"]["rt_local_attn"] for p in pts])}
 
 
+def event_stats(fn, reps, stream, flush=None):
+    """p10/p50/p90/mean (ms) of `reps` calls of fn(), each bracketed by its own
+    HIP event pair on `stream` (back to back, so warm); with `flush` (cold) a
+    write of that buffer (512 MB: beyond the 256 MB MALL) precedes every call,
+    outside its events."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        if flush is not None:
+            flush.fill_(1.0)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"p10": float(np.percentile(t, 10)), "p50": float(np.percentile(t, 50)),
+            "p90": float(np.percentile(t, 90)), "mean": float(t.mean()), "reps": reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long", choices=sorted(WORKLOADS))
+    ap.add_argument("--reps", type=int, default=200, help="calls per entry point for the "
+                    "p10/p50/p90 timing, warm and cold")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip timing the 22-layer stack of "
                     "the long workload (reported apart from the per-layer metric)")
@@ -520,8 +570,8 @@ def main():
                     "step (and of the stack) instead of launching eagerly on one stream; graph "
                     "replay measured slower here")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly (the default)")
-    ap.add_argument("--concurrent-local", action="store_true", help="run the local heads "
-                    "concurrently on a second stream instead of after the routed heads")
+    ap.add_argument("--concurrent-local", action="store_true", help="in the whole-layer step, "
+                    "run the local heads concurrently on a second stream")
     ap.add_argument("--sweep", action="store_true", help="instead of the benchmark step, time "
                     "the entry points at n = 1K..64K with k = sqrt(n) and print that as one JSON "
                     "line")
@@ -554,65 +604,83 @@ def main():
     mu0 = torch.from_numpy(inp["mu"].astype(np.float32)).cuda()
     mu = mu0.clone()
     B, R, n, d, k, w = cfg.B, cfg.R, cfg.n, cfg.d, cfg.k, cfg.w
-    inv = torch.empty((B, R, n), dtype=torch.float32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    inv = torch.empty((B, R, n), **f32)
     idx = torch.empty((B, R, k, w), dtype=torch.int32, device="cuda")
     mask = torch.empty((B, R, n, rt.mask_words(k)), dtype=torch.int32, device="cuda")
-    sum_q = torch.empty((B, R, k, d), dtype=torch.float32, device="cuda")
+    sum_q = torch.empty((B, R, k, d), **f32)
     out = torch.empty_like(qk)
     ws_route = torch.empty(rt.workspace_bytes("route", B, R, n, d, k, w), dtype=torch.uint8,
                            device="cuda")
-    ws_upd = torch.empty(rt.workspace_bytes("routed_attn_update", B, R, n, d, k, w),
-                         dtype=torch.uint8, device="cuda")
     ws_attn = torch.empty(rt.workspace_bytes("routed_attn", B, R, n, d, k, w), dtype=torch.uint8,
                           device="cuda")
+    ws_upd = torch.empty(rt.workspace_bytes("routed_attn_update", B, R, n, d, k, w),
+                         dtype=torch.uint8, device="cuda")
     if cfg.L > 0:
         ql, kl, vl = dev(inp["q_local"]), dev(inp["k_local"]), dev(inp["v_local"])
         out_l = torch.empty_like(ql)
     lse = None
     if cfg.backward:
         # the forward keeps its softmax statistics; the backward takes a seeded dO
-        lse = torch.empty((B, R, k, w), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, R, k, w), **f32)
         dout = dev(inp["dout"])
-        grads = tuple(torch.empty((B, R, n, d), dtype=torch.float32, device="cuda")
-                      for _ in range(3))
+        grads = tuple(torch.empty((B, R, n, d), **f32) for _ in range(3))
         ws_bwd = torch.empty(rt.workspace_bytes("routed_attn_bwd", B, R, n, d, k, w),
                              dtype=torch.uint8, device="cuda")
 
     def do_route():
         rt.route(qk, mu, w, out=(inv, idx, mask), ws=ws_route)
 
-    def do_attn():
-        rt.routed_attn(qk, qk, v, idx, inv, inv, scale=scale, mask=mask, sums=(sum_q, None),
-                       out=out, lse=lse, ws=ws_attn)
+    def do_cluster():
+        rt.cluster_attn(qk, qk, v, idx, inv, inv, mask, scale=scale, out=out, lse=lse,
+                        sums=(sum_q, None), ws=ws_attn)
+
+    def do_scatter_update():
+        rt.scatter_rows(mask, out, ws_attn, k, w, in_dtype=qk.dtype, mu=mu, sum_q=sum_q,
+                        lam=cfg.lam)
+
+    def do_scatter():
+        rt.scatter_rows(mask, out, ws_attn, k, w, in_dtype=qk.dtype)
+
+    def do_attn_update():
+        """Both stages in one call (the same two kernels)."""
+        rt.routed_attn_update_(qk, qk, v, idx, inv, inv, mu, cfg.lam, scale=scale, mask=mask,
+                               out=out, lse=lse, ws=ws_upd)
 
     def do_bwd():
         rt.routed_attn_bwd(qk, qk, v, idx, lse, dout, inv, inv, scale=scale, mask=mask,
                            out=grads, ws=ws_bwd)
 
-    def do_ema():
-        rt.centroid_update_sums_(mu, sum_q, cfg.lam)
-
-    def do_attn_update():
-        """do_attn then do_ema in one call (the update rides in the scatter launch)."""
-        rt.routed_attn_update_(qk, qk, v, idx, inv, inv, mu, cfg.lam, scale=scale, mask=mask,
-                               out=out, lse=lse, ws=ws_upd)
-
     def do_local():
-        if cfg.L > 0:
-            rt.local_attn(ql, kl, vl, cfg.window, scale=scale, out=out_l)
+        rt.local_attn(ql, kl, vl, cfg.window, scale=scale, out=out_l)
 
     stream = torch.cuda.Stream()
     side = torch.cuda.Stream()          # local heads: independent of the routed heads
+    cl_ev = []                          # HIP events around rt_cluster_attn in the timed steps
 
-    def step():
+    def routed_step(timed=False):
+        """The routed heads' forward (route, in-cluster attention, scatter-add and the
+        centroid update), plus the in-cluster backward for the stress workload."""
+        do_route()
+        if timed:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            do_cluster()
+            b.record(stream)
+            cl_ev.append((a, b))
+        else:
+            do_cluster()
+        do_scatter_update()
+        if cfg.backward:
+            do_bwd()
+
+    def layer_step():
+        """routed_step plus the local heads (after it, or concurrently)."""
         if cfg.L > 0 and args.concurrent_local:
             side.wait_stream(stream)
             with torch.cuda.stream(side):
                 do_local()
-        do_route()
-        do_attn_update()
-        if cfg.backward:
-            do_bwd()
+        routed_step()
         if cfg.L > 0:
             if not args.concurrent_local:
                 do_local()
@@ -629,57 +697,78 @@ def main():
         del src, dst
 
     use_graph = args.graph and not args.no_graph
+
+    def timed_loop(fn, steps, graph=None):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps, time.perf_counter() - t_wall
+
     with torch.cuda.stream(stream):
         for _ in range(max(1, args.warmup)):
-            step()
+            layer_step()
         torch.cuda.synchronize()
         graph = None
         if use_graph:
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=stream):
-                step()
+                routed_step()
             torch.cuda.synchronize()
             for _ in range(3):
                 graph.replay()
             torch.cuda.synchronize()
 
-        # Whole-step timing.
+        # The timed region: K routed steps (the metric).  The centroids evolve
+        # step by step as in training; they start from the same state each run.
         mu.copy_(mu0)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t_wall = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            if graph is not None:
-                graph.replay()
-            else:
-                step()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
-        ms_per_step = ev0.elapsed_time(ev1) / args.steps
+        ms_per_step, t_wall = timed_loop(routed_step, args.steps, graph)
+        # The same steps again with an event pair around each rt_cluster_attn (an
+        # event drains the stream, so this pass is kept out of the metric): the
+        # kernel's duration inside the step sequence, launch latency included.
+        mu.copy_(mu0)
+        timed_loop(lambda: routed_step(timed=True), args.steps)
+        cluster_in_step_ms = float(np.mean([a.elapsed_time(b) for a, b in cl_ev]))
 
-        # Per-call timing (events on the stream the kernels are launched on).
-        per_call = {}
-        for name, fn in (("rt_route", do_route), ("rt_routed_attn", do_attn),
-                         ("rt_centroid_update_sums", do_ema),
-                         ("rt_routed_attn_update", do_attn_update), ("rt_local_attn", do_local),
-                         ("rt_routed_attn_bwd", do_bwd if cfg.backward else None)):
-            if (name == "rt_local_attn" and cfg.L == 0) or fn is None:
-                continue
+        # The whole layer (routed + local heads), the same number of steps.
+        mu.copy_(mu0)
+        layer_ms, _ = timed_loop(layer_step, args.steps)
+
+        # Per call: amortised over back-to-back calls, and p10/p50/p90 per call,
+        # warm and cold (events on the stream the kernels are launched on).
+        calls = [("rt_route", do_route), ("rt_cluster_attn", do_cluster),
+                 ("rt_scatter_rows", do_scatter), ("rt_scatter_rows+update", do_scatter_update),
+                 ("rt_routed_attn_update", do_attn_update)]
+        if cfg.L > 0:
+            calls.append(("rt_local_attn", do_local))
+        if cfg.backward:
+            calls.append(("rt_routed_attn_bwd", do_bwd))
+        flush = torch.empty((512 << 20) // 4, **f32)
+        per_call, per_call_stats = {}, {}
+        for name, fn in calls:
             fn()                        # a first launch loads the kernel's code
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = max(5, args.steps)
+            reps = max(20, args.steps)
             a.record(stream)
             for _ in range(reps):
                 fn()
             b.record(stream)
             torch.cuda.synchronize()
             per_call[name] = a.elapsed_time(b) / reps
+            per_call_stats[name] = {"warm": event_stats(fn, args.reps, stream),
+                                    "cold": event_stats(fn, args.reps, stream, flush)}
+        del flush
+        mu.copy_(mu0)
 
     alg = algorithmic(cfg)
-    routed_ms = per_call["rt_route"] + per_call["rt_routed_attn_update"]
     tokens = B * n
 
     def rate(nbytes, flops, ms):
@@ -691,35 +780,49 @@ def main():
         return r
 
     stages = {
-        "rt_route": rate(alg["route_bytes"], alg["route_flops"], per_call["rt_route"]),
-        "rt_routed_attn": rate(alg["attn_bytes"], alg["attn_flops_tile"], per_call["rt_routed_attn"]),
-        "rt_centroid_update_sums": rate(2 * R * k * d * 4 + B * R * k * d * 4, 0,
-                                        per_call["rt_centroid_update_sums"]),
+        "rt_route": rate(alg["route_bytes"], 0, per_call["rt_route"]),
+        "rt_cluster_attn": rate(alg["attn_bytes"], alg["attn_flops_causal"],
+                                per_call["rt_cluster_attn"]),
+        "rt_scatter_rows+update": rate(alg["scatter_bytes"] + alg["ema_bytes"], 0,
+                                       per_call["rt_scatter_rows+update"]),
+        "rt_routed_attn_update": rate(alg["attn_bytes"] + alg["ema_bytes"],
+                                      alg["attn_flops_causal"], per_call["rt_routed_attn_update"]),
     }
+    stages["rt_route"]["scoring_TFLOP/s"] = alg["route_flops"] / (per_call["rt_route"] * 1e-3) / 1e12
     if cfg.backward:
-        stages["rt_routed_attn_bwd"] = rate(alg["bwd_bytes"], alg["bwd_flops_tile"],
+        stages["rt_routed_attn_bwd"] = rate(alg["bwd_bytes"], alg["bwd_flops_causal"],
                                             per_call["rt_routed_attn_bwd"])
     if cfg.L > 0:
-        stages["rt_local_attn"] = rate(alg["local_bytes"], alg["local_flops"], per_call["rt_local_attn"])
-        # The longest kernel of the step is the local-window attention; rt_local_attn launches
-        # exactly it, once, so its per-call time is that kernel's launch duration.  Its
-        # arithmetic intensity (about window/2 flop per byte) sits below the ridge point
-        # (peak flops / peak bandwidth), so HBM bounds it.
-        t = per_call["rt_local_attn"] * 1e-3
-        achieved = alg["local_bytes"] / t / 1e9
-        roofline = {"bound": "hbm", "kernel": "local_attn_bf16_kernel (rt_local_attn)",
-                    "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS,
-                    "traffic": measured_traffic(LOCAL_TRAFFIC, args.workload),
-                    "algorithmic_bytes": alg["local_bytes"],
-                    "mfma_frac": alg["local_flops"] / t / 1e12 / PEAK_BF16_TFLOPS}
-    else:
-        t = per_call["rt_routed_attn"] * 1e-3
-        achieved = alg["attn_bytes"] / t / 1e9
-        roofline = {"bound": "hbm", "kernel": "rt_routed_attn (in-cluster attention + combine)",
-                    "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                    "algorithmic_bytes": alg["attn_bytes"]}
+        stages["rt_local_attn"] = rate(alg["local_bytes"], alg["local_flops"],
+                                       per_call["rt_local_attn"])
+    # The dominant kernel of the routed step is the in-cluster attention:
+    # rt_cluster_attn launches exactly cluster_attn_bf16_kernel, so its per-call
+    # time (HIP events on its stream around back-to-back calls) is that kernel's
+    # average launch duration.  Its intensity
+    # (causal-useful flops over the bytes it must move, about w/3 flop/B) is far
+    # below the ridge point, so HBM bounds it; its fraction of the bf16 MFMA peak
+    # (the metric's second half) rides along.
+    t = per_call["rt_cluster_attn"] * 1e-3
+    achieved = alg["attn_bytes"] / t / 1e9
+    roofline = {"bound": "hbm", "kernel": "cluster_attn_bf16_kernel (rt_cluster_attn)",
+                "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS,
+                "traffic": measured_traffic(CLUSTER_TRAFFIC, args.workload),
+                "algorithmic_bytes": alg["attn_bytes"],
+                "launch_ms": t * 1e3,
+                "launch_ms_in_step": cluster_in_step_ms,
+                "mfma_frac": alg["attn_flops_causal"] / t / 1e12 / PEAK_BF16_TFLOPS,
+                "mfma_TFLOP/s": alg["attn_flops_causal"] / t / 1e12,
+                "flops": alg["attn_flops_causal"],
+                "flops_note": "causal-useful: 4 d (w (w+1)/2) per cluster (QK^T and PV over the "
+                              "visible pairs)",
+                "mfma_frac_hbm_ceiling": min(1.0, alg["attn_flops_causal"] / alg["attn_bytes"]
+                                             * PEAK_HBM_GBS / 1e3 / PEAK_BF16_TFLOPS),
+                "route_stage": {"entry": "rt_route", "algorithmic_bytes": alg["route_bytes"],
+                                "ms": per_call["rt_route"],
+                                "hbm_frac": stages["rt_route"]["hbm_frac"]}}
+    routed_ceiling = tokens / ((alg["route_bytes"] + alg["attn_bytes"] + alg["ema_bytes"])
+                               / (PEAK_HBM_GBS * 1e9))
     res = {
         "metric": "routed-attention tokens/sec/layer at n=8192 fwd; % bf16 MFMA peak",
         "value": tokens / (ms_per_step * 1e-3),
@@ -736,13 +839,19 @@ def main():
         "config": {"workload": WORKLOADS[args.workload], "batch": B, "seq_len": n,
                    "routed_heads": R, "local_heads": cfg.L, "d_head": d, "k": k, "w": w,
                    "window": cfg.window, "graph": use_graph, "backward": cfg.backward,
-                   "local_heads_stream": "concurrent" if args.concurrent_local else "same"},
+                   "step": "rt_route -> rt_cluster_attn -> rt_scatter_rows (+ centroid update)"
+                           + (" -> rt_routed_attn_bwd" if cfg.backward else "")},
         "roofline": roofline,
+        "hbm_bound_ceiling_tokens_per_s": routed_ceiling,
+        "frac_of_hbm_ceiling": tokens / (ms_per_step * 1e-3) / routed_ceiling,
+        "layer": {"ms_per_step": layer_ms, "tokens_per_s": tokens / (layer_ms * 1e-3),
+                  "local_heads_stream": "concurrent" if args.concurrent_local else "same",
+                  "note": "routed step plus the local heads' rt_local_attn"},
         "per_call_ms": per_call,
+        "per_call_stats_ms": per_call_stats,
         "stages": stages,
-        "routed_tokens_per_s": tokens / (routed_ms * 1e-3),
-        "routed_over_local_time": (routed_ms / per_call["rt_local_attn"]
-                                   if "rt_local_attn" in per_call else None),
+        "routed_over_local_time": (ms_per_step / per_call["rt_local_attn"]
+                                   if "rt_local_attn" in per_call and not cfg.backward else None),
         "wall_s_timed": t_wall,
     }
     if args.workload == "long" and not args.no_stack:

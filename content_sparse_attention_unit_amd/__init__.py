@@ -18,7 +18,7 @@ import torch
 __all__ = ["route", "route_noalloc", "routed_attn", "local_attn", "centroid_update_", "centroid_update_sums_",
            "routed_attn_bwd", "in_proj", "out_proj", "local_attn_bwd", "normalize_bwd",
            "out_proj_bwd", "in_proj_bwd", "local_attn_blocked", "centroid_update_argmax_",
-           "route_partition", "routed_attn_split", "routed_attn_update_", "attn_js", "decode_cache", "decode_fill", "decode_routed",
+           "route_partition", "routed_attn_split", "routed_attn_update_", "cluster_attn", "scatter_rows", "attn_js", "decode_cache", "decode_fill", "decode_routed",
            "decode_ring_fill", "decode_local", "workspace_bytes", "library_path",
            "mask_words", "RTError", "RT_OP"]
 
@@ -60,6 +60,9 @@ def _load():
         "rt_routed_attn": [P, P, P, I, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P, P, P, Z,
                            P],
         "rt_centroid_update_sums": [P, P, P, I, I, I, I, F, P],
+        "rt_cluster_attn": [P, P, P, I, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P, P, P, P, Z,
+                            P],
+        "rt_scatter_rows": [P, I, I, I, I, I, I, I, P, I, P, P, P, F, P, Z, P],
         "rt_local_attn": [P, P, P, I, I, I, I, I, I, F, I, P, I, P],
         "rt_centroid_update": [P, P, P, P, P, I, P, I, I, I, I, I, I, F, P],
         "rt_in_proj": [P, P, I, I, I, I, I, I, P, P, P, P, P, P],
@@ -287,6 +290,53 @@ def routed_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, idx: torch.T
                               _ptr(sum_k), _ptr(ws), 0 if ws is None else ws.numel(),
                               _stream(dev)))
     return (out, lse) if want_lse else out
+
+
+def cluster_attn(q, kk, v, idx, q_inv, k_inv, mask, *, scale=None, causal=True, out=None,
+                 out_dtype=None, lse=None, sums=(None, None), ws=None):
+    """The first stage of routed_attn: in-cluster attention, rows of tokens one
+    cluster holds written to ``out``, the others kept in ``ws`` for
+    scatter_rows (pass the same ``ws`` and ``out`` there).  ``mask`` (the bits
+    route() wrote for idx) is required.  Returns (out, ws)."""
+    lib = _load()
+    sum_q, sum_k = sums
+    dev = _gpu(q, kk, v, idx, q_inv, k_inv, mask, sum_q, sum_k, out, lse)
+    if mask is None:
+        raise ValueError("cluster_attn needs the membership bits route() wrote")
+    B, H, n, d, k, w = _check_routed(q, kk, v, idx, q_inv, k_inv, mask=mask, lse=lse,
+                                     sums=(sum_q, sum_k))
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+    _shape(out, q.shape, "out")
+    ws, _ = _workspace("routed_attn", dev, B, H, n, d, k, w, ws)
+    _check(lib.rt_cluster_attn(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),
+                               _ptr(k_inv), _ptr(idx), _ptr(mask), B, H, n, d, k, w, sc,
+                               int(causal), _ptr(out), _dtype_code(out), _ptr(lse), _ptr(sum_q),
+                               _ptr(sum_k), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(dev)))
+    return out, ws
+
+
+def scatter_rows(mask, out, ws, k: int, w: int, *, in_dtype=torch.bfloat16, mu=None,
+                 sum_q=None, sum_k=None, lam: float = 0.0):
+    """The second stage of routed_attn: sums the rows of tokens several
+    clusters hold into ``out`` (ascending centroid order) and zeroes tokens no
+    cluster holds; with ``mu`` also the centroid update from sum_q (sum_k).
+    ``mask``, ``out``, ``ws`` as given to cluster_attn; ``in_dtype`` is the
+    dtype of the attention's inputs.  Returns out."""
+    lib = _load()
+    dev = _gpu(mask, out, ws, mu, sum_q, sum_k)
+    B, H, n, d = out.shape
+    _expect(mask, (B, H, n, mask_words(k)), torch.int32, "mask")
+    _expect(mu, (H, k, d), torch.float32, "mu")
+    _expect(sum_q, (B, H, k, d), torch.float32, "sum_q")
+    _expect(sum_k, (B, H, k, d), torch.float32, "sum_k")
+    dt = RT_F32 if in_dtype == torch.float32 else RT_BF16
+    _check(lib.rt_scatter_rows(_ptr(mask), dt, B, H, n, d, k, w, _ptr(out), _dtype_code(out),
+                               _ptr(mu), _ptr(sum_q), _ptr(sum_k), float(lam), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(dev)))
+    return out
 
 
 def local_attn(q: torch.Tensor, kk: torch.Tensor, v: torch.Tensor, window: int, *,

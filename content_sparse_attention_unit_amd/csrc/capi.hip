@@ -277,6 +277,10 @@ rt_status rt_route_noalloc(const void* qk, int dtype, const float* mu, int B, in
 
 namespace {
 
+// Which kernels routed_attn_impl launches: the in-cluster rows, the scatter
+// of rows of tokens several clusters hold (and the update), or both.
+constexpr int kRowsPhase = 1, kScatterPhase = 2, kBothPhases = 3;
+
 // rt_routed_attn and rt_routed_attn_split: idx holds the clusters' keys and
 // values, idx_q their queries (nullptr: idx).
 rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const void* v, int dtype,
@@ -284,7 +288,8 @@ rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const 
                            const int32_t* idx_q, const uint32_t* member_mask, int B, int H, int n,
                            int d, int k, int w, float scale, int causal, void* out, int out_dtype,
                            float* lse, float* sum_q, float* sum_k, void* ws, size_t ws_bytes,
-                           void* stream, float* mu = nullptr, float lambda = 0.f) {
+                           void* stream, float* mu = nullptr, float lambda = 0.f,
+                           int phases = kBothPhases, bool sums_in_ws = true) {
     g_err[0] = 0;
     if (!q || !kk || !v || !idx || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
     if (mu != nullptr && !(lambda >= 0.f && lambda <= 1.f))
@@ -305,12 +310,13 @@ rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const 
     if (w > wmax)
         return fail(RT_EUNSUPPORTED, "%s: w=%d exceeds %d for this dtype, d and q/k sharing", fn,
                     w, wmax);
-    const size_t need = attn_ws(B, H, n, d, k, w) + (mu != nullptr ? update_sums_ws(B, H, k, d) : 0);
+    const size_t need = attn_ws(B, H, n, d, k, w) +
+                        (mu != nullptr && sums_in_ws ? update_sums_ws(B, H, k, d) : 0);
     if (ws == nullptr || ws_bytes < need)
         return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
     char* base = static_cast<char*>(ws);
-    if (mu != nullptr) {        // the member sums of the update, after the attention's parts
+    if (mu != nullptr && sums_in_ws) {   // the member sums of the update, after the attention's parts
         sum_q = reinterpret_cast<float*>(base + attn_ws(B, H, n, d, k, w));
         sum_k = shared ? nullptr : sum_q + (size_t)B * H * k * d;
     }
@@ -324,17 +330,23 @@ rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const 
     hipError_t e = hipSuccess;
     const uint32_t* mask = member_mask;             // the queries' memberships
     if (mask == nullptr) {
+        if (phases != kBothPhases)
+            return fail(RT_EINVAL, "%s: the membership bits are required", fn);
         e = rt::launch_mask(idx_q ? idx_q : idx, BH, n, k, w, mask_ws, s);
         if (e != hipSuccess) return hip_fail(fn, e);
         mask = mask_ws;
     }
-    e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, idx_q, mask, BH, n, d, k, w,
-                                scale, causal, out, out_dtype, lse, slots, ovf, dir, sum_q, sum_k,
-                                s);
-    if (e != hipSuccess) return hip_fail(fn, e);
-    e = rt::launch_combine(mask, slots, ovf, dir, out_dtype, BH, n, d, k, w, out, s, mu, sum_q,
-                           sum_k, B, H, lambda);
-    if (e != hipSuccess) return hip_fail(fn, e);
+    if (phases & kRowsPhase) {
+        e = rt::launch_cluster_attn(q, kk, v, dtype, q_inv, k_inv, idx, idx_q, mask, BH, n, d, k,
+                                    w, scale, causal, out, out_dtype, lse, slots, ovf, dir, sum_q,
+                                    sum_k, s);
+        if (e != hipSuccess) return hip_fail(fn, e);
+    }
+    if (phases & kScatterPhase) {
+        e = rt::launch_combine(mask, slots, ovf, dir, out_dtype, BH, n, d, k, w, out, s, mu, sum_q,
+                               sum_k, B, H, lambda);
+        if (e != hipSuccess) return hip_fail(fn, e);
+    }
     return RT_OK;
 }
 
@@ -366,6 +378,59 @@ rt_status rt_routed_attn_update(const void* q, const void* kk, const void* v, in
     return routed_attn_impl(fn, q, kk, v, dtype, q_inv, k_inv, idx, nullptr, member_mask, B, H, n,
                             d, k, w, scale, causal, out, out_dtype, lse, nullptr, nullptr, ws,
                             ws_bytes, stream, mu, lambda);
+}
+
+rt_status rt_cluster_attn(const void* q, const void* kk, const void* v, int dtype,
+                          const float* q_inv, const float* k_inv, const int32_t* idx,
+                          const uint32_t* member_mask, int B, int H, int n, int d, int k, int w,
+                          float scale, int causal, void* out, int out_dtype, float* lse,
+                          float* sum_q, float* sum_k, void* ws, size_t ws_bytes, void* stream) {
+    static const char* fn = "rt_cluster_attn";
+    if (!member_mask) {
+        g_err[0] = 0;
+        return fail(RT_EINVAL, "%s: null tensor pointer (member_mask)", fn);
+    }
+    return routed_attn_impl(fn, q, kk, v, dtype, q_inv, k_inv, idx, nullptr, member_mask, B, H, n,
+                            d, k, w, scale, causal, out, out_dtype, lse, sum_q, sum_k, ws,
+                            ws_bytes, stream, nullptr, 0.f, kRowsPhase);
+}
+
+rt_status rt_scatter_rows(const uint32_t* member_mask, int dtype, int B, int H, int n, int d,
+                          int k, int w, void* out, int out_dtype, float* mu, const float* sum_q,
+                          const float* sum_k, float lambda, void* ws, size_t ws_bytes,
+                          void* stream) {
+    static const char* fn = "rt_scatter_rows";
+    g_err[0] = 0;
+    if (!member_mask || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (mu != nullptr && sum_q == nullptr)
+        return fail(RT_EINVAL, "%s: the update needs sum_q", fn);
+    if (B <= 0 || H <= 0 || n <= 0 || d <= 0)
+        return fail(RT_EINVAL, "%s: sizes must be positive (B=%d H=%d n=%d d=%d)", fn, B, H, n, d);
+    if (!dim_ok(d)) return fail(RT_EUNSUPPORTED, "%s: d=%d not in {16,32,64,128}", fn, d);
+    rt_status st = check_clusters(fn, n, k, w);
+    if (st != RT_OK) return st;
+    if (mu != nullptr && !(lambda >= 0.f && lambda <= 1.f))
+        return fail(RT_EINVAL, "%s: lambda=%g outside [0, 1]", fn, (double)lambda);
+    if (!out_dtype_ok(out_dtype))
+        return fail(RT_EUNSUPPORTED, "%s: out_dtype %d is not RT_F32 or RT_BF16", fn, out_dtype);
+    if (dtype != RT_F32 && dtype != RT_BF16)
+        return fail(RT_EUNSUPPORTED, "%s: dtype %d is not RT_F32 or RT_BF16", fn, dtype);
+    if ((long long)B * H > 65535)
+        return fail(RT_EUNSUPPORTED, "%s: B*H=%lld exceeds 65535", fn, (long long)B * H);
+    const size_t need = attn_ws(B, H, n, d, k, w);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    ws == nullptr ? (size_t)0 : ws_bytes);
+    char* base = static_cast<char*>(ws);
+    float* slots = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k));
+    float* ovf = reinterpret_cast<float*>(base + attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d));
+    int32_t* dir = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ovf) +
+                                              attn_ws_ovf(B, H, d, k, w));
+    hipError_t e = rt::launch_combine(member_mask, slots, ovf, dir, out_dtype, B * H, n, d, k, w,
+                                      out, static_cast<hipStream_t>(stream), mu, sum_q, sum_k, B,
+                                      H, lambda);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return RT_OK;
 }
 
 rt_status rt_routed_attn_split(const void* q, const void* kk, const void* v, int dtype,

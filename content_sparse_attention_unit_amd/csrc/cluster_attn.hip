@@ -100,7 +100,9 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
     // partial member sums per wave (one side for shared q/k, else keys then queries)
     __shared__ float lsum[SHARED ? 1 : 2][C::NW][C::DP];
 
-    const int cl = blockIdx.x, bh = blockIdx.y;
+    // the clusters of one head on one XCD (they gather rows of the same head)
+    const int item = xcd_contiguous(blockIdx.x + gridDim.x * blockIdx.y, gridDim.x * gridDim.y);
+    const int cl = item % gridDim.x, bh = item / gridDim.x;
     const long tokbase = (long)bh * n;
     const long rowbase = ((long)bh * k + cl) * w;
     const int32_t* irow = idx + rowbase;              // the cluster's keys (and values)
@@ -437,7 +439,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
         ema.mu[i] = fmaf(ema.lam, ema.mu[i], (1.0f - ema.lam) * 0.5f * tot);
         return;
     }
-    const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+    // tokens of one head on one XCD, as in the attention kernel
+    const long gid = (long)xcd_contiguous(blockIdx.x, ema.first_block) * 256 + threadIdx.x;
     const long tok = gid / DG;
     if (tok >= BHn) return;
     const int d0 = 4 * QV * (int)(gid % DG);

@@ -392,7 +392,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
                                          // byte, counts of it and the 3 below (padded)
     __shared__ uint32_t wcnt[NWV], wgt[NWV], weq[NWV];
 
-    const int row = blockIdx.x;
+    // the rows of one head on one XCD: the scoring kernel wrote that head's
+    // scores from the same XCD
+    const int row = xcd_contiguous(blockIdx.x, gridDim.x);
     const float* srow = scores + (long)row * n;
     const int lane = lane_id(), wv = wave_id();
     const int seg0 = wv * kWave * KPT;

@@ -189,6 +189,41 @@ rt_status rt_routed_attn_update(const void *q, const void *kk, const void *v, in
                                 void *stream);
 
 /*
+ * rt_cluster_attn, rt_scatter_rows -- rt_routed_attn in its two stages, for
+ *   callers that schedule them apart (e.g. other work between them) and for
+ *   timing each.  The Spec names the stages: attention inside each cluster,
+ *   then the scatter-add of the cluster rows back to token order.
+ *
+ * rt_cluster_attn: gathers each cluster's rows and runs the in-cluster
+ *   attention (Summary §3, §4 as for rt_routed_attn).  Rows of tokens that
+ *   one cluster holds are written to `out` (final); rows of tokens that
+ *   several clusters hold go to the workspace for rt_scatter_rows.  Rows of
+ *   tokens that no cluster holds are not written.  member_mask is required
+ *   (the bits rt_route wrote for idx).  Other arguments as rt_routed_attn.
+ *
+ * rt_scatter_rows: completes `out` after rt_cluster_attn with the same
+ *   member_mask, ws, B, H, n, d, k, w, dtype (the attention's input dtype)
+ *   and out_dtype: tokens held by several clusters get the sum of their rows
+ *   in ascending centroid order, tokens held by none get zeros.  With mu !=
+ *   NULL it also applies rt_centroid_update_sums's update from sum_q (and
+ *   sum_k; NULL counts sum_q twice), both [B][H][k][d] float32 as
+ *   rt_cluster_attn wrote them; lambda in [0, 1].
+ *   The two calls in this order, on one stream, give rt_routed_attn's (and,
+ *   with mu, rt_routed_attn_update's) results bit for bit.
+ *   ws: rt_workspace_bytes(RT_OP_ROUTED_ATTN, ...) bytes, the same buffer for
+ *   both calls, untouched in between.
+ */
+rt_status rt_cluster_attn(const void *q, const void *kk, const void *v, int dtype,
+                          const float *q_inv, const float *k_inv, const int32_t *idx,
+                          const uint32_t *member_mask, int B, int H, int n, int d, int k, int w,
+                          float scale, int causal, void *out, int out_dtype, float *lse,
+                          float *sum_q, float *sum_k, void *ws, size_t ws_bytes, void *stream);
+rt_status rt_scatter_rows(const uint32_t *member_mask, int dtype, int B, int H, int n, int d,
+                          int k, int w, void *out, int out_dtype, float *mu, const float *sum_q,
+                          const float *sum_k, float lambda, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
  * rt_routed_attn_split -- rt_routed_attn for queries and keys routed on their
  *   own (distinct query and key vectors, each given to rt_route with the same
  *   centroids).

@@ -126,6 +126,47 @@ def test_routed_attn_validation(lib, kw, code, msg):
     assert msg in _last(lib)
 
 
+def cluster(lib, mask=FAKE, B=1, H=1, n=64, d=16, k=4, w=16, ws_bytes=1 << 30):
+    return lib.rt_cluster_attn(FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, mask, B, H, n, d, k, w, 0.25,
+                               1, ctypes.c_void_p(0x2000), 1, None, None, None, FAKE, ws_bytes,
+                               None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(mask=None), RT_EINVAL, "member_mask"),
+    (dict(w=65), RT_EINVAL, "exceeds n"),
+    (dict(d=48), RT_EUNSUPPORTED, "d=48"),
+    (dict(ws_bytes=10), RT_EINVAL, "workspace"),
+])
+def test_cluster_attn_validation(lib, kw, code, msg):
+    assert cluster(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def scatter(lib, mask=FAKE, dtype=1, B=1, H=1, n=64, d=16, k=4, w=16, out=FAKE, out_dtype=1,
+            mu=None, sum_q=None, lam=0.5, ws=FAKE, ws_bytes=1 << 30):
+    return lib.rt_scatter_rows(mask, dtype, B, H, n, d, k, w, out, out_dtype, mu, sum_q, None,
+                               lam, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(mask=None), RT_EINVAL, "null"),
+    (dict(out=None), RT_EINVAL, "null"),
+    (dict(mu=FAKE), RT_EINVAL, "sum_q"),
+    (dict(mu=FAKE, sum_q=FAKE, lam=1.5), RT_EINVAL, "lambda"),
+    (dict(n=0), RT_EINVAL, "positive"),
+    (dict(k=300), RT_EUNSUPPORTED, "k=300"),
+    (dict(d=8), RT_EUNSUPPORTED, "d=8"),
+    (dict(dtype=3), RT_EUNSUPPORTED, "dtype"),
+    (dict(out_dtype=4), RT_EUNSUPPORTED, "out_dtype"),
+    (dict(ws=None), RT_EINVAL, "workspace"),
+    (dict(ws_bytes=100), RT_EINVAL, "workspace"),
+])
+def test_scatter_rows_validation(lib, kw, code, msg):
+    assert scatter(lib, **kw) == code
+    assert msg in _last(lib)
+
+
 def test_routed_attn_limits_depend_on_sharing(lib):
     # distinct q/k at d=128 is limited to w=128, shared q/k to 256
     assert attn(lib, q=ctypes.c_void_p(0x3000), n=4096, d=128, w=200, ws_bytes=0) == RT_EUNSUPPORTED

@@ -231,6 +231,39 @@ def test_unrouted_tokens_are_zero_and_deterministic(rt, orc):
         assert torch.equal(out2, res["out"]) and torch.equal(mu3, res["mu_e"])
 
 
+@pytest.mark.parametrize("shape", [(2, 3, 300, 64, 10, 40, "bf16"), (1, 8, 8192, 128, 64, 128, "bf16"),
+                                   (1, 2, 257, 32, 9, 33, "f32")],
+                         ids=["ragged", "long", "f32"])
+def test_two_stage_matches_routed_attn(rt, shape):
+    """rt_cluster_attn then rt_scatter_rows (with and without the update) give
+    rt_routed_attn's and rt_routed_attn_update's results bit for bit."""
+    B, H, n, d, k, w, dtype = shape
+    print(f"[case] two-stage {shape}", flush=True)
+    qk = dev_tensor(S.normal_tensor(99_000, (B, H, n, d), dtype))
+    v = dev_tensor(S.normal_tensor(99_001, (B, H, n, d), dtype))
+    mu0 = torch.from_numpy(S.unit_rows_f32(99_002, H * k, d).reshape(H, k, d).astype(np.float32)).cuda()
+    inv, idx, mask = rt.route(qk, mu0, w, want_mask=True)
+    sc = 1.0 / math.sqrt(d)
+    for odt in (torch.float32, qk.dtype):
+        want, want_lse = rt.routed_attn(qk, qk, v, idx, inv, inv, scale=sc, mask=mask,
+                                        want_lse=True, out_dtype=odt)
+        mu_want = mu0.clone()
+        want_u = rt.routed_attn_update_(qk, qk, v, idx, inv, inv, mu_want, 0.9, scale=sc,
+                                        mask=mask, out_dtype=odt)
+        sum_q = torch.empty((B, H, k, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty_like(want_lse)
+        out, ws = rt.cluster_attn(qk, qk, v, idx, inv, inv, mask, scale=sc, out_dtype=odt,
+                                  lse=lse, sums=(sum_q, None))
+        rt.scatter_rows(mask, out, ws, k, w, in_dtype=qk.dtype)
+        out2, ws2 = rt.cluster_attn(qk, qk, v, idx, inv, inv, mask, scale=sc, out_dtype=odt,
+                                    sums=(sum_q, None))
+        mu = mu0.clone()
+        rt.scatter_rows(mask, out2, ws2, k, w, in_dtype=qk.dtype, mu=mu, sum_q=sum_q, lam=0.9)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want) and torch.equal(lse, want_lse)
+        assert torch.equal(out2, want_u) and torch.equal(mu, mu_want)
+
+
 def test_binding_rejects_bad_shapes(rt):
     """The binding checks every buffer the kernels index by the shape
     arguments alone before anything is launched."""
