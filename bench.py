@@ -42,9 +42,9 @@ CLUSTER_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "",
-    "fetch_kib": 0.0, "write_kib": 0.0,
-    "fetch_scale": 1.0, "write_scale": 1.0,
+    "sha256": "53e4087d9fbf1bcbe4839b13a1ddd40f2fd3140580ed21f0826f25c50c6ca9e0",
+    "fetch_kib": 11014.218, "write_kib": 26950.663,
+    "fetch_scale": 262144.0 / 131088.1875, "write_scale": 262144.0 / 262144.0,
 }
 
 
@@ -270,7 +270,7 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
     lse = torch.empty((B, R, k, w), **f32)
     do_r, do_l = torch.empty((B, R, n, d), **bf), torch.empty((B, L, n, d), **bf)
     dw_o = torch.empty((dm, (R + L) * d), **f32)
-    dqh, dkh, dv, dqk = (torch.empty((B, R, n, d), **f32) for _ in range(4))
+    dqh, dv, dqk = (torch.empty((B, R, n, d), **f32) for _ in range(3))
     dq_l, dk_l, dv_l = (torch.empty((B, L, n, d), **f32) for _ in range(3))
     dx = torch.empty((B, n, dm), **f32)
     dw_in = torch.empty(((2 * R + 3 * L) * d, dm), **f32)
@@ -287,10 +287,10 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
                             2 * 2.0 * T * dm * NO),
         "rt_routed_attn_bwd": (lambda: rt.routed_attn_bwd(t["qk"], t["qk"], t["v"], t["idx"], lse,
                                                           do_r, t["inv"], t["inv"], scale=scale,
-                                                          mask=t["mask"], out=(dqh, dkh, dv),
-                                                          ws=ws_b),
-                               10.0 * B * R * k * w * w * d),
-        "rt_normalize_bwd": (lambda: rt.normalize_bwd(t["qk"], t["inv"], dqh, dkh, out=dqk), 0.0),
+                                                          mask=t["mask"], out=(dqh, None, dv),
+                                                          ws=ws_b, sum_qk=True),
+                               10.0 * B * R * k * (w * (w + 1) / 2) * d),
+        "rt_normalize_bwd": (lambda: rt.normalize_bwd(t["qk"], t["inv"], dqh, None, out=dqk), 0.0),
         "rt_local_attn_bwd": (lambda: rt.local_attn_bwd(t["ql"], t["kl"], t["vl"], do_l,
                                                         sc.window, scale=scale,
                                                         out=(dq_l, dk_l, dv_l), ws=ws_l),
@@ -325,7 +325,7 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
             "tflops": tfl, "finite": finite,
             "note": "one layer's backward (membership fixed), the sum of back-to-back call "
                     "times; tflops on the algorithmic products (routed and local attention: "
-                    "5 products per visible pair)"}
+                    "5 products per visible pair; the routed backward returns dq_hat + dk_hat)"}
 
 
 def time_variants(rt, cfg, inp, reps=20):
@@ -624,7 +624,9 @@ def main():
         # the forward keeps its softmax statistics; the backward takes a seeded dO
         lse = torch.empty((B, R, k, w), **f32)
         dout = dev(inp["dout"])
-        grads = tuple(torch.empty((B, R, n, d), **f32) for _ in range(3))
+        # shared q/k: the backward returns dq_hat + dk_hat (what the normalisation's
+        # gradient consumes) and dv
+        grads = (torch.empty((B, R, n, d), **f32), None, torch.empty((B, R, n, d), **f32))
         ws_bwd = torch.empty(rt.workspace_bytes("routed_attn_bwd", B, R, n, d, k, w),
                              dtype=torch.uint8, device="cuda")
 
@@ -649,7 +651,7 @@ def main():
 
     def do_bwd():
         rt.routed_attn_bwd(qk, qk, v, idx, lse, dout, inv, inv, scale=scale, mask=mask,
-                           out=grads, ws=ws_bwd)
+                           out=grads, ws=ws_bwd, sum_qk=True)
 
     def do_local():
         rt.local_attn(ql, kl, vl, cfg.window, scale=scale, out=out_l)

@@ -381,24 +381,34 @@ def centroid_update_sums_(mu: torch.Tensor, sum_q: torch.Tensor, lam: float,
 
 
 def routed_attn_bwd(q, kk, v, idx, lse, dout, q_inv=None, k_inv=None, *, scale=None,
-                    causal=True, mask=None, out=None, ws=None):
+                    causal=True, mask=None, out=None, ws=None, sum_qk=False):
     """Gradients (dq_hat, dk_hat, dv), float32, of routed_attn for a fixed
     membership; ``lse`` comes from the forward call (want_lse=True), ``mask``
     may be the membership bitmask route() wrote for ``idx`` and ``out`` may
-    hold three preallocated float32 [B,H,n,d] tensors."""
+    hold three preallocated float32 [B,H,n,d] tensors.  ``sum_qk`` (shared
+    q/k only) returns (dq_hat + dk_hat, None, dv): the gradient of the shared
+    normalised vector, with one gradient fewer to scatter; ``out`` may then
+    hold (dqk, None, dv)."""
     lib = _load()
     dev = _gpu(q, kk, v, idx, lse, dout, q_inv, k_inv, mask)
     if lse is None or dout is None:
         raise ValueError("routed_attn_bwd needs the forward's lse and dout")
     B, H, n, d, k, w = _check_routed(q, kk, v, idx, q_inv, k_inv, mask=mask, lse=lse, dout=dout)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if sum_qk and (kk is not q or k_inv is not q_inv):
+        raise ValueError("sum_qk needs shared q/k (kk is q, k_inv is q_inv)")
     if out is None:
-        out = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        out = tuple(None if (sum_qk and i == 1) else
+                    torch.empty(q.shape, dtype=torch.float32, device=dev) for i in range(3))
     dq, dk, dv = out
+    if sum_qk:
+        dk = None
     _gpu(dq, dk, dv)
-    if any(t.dtype != torch.float32 for t in out):
-        raise TypeError("gradients are float32")
-    for name, t in zip(("dq", "dk", "dv"), out):
+    for name, t in zip(("dq", "dk", "dv"), (dq, dk, dv)):
+        if t is None:
+            continue
+        if t.dtype != torch.float32:
+            raise TypeError("gradients are float32")
         _shape(t, q.shape, name)
     ws, _ = _workspace("routed_attn_bwd", dev, B, H, n, d, k, w, ws)
     _check(lib.rt_routed_attn_bwd(_ptr(q), _ptr(kk), _ptr(v), _dtype_code(q), _ptr(q_inv),

@@ -594,14 +594,17 @@ rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int d
                              float* dv, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_routed_attn_bwd";
     g_err[0] = 0;
-    if (!q || !kk || !v || !idx || !lse || !dout || !dq_hat || !dk_hat || !dv)
+    if (!q || !kk || !v || !idx || !lse || !dout || !dq_hat || !dv)
         return fail(RT_EINVAL, "%s: null tensor pointer", fn);
     if ((q_inv == nullptr) != (k_inv == nullptr))
         return fail(RT_EINVAL, "%s: q_inv and k_inv must both be given or both be NULL", fn);
+    if (dk_hat == nullptr && !(q == kk && q_inv == k_inv))
+        return fail(RT_EINVAL, "%s: dk_hat may be NULL only with shared q/k (q == kk)", fn);
     {
         const void* outs[3] = {dq_hat, dk_hat, dv};
         const void* ins[5] = {q, kk, v, dout, lse};
         for (int i = 0; i < 3; ++i) {
+            if (outs[i] == nullptr) continue;
             for (int j = 0; j < 5; ++j)
                 if (outs[i] == ins[j]) return fail(RT_EINVAL, "%s: a gradient aliases an input", fn);
             for (int j = i + 1; j < 3; ++j)

@@ -626,6 +626,14 @@ hipError_t launch_combine(const uint32_t* mask, const float* slots, const float*
     return hipGetLastError();
 }
 
+hipError_t launch_combine2_f32(const uint32_t* mask, const float* const slots[2],
+                               const float* const ovf[2], const int32_t* dir, int BH, int n, int d,
+                               int k, int w, float* const out[2], hipStream_t s) {
+    const CombineSet<2> cs{{slots[0], slots[1]}, {ovf[0], ovf[1]}, {out[0], out[1]}};
+    launch_combine_t<float, 2>(mask, dir, cs, BH, n, d, k, w, FoldedEma{}, s);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine3_f32(const uint32_t* mask, const float* const slots[3],
                                const float* const ovf[3], const int32_t* dir, int BH, int n, int d,
                                int k, int w, float* const out[3], hipStream_t s) {

@@ -106,7 +106,9 @@ __device__ __forceinline__ void store_row(const f32x4 (&o)[NJ], float mul, int d
 }
 
 struct BwdOut {
-    float *dq, *dk, *dv;           // token order (rows of tokens held by one cluster)
+    // token order (rows of tokens held by one cluster); dk == nullptr (shared
+    // q/k only): dq receives dq^ + dk^, the gradient of the shared vector
+    float *dq, *dk, *dv;
     float *sq, *sk, *sv;           // rank slots
     float *oq, *ok, *ov;           // overflow ranks
     int32_t* dir;                  // overflow directory (shared by the three)
@@ -168,8 +170,16 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
     const int nb = (w + 15) / 16;
     const float sl2 = scale * 1.4426950408889634f;
 
+    // With shared q/k a wave takes the same 16-row blocks in both phases, in
+    // the same lane layout, so dq^ rows can wait in registers for dk^.
+    const bool sum_qk = SHARED && out.dk == nullptr;
+    constexpr int RMAX = (WMAX / 16 + C::NW - 1) / C::NW;   // rounds of blocks per wave
+    f32x4 oa[RMAX][C::NJ];
+
     // ---- phase A: lanes own queries -------------------------------------------
-    for (int round = 0; round * C::NW < nb; ++round) {
+#pragma unroll
+    for (int round = 0; round < RMAX; ++round) {
+        if (round * C::NW >= nb) break;
         const int qb = round * C::NW + ((round & 1) ? (C::NW - 1 - wv) : wv);
         if (qb >= nb) continue;
         const int qrow = qb * 16 + r16;
@@ -236,7 +246,10 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
             }
             acc_xt_w<C::NJ, C::LDX>(pw, o, &lk[kc * C::LDX], r16, g, 1 | ((kc + 32 < kend) ? 2 : 0));
         }
-        if (qrow < w) {
+        if (sum_qk) {
+#pragma unroll
+            for (int jb = 0; jb < C::NJ; ++jb) oa[round][jb] = o[jb];
+        } else if (qrow < w) {
             const int t = clamp_pos(irow[qrow], n);
             store_row<C::NJ>(o, scale, ldest[qrow], tokbase + t, rowbase + qrow, D, g, out.dq,
                              out.sq, out.oq);
@@ -245,7 +258,9 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
     __syncthreads();   // D_r of every query is in lD
 
     // ---- phase B: lanes own keys ----------------------------------------------
-    for (int round = 0; round * C::NW < nb; ++round) {
+#pragma unroll
+    for (int round = 0; round < RMAX; ++round) {
+        if (round * C::NW >= nb) break;
         const int kbk = round * C::NW + ((round & 1) ? (C::NW - 1 - wv) : wv);
         if (kbk >= nb) continue;
         const int key = kbk * 16 + r16;
@@ -300,8 +315,15 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
         if (key < w) {
             const int t = clamp_pos(irow[key], n);
             const int dest = ldest[key];
-            store_row<C::NJ>(odk, scale, dest, tokbase + t, rowbase + key, D, g, out.dk, out.sk,
-                             out.ok);
+            if (sum_qk) {        // this row's dq^ (phase A, same block, same lanes) + dk^
+#pragma unroll
+                for (int jb = 0; jb < C::NJ; ++jb) odk[jb] += oa[round][jb];
+                store_row<C::NJ>(odk, scale, dest, tokbase + t, rowbase + key, D, g, out.dq,
+                                 out.sq, out.oq);
+            } else {
+                store_row<C::NJ>(odk, scale, dest, tokbase + t, rowbase + key, D, g, out.dk,
+                                 out.sk, out.ok);
+            }
             store_row<C::NJ>(odv, 1.f, dest, tokbase + t, rowbase + key, D, g, out.dv, out.sv,
                              out.ov);
         }
@@ -378,11 +400,14 @@ __global__ __launch_bounds__(256) void cluster_attn_bwd_f32_kernel(
         const int dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
         if (dest >= kSlots && i == 0)
             out.dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
-        const float vals[3] = {aq * scale, ak * scale, av};
+        // dk == nullptr (shared q/k): dq receives dq^ + dk^
+        const bool sum_qk = out.dk == nullptr;
+        const float vals[3] = {sum_qk ? (aq + ak) * scale : aq * scale, ak * scale, av};
         float* direct[3] = {out.dq, out.dk, out.dv};
         float* slot[3] = {out.sq, out.sk, out.sv};
         float* over[3] = {out.oq, out.ok, out.ov};
         for (int j = 0; j < 3; ++j) {
+            if (j == 1 && sum_qk) continue;
             if (dest == -1) direct[j][(tokbase + raw) * D + i] = vals[j];
             else if (dest < kSlots) slot[j][((tokbase + raw) * kSlots + dest) * D + i] = vals[j];
             else over[j][(rowbase + r) * D + i] = vals[j];
@@ -510,6 +535,12 @@ hipError_t launch_cluster_attn_bwd(const void* q, const void* kk, const void* v,
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (dk == nullptr) {      // dq + dk in dq: two gradients to scatter
+        float* const grads[2] = {dq, dv};
+        const float* const sl[2] = {part[0][0], part[2][0]};
+        const float* const ov[2] = {part[0][1], part[2][1]};
+        return launch_combine2_f32(mask, sl, ov, dir, BH, n, d, k, w, grads, s);
+    }
     float* const grads[3] = {dq, dk, dv};
     const float* const sl[3] = {part[0][0], part[1][0], part[2][0]};
     const float* const ov[3] = {part[0][1], part[1][1], part[2][1]};

@@ -82,6 +82,9 @@ hipError_t launch_combine(const uint32_t* mask, const float* slots, const float*
 hipError_t launch_combine3_f32(const uint32_t* mask, const float* const slots[3],
                                const float* const ovf[3], const int32_t* dir, int BH, int n, int d,
                                int k, int w, float* const out[3], hipStream_t s);
+hipError_t launch_combine2_f32(const uint32_t* mask, const float* const slots[2],
+                               const float* const ovf[2], const int32_t* dir, int BH, int n, int d,
+                               int k, int w, float* const out[2], hipStream_t s);
 
 // mu <- lambda*mu + (1-lambda)/2 * (sum_b sum_q[b] + sum_b sum_k[b]); sum_k may
 // be NULL (keys are the queries: S_K = S_Q).  sums are [B][H][k][d].

@@ -309,7 +309,10 @@ rt_status rt_centroid_update_sums(float *mu, const float *sum_q, const float *su
  *   dq_hat, dk_hat  out [B][H][n][d] float32: gradients w.r.t. the
  *                   normalised vectors q*q_inv and kk*k_inv (token order,
  *                   summed over clusters).  With shared QK the gradient of
- *                   the shared normalised vector is dq_hat + dk_hat.
+ *                   the shared normalised vector is dq_hat + dk_hat; pass
+ *                   dk_hat = NULL (shared QK only: q == kk, q_inv == k_inv)
+ *                   to receive that sum in dq_hat directly (one gradient
+ *                   fewer to scatter; summed per cluster row in float32).
  *   dv              out [B][H][n][d] float32.
  *   member_mask     [B][H][n][ceil(k/32)] uint32 or NULL, as for rt_routed_attn:
  *                   the membership bits rt_route wrote for this idx (saves

@@ -262,6 +262,8 @@ def bwd(lib, q=FAKE, kk=FAKE, v=FAKE, dtype=1, q_inv=FAKE, k_inv=FAKE, idx=FAKE,
     (dict(q_inv=None), RT_EINVAL, "both"),
     (dict(dq=FAKE), RT_EINVAL, "aliases an input"),
     (dict(dk=ctypes.c_void_p(0x6000)), RT_EINVAL, "alias each other"),
+    (dict(q=ctypes.c_void_p(0x3000), dk=None), RT_EINVAL, "only with shared"),
+    (dict(dk=None), RT_EINVAL, "workspace"),      # shared q/k: dk may be NULL
     (dict(w=65), RT_EINVAL, "exceeds n"),
     (dict(d=24), RT_EUNSUPPORTED, "d=24"),
     (dict(causal=3), RT_EINVAL, "causal"),

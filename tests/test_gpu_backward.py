@@ -114,6 +114,19 @@ def run_bwd_case(rt, orc, cfg, causal=True, scale=None, distinct=False, heads=No
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2), \
         "backward is not deterministic, or differs with the membership bits given"
+    dqk = None
+    if not distinct:
+        # shared q/k: the summed gradient dq_hat + dk_hat straight from the call,
+        # deterministic, with the same dv
+        dqk, none_, dv3 = rt.routed_attn_bwd(q, kk, v, idx, lse, g, q_inv, k_inv, scale=sc,
+                                             causal=causal, mask=mask, sum_qk=True)
+        dqk2, _, _ = rt.routed_attn_bwd(q, kk, v, idx, lse, g, q_inv, k_inv, scale=sc,
+                                        causal=causal, mask=mask, sum_qk=True)
+        torch.cuda.synchronize()
+        assert none_ is None and torch.equal(dqk, dqk2) and torch.equal(dv3, dv)
+        # the same sum as the two gradients added (float32 rounding of the sum apart)
+        sep = host(dq) + host(dk)
+        assert np.abs(host(dqk) - sep).max() <= 1e-5 * max(1.0, np.abs(sep).max())
     hs = range(cfg.R) if heads is None else heads
     for h in hs:
         sl = (slice(None), slice(h, h + 1))
@@ -122,12 +135,14 @@ def run_bwd_case(rt, orc, cfg, causal=True, scale=None, distinct=False, heads=No
         assert_grad_close(host(dq)[sl], dq_o, cfg.dtype, f"dq_hat head {h}")
         assert_grad_close(host(dk)[sl], dk_o, cfg.dtype, f"dk_hat head {h}")
         assert_grad_close(host(dv)[sl], dv_o, cfg.dtype, f"dv head {h}")
+        if dqk is not None:
+            assert_grad_close(host(dqk)[sl], dq_o + dk_o, cfg.dtype, f"dq_hat + dk_hat head {h}")
     # tokens no cluster holds get exactly zero gradients
     cnt = np.zeros((cfg.B, cfg.R, cfg.n), np.int64)
     for b in range(cfg.B):
         for h in range(cfg.R):
             cnt[b, h] = np.bincount(idx_o[b, h].ravel(), minlength=cfg.n)
-    for t in (dq, dk, dv):
+    for t in (dq, dk, dv) + (() if dqk is None else (dqk,)):
         assert np.all(host(t)[cnt == 0] == 0.0)
     return cnt
 
