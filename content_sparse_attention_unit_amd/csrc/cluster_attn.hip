@@ -110,55 +110,107 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
     // (then only without causality: the mask below compares row indices)
     const int32_t* irowq = SHARED ? irow : idx_q + rowbase;
 
-    // Request every member row at once: keys/queries, then values.  Thread t
-    // holds the 16-byte chunk t % CPR of rows t / CPR + (NT / CPR) * it.
+    // Request every member row at once.  First the row indices, all in flight
+    // together with this thread's output row; then that row's inverse norms and
+    // membership words and every key/query and value row the indices name.
+    // The loads go through buffer resources (one per (batch, head) slice or
+    // cluster row): rows past w and absent inverse norms read as zeros from an
+    // offset out of range, so no load sits under a branch, and nothing loaded is
+    // used before the last load is issued.  (A load under a branch, or one whose
+    // address needs another load, makes the compiler wait for every load issued
+    // before it: one memory round trip per row instead of two in all.)
+    // Thread t holds the 16-byte chunk t % CPR of rows t / CPR + (NT / CPR) * it.
+    static_assert(C::NT >= WMAX, "one output row per thread");
     const bool want_sums = sum_q != nullptr || sum_k != nullptr;
+    const uint32_t slice = (uint32_t)n * D * 2u;   // bytes of one (batch, head) slice
+    const buf_rsrc krs = make_rsrc(kk + tokbase * D, slice);
+    const buf_rsrc qrs = make_rsrc(q + tokbase * D, slice);
+    const buf_rsrc vrs = make_rsrc(v + tokbase * D, slice);
+    const buf_rsrc irs = make_rsrc(irow, 4u * (uint32_t)w);
+    const buf_rsrc iqrs = make_rsrc(irowq, 4u * (uint32_t)w);
+    const buf_rsrc kinv_rs = make_rsrc(k_inv ? k_inv + tokbase : nullptr, k_inv ? 4u * n : 0u);
+    const buf_rsrc qinv_rs = make_rsrc(q_inv ? q_inv + tokbase : nullptr, q_inv ? 4u * n : 0u);
+    const buf_rsrc mrs = make_rsrc(mask + tokbase * KW, 4u * (uint32_t)n * KW);
+
+    int tk[C::XPT], tq[SHARED ? 1 : C::XPT];
+#pragma unroll
+    for (int it = 0; it < C::XPT; ++it) {
+        const int r = (int)(threadIdx.x + it * C::NT) / C::CPR;
+        const uint32_t off = r < w ? 4u * r : kOutOfRange;
+        tk[it] = (int)buffer_load_u32(irs, off);
+        if (!SHARED) tq[it] = (int)buffer_load_u32(iqrs, off);
+    }
+    constexpr bool VROWS = C::DCH == C::CPR;   // value chunks lie on the key rows
+    int tv[VROWS ? 1 : C::VPT];
+    if constexpr (!VROWS) {
+#pragma unroll
+        for (int it = 0; it < C::VPT; ++it) {
+            const int r = (int)(threadIdx.x + it * C::NT) / C::DCH;
+            tv[it] = (int)buffer_load_u32(irs, r < w ? 4u * r : kOutOfRange);
+        }
+    }
+    const int orow = threadIdx.x;
+    const uint32_t ooff = orow < w ? 4u * orow : kOutOfRange;
+    const int raw = (int)buffer_load_u32(iqrs, ooff);   // row orow's query token (if orow < w)
+    const int kraw = SHARED ? raw : (int)buffer_load_u32(irs, ooff);  // and its key token
+
+    // this thread's output row: inverse norms (0 when absent) and membership words
+    const bool qok = orow < w && raw >= 0 && raw < n;
+    const float ik_ld = __uint_as_float(
+        buffer_load_u32(kinv_rs, orow < w ? 4u * clamp_pos(kraw, n) : kOutOfRange));
+    const float iq_ld = SHARED ? ik_ld : __uint_as_float(
+        buffer_load_u32(qinv_rs, orow < w ? 4u * clamp_pos(raw, n) : kOutOfRange));
+    uint32_t wd[8];
+    load_words(mrs, qok, clamp_pos(raw, n), KW, wd);
+
     uint4 xk[C::XPT], xq[SHARED ? 1 : C::XPT];
-    float ikr[C::XPT], iqr[SHARED ? 1 : C::XPT];   // their inverse norms (0 on padding)
+    float ikr[C::XPT], iqr[SHARED ? 1 : C::XPT];   // their inverse norms (0 when absent)
 #pragma unroll
     for (int it = 0; it < C::XPT; ++it) {
         const int e = threadIdx.x + it * C::NT;
         const int r = e / C::CPR, ch = e % C::CPR;
-        xk[it] = zero_u4();
-        if (!SHARED) xq[it] = zero_u4();
-        ikr[it] = 0.f;
-        if (!SHARED) iqr[it] = 0.f;
-        if (r < w && 8 * ch < D) {
-            const long tok = tokbase + clamp_pos(irow[r], n);
-            const long tokq = tokbase + clamp_pos(irowq[r], n);
-            xk[it] = *reinterpret_cast<const uint4*>(kk + tok * D + 8 * ch);
-            if (!SHARED) xq[it] = *reinterpret_cast<const uint4*>(q + tokq * D + 8 * ch);
-            if (want_sums) {
-                ikr[it] = k_inv ? k_inv[tok] : 1.f;
-                if (!SHARED) iqr[it] = q_inv ? q_inv[tokq] : 1.f;
-            }
-        }
+        const bool ok = r < w && 8 * ch < D;
+        xk[it] = buffer_load16(krs, ok ? 2u * (uint32_t)(clamp_pos(tk[it], n) * D + 8 * ch) : kOutOfRange);
+        if (!SHARED)
+            xq[it] = buffer_load16(qrs, ok ? 2u * (uint32_t)(clamp_pos(tq[it], n) * D + 8 * ch) : kOutOfRange);
+        // (read as zeros unless the sums are wanted)
+        ikr[it] = __uint_as_float(buffer_load_u32(
+            kinv_rs, ok && want_sums ? 4u * clamp_pos(tk[it], n) : kOutOfRange));
+        if (!SHARED)
+            iqr[it] = __uint_as_float(buffer_load_u32(
+                qinv_rs, ok && want_sums ? 4u * clamp_pos(tq[it], n) : kOutOfRange));
     }
     uint4 va[C::VPT];
 #pragma unroll
     for (int it = 0; it < C::VPT; ++it) {
         const int e = threadIdx.x + it * C::NT;
         const int r = e / C::DCH, ch = e % C::DCH;
-        va[it] = zero_u4();
-        if (r < w) va[it] = *reinterpret_cast<const uint4*>(v + (tokbase + clamp_pos(irow[r], n)) * D + 8 * ch);
+        const int t = clamp_pos(VROWS ? tk[VROWS ? it : 0] : tv[VROWS ? 0 : it], n);
+        va[it] = buffer_load16(vrs, r < w ? 2u * (uint32_t)(t * D + 8 * ch) : kOutOfRange);
     }
-    for (int r = threadIdx.x; r < WMAX; r += C::NT) {
-        int pos = -1, dest = -2;
-        float ik = 0.f, iq = 0.f;
-        if (r < w) {
-            const int raw = irowq[r];                 // row r's query token: where its output goes
-            if (raw >= 0 && raw < n) {
-                pos = raw;
-                dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
-                if (dest >= kSlots) dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
-            }
-            ik = k_inv ? k_inv[tokbase + clamp_pos(irow[r], n)] : 1.f;
-            iq = q_inv ? q_inv[tokbase + clamp_pos(raw, n)] : 1.f;
+    if (want_sums) {
+        // absent inverse norms: the rows are unit vectors already
+#pragma unroll
+        for (int it = 0; it < C::XPT; ++it) {
+            const int e = threadIdx.x + it * C::NT;
+            const bool ok = e / C::CPR < w && 8 * (e % C::CPR) < D;
+            if (k_inv == nullptr) ikr[it] = ok ? 1.f : 0.f;
+            if (!SHARED && q_inv == nullptr) iqr[SHARED ? 0 : it] = ok ? 1.f : 0.f;
         }
-        lpos[r] = pos;
-        ldest[r] = dest;
-        linvk[r] = ik;
-        if (!SHARED) linvq[r] = iq;
+    }
+    {
+        int pos = -1, dest = -2;
+        if (qok) {
+            pos = raw;
+            dest = dest_from_words(wd, cl);
+            if (dest >= kSlots) dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + orow;
+        }
+        if (orow < WMAX) {
+            lpos[orow] = pos;
+            ldest[orow] = dest;
+            linvk[orow] = orow < w ? (k_inv ? ik_ld : 1.f) : 0.f;
+            if (!SHARED) linvq[orow] = orow < w ? (q_inv ? iq_ld : 1.f) : 0.f;
+        }
     }
 #pragma unroll
     for (int it = 0; it < C::XPT; ++it) {

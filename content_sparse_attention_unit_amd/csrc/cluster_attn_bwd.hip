@@ -48,32 +48,57 @@ struct BwdCfg {
     static constexpr int XPT = (WMAX * CPR + NT - 1) / NT;
 };
 
-// Gather `w` member rows of x (row r = token irow[r]) into a padded LDS tile
-// (rows >= w and dims >= D are zero).
-template <int D, int WMAX, int NT, int LDX>
-__device__ __forceinline__ void gather_rows(const u16* __restrict__ x, long tokbase,
-                                            const int32_t* __restrict__ irow, int n, int w,
-                                            u16* lx) {
+// Gather the `w` member rows (row r = token irow[r]) of NX tensors into padded
+// LDS tiles (rows >= w and dims >= D are zero).  The row indices are loaded
+// first, all together, then every row of every tensor, through buffer
+// resources of the (batch, head) slices: rows past w read as zeros from an
+// offset out of range, so no load sits under a branch.  (A load under a
+// branch, or one whose address needs another load, makes the compiler wait
+// for every load issued before it: one memory round trip per row instead of
+// two in all.)  `mid(raw)` runs before the rows are requested, with
+// raw = irow[threadIdx.x] (any value when threadIdx.x >= w) loaded with the
+// indices, so that its own loads join the rows' round trip; it returns a step
+// that runs once every row is requested and before they are stored (the place
+// to use what `mid` loaded).
+template <int D, int WMAX, int NT, int LDX, int NX, typename Mid>
+__device__ __forceinline__ void gather_tiles(const u16* const (&xs)[NX], long tokbase,
+                                             const int32_t* __restrict__ irow, int n, int w,
+                                             u16* const (&lxs)[NX], Mid&& mid) {
     constexpr int DP = D < 32 ? 32 : D;
     constexpr int CPR = DP / 8;
     constexpr int XPT = (WMAX * CPR + NT - 1) / NT;
-    uint4 t[XPT];
+    const buf_rsrc irs = make_rsrc(irow, 4u * (uint32_t)w);
+    int tr[XPT];
 #pragma unroll
     for (int it = 0; it < XPT; ++it) {
-        const int e = threadIdx.x + it * NT;
-        const int r = e / CPR, ch = e % CPR;
-        t[it] = zero_u4();
-        if (r < w && 8 * ch < D)
-            t[it] = *reinterpret_cast<const uint4*>(x + (tokbase + clamp_pos(irow[r], n)) * D + 8 * ch);
+        const int r = (int)(threadIdx.x + it * NT) / CPR;
+        tr[it] = (int)buffer_load_u32(irs, r < w ? 4u * r : kOutOfRange);
     }
+    const int raw = (int)buffer_load_u32(irs, (int)threadIdx.x < w ? 4u * threadIdx.x : kOutOfRange);
+    auto fin = mid(raw);
+    uint4 t[NX][XPT];
 #pragma unroll
-    for (int it = 0; it < XPT; ++it) {
-        const int e = threadIdx.x + it * NT;
-        if (e < WMAX * CPR) {
+    for (int x = 0; x < NX; ++x) {
+        const buf_rsrc rs = make_rsrc(xs[x] + tokbase * D, (uint32_t)n * D * 2u);
+#pragma unroll
+        for (int it = 0; it < XPT; ++it) {
+            const int e = threadIdx.x + it * NT;
             const int r = e / CPR, ch = e % CPR;
-            *reinterpret_cast<uint4*>(&lx[r * LDX + 8 * ch]) = t[it];
+            t[x][it] = buffer_load16(
+                rs, r < w && 8 * ch < D ? 2u * (uint32_t)(clamp_pos(tr[it], n) * D + 8 * ch) : kOutOfRange);
         }
     }
+    fin();
+#pragma unroll
+    for (int x = 0; x < NX; ++x)
+#pragma unroll
+        for (int it = 0; it < XPT; ++it) {
+            const int e = threadIdx.x + it * NT;
+            if (e < WMAX * CPR) {
+                const int r = e / CPR, ch = e % CPR;
+                *reinterpret_cast<uint4*>(&lxs[x][r * LDX + 8 * ch]) = t[x][it];
+            }
+        }
 }
 
 // One 16 x 16 block of A B^T over d: rows of A from an LDS tile (row a0 + r16),
@@ -137,29 +162,45 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
     const long rowbase = ((long)bh * k + cl) * w;
     const int32_t* irow = idx + rowbase;
 
-    gather_rows<D, WMAX, C::NT, C::LDX>(kk, tokbase, irow, n, w, lk);
-    if (!SHARED) gather_rows<D, WMAX, C::NT, C::LDX>(q, tokbase, irow, n, w, lq);
-    gather_rows<D, WMAX, C::NT, C::LDX>(v, tokbase, irow, n, w, lv);
-    gather_rows<D, WMAX, C::NT, C::LDX>(dout, tokbase, irow, n, w, ldo);
-    for (int r = threadIdx.x; r < WMAX; r += C::NT) {
-        int dest = -2;
-        float ik = 0.f, iq = 0.f, l2 = INFINITY;
-        if (r < w) {
-            const int raw = irow[r];
-            const int posc = clamp_pos(raw, n);
-            if (raw >= 0 && raw < n) {
-                dest = row_dest(mask + (tokbase + raw) * KW, KW, cl);
+    static_assert(C::NT >= WMAX, "one row per thread");
+    // this thread's row: destination, inverse norms and log-denominator
+    auto row_info = [&](int raw) {
+        const int r = threadIdx.x;
+        const bool rok = r < w, tok = rok && raw >= 0 && raw < n;
+        const uint32_t toff = rok ? 4u * clamp_pos(raw, n) : kOutOfRange;
+        const float ik = __uint_as_float(buffer_load_u32(
+            make_rsrc(k_inv ? k_inv + tokbase : nullptr, k_inv ? 4u * n : 0u), toff));
+        const float iq = __uint_as_float(buffer_load_u32(
+            make_rsrc(q_inv ? q_inv + tokbase : nullptr, q_inv ? 4u * n : 0u), toff));
+        const float lr = __uint_as_float(buffer_load_u32(
+            make_rsrc(lse + rowbase, 4u * (uint32_t)w), rok ? 4u * r : kOutOfRange));
+        uint32_t wd[8];
+        load_words(make_rsrc(mask + tokbase * KW, 4u * (uint32_t)n * KW), tok, clamp_pos(raw, n),
+                   KW, wd);
+        return [=]() {
+            int dest = -2;
+            if (tok) {
+                dest = dest_from_words(wd, cl);
                 if (dest >= kSlots)
                     out.dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
             }
-            ik = k_inv ? k_inv[tokbase + posc] : 1.f;
-            iq = q_inv ? q_inv[tokbase + posc] : 1.f;
-            l2 = lse[rowbase + r] * 1.4426950408889634f;
-        }
-        ldest[r] = dest;
-        linvk[r] = ik;
-        if (!SHARED) linvq[r] = iq;
-        llse[r] = l2;
+            if (r < WMAX) {
+                ldest[r] = dest;
+                // absent inverse norms: the rows are unit vectors already
+                linvk[r] = rok ? (k_inv ? ik : 1.f) : 0.f;
+                if (!SHARED) linvq[r] = rok ? (q_inv ? iq : 1.f) : 0.f;
+                llse[r] = rok ? lr * 1.4426950408889634f : INFINITY;
+            }
+        };
+    };
+    if constexpr (SHARED) {
+        const u16* const xs[3] = {kk, v, dout};
+        u16* const ls[3] = {lk, lv, ldo};
+        gather_tiles<D, WMAX, C::NT, C::LDX, 3>(xs, tokbase, irow, n, w, ls, row_info);
+    } else {
+        const u16* const xs[4] = {kk, q, v, dout};
+        u16* const ls[4] = {lk, lq, lv, ldo};
+        gather_tiles<D, WMAX, C::NT, C::LDX, 4>(xs, tokbase, irow, n, w, ls, row_info);
     }
     __syncthreads();
 

@@ -31,6 +31,9 @@
 namespace rt {
 namespace {
 
+// rows up to this many tokens keep all their keys in registers in topw_kernel
+constexpr int kTopwRegisterRow = 8192;
+
 template <int D>
 struct ScoreCfg {
     static constexpr int DP = D < 32 ? 32 : D;         // dims padded to the MFMA k-depth
@@ -191,9 +194,23 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
                         if (s0 > bs[0]) { bs[0] = s0; bc[0] = c; }
                         if (s1 > bs[1]) { bs[1] = s1; bc[1] = c; }
                     } else {
+                        // Up to 8192 tokens the top-w selection reads every
+                        // score once, in the next launch, after L2 has been
+                        // written back and invalidated: the scores are
+                        // streamed past it (kept dirty there they would only
+                        // lengthen the write-back at the end of this launch).
+                        // Longer rows re-read their candidates, and those
+                        // re-reads find the scores written the ordinary way
+                        // in the cache behind L2 (measured at n = 32768:
+                        // streamed stores cost the route 13 us of 86).
                         float* row = scores + ((long)bh * k + c) * n;
-                        if (tok[0] < n) row[tok[0]] = s0;
-                        if (tok[1] < n) row[tok[1]] = s1;
+                        if (n <= kTopwRegisterRow) {
+                            if (tok[0] < n) __builtin_nontemporal_store(s0, &row[tok[0]]);
+                            if (tok[1] < n) __builtin_nontemporal_store(s1, &row[tok[1]]);
+                        } else {
+                            if (tok[0] < n) row[tok[0]] = s0;
+                            if (tok[1] < n) row[tok[1]] = s1;
+                        }
                     }
                 }
             }
@@ -849,7 +866,7 @@ hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t
     else if (n <= 1024) launch_topw_k<256, 4>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 2048) launch_topw_k<256, 8>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 4096) launch_topw_k<256, 16>(scores, rows, n, w, idx, k, mask, s);
-    else if (n <= 8192) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= kTopwRegisterRow) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
     // beyond 8K keys a row, top bytes only: fewer registers, two rows a CU
     else if (n <= 16384) launch_topw_k<512, 32, true>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 32768) launch_topw_k<1024, 32, true>(scores, rows, n, w, idx, k, mask, s);

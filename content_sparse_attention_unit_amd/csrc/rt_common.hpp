@@ -107,10 +107,14 @@ __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) 
 __device__ __forceinline__ uint4 buffer_load16(buf_rsrc r, uint32_t byte_off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
+__device__ __forceinline__ uint32_t buffer_load_u32(buf_rsrc r, uint32_t byte_off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0);
+}
 #else
 struct buf_rsrc {};
 __device__ __forceinline__ buf_rsrc make_rsrc(const void*, uint32_t) { return buf_rsrc{}; }
 __device__ __forceinline__ uint4 buffer_load16(buf_rsrc, uint32_t) { return make_uint4(0u, 0u, 0u, 0u); }
+__device__ __forceinline__ uint32_t buffer_load_u32(buf_rsrc, uint32_t) { return 0u; }
 #endif
 // a byte offset no range reaches (loads from it return zeros)
 constexpr uint32_t kOutOfRange = 0xfffffff0u;
@@ -206,6 +210,27 @@ __device__ __forceinline__ int row_dest(const uint32_t* __restrict__ m, int KW, 
         cnt += __popc(word);
         if (i < (c >> 5)) below += __popc(word);
         else if (i == (c >> 5)) below += __popc(word & ((1u << (c & 31)) - 1u));
+    }
+    return cnt == 1 ? -1 : below;
+}
+
+// The same in two steps, so that the words can be requested together with
+// other loads and counted only after all of them are issued: load_words reads
+// token t's KW <= 8 words (k <= 256) from the resource of its (batch, head)
+// slice of the mask, or zeros unless `ok`; dest_from_words counts them.
+__device__ __forceinline__ void load_words(buf_rsrc mrs, bool ok, int t, int KW,
+                                           uint32_t (&wd)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        wd[i] = buffer_load_u32(mrs, ok && i < KW ? 4u * (uint32_t)(t * KW + i) : kOutOfRange);
+}
+__device__ __forceinline__ int dest_from_words(const uint32_t (&wd)[8], int c) {
+    int cnt = 0, below = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        cnt += __popc(wd[i]);
+        if (i < (c >> 5)) below += __popc(wd[i]);
+        else if (i == (c >> 5)) below += __popc(wd[i] & ((1u << (c & 31)) - 1u));
     }
     return cnt == 1 ? -1 : below;
 }
