@@ -496,9 +496,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint32_t* __restrict
     const long tok = gid / DG;
     if (tok >= BHn) return;
     const int d0 = 4 * QV * (int)(gid % DG);
+    // the token's membership words, requested together (KW <= 8; the tests
+    // on KW are the same for every thread), then counted
     const uint32_t* mrow = mask + tok * KW;
+    uint32_t wd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        wd[i] = 0u;
+        if (i < KW) wd[i] = mrow[i];
+    }
     int cnt = 0;
-    for (int i = 0; i < KW; ++i) cnt += __popc(mrow[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt += __popc(wd[i]);
     if (cnt == 1) return;
     const long bhkw = (tok / n) * k * (long)w;
     const int32_t* drow = dir + tok * (k - kSlots);
