@@ -42,9 +42,9 @@ CLUSTER_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "53e4087d9fbf1bcbe4839b13a1ddd40f2fd3140580ed21f0826f25c50c6ca9e0",
-    "fetch_kib": 11014.218, "write_kib": 26950.663,
-    "fetch_scale": 262144.0 / 131088.1875, "write_scale": 262144.0 / 262144.0,
+    "sha256": "0653b88d20269d0679f84eb4dc9634e2fb0baccfae6fb4f25df5d8198c998996",
+    "fetch_kib": 11017.715, "write_kib": 26950.653,
+    "fetch_scale": 262144.0 / 131088.0, "write_scale": 262144.0 / 262144.0,
 }
 
 
