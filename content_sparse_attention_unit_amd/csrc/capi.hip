@@ -114,6 +114,12 @@ size_t attn_ws_ovf(int B, int H, int d, int k, int w) {
     return align256((size_t)B * H * k * w * d * sizeof(float));
 }
 
+// rt_route_partition workspace: label, best, grp, cl [B*H*n] (4 bytes each) | goff
+// [B*H][k + 1] int32.
+size_t partition_ws(int B, int H, int n, int k) {
+    return (size_t)B * H * n * 4 * 4 + (size_t)B * H * (k + 1) * 4;
+}
+
 size_t attn_ws(int B, int H, int n, int d, int k, int w) {
     return attn_ws_mask(B, H, n, k) + attn_ws_slots(B, H, n, d) + attn_ws_ovf(B, H, d, k, w) +
            (size_t)B * H * n * rt::ovf_ranks(k) * sizeof(int32_t);
@@ -158,7 +164,7 @@ size_t rt_workspace_bytes(int op, int B, int H, int n, int d, int k, int w) {
         case RT_OP_ROUTED_ATTN_BWD: return rt::bwd_workspace_bytes(B * H, n, d, k, w);
         case RT_OP_LOCAL_ATTN_BWD: return rt::local_bwd_workspace_bytes(B * H, n);
         case RT_OP_CENTROID_UPDATE_ARGMAX: return argmax_ema_ws(B, H, n, d, k);
-        case RT_OP_ROUTE_PARTITION: return (size_t)B * H * n * 2 * 4;
+        case RT_OP_ROUTE_PARTITION: return partition_ws(B, H, n, k);
         case RT_OP_ROUTED_ATTN_UPDATE: return attn_ws(B, H, n, d, k, w) + update_sums_ws(B, H, k, d);
         case RT_OP_ATTN_JS: return align256((size_t)B * H * n * d * 2) + align256((size_t)B * H * n * 4);
         default: return (size_t)-1;
@@ -885,16 +891,21 @@ rt_status rt_route_partition(const void* qk, int dtype, const float* mu, int B, 
     if (n % k != 0) return fail(RT_EINVAL, "%s: n=%d is not a multiple of k=%d", fn, n, k);
     if (n > rt::kPartitionMaxN)
         return fail(RT_EUNSUPPORTED, "%s: n=%d exceeds %d", fn, n, rt::kPartitionMaxN);
-    const size_t need = (size_t)B * H * n * 2 * 4;
+    const size_t need = partition_ws(B, H, n, k);
     if (ws == nullptr || ws_bytes < need)
         return fail(RT_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                     ws == nullptr ? (size_t)0 : ws_bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t tok = (size_t)B * H * n;
     int32_t* label = static_cast<int32_t*>(ws);
-    float* best = reinterpret_cast<float*>(label + (size_t)B * H * n);
+    float* best = reinterpret_cast<float*>(label + tok);
+    int32_t* grp = label + 2 * tok;
+    int32_t* cl = label + 3 * tok;
+    int32_t* goff = label + 4 * tok;
     hipError_t e = rt::launch_nearest(qk, dtype, mu, B, H, n, d, k, inv_norm, label, best,
                                       member_mask, s);
-    if (e == hipSuccess) e = rt::launch_partition(label, best, B * H, n, k, idx, member_mask, s);
+    if (e == hipSuccess)
+        e = rt::launch_partition(label, best, B * H, n, k, idx, member_mask, grp, cl, goff, s);
     if (e != hipSuccess) return hip_fail(fn, e);
     return RT_OK;
 }

@@ -739,61 +739,171 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     });
 }
 
-// Partition-style balanced clusters, one workgroup per (batch, head): every
-// token sits in exactly one cluster of w = n / k.  A bitonic sort in LDS orders
-// the tokens by (nearest centroid, descending score against it, position);
-// rank r goes to cluster r / w; a second sort by (cluster, position) lists each
-// cluster by ascending position.  Keys are 64-bit: label | score key | token.
+// Partition-style balanced clusters: every token sits in exactly one cluster
+// of w = n / k.  The tokens of a (batch, head) are ordered by (nearest
+// centroid, descending score against it, position); rank r goes to cluster
+// r / w, and each cluster is listed by ascending position.  Three launches:
+//   part_group_kernel  one workgroup per (batch, head): the label histogram,
+//                      its exclusive sums (group offsets), and every token
+//                      placed in its label's group (in any order inside it);
+//   part_rank_kernel   one workgroup per (batch, head, label): each member's
+//                      rank inside its group is the number of members before
+//                      it in (descending score, position), so the order the
+//                      group was filled in does not matter; offset + rank
+//                      gives the cluster and the token's membership bit;
+//   part_emit_kernel   one workgroup per (batch, head, cluster): its members
+//                      listed in ascending position with wave ballots.
+// Each thread requests all its values before using any (kPartPerThread per
+// thread, 1024 threads: n <= kPartitionMaxN).
+constexpr int kPartThreads = 1024;
+constexpr int kPartPerThread = kPartitionMaxN / kPartThreads;
 
-__device__ __forceinline__ void bitonic_sort_lds(unsigned long long* keys, int n2) {
-    for (int size = 2; size <= n2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < (n2 >> 1); i += blockDim.x) {
-                const int lo = 2 * stride * (i / stride) + (i % stride), hi = lo + stride;
-                const unsigned long long a = keys[lo], b = keys[hi];
-                const bool up = (lo & size) == 0;
-                if ((a > b) == up) {
-                    keys[lo] = b;
-                    keys[hi] = a;
+__global__ __launch_bounds__(kPartThreads) void part_group_kernel(const int32_t* __restrict__ label,
+                                                                  int n, int k,
+                                                                  int32_t* __restrict__ grp,
+                                                                  int32_t* __restrict__ goff) {
+    __shared__ int hist[256], cursor[256];
+    const long base = (long)blockIdx.x * n;
+    const buf_rsrc lrs = make_rsrc(label + base, 4u * (uint32_t)n);
+    int lab[kPartPerThread];
+#pragma unroll
+    for (int j = 0; j < kPartPerThread; ++j) {
+        const int t = (int)threadIdx.x + kPartThreads * j;
+        lab[j] = (int)buffer_load_u32(lrs, t < n ? 4u * t : kOutOfRange);
+    }
+    for (int c = threadIdx.x; c < k; c += kPartThreads) hist[c] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPartPerThread; ++j)
+        if ((int)threadIdx.x + kPartThreads * j < n) atomicAdd(&hist[lab[j]], 1);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        // exclusive sums over the k <= 256 labels: four a lane, then across lanes
+        const int lane = threadIdx.x;
+        int v[4], tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i] = 4 * lane + i < k ? hist[4 * lane + i] : 0;
+            tot += v[i];
+        }
+        int incl = tot;
+#pragma unroll
+        for (int dl = 1; dl < kWave; dl <<= 1) {
+            const int o = __shfl_up(incl, dl);
+            if (lane >= dl) incl += o;
+        }
+        int run = incl - tot;
+        int32_t* go = goff + (long)blockIdx.x * (k + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * lane + i;
+            if (c < k) {
+                cursor[c] = run;
+                go[c] = run;
+            }
+            run += v[i];
+        }
+        if (lane == kWave - 1) go[k] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPartPerThread; ++j) {
+        const int t = (int)threadIdx.x + kPartThreads * j;
+        if (t < n) grp[base + atomicAdd(&cursor[lab[j]], 1)] = t;
+    }
+}
+
+constexpr int kRankThreads = 256;
+constexpr int kRankTile = 1024;   // group members staged in LDS at a time
+
+__global__ __launch_bounds__(kRankThreads) void part_rank_kernel(
+    const float* __restrict__ best, const int32_t* __restrict__ grp,
+    const int32_t* __restrict__ goff, int n, int k, int w, int KW, int32_t* __restrict__ cl,
+    uint32_t* __restrict__ mask) {
+    __shared__ uint32_t skey[kRankTile];
+    __shared__ int spos[kRankTile];
+    const int c = blockIdx.x;
+    const long bh = blockIdx.y, base = bh * n;
+    const int32_t* go = goff + bh * (k + 1);
+    const int g0 = go[c], m = go[c + 1] - g0;
+    for (int i0 = 0; i0 < m; i0 += kRankThreads) {
+        const int i = i0 + (int)threadIdx.x;
+        const int tok = i < m ? grp[base + g0 + i] : 0;
+        const uint32_t key = i < m ? order_key(best[base + tok]) : 0u;
+        int before = 0;   // members before this one: higher score, or equal and earlier
+        for (int j0 = 0; j0 < m; j0 += kRankTile) {
+            const int jn = min(kRankTile, m - j0);
+            __syncthreads();   // the previous tile is no longer read
+            int tj[kRankTile / kRankThreads];
+#pragma unroll
+            for (int u = 0; u < kRankTile / kRankThreads; ++u) {
+                const int j = (int)threadIdx.x + kRankThreads * u;
+                tj[u] = j < jn ? grp[base + g0 + j0 + j] : 0;
+            }
+            float bj[kRankTile / kRankThreads];
+#pragma unroll
+            for (int u = 0; u < kRankTile / kRankThreads; ++u) {
+                const int j = (int)threadIdx.x + kRankThreads * u;
+                bj[u] = j < jn ? best[base + tj[u]] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kRankTile / kRankThreads; ++u) {
+                const int j = (int)threadIdx.x + kRankThreads * u;
+                if (j < jn) {
+                    skey[j] = order_key(bj[u]);
+                    spos[j] = tj[u];
                 }
             }
             __syncthreads();
+            if (i < m)
+                for (int j = 0; j < jn; ++j) {
+                    const uint32_t kj = skey[j];
+                    before += (kj > key || (kj == key && spos[j] < tok)) ? 1 : 0;
+                }
+        }
+        if (i < m) {
+            const int clu = (g0 + before) / w;
+            cl[base + tok] = clu;
+            if (mask != nullptr) mask[(base + tok) * KW + (clu >> 5)] = 1u << (clu & 31);
         }
     }
 }
 
-__global__ __launch_bounds__(1024) void partition_kernel(const int32_t* __restrict__ label,
-                                                         const float* __restrict__ best, int n,
-                                                         int k, int w, int32_t* __restrict__ idx,
-                                                         uint32_t* __restrict__ mask, int KW) {
-    __shared__ unsigned long long keys[kPartitionMaxN];
-    const long bh = blockIdx.x;
-    int n2 = 1;
-    while (n2 < n) n2 <<= 1;
-    for (int t = threadIdx.x; t < n2; t += blockDim.x) {
-        unsigned long long key = ~0ull;   // padding sorts last
-        if (t < n) {
-            const uint32_t sk = ~order_key(best[bh * n + t]);   // larger score, smaller key
-            key = ((unsigned long long)(uint32_t)label[bh * n + t] << 56) |
-                  ((unsigned long long)sk << 24) | (unsigned long long)t;
-        }
-        keys[t] = key;
+__global__ __launch_bounds__(kPartThreads) void part_emit_kernel(const int32_t* __restrict__ cl,
+                                                                 int n, int k, int w,
+                                                                 int32_t* __restrict__ idx) {
+    constexpr int NWV = kPartThreads / kWave;
+    __shared__ int wcount[NWV];
+    const int c = blockIdx.x;
+    const long bh = blockIdx.y, base = bh * n;
+    const int lane = lane_id(), wv = wave_id();
+    // wave wv takes positions [wv * seg, (wv + 1) * seg), 64 at a time
+    const int seg = kWave * kPartPerThread;
+    const buf_rsrc crs = make_rsrc(cl + base, 4u * (uint32_t)n);
+    int cv[kPartPerThread];
+#pragma unroll
+    for (int j = 0; j < kPartPerThread; ++j) {
+        const int p = wv * seg + kWave * j + lane;
+        cv[j] = (int)buffer_load_u32(crs, p < n ? 4u * p : kOutOfRange);
     }
-    __syncthreads();
-    bitonic_sort_lds(keys, n2);
-    // rank r -> cluster r / w; re-key by (cluster, position)
-    for (int r = threadIdx.x; r < n2; r += blockDim.x) {
-        if (r < n) {
-            const unsigned long long t = keys[r] & 0xffffffull;
-            keys[r] = ((unsigned long long)(r / w) << 24) | t;
-        }
+    bool is[kPartPerThread];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kPartPerThread; ++j) {
+        is[j] = wv * seg + kWave * j + lane < n && cv[j] == c;
+        cnt += __popcll(__ballot(is[j]));
     }
+    if (lane == 0) wcount[wv] = cnt;
     __syncthreads();
-    bitonic_sort_lds(keys, n2);
-    for (int r = threadIdx.x; r < n; r += blockDim.x) {
-        const int cl = (int)(keys[r] >> 24), t = (int)(keys[r] & 0xffffffull);
-        idx[(bh * k + cl) * w + (r - cl * w)] = t;
-        if (mask != nullptr) mask[(bh * n + t) * KW + (cl >> 5)] = 1u << (cl & 31);
+    int before = 0;
+    for (int v2 = 0; v2 < wv; ++v2) before += wcount[v2];
+    int32_t* out = idx + (bh * k + c) * (long)w;
+#pragma unroll
+    for (int j = 0; j < kPartPerThread; ++j) {
+        const uint64_t b = __ballot(is[j]);
+        const int slot = before + lanes_below(b);
+        if (is[j] && slot < w) out[slot] = wv * seg + kWave * j + lane;
+        before += __popcll(b);
     }
 }
 
@@ -852,9 +962,14 @@ hipError_t launch_nearest(const void* qk, int dtype, const float* mu, int B, int
 }
 
 hipError_t launch_partition(const int32_t* label, const float* best, int BH, int n, int k,
-                            int32_t* idx, uint32_t* mask, hipStream_t s) {
-    hipLaunchKernelGGL(partition_kernel, dim3(BH), dim3(1024), 0, s, label, best, n, k, n / k, idx,
-                       mask, mask_words(k));
+                            int32_t* idx, uint32_t* mask, int32_t* grp, int32_t* cl,
+                            int32_t* goff, hipStream_t s) {
+    const int w = n / k;
+    hipLaunchKernelGGL(part_group_kernel, dim3(BH), dim3(kPartThreads), 0, s, label, n, k, grp,
+                       goff);
+    hipLaunchKernelGGL(part_rank_kernel, dim3(k, BH), dim3(kRankThreads), 0, s, best, grp, goff,
+                       n, k, w, mask_words(k), cl, mask);
+    hipLaunchKernelGGL(part_emit_kernel, dim3(k, BH), dim3(kPartThreads), 0, s, cl, n, k, w, idx);
     return hipGetLastError();
 }
 

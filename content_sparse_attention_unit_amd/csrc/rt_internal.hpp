@@ -26,10 +26,11 @@ hipError_t launch_nearest(const void* qk, int dtype, const float* mu, int B, int
 
 // Partition-style balanced clusters from the nearest-centroid labels and
 // scores (n a multiple of k, n <= kPartitionMaxN); mask (nullable) must be
-// zeroed.
+// zeroed.  Scratch: grp and cl [BH][n] int32, goff [BH][k + 1] int32.
 constexpr int kPartitionMaxN = 16384;
 hipError_t launch_partition(const int32_t* label, const float* best, int BH, int n, int k,
-                            int32_t* idx, uint32_t* mask, hipStream_t s);
+                            int32_t* idx, uint32_t* mask, int32_t* grp, int32_t* cl,
+                            int32_t* goff, hipStream_t s);
 
 // The nearest-centroid EMA: per-chunk sums of each label's normalised rows
 // (part_q / part_k: label_chunks(B, n) * H * k * d floats each; kk == nullptr
