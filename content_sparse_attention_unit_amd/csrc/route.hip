@@ -73,6 +73,9 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
     // group with one 16-byte LDS write.
     constexpr int GPR = C::DP / 8;                   // 8-dim groups per centroid row
     constexpr int MG = (C::KC * GPR) / C::NT;        // groups per thread
+    // Loads go through buffer resources (offsets out of range read zeros), so
+    // none sits under a branch and the waits for them stay exact.
+    const buf_rsrc mrs = make_rsrc(mu + (long)h * k * D, 4u * (uint32_t)k * D);
     float4 mreg[MG][2];
     auto load_mu = [&](int c0) {
 #pragma unroll
@@ -80,9 +83,9 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
             const int e = threadIdx.x + C::NT * j;
             const int c = e / GPR, dim0 = 8 * (e % GPR);
             const bool ok = c0 + c < k && dim0 < D;
-            const float* src = mu + ((long)h * k + c0 + c) * D + dim0;
-            mreg[j][0] = ok ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
-            mreg[j][1] = ok ? *reinterpret_cast<const float4*>(src + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const uint32_t off = ok ? 4u * (uint32_t)((c0 + c) * D + dim0) : kOutOfRange;
+            mreg[j][0] = __builtin_bit_cast(float4, buffer_load16(mrs, off));
+            mreg[j][1] = __builtin_bit_cast(float4, buffer_load16(mrs, ok ? off + 16u : kOutOfRange));
         }
     };
     auto stage_mu = [&]() {
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
     };
     load_mu(0);
 
+    const buf_rsrc xrs = make_rsrc(qk + base * D, 2u * (uint32_t)n * D);
     uint4 breg[2][C::NS];
     float inv[2];
     int tok[2];
@@ -122,11 +126,16 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
 #pragma unroll
         for (int s = 0; s < C::NS; ++s) {
             const int d0 = 32 * s + 8 * g;
-            breg[tb][s] = (t < n && d0 < D) ? *reinterpret_cast<const uint4*>(qk + (base + t) * D + d0)
-                                           : zero_u4();
+            breg[tb][s] = buffer_load16(xrs, t < n && d0 < D ? 2u * (uint32_t)(t * D + d0) : kOutOfRange);
         }
     }
     stage_mu();
+    // every wave's terms are in LDS; the barrier comes before any wave waits
+    // for its token rows, so that a wave starts its products once its own rows
+    // are in, not once every wave's are (nothing that reads them is moved
+    // above it)
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         const int t = tok[tb];
@@ -169,8 +178,8 @@ __global__ __launch_bounds__(ScoreCfg<D>::NT) void score_bf16_kernel(const u16* 
             __syncthreads();          // previous chunk's MFMAs are done with lmu
             load_mu(c0);
             stage_mu();
+            __syncthreads();
         }
-        __syncthreads();
         const int cn = min(C::KC, k - c0);
         for (int cb = 0; cb * 16 < cn; ++cb) {
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
