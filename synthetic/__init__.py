@@ -237,19 +237,24 @@ STACKS = {
 
 
 def separated_tokens(seed: int, B: int, H: int, n: int, d: int, k: int, dtype: str = "bf16",
-                     spacing: float = 1.5e-3):
+                     spacing: float = 1.5e-3, weights=None):
     """Tokens gathered around k random unit centres, for inputs whose
     nearest-centre assignment and within-group order hold no near-equal
     values.  Returns (tokens [B,H,n,d] as a Tensor, centres [H,k,d] float32
     values).
 
     Each token draws its group c with probability proportional to a weight in
-    [0.7, 1.3] per (head, group), so groups are unequal in size.  The j-th
-    token of a group (in a seeded random order) is 2 * (cos(a) m_c + sin(a) u),
-    with cos(a) = 0.995 - spacing * j and u a random unit vector orthogonal to
-    the centre m_c, so the cosines inside a group are `spacing` apart."""
+    [0.7, 1.3] per (head, group) (or to `weights` [k], the same for every head),
+    so groups are unequal in size.  The j-th token of a group (in a seeded
+    random order) is 2 * (cos(a) m_c + sin(a) u), with
+    cos(a) = 0.995 - spacing * j and u a random unit vector orthogonal to the
+    centre m_c, so the cosines inside a group are `spacing` apart (a group must
+    hold fewer than 0.4 / spacing tokens for them to stay nearest their own
+    centre)."""
     mu = unit_rows_f32(seed, H * k, d).reshape(H, k, d)
     weight = 0.7 + 0.6 * uniform01(seed + 1, H * k).reshape(H, k)
+    if weights is not None:
+        weight = np.broadcast_to(np.asarray(weights, dtype=np.float64), (H, k))
     u_lab = uniform01(seed + 2, B * H * n).reshape(B, H, n)
     order_keys = splitmix64(seed + 3, B * H * n).reshape(B, H, n)
     g = normal(seed + 4, (B, H, n, d))

@@ -217,6 +217,29 @@ def test_route_partition_separated_exact(rt, orc, name):
     np.testing.assert_array_equal(got, orc.route_partition(x.value, mu0))
 
 
+SKEWED = {
+    # name: (B, H, n, d, k, weight of group 0 against 1 for the others)
+    "one_large_group": (1, 2, 4096, 64, 16, 20.0),
+    "nearly_all_one_group": (1, 1, 4096, 64, 16, 1000.0),
+}
+
+
+@pytest.mark.parametrize("name", list(SKEWED))
+def test_route_partition_skewed_groups(rt, orc, name):
+    """Most tokens nearest one centroid: that group holds thousands of members,
+    so ranking them inside the group spans several tiles of members and several
+    rounds of them per thread.  Every token must sit in a cluster its oracle
+    rank allows, on every (batch, head)."""
+    B, H, n, d, k, w0 = SKEWED[name]
+    say(f"[case] partition skewed {name}")
+    weights = np.ones(k)
+    weights[0] = w0
+    x, mu0 = S.separated_tokens(98_000 + 10 * list(SKEWED).index(name), B, H, n, d, k,
+                                spacing=0.3 / n, weights=weights)
+    got, pinned, free = run_partition(rt, orc, x, mu0, name)
+    assert pinned >= 0.9 * B * H * n
+
+
 def test_partition_clusters_feed_routed_attention(rt, orc):
     """Partition clusters are ordinary memberships: routed attention on the
     device's partition against the oracle's attention on the same partition."""
