@@ -22,10 +22,10 @@
 //                       the caller passes the mask rt_route produced).
 //   cluster_attn_bf16   one workgroup per cluster.  Every member row of the
 //                       keys (raw bf16) and values is requested from memory at
-//                       once (the row index straight from idx); keys are
-//                       staged in LDS, values stay in flight while the first
-//                       query block's logits are computed, then are stored
-//                       transposed.  Each wave takes 16-row query blocks in a
+//                       once, in two round trips (all row indices, then all
+//                       rows); keys are staged in LDS, values stay in flight
+//                       while the first query block's logits are computed, then
+//                       are stored transposed.  Each wave takes 16-row query blocks in a
 //                       zig-zag order that balances the causal triangle,
 //                       computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
 //                       (each lane owns one query, so the row statistics are

@@ -27,6 +27,9 @@
 // tiles through ds_read_b64_tr_b16.  Output rows follow the forward's
 // destinations: a token held by one cluster is written directly, otherwise
 // its rank slot is, and the combine step sums the slots in centroid order.
+// With shared queries and keys the caller may take dq^ + dk^ as one gradient
+// (dk == nullptr): a wave keeps phase A's dq^ rows in registers and adds phase
+// B's dk^ rows of the same block to them before the one store.
 #include "rt_common.hpp"
 #include "rt_internal.hpp"
 

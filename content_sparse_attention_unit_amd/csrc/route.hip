@@ -9,7 +9,7 @@
 // far less than the attention itself.
 //
 // Kernels
-//   score_bf16_kernel  one workgroup = 128 tokens x all centroids of a head.
+//   score_bf16_kernel  one workgroup = 256 tokens x all centroids of a head.
 //                      The raw bf16 token rows are the B operand of
 //                      v_mfma_f32_16x16x32_bf16 straight from HBM; the fp32
 //                      centroids are split into three bf16 terms in LDS
@@ -23,6 +23,10 @@
 //                      LDS), then a position-ordered compaction with wave
 //                      ballots, so the w members come out sorted by position
 //                      with ties taken at the lowest positions.
+//   part_group_kernel, part_rank_kernel, part_emit_kernel
+//                      partition-style routing (every token in one cluster):
+//                      group by nearest centroid, rank inside the group,
+//                      list each cluster by position.
 #include <type_traits>
 
 #include "rt_common.hpp"
