@@ -42,7 +42,7 @@ CLUSTER_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "0653b88d20269d0679f84eb4dc9634e2fb0baccfae6fb4f25df5d8198c998996",
+    "sha256": "870fe3c0f93867129a0370b79594d4257b5c6895d1bb8ea4d5eb4dc489a432c6",
     "fetch_kib": 11017.715, "write_kib": 26950.653,
     "fetch_scale": 262144.0 / 131088.0, "write_scale": 262144.0 / 262144.0,
 }
