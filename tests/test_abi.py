@@ -89,6 +89,36 @@ def test_route_noalloc_validation(lib, kw, code, msg):
     assert msg in _last(lib)
 
 
+def route_partition(lib, qk=FAKE, dtype=1, mu=FAKE, B=1, H=1, n=64, d=16, k=4, inv=FAKE,
+                    idx=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return lib.rt_route_partition(qk, dtype, mu, B, H, n, d, k, inv, idx, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(qk=None), RT_EINVAL, "null"),
+    (dict(idx=None), RT_EINVAL, "null"),
+    (dict(k=0), RT_EINVAL, "positive"),
+    (dict(k=257, n=257 * 4), RT_EUNSUPPORTED, "k=257"),
+    (dict(n=100, k=8), RT_EINVAL, "multiple"),
+    (dict(n=32768, k=64), RT_EUNSUPPORTED, "exceeds 16384"),
+    (dict(ws=None), RT_EINVAL, "workspace"),
+    (dict(ws_bytes=64 * 16 + 5 * 4 - 1), RT_EINVAL, "workspace"),
+    (dict(d=48), RT_EUNSUPPORTED, "d=48"),
+])
+def test_route_partition_validation(lib, kw, code, msg):
+    """Checked on the host before anything is launched: n a multiple of k,
+    n <= 16384, k <= 256, and the workspace rt_workspace_bytes names."""
+    assert route_partition(lib, **kw) == code
+    assert msg in _last(lib)
+
+
+def test_route_partition_workspace(lib):
+    # label, best, group list and cluster per token (4 bytes each), then k + 1
+    # group offsets per (batch, head)
+    B, H, n, d, k = 2, 3, 8192, 128, 64
+    assert lib.rt_workspace_bytes(7, B, H, n, d, k, 1) == B * H * n * 16 + B * H * (k + 1) * 4
+
+
 def test_route_noalloc_limit_matches_header():
     import content_sparse_attention_unit_amd as rt
     text = open(HEADER).read()
