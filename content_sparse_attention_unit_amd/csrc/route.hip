@@ -829,52 +829,65 @@ __global__ __launch_bounds__(kPartThreads) void part_group_kernel(const int32_t*
 constexpr int kRankThreads = 256;
 constexpr int kRankTile = 1024;   // group members staged in LDS at a time
 
+// A member's place in its group's order as one unsigned 64-bit number: the
+// order-preserving score key above the complemented position, so that a
+// larger number means a higher score, or an equal one at a lower position.
+__device__ __forceinline__ unsigned long long rank_key(float score, int pos) {
+    return ((unsigned long long)order_key(score) << 32) | (unsigned long long)(~(uint32_t)pos);
+}
+
 __global__ __launch_bounds__(kRankThreads) void part_rank_kernel(
     const float* __restrict__ best, const int32_t* __restrict__ grp,
     const int32_t* __restrict__ goff, int n, int k, int w, int KW, int32_t* __restrict__ cl,
     uint32_t* __restrict__ mask) {
-    __shared__ uint32_t skey[kRankTile];
-    __shared__ int spos[kRankTile];
+    constexpr int PER = kRankTile / kRankThreads;
+    __shared__ __attribute__((aligned(16))) unsigned long long skey[kRankTile + 2];
     const int c = blockIdx.x;
     const long bh = blockIdx.y, base = bh * n;
     const int32_t* go = goff + bh * (k + 1);
     const int g0 = go[c], m = go[c + 1] - g0;
     for (int i0 = 0; i0 < m; i0 += kRankThreads) {
         const int i = i0 + (int)threadIdx.x;
-        const int tok = i < m ? grp[base + g0 + i] : 0;
-        const uint32_t key = i < m ? order_key(best[base + tok]) : 0u;
-        int before = 0;   // members before this one: higher score, or equal and earlier
+        // this member's key: from the first tile when the group fits one,
+        // else read for itself
+        unsigned long long mine = 0ull;
+        if (m > kRankTile && i < m) {
+            const int t = grp[base + g0 + i];
+            mine = rank_key(best[base + t], t);
+        }
+        int before = 0;   // members with a larger key
         for (int j0 = 0; j0 < m; j0 += kRankTile) {
             const int jn = min(kRankTile, m - j0);
             __syncthreads();   // the previous tile is no longer read
-            int tj[kRankTile / kRankThreads];
+            // (indices clamped into the tile, so that every load is issued
+            // unconditionally and none waits for the one before it)
+            int tj[PER];
 #pragma unroll
-            for (int u = 0; u < kRankTile / kRankThreads; ++u) {
-                const int j = (int)threadIdx.x + kRankThreads * u;
-                tj[u] = j < jn ? grp[base + g0 + j0 + j] : 0;
+            for (int u = 0; u < PER; ++u) {
+                const int j = min((int)threadIdx.x + kRankThreads * u, jn - 1);
+                tj[u] = grp[base + g0 + j0 + j];
             }
-            float bj[kRankTile / kRankThreads];
+            float bj[PER];
 #pragma unroll
-            for (int u = 0; u < kRankTile / kRankThreads; ++u) {
-                const int j = (int)threadIdx.x + kRankThreads * u;
-                bj[u] = j < jn ? best[base + tj[u]] : 0.f;
-            }
+            for (int u = 0; u < PER; ++u) bj[u] = best[base + tj[u]];
 #pragma unroll
-            for (int u = 0; u < kRankTile / kRankThreads; ++u) {
+            for (int u = 0; u < PER; ++u) {
                 const int j = (int)threadIdx.x + kRankThreads * u;
-                if (j < jn) {
-                    skey[j] = order_key(bj[u]);
-                    spos[j] = tj[u];
-                }
+                if (j < jn) skey[j] = rank_key(bj[u], tj[u]);
             }
+            // padding past the tile: 0 is below every member's key
+            if (threadIdx.x < 2) skey[jn + threadIdx.x] = 0ull;
             __syncthreads();
-            if (i < m)
-                for (int j = 0; j < jn; ++j) {
-                    const uint32_t kj = skey[j];
-                    before += (kj > key || (kj == key && spos[j] < tok)) ? 1 : 0;
+            if (m <= kRankTile && i < m) mine = skey[i];
+            if (i < m) {
+                for (int j = 0; j < jn; j += 2) {
+                    const ulonglong2 kj = *reinterpret_cast<const ulonglong2*>(&skey[j]);
+                    before += (kj.x > mine ? 1 : 0) + (kj.y > mine ? 1 : 0);
                 }
+            }
         }
         if (i < m) {
+            const int tok = (int)~(uint32_t)(mine & 0xffffffffull);
             const int clu = (g0 + before) / w;
             cl[base + tok] = clu;
             if (mask != nullptr) mask[(base + tok) * KW + (clu >> 5)] = 1u << (clu & 31);
