@@ -68,54 +68,81 @@ __device__ __forceinline__ const void* op_addr(const GemmOperand& o, int idx, in
     return static_cast<const char*>(o.p[s]) + off * esz;
 }
 
-// Eight consecutive elements along the operand's contiguous direction, as bf16.
+// Eight consecutive elements along the operand's contiguous direction, as
+// loaded: bf16 as they are, float32 kept whole until the tile is stored to LDS
+// (rounding them at the load would make the load wait, before the products of
+// the tile in LDS, for data that has a whole contraction step to arrive).
+template <bool F32> struct Chunk8;
+template <> struct Chunk8<false> { uint4 v; };
+template <> struct Chunk8<true> { float4 a, b; };
+
 template <bool F32>
-__device__ __forceinline__ uint4 load8(const void* p, bool ok) {
-    if (!ok) return zero_u4();
+__device__ __forceinline__ Chunk8<F32> load8(const void* p) {
     if constexpr (F32) {
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *(reinterpret_cast<const float4*>(p) + 1);
-        return make_uint4(cvt_pk_bf16(a.x, a.y), cvt_pk_bf16(a.z, a.w), cvt_pk_bf16(b.x, b.y),
-                          cvt_pk_bf16(b.z, b.w));
+        return Chunk8<true>{*reinterpret_cast<const float4*>(p),
+                            *(reinterpret_cast<const float4*>(p) + 1)};
     } else {
-        return *reinterpret_cast<const uint4*>(p);
+        return Chunk8<false>{*reinterpret_cast<const uint4*>(p)};
+    }
+}
+
+template <bool F32>
+__device__ __forceinline__ uint4 as_bf16x8_bits(const Chunk8<F32>& c) {
+    if constexpr (F32) {
+        return make_uint4(cvt_pk_bf16(c.a.x, c.a.y), cvt_pk_bf16(c.a.z, c.a.w),
+                          cvt_pk_bf16(c.b.x, c.b.y), cvt_pk_bf16(c.b.z, c.b.w));
+    } else {
+        return c.v;
     }
 }
 
 constexpr bool k_contig(int mode) { return mode == OP_KC_RM || mode == OP_KC_HM; }
 
+// Element (idx, k) of chunk `it` of this thread in a ROWS x 64 operand tile.
+template <int MODE, int ROWS, int NT>
+__device__ __forceinline__ void chunk_pos(int it, int idx0, int k0, int& idx, int& k) {
+    const int e = threadIdx.x + NT * it;
+    if constexpr (k_contig(MODE)) {
+        idx = idx0 + e / 8;
+        k = k0 + 8 * (e % 8);
+    } else {
+        idx = idx0 + 8 * (e % (ROWS / 8));
+        k = k0 + e / (ROWS / 8);
+    }
+}
+
 // One ROWS x 64 operand tile (rows idx0.., contraction k0..) into registers,
-// NT threads, CPT = ROWS * 8 / NT chunks of eight elements each.
+// NT threads, CPT = ROWS * 8 / NT chunks of eight elements each.  Addresses
+// are clamped into the operand so that every load is issued unconditionally;
+// chunks outside it are zeroed by tile_store.
 template <int MODE, bool F32, int ROWS, int NT, int CPT>
 __device__ __forceinline__ void tile_load(const GemmOperand& o, int idx0, int nidx, int k0, int K,
-                                          int n, int d, uint4 (&r)[CPT]) {
+                                          int n, int d, Chunk8<F32> (&r)[CPT]) {
     static_assert(ROWS * 8 == NT * CPT, "whole chunks per thread");
+#pragma unroll
+    for (int it = 0; it < CPT; ++it) {
+        int idx, k;
+        chunk_pos<MODE, ROWS, NT>(it, idx0, k0, idx, k);
+        // the eight elements run along k (k-contiguous) or along idx
+        const int ic = k_contig(MODE) ? min(idx, nidx - 1) : max(0, min(idx, nidx - 8));
+        const int kc = k_contig(MODE) ? max(0, min(k, K - 8)) : min(k, K - 1);
+        r[it] = load8<F32>(op_addr<MODE, F32>(o, ic, kc, n, d));
+    }
+}
+
+template <int MODE, bool F32, int ROWS, int NT, int CPT>
+__device__ __forceinline__ void tile_store(u16* t, const Chunk8<F32> (&r)[CPT], int idx0, int nidx,
+                                           int k0, int K) {
 #pragma unroll
     for (int it = 0; it < CPT; ++it) {
         const int e = threadIdx.x + NT * it;
         int idx, k;
-        if constexpr (k_contig(MODE)) {
-            idx = idx0 + e / 8;
-            k = k0 + 8 * (e % 8);
-        } else {
-            idx = idx0 + 8 * (e % (ROWS / 8));
-            k = k0 + e / (ROWS / 8);
-        }
-        const bool ok = idx < nidx && k < K;
-        r[it] = load8<F32>(ok ? op_addr<MODE, F32>(o, idx, k, n, d) : nullptr, ok);
-    }
-}
-
-template <int MODE, int ROWS, int NT, int CPT>
-__device__ __forceinline__ void tile_store(u16* t, const uint4 (&r)[CPT]) {
-#pragma unroll
-    for (int it = 0; it < CPT; ++it) {
-        const int e = threadIdx.x + NT * it;
+        chunk_pos<MODE, ROWS, NT>(it, idx0, k0, idx, k);
+        const uint4 v = idx < nidx && k < K ? as_bf16x8_bits<F32>(r[it]) : zero_u4();
         if constexpr (k_contig(MODE))
-            *reinterpret_cast<uint4*>(&t[(e / 8) * GPLD + 8 * (e % 8)]) = r[it];
+            *reinterpret_cast<uint4*>(&t[(e / 8) * GPLD + 8 * (e % 8)]) = v;
         else
-            *reinterpret_cast<uint4*>(&t[(e / (ROWS / 8)) * gldi<ROWS>() + 8 * (e % (ROWS / 8))]) =
-                r[it];
+            *reinterpret_cast<uint4*>(&t[(e / (ROWS / 8)) * gldi<ROWS>() + 8 * (e % (ROWS / 8))]) = v;
     }
 }
 
@@ -161,7 +188,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(GemmArgs p) {
     const int g = lane >> 4, r16 = lane & 15;
     const int wm = wv / WN, wn = wv % WN;
 
-    uint4 ra[G::ACPT], rb[G::BCPT];
+    Chunk8<AF> ra[G::ACPT];
+    Chunk8<BF> rb[G::BCPT];
     // [n block][m block]: C^T rows n0 + TN wn + 16ni + 4g + i, col m0 + TM wm + 16mi + r16
     f32x4 acc[G::NI][G::MI];
 #pragma unroll
@@ -176,8 +204,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(GemmArgs p) {
     const int nk = min(nk_all, kt0 + per);
     tile_load<AM, AF, TBM, NT>(p.a, m0, p.M, kt0 * GBK, p.K, p.n, p.d, ra);
     tile_load<BM, BF, TBN, NT>(p.b, n0, p.N, kt0 * GBK, p.K, p.n, p.d, rb);
-    tile_store<AM, TBM, NT>(la[0], ra);
-    tile_store<BM, TBN, NT>(lb[0], rb);
+    tile_store<AM, AF, TBM, NT>(la[0], ra, m0, p.M, kt0 * GBK, p.K);
+    tile_store<BM, BF, TBN, NT>(lb[0], rb, n0, p.N, kt0 * GBK, p.K);
     __syncthreads();
     for (int kt = kt0; kt < nk; ++kt) {
         const int buf = (kt - kt0) & 1;
@@ -198,14 +226,28 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(GemmArgs p) {
                 for (int mi = 0; mi < G::MI; ++mi) acc[ni][mi] = mfma16(fb[ni], fa[mi], acc[ni][mi]);
         }
         if (kt + 1 < nk) {
-            tile_store<AM, TBM, NT>(la[buf ^ 1], ra);
-            tile_store<BM, TBN, NT>(lb[buf ^ 1], rb);
+            tile_store<AM, AF, TBM, NT>(la[buf ^ 1], ra, m0, p.M, (kt + 1) * GBK, p.K);
+            tile_store<BM, BF, TBN, NT>(lb[buf ^ 1], rb, n0, p.N, (kt + 1) * GBK, p.K);
             __syncthreads();
         }
     }
 
     // Epilogue: lane holds C[m][n .. n+3] for m = m0 + TM wm + 16mi + r16,
-    // n = n0 + TN wn + 16ni + 4g.
+    // n = n0 + TN wn + 16ni + 4g.  The residual's elements are all requested
+    // first (addresses clamped into it, so no load sits under a branch), then
+    // added: one memory round trip rather than one per block.
+    const bool with_res = CM == 0 && p.ksplit <= 1 && p.res != nullptr;
+    uint2 rres[G::MI][G::NI];
+    if (with_res) {
+#pragma unroll
+        for (int mi = 0; mi < G::MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < G::NI; ++ni) {
+                const int m = min(m0 + G::TM * wm + 16 * mi + r16, p.M - 1);
+                const int nn = min(n0 + G::TN * wn + 16 * ni + 4 * g, p.N - 4);
+                rres[mi][ni] = *reinterpret_cast<const uint2*>(p.res + (long)m * p.N + nn);
+            }
+    }
 #pragma unroll
     for (int mi = 0; mi < G::MI; ++mi) {
         const int m = m0 + G::TM * wm + 16 * mi + r16;
@@ -219,8 +261,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(GemmArgs p) {
                 store4<float>(p.part + ((long)blockIdx.z * p.M + m) * p.N + nn, c0, c1, c2, c3);
             } else if constexpr (CM == 0) {
                 const long off = (long)m * p.N + nn;
-                if (p.res != nullptr) {
-                    const uint2 rr = *reinterpret_cast<const uint2*>(p.res + off);
+                if (with_res) {
+                    const uint2 rr = rres[mi][ni];
                     c0 += bf2f((u16)(rr.x & 0xffffu));
                     c1 += bf2f((u16)(rr.x >> 16));
                     c2 += bf2f((u16)(rr.y & 0xffffu));

@@ -140,7 +140,22 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void proj_kernel(ProjArgs p) {
     }
 
     // Epilogue: lane holds C[m][n .. n+3] for m = m0 + TM wm + 16 mi + r16,
-    // n = n0 + TN wn + 16 ni + 4 g.
+    // n = n0 + TN wn + 16 ni + 4 g.  The residual's elements are all requested
+    // first (addresses clamped into it, so no load sits under a branch), then
+    // added: one memory round trip rather than one per block.
+    const bool with_res = CMODE == 0 && p.res != nullptr;
+    uint2 rres[C::MI][C::NI];
+    if (with_res) {
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni) {
+                const int m = min(m0 + C::TM * wm + 16 * mi + r16, p.M - 1);
+                const int nn = min(n0 + C::TN * wn + 16 * ni + 4 * g, p.N - 4);
+                rres[mi][ni] = *reinterpret_cast<const uint2*>(static_cast<const u16*>(p.res) +
+                                                               (long)m * p.N + nn);
+            }
+    }
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
         const int m = m0 + C::TM * wm + 16 * mi + r16;
@@ -152,8 +167,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void proj_kernel(ProjArgs p) {
             float c0 = acc[ni][mi][0], c1 = acc[ni][mi][1], c2 = acc[ni][mi][2], c3 = acc[ni][mi][3];
             if constexpr (CMODE == 0) {
                 const long off = (long)m * p.N + nn;
-                if (p.res != nullptr) {
-                    const uint2 rr = *reinterpret_cast<const uint2*>(static_cast<const u16*>(p.res) + off);
+                if (with_res) {
+                    const uint2 rr = rres[mi][ni];
                     c0 += bf2f((u16)(rr.x & 0xffffu));
                     c1 += bf2f((u16)(rr.x >> 16));
                     c2 += bf2f((u16)(rr.y & 0xffffu));
