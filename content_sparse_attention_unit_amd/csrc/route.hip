@@ -354,6 +354,26 @@ __device__ __forceinline__ uint32_t row16_reduce_u32(uint32_t x) {
 }
 #undef RT_DPP
 
+// Inclusive prefix sum over the 64 lanes of a wave on the DPP network: a
+// scan inside each row of 16 lanes, then the totals of the rows below added
+// (read with readlane).  No LDS round trips.
+__device__ __forceinline__ uint32_t wave_prefix_u32(uint32_t x, uint32_t& total) {
+#define RT_DPP_SHR(v, n) (uint32_t) __builtin_amdgcn_update_dpp(0, (int)(v), 0x110 + (n), 0xf, 0xf, true)
+    x += RT_DPP_SHR(x, 1);
+    x += RT_DPP_SHR(x, 2);
+    x += RT_DPP_SHR(x, 4);
+    x += RT_DPP_SHR(x, 8);
+#undef RT_DPP_SHR
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    const int row = lane_id() >> 4;
+    x += (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+    total = r0 + r1 + r2 + r3;
+    return x;
+}
+
 // Each wave finds for itself, in a shared 256-bin histogram, the bin holding
 // the `remaining`-th largest key: every lane gets the bin and the rank left
 // inside it (no barrier needed after it).
@@ -364,13 +384,9 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t rem
     const uint4 c4 = *reinterpret_cast<const uint4*>(hist + 4 * lane);
     const uint32_t cnt[4] = {c4.x, c4.y, c4.z, c4.w};
     const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-    uint32_t suf = tot;   // inclusive suffix sum over lanes
-#pragma unroll
-    for (int dl = 1; dl < kWave; dl <<= 1) {
-        const uint32_t o = __shfl_down(suf, dl);
-        if (lane + dl < kWave) suf += o;
-    }
-    uint32_t above = suf - tot;
+    uint32_t all;
+    const uint32_t incl = wave_prefix_u32(tot, all);
+    uint32_t above = all - incl;   // keys in the bins of the lanes above this one
     int fb = -1;
     uint32_t fr = 0u;
 #pragma unroll
@@ -383,8 +399,8 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t rem
     }
     const uint64_t m = __ballot(fb >= 0);
     const int src = m ? __builtin_ctzll(m) : 0;
-    bin = (uint32_t)__shfl(fb, src);
-    rem = (uint32_t)__shfl((int)fr, src);
+    bin = (uint32_t)__builtin_amdgcn_readlane(fb, src);
+    rem = (uint32_t)__builtin_amdgcn_readlane((int)fr, src);
 }
 
 // Balanced top-w of one row of n scores; one workgroup per row.  Key j of
