@@ -202,7 +202,7 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
         int pos = -1, dest = -2;
         if (qok) {
             pos = raw;
-            dest = dest_from_words(wd, cl);
+            dest = dest_from_words(wd, cl, KW);
             if (dest >= kSlots) dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + orow;
         }
         if (orow < WMAX) {
@@ -291,6 +291,9 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
         const int kend = !active ? 0 : (causal ? min(w, qb * 16 + 16) : w);
         // keys below `clean` are visible to every query of the block
         const int clean = causal ? qb * 16 : w;
+        // this lane's last visible key (the row's last, or its own under
+        // causality), less the lane's key offset 4 g
+        const int glim = (causal ? min(qrow, w - 1) : w - 1) - 4 * g;
 
         for (int kc = 0; kc < kend || !values_staged; kc += 64) {
             f32x4 sv[4];
@@ -328,14 +331,12 @@ __global__ __launch_bounds__((AttnCfg<D, WMAX, SHARED>::NT), 2) void cluster_att
                 if (kc >= kend) break;
             }
             if (kc + 64 > clean) {  // chunk reaches the diagonal or the tail: mask
+                // key kc + 16 kb + 4 g + i is visible iff kc + 16 kb + i <= glim
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = kc + 16 * kb + 4 * g + i;
-                        const bool ok = key < w && (!causal || key <= qrow);
-                        sv[kb][i] = ok ? sv[kb][i] : -INFINITY;
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        sv[kb][i] = (kc + 16 * kb + i <= glim) ? sv[kb][i] : -INFINITY;
             }
             const int halves = 1 | ((kc + 32 < kend) ? 2 : 0);
             softmax_pv_chunk<C::NJ, C::LDX>(sv, m, zacc, o, &lv[kc * C::LDX], r16, g, halves);

@@ -183,7 +183,7 @@ __global__ __launch_bounds__((BwdCfg<D, WMAX, SHARED>::NT)) void cluster_attn_bw
         return [=]() {
             int dest = -2;
             if (tok) {
-                dest = dest_from_words(wd, cl);
+                dest = dest_from_words(wd, cl, KW);
                 if (dest >= kSlots)
                     out.dir[(tokbase + raw) * (k - kSlots) + (dest - kSlots)] = cl * w + r;
             }

@@ -25,15 +25,6 @@
 namespace rt {
 namespace {
 
-// max of three floats in one instruction.  Written out because fmaxf on the
-// MFMA results makes the compiler quiet each operand first (they are not known
-// to be canonical), which costs an instruction per value.
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
 // softmax_pv_half on unscaled logits: the scale enters as one fma with the
 // reference, exp2(s * sl2 - m), and the chunk maximum is scaled once (sl2 > 0).
 // The fma does not round s * sl2 while m is the rounded product, so for the
@@ -45,9 +36,9 @@ template <int NJ, int LDX>
 __device__ __forceinline__ void softmax_pv_half_unscaled(f32x4 (&sv)[2], float sl2, float& m,
                                                          f32x4& zacc, f32x4 (&o)[NJ],
                                                          const u16* lv, int r16, int g) {
-    const float r1 = max3f(sv[0][0], sv[0][1], sv[0][2]);
-    const float r2 = max3f(sv[0][3], sv[1][0], sv[1][1]);
-    const float lmax = sl2 * max3f(max3f(sv[1][2], sv[1][3], r1), r2, r2);
+    const float r1 = max3_logits(sv[0][0], sv[0][1], sv[0][2]);
+    const float r2 = max3_logits(sv[0][3], sv[1][0], sv[1][1]);
+    const float lmax = sl2 * max3_logits(max3_logits(sv[1][2], sv[1][3], r1), r2, r2);
     lazy_rescale<NJ>(lmax, m, zacc, o);
     const float nm = (m == -INFINITY) ? 0.f : -m;
     uint32_t pw[2][2];

@@ -149,11 +149,25 @@ __device__ __forceinline__ bf16x8 bf16_ones() {
     return as_bf16x8(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 }
 
+// Maximum of three floats in one v_max3_f32.  Written out because the
+// compiler quiets every operand it cannot prove a non-signalling value (the
+// logits come from MFMA results) with an extra v_max each; the logits here are
+// finite or -inf.
+__device__ __forceinline__ float max3_logits(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float max16(const f32x4 (&sv)[4]) {
-    return fmaxf(fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
-                       fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3]))),
-                 fmaxf(fmaxf(fmaxf(sv[2][0], sv[2][1]), fmaxf(sv[2][2], sv[2][3])),
-                       fmaxf(fmaxf(sv[3][0], sv[3][1]), fmaxf(sv[3][2], sv[3][3]))));
+    const float r1 = max3_logits(sv[0][0], sv[0][1], sv[0][2]);
+    const float r2 = max3_logits(sv[0][3], sv[1][0], sv[1][1]);
+    const float r3 = max3_logits(sv[1][2], sv[1][3], sv[2][0]);
+    const float r4 = max3_logits(sv[2][1], sv[2][2], sv[2][3]);
+    const float r5 = max3_logits(sv[3][0], sv[3][1], sv[3][2]);
+    const float r6 = max3_logits(r1, r2, r3);
+    const float r7 = max3_logits(r4, r5, sv[3][3]);
+    return max3_logits(r6, r7, r7);
 }
 
 // Online-softmax step shared by the attention kernels.  `sv[kb][i]` holds the
@@ -224,13 +238,22 @@ __device__ __forceinline__ void load_words(buf_rsrc mrs, bool ok, int t, int KW,
     for (int i = 0; i < 8; ++i)
         wd[i] = buffer_load_u32(mrs, ok && i < KW ? 4u * (uint32_t)(t * KW + i) : kOutOfRange);
 }
-__device__ __forceinline__ int dest_from_words(const uint32_t (&wd)[8], int c) {
+__device__ __forceinline__ int dest_from_words(const uint32_t (&wd)[8], int c, int KW) {
     int cnt = 0, below = 0;
+    if (KW <= 2) {   // k <= 64 (wave-uniform): only the first two words can be set
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        cnt += __popc(wd[i]);
-        if (i < (c >> 5)) below += __popc(wd[i]);
-        else if (i == (c >> 5)) below += __popc(wd[i] & ((1u << (c & 31)) - 1u));
+        for (int i = 0; i < 2; ++i) {
+            cnt += __popc(wd[i]);
+            if (i < (c >> 5)) below += __popc(wd[i]);
+            else if (i == (c >> 5)) below += __popc(wd[i] & ((1u << (c & 31)) - 1u));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            cnt += __popc(wd[i]);
+            if (i < (c >> 5)) below += __popc(wd[i]);
+            else if (i == (c >> 5)) below += __popc(wd[i] & ((1u << (c & 31)) - 1u));
+        }
     }
     return cnt == 1 ? -1 : below;
 }
