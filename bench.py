@@ -42,9 +42,9 @@ CLUSTER_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "870fe3c0f93867129a0370b79594d4257b5c6895d1bb8ea4d5eb4dc489a432c6",
-    "fetch_kib": 11017.715, "write_kib": 26950.653,
-    "fetch_scale": 262144.0 / 131088.0, "write_scale": 262144.0 / 262144.0,
+    "sha256": "9c99f071b47f8aae69aeecd9efddb94033a56dba159cbd8ffe5092d94881d94f",
+    "fetch_kib": 11007.258, "write_kib": 26950.656,
+    "fetch_scale": 262144.0 / 131087.875, "write_scale": 262144.0 / 262144.0,
 }
 
 
