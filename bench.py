@@ -770,6 +770,26 @@ def main():
         del flush
         mu.copy_(mu0)
 
+        # The floor of one dependent launch on the GPU: a captured graph of 100
+        # one-element kernels, each waiting for the one before, replayed (so the
+        # host's launch rate is out of it).
+        tiny = torch.zeros(1, **f32)
+        tiny_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(tiny_graph, stream=stream):
+            for _ in range(100):
+                tiny.add_(1.0)
+        for _ in range(3):
+            tiny_graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            tiny_graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        launch_floor_ms = a.elapsed_time(b) / 500
+        del tiny_graph
+
     alg = algorithmic(cfg)
     tokens = B * n
 
@@ -844,6 +864,15 @@ def main():
                    "step": "rt_route -> rt_cluster_attn -> rt_scatter_rows (+ centroid update)"
                            + (" -> rt_routed_attn_bwd" if cfg.backward else "")},
         "roofline": roofline,
+        "launch_floor": {
+            "us_per_launch": launch_floor_ms * 1e3,
+            "launches_per_step": 4 + (2 if cfg.backward else 0),
+            "us_per_step": (4 + (2 if cfg.backward else 0)) * launch_floor_ms * 1e3,
+            "share_of_step": (4 + (2 if cfg.backward else 0)) * launch_floor_ms / ms_per_step,
+            "note": "a replayed graph of dependent one-element kernels: the least a dependent "
+                    "launch costs on the GPU; the step makes 4 (scoring, top-w, in-cluster attention, "
+                    "scatter with the centroid update)" + (" plus 2 for the backward"
+                                                           if cfg.backward else "")},
         "hbm_bound_ceiling_tokens_per_s": routed_ceiling,
         "frac_of_hbm_ceiling": tokens / (ms_per_step * 1e-3) / routed_ceiling,
         "layer": {"ms_per_step": layer_ms, "tokens_per_s": tokens / (layer_ms * 1e-3),
