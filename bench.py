@@ -62,6 +62,32 @@ def measured_traffic(rec, workload):
         return None
     return 1024.0 * (rec["fetch_kib"] * rec["fetch_scale"] + rec["write_kib"] * rec["write_scale"])
 
+# GPU clock cycles per microsecond of torch's spin kernel (torch.cuda._sleep),
+# calibrated at start-up.
+_SPIN_CYCLES_PER_US = 2370.0
+
+
+def calibrate_gpu_ahead():
+    global _SPIN_CYCLES_PER_US
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    a.record()
+    torch.cuda._sleep(400000)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3
+    if us > 0:
+        _SPIN_CYCLES_PER_US = 400000.0 / us
+
+
+def gpu_ahead(us):
+    """Keep the current stream busy for about `us` microseconds, so that the host
+    has enqueued the calls timed next before the GPU reaches them: back-to-back
+    and per-call times then measure the GPU, not the host's launch rate (the
+    binding's marshalling is several microseconds a call)."""
+    torch.cuda._sleep(max(1, int(us * _SPIN_CYCLES_PER_US)))
+
+
 WORKLOADS = {
     "long": "long: B=1, 8 routed heads (k=64, w=128) + 4 local heads (window 512), "
             "n=8192, d=128, bf16, causal, shared QK, EMA lambda=0.999",
@@ -311,6 +337,7 @@ def time_layer_bwd(rt, sc, stream, layer, x0, t, reps=10):
         for name, (fn, flops) in calls.items():
             for _ in range(3):
                 fn()
+            gpu_ahead(30 * reps)
             a.record(stream)
             for _ in range(reps):
                 fn()
@@ -375,6 +402,7 @@ def time_variants(rt, cfg, inp, reps=20):
     for name, fn in calls.items():
         for _ in range(3):
             fn()
+        gpu_ahead(30 * reps)
         a.record()
         for _ in range(reps):
             fn()
@@ -506,6 +534,7 @@ def run_sweep(rt, reps=20, only=None):
             for _ in range(3):
                 fn()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            gpu_ahead(30 * reps)
             a.record()
             for _ in range(reps):
                 fn()
@@ -544,6 +573,7 @@ def event_stats(fn, reps, stream, flush=None):
     for a, b in evs:
         if flush is not None:
             flush.fill_(1.0)
+        gpu_ahead(40)
         a.record(stream)
         fn()
         b.record(stream)
@@ -591,6 +621,7 @@ def main():
 
     import content_sparse_attention_unit_amd as rt
     rt._load()
+    calibrate_gpu_ahead()
 
     if args.sweep:
         only = {int(x) for x in args.sweep_n.split(",") if x}
@@ -759,6 +790,7 @@ def main():
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = max(20, args.steps)
+            gpu_ahead(30 * reps)
             a.record(stream)
             for _ in range(reps):
                 fn()

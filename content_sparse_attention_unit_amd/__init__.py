@@ -110,11 +110,19 @@ def _check(status: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """A tensor's device address for a c_void_p argument (ctypes takes the int)."""
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device) -> int:
+    """The current stream of ``device`` as a raw handle (torch's own accessor
+    when it has one: no Stream object per call)."""
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -126,7 +134,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _gpu(*ts):
-    dev = None
+    dev, idx = None, -1
     for t in ts:
         if t is None:
             continue
@@ -135,8 +143,8 @@ def _gpu(*ts):
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
         if dev is None:
-            dev = t.device
-        elif t.device != dev:
+            dev, idx = t.device, t.get_device()
+        elif t.get_device() != idx:
             raise ValueError("all tensors must be on the same device")
     return dev
 
@@ -146,7 +154,7 @@ def _expect(t, shape, dtype, what):
     kernels index these buffers by the shape arguments alone."""
     if t is None:
         return
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:                   # torch.Size is a tuple
         raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{what} has dtype {t.dtype}, expected {dtype}")
@@ -185,9 +193,11 @@ def workspace_bytes(op: str, B: int, H: int, n: int, d: int, k: int, w: int) -> 
 
 
 def _workspace(op, dev, B, H, n, d, k, w, ws=None):
-    need = workspace_bytes(op, B, H, n, d, k, w)
+    """``ws`` if given (the library checks its size against the call), else a
+    new one of rt_workspace_bytes bytes; returns (ws, bytes needed or None)."""
     if ws is not None:
-        return ws, need
+        return ws, None
+    need = workspace_bytes(op, B, H, n, d, k, w)
     if need == 0:
         return None, 0
     return torch.empty(need, dtype=torch.uint8, device=dev), need
@@ -695,7 +705,7 @@ def _bf16(*ts):
 
 
 def _shape(t, want, what):
-    if tuple(t.shape) != tuple(want):
+    if t.shape != tuple(want):
         raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(want)}")
 
 
