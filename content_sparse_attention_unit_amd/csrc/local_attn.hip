@@ -18,7 +18,9 @@
 // from the row-major tile) and an online softmax over its keys; at the end the
 // two partial softmax states of a block are merged through LDS.  Splitting the
 // keys halves each wave's serial chain and doubles the waves per SIMD.  Key
-// blocks outside a block's band are skipped.
+// blocks outside a block's band are skipped.  A wave raises its priority
+// while it issues a block of matrix products, so that its products go out
+// back to back while the other waves of its SIMD do vector work.
 #include "rt_common.hpp"
 #include "rt_internal.hpp"
 
@@ -62,6 +64,7 @@ __device__ __forceinline__ void softmax_pv_half_unscaled(f32x4 (&sv)[2], float s
     }
     const bf16x8 pbv = as_bf16x8(make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
     const u16* vb = lv + (4 * g + (r16 >> 2)) * LDX + 4 * (r16 & 3);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int jb = 0; jb < NJ; ++jb) {
         const uint2 lo = lds_read_tr16(vb + 16 * jb);
@@ -69,6 +72,7 @@ __device__ __forceinline__ void softmax_pv_half_unscaled(f32x4 (&sv)[2], float s
         o[jb] = mfma16(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pbv, o[jb]);
     }
     zacc = mfma16(bf16_ones(), pbv, zacc);
+    __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D>
@@ -205,6 +209,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
         if (kh_ + 31 >= blo && kh_ <= bhi) {               /* half meets the band */         \
             const u16* LK = lk[BUF] + 32 * hf * C::LDX;                                      \
             f32x4 sv[2];                                                                     \
+            __builtin_amdgcn_s_setprio(1);     /* products first, see the header */          \
             _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                               \
                 const int key0 = kh_ + 16 * kb;                                              \
                 if (key0 + 15 < blo || key0 > bhi || key0 >= n) {                            \
@@ -219,6 +224,7 @@ __global__ __launch_bounds__(1024) void local_attn_bf16_kernel(const u16* __rest
                 }                                                                            \
                 sv[kb] = acc;                          /* unscaled: sl2 enters in exp2 */  \
             }                                                                                \
+            __builtin_amdgcn_s_setprio(0);                                                   \
             if (kh_ < clo || kh_ + 31 > chi) {     /* not inside every band: mask */         \
                 const uint32_t rel0 = (uint32_t)(kh_ + 4 * g - qlo_m);                       \
                 _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
