@@ -94,6 +94,7 @@ WORKLOADS = {
     "mixed": "mixed: B=2, 8 routed heads (k=64, w=64) + 8 local heads (window 256), "
              "n=4096, d=64, bf16",
     "routed": "routed: B=4, 8 routed heads (k=32, w=32), n=1024, d=64, bf16",
+    "tiny": "tiny: B=1, 1 routed head (k=4, w=16), n=64, d=16, float32",
     "stress": "stress: B=1, 8 routed heads (k=128, w=256) + 8 local (window 256), "
               "n=32768, d=64, bf16, 10% skewed tokens, forward + in-cluster backward",
 }
