@@ -43,8 +43,8 @@ CLUSTER_TRAFFIC = {
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
     "sha256": "9c99f071b47f8aae69aeecd9efddb94033a56dba159cbd8ffe5092d94881d94f",
-    "fetch_kib": 11007.258, "write_kib": 26950.656,
-    "fetch_scale": 262144.0 / 131087.875, "write_scale": 262144.0 / 262144.0,
+    "fetch_kib": 11007.261, "write_kib": 26950.662,
+    "fetch_scale": 262144.0 / 131088.938, "write_scale": 262144.0 / 262144.0,
 }
 
 
