@@ -429,7 +429,13 @@ template <int NT, int KPT, bool TOPB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void topw_kernel(const float* __restrict__ scores, int n, int w,
                                                   int32_t* __restrict__ idx, int k,
                                                   uint32_t* __restrict__ mask, int KW) {
-    static_assert(NT >= 256 && NT % kWave == 0, "one thread per histogram bin");
+    static_assert(NT % kWave == 0, "whole waves");
+    // clears a 256-bin histogram (one bin a thread from 256 threads on)
+    auto zero_hist = [&](uint32_t* h) {
+#pragma unroll
+        for (int i = 0; i < (256 + NT - 1) / NT; ++i)
+            if (NT >= 256 ? threadIdx.x < 256 : true) h[threadIdx.x + NT * i] = 0u;
+    };
     constexpr int NWV = NT / kWave;
     constexpr int CW = kCandPerWave;
     __shared__ __attribute__((aligned(16))) uint2 cand[NWV][CW];   // (key, position)
@@ -498,7 +504,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         wtop[wv][3] = c23 & 0xffffu;
         wtop[wv][4] = c23 >> 16;
     }
-    if (threadIdx.x < 256) hist3[0][threadIdx.x] = 0u;
+    zero_hist(hist3[0]);
     __syncthreads();
 
     // 2. The row's four highest top bytes: lane v < NWV holds wave v's entry.
@@ -580,7 +586,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             if ((kc >> 24) == bin0) atomicAdd(&hist3[0][(kc >> 16) & 255u], 1u);
         }
         if (lane == 0) wcnt[wv] = ovf ? 0xffffffffu : cnt;
-        if (threadIdx.x < 256) hist3[1][threadIdx.x] = 0u;
+        zero_hist(hist3[1]);
     }
     __syncthreads();
     bool slow = !found;
@@ -600,7 +606,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
                     const uint32_t kc = cand[wv][i].x;
                     if ((kc & himask) == prefix) atomicAdd(&hist3[pass][(kc >> shift) & 255u], 1u);
                 }
-                if (threadIdx.x < 256) hist3[(pass + 1) % 3][threadIdx.x] = 0u;
+                zero_hist(hist3[(pass + 1) % 3]);
                 __syncthreads();
             }
             uint32_t b, r;
@@ -684,14 +690,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         himask = 0u;
         remaining = (uint32_t)w;
     }
-    if (threadIdx.x < 256) hist3[0][threadIdx.x] = 0u;
+    zero_hist(hist3[0]);
     __syncthreads();
     for (int shift = found ? 16 : 24, it = 0; shift >= 0; shift -= 8, ++it) {
         uint32_t* h = hist3[it % 3];
         for_keys([&](int, uint32_t kj) {
             if ((kj & himask) == prefix) atomicAdd(&h[(kj >> shift) & 255u], 1u);
         });
-        if (threadIdx.x < 256) hist3[(it + 1) % 3][threadIdx.x] = 0u;
+        zero_hist(hist3[(it + 1) % 3]);
         __syncthreads();
         uint32_t b, r;
         find_bin_wave(h, remaining, b, r);
@@ -1018,9 +1024,12 @@ hipError_t launch_partition(const int32_t* label, const float* best, int BH, int
 hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t* idx,
                        uint32_t* mask, hipStream_t s) {
     const int rows = BH * k;
-    if (n <= 256) launch_topw_k<256, 1>(scores, rows, n, w, idx, k, mask, s);
-    else if (n <= 512) launch_topw_k<256, 2>(scores, rows, n, w, idx, k, mask, s);
-    else if (n <= 1024) launch_topw_k<256, 4>(scores, rows, n, w, idx, k, mask, s);
+    // up to 1024 keys a row: one wave a row (its barriers cost next to
+    // nothing; four waves of 4 keys a lane measured 12.1 vs 11.8 us for the
+    // route of 4 x 8 rows of 1024 tokens)
+    if (n <= 256) launch_topw_k<64, 4>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 512) launch_topw_k<64, 8>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 1024) launch_topw_k<64, 16>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 2048) launch_topw_k<256, 8>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 4096) launch_topw_k<256, 16>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= kTopwRegisterRow) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
