@@ -37,6 +37,9 @@ namespace {
 
 // rows up to this many tokens keep all their keys in registers in topw_kernel
 constexpr int kTopwRegisterRow = 8192;
+// rows of up to 1024 keys take one wave each from this many rows on (one per
+// SIMD of the 256 CUs)
+constexpr int kTopwOneWaveRows = 1024;
 
 template <int D>
 struct ScoreCfg {
@@ -1024,12 +1027,18 @@ hipError_t launch_partition(const int32_t* label, const float* best, int BH, int
 hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t* idx,
                        uint32_t* mask, hipStream_t s) {
     const int rows = BH * k;
-    // up to 1024 keys a row: one wave a row (its barriers cost next to
-    // nothing; four waves of 4 keys a lane measured 12.1 vs 11.8 us for the
-    // route of 4 x 8 rows of 1024 tokens)
-    if (n <= 256) launch_topw_k<64, 4>(scores, rows, n, w, idx, k, mask, s);
-    else if (n <= 512) launch_topw_k<64, 8>(scores, rows, n, w, idx, k, mask, s);
-    else if (n <= 1024) launch_topw_k<64, 16>(scores, rows, n, w, idx, k, mask, s);
+    // Up to 1024 keys a row and rows enough to give each of the chip's 1024
+    // SIMDs one: a single wave a row, whose barriers cost next to nothing
+    // (1024 rows of 1024 keys: route 12.0 -> 11.7 us).  Fewer rows keep four
+    // waves a row, which spread each row's chain over more of the chip (512
+    // rows: 10.1 us against 10.9 with one wave a row; 256 rows: 10.5 vs 11.0).
+    const bool one_wave = rows >= kTopwOneWaveRows;
+    if (one_wave && n <= 256) launch_topw_k<64, 4>(scores, rows, n, w, idx, k, mask, s);
+    else if (one_wave && n <= 512) launch_topw_k<64, 8>(scores, rows, n, w, idx, k, mask, s);
+    else if (one_wave && n <= 1024) launch_topw_k<64, 16>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 256) launch_topw_k<256, 1>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 512) launch_topw_k<256, 2>(scores, rows, n, w, idx, k, mask, s);
+    else if (n <= 1024) launch_topw_k<256, 4>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 2048) launch_topw_k<256, 8>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 4096) launch_topw_k<256, 16>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= kTopwRegisterRow) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
