@@ -426,8 +426,11 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t rem
 // last among equals and are never selected.
 constexpr int kCandPerWave = 512;
 
-// TOPB: only the keys' top bytes stay in registers (four to a register, for
-// 64 keys a lane); listed keys are re-read in full from the score row.
+// TOPB: only the keys' high halves stay in registers (two to a register, for
+// 32 or 64 keys a lane).  The lists carry those halves; once the first digit
+// pass over them has fixed the threshold's top 16 bits, the listed keys inside
+// that 16-bit bucket (a few a wave) are re-read in full from the score row.
+// The slow path re-reads every key it needs.
 template <int NT, int KPT, bool TOPB>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void topw_kernel(const float* __restrict__ scores, int n, int w,
                                                   int32_t* __restrict__ idx, int k,
@@ -462,8 +465,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     // 1. Keys.  Every load is issued unconditionally (a wave keeps them all in
     // flight); only a wave whose segment runs past the row checks positions.
     const buf_rsrc srs = make_rsrc(srow, 4u * (uint32_t)n);
-    constexpr int NKR = TOPB ? (KPT + 3) / 4 : KPT;
-    uint32_t key[NKR];   // the keys, or (TOPB) their top bytes
+    constexpr int NKR = TOPB ? (KPT + 1) / 2 : KPT;
+    uint32_t key[NKR];   // the keys, or (TOPB) their high halves
     uint32_t mw = 0u;
     auto load = [&](auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
@@ -476,8 +479,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             kj = in ? kj : 0u;
             mw = max(mw, kj);
             if constexpr (TOPB) {
-                if (j % 4 == 0) key[j / 4] = kj >> 24;
-                else key[j / 4] |= (kj >> 24) << (8 * (j % 4));
+                if (j % 2 == 0) key[j / 2] = kj >> 16;
+                else key[j / 2] |= kj & 0xffff0000u;
             } else {
                 key[j] = kj;
             }
@@ -485,10 +488,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     };
     if (seg0 + kWave * KPT <= n) load(std::false_type{});
     else load(std::true_type{});
-    auto top8 = [&](int j) -> uint32_t {
-        if constexpr (TOPB) return (key[j / 4] >> (8 * (j % 4))) & 0xffu;
-        else return key[j] >> 24;
+    // (TOPB) key j with its low half zero
+    auto hi16 = [&](int j) -> uint32_t {
+        if constexpr (TOPB) return (j % 2 == 0) ? key[j / 2] << 16 : key[j / 2] & 0xffff0000u;
+        else return key[j] & 0xffff0000u;
     };
+    auto top8 = [&](int j) -> uint32_t { return hi16(j) >> 24; };
     mw = wave_reduce_u32<true>(mw) >> 24;
     // 7-bit counters of the top bytes mw, mw-1, mw-2, mw-3 (bits 28.. take the
     // rest and may wrap); a lane holds at most 64 keys
@@ -557,33 +562,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             if (cnt + pc <= (uint32_t)CW) {
                 if (is)
                     cand[wv][cnt + (uint32_t)lanes_below(mb)] =
-                        make_uint2(TOPB ? 0u : key[TOPB ? 0 : j], (uint32_t)(pl + kWave * j));
+                        make_uint2(TOPB ? hi16(j) : key[TOPB ? 0 : j], (uint32_t)(pl + kWave * j));
             } else {
                 ovf = true;
             }
             cnt += pc;
         }
         nl = min(cnt, (uint32_t)CW);
-        if constexpr (TOPB) {
-            // the listed keys in full, from the score row (eight loads in flight)
-            for (uint32_t i0 = 0; i0 < nl; i0 += 8 * kWave) {
-                uint32_t pp[8], kv[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t i = i0 + (uint32_t)(u * kWave + lane);
-                    pp[u] = i < nl ? cand[wv][i].y : 0xffffffffu;
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    kv[u] = order_key(__uint_as_float(
-                        buffer_load4(srs, pp[u] < (uint32_t)n ? 4u * pp[u] : kOutOfRange)));
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t i = i0 + (uint32_t)(u * kWave + lane);
-                    if (i < nl) cand[wv][i].x = pp[u] < (uint32_t)n ? kv[u] : 0u;
-                }
-            }
-        }
         for (uint32_t i = lane; i < nl; i += kWave) {
             const uint32_t kc = cand[wv][i].x;
             if ((kc >> 24) == bin0) atomicAdd(&hist3[0][(kc >> 16) & 255u], 1u);
@@ -605,6 +590,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         for (int pass = pass0; pass < 3; ++pass) {
             const int shift = 16 - 8 * pass;
             if (pass > 0) {
+                if (TOPB && pass == 1 && pass0 == 0) {
+                    // lists of high halves: the entries in the threshold's
+                    // 16-bit bucket get their keys in full from the score row
+                    // (every load issued at once, out of range for the others)
+                    const uint32_t p16 = prefix & 0xffff0000u;
+                    static_assert(kCandPerWave <= 8 * kWave, "one round of loads covers a list");
+                    uint32_t pp[8], kv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const uint32_t i = (uint32_t)(u * kWave + lane);
+                        const uint2 e = i < nl ? cand[wv][i] : make_uint2(0u, 0u);
+                        pp[u] = (i < nl && (e.x & 0xffff0000u) == p16 && e.y < (uint32_t)n)
+                                    ? e.y : 0xffffffffu;
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        kv[u] = order_key(__uint_as_float(
+                            buffer_load4(srs, pp[u] != 0xffffffffu ? 4u * pp[u] : kOutOfRange)));
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (pp[u] != 0xffffffffu) cand[wv][(uint32_t)(u * kWave + lane)].x = kv[u];
+                }
                 for (uint32_t i = lane; i < nl; i += kWave) {
                     const uint32_t kc = cand[wv][i].x;
                     if ((kc & himask) == prefix) atomicAdd(&hist3[pass][(kc >> shift) & 255u], 1u);
