@@ -18,11 +18,13 @@
 //                      the token's inverse norm in fp32 afterwards.
 //   score_f32_kernel   the same on the vector ALUs for float32 inputs.
 //   topw_kernel        one workgroup per (batch, head, centroid) row of n
-//                      scores: an exact radix select of the w-th largest
-//                      order-preserving key (4 passes of 8 bits, histogram in
-//                      LDS), then a position-ordered compaction with wave
-//                      ballots, so the w members come out sorted by position
-//                      with ties taken at the lowest positions.
+//                      scores (a single wave for short rows when there are
+//                      enough of them): an exact radix select of the w-th
+//                      largest order-preserving key (8-bit digits, histograms
+//                      in LDS, mostly over short lists of the candidates),
+//                      then a position-ordered compaction with wave ballots,
+//                      so the w members come out sorted by position with ties
+//                      taken at the lowest positions.
 //   part_group_kernel, part_rank_kernel, part_emit_kernel
 //                      partition-style routing (every token in one cluster):
 //                      group by nearest centroid, rank inside the group,
@@ -1049,7 +1051,7 @@ hipError_t launch_topw(const float* scores, int BH, int n, int k, int w, int32_t
     else if (n <= 2048) launch_topw_k<256, 8>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 4096) launch_topw_k<256, 16>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= kTopwRegisterRow) launch_topw_k<512, 16>(scores, rows, n, w, idx, k, mask, s);
-    // beyond 8K keys a row, top bytes only: fewer registers, two rows a CU
+    // beyond 8K keys a row, the keys' high halves only: fewer registers, two rows a CU
     else if (n <= 16384) launch_topw_k<512, 32, true>(scores, rows, n, w, idx, k, mask, s);
     else if (n <= 32768) launch_topw_k<1024, 32, true>(scores, rows, n, w, idx, k, mask, s);
     else launch_topw_k<1024, 64, true>(scores, rows, n, w, idx, k, mask, s);
