@@ -353,8 +353,8 @@ def test_sweep_long_rows(rt, orc, n, k):
     say(f"[sweep] n={n}: {int(res['differs'].sum())} near-tie clusters differ")
 
 
-# Selection paths of the top-w kernel, for each place its keys live (registers
-# up to n = 16K, LDS up to 32K, 16-bit prefixes in LDS beyond): exact ties
+# Selection paths of the top-w kernel, for each place its keys live (full keys
+# in registers up to n = 8K, their high halves beyond): exact ties
 # (tokens drawn from a pool of 97 vectors), a threshold deep in a crowded top
 # byte (tokens close to one direction: more candidates than the short list
 # holds, even at 16-bit prefixes), a top byte too crowded for the short lists
@@ -365,21 +365,20 @@ TOPW_PATHS = {"ties": (97, None), "crowded": (None, 0.01), "refine": (None, 1.0)
               "median": (None, None)}
 
 
-@pytest.mark.parametrize("n", [3000, 20000, 40000, 65536])
-@pytest.mark.parametrize("kind", list(TOPW_PATHS))
-def test_topw_selection_paths(rt, orc, n, kind):
-    say(f"[topw] n={n} kind={kind}")
-    cid = 88 + list(TOPW_PATHS).index(kind)
-    d, k, H = 64, 2, 1
+def run_topw_case(rt, orc, n, kind, H, k, cid):
+    """One route call on inputs built to take `kind`'s selection path, checked
+    against the oracle: membership (margin rule), the bitmask, and for exact
+    ties the lowest positions taken."""
+    d = 64
     pool, spread = TOPW_PATHS[kind]
     if pool is not None:
         base_rows = S.normal(1000 * cid + 1, (pool, d))
-        val = base_rows[np.arange(n) % pool]
+        val = np.tile(base_rows[np.arange(n) % pool], (H, 1, 1))
     elif spread is not None:
         centre = S.normal(1000 * cid + 1, (1, d))
-        val = centre + spread * S.normal(1000 * cid + 2, (n, d))
+        val = centre + spread * S.normal(1000 * cid + 2, (H, n, d))
     else:
-        val = S.normal(1000 * cid + 1, (n, d))
+        val = S.normal(1000 * cid + 1, (H, n, d))
     qk_t = S.rounded(val.reshape(1, H, n, d), "bf16")
     mu_val = S.unit_rows_f32(1000 * cid + 3, H * k, d).reshape(H, k, d)
     if kind == "refine":
@@ -398,14 +397,30 @@ def test_topw_selection_paths(rt, orc, n, kind):
     if kind == "ties":
         # equal scores are taken in position order: the chosen set is the
         # lowest positions among the tokens tied at the threshold
+        xhat, _ = orc.normalize(qk_t.value[0, 0])
         for c in range(k):
-            xhat, _ = orc.normalize(qk_t.value[0, 0])
             s = orc.scores(xhat, mu_val[0, c:c + 1])[0]
             row = gidx[0, 0, c]
             thr = s[row].min()
             tied = np.flatnonzero(s == thr)
             taken = np.intersect1d(row, tied)
             assert np.array_equal(taken, tied[:len(taken)])
+
+
+@pytest.mark.parametrize("n", [3000, 20000, 40000, 65536])
+@pytest.mark.parametrize("kind", list(TOPW_PATHS))
+def test_topw_selection_paths(rt, orc, n, kind):
+    say(f"[topw] n={n} kind={kind}")
+    run_topw_case(rt, orc, n, kind, H=1, k=2, cid=88 + list(TOPW_PATHS).index(kind))
+
+
+@pytest.mark.parametrize("n", [1024, 777])
+@pytest.mark.parametrize("kind", list(TOPW_PATHS))
+def test_topw_selection_paths_one_wave(rt, orc, n, kind):
+    """The same paths where rows of up to 1024 keys, 1024 rows or more, take
+    one wave a row (16 heads of 64 centroids)."""
+    say(f"[topw one wave] n={n} kind={kind}")
+    run_topw_case(rt, orc, n, kind, H=16, k=64, cid=92 + list(TOPW_PATHS).index(kind))
 
 
 # Full-size workloads, in the launch configuration the benchmark times.
