@@ -42,9 +42,9 @@ CLUSTER_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "78e94ef4b7681e4a6560f6cb9dbdf1675a9e7c95fe1da388872ada999095d027",
-    "fetch_kib": 11007.253, "write_kib": 26950.658,
-    "fetch_scale": 262144.0 / 131095.938, "write_scale": 262144.0 / 262144.0,
+    "sha256": "ed0a7dffa23873d1bcb4609b127d81f00b9c6d669be4fd0b96042052aefda197",
+    "fetch_kib": 11007.270, "write_kib": 26950.658,
+    "fetch_scale": 262144.0 / 131095.312, "write_scale": 262144.0 / 262144.0,
 }
 
 
