@@ -42,9 +42,9 @@ CLUSTER_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "ed0a7dffa23873d1bcb4609b127d81f00b9c6d669be4fd0b96042052aefda197",
-    "fetch_kib": 11007.270, "write_kib": 26950.658,
-    "fetch_scale": 262144.0 / 131095.312, "write_scale": 262144.0 / 262144.0,
+    "sha256": "9849623676254ff5ddba929077b458600463d3bf6abd11be3165da442d0481bb",
+    "fetch_kib": 11007.239, "write_kib": 32218.937,
+    "fetch_scale": 262144.0 / 131096.312, "write_scale": 262144.0 / 262144.0,
 }
 
 
