@@ -42,9 +42,9 @@ CLUSTER_TRAFFIC = {
     "workload": "long",
     "sources": ["content_sparse_attention_unit_amd/csrc/cluster_attn.hip",
                 "content_sparse_attention_unit_amd/csrc/rt_common.hpp"],
-    "sha256": "9849623676254ff5ddba929077b458600463d3bf6abd11be3165da442d0481bb",
-    "fetch_kib": 11007.239, "write_kib": 32218.937,
-    "fetch_scale": 262144.0 / 131096.312, "write_scale": 262144.0 / 262144.0,
+    "sha256": "e63b17b1c985c28d854e13173c5f455a41fc1fbc642f25c8d2d5c8d8f41a4320",
+    "fetch_kib": 11013.253, "write_kib": 28480.546,
+    "fetch_scale": 262144.0 / 131088.438, "write_scale": 262144.0 / 262144.0,
 }
 
 
