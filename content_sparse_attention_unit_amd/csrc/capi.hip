@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <cmath>
 #include <mutex>
 
@@ -26,6 +27,20 @@ rt_status fail(rt_status st, const char* fmt, ...) {
 
 rt_status hip_fail(const char* where, hipError_t e) {
     return fail(RT_EHIP, "%s: kernel launch failed: %s", where, hipGetErrorString(e));
+}
+
+// Required tensor pointers: non-null and 16-byte aligned (the kernels move
+// token rows, centroids and index lists in 16-byte vector accesses).
+rt_status check_ptrs(const char* fn, std::initializer_list<const void*> ptrs) {
+    int i = 0;
+    for (const void* p : ptrs) {
+        if (p == nullptr) return fail(RT_EINVAL, "%s: null tensor pointer (argument %d)", fn, i);
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(RT_EINVAL, "%s: tensor pointer %p (argument %d) not 16-byte aligned", fn,
+                        p, i);
+        ++i;
+    }
+    return RT_OK;
 }
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -178,7 +193,7 @@ namespace {
 rt_status check_route(const char* fn, const void* qk, int dtype, const float* mu, int B, int H,
                       int n, int d, int k, int w, const float* inv_norm, const int32_t* idx) {
     g_err[0] = 0;
-    if (!qk || !mu || !inv_norm || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {qk, mu, inv_norm, idx})) return st;
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
     if (st != RT_OK) return st;
     if (k <= 0 || w <= 0) return fail(RT_EINVAL, "%s: k=%d and w=%d must be positive", fn, k, w);
@@ -297,7 +312,7 @@ rt_status routed_attn_impl(const char* fn, const void* q, const void* kk, const 
                            void* stream, float* mu = nullptr, float lambda = 0.f,
                            int phases = kBothPhases, bool sums_in_ws = true) {
     g_err[0] = 0;
-    if (!q || !kk || !v || !idx || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {q, kk, v, idx, out})) return st;
     if (mu != nullptr && !(lambda >= 0.f && lambda <= 1.f))
         return fail(RT_EINVAL, "%s: lambda=%g outside [0, 1]", fn, (double)lambda);
     if ((q_inv == nullptr) != (k_inv == nullptr))
@@ -377,9 +392,9 @@ rt_status rt_routed_attn_update(const void* q, const void* kk, const void* v, in
                                 float* lse, float* mu, float lambda, void* ws, size_t ws_bytes,
                                 void* stream) {
     static const char* fn = "rt_routed_attn_update";
-    if (!mu) {
+    if (!mu || reinterpret_cast<uintptr_t>(mu) % 16 != 0) {
         g_err[0] = 0;
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+        return check_ptrs(fn, {mu});
     }
     return routed_attn_impl(fn, q, kk, v, dtype, q_inv, k_inv, idx, nullptr, member_mask, B, H, n,
                             d, k, w, scale, causal, out, out_dtype, lse, nullptr, nullptr, ws,
@@ -407,7 +422,7 @@ rt_status rt_scatter_rows(const uint32_t* member_mask, int dtype, int B, int H, 
                           void* stream) {
     static const char* fn = "rt_scatter_rows";
     g_err[0] = 0;
-    if (!member_mask || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {member_mask, out})) return st;
     if (mu != nullptr && sum_q == nullptr)
         return fail(RT_EINVAL, "%s: the update needs sum_q", fn);
     if (B <= 0 || H <= 0 || n <= 0 || d <= 0)
@@ -446,9 +461,9 @@ rt_status rt_routed_attn_split(const void* q, const void* kk, const void* v, int
                                float* lse, float* sum_q, float* sum_k, void* ws, size_t ws_bytes,
                                void* stream) {
     static const char* fn = "rt_routed_attn_split";
-    if (!idx_q) {
+    if (!idx_q || reinterpret_cast<uintptr_t>(idx_q) % 16 != 0) {
         g_err[0] = 0;
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+        return check_ptrs(fn, {idx_q});
     }
     return routed_attn_impl(fn, q, kk, v, dtype, q_inv, k_inv, idx_k, idx_q, q_mask, B, H, n, d,
                             k, w, scale, 0, out, out_dtype, lse, sum_q, sum_k, ws, ws_bytes,
@@ -460,7 +475,7 @@ rt_status rt_local_attn(const void* q, const void* kk, const void* v, int dtype,
                         int out_dtype, void* stream) {
     static const char* fn = "rt_local_attn";
     g_err[0] = 0;
-    if (!q || !kk || !v || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {q, kk, v, out})) return st;
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
     if (st != RT_OK) return st;
     if (window < 1) return fail(RT_EINVAL, "%s: window=%d must be >= 1", fn, window);
@@ -480,7 +495,7 @@ rt_status rt_centroid_update(float* mu, const void* q, const float* q_inv, const
                              int d, int k, int w, float lambda, void* stream) {
     static const char* fn = "rt_centroid_update";
     g_err[0] = 0;
-    if (!mu || !q || !q_inv || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {mu, q, q_inv, idx})) return st;
     if ((kk == nullptr) != (k_inv == nullptr))
         return fail(RT_EINVAL, "%s: kk and k_inv must both be given or both be NULL", fn);
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
@@ -517,7 +532,7 @@ rt_status rt_in_proj(const void* x, const void* w_in, int B, int n, int dm, int 
                      void* qk, void* v, void* q_l, void* k_l, void* v_l, void* stream) {
     static const char* fn = "rt_in_proj";
     g_err[0] = 0;
-    if (!x || !w_in || !qk || !v) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {x, w_in, qk, v})) return st;
     if (L > 0 && (!q_l || !k_l || !v_l))
         return fail(RT_EINVAL, "%s: null local-head output with L=%d", fn, L);
     rt_status st = check_proj(fn, B, n, dm, d, R, L);
@@ -553,7 +568,9 @@ rt_status rt_out_proj(const void* o_r, const void* o_l, const void* w_o, const v
                       int n, int dm, int d, int R, int L, void* y, void* stream) {
     static const char* fn = "rt_out_proj";
     g_err[0] = 0;
-    if (!o_r || !w_o || !y || (L > 0 && !o_l)) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {o_r, w_o, y})) return st;
+    if (L > 0)
+        if (rt_status st = check_ptrs(fn, {o_l})) return st;
     rt_status st = check_proj(fn, B, n, dm, d, R, L);
     if (st != RT_OK) return st;
     if (y == o_r || y == w_o || (L > 0 && y == o_l))
@@ -580,7 +597,7 @@ rt_status rt_centroid_update_sums(float* mu, const float* sum_q, const float* su
                                   int H, int k, int d, float lambda, void* stream) {
     static const char* fn = "rt_centroid_update_sums";
     g_err[0] = 0;
-    if (!mu || !sum_q) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {mu, sum_q})) return st;
     if (B <= 0 || H <= 0 || k <= 0 || d <= 0)
         return fail(RT_EINVAL, "%s: sizes must be positive (B=%d H=%d k=%d d=%d)", fn, B, H, k, d);
     if (!(lambda >= 0.f && lambda <= 1.f))
@@ -600,8 +617,7 @@ rt_status rt_routed_attn_bwd(const void* q, const void* kk, const void* v, int d
                              float* dv, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_routed_attn_bwd";
     g_err[0] = 0;
-    if (!q || !kk || !v || !idx || !lse || !dout || !dq_hat || !dv)
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {q, kk, v, idx, lse, dout, dq_hat, dv})) return st;
     if ((q_inv == nullptr) != (k_inv == nullptr))
         return fail(RT_EINVAL, "%s: q_inv and k_inv must both be given or both be NULL", fn);
     if (dk_hat == nullptr && !(q == kk && q_inv == k_inv))
@@ -649,8 +665,7 @@ rt_status rt_local_attn_bwd(const void* q, const void* kk, const void* v, const 
                             size_t ws_bytes, void* stream) {
     static const char* fn = "rt_local_attn_bwd";
     g_err[0] = 0;
-    if (!q || !kk || !v || !dout || !dq || !dk || !dv)
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {q, kk, v, dout, dq, dk, dv})) return st;
     {
         const void* outs[3] = {dq, dk, dv};
         const void* ins[4] = {q, kk, v, dout};
@@ -682,7 +697,7 @@ rt_status rt_normalize_bwd(const void* x, int dtype, const float* inv_norm, cons
                            const float* g2, long rows, int d, float* dx, void* stream) {
     static const char* fn = "rt_normalize_bwd";
     g_err[0] = 0;
-    if (!x || !inv_norm || !g1 || !dx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {x, inv_norm, g1, dx})) return st;
     if (rows <= 0 || d <= 0) return fail(RT_EINVAL, "%s: rows=%ld and d=%d must be positive", fn,
                                          rows, d);
     if (dtype != RT_F32 && dtype != RT_BF16)
@@ -702,8 +717,9 @@ rt_status rt_out_proj_bwd(const void* dy, const void* o_r, const void* o_l, cons
                           float* dw_o, void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_out_proj_bwd";
     g_err[0] = 0;
-    if (!dy || !o_r || !w_o || !do_r || !dw_o || (L > 0 && (!o_l || !do_l)))
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {dy, o_r, w_o, do_r, dw_o})) return st;
+    if (L > 0)
+        if (rt_status st = check_ptrs(fn, {o_l, do_l})) return st;
     rt_status st = check_proj(fn, B, n, dm, d, R, L);
     if (st != RT_OK) return st;
     {
@@ -761,8 +777,9 @@ rt_status rt_in_proj_bwd(const void* x, const void* w_in, const float* dqk, cons
                          void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_in_proj_bwd";
     g_err[0] = 0;
-    if (!x || !w_in || !dqk || !dv || !dx || !dw_in || (L > 0 && (!dq_l || !dk_l || !dv_l)))
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {x, w_in, dqk, dv, dx, dw_in})) return st;
+    if (L > 0)
+        if (rt_status st = check_ptrs(fn, {dq_l, dk_l, dv_l})) return st;
     rt_status st = check_proj(fn, B, n, dm, d, R, L);
     if (st != RT_OK) return st;
     {
@@ -819,7 +836,7 @@ rt_status rt_local_attn_blocked(const void* q, const void* kk, const void* v, in
                                 void* out, int out_dtype, void* stream) {
     static const char* fn = "rt_local_attn_blocked";
     g_err[0] = 0;
-    if (!q || !kk || !v || !out) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {q, kk, v, out})) return st;
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
     if (st != RT_OK) return st;
     if (block < 1) return fail(RT_EINVAL, "%s: block=%d must be >= 1", fn, block);
@@ -841,7 +858,7 @@ rt_status rt_centroid_update_argmax(float* mu, const void* q, const void* kk, in
                                     size_t ws_bytes, void* stream) {
     static const char* fn = "rt_centroid_update_argmax";
     g_err[0] = 0;
-    if (!mu || !q) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {mu, q})) return st;
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
     if (st != RT_OK) return st;
     if (k <= 0) return fail(RT_EINVAL, "%s: k=%d must be positive", fn, k);
@@ -883,7 +900,7 @@ rt_status rt_route_partition(const void* qk, int dtype, const float* mu, int B, 
                              void* ws, size_t ws_bytes, void* stream) {
     static const char* fn = "rt_route_partition";
     g_err[0] = 0;
-    if (!qk || !mu || !inv_norm || !idx) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {qk, mu, inv_norm, idx})) return st;
     rt_status st = check_tokens(fn, dtype, B, H, n, d);
     if (st != RT_OK) return st;
     if (k <= 0) return fail(RT_EINVAL, "%s: k=%d must be positive", fn, k);
@@ -918,9 +935,7 @@ rt_status rt_decode_fill(const void* qk, const float* inv_norm, const void* v, c
                          void* stream) {
     static const char* fn = "rt_decode_fill";
     g_err[0] = 0;
-    if (!qk || !inv_norm || !v || !idx || !cache_k || !cache_inv || !cache_v || !cache_pos ||
-        !cache_len)
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {qk, inv_norm, v, idx, cache_k, cache_inv, cache_v, cache_pos, cache_len})) return st;
     rt_status st = check_tokens(fn, RT_BF16, B, H, n, d);
     if (st == RT_OK) st = check_clusters(fn, n, k, w);
     if (st == RT_OK) st = check_entries(fn, "cap", cap);
@@ -939,7 +954,7 @@ rt_status rt_decode_ring_fill(const void* kk, const void* v, int B, int H, int n
                               int window, void* ring_k, void* ring_v, void* stream) {
     static const char* fn = "rt_decode_ring_fill";
     g_err[0] = 0;
-    if (!kk || !v || !ring_k || !ring_v) return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {kk, v, ring_k, ring_v})) return st;
     rt_status st = check_tokens(fn, RT_BF16, B, H, n, d);
     if (st == RT_OK) st = check_entries(fn, "window", window);
     if (st != RT_OK) return st;
@@ -955,9 +970,7 @@ rt_status rt_decode_routed(const void* qk_t, const void* v_t, const float* mu, i
                            int out_dtype, int32_t* label, void* stream) {
     static const char* fn = "rt_decode_routed";
     g_err[0] = 0;
-    if (!qk_t || !v_t || !mu || !cache_k || !cache_inv || !cache_v || !cache_pos || !cache_len ||
-        !out)
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {qk_t, v_t, mu, cache_k, cache_inv, cache_v, cache_pos, cache_len, out})) return st;
     rt_status st = check_decode(fn, B, H, d);
     if (st == RT_OK) st = check_entries(fn, "cap", cap);
     if (st != RT_OK) return st;
@@ -979,8 +992,7 @@ rt_status rt_decode_local(const void* q_t, const void* k_t, const void* v_t, int
                           int out_dtype, void* stream) {
     static const char* fn = "rt_decode_local";
     g_err[0] = 0;
-    if (!q_t || !k_t || !v_t || !ring_k || !ring_v || !out)
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {q_t, k_t, v_t, ring_k, ring_v, out})) return st;
     rt_status st = check_decode(fn, B, H, d);
     if (st == RT_OK) st = check_entries(fn, "window", window);
     if (st != RT_OK) return st;
@@ -1000,8 +1012,7 @@ rt_status rt_attn_js(const void* qk, const float* q_inv, const int32_t* idx, con
                      size_t ws_bytes, void* stream) {
     static const char* fn = "rt_attn_js";
     g_err[0] = 0;
-    if (!qk || !q_inv || !idx || !q_l || !k_l || !js)
-        return fail(RT_EINVAL, "%s: null tensor pointer", fn);
+    if (rt_status st = check_ptrs(fn, {qk, q_inv, idx, q_l, k_l, js})) return st;
     rt_status st = check_tokens(fn, RT_BF16, B, H, n, d);
     if (st == RT_OK) st = check_clusters(fn, n, k, w);
     if (st != RT_OK) return st;

@@ -10,7 +10,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every tensor pointer is a DEVICE pointer to contiguous row-major memory
- *    owned by the caller.  Token tensors are [B][H][n][d] (d fastest);
+ *    owned by the caller, aligned to 16 bytes (the kernels use 16-byte vector
+ *    accesses); a required pointer that is NULL or misaligned returns
+ *    RT_EINVAL.  Optional pointers (documented as such) may be NULL.  Token tensors are [B][H][n][d] (d fastest);
  *    centroids [H][k][d] float32; inverse norms [B][H][n] float32;
  *    memberships idx [B][H][k][w] int32; lse [B][H][k][w] float32;
  *    scores [B][H][k][n] float32.
